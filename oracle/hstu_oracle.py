@@ -1,0 +1,341 @@
+"""Float64 CPU oracle of the HSTU layer forward on jagged sequences.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module. It shares no
+code, constants or helpers with the HIP library.
+
+Every function is the plain definition, evaluated in float64 with NumPy,
+looping over sequences and heads with dense per-sequence matrices. Pages
+cited (by title; section, equation or figure):
+
+[GR-7.1]   "HSTU：Scaling Law 的首次探索" (fun-rec mdbook, chapter 7.1)
+[NOTES]    "万亿参数推荐大模型：HSTU 架构如何超越传统 Self-Attention"
+           (reading notes on arXiv:2402.17152)
+[GENRANK]  "6.2. HSTU的工程突破" (fun-rec, chapter 6.2, GenRank)
+[SA2HSTU]  "从自注意力到 HSTU：解构下一代推荐系统引擎"
+
+Readings taken where the pages leave a step open (each also listed in the
+design notes of the repository):
+
+* score scale alpha defaults to 1: the layer equations in [NOTES] §2.1 and
+  [SA2HSTU] step 2 carry no 1/sqrt(d) (only [GENRANK] eq. 6.2.3 restates the
+  score with one); alpha is a parameter;
+* phi2(.) V(X) is a matrix product ([NOTES] §2.1 and [SA2HSTU] step 2 print
+  a product; the element-wise sign in [GR-7.1] §7.1.4 cannot apply to an
+  N x N by N x d pair);
+* no softmax and no normalisation of the SiLU weights ([GR-7.1] §7.1.4,
+  innovation 1);
+* the causal mask keeps the diagonal (j <= i);
+* the residual Y = X + f2(...) comes from the block diagram of [NOTES] §2.1
+  ("残差连接", residual connection); no LayerNorm before f1;
+* Norm is LayerNorm over all d features of the token, biased variance,
+  eps from the caller (1e-5), affine gamma/beta;
+* Split order is U, V, Q, K, contiguous chunks of width d; head h owns
+  columns [h*dh, (h+1)*dh) of each chunk;
+* rab_{p,t}(i, j) = pos_bias[(p_i - p_j) + n_max - 1]
+                  + time_bias[min(nb - 1, floor(log2(|t_i - t_j| + 1)))],
+  shared by all heads ([GR-7.1] §7.1.4 innovation 2 names the position and
+  time differences; the bucketed time difference follows [GENRANK] eq.
+  6.2.6's bucket(t_i - t_j)); the floor(log2) is taken in integers;
+* targets (ranking candidates, [GR-7.1] §7.1.5 M-FALCON and [GENRANK]
+  §6.2.2 Fig. 6.2.2): history is causal, a candidate sees the whole history
+  and itself but no other candidate; all candidates of a sequence share the
+  "next" position n + (L - m).
+
+Visibility, in one rule: within sequence b the keys are [its cache rows,
+then its own tokens]. Key j is visible to query i iff j is a cache row, or
+j <= i and (j is not a target or j == i) (own-token indices).
+"""
+
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+F64 = np.float64
+
+
+# --------------------------------------------------------------------------
+# scalar pieces
+# --------------------------------------------------------------------------
+
+def silu(z):
+    """SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z)).
+
+    phi1 and phi2 of [NOTES] §2.1 are both SiLU. Written as z / (1 + e^{-z});
+    for very negative z the denominator overflows to +inf and the value
+    correctly tends to -0."""
+    z = np.asarray(z, dtype=F64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def time_bucket(dt, num_buckets: int = 32):
+    """min(num_buckets - 1, floor(log2(|dt| + 1))) computed in integers.
+
+    floor(log2(a)) for an integer a >= 1 is its bit length minus one, found
+    here by repeated halving of the shift width (no floating point)."""
+    a = np.abs(np.asarray(dt, dtype=np.int64)).astype(np.uint64) + np.uint64(1)
+    r = np.zeros(a.shape, dtype=np.int64)
+    for s in (32, 16, 8, 4, 2, 1):
+        hi = (a >> np.uint64(s)) > 0
+        a = np.where(hi, a >> np.uint64(s), a)
+        r = r + np.where(hi, s, 0)
+    return np.minimum(r, num_buckets - 1)
+
+
+# --------------------------------------------------------------------------
+# the three steps of the layer
+# --------------------------------------------------------------------------
+
+def proj(x, w1, b1, d: int):
+    """Pointwise projection: U, V, Q, K = Split(SiLU(X W1^T + b1)).
+
+    [NOTES] §2.1 first equation; [SA2HSTU] step 1. f1 is one linear layer
+    (weight [4d, d] in out x in layout), phi1 = SiLU."""
+    x = np.asarray(x, F64)
+    z = x @ np.asarray(w1, F64).T
+    if b1 is not None:
+        z = z + np.asarray(b1, F64)
+    h = silu(z)
+    return h[:, 0:d], h[:, d:2 * d], h[:, 2 * d:3 * d], h[:, 3 * d:4 * d]
+
+
+def _positions(L: int, m: int, n_cache: int) -> np.ndarray:
+    """Positions of a sequence's own tokens: non-targets n_cache + j, all
+    targets share n_cache + (L - m)."""
+    p = n_cache + np.arange(L, dtype=np.int64)
+    if m > 0:
+        p[L - m:] = n_cache + (L - m)
+    return p
+
+
+def _visibility(L: int, m: int, n_cache: int, rows: np.ndarray) -> np.ndarray:
+    """Boolean [len(rows), n_cache + L] mask of visible keys for the given
+    own-token query rows."""
+    j = np.arange(L)
+    i = rows[:, None]
+    own = (j[None, :] <= i) & ((j[None, :] < L - m) | (j[None, :] == i))
+    cache = np.ones((rows.shape[0], n_cache), dtype=bool)
+    return np.concatenate([cache, own], axis=1)
+
+
+def attention(q, k, v, offsets, timestamps, pos_bias, time_bias, num_heads: int,
+              n_max: int, alpha: float = 1.0, num_targets=None, cache=None,
+              rows=None, row_chunk: int = 2048):
+    """Spatial aggregation, per head h of every sequence b:
+
+        AV_h = (SiLU(alpha * Q_h K_h^T + rab_{p,t}) * Mask) V_h
+
+    [NOTES] §2.1 second equation; [SA2HSTU] step 2; no softmax, no row
+    normalisation ([GR-7.1] §7.1.4 innovation 1). rab and the mask as in the
+    module docstring.
+
+    q, k, v: [T, d] own tokens. offsets [B+1], timestamps [T].
+    num_targets: None or int array [B] (last m_b tokens of b are targets).
+    cache: None or dict(k=[Tc, d], v=[Tc, d], offsets=[B+1], timestamps=[Tc])
+           holding keys/values visible to every query of the same sequence.
+    rows: None (all tokens) or a sorted int array of global token rows; the
+          result then has one row per requested token. Query rows are
+          evaluated in chunks of ``row_chunk`` (each row's value is its own
+          dense definition; chunking only bounds memory).
+    Returns AV [T or len(rows), d] float64.
+    """
+    q = np.asarray(q, F64)
+    k = np.asarray(k, F64)
+    v = np.asarray(v, F64)
+    offsets = np.asarray(offsets, np.int64)
+    timestamps = np.asarray(timestamps, np.int64)
+    pos_bias = np.asarray(pos_bias, F64)
+    time_bias = np.asarray(time_bias, F64)
+    T, d = q.shape
+    dh = d // num_heads
+    B = offsets.shape[0] - 1
+    want = np.arange(T) if rows is None else np.asarray(rows, np.int64)
+    out = np.zeros((want.shape[0], d), dtype=F64)
+    nb = time_bias.shape[0]
+    for b in range(B):
+        s, e = int(offsets[b]), int(offsets[b + 1])
+        L = e - s
+        sel = np.nonzero((want >= s) & (want < e))[0]
+        if L == 0 or sel.size == 0:
+            continue
+        m = 0 if num_targets is None else int(num_targets[b])
+        if cache is not None:
+            cs, ce = int(cache["offsets"][b]), int(cache["offsets"][b + 1])
+            kc = np.asarray(cache["k"][cs:ce], F64)
+            vc = np.asarray(cache["v"][cs:ce], F64)
+            tc = np.asarray(cache["timestamps"][cs:ce], np.int64)
+        else:
+            cs = ce = 0
+            kc = np.zeros((0, d))
+            vc = np.zeros((0, d))
+            tc = np.zeros(0, np.int64)
+        nc = ce - cs
+        keys_k = np.concatenate([kc, k[s:e]], axis=0)
+        keys_v = np.concatenate([vc, v[s:e]], axis=0)
+        key_t = np.concatenate([tc, timestamps[s:e]])
+        key_p = np.concatenate([np.arange(nc, dtype=np.int64), _positions(L, m, nc)])
+        own_p = _positions(L, m, nc)
+        for c0 in range(0, sel.size, row_chunk):
+            csel = sel[c0:c0 + row_chunk]
+            qrows = want[csel] - s                      # own-token indices
+            dp = own_p[qrows][:, None] - key_p[None, :]
+            dt = timestamps[s + qrows][:, None] - key_t[None, :]
+            idx = dp + (n_max - 1)
+            mask = _visibility(L, m, nc, qrows)
+            if np.any(mask & ((idx < 0) | (idx >= pos_bias.shape[0]))):
+                raise ValueError("position difference outside the position table")
+            idx = np.clip(idx, 0, pos_bias.shape[0] - 1)
+            rab = pos_bias[idx] + time_bias[time_bucket(dt, nb)]
+            for h in range(num_heads):
+                cols = slice(h * dh, (h + 1) * dh)
+                scores = alpha * (q[s + qrows, cols] @ keys_k[:, cols].T) + rab
+                a = np.where(mask, silu(scores), 0.0)
+                out[csel, cols] = a @ keys_v[:, cols]
+    return out
+
+
+def norm_gate(av, u, gamma, beta, eps: float):
+    """G = (LayerNorm(AV) * gamma + beta) (.) U.
+
+    [NOTES] §2.1 third equation and block diagram (LayerNorm, then the
+    product with U); [SA2HSTU] step 3. LayerNorm over all d features of the
+    token with the biased variance."""
+    av = np.asarray(av, F64)
+    mu = av.mean(axis=1, keepdims=True)
+    var = ((av - mu) ** 2).mean(axis=1, keepdims=True)
+    n = (av - mu) / np.sqrt(var + eps)
+    if gamma is not None:
+        n = n * np.asarray(gamma, F64)
+    if beta is not None:
+        n = n + np.asarray(beta, F64)
+    return n * np.asarray(u, F64)
+
+
+def output(x, g, w2, b2):
+    """Y = X + G W2^T + b2: f2 is one linear layer ([NOTES] §2.1 third
+    equation) and the residual from the input is the block diagram's skip
+    connection."""
+    y = np.asarray(x, F64) + np.asarray(g, F64) @ np.asarray(w2, F64).T
+    if b2 is not None:
+        y = y + np.asarray(b2, F64)
+    return y
+
+
+def _needed_prefix_rows(offsets, rows):
+    """Global rows whose projections the requested query rows depend on: for
+    each sequence, its prefix up to the last requested row."""
+    offsets = np.asarray(offsets, np.int64)
+    need = []
+    for b in range(offsets.shape[0] - 1):
+        s, e = int(offsets[b]), int(offsets[b + 1])
+        r = rows[(rows >= s) & (rows < e)]
+        if r.size:
+            need.append(np.arange(s, int(r.max()) + 1))
+    return np.concatenate(need) if need else np.zeros(0, np.int64)
+
+
+def layer(x, p, offsets, timestamps, num_heads: int, n_max: int, alpha: float = 1.0,
+          eps: float = 1e-5, num_targets=None, cache=None, rows=None) -> Dict[str, np.ndarray]:
+    """One HSTU layer: projection, spatial aggregation, pointwise
+    transformation ([NOTES] §2.1, all three equations, plus the residual).
+
+    ``p`` has attributes w1, b1, w2, b2, gamma, beta, pos_bias, time_bias.
+    With ``rows`` given, only those token rows are produced (their causal
+    prefixes are projected as needed). Returns a dict with u, v, q, k (for
+    the projected rows ``proj_rows``), av, g and y (for the output rows)."""
+    x = np.asarray(x, F64)
+    offsets = np.asarray(offsets, np.int64)
+    T, d = x.shape
+    if rows is None:
+        prow = np.arange(T)
+        orow = np.arange(T)
+    else:
+        orow = np.asarray(rows, np.int64)
+        prow = _needed_prefix_rows(offsets, orow)
+    u = np.zeros((T, d)); vv = np.zeros((T, d)); qq = np.zeros((T, d)); kk = np.zeros((T, d))
+    pu, pv, pq, pk = proj(x[prow], p.w1, p.b1, d)
+    u[prow], vv[prow], qq[prow], kk[prow] = pu, pv, pq, pk
+    av = attention(qq, kk, vv, offsets, timestamps, p.pos_bias, p.time_bias, num_heads,
+                   n_max, alpha, num_targets=num_targets, cache=cache,
+                   rows=None if rows is None else orow)
+    g = norm_gate(av, u[orow], p.gamma, p.beta, eps)
+    y = output(x[orow], g, p.w2, p.b2)
+    return dict(u=u, v=vv, q=qq, k=kk, av=av, g=g, y=y, proj_rows=prow, rows=orow)
+
+
+def stack(x, layers: Sequence, offsets, timestamps, num_heads: int, n_max: int,
+          alpha: float = 1.0, eps: float = 1e-5, return_all: bool = False):
+    """L stacked layers: layer l's output is layer l+1's input ([GR-7.1]
+    §7.1.6 scales depth; [NOTES] §2.1 defines one layer)."""
+    h = np.asarray(x, F64)
+    outs = [h]
+    for p in layers:
+        h = layer(h, p, offsets, timestamps, num_heads, n_max, alpha, eps)["y"]
+        outs.append(h)
+    return outs if return_all else h
+
+
+def embed(item_emb, action_emb, item_ids, actions):
+    """Action-oriented token: e_i = phi(x_i) + varphi(a_i), item embedding
+    plus action embedding ([GENRANK] §6.2.2, eq. 6.2.2)."""
+    return (np.asarray(item_emb, F64)[np.asarray(item_ids)] +
+            np.asarray(action_emb, F64)[np.asarray(actions)])
+
+
+# --------------------------------------------------------------------------
+# ranking inference over a cached history (M-FALCON)
+# --------------------------------------------------------------------------
+
+def ranking(w, b_m: Optional[int] = None, eps: Optional[float] = None) -> Dict[str, List]:
+    """Candidate scoring with micro-batches over a cached history, following
+    [GR-7.1] §7.1.5 (M-FALCON: batched candidates with a mask, micro-batches,
+    history K/V computed once and reused by every micro-batch).
+
+    1. The history runs causally through every layer; layer l keeps K_l, V_l.
+    2. Candidates are cut per user into micro-batches of b_m. Each
+       micro-batch runs through the layers; at layer l its own tokens are all
+       targets and the cache is (K_l, V_l) of the history.
+
+    ``w`` is a ranking workload (``hstu_inputs.gen.make_ranking``). Returns
+    dict(hist_y=[per layer outputs], cand_y=[T_cand, d] final candidate
+    outputs in cand_x row order)."""
+    from hstu_inputs.gen import micro_batches  # input layout only
+    eps = w.ln_eps if eps is None else eps
+    x = np.asarray(w.x, F64)
+    caches = []
+    hist_out = [x]
+    for p in w.layers:
+        r = layer(x, p, w.offsets, w.timestamps, w.num_heads, w.n_max, w.alpha, eps)
+        caches.append(dict(k=r["k"], v=r["v"], offsets=w.offsets, timestamps=w.timestamps))
+        x = r["y"]
+        hist_out.append(x)
+    cand_y = np.zeros((int(w.cand_offsets[-1]), w.d_model))
+    for offs, rws in micro_batches(w, b_m):
+        xc = np.asarray(w.cand_x, F64)[rws]
+        tc = np.asarray(w.cand_timestamps, np.int64)[rws]
+        m = np.diff(offs)
+        for l, p in enumerate(w.layers):
+            xc = layer(xc, p, offs, tc, w.num_heads, w.n_max, w.alpha, eps,
+                       num_targets=m, cache=caches[l])["y"]
+        cand_y[rws] = xc
+    return dict(hist_y=hist_out, cand_y=cand_y)
+
+
+def ranking_independent(w, user: int, cand: int, eps: Optional[float] = None):
+    """One candidate scored on its own: a plain causal forward over
+    [history of ``user``, that one candidate] through every layer, no cache
+    and no target mask. Returns the candidate's final output row. M-FALCON's
+    batched, micro-batched and cached scoring must reproduce it ([GR-7.1]
+    §7.1.5: batching changes the cost, not the per-candidate scores)."""
+    eps = w.ln_eps if eps is None else eps
+    s, e = int(w.offsets[user]), int(w.offsets[user + 1])
+    c = int(w.cand_offsets[user]) + cand
+    x = np.concatenate([np.asarray(w.x[s:e], F64), np.asarray(w.cand_x[c:c + 1], F64)])
+    ts = np.concatenate([w.timestamps[s:e], w.cand_timestamps[c:c + 1]])
+    offs = np.array([0, x.shape[0]], np.int64)
+    for p in w.layers:
+        x = layer(x, p, offs, ts, w.num_heads, w.n_max, w.alpha, eps)["y"]
+    return x[-1]

@@ -1,0 +1,547 @@
+"""Pins for the CPU oracle (no GPU).
+
+The oracle is checked against things other than itself: brute force on tiny
+inputs, independent library routines (scipy's expit, torch's layer_norm and
+linear in float64), closed forms, invariants (causality, jagged-vs-padded,
+head independence, linearity), the bucket definition in integers, and the
+worked intensity example of the pointwise-aggregation section.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from hstu_inputs import gen
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+
+def _tiny(lengths, d=8, H=2, seed=0, affine="random", n_max=None, dtype="f32"):
+    return gen.make_custom(lengths, d, H, dtype=dtype, seed=seed, affine=affine, n_max=n_max)
+
+
+def _attn(w, q, k, v, p=None, **kw):
+    p = p or w.layers[0]
+    return oracle.attention(q, k, v, w.offsets, w.timestamps, p.pos_bias, p.time_bias,
+                            w.num_heads, w.n_max, w.alpha, **kw)
+
+
+def _qkv(w, l=0):
+    return oracle.proj(w.x, w.layers[l].w1, w.layers[l].b1, w.d_model)
+
+
+def _brute_attention(q, k, v, offsets, ts, pb, tb, H, n_max, alpha, num_targets=None,
+                     cache=None):
+    """Scalar triple loop straight from the definition (pure Python floats)."""
+    T, d = len(q), len(q[0])
+    dh = d // H
+    out = [[0.0] * d for _ in range(T)]
+    for b in range(len(offsets) - 1):
+        s, e = int(offsets[b]), int(offsets[b + 1])
+        L = e - s
+        m = 0 if num_targets is None else int(num_targets[b])
+        keys = []  # (k_row, v_row, position, timestamp, kind, own index)
+        nc = 0
+        if cache is not None:
+            cs, ce = int(cache["offsets"][b]), int(cache["offsets"][b + 1])
+            nc = ce - cs
+            for c in range(nc):
+                keys.append((cache["k"][cs + c], cache["v"][cs + c], c,
+                             int(cache["timestamps"][cs + c]), "cache", -1))
+        for j in range(L):
+            pos = nc + (j if j < L - m else L - m)
+            keys.append((k[s + j], v[s + j], pos, int(ts[s + j]), "own", j))
+        for i in range(L):
+            p_i = nc + (i if i < L - m else L - m)
+            t_i = int(ts[s + i])
+            for (kr, vr, p_j, t_j, kind, j) in keys:
+                if kind == "own":
+                    if j > i:
+                        continue
+                    if j >= L - m and j != i:
+                        continue
+                bucket = min(len(tb) - 1, (abs(t_i - t_j) + 1).bit_length() - 1)
+                rab = float(pb[p_i - p_j + n_max - 1]) + float(tb[bucket])
+                for h in range(H):
+                    dot = 0.0
+                    for c in range(h * dh, (h + 1) * dh):
+                        dot += float(q[s + i][c]) * float(kr[c])
+                    sc = alpha * dot + rab
+                    wgt = sc / (1.0 + math.exp(-sc)) if sc > -700 else 0.0
+                    for c in range(h * dh, (h + 1) * dh):
+                        out[s + i][c] += wgt * float(vr[c])
+    return np.array(out)
+
+
+# ---------------------------------------------------------------------------
+# scalar pieces
+# ---------------------------------------------------------------------------
+
+def test_time_bucket_bruteforce_small():
+    dt = np.arange(0, 1 << 20, dtype=np.int64)
+    want = np.array([min(31, (int(a) + 1).bit_length() - 1) for a in dt[:5000]])
+    assert np.array_equal(oracle.time_bucket(dt[:5000]), want)
+    # full range against the integer definition via Python ints (vectorised
+    # through a lookup of bit lengths per power-of-two band)
+    got = oracle.time_bucket(dt)
+    for kk in range(21):
+        lo, hi = (1 << kk) - 1, (1 << (kk + 1)) - 1   # |dt|+1 in [2^k, 2^(k+1))
+        band = got[lo:min(hi, dt.size)]
+        assert np.all(band == min(kk, 31)), kk
+
+
+def test_time_bucket_boundaries_and_clamp():
+    for kk in range(1, 63):
+        dt = (1 << kk) - 1  # |dt| + 1 == 2^k     -> bucket k
+        assert oracle.time_bucket(np.array([dt]), 64)[0] == kk
+        assert oracle.time_bucket(np.array([dt]))[0] == min(kk, 31)
+        # |dt| + 1 == 2^k - 1 -> bucket k - 1;  |dt| + 1 == 2^k + 1 -> bucket k
+        assert oracle.time_bucket(np.array([dt - 1]), 64)[0] == kk - 1
+        assert oracle.time_bucket(np.array([dt + 1]), 64)[0] == kk
+    assert oracle.time_bucket(np.array([0]))[0] == 0
+    assert oracle.time_bucket(np.array([1]))[0] == 1
+    assert oracle.time_bucket(np.array([2]))[0] == 1
+    assert oracle.time_bucket(np.array([3]))[0] == 2
+    # symmetric in the sign of dt, clamp at num_buckets-1
+    x = np.array([-5, 5, -(1 << 40), (1 << 40)])
+    assert list(oracle.time_bucket(x)) == [2, 2, 31, 31]
+    assert list(oracle.time_bucket(x, num_buckets=8)) == [2, 2, 7, 7]
+
+
+def test_silu_against_expit_and_identities():
+    from scipy.special import expit
+    z = np.linspace(-60, 60, 4001)
+    np.testing.assert_allclose(oracle.silu(z), z * expit(z), rtol=1e-14, atol=1e-300)
+    assert oracle.silu(0.0) == 0.0
+    np.testing.assert_allclose(oracle.silu(z) - oracle.silu(-z), z, rtol=1e-13, atol=1e-13)
+    assert oracle.silu(-1e4) == 0.0
+    assert oracle.silu(1e4) == 1e4
+
+
+# ---------------------------------------------------------------------------
+# projection
+# ---------------------------------------------------------------------------
+
+def test_proj_against_torch_linear():
+    import torch
+    w = _tiny([5, 3], d=8, H=2, seed=3)
+    p = w.layers[0]
+    u, v, q, k = oracle.proj(w.x, p.w1, p.b1, 8)
+    z = torch.nn.functional.linear(torch.tensor(w.x, dtype=torch.float64),
+                                   torch.tensor(p.w1, dtype=torch.float64),
+                                   torch.tensor(p.b1, dtype=torch.float64))
+    h = torch.nn.functional.silu(z).numpy()
+    np.testing.assert_allclose(np.concatenate([u, v, q, k], 1), h, rtol=1e-13, atol=1e-15)
+
+
+def test_proj_bruteforce_and_split_order():
+    w = _tiny([4], d=4, H=1, seed=4)
+    p = w.layers[0]
+    u, v, q, k = oracle.proj(w.x, p.w1, p.b1, 4)
+    for t in range(4):
+        for o in range(16):
+            z = float(p.b1[o]) + sum(float(w.x[t][i]) * float(p.w1[o][i]) for i in range(4))
+            want = z / (1 + math.exp(-z))
+            got = [u, v, q, k][o // 4][t][o % 4]
+            assert abs(got - want) < 1e-12
+    # split order U, V, Q, K: W1 = 0 and chunk biases 1, 2, 3, 4
+    b1 = np.repeat(np.arange(1.0, 5.0), 4)
+    u, v, q, k = oracle.proj(w.x, np.zeros((16, 4)), b1, 4)
+    for chunk, c in zip((u, v, q, k), (1.0, 2.0, 3.0, 4.0)):
+        np.testing.assert_allclose(chunk, c / (1 + math.exp(-c)), rtol=1e-15)
+
+
+def test_u_chunk_zero_gives_residual_plus_bias():
+    w = _tiny([6, 4], d=8, H=2, seed=5)
+    p = w.layers[0]
+    p.w1[0:8] = 0.0
+    p.b1[0:8] = 0.0
+    r = oracle.layer(w.x, p, w.offsets, w.timestamps, 2, w.n_max)
+    assert np.all(r["u"] == 0.0)
+    np.testing.assert_allclose(r["y"], w.x.astype(np.float64) + p.b2.astype(np.float64), rtol=0, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("lengths,H,d", [([1], 1, 4), ([5, 1, 7], 2, 8), ([9, 16], 2, 4),
+                                         ([0, 3, 0, 6], 2, 8)])
+def test_attention_bruteforce(lengths, H, d):
+    w = _tiny(lengths, d=d, H=H, seed=7, n_max=16)
+    w.alpha = 0.7
+    p = w.layers[0]
+    # widen the time gaps so that many buckets are exercised
+    w.timestamps = w.timestamps + np.arange(w.total_tokens) ** 3
+    u, v, q, k = _qkv(w)
+    got = _attn(w, q, k, v)
+    want = _brute_attention(q, k, v, w.offsets, w.timestamps, p.pos_bias, p.time_bias,
+                            H, w.n_max, w.alpha)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_bruteforce_targets_and_cache():
+    w = gen.make_ranking(seed=11, users=3, history=[4, 0, 6], candidates=[3, 2, 1],
+                         micro_batch=2, d_model=8, num_heads=2, num_layers=1, affine="random",
+                         dtype="f32")
+    p = w.layers[0]
+    rng = np.random.default_rng(0)
+    hk = rng.standard_normal((w.total_tokens, 8))
+    hv = rng.standard_normal((w.total_tokens, 8))
+    cache = dict(k=hk, v=hv, offsets=w.offsets, timestamps=w.timestamps)
+    cq = rng.standard_normal((int(w.cand_offsets[-1]), 8))
+    ck = rng.standard_normal(cq.shape)
+    cv = rng.standard_normal(cq.shape)
+    # own tokens: 1 non-target followed by the rest as targets, per sequence
+    m = np.maximum(np.diff(w.cand_offsets) - 1, 0)
+    got = oracle.attention(cq, ck, cv, w.cand_offsets, w.cand_timestamps, p.pos_bias,
+                           p.time_bias, 2, w.n_max, 1.0, num_targets=m, cache=cache)
+    want = _brute_attention(cq, ck, cv, w.cand_offsets, w.cand_timestamps, p.pos_bias,
+                            p.time_bias, 2, w.n_max, 1.0, num_targets=m, cache=cache)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_closed_form_zero():
+    w = _tiny([7, 3], d=8, H=2)
+    p = w.layers[0]
+    p.pos_bias[:] = 0.0
+    p.time_bias[:] = 0.0
+    z = np.zeros((w.total_tokens, 8))
+    v = np.random.default_rng(1).standard_normal((w.total_tokens, 8))
+    assert np.all(_attn(w, z, z, v) == 0.0)
+
+
+def test_attention_closed_form_cumsum():
+    """Q = K = 0 and rab == c: AV_i = SiLU(c) * sum_{j<=i} v_j (weights sum
+    to (i+1) SiLU(c), more than 1: no normalisation)."""
+    w = _tiny([9, 4], d=8, H=2)
+    p = w.layers[0]
+    c = 0.375
+    p.pos_bias[:] = c
+    p.time_bias[:] = 0.0
+    z = np.zeros((w.total_tokens, 8))
+    v = np.random.default_rng(2).standard_normal((w.total_tokens, 8))
+    got = _attn(w, z, z, v)
+    sc = c / (1 + math.exp(-c))
+    for b in range(2):
+        s, e = w.offsets[b], w.offsets[b + 1]
+        np.testing.assert_allclose(got[s:e], sc * np.cumsum(v[s:e], axis=0), rtol=1e-13)
+
+
+def test_attention_closed_form_position_convolution():
+    """Q = K = 0, time table 0: AV = causal convolution of V with the kernel
+    SiLU(pos_bias[n_max - 1 + lag])."""
+    L = 12
+    w = _tiny([L], d=4, H=1, n_max=L)
+    p = w.layers[0]
+    p.time_bias[:] = 0.0
+    z = np.zeros((L, 4))
+    v = np.random.default_rng(3).standard_normal((L, 4))
+    got = _attn(w, z, z, v)
+    kern = oracle.silu(p.pos_bias.astype(np.float64)[L - 1:2 * L - 1])
+    for f in range(4):
+        np.testing.assert_allclose(got[:, f], np.convolve(v[:, f], kern)[:L], rtol=1e-12,
+                                   atol=1e-14)
+
+
+def test_attention_closed_form_time_convolution():
+    """Q = K = 0, pos table 0, timestamps t_j = t0 + j: the weight of lag k
+    is SiLU(time_bias[bit_length(k + 1) - 1])."""
+    L = 40
+    w = _tiny([L], d=4, H=1, n_max=L)
+    p = w.layers[0]
+    p.pos_bias[:] = 0.0
+    w.timestamps = 1_600_000_000 + np.arange(L, dtype=np.int64)
+    z = np.zeros((L, 4))
+    v = np.random.default_rng(4).standard_normal((L, 4))
+    got = _attn(w, z, z, v)
+    kern = np.array([p.time_bias[(lag + 1).bit_length() - 1] for lag in range(L)], np.float64)
+    kern = oracle.silu(kern)
+    for f in range(4):
+        np.testing.assert_allclose(got[:, f], np.convolve(v[:, f], kern)[:L], rtol=1e-12,
+                                   atol=1e-14)
+
+
+def test_attention_genrank_linear_tables():
+    """Tables filled linearly reproduce the parameter-free position/time bias
+    -m_p (p_i - p_j) - m_t bucket(t_i - t_j) (GenRank eq. 6.2.6)."""
+    L, mp, mt = 10, 0.0625, 0.25
+    w = _tiny([L], d=4, H=1, n_max=L)
+    p = w.layers[0]
+    p.pos_bias[:] = -mp * (np.arange(2 * L - 1) - (L - 1))
+    p.time_bias[:] = -mt * np.arange(32)
+    w.timestamps = 1_600_000_000 + np.array([0, 1, 3, 7, 100, 101, 5000, 5001, 90000, 90003])
+    z = np.zeros((L, 4))
+    v = np.random.default_rng(5).standard_normal((L, 4))
+    got = _attn(w, z, z, v)
+    want = np.zeros((L, 4))
+    for i in range(L):
+        for j in range(i + 1):
+            dt = int(w.timestamps[i] - w.timestamps[j])
+            bias = -mp * (i - j) - mt * ((dt + 1).bit_length() - 1)
+            want[i] += bias / (1 + math.exp(-bias)) * v[j]
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+
+
+def test_attention_single_token():
+    w = _tiny([1], d=8, H=2, n_max=4)
+    p = w.layers[0]
+    u, v, q, k = _qkv(w)
+    got = _attn(w, q, k, v)
+    for h in range(2):
+        c = slice(4 * h, 4 * h + 4)
+        s = float(q[0, c] @ k[0, c]) + float(p.pos_bias[3]) + float(p.time_bias[0])
+        np.testing.assert_allclose(got[0, c], s / (1 + math.exp(-s)) * v[0, c], rtol=1e-13)
+
+
+def test_attention_causality():
+    w = _tiny([14, 9], d=8, H=2)
+    u, v, q, k = _qkv(w)
+    base = _attn(w, q, k, v)
+    rng = np.random.default_rng(6)
+    for kk in (0, 5, 13):
+        q2, k2, v2 = q.copy(), k.copy(), v.copy()
+        for a in (q2, k2, v2):
+            a[kk] += rng.standard_normal(8)
+        out = _attn(w, q2, k2, v2)
+        np.testing.assert_array_equal(out[:kk], base[:kk])
+        np.testing.assert_array_equal(out[14:], base[14:])  # other sequence untouched
+        assert not np.allclose(out[kk], base[kk])
+
+
+def test_layer_causality():
+    w = _tiny([12, 6], d=8, H=2)
+    p = w.layers[0]
+    base = oracle.layer(w.x, p, w.offsets, w.timestamps, 2, w.n_max)["y"]
+    x2 = w.x.copy()
+    x2[7] += 1.0
+    ts2 = w.timestamps.copy()
+    ts2[9] += 1234  # later timestamp only affects rows >= 9
+    out = oracle.layer(x2, p, w.offsets, ts2, 2, w.n_max)["y"]
+    np.testing.assert_array_equal(out[:7], base[:7])
+    np.testing.assert_array_equal(out[12:], base[12:])
+
+
+def test_jagged_equals_per_sequence_and_padded():
+    lengths = [5, 1, 8, 3]
+    w = _tiny(lengths, d=8, H=2, n_max=12)
+    p = w.layers[0]
+    full = oracle.layer(w.x, p, w.offsets, w.timestamps, 2, w.n_max)["y"]
+    rng = np.random.default_rng(7)
+    for b, L in enumerate(lengths):
+        s, e = w.offsets[b], w.offsets[b + 1]
+        one = oracle.layer(w.x[s:e], p, np.array([0, L]), w.timestamps[s:e], 2, w.n_max)["y"]
+        np.testing.assert_allclose(one, full[s:e], rtol=1e-13, atol=1e-14)
+        # padded to 12 with garbage tokens at the end: the first L rows stay
+        pad = 12 - L
+        xp = np.concatenate([w.x[s:e], rng.standard_normal((pad, 8))])
+        tp = np.concatenate([w.timestamps[s:e],
+                             w.timestamps[e - 1] + 1 + np.arange(pad, dtype=np.int64)])
+        padded = oracle.layer(xp, p, np.array([0, 12]), tp, 2, w.n_max)["y"]
+        np.testing.assert_allclose(padded[:L], full[s:e], rtol=1e-13, atol=1e-14)
+
+
+def test_attention_structure_linearity_heads_permutation():
+    w = _tiny([6, 4, 5], d=8, H=2)
+    u, v, q, k = _qkv(w)
+    base = _attn(w, q, k, v)
+    rng = np.random.default_rng(8)
+    v2 = rng.standard_normal(v.shape)
+    np.testing.assert_allclose(_attn(w, q, k, 2.0 * v - 3.0 * v2),
+                               2.0 * base - 3.0 * _attn(w, q, k, v2), rtol=1e-11, atol=1e-12)
+    # head independence: change head 1's inputs, head 0 is untouched
+    q3, k3 = q.copy(), k.copy()
+    q3[:, 4:] += 1.0
+    k3[:, 4:] -= 0.5
+    out = _attn(w, q3, k3, v)
+    np.testing.assert_array_equal(out[:, :4], base[:, :4])
+    assert not np.allclose(out[:, 4:], base[:, 4:])
+    # permuting sequences permutes outputs
+    order = [2, 0, 1]
+    segs = [np.arange(w.offsets[b], w.offsets[b + 1]) for b in order]
+    perm = np.concatenate(segs)
+    offs = gen.make_jagged([len(s) for s in segs])
+    p = w.layers[0]
+    out = oracle.attention(q[perm], k[perm], v[perm], offs, w.timestamps[perm], p.pos_bias,
+                           p.time_bias, 2, w.n_max)
+    np.testing.assert_allclose(out, base[perm], rtol=1e-14, atol=1e-15)
+
+
+def test_attention_rows_subset_matches_full():
+    w = _tiny([7, 11, 2], d=8, H=2)
+    u, v, q, k = _qkv(w)
+    base = _attn(w, q, k, v)
+    rows = np.array([0, 3, 8, 17, 19])
+    np.testing.assert_allclose(_attn(w, q, k, v, rows=rows), base[rows], rtol=1e-14)
+    full = oracle.layer(w.x, w.layers[0], w.offsets, w.timestamps, 2, w.n_max)
+    part = oracle.layer(w.x, w.layers[0], w.offsets, w.timestamps, 2, w.n_max, rows=rows)
+    np.testing.assert_allclose(part["y"], full["y"][rows], rtol=1e-13, atol=1e-14)
+
+
+def test_pos_table_range_error():
+    w = _tiny([6], d=4, H=1, n_max=3)
+    u, v, q, k = _qkv(w)
+    with pytest.raises(ValueError):
+        _attn(w, q, k, v)
+
+
+def test_golden_intensity_example():
+    """Worked example of the pointwise-aggregation section: softmax gives
+    users A and B the same split; SiLU aggregation keeps B's 10x
+    intensity."""
+    g = json.load(open(os.path.join(HERE, "golden", "intensity_example.json")))
+    c = 0.75
+    outs = {}
+    for name, cnt in g["users"].items():
+        L = cnt["tech"] + cnt["ent"] + 1
+        w = _tiny([L], d=2, H=1, n_max=L)
+        p = w.layers[0]
+        p.pos_bias[:] = c
+        p.time_bias[:] = 0.0
+        v = np.zeros((L, 2))
+        v[:cnt["tech"], 0] = 1.0
+        v[cnt["tech"]:L - 1, 1] = 1.0
+        z = np.zeros((L, 2))
+        outs[name] = _attn(w, z, z, v)[L - 1]
+        sc = c / (1 + math.exp(-c))
+        np.testing.assert_allclose(outs[name] / sc, g["pointwise_counts_over_silu_c"][name],
+                                   rtol=1e-13)
+        split = outs[name] / outs[name].sum()
+        np.testing.assert_allclose(split, g["softmax_split"], rtol=1e-12)
+    np.testing.assert_allclose(outs["B"], 10.0 * outs["A"], rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# pointwise transformation
+# ---------------------------------------------------------------------------
+
+def test_norm_gate_against_torch_layer_norm():
+    import torch
+    rng = np.random.default_rng(9)
+    av = rng.standard_normal((7, 16)) * 3 + 5
+    u = rng.standard_normal((7, 16))
+    gm = 1 + 0.1 * rng.standard_normal(16)
+    bt = 0.1 * rng.standard_normal(16)
+    ln = torch.nn.functional.layer_norm(torch.tensor(av), (16,), torch.tensor(gm),
+                                        torch.tensor(bt), eps=1e-5).numpy()
+    np.testing.assert_allclose(oracle.norm_gate(av, u, gm, bt, 1e-5), ln * u, rtol=1e-12,
+                               atol=1e-13)
+
+
+def test_norm_gate_moments_and_scale_invariance():
+    rng = np.random.default_rng(10)
+    av = rng.standard_normal((5, 32)) + 4
+    ones = np.ones((5, 32))
+    g = oracle.norm_gate(av, ones, np.full(32, 2.0), np.full(32, 0.5), 0.0)
+    np.testing.assert_allclose(g.mean(axis=1), 0.5, rtol=1e-12)
+    np.testing.assert_allclose(g.var(axis=1), 4.0, rtol=1e-12)
+    np.testing.assert_allclose(oracle.norm_gate(7.5 * av, ones, None, None, 0.0),
+                               oracle.norm_gate(av, ones, None, None, 0.0), rtol=1e-12)
+
+
+def test_output_closed_forms():
+    w = _tiny([5], d=8, H=2, seed=12)
+    p = w.layers[0]
+    p.w2[:] = 0.0
+    r = oracle.layer(w.x, p, w.offsets, w.timestamps, 2, w.n_max)
+    np.testing.assert_allclose(r["y"], w.x.astype(np.float64) + p.b2.astype(np.float64), rtol=0, atol=1e-15)
+    # V scaled by c leaves Y unchanged when eps = 0 (LayerNorm scale invariance)
+    w = _tiny([6], d=8, H=2, seed=13)
+    p = w.layers[0]
+    y0 = oracle.layer(w.x, p, w.offsets, w.timestamps, 2, w.n_max, eps=0.0)["y"]
+    u, v, q, k = _qkv(w)
+    av = _attn(w, q, k, 3.0 * v)
+    y1 = oracle.output(w.x, oracle.norm_gate(av, u, p.gamma, p.beta, 0.0), p.w2, p.b2)
+    np.testing.assert_allclose(y1, y0, rtol=1e-11, atol=1e-12)
+
+
+def test_output_bruteforce():
+    rng = np.random.default_rng(14)
+    x, g = rng.standard_normal((3, 4)), rng.standard_normal((3, 4))
+    w2, b2 = rng.standard_normal((4, 4)), rng.standard_normal(4)
+    y = oracle.output(x, g, w2, b2)
+    for t in range(3):
+        for o in range(4):
+            want = x[t][o] + b2[o] + sum(g[t][i] * w2[o][i] for i in range(4))
+            assert abs(y[t][o] - want) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# stack, embedding, ranking
+# ---------------------------------------------------------------------------
+
+def test_stack_equals_chained_layers():
+    w = gen.make_custom([5, 9], 8, 2, dtype="f32", seed=15, num_layers=3, affine="random")
+    outs = oracle.stack(w.x, w.layers, w.offsets, w.timestamps, 2, w.n_max, return_all=True)
+    h = w.x
+    for l, p in enumerate(w.layers):
+        h = oracle.layer(h, p, w.offsets, w.timestamps, 2, w.n_max)["y"]
+        np.testing.assert_array_equal(outs[l + 1], h)
+
+
+def test_embed_closed_form():
+    item = np.arange(50, dtype=np.float64)[:, None] * np.ones((1, 4))
+    act = 1000.0 * np.arange(16, dtype=np.float64)[:, None] * np.ones((1, 4))
+    ids = np.array([3, 49, 0, 3])
+    a = np.array([0, 15, 2, 7])
+    x = oracle.embed(item, act, ids, a)
+    np.testing.assert_array_equal(x[:, 0], ids + 1000.0 * a)
+    np.testing.assert_array_equal(x[:, 3], ids + 1000.0 * a)
+
+
+def _small_ranking(seed=21, history=(6, 3, 9), candidates=(5, 7, 2), layers=2):
+    return gen.make_ranking(seed=seed, users=3, history=list(history),
+                            candidates=list(candidates), micro_batch=2, d_model=8,
+                            num_heads=2, num_layers=layers, affine="random", dtype="f32")
+
+
+def test_ranking_equals_independent_forwards():
+    w = _small_ranking()
+    r = oracle.ranking(w)
+    for u in range(3):
+        for c in range(int(w.cand_offsets[u + 1] - w.cand_offsets[u])):
+            want = oracle.ranking_independent(w, u, c)
+            np.testing.assert_allclose(r["cand_y"][w.cand_offsets[u] + c], want, rtol=1e-11,
+                                       atol=1e-12)
+
+
+@pytest.mark.parametrize("b_m", [1, 3, 7, 512])
+def test_ranking_microbatch_invariance(b_m):
+    w = _small_ranking()
+    full = oracle.ranking(w, b_m=512)["cand_y"]
+    np.testing.assert_allclose(oracle.ranking(w, b_m=b_m)["cand_y"], full, rtol=1e-12,
+                               atol=1e-13)
+
+
+def test_history_pass_is_plain_stack():
+    w = _small_ranking()
+    r = oracle.ranking(w)
+    outs = oracle.stack(w.x, w.layers, w.offsets, w.timestamps, w.num_heads, w.n_max,
+                        return_all=True)
+    for a, b in zip(r["hist_y"], outs):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_generator_recipe():
+    for k in (0, 1, 2):
+        w = gen.make_config(k)
+        L = w.lengths
+        for b in range(w.num_seqs):
+            t = w.timestamps[w.offsets[b]:w.offsets[b + 1]]
+            assert t[0] == gen.T0_SECONDS and np.all(np.diff(t) >= 1)
+        if k == 1:
+            assert L.min() >= 16 and L.max() <= 512 and w.num_seqs == 64
+        if k == 2:
+            assert L[0] == 8192 and L.min() >= 2048 and w.num_seqs == 16
+        assert w.layers[0].pos_bias.shape[0] == 2 * w.n_max - 1
+        if w.dtype == "bf16":
+            np.testing.assert_array_equal(gen.bf16_round(w.x), w.x)
+            np.testing.assert_array_equal(gen.bf16_round(w.layers[0].w1), w.layers[0].w1)
