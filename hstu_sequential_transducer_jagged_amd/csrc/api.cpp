@@ -1,0 +1,361 @@
+// C ABI of the HSTU jagged layer forward: argument validation, workspace
+// carving, dispatch to the gfx950 kernels and the layer composition
+// (projection -> attention -> norm/gate -> f2 + residual). Every check runs
+// on host scalars before anything is enqueued; no entry point allocates.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/hstu.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return HSTU_OK;
+}
+
+int device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(HSTU_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_size(int dtype) { return dtype == HSTU_BF16 ? 2 : 4; }
+
+#define CHECK(cond, code, ...)          \
+  do {                                  \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+int check_desc(const hstu_layer_desc* d) {
+  CHECK(d != nullptr, HSTU_E_INVAL, "desc is NULL");
+  CHECK(d->dtype == HSTU_F32 || d->dtype == HSTU_BF16, HSTU_E_INVAL, "unknown dtype %d", d->dtype);
+  CHECK(d->num_heads > 0 && d->head_dim > 0, HSTU_E_INVAL, "num_heads and head_dim must be positive");
+  CHECK(d->d_model == d->num_heads * d->head_dim, HSTU_E_INVAL,
+        "d_model (%d) != num_heads (%d) * head_dim (%d)", d->d_model, d->num_heads, d->head_dim);
+  if (d->dtype == HSTU_BF16) {
+    CHECK(d->head_dim == 64, HSTU_E_UNSUPPORTED, "bf16 supports head_dim 64 (got %d)", d->head_dim);
+    CHECK(d->d_model <= 1024, HSTU_E_UNSUPPORTED, "d_model %d > 1024", d->d_model);
+  } else {
+    CHECK(d->head_dim == 32 || d->head_dim == 64, HSTU_E_UNSUPPORTED,
+          "f32 supports head_dim 32 or 64 (got %d)", d->head_dim);
+    CHECK(d->d_model <= 1024, HSTU_E_UNSUPPORTED, "d_model %d > 1024", d->d_model);
+  }
+  CHECK(std::isfinite(d->alpha) && std::fabs(d->alpha) >= 1e-6f && std::fabs(d->alpha) <= 1e6f,
+        HSTU_E_INVAL, "alpha must satisfy 1e-6 <= |alpha| <= 1e6 (got %g)", d->alpha);
+  CHECK(std::isfinite(d->ln_eps) && d->ln_eps >= 0.0f, HSTU_E_INVAL, "ln_eps must be finite and >= 0");
+  CHECK(d->pos_table_len >= 1 && (d->pos_table_len & 1) == 1, HSTU_E_INVAL,
+        "pos_table_len must be odd and positive (2*n_max-1), got %d", d->pos_table_len);
+  CHECK(d->num_time_buckets >= 1 && d->num_time_buckets <= 64, HSTU_E_INVAL,
+        "num_time_buckets must be in [1, 64] (got %d)", d->num_time_buckets);
+  return HSTU_OK;
+}
+
+int check_jagged(const hstu_layer_desc* d, const hstu_jagged* j, const hstu_kv_cache* c) {
+  CHECK(j != nullptr, HSTU_E_INVAL, "jagged is NULL");
+  CHECK(j->num_seqs >= 0 && j->total_tokens >= 0 && j->max_seq_len >= 0, HSTU_E_INVAL,
+        "negative jagged sizes");
+  if (j->num_seqs > 0) CHECK(j->offsets != nullptr, HSTU_E_INVAL, "jagged offsets is NULL");
+  if (j->total_tokens > 0) CHECK(j->timestamps != nullptr, HSTU_E_INVAL, "jagged timestamps is NULL");
+  int64_t cache_max = 0;
+  if (c) {
+    CHECK(c->offsets != nullptr || j->num_seqs == 0, HSTU_E_INVAL, "cache offsets is NULL");
+    CHECK(c->max_len >= 0 && c->total_tokens >= 0, HSTU_E_INVAL, "negative cache sizes");
+    if (c->total_tokens > 0) {
+      CHECK(c->k && c->v && c->timestamps, HSTU_E_INVAL, "cache k/v/timestamps is NULL");
+      CHECK(aligned16(c->k) && aligned16(c->v), HSTU_E_INVAL, "cache k/v must be 16-byte aligned");
+    }
+    cache_max = c->max_len;
+  }
+  // Without targets the largest position difference is cache_len + L - 1,
+  // bounded by the host scalars. With targets it depends on device data
+  // (targets share one position); the kernels clamp table indices, and
+  // hstu_check_inputs() checks the exact bound.
+  const int64_t n_max = (static_cast<int64_t>(d->pos_table_len) + 1) / 2;
+  if (j->num_targets == nullptr)
+    CHECK(static_cast<int64_t>(j->max_seq_len) + cache_max <= n_max, HSTU_E_INVAL,
+          "position table too small: max_seq_len (%d) + cache max_len (%lld) > n_max (%lld)",
+          j->max_seq_len, static_cast<long long>(cache_max), static_cast<long long>(n_max));
+  return HSTU_OK;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+hstu::AttnArgs make_attn_args(const hstu_layer_desc* d, const hstu_jagged* j,
+                              const hstu_kv_cache* c, const void* q, const void* k,
+                              const void* v, const float* pb, const float* tb, float* av) {
+  hstu::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.ck = c ? c->k : nullptr;
+  a.cv = c ? c->v : nullptr;
+  a.offsets = j->offsets;
+  a.ts = j->timestamps;
+  a.num_targets = j->num_targets;
+  a.c_offsets = c ? c->offsets : nullptr;
+  a.c_ts = c ? c->timestamps : nullptr;
+  a.pos_bias = pb;
+  a.time_bias = tb;
+  a.av = av;
+  a.d_model = d->d_model;
+  a.num_heads = d->num_heads;
+  a.head_dim = d->head_dim;
+  a.pos_len = d->pos_table_len;
+  a.pos_center = (d->pos_table_len - 1) / 2;
+  a.nb = d->num_time_buckets;
+  a.alpha = d->alpha;
+  a.num_seqs = j->num_seqs;
+  a.max_seq_len = j->max_seq_len;
+  a.max_cache_len = c ? c->max_len : 0;
+  return a;
+}
+
+int do_proj(const hstu_layer_desc* d, const hstu_layer_params* p, int64_t T, const void* x,
+            void* u, void* v, void* q, void* k, hipStream_t s) {
+  hstu::ProjArgs a{};
+  a.x = x;
+  a.w = p->w1;
+  a.bias = p->b1;
+  a.out[0] = u;
+  a.out[1] = v;
+  a.out[2] = q;
+  a.out[3] = k;
+  a.M = T;
+  a.K = d->d_model;
+  return device_status(d->dtype == HSTU_BF16 ? hstu::launch_proj_bf16(a, s) : hstu::launch_proj_f32(a, s),
+                       "proj launch");
+}
+
+int do_attn(const hstu_layer_desc* d, const hstu_jagged* j, const hstu_kv_cache* c, const void* q,
+            const void* k, const void* v, const float* pb, const float* tb, float* av, hipStream_t s) {
+  const hstu::AttnArgs a = make_attn_args(d, j, c, q, k, v, pb, tb, av);
+  return device_status(d->dtype == HSTU_BF16 ? hstu::launch_attn_bf16(a, s) : hstu::launch_attn_f32(a, s),
+                       "attention launch");
+}
+
+int do_norm_gate(const hstu_layer_desc* d, int64_t T, const float* av, const void* u,
+                 const float* gamma, const float* beta, void* g, hipStream_t s) {
+  hstu::NormGateArgs a{av, u, gamma, beta, g, T, d->d_model, d->ln_eps};
+  return device_status(d->dtype == HSTU_BF16 ? hstu::launch_norm_gate_bf16(a, s)
+                                             : hstu::launch_norm_gate_f32(a, s),
+                       "norm_gate launch");
+}
+
+int do_out(const hstu_layer_desc* d, int64_t T, const void* g, const void* x, const void* w2,
+           const float* b2, void* y, hipStream_t s) {
+  hstu::OutArgs a{g, w2, b2, x, y, T, d->d_model};
+  return device_status(d->dtype == HSTU_BF16 ? hstu::launch_out_bf16(a, s) : hstu::launch_out_f32(a, s),
+                       "out launch");
+}
+
+size_t round256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+
+extern "C" {
+
+int hstu_abi_version(void) { return HSTU_ABI_VERSION; }
+
+const char* hstu_last_error(void) { return g_last_error.c_str(); }
+
+int hstu_proj_fwd(const hstu_layer_desc* desc, const hstu_layer_params* params, int64_t T,
+                  const void* x, void* u, void* v, void* q, void* k, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  CHECK(params != nullptr && params->w1 != nullptr, HSTU_E_INVAL, "params or w1 is NULL");
+  CHECK(T >= 0, HSTU_E_INVAL, "T must be >= 0");
+  if (T == 0) return ok();
+  CHECK(x && u && v && q && k, HSTU_E_INVAL, "x/u/v/q/k must not be NULL");
+  CHECK(aligned16(x) && aligned16(u) && aligned16(v) && aligned16(q) && aligned16(k) &&
+            aligned16(params->w1),
+        HSTU_E_INVAL, "activations and w1 must be 16-byte aligned");
+  return do_proj(desc, params, T, x, u, v, q, k, as_stream(stream));
+}
+
+int hstu_attn_fwd(const hstu_layer_desc* desc, const hstu_jagged* jagged,
+                  const hstu_kv_cache* cache, const void* q, const void* k, const void* v,
+                  const float* pos_bias, const float* time_bias, float* av, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  st = check_jagged(desc, jagged, cache);
+  if (st) return st;
+  if (jagged->num_seqs == 0 || jagged->total_tokens == 0) return ok();
+  CHECK(q && k && v && av, HSTU_E_INVAL, "q/k/v/av must not be NULL");
+  CHECK(pos_bias && time_bias, HSTU_E_INVAL, "pos_bias/time_bias must not be NULL");
+  CHECK(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(av), HSTU_E_INVAL,
+        "q/k/v/av must be 16-byte aligned");
+  return do_attn(desc, jagged, cache, q, k, v, pos_bias, time_bias, av, as_stream(stream));
+}
+
+int hstu_norm_gate_fwd(const hstu_layer_desc* desc, int64_t T, const float* av, const void* u,
+                       const float* gamma, const float* beta, void* g, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  CHECK(T >= 0, HSTU_E_INVAL, "T must be >= 0");
+  if (T == 0) return ok();
+  CHECK(av && u && g, HSTU_E_INVAL, "av/u/g must not be NULL");
+  CHECK(aligned16(av) && aligned16(u) && aligned16(g), HSTU_E_INVAL, "av/u/g must be 16-byte aligned");
+  CHECK(!gamma || aligned16(gamma), HSTU_E_INVAL, "gamma must be 16-byte aligned");
+  CHECK(!beta || aligned16(beta), HSTU_E_INVAL, "beta must be 16-byte aligned");
+  return do_norm_gate(desc, T, av, u, gamma, beta, g, as_stream(stream));
+}
+
+int hstu_out_fwd(const hstu_layer_desc* desc, int64_t T, const void* g, const void* x,
+                 const void* w2, const float* b2, void* y, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  CHECK(T >= 0, HSTU_E_INVAL, "T must be >= 0");
+  if (T == 0) return ok();
+  CHECK(g && x && w2 && y, HSTU_E_INVAL, "g/x/w2/y must not be NULL");
+  CHECK(aligned16(g) && aligned16(x) && aligned16(w2) && aligned16(y), HSTU_E_INVAL,
+        "g/x/w2/y must be 16-byte aligned");
+  CHECK(y != x && y != g, HSTU_E_INVAL, "y must not alias x or g");
+  return do_out(desc, T, g, x, w2, b2, y, as_stream(stream));
+}
+
+size_t hstu_layer_workspace_size(const hstu_layer_desc* desc, int64_t T, int32_t num_seqs) {
+  (void)num_seqs;
+  if (!desc || T < 0 || desc->d_model <= 0) return 0;
+  const size_t act = round256(static_cast<size_t>(T) * desc->d_model * elem_size(desc->dtype));
+  const size_t av = round256(static_cast<size_t>(T) * desc->d_model * sizeof(float));
+  return 4 * act + av;  // U, V, Q, K (G overwrites U in place), AV
+}
+
+int hstu_layer_fwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
+                   const hstu_jagged* jagged, const hstu_kv_cache* cache, const void* x, void* y,
+                   void* k_out, void* v_out, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  st = check_jagged(desc, jagged, cache);
+  if (st) return st;
+  CHECK(params && params->w1 && params->w2 && params->pos_bias && params->time_bias, HSTU_E_INVAL,
+        "params, w1, w2, pos_bias and time_bias must not be NULL");
+  const int64_t T = jagged->total_tokens;
+  if (T == 0 || jagged->num_seqs == 0) return ok();
+  CHECK(x && y, HSTU_E_INVAL, "x/y must not be NULL");
+  CHECK(x != y, HSTU_E_INVAL, "y must not alias x");
+  CHECK(aligned16(x) && aligned16(y) && aligned16(params->w1) && aligned16(params->w2),
+        HSTU_E_INVAL, "x/y/w1/w2 must be 16-byte aligned");
+  CHECK((!k_out || aligned16(k_out)) && (!v_out || aligned16(v_out)), HSTU_E_INVAL,
+        "k_out/v_out must be 16-byte aligned");
+  CHECK(!params->ln_gamma || aligned16(params->ln_gamma), HSTU_E_INVAL, "ln_gamma must be 16-byte aligned");
+  CHECK(!params->ln_beta || aligned16(params->ln_beta), HSTU_E_INVAL, "ln_beta must be 16-byte aligned");
+  const size_t need = hstu_layer_workspace_size(desc, T, jagged->num_seqs);
+  CHECK(workspace != nullptr && workspace_bytes >= need, HSTU_E_WORKSPACE,
+        "workspace too small: need %zu bytes, got %zu", need, workspace_bytes);
+  CHECK((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, HSTU_E_INVAL,
+        "workspace must be 256-byte aligned");
+  const size_t act = round256(static_cast<size_t>(T) * desc->d_model * elem_size(desc->dtype));
+  char* ws = static_cast<char*>(workspace);
+  void* u = ws;
+  void* v = ws + act;
+  void* q = ws + 2 * act;
+  void* k = ws + 3 * act;
+  float* av = reinterpret_cast<float*>(ws + 4 * act);
+  if (k_out) k = k_out;
+  if (v_out) v = v_out;
+  hipStream_t s = as_stream(stream);
+  st = do_proj(desc, params, T, x, u, v, q, k, s);
+  if (st) return st;
+  st = do_attn(desc, jagged, cache, q, k, v, params->pos_bias, params->time_bias, av, s);
+  if (st) return st;
+  st = do_norm_gate(desc, T, av, u, params->ln_gamma, params->ln_beta, u, s);
+  if (st) return st;
+  return do_out(desc, T, u, x, params->w2, params->b2, y, s);
+}
+
+int hstu_embed_fwd(int64_t T, int32_t d_model, int32_t dtype, const void* item_emb,
+                   int64_t num_items, const void* action_emb, int32_t num_actions,
+                   const int64_t* item_ids, const int32_t* actions, void* x, void* stream) {
+  CHECK(dtype == HSTU_F32 || dtype == HSTU_BF16, HSTU_E_INVAL, "unknown dtype %d", dtype);
+  CHECK(T >= 0 && d_model > 0 && num_items >= 0 && num_actions >= 0, HSTU_E_INVAL, "bad sizes");
+  CHECK(d_model % 8 == 0, HSTU_E_UNSUPPORTED, "d_model must be a multiple of 8");
+  if (T == 0) return ok();
+  CHECK(item_emb && action_emb && item_ids && actions && x, HSTU_E_INVAL, "NULL pointer");
+  CHECK(aligned16(item_emb) && aligned16(action_emb) && aligned16(x), HSTU_E_INVAL,
+        "tables and x must be 16-byte aligned");
+  hstu::EmbedArgs a{item_emb, action_emb, item_ids, actions, x, T, num_items, num_actions, d_model};
+  return device_status(dtype == HSTU_BF16 ? hstu::launch_embed_bf16(a, as_stream(stream))
+                                          : hstu::launch_embed_f32(a, as_stream(stream)),
+                       "embed launch");
+}
+
+int hstu_check_inputs(const hstu_layer_desc* desc, const hstu_jagged* jagged,
+                      const hstu_kv_cache* cache, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  st = check_jagged(desc, jagged, cache);
+  if (st) return st;
+  const int B = jagged->num_seqs;
+  hipStream_t s = as_stream(stream);
+  std::vector<int64_t> off(B + 1, 0), coff;
+  std::vector<int32_t> tgt;
+  hipError_t e = hipSuccess;
+  if (B > 0) e = hipMemcpyAsync(off.data(), jagged->offsets, sizeof(int64_t) * (B + 1),
+                                hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess && B > 0 && jagged->num_targets) {
+    tgt.resize(B);
+    e = hipMemcpyAsync(tgt.data(), jagged->num_targets, sizeof(int32_t) * B, hipMemcpyDeviceToHost, s);
+  }
+  if (e == hipSuccess && B > 0 && cache) {
+    coff.resize(B + 1);
+    e = hipMemcpyAsync(coff.data(), cache->offsets, sizeof(int64_t) * (B + 1), hipMemcpyDeviceToHost, s);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return device_status(e, "check_inputs copy");
+  CHECK(B == 0 || off[0] == 0, HSTU_E_DATA, "offsets[0] = %lld, expected 0", static_cast<long long>(off[0]));
+  for (int b = 0; b < B; ++b) {
+    const int64_t L = off[b + 1] - off[b];
+    CHECK(L >= 0, HSTU_E_DATA, "offsets decrease at sequence %d", b);
+    CHECK(L <= jagged->max_seq_len, HSTU_E_DATA, "sequence %d has length %lld > max_seq_len %d", b,
+          static_cast<long long>(L), jagged->max_seq_len);
+    if (!tgt.empty())
+      CHECK(tgt[b] >= 0 && tgt[b] <= L, HSTU_E_DATA, "num_targets[%d] = %d outside [0, %lld]", b, tgt[b],
+            static_cast<long long>(L));
+    int64_t C = 0;
+    if (cache) {
+      C = coff[b + 1] - coff[b];
+      CHECK(C >= 0 && C <= cache->max_len, HSTU_E_DATA, "cache length of sequence %d is %lld (max_len %d)",
+            b, static_cast<long long>(C), cache->max_len);
+    }
+    // largest visible position difference: the last query against cache row 0
+    // (or own token 0); targets sit at C + (L - m)
+    const int64_t m = tgt.empty() ? 0 : tgt[b];
+    const int64_t max_dp = L == 0 ? 0 : (m > 0 ? C + (L - m) : C + L - 1);
+    const int64_t n_max = (static_cast<int64_t>(desc->pos_table_len) + 1) / 2;
+    CHECK(max_dp <= n_max - 1, HSTU_E_DATA,
+          "sequence %d needs position differences up to %lld but the table covers %lld", b,
+          static_cast<long long>(max_dp), static_cast<long long>(n_max - 1));
+  }
+  CHECK(B == 0 || off[B] == jagged->total_tokens, HSTU_E_DATA, "offsets[B] = %lld != total_tokens %lld",
+        static_cast<long long>(B ? off[B] : 0), static_cast<long long>(jagged->total_tokens));
+  if (cache && B > 0) {
+    CHECK(coff[0] == 0 && coff[B] == cache->total_tokens, HSTU_E_DATA,
+          "cache offsets must start at 0 and end at cache total_tokens");
+  }
+  return ok();
+}
+
+}  // extern "C"

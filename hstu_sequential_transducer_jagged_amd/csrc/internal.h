@@ -1,0 +1,93 @@
+// Internal declarations shared by the host ABI (api.cpp) and the HIP kernel
+// translation units. Launchers enqueue on the given stream and return the
+// hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hstu {
+
+// Arguments of the jagged attention kernels (all pointers device memory).
+struct AttnArgs {
+  const void* q;             // [T, d] own queries
+  const void* k;             // [T, d] own keys
+  const void* v;             // [T, d] own values
+  const void* ck;            // [Tc, d] cached keys or null
+  const void* cv;            // [Tc, d] cached values or null
+  const int64_t* offsets;    // [B+1]
+  const int64_t* ts;         // [T]
+  const int32_t* num_targets;// [B] or null
+  const int64_t* c_offsets;  // [B+1] or null
+  const int64_t* c_ts;       // [Tc] or null
+  const float* pos_bias;     // [pos_len]
+  const float* time_bias;    // [nb]
+  float* av;                 // [T, d] fp32 out
+  int d_model;
+  int num_heads;
+  int head_dim;
+  int pos_len;
+  int pos_center;            // n_max - 1
+  int nb;
+  float alpha;
+  int num_seqs;
+  int max_seq_len;
+  int max_cache_len;
+};
+
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
+
+// C[M, N] = A[M, K] B[N, K]^T (+ epilogue). Both operands row-major with K
+// contiguous (nn.Linear weight layout for B).
+struct ProjArgs {
+  const void* x;   // [M, K]
+  const void* w;   // [N, K] (N = 4K)
+  const float* bias;  // [N] or null
+  void* out[4];    // U, V, Q, K  [M, K] each
+  int64_t M;
+  int K;           // d_model
+};
+struct OutArgs {
+  const void* g;   // [M, K]
+  const void* w;   // [K, K]
+  const float* bias;  // [K] or null
+  const void* x;   // [M, K] residual
+  void* y;         // [M, K]
+  int64_t M;
+  int K;
+};
+
+hipError_t launch_proj_bf16(const ProjArgs& a, hipStream_t s);
+hipError_t launch_proj_f32(const ProjArgs& a, hipStream_t s);
+hipError_t launch_out_bf16(const OutArgs& a, hipStream_t s);
+hipError_t launch_out_f32(const OutArgs& a, hipStream_t s);
+
+struct NormGateArgs {
+  const float* av;   // [M, d]
+  const void* u;     // [M, d]
+  const float* gamma;
+  const float* beta;
+  void* g;           // [M, d]
+  int64_t M;
+  int d;
+  float eps;
+};
+hipError_t launch_norm_gate_bf16(const NormGateArgs& a, hipStream_t s);
+hipError_t launch_norm_gate_f32(const NormGateArgs& a, hipStream_t s);
+
+struct EmbedArgs {
+  const void* item;
+  const void* action;
+  const int64_t* ids;
+  const int32_t* acts;
+  void* x;
+  int64_t T;
+  int64_t num_items;
+  int num_actions;
+  int d;
+};
+hipError_t launch_embed_bf16(const EmbedArgs& a, hipStream_t s);
+hipError_t launch_embed_f32(const EmbedArgs& a, hipStream_t s);
+
+}  // namespace hstu

@@ -1,0 +1,196 @@
+/*
+ * hstu.h — C ABI of the MI355X (gfx950) HSTU jagged layer forward.
+ *
+ * One HSTU layer on jagged (offset-packed, variable-length) sequences:
+ *
+ *   U, V, Q, K = Split(SiLU(X W1^T + b1))                       (projection)
+ *   AV_h       = (SiLU(alpha Q_h K_h^T + rab_{p,t}) * Mask) V_h  (per head)
+ *   Y          = X + (LayerNorm(AV) * gamma + beta) (.) U  W2^T + b2
+ *
+ * The three equations are the ones of "万亿参数推荐大模型：HSTU 架构如何超越
+ * 传统 Self-Attention" §2.1 (and of "从自注意力到 HSTU：解构下一代推荐系统引擎"
+ * part 2, steps 1-3); the residual is that page's block-diagram skip
+ * connection. There is no softmax and no normalisation of the SiLU weights
+ * ("HSTU：Scaling Law 的首次探索" §7.1.4, innovation 1).
+ *
+ * rab_{p,t}(i, j) = pos_bias[(p_i - p_j) + n_max - 1]
+ *                 + time_bias[min(nb - 1, floor(log2(|t_i - t_j| + 1)))]
+ * is shared by all heads; position and real-time differences follow
+ * §7.1.4 innovation 2 of the chapter-7.1 page, the bucketed time difference
+ * eq. 6.2.6 of "6.2. HSTU的工程突破". The floor(log2) is exact (integer).
+ *
+ * Visibility. Within sequence b the keys are [the cache rows of b, then the
+ * call's own tokens of b]. Key j is visible to query i iff j is a cache row,
+ * or j <= i and (j is not a target or j == i) (own-token indices; the last
+ * num_targets[b] own tokens are targets). Plain causal attention is the case
+ * without cache and targets. Targets and the cache implement candidate
+ * scoring with micro-batches over a cached history (M-FALCON, §7.1.5 of the
+ * chapter-7.1 page; the candidate mask of Fig. 6.2.2 of the GenRank page).
+ *
+ * Positions. Cache rows of b: 0 .. n_b-1 (n_b = its cache length). Own
+ * non-targets: n_b + j. All targets of b share n_b + (L_b - m_b).
+ *
+ * Conventions for every entry point:
+ *  - returns an hstu_status; on error nothing has been enqueued (argument
+ *    errors) or the outputs are undefined (HSTU_E_DEVICE); a message is
+ *    available from hstu_last_error() on the calling thread;
+ *  - asynchronous: work is enqueued on `stream` (a hipStream_t; NULL is the
+ *    default stream) and the call returns without waiting;
+ *  - never allocates device memory; the caller owns every buffer;
+ *  - "device" pointers are HIP device memory; all arrays are dense and
+ *    row-major; activations [T, d_model] must be 16-byte aligned;
+ *  - outputs must not alias inputs;
+ *  - device-resident index data (offsets, num_targets, timestamps) are not
+ *    validated by the fast path; hstu_check_inputs() validates them.
+ *
+ * dtype HSTU_BF16: X, W1, W2, U/V/Q/K, G, Y, cache K/V are bf16 (raw 16-bit
+ * patterns), arithmetic accumulates in fp32. HSTU_F32: all of those fp32.
+ * Bias tables, linear biases, LayerNorm parameters and AV are always fp32.
+ */
+#ifndef HSTU_H_
+#define HSTU_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HSTU_ABI_VERSION 1
+
+typedef enum {
+  HSTU_OK = 0,
+  HSTU_E_INVAL = -1,        /* bad argument (null pointer, size, alignment, range) */
+  HSTU_E_UNSUPPORTED = -2,  /* valid but not implemented (e.g. head_dim) */
+  HSTU_E_WORKSPACE = -3,    /* workspace too small */
+  HSTU_E_DEVICE = -4,       /* HIP runtime error (launch, device query, copy) */
+  HSTU_E_DATA = -5          /* hstu_check_inputs found inconsistent device data */
+} hstu_status;
+
+typedef enum { HSTU_F32 = 0, HSTU_BF16 = 1 } hstu_dtype;
+
+/* Host-side layer description, passed by pointer, read during the call only. */
+typedef struct {
+  int32_t d_model;          /* == num_heads * head_dim */
+  int32_t num_heads;
+  int32_t head_dim;         /* bf16: 64; f32: 32 or 64 */
+  int32_t dtype;            /* hstu_dtype */
+  float alpha;              /* score scale, 1e-6 <= |alpha| <= 1e6 (1.0 by default) */
+  float ln_eps;             /* LayerNorm epsilon, >= 0 (1e-5 by default) */
+  int32_t pos_table_len;    /* 2*n_max - 1 (odd); index = (p_i - p_j) + n_max - 1 */
+  int32_t num_time_buckets; /* 1..64 (32 by default) */
+} hstu_layer_desc;
+
+/* A jagged batch of the call's own tokens. */
+typedef struct {
+  int32_t num_seqs;             /* B >= 0 (host) */
+  int32_t max_seq_len;          /* >= every L_b (host); sizes the launch grid */
+  int64_t total_tokens;         /* T = offsets[B] (host) */
+  const int64_t *offsets;       /* device [B+1]: offsets[0] = 0, nondecreasing, offsets[B] = T */
+  const int64_t *timestamps;    /* device [T], int64 seconds (any order) */
+  const int32_t *num_targets;   /* device [B] or NULL: the last m_b tokens of b are targets,
+                                   0 <= m_b <= L_b */
+} hstu_jagged;
+
+/* Optional cached history (keys/values visible to every own token of the
+ * same sequence). Pass NULL when there is none. */
+typedef struct {
+  const int64_t *offsets;       /* device [B+1] rows of k/v per sequence (same B as the batch) */
+  const int64_t *timestamps;    /* device [cache_T] */
+  const void *k;                /* device [cache_T, d_model], dtype */
+  const void *v;                /* device [cache_T, d_model], dtype */
+  int32_t max_len;              /* >= every cache length (host) */
+  int64_t total_tokens;         /* cache_T (host) */
+} hstu_kv_cache;
+
+/* Layer parameters: device pointers, caller-owned. */
+typedef struct {
+  const void *w1;               /* [4d, d] dtype, nn.Linear layout (out x in) */
+  const float *b1;              /* [4d] or NULL (zeros) */
+  const void *w2;               /* [d, d] dtype */
+  const float *b2;              /* [d] or NULL (zeros) */
+  const float *ln_gamma;        /* [d] or NULL (ones) */
+  const float *ln_beta;         /* [d] or NULL (zeros) */
+  const float *pos_bias;        /* [pos_table_len] */
+  const float *time_bias;       /* [num_time_buckets] */
+} hstu_layer_params;
+
+/* ABI version of the loaded library (HSTU_ABI_VERSION). */
+int hstu_abi_version(void);
+
+/* Message describing the last error on this thread ("" if none). Valid until
+ * the next call on the same thread. */
+const char *hstu_last_error(void);
+
+/* Pointwise projection, "万亿参数推荐大模型…" §2.1 first equation:
+ *   [U | V | Q | K] = SiLU(x W1^T + b1), split into four [T, d] outputs in
+ *   the order U, V, Q, K (head h owns columns [h*dh, (h+1)*dh) of each).
+ * x [T, d], u/v/q/k [T, d] (dtype). T >= 0. */
+int hstu_proj_fwd(const hstu_layer_desc *desc, const hstu_layer_params *params, int64_t T,
+                  const void *x, void *u, void *v, void *q, void *k, void *stream);
+
+/* Spatial aggregation, §2.1 second equation, with the visibility, position
+ * and bias rules above:
+ *   av[i, h*dh:(h+1)*dh] = sum_{j visible} SiLU(alpha q_i.k_j + rab(i, j)) v_j
+ * q, k, v [T, d] (dtype, own tokens of `jagged`); cache may be NULL;
+ * pos_bias [pos_table_len], time_bias [num_time_buckets] (fp32);
+ * av [T, d] fp32 output. Every visible position difference must lie in
+ * the table: per sequence, C_b + L_b - 1 <= n_max - 1 without targets and
+ * C_b + (L_b - m_b) <= n_max - 1 with m_b > 0 targets (C_b = cache length).
+ * Without num_targets the call checks max_seq_len + cache max_len <= n_max
+ * (HSTU_E_INVAL); with targets the bound depends on device data and only
+ * hstu_check_inputs() checks it (the kernels clamp table indices, so a
+ * violation never reads out of bounds). */
+int hstu_attn_fwd(const hstu_layer_desc *desc, const hstu_jagged *jagged,
+                  const hstu_kv_cache *cache, const void *q, const void *k, const void *v,
+                  const float *pos_bias, const float *time_bias, float *av, void *stream);
+
+/* Pointwise transformation, first half (§2.1 third equation and the block
+ * diagram: LayerNorm, then the product with U):
+ *   g = (LayerNorm_d(av) * gamma + beta) (.) u
+ * LayerNorm over all d features with the biased variance and desc->ln_eps.
+ * av [T, d] fp32, u and g [T, d] dtype (g may equal u: in place). */
+int hstu_norm_gate_fwd(const hstu_layer_desc *desc, int64_t T, const float *av, const void *u,
+                       const float *gamma, const float *beta, void *g, void *stream);
+
+/* Pointwise transformation, second half: y = x + g W2^T + b2
+ * (f2 with the residual connection). g, x, y [T, d] dtype. */
+int hstu_out_fwd(const hstu_layer_desc *desc, int64_t T, const void *g, const void *x,
+                 const void *w2, const float *b2, void *y, void *stream);
+
+/* Workspace bytes hstu_layer_fwd needs for T tokens. */
+size_t hstu_layer_workspace_size(const hstu_layer_desc *desc, int64_t T, int32_t num_seqs);
+
+/* One full layer: projection -> attention -> norm/gate -> f2 + residual.
+ * x, y [T, d] dtype (y must not alias x). k_out / v_out: NULL, or [T, d]
+ * dtype buffers that receive this call's K and V (to build a cache for later
+ * calls). workspace: device, >= hstu_layer_workspace_size() bytes, 256-byte
+ * aligned. */
+int hstu_layer_fwd(const hstu_layer_desc *desc, const hstu_layer_params *params,
+                   const hstu_jagged *jagged, const hstu_kv_cache *cache, const void *x,
+                   void *y, void *k_out, void *v_out, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/* Action-oriented token embedding, "6.2. HSTU的工程突破" eq. 6.2.2:
+ *   x[t] = item_emb[item_ids[t]] + action_emb[actions[t]]
+ * item_emb [num_items, d], action_emb [num_actions, d], x [T, d] (dtype);
+ * item_ids int64 [T], actions int32 [T] (device). A row whose id or action
+ * is out of range is written as NaN (no out-of-bounds read). */
+int hstu_embed_fwd(int64_t T, int32_t d_model, int32_t dtype, const void *item_emb,
+                   int64_t num_items, const void *action_emb, int32_t num_actions,
+                   const int64_t *item_ids, const int32_t *actions, void *x, void *stream);
+
+/* Debug validation of device-resident index data (copies it to the host and
+ * synchronises `stream`): offsets start at 0, do not decrease and end at T;
+ * max_seq_len bounds every length; 0 <= num_targets[b] <= L_b; the cache
+ * offsets likewise; every visible position difference fits the table. Returns
+ * HSTU_OK or HSTU_E_DATA (with a message). */
+int hstu_check_inputs(const hstu_layer_desc *desc, const hstu_jagged *jagged,
+                      const hstu_kv_cache *cache, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSTU_H_ */

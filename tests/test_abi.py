@@ -1,0 +1,141 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+entry point the header declares, and rejects bad arguments before touching
+the device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from hstu_sequential_transducer_jagged_amd import hstu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hstu.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hstu.LIB_PATH):
+        from hstu_sequential_transducer_jagged_amd import build
+        build.build()
+    return hstu.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char \*)\s*(hstu_\w+)\s*\(", text,
+                                 re.MULTILINE)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(hstu.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert lib.hstu_abi_version() == 1
+
+
+def _desc(**kw):
+    d = dict(d_model=512, num_heads=8, dtype=hstu.HSTU_BF16, pos_table_len=255)
+    d.update(kw)
+    return hstu.make_desc(d["d_model"], d["num_heads"], d["dtype"], d["pos_table_len"])
+
+
+FAKE = 0x100000   # never dereferenced: validation rejects or returns before any launch
+
+
+def _attn(lib, desc, jag, cache=None, ptrs=FAKE):
+    P = ctypes.c_void_p
+    return lib.hstu_attn_fwd(ctypes.byref(desc) if desc else None,
+                             ctypes.byref(jag) if jag else None,
+                             ctypes.byref(cache) if cache else None,
+                             P(ptrs), P(ptrs), P(ptrs), P(ptrs), P(ptrs), P(ptrs), None)
+
+
+def _jag(B=2, T=10, mx=6):
+    return hstu.Jagged(B, mx, T, FAKE, FAKE, None)
+
+
+def test_validation_errors(lib):
+    assert _attn(lib, None, _jag()) == hstu.HSTU_E_INVAL
+    assert b"desc" in lib.hstu_last_error()
+    d = _desc()
+    d.head_dim = 32
+    assert _attn(lib, d, _jag()) == hstu.HSTU_E_INVAL          # d_model != H * dh
+    d = hstu.make_desc(256, 8, hstu.HSTU_BF16, 255)            # dh = 32 in bf16
+    assert _attn(lib, d, _jag()) == hstu.HSTU_E_UNSUPPORTED
+    d = _desc()
+    d.dtype = 7
+    assert _attn(lib, d, _jag()) == hstu.HSTU_E_INVAL
+    for alpha in (0.0, float("nan"), 1e9):
+        d = _desc()
+        d.alpha = alpha
+        assert _attn(lib, d, _jag()) == hstu.HSTU_E_INVAL
+    d = _desc()
+    d.pos_table_len = 256                                       # even
+    assert _attn(lib, d, _jag()) == hstu.HSTU_E_INVAL
+    d = _desc()
+    d.num_time_buckets = 0
+    assert _attn(lib, d, _jag()) == hstu.HSTU_E_INVAL
+    d = _desc(pos_table_len=9)                                  # n_max 5 < max_seq_len 6
+    assert _attn(lib, d, _jag()) == hstu.HSTU_E_INVAL
+    assert b"position table" in lib.hstu_last_error()
+    cache = hstu.KVCache(FAKE, FAKE, FAKE, FAKE, 125, 100)     # 6 + 125 > 128
+    assert _attn(lib, _desc(), _jag(), cache) == hstu.HSTU_E_INVAL
+    assert _attn(lib, _desc(), _jag(B=-1)) == hstu.HSTU_E_INVAL
+    assert _attn(lib, _desc(), _jag(), ptrs=FAKE + 8) == hstu.HSTU_E_INVAL   # misaligned
+    assert _attn(lib, _desc(), _jag(), ptrs=0) == hstu.HSTU_E_INVAL          # NULL
+
+
+def test_empty_batches_return_ok_without_device(lib):
+    assert _attn(lib, _desc(), _jag(B=0, T=0, mx=0)) == hstu.HSTU_OK
+    assert _attn(lib, _desc(), _jag(B=3, T=0, mx=0)) == hstu.HSTU_OK
+    P = ctypes.c_void_p
+    params = hstu.LayerParams(FAKE, None, FAKE, None, None, None, FAKE, FAKE)
+    assert lib.hstu_proj_fwd(ctypes.byref(_desc()), ctypes.byref(params), 0, None, None, None,
+                             None, None, None) == hstu.HSTU_OK
+    assert lib.hstu_proj_fwd(ctypes.byref(_desc()), ctypes.byref(params), -1, None, None, None,
+                             None, None, None) == hstu.HSTU_E_INVAL
+    assert lib.hstu_norm_gate_fwd(ctypes.byref(_desc()), 0, None, None, None, None, None,
+                                  None) == hstu.HSTU_OK
+    assert lib.hstu_out_fwd(ctypes.byref(_desc()), 5, P(FAKE), P(FAKE), P(FAKE), None,
+                            P(FAKE), None) == hstu.HSTU_E_INVAL   # y aliases x
+    assert lib.hstu_embed_fwd(0, 512, hstu.HSTU_BF16, None, 0, None, 0, None, None, None,
+                              None) == hstu.HSTU_OK
+    assert lib.hstu_embed_fwd(4, 12, hstu.HSTU_BF16, P(FAKE), 1, P(FAKE), 1, P(FAKE), P(FAKE),
+                              P(FAKE), None) == hstu.HSTU_E_UNSUPPORTED
+
+
+def test_layer_workspace_checks(lib):
+    d = _desc()
+    need = lib.hstu_layer_workspace_size(ctypes.byref(d), 10, 2)
+    assert need == 4 * 10240 + 20480
+    params = hstu.LayerParams(FAKE, None, FAKE, None, None, None, FAKE, FAKE)
+    P = ctypes.c_void_p
+    st = lib.hstu_layer_fwd(ctypes.byref(d), ctypes.byref(params), ctypes.byref(_jag()), None,
+                            P(FAKE), P(FAKE + 4096), None, None, P(FAKE), need - 1, None)
+    assert st == hstu.HSTU_E_WORKSPACE
+    st = lib.hstu_layer_fwd(ctypes.byref(d), ctypes.byref(params), ctypes.byref(_jag()), None,
+                            P(FAKE), P(FAKE + 4096), None, None, P(FAKE + 16), need, None)
+    assert st == hstu.HSTU_E_INVAL                             # workspace not 256-aligned
+    st = lib.hstu_layer_fwd(ctypes.byref(d), ctypes.byref(params), ctypes.byref(_jag()), None,
+                            P(FAKE), P(FAKE), None, None, P(FAKE), need, None)
+    assert st == hstu.HSTU_E_INVAL                             # y aliases x
+
+
+def test_binding_raises_with_message(lib):
+    with pytest.raises(hstu.HstuError) as e:
+        hstu.hstu_attn_fwd(None, _jag(), None, None, None, None, None, None, None, stream=0)
+    assert e.value.status == hstu.HSTU_E_INVAL
+
+
+def test_product_path_does_not_use_the_oracle():
+    pkg = os.path.join(ROOT, "hstu_sequential_transducer_jagged_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f

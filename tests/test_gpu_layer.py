@@ -1,0 +1,221 @@
+"""Layer, stack and ranking parity on the GPU against the CPU oracle, on the
+five workloads (full-size ones checked on sampled rows, sequences or users
+the oracle can evaluate in seconds)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from hstu_inputs import gen
+from tests.helpers import TOL, row_rel_err, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _runner():
+    from hstu_sequential_transducer_jagged_amd import runner
+    return runner
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _layer_gpu(w, l=0, k_out=False):
+    runner = _runner()
+    dw = runner.DeviceWorkload(w)
+    if not k_out:
+        y = runner.layer_forward(dw, dw.x, l)
+        _sync()
+        return to_np(y)[:w.total_tokens]
+    kk, vv = dw.empty_act(w.total_tokens), dw.empty_act(w.total_tokens)
+    y = runner.layer_forward(dw, dw.x, l, k_out=kk, v_out=vv)
+    _sync()
+    return to_np(y)[:w.total_tokens], to_np(kk), to_np(vv)
+
+
+def _oracle_layer(w, l=0, rows=None, x=None):
+    x = w.x if x is None else x
+    return oracle.layer(x, w.layers[l], w.offsets, w.timestamps, w.num_heads, w.n_max, w.alpha,
+                        w.ln_eps, rows=rows)
+
+
+@pytest.mark.parametrize("affine", ["default", "random"])
+def test_config0_fp32_layer(gpu_lib, affine):
+    w = gen.make_config(0, affine=affine)
+    got = _layer_gpu(w)
+    err = row_rel_err(got, _oracle_layer(w)["y"])
+    print(f"config 0 ({affine}): {err:.3e}")
+    assert err < TOL["f32"]
+
+
+@pytest.mark.parametrize("affine", ["default", "random"])
+def test_config1_bf16_layer_full(gpu_lib, affine):
+    w = gen.make_config(1, affine=affine)
+    got = _layer_gpu(w)
+    err = row_rel_err(got, _oracle_layer(w)["y"])
+    print(f"config 1 ({affine}) T={w.total_tokens}: {err:.3e}")
+    assert err < TOL["bf16"]
+
+
+def test_config2_bf16_layer_sampled_rows(gpu_lib):
+    """Full-size workload 2 (16 sequences up to 8192), in the launch the
+    benchmark times; the oracle evaluates sampled rows of the 8192 sequence
+    and the ends of two others."""
+    w = gen.make_config(2)
+    got = _layer_gpu(w)
+    o = w.offsets
+    rows = np.array([0, 1, 64, 777, 4096, 8127, 8190, 8191,
+                     int(o[1]) + 5, int(o[2]) - 1, int(o[16]) - 1, int(o[16]) - 2])
+    ref = _oracle_layer(w, rows=rows)["y"]
+    err = row_rel_err(got[rows], ref)
+    print(f"config 2 sampled rows: {err:.3e}")
+    assert err < TOL["bf16"]
+
+
+@pytest.mark.parametrize("lengths,H", [([1, 2, 63, 64, 65, 0, 129], 4), ([128] * 5, 8),
+                                       ([1] * 9, 2), ([300], 1)])
+def test_small_bf16_layers(gpu_lib, lengths, H):
+    w = gen.make_custom(lengths, 64 * H, H, dtype="bf16", seed=sum(lengths) + H,
+                        n_max=max(lengths), affine="random")
+    got = _layer_gpu(w)
+    assert row_rel_err(got, _oracle_layer(w)["y"]) < TOL["bf16"]
+
+
+def test_k_out_v_out_match_projection(gpu_lib):
+    w = gen.make_custom([50, 7], 256, 4, dtype="bf16", seed=77, n_max=50)
+    y, kk, vv = _layer_gpu(w, k_out=True)
+    r = _oracle_layer(w)
+    assert row_rel_err(kk[:57], r["k"]) < 8e-3
+    assert row_rel_err(vv[:57], r["v"]) < 8e-3
+    assert row_rel_err(y, r["y"]) < TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# workload 3: 8-layer stack over item + action embeddings
+# ---------------------------------------------------------------------------
+
+def _sub_workload(w, seqs):
+    """The chosen sequences of a workload as a workload of their own
+    (sequences are independent in the forward)."""
+    rows = np.concatenate([np.arange(w.offsets[b], w.offsets[b + 1]) for b in seqs])
+    sub = gen.Workload(**{f: getattr(w, f) for f in gen.Workload.__dataclass_fields__})
+    sub.offsets = gen.make_jagged([int(w.offsets[b + 1] - w.offsets[b]) for b in seqs])
+    sub.timestamps = w.timestamps[rows]
+    if w.x is not None:
+        sub.x = w.x[rows]
+    if w.item_ids is not None:
+        sub.item_ids = w.item_ids[rows]
+        sub.actions = w.actions[rows]
+    return sub, rows
+
+
+@pytest.fixture(scope="module")
+def config3_run(gpu_lib):
+    runner = _runner()
+    w = gen.make_config(3)
+    dw = runner.DeviceWorkload(w)
+    outs = runner.stack_forward(dw, return_all=True)
+    _sync()
+    return w, [to_np(o)[:w.total_tokens] for o in outs]
+
+
+def test_config3_embedding(config3_run):
+    w, outs = config3_run
+    rows = np.arange(0, w.total_tokens, 997)
+    ref = oracle.embed(w.item_emb, w.action_emb, w.item_ids[rows], w.actions[rows])
+    assert row_rel_err(outs[0][rows], ref) < 4e-3
+
+
+def test_config3_stack_end_to_end(config3_run):
+    """Whole 8-layer stack on three sequences (the longest, a middle and a
+    short one) recomputed by the oracle from the embeddings."""
+    w, outs = config3_run
+    L = w.lengths
+    seqs = [int(np.argmax(L)), int(np.argsort(L)[len(L) // 2 + 10]), int(np.argmin(L))]
+    sub, rows = _sub_workload(w, seqs)
+    x0 = oracle.embed(w.item_emb, w.action_emb, sub.item_ids, sub.actions)
+    ref = oracle.stack(x0, w.layers, sub.offsets, sub.timestamps, w.num_heads, w.n_max,
+                       w.alpha, w.ln_eps)
+    err = row_rel_err(outs[-1][rows], ref)
+    print(f"config 3 end-to-end (lengths {[int(L[s]) for s in seqs]}): {err:.3e}")
+    assert err < TOL["bf16"]
+
+
+def test_config3_teacher_forced_layers(config3_run):
+    """Each layer fed the device's own bf16 input: separates the per-layer
+    kernel error from error carried through the stack."""
+    w, outs = config3_run
+    rng = np.random.default_rng(3)
+    L = w.lengths
+    long_seq = int(np.argmax(L))
+    rows = np.concatenate([rng.choice(w.total_tokens, 24, replace=False),
+                           [int(w.offsets[long_seq + 1]) - 1]])
+    rows.sort()
+    for l in range(len(w.layers)):
+        ref = _oracle_layer(w, l, rows=rows, x=outs[l])["y"]
+        err = row_rel_err(outs[l + 1][rows], ref)
+        print(f"config 3 layer {l} teacher-forced: {err:.3e}")
+        assert err < TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# workload 4: micro-batched candidate scoring over a cached history
+# ---------------------------------------------------------------------------
+
+def _ranking_gpu(w, b_m=None):
+    runner = _runner()
+    dw = runner.DeviceWorkload(w)
+    plan = runner.RankingPlan(w, b_m)
+    out = to_np(runner.ranking_forward(dw, plan))
+    res = np.zeros_like(out)
+    res[plan.order] = out
+    return res
+
+
+def _sub_ranking(w, users):
+    hist_rows = np.concatenate([np.arange(w.offsets[u], w.offsets[u + 1]) for u in users])
+    cand_rows = np.concatenate([np.arange(w.cand_offsets[u], w.cand_offsets[u + 1]) for u in users])
+    sub = gen.Workload(**{f: getattr(w, f) for f in gen.Workload.__dataclass_fields__})
+    sub.offsets = gen.make_jagged([int(w.offsets[u + 1] - w.offsets[u]) for u in users])
+    sub.cand_offsets = gen.make_jagged([int(w.cand_offsets[u + 1] - w.cand_offsets[u]) for u in users])
+    sub.x, sub.timestamps = w.x[hist_rows], w.timestamps[hist_rows]
+    sub.cand_x, sub.cand_timestamps = w.cand_x[cand_rows], w.cand_timestamps[cand_rows]
+    return sub, cand_rows
+
+
+@pytest.mark.parametrize("b_m", [1, 2, 5, 128])
+def test_small_ranking_full(gpu_lib, b_m):
+    w = gen.make_ranking(seed=41, users=4, history=[100, 0, 65, 1], candidates=[9, 4, 0, 130],
+                         micro_batch=b_m, d_model=256, num_heads=4, num_layers=2,
+                         affine="random")
+    got = _ranking_gpu(w)
+    ref = oracle.ranking(w)["cand_y"]
+    err = row_rel_err(got, ref)
+    print(f"small ranking b_m={b_m}: {err:.3e}")
+    assert err < TOL["bf16"]
+
+
+def test_ranking_batched_equals_independent(gpu_lib):
+    """Candidates scored in micro-batches against the cache equal each
+    candidate scored alone after its user's history (oracle)."""
+    w = gen.make_ranking(seed=43, users=2, history=[70, 129], candidates=[5, 3], micro_batch=2,
+                         d_model=256, num_heads=4, num_layers=2)
+    got = _ranking_gpu(w)
+    for u in range(2):
+        for c in range(int(w.cand_offsets[u + 1] - w.cand_offsets[u])):
+            ref = oracle.ranking_independent(w, u, c)
+            err = row_rel_err(got[w.cand_offsets[u] + c][None], ref[None])
+            assert err < TOL["bf16"], (u, c, err)
+
+
+def test_config4_ranking_sampled_users(gpu_lib):
+    w = gen.make_config(4)
+    got = _ranking_gpu(w)
+    users = [0, 17]
+    sub, cand_rows = _sub_ranking(w, users)
+    ref = oracle.ranking(sub)["cand_y"]
+    err = row_rel_err(got[cand_rows], ref)
+    print(f"config 4 users {users}: {err:.3e}")
+    assert err < TOL["bf16"]
