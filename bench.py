@@ -117,6 +117,7 @@ def main():
     av = mk(torch.float32)
     x = dw.x
     desc, jag = dw.desc, dw.jagged
+    attn_ws = hstu.workspace_tensor(hstu.hstu_attn_workspace_size(desc, jag))
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
@@ -124,7 +125,7 @@ def main():
         hstu.hstu_proj_fwd(desc, lay.params, T, x, u, v, q, k, sh)
         if ev is not None:
             ev[0].record(stream)
-        hstu.hstu_attn_fwd(desc, jag, None, q, k, v, lay.pos_bias, lay.time_bias, av, sh)
+        hstu.hstu_attn_fwd(desc, jag, None, q, k, v, lay.pos_bias, lay.time_bias, av, attn_ws, sh)
         if ev is not None:
             ev[1].record(stream)
         hstu.hstu_norm_gate_fwd(desc, T, av, u, lay.gamma, lay.beta, g, sh)
@@ -148,7 +149,7 @@ def main():
     attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     # cross-check: the same layer through the single hstu_layer_fwd entry point
-    ws = dw.workspace(T, w.num_seqs)
+    ws = dw.workspace()
     y2 = mk()
     for _ in range(2):
         hstu.hstu_layer_fwd(desc, lay.params, jag, None, x, y2, None, None, ws, sh)

@@ -103,8 +103,10 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 hstu::AttnArgs make_attn_args(const hstu_layer_desc* d, const hstu_jagged* j,
                               const hstu_kv_cache* c, const void* q, const void* k,
-                              const void* v, const float* pb, const float* tb, float* av) {
+                              const void* v, const float* pb, const float* tb, float* av,
+                              void* ws) {
   hstu::AttnArgs a{};
+  a.sched = static_cast<int*>(ws);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -148,8 +150,9 @@ int do_proj(const hstu_layer_desc* d, const hstu_layer_params* p, int64_t T, con
 }
 
 int do_attn(const hstu_layer_desc* d, const hstu_jagged* j, const hstu_kv_cache* c, const void* q,
-            const void* k, const void* v, const float* pb, const float* tb, float* av, hipStream_t s) {
-  const hstu::AttnArgs a = make_attn_args(d, j, c, q, k, v, pb, tb, av);
+            const void* k, const void* v, const float* pb, const float* tb, float* av, void* ws,
+            hipStream_t s) {
+  const hstu::AttnArgs a = make_attn_args(d, j, c, q, k, v, pb, tb, av, ws);
   return device_status(d->dtype == HSTU_BF16 ? hstu::launch_attn_bf16(a, s) : hstu::launch_attn_f32(a, s),
                        "attention launch");
 }
@@ -170,6 +173,19 @@ int do_out(const hstu_layer_desc* d, int64_t T, const void* g, const void* x, co
 }
 
 size_t round256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+size_t attn_ws(const hstu_layer_desc* d, const hstu_jagged* j) {
+  if (d->dtype != HSTU_BF16 || j->num_seqs <= 0 || j->max_seq_len <= 0) return 0;
+  return round256(hstu::attn_workspace_bytes(j->num_seqs, j->max_seq_len));
+}
+
+// the work list indexes items as seq * n_tiles + tile in int32
+int check_items(const hstu_jagged* j) {
+  const int64_t n_qt = (static_cast<int64_t>(j->max_seq_len) + 63) / 64;
+  CHECK(static_cast<int64_t>(j->num_seqs) * n_qt < (int64_t{1} << 31) - 1, HSTU_E_UNSUPPORTED,
+        "num_seqs * ceil(max_seq_len / 64) must stay below 2^31");
+  return HSTU_OK;
+}
 
 }  // namespace
 
@@ -193,19 +209,33 @@ int hstu_proj_fwd(const hstu_layer_desc* desc, const hstu_layer_params* params, 
   return do_proj(desc, params, T, x, u, v, q, k, as_stream(stream));
 }
 
+size_t hstu_attn_workspace_size(const hstu_layer_desc* desc, const hstu_jagged* jagged) {
+  if (!desc || !jagged) return 0;
+  return attn_ws(desc, jagged);
+}
+
 int hstu_attn_fwd(const hstu_layer_desc* desc, const hstu_jagged* jagged,
                   const hstu_kv_cache* cache, const void* q, const void* k, const void* v,
-                  const float* pos_bias, const float* time_bias, float* av, void* stream) {
+                  const float* pos_bias, const float* time_bias, float* av, void* workspace,
+                  size_t workspace_bytes, void* stream) {
   int st = check_desc(desc);
   if (st) return st;
   st = check_jagged(desc, jagged, cache);
+  if (st) return st;
+  st = check_items(jagged);
   if (st) return st;
   if (jagged->num_seqs == 0 || jagged->total_tokens == 0) return ok();
   CHECK(q && k && v && av, HSTU_E_INVAL, "q/k/v/av must not be NULL");
   CHECK(pos_bias && time_bias, HSTU_E_INVAL, "pos_bias/time_bias must not be NULL");
   CHECK(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(av), HSTU_E_INVAL,
         "q/k/v/av must be 16-byte aligned");
-  return do_attn(desc, jagged, cache, q, k, v, pos_bias, time_bias, av, as_stream(stream));
+  const size_t need = attn_ws(desc, jagged);
+  CHECK(workspace_bytes >= need && (need == 0 || workspace != nullptr), HSTU_E_WORKSPACE,
+        "workspace too small: need %zu bytes, got %zu", need, workspace_bytes);
+  CHECK((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, HSTU_E_INVAL,
+        "workspace must be 256-byte aligned");
+  return do_attn(desc, jagged, cache, q, k, v, pos_bias, time_bias, av, workspace,
+                 as_stream(stream));
 }
 
 int hstu_norm_gate_fwd(const hstu_layer_desc* desc, int64_t T, const float* av, const void* u,
@@ -234,12 +264,12 @@ int hstu_out_fwd(const hstu_layer_desc* desc, int64_t T, const void* g, const vo
   return do_out(desc, T, g, x, w2, b2, y, as_stream(stream));
 }
 
-size_t hstu_layer_workspace_size(const hstu_layer_desc* desc, int64_t T, int32_t num_seqs) {
-  (void)num_seqs;
-  if (!desc || T < 0 || desc->d_model <= 0) return 0;
-  const size_t act = round256(static_cast<size_t>(T) * desc->d_model * elem_size(desc->dtype));
-  const size_t av = round256(static_cast<size_t>(T) * desc->d_model * sizeof(float));
-  return 4 * act + av;  // U, V, Q, K (G overwrites U in place), AV
+size_t hstu_layer_workspace_size(const hstu_layer_desc* desc, const hstu_jagged* jagged) {
+  if (!desc || !jagged || jagged->total_tokens < 0 || desc->d_model <= 0) return 0;
+  const size_t T = static_cast<size_t>(jagged->total_tokens);
+  const size_t act = round256(T * desc->d_model * elem_size(desc->dtype));
+  const size_t av = round256(T * desc->d_model * sizeof(float));
+  return 4 * act + av + attn_ws(desc, jagged);  // U, V, Q, K (G overwrites U), AV, work list
 }
 
 int hstu_layer_fwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
@@ -252,6 +282,8 @@ int hstu_layer_fwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
   if (st) return st;
   CHECK(params && params->w1 && params->w2 && params->pos_bias && params->time_bias, HSTU_E_INVAL,
         "params, w1, w2, pos_bias and time_bias must not be NULL");
+  st = check_items(jagged);
+  if (st) return st;
   const int64_t T = jagged->total_tokens;
   if (T == 0 || jagged->num_seqs == 0) return ok();
   CHECK(x && y, HSTU_E_INVAL, "x/y must not be NULL");
@@ -262,7 +294,7 @@ int hstu_layer_fwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
         "k_out/v_out must be 16-byte aligned");
   CHECK(!params->ln_gamma || aligned16(params->ln_gamma), HSTU_E_INVAL, "ln_gamma must be 16-byte aligned");
   CHECK(!params->ln_beta || aligned16(params->ln_beta), HSTU_E_INVAL, "ln_beta must be 16-byte aligned");
-  const size_t need = hstu_layer_workspace_size(desc, T, jagged->num_seqs);
+  const size_t need = hstu_layer_workspace_size(desc, jagged);
   CHECK(workspace != nullptr && workspace_bytes >= need, HSTU_E_WORKSPACE,
         "workspace too small: need %zu bytes, got %zu", need, workspace_bytes);
   CHECK((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, HSTU_E_INVAL,
@@ -274,12 +306,13 @@ int hstu_layer_fwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
   void* q = ws + 2 * act;
   void* k = ws + 3 * act;
   float* av = reinterpret_cast<float*>(ws + 4 * act);
+  void* attn_work = ws + 4 * act + round256(static_cast<size_t>(T) * desc->d_model * sizeof(float));
   if (k_out) k = k_out;
   if (v_out) v = v_out;
   hipStream_t s = as_stream(stream);
   st = do_proj(desc, params, T, x, u, v, q, k, s);
   if (st) return st;
-  st = do_attn(desc, jagged, cache, q, k, v, params->pos_bias, params->time_bias, av, s);
+  st = do_attn(desc, jagged, cache, q, k, v, params->pos_bias, params->time_bias, av, attn_work, s);
   if (st) return st;
   st = do_norm_gate(desc, T, av, u, params->ln_gamma, params->ln_beta, u, s);
   if (st) return st;

@@ -10,20 +10,28 @@
 // Visibility: cache rows always; own key j for own query i iff j <= i and
 // (j is not a target or j == i).
 //
-// bf16 kernel design (head_dim 64):
-//  * one workgroup = one 64-row query tile of one sequence and HPB heads, one
-//    wave per head; the relative bias is shared by all heads, so the block
-//    computes each 64 x 32 bias tile once and every wave reads it from LDS
-//    as the initial accumulator of its Q.K MFMA (the bias add is free);
-//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: the accumulator layout of S^T
-//    (lane = query, 4 consecutive keys) is directly the A-operand layout of
-//    the S.V MFMA, so P never leaves registers;
-//  * alpha is folded out of the inner loop: the block works on
-//    S' = q.k + rab/alpha and evaluates P' = S' / (1 + 2^(-alpha log2(e) S'))
-//    (= SiLU(alpha S') / alpha), scaling the output by alpha once at the end;
-//    masked pairs get a bias that drives 2^(...) to +inf, i.e. P' = 0;
-//  * key tiles entirely above the diagonal are never visited (loop bound);
-//    key tiles of other targets are skipped; no softmax statistics exist.
+// bf16 kernel (head_dim 64) design:
+//  * a workgroup owns one 64-query tile of one sequence for HPB heads, one
+//    wave per head, and walks the visible 32-key tiles (tiles above the
+//    diagonal and tiles of other targets are never visited);
+//  * K and V tiles of all HPB heads arrive by direct global->LDS loads
+//    (global_load_lds_dwordx4) into a double buffer, one tile ahead;
+//  * the relative bias is shared by all heads: the workgroup builds each
+//    64 x 32 bias tile once, one step ahead, from per-key timestamps staged in
+//    LDS and a sliding window of the position table, and every wave uses it
+//    as the initial accumulator of its Q.K MFMAs (the add is free);
+//  * scores are produced directly in the base-2 domain: Q is prescaled by
+//    -alpha*log2(e) and the bias by -log2(e), so with S' = -log2(e) S
+//    SiLU(S) = -ln2 * S' / (1 + 2^S'): one exp2, one add, one rcp and one
+//    mul per score; -ln2 is applied once to the output; invisible pairs get
+//    a bias that sends 2^S' to +inf (P = 0);
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: the accumulator layout of S^T
+//    (lane = query, 16 keys) is the A-operand layout of the S.V MFMA, so P
+//    stays in registers; V's B operand is read with ds_read_b64_tr_b16
+//    (transposing 16-bit reads) from the row-major tile;
+//  * time buckets are exact integers: 32-bit |dt|+1 and a leading-zero count
+//    when every pair of the tile is within 2^30 s of the block's reference
+//    time, a 64-bit path otherwise.
 #include "common.h"
 #include "internal.h"
 
@@ -33,15 +41,27 @@ namespace {
 constexpr int kBM = 64;   // query rows per workgroup
 constexpr int kBN = 32;   // keys per step
 constexpr int kDH = 64;   // head dim of the bf16 kernel
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kMaskBias = 1.0e30f;   // base-2 score bias of an invisible pair
+constexpr int kPosWin = 128;           // position-window entries per tile
 
-__device__ __forceinline__ int time_bucket(int64_t dt, int nb) {
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int time_bucket64(int64_t dt, int nb) {
   uint64_t a = dt < 0 ? (0ull - static_cast<uint64_t>(dt)) : static_cast<uint64_t>(dt);
-  a += 1ull;  // |dt| + 1 >= 1 (wraps only for |dt| = 2^64-1, impossible for int64)
-  int b = 63 - __clzll(static_cast<long long>(a));
+  a += 1ull;
+  const int b = 63 - __clzll(static_cast<long long>(a));
   return b < nb - 1 ? b : nb - 1;
 }
 
-// Key-space helpers: key index kk in [0, nc + L): cache rows first.
 struct SeqInfo {
   int64_t s;     // first own token row
   int L;         // own length
@@ -66,194 +86,502 @@ __device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b) {
   return si;
 }
 
-__device__ __forceinline__ float silu_scaled(float s, float exp_scale) {
-  const float e = __builtin_amdgcn_exp2f(s * exp_scale);
-  return s * __builtin_amdgcn_rcpf(1.0f + e);
-}
+// Per-key data of one key tile, delivered to LDS by DMA two tiles ahead.
+struct KeyData {
+  alignas(16) uint32_t tlo[kBN];    // low words of the key timestamps
+  alignas(16) uint32_t thi[kBN];    // high words (64-bit path)
+  alignas(16) float pos[kPosWin];   // raw position-bias window, entry e <-> dp = w0 + e
+};
 
 template <int HPB>
-__global__ __launch_bounds__(64 * HPB) void attn_bf16_kernel(AttnArgs a) {
-  constexpr int NT = 64 * HPB;
-  constexpr int ROW = HPB * kDH + 8;        // LDS row stride (bf16), +16 B pad
-  constexpr int CPR = HPB * kDH / 8;        // 16-byte chunks per K/V row
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kBN * ROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kBN * ROW];
-  __shared__ __attribute__((aligned(16))) float sBias[8 * 64 * 4];
-  __shared__ float sTime[64];
+struct Rows {
+  static constexpr int ROWB = HPB * kDH * 2 + 32;   // bytes per staged K/V row (+32 B pad)
+};
 
-  const int seq = blockIdx.x;
-  const int n_qt = (a.max_seq_len + kBM - 1) / kBM;
-  const int qt = n_qt - 1 - static_cast<int>(blockIdx.y);   // heaviest tiles first
-  const SeqInfo si = seq_info(a, seq);
-  const int q0 = qt * kBM;
-  if (q0 >= si.L) return;
+// Position of key kk (block key index: cache rows first).
+__device__ __forceinline__ int key_pos(int kk, int nc, int first_tgt) {
+  return kk < nc ? kk : nc + min(kk - nc, first_tgt);
+}
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int g = lane >> 4;
-  const int l16 = lane & 15;
-  const int d = a.d_model;
-  const int col0 = blockIdx.z * HPB * kDH;
-  const int h_col = col0 + wave * kDH;
-  const float inv_alpha = 1.0f / a.alpha;
-  const float exp_scale = -a.alpha * 1.4426950408889634f;
-  const float mask_raw = -1.0e30f * inv_alpha;
+// Block-uniform integers of one query tile.
+struct Ctx {
+  int64_t s, cs;
+  int L, nc, first_tgt, q0, q_hi, nkeys, d, col0, pmin_q, pos_len, pos_center;
+  uint32_t tb_lo;     // low word of the block's reference time (minimum timestamp)
+  int wide;           // the block's timestamps span >= 2^31 s: 64-bit bucket path
+};
 
-  const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.q);
-  const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.k);
-  const uint16_t* __restrict__ V = static_cast<const uint16_t*>(a.v);
-  const uint16_t* __restrict__ CK = static_cast<const uint16_t*>(a.ck);
-  const uint16_t* __restrict__ CV = static_cast<const uint16_t*>(a.cv);
+// Window origin (position difference of window entry 0) of key tile `tile`.
+__device__ __forceinline__ int window_origin(const Ctx& c, int tile) {
+  const int klast = min(tile * kBN + kBN, c.nkeys) - 1;
+  return c.pmin_q - key_pos(klast, c.nc, c.first_tgt);
+}
 
-  for (int i = tid; i < 64; i += NT) sTime[i] = i < a.nb ? a.time_bias[i] * inv_alpha : 0.0f;
+// Source row (global element offset of the row start) of block key kk.
+__device__ __forceinline__ int64_t key_row(const Ctx& c, int kk) {
+  return kk < c.nc ? (c.cs + kk) : (c.s + kk - c.nc);
+}
 
-  // Q fragments (B operand of S^T = K Q^T): lane -> query l16, 8 dims at 8g.
-  bf16x8 qf[4][2];
+// DMA of a tile's key data: wave 0 the timestamps (lanes 0..31 low words,
+// 32..63 high words), waves 1 and 2 the two halves of the position window.
+template <int HPB>
+__device__ __forceinline__ void load_keydata(const Ctx& c, const int64_t* ts, const int64_t* c_ts,
+                                             const float* pos_bias, KeyData& kd, int tile, int wave,
+                                             int lane) {
+  if (wave == 0) {
+    const int kk = min(tile * kBN + (lane & (kBN - 1)), c.nkeys - 1);
+    const int64_t* tp = kk < c.nc ? c_ts + (c.cs + kk) : ts + (c.s + kk - c.nc);
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(tp) + (lane >> 5);
+    __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, kd.tlo), 4, 0, 0);
+  } else if (wave <= 2 || HPB < 4) {
+    // with fewer than 3 waves, wave 0 / 1 issue the window halves too
+    const int w0 = window_origin(c, tile);
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
-    const int qi = q0 + qb * 16 + l16;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      uint4 raw = make_uint4(0, 0, 0, 0);
-      if (qi < si.L)
-        raw = *reinterpret_cast<const uint4*>(Q + (si.s + qi) * d + h_col + c * 32 + 8 * g);
-      qf[qb][c] = __builtin_bit_cast(bf16x8, raw);
+    for (int half = 0; half < 2; ++half) {
+      if (HPB >= 4 && half != wave - 1) continue;
+      int idx = c.pos_center + w0 + half * 64 + lane;
+      idx = idx < 0 ? 0 : (idx >= c.pos_len ? c.pos_len - 1 : idx);
+      __builtin_amdgcn_global_load_lds(pos_bias + idx, LDS_PTR(void, kd.pos + half * 64), 4, 0, 0);
     }
   }
-
-  f32x4 acc[4][4];
+  if (HPB < 4 && wave == 0) {
+    const int w0 = window_origin(c, tile);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int q_hi = min(q0 + kBM, si.L);        // exclusive bound of own queries
-  const int nkeys = si.nc + q_hi;                // keys any query of the tile may see
-  const int nkt = (nkeys + kBN - 1) / kBN;
-  const int first_tgt = si.L - si.m;
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int k0 = kt * kBN;
-    const int own_lo = k0 - si.nc;
-    // A tile made only of targets that are not queries of this block is
-    // invisible to every query of the block.
-    if (own_lo >= 0 && own_lo >= first_tgt && own_lo + kBN <= q0) continue;
-
-    __syncthreads();  // previous step's readers are done with sK/sV/sBias
-
-    // ---- stage K and V rows [k0, k0 + kBN) of this head group into LDS ----
-    for (int c = tid; c < kBN * CPR; c += NT) {
-      const int r = c / CPR;
-      const int cc = c - r * CPR;
-      const int kk = k0 + r;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (kk < nkeys) {
-        const int64_t off = (kk < si.nc ? (si.cs + kk) : (si.s + kk - si.nc)) * d + col0 + cc * 8;
-        const uint16_t* kp = kk < si.nc ? CK : K;
-        const uint16_t* vp = kk < si.nc ? CV : V;
-        kv = *reinterpret_cast<const uint4*>(kp + off);
-        vv = *reinterpret_cast<const uint4*>(vp + off);
-      }
-      *reinterpret_cast<uint4*>(&sK[r * ROW + cc * 8]) = kv;
-      *reinterpret_cast<uint4*>(&sV[r * ROW + cc * 8]) = vv;
+    for (int half = 0; half < 2; ++half) {
+      int idx = c.pos_center + w0 + half * 64 + lane;
+      idx = idx < 0 ? 0 : (idx >= c.pos_len ? c.pos_len - 1 : idx);
+      __builtin_amdgcn_global_load_lds(pos_bias + idx, LDS_PTR(void, kd.pos + half * 64), 4, 0, 0);
     }
+  }
+}
 
-    // ---- bias tile, stored in the S^T accumulator layout ----
-    // slot = (kb*4 + qb)*64 + lane: query qb*16 + lane%16, keys kb*16 + 4(lane/16) + r
-    for (int slot = tid; slot < 512; slot += NT) {
-      const int tile = slot >> 6;
-      const int l = slot & 63;
-      const int kb = tile >> 2;
-      const int qb = tile & 3;
-      const int qi = q0 + qb * 16 + (l & 15);
-      const int kbase = k0 + kb * 16 + 4 * (l >> 4);
-      float bv[4];
-      const bool qvalid = qi < si.L;
-      const int pq = si.nc + (qi < first_tgt ? qi : first_tgt);
-      const int64_t tq = qvalid ? a.ts[si.s + qi] : 0;
+// Direct global->LDS loads of the K and V rows of a key tile. Wave w loads
+// rows w, w + HPB, ... of K and of V (rows past the last key repeat it; their
+// scores are masked). Row pointers are wave-uniform: block key kk lives at
+// base + kk*d for both the own rows (base shifted back by the cache length)
+// and the cache rows; only the lane's 16-byte column offset is per lane.
+template <int HPB>
+__device__ __forceinline__ void load_kv(const Ctx& c, const uint16_t* kbase_o, const uint16_t* kbase_c,
+                                        const uint16_t* vbase_o, const uint16_t* vbase_c, uint8_t* sk,
+                                        uint8_t* sv, int tile, int wave, int lane) {
+  constexpr int ROWB = Rows<HPB>::ROWB;
+  const int k0 = tile * kBN;
+#pragma unroll
+  for (int it = 0; it < kBN / HPB; ++it) {
+    const int r = wave + it * HPB;
+    const int kk = min(k0 + r, c.nkeys - 1);
+    const bool cached = kk < c.nc;
+    const int64_t off = static_cast<int64_t>(kk) * c.d;
+    const uint16_t* krow = (cached ? kbase_c : kbase_o) + off;
+    const uint16_t* vrow = (cached ? vbase_c : vbase_o) + off;
+    if (lane < HPB * 8) {
+      __builtin_amdgcn_global_load_lds(krow + lane * 8, LDS_PTR(void, sk + r * ROWB), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vrow + lane * 8, LDS_PTR(void, sv + r * ROWB), 16, 0, 0);
+    }
+  }
+}
+
+// Per-thread slot data of the bias builder: slot = (qb*4 + j)*64 + l covers
+// query qb*32 + l%32 and keys 8j + 4(l/32) + r, r = 0..3 (the S^T
+// accumulator order of v_mfma_f32_32x32x16).
+template <int SPT>
+struct SlotQ {
+  int qi[SPT], pq[SPT];
+  uint32_t uq[SPT];     // query time relative to the block reference (32-bit path)
+  int64_t tq[SPT];      // raw query time (64-bit path)
+};
+
+// Bias tile (base-2 domain) of key tile `tile` from its key data.
+template <int HPB>
+__device__ __forceinline__ void build_bias(const Ctx& c, const SlotQ<512 / (64 * HPB)>& sq,
+                                           const KeyData& kd, float* bias, const float* tb_clz,
+                                           const float* tb_lin, int nb, int tile, int tid) {
+  constexpr int NT = 64 * HPB;
+  constexpr int SPT = 512 / NT;
+  const int k0 = tile * kBN;
+  const int w0 = window_origin(c, tile);
+  // all keys are non-targets visible to every query of the block
+  const bool full = (k0 + kBN - 1 - c.nc <= c.q0) && (k0 + kBN - 1 - c.nc < c.first_tgt);
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    const int slot = tid + i * NT;
+    const int kr = 8 * ((slot >> 6) & 3) + 4 * ((slot >> 5) & 1);
+    const int kbase = k0 + kr;
+    const int qi = sq.qi[i];
+    float b[4];
+    if (full && !c.wide) {
+      const uint4 t4 = *reinterpret_cast<const uint4*>(&kd.tlo[kr]);
+      const uint32_t tk[4] = {t4.x, t4.y, t4.z, t4.w};
+      const float* pw = kd.pos + (sq.pq[i] - kbase - w0);   // p_k = kk for non-target keys
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t x = sq.uq[i], y = tk[r] - c.tb_lo;
+        const uint32_t ad = (x > y ? x - y : y - x) + 1u;   // |dt| + 1 >= 1
+        b[r] = __builtin_fmaf(pw[-r], -kLog2e, tb_clz[__builtin_clz(ad)]);
+      }
+    } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kk = kbase + r;
-        bool vis = false;
-        int pk = 0;
-        int64_t tk = 0;
-        if (qvalid && kk < nkeys) {
-          if (kk < si.nc) {
-            vis = true;
-            pk = kk;
-            tk = a.c_ts[si.cs + kk];
-          } else {
-            const int j = kk - si.nc;
-            vis = (j <= qi) && (j < first_tgt || j == qi);
-            pk = si.nc + (j < first_tgt ? j : first_tgt);
-            tk = a.ts[si.s + j];
-          }
+        const int jo = kk - c.nc;
+        const bool vis = qi < c.L && kk < c.nkeys &&
+                         (kk < c.nc || (jo <= qi && (jo < c.first_tgt || jo == qi)));
+        int pidx = sq.pq[i] - key_pos(kk, c.nc, c.first_tgt) - w0;
+        pidx = pidx < 0 ? 0 : (pidx >= kPosWin ? kPosWin - 1 : pidx);
+        float tbv;
+        if (!c.wide) {
+          const uint32_t x = sq.uq[i], y = kd.tlo[kr + r] - c.tb_lo;
+          const uint32_t ad = (x > y ? x - y : y - x) + 1u;
+          tbv = tb_clz[__builtin_clz(ad)];
+        } else {
+          const int64_t tk = static_cast<int64_t>((static_cast<uint64_t>(kd.thi[kr + r]) << 32) |
+                                                  kd.tlo[kr + r]);
+          tbv = tb_lin[time_bucket64(sq.tq[i] - tk, nb)];
         }
-        float b = mask_raw;
-        if (vis) {
-          int pidx = pq - pk + a.pos_center;
-          pidx = pidx < 0 ? 0 : (pidx >= a.pos_len ? a.pos_len - 1 : pidx);
-          b = a.pos_bias[pidx] * inv_alpha + sTime[time_bucket(tq - tk, a.nb)];
-        }
-        bv[r] = b;
+        b[r] = vis ? __builtin_fmaf(kd.pos[pidx], -kLog2e, tbv) : kMaskBias;
       }
-      *reinterpret_cast<float4*>(&sBias[slot * 4]) = make_float4(bv[0], bv[1], bv[2], bv[3]);
+    }
+    *reinterpret_cast<float4*>(&bias[slot * 4]) = make_float4(b[0], b[1], b[2], b[3]);
+  }
+}
+
+// One wave's share of a key tile, in phases so that the step can interleave
+// other work between them: S^T = K Q^T + bias for both 32-query blocks
+// (two independent MFMA chains), then per block P = S' / (1 + 2^S') and
+// O += P V.
+template <int HPB>
+__device__ __forceinline__ void scores(const uint8_t* kb, const float* bias,
+                                       const bf16x8 (&qf)[2][4], f32x16 (&st)[2], int koff,
+                                       int lane) {
+  bf16x8 kf[4];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc)
+    kf[cc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + koff + cc * 32));
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 bv = *reinterpret_cast<const float4*>(&bias[((qb * 4 + j) * 64 + lane) * 4]);
+      st[qb][4 * j + 0] = bv.x;
+      st[qb][4 * j + 1] = bv.y;
+      st[qb][4 * j + 2] = bv.z;
+      st[qb][4 * j + 3] = bv.w;
+    }
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) st[qb] = mfma32(kf[cc], qf[qb][cc], st[qb]);
+}
+
+__device__ __forceinline__ void silu_pack(const f32x16& st, bf16x8 (&pa)[2]) {
+  uint32_t pk[8];
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    const float x0 = st[r], x1 = st[r + 1];
+    const float p0 = x0 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x0));
+    const float p1 = x1 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x1));
+    pk[r >> 1] = pack_bf16x2(p0, p1);
+  }
+  pa[0] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+  pa[1] = __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]));
+}
+
+// V's B operands for both 16-key halves and both 32-dim blocks (transposing
+// 16-bit reads of the row-major tile).
+template <int HPB>
+__device__ __forceinline__ void load_v(const uint8_t* vb, int voff, bf16x8 (&vf)[2][2]) {
+  constexpr int ROWB = Rows<HPB>::ROWB;
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const uint8_t* p = vb + voff + kh * 16 * ROWB + db * 64;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p + 8 * ROWB));
+      vf[db][kh] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+}
+
+__device__ __forceinline__ void pv(const bf16x8 (&pa)[2], const bf16x8 (&vf)[2][2], f32x16 (&acc)[2]) {
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int db = 0; db < 2; ++db) acc[db] = mfma32(pa[kh], vf[db][kh], acc[db]);
+}
+
+// Number of key steps (32-key tiles visited) of query tile qt of a sequence:
+// the cost the schedule sorts by.
+__device__ __forceinline__ int tile_steps(const SeqInfo& si, int qt) {
+  const int q0 = qt * kBM;
+  const int q_hi = min(q0 + kBM, si.L);
+  const int nkeys = si.nc + q_hi;
+  const int n_kt = (nkeys + kBN - 1) / kBN;
+  const int first_tgt = si.L - si.m;
+  const int skip_a = (si.nc + first_tgt + kBN - 1) / kBN;
+  const int skip_b = max((si.nc + q0) / kBN, skip_a);
+  return n_kt - (skip_b - skip_a);
+}
+
+constexpr int kSchedBuckets = 8192;
+
+// Work list of the bf16 attention: every non-empty (sequence, 64-query tile)
+// item, counting-sorted by its number of key steps, most expensive first.
+// sched[0] = number of items, sched[1 + i] = seq * n_qt + tile of item i.
+// One workgroup; cost buckets in LDS (costs above the last bucket share it).
+__global__ __launch_bounds__(1024) void attn_schedule_kernel(AttnArgs a, int n_qt, int cmax) {
+  __shared__ int cnt[kSchedBuckets];
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  for (int i = tid; i <= cmax; i += 1024) cnt[i] = 0;
+  __syncthreads();
+  for (int b = tid; b < a.num_seqs; b += 1024) {
+    const SeqInfo si = seq_info(a, b);
+    // tiles past max_seq_len (a violated contract) are not scheduled
+    const int nt = min((si.L + kBM - 1) / kBM, n_qt);
+    for (int t = 0; t < nt; ++t) atomicAdd(&cnt[min(tile_steps(si, t), cmax)], 1);
+  }
+  __syncthreads();
+  // exclusive scan in descending cost order: start(c) = items costing more than c
+  const int per = (cmax + 1 + 1023) / 1024;
+  const int lo = cmax - tid * per;   // this thread scans buckets lo, lo-1, ..., lo-per+1
+  int sum = 0;
+  for (int i = 0; i < per; ++i)
+    if (lo - i >= 0) sum += cnt[lo - i];
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = tid ? part[tid - 1] : 0;
+  for (int i = 0; i < per; ++i)
+    if (lo - i >= 0) {
+      const int c = cnt[lo - i];
+      cnt[lo - i] = run;
+      run += c;
+    }
+  if (tid == 1023) a.sched[0] = part[1023];
+  __syncthreads();
+  for (int b = tid; b < a.num_seqs; b += 1024) {
+    const SeqInfo si = seq_info(a, b);
+    const int nt = min((si.L + kBM - 1) / kBM, n_qt);
+    for (int t = 0; t < nt; ++t) {
+      const int pos = atomicAdd(&cnt[min(tile_steps(si, t), cmax)], 1);
+      a.sched[1 + pos] = b * n_qt + t;
+    }
+  }
+}
+
+template <int HPB>
+__global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
+  constexpr int NT = 64 * HPB;
+  constexpr int ROWB = Rows<HPB>::ROWB;
+  constexpr int SPT = 512 / NT;   // bias slots per thread (512 slots of 4 pairs)
+  // Double buffers as distinct LDS objects: the compiler then knows that the
+  // DMA filling one buffer cannot alias the reads of the other and does not
+  // wait for it.
+  __shared__ __attribute__((aligned(16))) uint8_t sK0[kBN * ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t sK1[kBN * ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t sV0[kBN * ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t sV1[kBN * ROWB];
+  __shared__ __attribute__((aligned(16))) float sB0[kBM * kBN];
+  __shared__ __attribute__((aligned(16))) float sB1[kBM * kBN];
+  __shared__ KeyData sD0, sD1;
+  __shared__ float tb_clz[32];   // base-2 time bias indexed by clz(|dt|+1)
+  __shared__ float tb_lin[64];   // base-2 time bias indexed by bucket
+  __shared__ int64_t red_min[HPB], red_max[HPB];
+
+  // work item of this workgroup: the list is sorted heaviest first, so
+  // consecutive workgroups (dealt round-robin to the XCDs) carry equal work
+  const int total = a.sched[0];
+  const int item = a.sched[1 + blockIdx.x];
+  if (static_cast<int>(blockIdx.x) >= total) return;
+  const int n_qt = (a.max_seq_len + kBM - 1) / kBM;
+  const int seq = item / n_qt;
+  const int qt = item - seq * n_qt;
+  const SeqInfo si = seq_info(a, seq);
+  const int q0 = qt * kBM;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int lane = tid & 63;
+  const int hcol = wave * kDH;                     // this wave's head within the group
+
+  Ctx c;
+  c.s = si.s;
+  c.cs = si.cs;
+  c.L = si.L;
+  c.nc = si.nc;
+  c.first_tgt = si.L - si.m;
+  c.q0 = q0;
+  c.q_hi = min(q0 + kBM, si.L);
+  c.nkeys = c.nc + c.q_hi;
+  c.d = a.d_model;
+  c.col0 = blockIdx.z * HPB * kDH;
+  c.pmin_q = c.nc + min(q0, c.first_tgt);
+  c.pos_len = a.pos_len;
+  c.pos_center = a.pos_center;
+
+  // ---- reference time: min / max timestamp over every key of the block
+  // (queries are among them) ----
+  {
+    int64_t tmin = INT64_MAX, tmax = INT64_MIN;
+    for (int kk = tid; kk < c.nkeys; kk += NT) {
+      const int64_t t = kk < c.nc ? a.c_ts[c.cs + kk] : a.ts[c.s + kk - c.nc];
+      tmin = min(tmin, t);
+      tmax = max(tmax, t);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      tmin = min(tmin, static_cast<int64_t>(__shfl_xor(tmin, off, 64)));
+      tmax = max(tmax, static_cast<int64_t>(__shfl_xor(tmax, off, 64)));
+    }
+    if (lane == 0) {
+      red_min[wave] = tmin;
+      red_max[wave] = tmax;
+    }
+    // time tables in the base-2 domain
+    for (int i = tid; i < 64; i += NT) {
+      tb_lin[i] = -kLog2e * a.time_bias[min(i, a.nb - 1)];
+      if (i < 32) tb_clz[i] = -kLog2e * a.time_bias[min(31 - i, a.nb - 1)];  // clz i <=> bucket 31-i
     }
     __syncthreads();
-
-    // ---- S^T = K Q^T + bias (per 16-key x 16-query tile), SiLU, P.V ----
-    bf16x8 kf[2][2];
+    tmin = red_min[0];
+    tmax = red_max[0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        kf[kb][c] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const uint4*>(&sK[(kb * 16 + l16) * ROW + wave * kDH + c * 32 + 8 * g]));
-
-    bf16x8 pf[4];
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      uint32_t pk[4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x4 st = *reinterpret_cast<const f32x4*>(&sBias[((kb * 4 + qb) * 64 + lane) * 4]);
-        st = mfma_16x16x32(kf[kb][0], qf[qb][0], st);
-        st = mfma_16x16x32(kf[kb][1], qf[qb][1], st);
-        pk[kb * 2 + 0] = pack_bf16x2(silu_scaled(st[0], exp_scale), silu_scaled(st[1], exp_scale));
-        pk[kb * 2 + 1] = pack_bf16x2(silu_scaled(st[2], exp_scale), silu_scaled(st[3], exp_scale));
-      }
-      pf[qb] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    for (int w = 1; w < HPB; ++w) {
+      tmin = min(tmin, red_min[w]);
+      tmax = max(tmax, red_max[w]);
     }
+    c.tb_lo = static_cast<uint32_t>(tmin);
+    // |dt| + 1 must fit 31 bits for the 32-bit path
+    c.wide = (static_cast<uint64_t>(tmax) - static_cast<uint64_t>(tmin)) >= (1ull << 31) - 1;
+  }
 
+  const int n_kt = (c.nkeys + kBN - 1) / kBN;
+  // key tiles made only of targets that are not queries of this block are
+  // invisible to the whole block: a contiguous run [skip_a, skip_b)
+  const int skip_a = (c.nc + c.first_tgt + kBN - 1) / kBN;
+  const int skip_b = max((c.nc + q0) / kBN, skip_a);
+  const int n_skip = skip_b - skip_a;
+  const int n_steps = n_kt - n_skip;
+  auto tile_of = [=](int st) { return st < skip_a ? st : st + n_skip; };
+
+  // ---- per-slot query data of the bias builder ----
+  SlotQ<SPT> sq;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      // B operand: the same 8 keys as P's A operand (4g..4g+3, 16+4g..16+4g+3),
-      // column dt*16 + lane%16 of this head.
-      const uint16_t* vcol = &sV[wave * kDH + dt * 16 + l16];
-      u16x8 vr;
+  for (int i = 0; i < SPT; ++i) {
+    const int slot = tid + i * NT;
+    const int qi = q0 + (slot >> 8) * 32 + (slot & 31);
+    sq.qi[i] = qi;
+    sq.pq[i] = c.nc + min(qi, c.first_tgt);
+    const int64_t tq = a.ts[si.s + min(qi, si.L - 1)];
+    sq.tq[i] = tq;
+    sq.uq[i] = static_cast<uint32_t>(tq) - c.tb_lo;
+  }
+
+  // ---- Q fragments (B operand of S^T = K Q^T), prescaled by -alpha*log2(e) ----
+  // lane: query qb*32 + lane%32, dims 16c + 8(lane/32) .. +7 of this head
+  const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.q);
+  const float qscale = -a.alpha * kLog2e;
+  bf16x8 qf[2][4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int key = (i < 4) ? (4 * g + i) : (16 + 4 * g + (i - 4));
-        vr[i] = vcol[key * ROW];
-      }
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, vr);
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qi = q0 + qb * 32 + (lane & 31);
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) acc[qb][dt] = mfma_16x16x32(pf[qb], vf, acc[qb][dt]);
+    for (int cc = 0; cc < 4; ++cc) {
+      uint4 raw = make_uint4(0, 0, 0, 0);
+      if (qi < si.L)
+        raw = *reinterpret_cast<const uint4*>(Q + (si.s + qi) * c.d + c.col0 + hcol + cc * 16 +
+                                              8 * (lane >> 5));
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o[e] = pack_bf16x2(bf2f(w[e] & 0xffff) * qscale, bf2f(w[e] >> 16) * qscale);
+      qf[qb][cc] = __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
     }
   }
 
-  // ---- write AV (fp32): lane -> queries qb*16 + 4g + r, column dt*16 + lane%16 ----
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // wave-uniform DMA row bases of this head group: block key kk is row
+  // base + kk*d (own rows shifted back by the cache length)
+  const uint16_t* kbase_o = static_cast<const uint16_t*>(a.k) + (c.s - c.nc) * c.d + c.col0;
+  const uint16_t* vbase_o = static_cast<const uint16_t*>(a.v) + (c.s - c.nc) * c.d + c.col0;
+  const uint16_t* kbase_c = a.ck ? static_cast<const uint16_t*>(a.ck) + c.cs * c.d + c.col0 : kbase_o;
+  const uint16_t* vbase_c = a.cv ? static_cast<const uint16_t*>(a.cv) + c.cs * c.d + c.col0 : vbase_o;
+
+  // per-lane LDS offsets of the MFMA operands
+  const int g16 = lane >> 4;            // 16-lane group of the transposing reads
+  const int sl = lane & 15;
+  const int h2 = lane >> 5;             // half of the wave
+  // A operand K: row lane%32, dims 16c + 8*h2 of this head
+  const int koff = (lane & 31) * ROWB + (hcol + 8 * h2) * 2;
+  // B operand V (transposing read): source lane sl reads row 4*h2 + sl/4
+  // (+8, +16*kh), dims 32db + 16*(g16&1) + 4*(sl&3)
+  const int voff = (4 * h2 + (sl >> 2)) * ROWB + (hcol + 16 * (g16 & 1) + 4 * (sl & 3)) * 2;
+
+  // ---- prologue: key data of tiles 0 and 1, K/V and bias of tile 0 ----
+  load_keydata<HPB>(c, a.ts, a.c_ts, a.pos_bias, sD0, tile_of(0), wave, lane);
+  load_keydata<HPB>(c, a.ts, a.c_ts, a.pos_bias, sD1, tile_of(min(1, n_steps - 1)), wave, lane);
+  load_kv<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, sK0, sV0, tile_of(0), wave, lane);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  build_bias<HPB>(c, sq, sD0, sB0, tb_clz, tb_lin, a.nb, tile_of(0), tid);
+  __syncthreads();
+
+  // Step `st` computes key tile st from buffer st&1. Meanwhile it loads the
+  // K/V rows of tile st+1 and the key data of tile st+2 by DMA into the other
+  // buffers, and builds the bias of tile st+1 from the key data that arrived
+  // a step earlier. Unrolled by two so that every buffer is a fixed LDS object.
+#define HSTU_ATTN_STEP(CUR_K, CUR_V, CUR_B, CUR_D, NXT_K, NXT_V, NXT_B, NXT_D)                    \
+  {                                                                                              \
+    const int nxt = st + 1;                                                                      \
+    f32x16 sc[2];                                                                                \
+    scores<HPB>(CUR_K, CUR_B, qf, sc, koff, lane);                                               \
+    if (nxt < n_steps) {                                                                         \
+      load_kv<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, NXT_K, NXT_V, tile_of(nxt), wave, lane); \
+      if (st + 2 < n_steps)                                                                      \
+        load_keydata<HPB>(c, a.ts, a.c_ts, a.pos_bias, CUR_D, tile_of(st + 2), wave, lane);      \
+      build_bias<HPB>(c, sq, NXT_D, NXT_B, tb_clz, tb_lin, a.nb, tile_of(nxt), tid);             \
+    }                                                                                            \
+    bf16x8 vf[2][2];                                                                             \
+    load_v<HPB>(CUR_V, voff, vf);                                                                \
+    bf16x8 pa[2];                                                                                \
+    silu_pack(sc[0], pa);                                                                        \
+    pv(pa, vf, acc[0]);                                                                          \
+    silu_pack(sc[1], pa);                                                                        \
+    pv(pa, vf, acc[1]);                                                                          \
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                             \
+    __syncthreads();                                                                             \
+  }
+  for (int st = 0; st < n_steps; ++st) {
+    HSTU_ATTN_STEP(sK0, sV0, sB0, sD0, sK1, sV1, sB1, sD1)
+    if (++st >= n_steps) break;
+    HSTU_ATTN_STEP(sK1, sV1, sB1, sD1, sK0, sV0, sB0, sD0)
+  }
+#undef HSTU_ATTN_STEP
+
+  // ---- AV = -ln2 * O: lane -> query qb*32 + 8(r/4) + 4*h2 + r%4, dim 32db + lane%32 ----
   float* __restrict__ out = a.av;
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb)
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int qi = q0 + qb * 16 + 4 * g + r;
+    for (int r = 0; r < 16; ++r) {
+      const int qi = q0 + qb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
       if (qi < si.L) {
-        float* row = out + (si.s + qi) * d + h_col + l16;
+        float* row = out + (si.s + qi) * c.d + c.col0 + hcol + (lane & 31);
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) row[dt * 16] = acc[qb][dt][r] * a.alpha;
+        for (int db = 0; db < 2; ++db) row[db * 32] = -kLn2 * acc[qb][db][r];
       }
     }
 }
@@ -290,10 +618,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
     const bool cache = kk < si.nc;
     const int j = kk - si.nc;
     const bool vis = qvalid && (cache || ((j <= qi) && (j < first_tgt || j == qi)));
+    if (!vis) continue;
     const int64_t row = cache ? (si.cs + kk) : (si.s + j);
     const float* kr = (cache ? CK : K) + row * d + h * DH;
     const float* vr = (cache ? CV : V) + row * d + h * DH;
-    if (!vis) continue;
     float dot = 0.0f;
 #pragma unroll
     for (int c = 0; c < DH; ++c) dot = fmaf(qv[c], kr[c], dot);
@@ -301,7 +629,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
     const int64_t tk = cache ? a.c_ts[si.cs + kk] : a.ts[si.s + j];
     int pidx = pq - pk + a.pos_center;
     pidx = pidx < 0 ? 0 : (pidx >= a.pos_len ? a.pos_len - 1 : pidx);
-    const float s = a.alpha * dot + a.pos_bias[pidx] + a.time_bias[time_bucket(tq - tk, a.nb)];
+    const float s = a.alpha * dot + a.pos_bias[pidx] + a.time_bias[time_bucket64(tq - tk, a.nb)];
     const float w = s / (1.0f + expf(-s));
 #pragma unroll
     for (int c = 0; c < DH; ++c) acc[c] = fmaf(w, vr[c], acc[c]);
@@ -314,13 +642,23 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 
 }  // namespace
 
+size_t attn_workspace_bytes(int num_seqs, int max_seq_len) {
+  const int64_t n_qt = (static_cast<int64_t>(max_seq_len) + kBM - 1) / kBM;
+  return static_cast<size_t>(1 + static_cast<int64_t>(num_seqs) * n_qt) * sizeof(int);
+}
+
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   const int n_qt = (a.max_seq_len + kBM - 1) / kBM;
   if (a.num_seqs == 0 || n_qt == 0) return hipSuccess;
+  const int cmax = min((a.max_seq_len + a.max_cache_len) / kBN + 2, kSchedBuckets - 1);
+  hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, s, a, n_qt, cmax);
   int hpb = 1;
   for (int c : {8, 4, 2, 1})
-    if (a.num_heads % c == 0) { hpb = c; break; }
-  dim3 grid(a.num_seqs, n_qt, a.num_heads / hpb);
+    if (a.num_heads % c == 0) {
+      hpb = c;
+      break;
+    }
+  dim3 grid(a.num_seqs * n_qt, a.num_heads / hpb);
   switch (hpb) {
     case 8: hipLaunchKernelGGL(attn_bf16_kernel<8>, grid, dim3(512), 0, s, a); break;
     case 4: hipLaunchKernelGGL(attn_bf16_kernel<4>, grid, dim3(256), 0, s, a); break;

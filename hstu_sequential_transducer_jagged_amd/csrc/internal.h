@@ -33,8 +33,11 @@ struct AttnArgs {
   int num_seqs;
   int max_seq_len;
   int max_cache_len;
+  int* sched;                // bf16 path: work list built by the scheduling pass
 };
 
+// Workspace bytes of the bf16 attention (its work list).
+size_t attn_workspace_bytes(int num_seqs, int max_seq_len);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
 

@@ -26,7 +26,8 @@ HSTU_E_DATA = -5
 HSTU_F32 = 0
 HSTU_BF16 = 1
 
-EXPORTS = ("hstu_abi_version", "hstu_last_error", "hstu_proj_fwd", "hstu_attn_fwd",
+EXPORTS = ("hstu_abi_version", "hstu_last_error", "hstu_proj_fwd", "hstu_attn_workspace_size",
+           "hstu_attn_fwd",
            "hstu_norm_gate_fwd", "hstu_out_fwd", "hstu_layer_workspace_size",
            "hstu_layer_fwd", "hstu_embed_fwd", "hstu_check_inputs")
 
@@ -82,10 +83,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "hstu_abi_version": (ctypes.c_int, []),
         "hstu_last_error": (ctypes.c_char_p, []),
         "hstu_proj_fwd": (ctypes.c_int, [P, P, i64, P, P, P, P, P, P]),
-        "hstu_attn_fwd": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P]),
+        "hstu_attn_workspace_size": (ctypes.c_size_t, [P, P]),
+        "hstu_attn_fwd": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "hstu_norm_gate_fwd": (ctypes.c_int, [P, i64, P, P, P, P, P, P]),
         "hstu_out_fwd": (ctypes.c_int, [P, i64, P, P, P, P, P, P]),
-        "hstu_layer_workspace_size": (ctypes.c_size_t, [P, i64, i32]),
+        "hstu_layer_workspace_size": (ctypes.c_size_t, [P, P]),
         "hstu_layer_fwd": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "hstu_embed_fwd": (ctypes.c_int, [i64, i32, i32, P, i64, P, i32, P, P, P, P]),
         "hstu_check_inputs": (ctypes.c_int, [P, P, P, P]),
@@ -157,9 +159,15 @@ def hstu_proj_fwd(desc, params, T, x, u, v, q, k, stream=None) -> None:
                                 ptr(q), ptr(k), stream if stream is not None else current_stream()))
 
 
-def hstu_attn_fwd(desc, jagged, cache, q, k, v, pos_bias, time_bias, av, stream=None) -> None:
+def hstu_attn_workspace_size(desc, jagged) -> int:
+    return int(load().hstu_attn_workspace_size(_ref(desc), _ref(jagged)))
+
+
+def hstu_attn_fwd(desc, jagged, cache, q, k, v, pos_bias, time_bias, av, workspace,
+                  stream=None) -> None:
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().hstu_attn_fwd(_ref(desc), _ref(jagged), _ref(cache), ptr(q), ptr(k), ptr(v),
-                                ptr(pos_bias), ptr(time_bias), ptr(av),
+                                ptr(pos_bias), ptr(time_bias), ptr(av), ptr(workspace), nbytes,
                                 stream if stream is not None else current_stream()))
 
 
@@ -173,8 +181,14 @@ def hstu_out_fwd(desc, T, g, x, w2, b2, y, stream=None) -> None:
                                stream if stream is not None else current_stream()))
 
 
-def hstu_layer_workspace_size(desc, T, num_seqs) -> int:
-    return int(load().hstu_layer_workspace_size(_ref(desc), int(T), int(num_seqs)))
+def hstu_layer_workspace_size(desc, jagged) -> int:
+    return int(load().hstu_layer_workspace_size(_ref(desc), _ref(jagged)))
+
+
+def workspace_tensor(nbytes: int, device="cuda"):
+    """Device buffer for a workspace (torch allocations are 256-byte aligned)."""
+    import torch
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 def hstu_layer_fwd(desc, params, jagged, cache, x, y, k_out, v_out, workspace,

@@ -79,10 +79,9 @@ class DeviceWorkload:
         torch = _torch()
         return torch.empty((max(T, 1), self.w.d_model), dtype=self.act, device=self.device)
 
-    def workspace(self, T: int, num_seqs: int):
-        torch = _torch()
-        n = hstu.hstu_layer_workspace_size(self.desc, T, num_seqs)
-        return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+    def workspace(self, jagged=None):
+        return hstu.workspace_tensor(hstu.hstu_layer_workspace_size(self.desc, jagged or self.jagged),
+                                     self.device)
 
 
 def layer_forward(dw: DeviceWorkload, x, layer: int = 0, y=None, workspace=None, jagged=None,
@@ -90,7 +89,7 @@ def layer_forward(dw: DeviceWorkload, x, layer: int = 0, y=None, workspace=None,
     jagged = jagged or dw.jagged
     T = jagged.total_tokens
     y = dw.empty_act(T) if y is None else y
-    ws = dw.workspace(T, jagged.num_seqs) if workspace is None else workspace
+    ws = dw.workspace(jagged) if workspace is None else workspace
     hstu.hstu_layer_fwd(dw.desc, dw.layers[layer].params, jagged, cache, x, y, k_out, v_out, ws)
     return y
 
@@ -107,7 +106,7 @@ def stack_forward(dw: DeviceWorkload, x=None, return_all: bool = False):
     """Embedding (when the workload has tables) then every layer in turn."""
     T = dw.w.total_tokens
     h = embed_forward(dw) if x is None and dw.x is None else (dw.x if x is None else x)
-    ws = dw.workspace(T, dw.w.num_seqs)
+    ws = dw.workspace()
     outs = [h]
     for l in range(len(dw.layers)):
         y = dw.empty_act(T)
@@ -156,7 +155,7 @@ def ranking_forward(dw: DeviceWorkload, plan: RankingPlan, keep_history: bool = 
     L = len(dw.layers)
     kc = [dw.empty_act(Th) for _ in range(L)]
     vc = [dw.empty_act(Th) for _ in range(L)]
-    ws = dw.workspace(Th, w.num_seqs)
+    ws = dw.workspace()
     h = dw.x
     hist = [h]
     for l in range(L):
@@ -179,7 +178,7 @@ def ranking_forward(dw: DeviceWorkload, plan: RankingPlan, keep_history: bool = 
         jag = hstu.Jagged(len(offs) - 1, mlen, n, hstu.ptr(offs_d),
                           hstu.ptr(cts) + 8 * start, hstu.ptr(tgt_d))
         keep.append((offs_d, tgt_d))
-        wsc = dw.workspace(n, len(offs) - 1)
+        wsc = dw.workspace(jag)
         xin = cx[start:start + n]
         for l in range(L):
             y = out[start:start + n] if l == L - 1 else dw.empty_act(n)

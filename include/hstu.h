@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 1
+#define HSTU_ABI_VERSION 2
 
 typedef enum {
   HSTU_OK = 0,
@@ -130,21 +130,30 @@ const char *hstu_last_error(void);
 int hstu_proj_fwd(const hstu_layer_desc *desc, const hstu_layer_params *params, int64_t T,
                   const void *x, void *u, void *v, void *q, void *k, void *stream);
 
+/* Workspace bytes hstu_attn_fwd needs for this batch (bf16: the work list
+ * of its scheduling pass, 4 * (1 + num_seqs * ceil(max_seq_len / 64)) bytes
+ * rounded up to 256; f32: 0). */
+size_t hstu_attn_workspace_size(const hstu_layer_desc *desc, const hstu_jagged *jagged);
+
 /* Spatial aggregation, §2.1 second equation, with the visibility, position
  * and bias rules above:
  *   av[i, h*dh:(h+1)*dh] = sum_{j visible} SiLU(alpha q_i.k_j + rab(i, j)) v_j
  * q, k, v [T, d] (dtype, own tokens of `jagged`); cache may be NULL;
  * pos_bias [pos_table_len], time_bias [num_time_buckets] (fp32);
- * av [T, d] fp32 output. Every visible position difference must lie in
+ * av [T, d] fp32 output. workspace: device, 256-byte aligned, at least
+ * hstu_attn_workspace_size() bytes (may be NULL when that is 0); its
+ * contents are scratch. Every visible position difference must lie in
  * the table: per sequence, C_b + L_b - 1 <= n_max - 1 without targets and
  * C_b + (L_b - m_b) <= n_max - 1 with m_b > 0 targets (C_b = cache length).
  * Without num_targets the call checks max_seq_len + cache max_len <= n_max
  * (HSTU_E_INVAL); with targets the bound depends on device data and only
  * hstu_check_inputs() checks it (the kernels clamp table indices, so a
- * violation never reads out of bounds). */
+ * violation never reads out of bounds). Lengths above max_seq_len are a
+ * contract violation: their query tiles past max_seq_len are not computed. */
 int hstu_attn_fwd(const hstu_layer_desc *desc, const hstu_jagged *jagged,
                   const hstu_kv_cache *cache, const void *q, const void *k, const void *v,
-                  const float *pos_bias, const float *time_bias, float *av, void *stream);
+                  const float *pos_bias, const float *time_bias, float *av, void *workspace,
+                  size_t workspace_bytes, void *stream);
 
 /* Pointwise transformation, first half (§2.1 third equation and the block
  * diagram: LayerNorm, then the product with U):
@@ -159,8 +168,9 @@ int hstu_norm_gate_fwd(const hstu_layer_desc *desc, int64_t T, const float *av, 
 int hstu_out_fwd(const hstu_layer_desc *desc, int64_t T, const void *g, const void *x,
                  const void *w2, const float *b2, void *y, void *stream);
 
-/* Workspace bytes hstu_layer_fwd needs for T tokens. */
-size_t hstu_layer_workspace_size(const hstu_layer_desc *desc, int64_t T, int32_t num_seqs);
+/* Workspace bytes hstu_layer_fwd needs for this batch (host fields of
+ * `jagged` only). */
+size_t hstu_layer_workspace_size(const hstu_layer_desc *desc, const hstu_jagged *jagged);
 
 /* One full layer: projection -> attention -> norm/gate -> f2 + residual.
  * x, y [T, d] dtype (y must not alias x). k_out / v_out: NULL, or [T, d]

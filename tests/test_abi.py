@@ -35,7 +35,7 @@ def test_header_declares_the_binding_exports():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.hstu_abi_version() == 1
+    assert lib.hstu_abi_version() == 2
 
 
 def _desc(**kw):
@@ -52,7 +52,8 @@ def _attn(lib, desc, jag, cache=None, ptrs=FAKE):
     return lib.hstu_attn_fwd(ctypes.byref(desc) if desc else None,
                              ctypes.byref(jag) if jag else None,
                              ctypes.byref(cache) if cache else None,
-                             P(ptrs), P(ptrs), P(ptrs), P(ptrs), P(ptrs), P(ptrs), None)
+                             P(ptrs), P(ptrs), P(ptrs), P(ptrs), P(ptrs), P(ptrs),
+                             P(FAKE), 1 << 20, None)
 
 
 def _jag(B=2, T=10, mx=6):
@@ -111,8 +112,16 @@ def test_empty_batches_return_ok_without_device(lib):
 
 def test_layer_workspace_checks(lib):
     d = _desc()
-    need = lib.hstu_layer_workspace_size(ctypes.byref(d), 10, 2)
-    assert need == 4 * 10240 + 20480
+    need = lib.hstu_layer_workspace_size(ctypes.byref(d), ctypes.byref(_jag()))
+    attn = lib.hstu_attn_workspace_size(ctypes.byref(d), ctypes.byref(_jag()))
+    assert attn == 256            # 4 * (1 + 2 sequences * 1 tile), rounded to 256
+    assert need == 4 * 10240 + 20480 + attn
+    f = hstu.make_desc(64, 2, hstu.HSTU_F32, 255)
+    assert lib.hstu_attn_workspace_size(ctypes.byref(f), ctypes.byref(_jag())) == 0
+    P = ctypes.c_void_p
+    st = lib.hstu_attn_fwd(ctypes.byref(d), ctypes.byref(_jag()), None, P(FAKE), P(FAKE), P(FAKE),
+                           P(FAKE), P(FAKE), P(FAKE), P(FAKE), attn - 1, None)
+    assert st == hstu.HSTU_E_WORKSPACE
     params = hstu.LayerParams(FAKE, None, FAKE, None, None, None, FAKE, FAKE)
     P = ctypes.c_void_p
     st = lib.hstu_layer_fwd(ctypes.byref(d), ctypes.byref(params), ctypes.byref(_jag()), None,
@@ -128,7 +137,7 @@ def test_layer_workspace_checks(lib):
 
 def test_binding_raises_with_message(lib):
     with pytest.raises(hstu.HstuError) as e:
-        hstu.hstu_attn_fwd(None, _jag(), None, None, None, None, None, None, None, stream=0)
+        hstu.hstu_attn_fwd(None, _jag(), None, None, None, None, None, None, None, None, stream=0)
     assert e.value.status == hstu.HSTU_E_INVAL
 
 

@@ -40,7 +40,8 @@ def _run_attn(hs, w, dtype, q, k, v, num_targets=None, cache=None, alpha=1.0):
     pb, tb = f32(p.pos_bias), f32(p.time_bias)
     av = torch.full((max(w.total_tokens, 1), w.d_model), float("nan"), dtype=torch.float32,
                     device="cuda")
-    hs.hstu_attn_fwd(desc, jag, cch, qd, kd, vd, pb, tb, av)
+    ws = hs.workspace_tensor(hs.hstu_attn_workspace_size(desc, jag))
+    hs.hstu_attn_fwd(desc, jag, cch, qd, kd, vd, pb, tb, av, ws)
     torch.cuda.synchronize()
     del keep
     return to_np(av)[:w.total_tokens]
@@ -232,7 +233,7 @@ def test_zero_tokens_and_empty_batch(gpu_lib):
     offs = i64([0, 0, 0])
     ts = i64([0])
     jag = hs.make_jagged(offs, ts, 0)
-    hs.hstu_attn_fwd(desc, jag, None, None, None, None, None, None, None)
+    hs.hstu_attn_fwd(desc, jag, None, None, None, None, None, None, None, None)
     hs.hstu_proj_fwd(desc, hs.make_params(offs, None, None, None, None, None, None, None), 0,
                      None, None, None, None, None)
 
