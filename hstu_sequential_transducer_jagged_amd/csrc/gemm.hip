@@ -7,33 +7,54 @@
 //         equation plus the block diagram's skip connection).
 //
 // Both are C[M, N] = A[M, K] B[N, K]^T with A and B row-major and K
-// contiguous, which is exactly the operand layout of
-// v_mfma_f32_16x16x32_bf16 (lane = row, 8 consecutive k), so tiles are
-// staged through LDS unchanged. Block tile 128 x 128, K step 32, four waves
-// of 64 x 64; the next K step's global loads are issued before the current
-// step's MFMAs.
+// contiguous, which is the operand layout of v_mfma_f32_32x32x16_bf16
+// (lane = row, 8 consecutive k), so tiles are staged through LDS unchanged
+// apart from a bank swizzle. The next K step's global loads are issued
+// before the current step's MFMAs (register staging, double-buffered LDS).
 #include "common.h"
 #include "internal.h"
 
 namespace hstu {
 namespace {
 
-constexpr int kTM = 128;
-constexpr int kTN = 128;
-constexpr int kTK = 32;
-constexpr int kLdsRow = kTK + 8;   // bf16 per LDS row (+16 B pad)
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ float silu_exact(float z) { return z / (1.0f + __expf(-z)); }
+// Block tile: 256 rows (M) x 128 output columns (N), K staged 32 at a time.
+// Four waves, each 128 rows x 64 columns; the product is formed transposed,
+// C^T[n][m] = sum_k W[n][k] X[m][k] (A operand = W rows, B operand = X rows),
+// so that a lane's accumulator holds 4 consecutive output columns of one row
+// and the epilogue stores 8-byte bf16 quads.
+constexpr int kGM = 256;
+constexpr int kGN = 128;
+constexpr int kGK = 32;
+constexpr int kRowB = kGK * 2;   // 64-byte LDS rows
 
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16-byte chunk c (0..3) of LDS row r: XOR-swizzled so that the 8 rows one
+// ds_read_b128 cycle serves fall on distinct banks.
+__device__ __forceinline__ int swz(int r, int c) { return r * kRowB + ((c ^ ((r >> 1) & 3)) << 4); }
+
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
+
+// Epilogues receive one row m and 4 consecutive columns n..n+3.
 struct ProjEpi {
   const float* bias;
   uint16_t* out[4];
-  int K;
-  __device__ __forceinline__ void operator()(int64_t m, int n, float acc) const {
-    const float z = acc + (bias ? bias[n] : 0.0f);
+  int K;   // d_model: width of each of U, V, Q, K
+  __device__ __forceinline__ void operator()(int64_t m, int n, const float (&v)[4]) const {
+    float z[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z[e] = silu_fast(v[e] + (bias ? bias[n + e] : 0.0f));
     const int chunk = n / K;
-    const int c = n - chunk * K;
-    out[chunk][m * K + c] = f2bf(silu_exact(z));
+    uint2 o;
+    o.x = pack_bf16x2(z[0], z[1]);
+    o.y = pack_bf16x2(z[2], z[3]);
+    *reinterpret_cast<uint2*>(out[chunk] + m * K + (n - chunk * K)) = o;
   }
 };
 
@@ -42,95 +63,134 @@ struct OutEpi {
   const uint16_t* x;
   uint16_t* y;
   int K;
-  __device__ __forceinline__ void operator()(int64_t m, int n, float acc) const {
-    const float r = acc + (bias ? bias[n] : 0.0f) + bf2f(x[m * K + n]);
-    y[m * K + n] = f2bf(r);
+  __device__ __forceinline__ void operator()(int64_t m, int n, const float (&v)[4]) const {
+    const uint2 xr = *reinterpret_cast<const uint2*>(x + m * K + n);
+    const float xv[4] = {bf2f(xr.x & 0xffff), bf2f(xr.x >> 16), bf2f(xr.y & 0xffff), bf2f(xr.y >> 16)};
+    float z[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z[e] = v[e] + (bias ? bias[n + e] : 0.0f) + xv[e];
+    uint2 o;
+    o.x = pack_bf16x2(z[0], z[1]);
+    o.y = pack_bf16x2(z[2], z[3]);
+    *reinterpret_cast<uint2*>(y + m * K + n) = o;
   }
 };
 
+// X [M, K] row-major, W [N, K] row-major (nn.Linear), K % 32 == 0,
+// N % 4 == 0. Grid: 8 * ceil(nm / 8) * nn workgroups (nm = ceil(M/256),
+// nn = N/128); workgroup id -> XCD id % 8 (round-robin dispatch); XCD x
+// takes row blocks x, x+8, ... and sweeps all nn column tiles of one row
+// block before the next, so each X row block is read from HBM once and W
+// stays in that XCD's L2.
 template <class Epi>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
-                                                        const uint16_t* __restrict__ B,
-                                                        int64_t M, int N, int K, Epi epi) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[kTM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[kTN * kLdsRow];
+__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __restrict__ X,
+                                                           const uint16_t* __restrict__ W,
+                                                           int64_t M, int N, int K, int nm, int nn,
+                                                           Epi epi) {
+  __shared__ __attribute__((aligned(16))) uint8_t sX[2][kGM * kRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t sW[2][kGN * kRowB];
+
+  const int id = blockIdx.x;
+  const int xcd = id & 7;
+  const int slot = id >> 3;
+  const int mb = (slot / nn) * 8 + xcd;
+  const int nb = slot - (slot / nn) * nn;
+  if (mb >= nm) return;
+  const int64_t m0 = static_cast<int64_t>(mb) * kGM;
+  const int n0 = nb * kGN;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int g = lane >> 4;
-  const int l16 = lane & 15;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * kTM;
-  const int n0 = blockIdx.y * kTN;
+  const int wm = wave & 1;         // 128-row half
+  const int wn = wave >> 1;        // 64-column half
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
 
-  // each thread stages two 16-byte chunks of A and two of B per K step
-  // chunk c in [0, 512): row c/4, k offset (c%4)*8
-  uint4 ra[2], rb[2];
-  auto load = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + i * 256;
-      const int r = c >> 2;
-      const int kc = (c & 3) * 8;
-      const int64_t am = m0 + r;
-      ra[i] = am < M ? *reinterpret_cast<const uint4*>(A + am * K + k0 + kc) : make_uint4(0, 0, 0, 0);
-      const int bn = n0 + r;
-      rb[i] = bn < N ? *reinterpret_cast<const uint4*>(B + static_cast<int64_t>(bn) * K + k0 + kc)
-                     : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store = [&]() {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + i * 256;
-      const int r = c >> 2;
-      const int kc = (c & 3) * 8;
-      *reinterpret_cast<uint4*>(&sA[r * kLdsRow + kc]) = ra[i];
-      *reinterpret_cast<uint4*>(&sB[r * kLdsRow + kc]) = rb[i];
-    }
-  };
-
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  load(0);
-  for (int k0 = 0; k0 < K; k0 += kTK) {
-    __syncthreads();
-    store();
-    __syncthreads();
-    if (k0 + kTK < K) load(k0 + kTK);
-    bf16x8 af[4], bfr[4];
+  // staging: X tile 256 rows x 4 chunks (4 per thread), W tile 128 rows x 4 chunks (2 per thread)
+  uint4 rx[4], rw[2];
+  auto gload = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      af[i] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const uint4*>(&sA[(wm * 64 + i * 16 + l16) * kLdsRow + 8 * g]));
-      bfr[i] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const uint4*>(&sB[(wn * 64 + i * 16 + l16) * kLdsRow + 8 * g]));
+      const int c = tid + i * 256;
+      const int r = c >> 2;
+      const int64_t gm = m0 + r;
+      rx[i] = gm < M ? *reinterpret_cast<const uint4*>(X + gm * K + k0 + (c & 3) * 8)
+                     : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + i * 256;
+      const int r = c >> 2;
+      rw[i] = n0 + r < N ? *reinterpret_cast<const uint4*>(W + static_cast<int64_t>(n0 + r) * K + k0 + (c & 3) * 8)
+                         : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto lstore = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(af[i], bfr[j], acc[i][j]);
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + i * 256;
+      *reinterpret_cast<uint4*>(&sX[buf][swz(c >> 2, c & 3)]) = rx[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + i * 256;
+      *reinterpret_cast<uint4*>(&sW[buf][swz(c >> 2, c & 3)]) = rw[i];
+    }
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nsteps = K / kGK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nsteps) gload((st + 1) * kGK);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {     // two 16-deep MFMA steps
+      const int c = 2 * kk + h;          // 16-byte chunk of this lane's 8 k values
+      bf16x8 a[2], b[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                              &sW[buf][swz(wn * 64 + i * 32 + l32, c)]));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                              &sX[buf][swz(wm * 128 + j * 32 + l32, c)]));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+    }
+    if (st + 1 < nsteps) lstore(buf ^ 1);
+    __syncthreads();
   }
 
-  // C layout: lane holds rows 4g + r, column lane%16 of each 16 x 16 tile
+  // C^T accumulator: lane -> m = j*32 + lane%32, n = i*32 + 8*(r/4) + 4*h + r%4
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < 4; ++j) {
+    const int64_t m = m0 + wm * 128 + j * 32 + l32;
+    if (m >= M) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn * 64 + j * 16 + l16;
-      if (n >= N) continue;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t m = m0 + wm * 64 + i * 16 + 4 * g + r;
-        if (m < M) epi(m, n, acc[i][j][r]);
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * 64 + i * 32 + 8 * g + 4 * h;
+        if (n >= N) continue;
+        const float v[4] = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                            acc[i][j][4 * g + 3]};
+        epi(m, n, v);
       }
-    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -183,28 +243,31 @@ struct OutEpiF32 {
 
 }  // namespace
 
+template <class Epi>
+hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, int64_t M, int N, int K, Epi epi,
+                            hipStream_t s) {
+  const int nm = static_cast<int>((M + kGM - 1) / kGM);
+  const int nn = (N + kGN - 1) / kGN;
+  const int grid = 8 * ((nm + 7) / 8) * nn;
+  hipLaunchKernelGGL(gemm_bf16_kernel<Epi>, dim3(grid), dim3(256), 0, s, x, w, M, N, K, nm, nn, epi);
+  return hipGetLastError();
+}
+
 hipError_t launch_proj_bf16(const ProjArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
-  const int N = 4 * a.K;
   ProjEpi epi{a.bias,
               {static_cast<uint16_t*>(a.out[0]), static_cast<uint16_t*>(a.out[1]),
                static_cast<uint16_t*>(a.out[2]), static_cast<uint16_t*>(a.out[3])},
               a.K};
-  dim3 grid(static_cast<unsigned>((a.M + kTM - 1) / kTM), (N + kTN - 1) / kTN);
-  hipLaunchKernelGGL(gemm_bf16_kernel<ProjEpi>, grid, dim3(256), 0, s,
-                     static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.w), a.M,
-                     N, a.K, epi);
-  return hipGetLastError();
+  return launch_gemm_bf16(static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.w), a.M,
+                          4 * a.K, a.K, epi, s);
 }
 
 hipError_t launch_out_bf16(const OutArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
   OutEpi epi{a.bias, static_cast<const uint16_t*>(a.x), static_cast<uint16_t*>(a.y), a.K};
-  dim3 grid(static_cast<unsigned>((a.M + kTM - 1) / kTM), (a.K + kTN - 1) / kTN);
-  hipLaunchKernelGGL(gemm_bf16_kernel<OutEpi>, grid, dim3(256), 0, s,
-                     static_cast<const uint16_t*>(a.g), static_cast<const uint16_t*>(a.w), a.M,
-                     a.K, a.K, epi);
-  return hipGetLastError();
+  return launch_gemm_bf16(static_cast<const uint16_t*>(a.g), static_cast<const uint16_t*>(a.w), a.M,
+                          a.K, a.K, epi, s);
 }
 
 hipError_t launch_proj_f32(const ProjArgs& a, hipStream_t s) {
