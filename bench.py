@@ -39,7 +39,27 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
                     help="approximate CPU seconds for the oracle sample")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="first run a plain elementwise copy of known size (512 MiB read, "
+                         "512 MiB written) so that HBM counters can be scaled against it")
     return ap.parse_args()
+
+
+COPY_CALIB_BYTES = 512 << 20
+
+
+def copy_calibration(torch):
+    """torch.neg over a 512 MiB bf16 buffer into another: a streaming kernel
+    whose HBM traffic is known exactly (each byte read once, written once)."""
+    n = COPY_CALIB_BYTES // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    return {"kernel": "torch.neg bf16", "bytes_read": COPY_CALIB_BYTES,
+            "bytes_written": COPY_CALIB_BYTES}
 
 
 def visible_pairs(offsets):
@@ -122,22 +142,24 @@ def main():
     sh = stream.cuda_stream
 
     def step(ev=None):
+        rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
+        rec(0)
         hstu.hstu_proj_fwd(desc, lay.params, T, x, u, v, q, k, sh)
-        if ev is not None:
-            ev[0].record(stream)
+        rec(1)
         hstu.hstu_attn_fwd(desc, jag, None, q, k, v, lay.pos_bias, lay.time_bias, av, attn_ws, sh)
-        if ev is not None:
-            ev[1].record(stream)
+        rec(2)
         hstu.hstu_norm_gate_fwd(desc, T, av, u, lay.gamma, lay.beta, g, sh)
+        rec(3)
         hstu.hstu_out_fwd(desc, T, g, x, lay.w2, lay.b2, y, sh)
+        rec(4)
 
+    calib = copy_calibration(torch) if args.copy_calib else None
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -146,7 +168,13 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / K
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    # per-launch durations (ms) of each kernel, one sample per timed step
+    per = {name: np.array([e[j].elapsed_time(e[j + 1]) for e in evs])
+           for j, name in enumerate(["proj", "attn", "norm_gate", "out"])}
+    steps_ms = np.array([e[0].elapsed_time(e[4]) for e in evs])
+    attn_ms = float(np.mean(per["attn"]))
+    pct = lambda a: {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+                     "p90": float(np.percentile(a, 90))}
 
     # cross-check: the same layer through the single hstu_layer_fwd entry point
     ws = dw.workspace()
@@ -163,6 +191,21 @@ def main():
     same = bool(torch.equal(y, y2))
 
     attn_tflops = attn_flop / (attn_ms * 1e-3) / 1e12
+    esz = 2
+    proj_flop, out_flop = 8.0 * T * d * d, 2.0 * T * d * d
+    ng_bytes = T * d * (4 + esz + esz)        # read AV (fp32) and U, write G
+    kernels = {
+        "proj": {"ms": pct(per["proj"]), "tflops": proj_flop / np.mean(per["proj"]) / 1e9,
+                 "pct_bf16_peak": 100 * proj_flop / np.mean(per["proj"]) / 1e9 / PEAK_BF16_TFLOPS},
+        "attn": {"ms": pct(per["attn"]), "tflops": attn_tflops,
+                 "pct_bf16_peak": 100 * attn_tflops / PEAK_BF16_TFLOPS},
+        "norm_gate": {"ms": pct(per["norm_gate"]),
+                      "gbs": ng_bytes / np.mean(per["norm_gate"]) / 1e6,
+                      "pct_hbm_peak": 100 * ng_bytes / np.mean(per["norm_gate"]) / 1e6 / PEAK_HBM_GBS},
+        "out": {"ms": pct(per["out"]), "tflops": out_flop / np.mean(per["out"]) / 1e9,
+                "pct_bf16_peak": 100 * out_flop / np.mean(per["out"]) / 1e9 / PEAK_BF16_TFLOPS},
+        "step": {"ms": pct(steps_ms)},
+    }
     src = os.path.join(ROOT, "hstu_sequential_transducer_jagged_amd", "csrc", "attn.hip")
     rec = {
         "metric": METRIC,
@@ -190,7 +233,10 @@ def main():
         "attn_pct_bf16_peak": 100.0 * attn_tflops / PEAK_BF16_TFLOPS,
         "hstu_layer_fwd_ms": layer_ms,
         "hstu_layer_fwd_matches_steps": same,
+        "kernels": kernels,
     }
+    if calib is not None:
+        rec["copy_calib"] = calib
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
     print(json.dumps(rec), flush=True)

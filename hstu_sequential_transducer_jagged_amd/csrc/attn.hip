@@ -334,11 +334,13 @@ __global__ __launch_bounds__(1024) void attn_schedule_kernel(AttnArgs a, int n_q
   const int tid = threadIdx.x;
   for (int i = tid; i <= cmax; i += 1024) cnt[i] = 0;
   __syncthreads();
-  for (int b = tid; b < a.num_seqs; b += 1024) {
+  // One (sequence, tile) item per thread and pass. Tiles past max_seq_len (a
+  // violated contract) are not scheduled.
+  const int items = a.num_seqs * n_qt;
+  for (int i = tid; i < items; i += 1024) {
+    const int b = i / n_qt, t = i - b * n_qt;
     const SeqInfo si = seq_info(a, b);
-    // tiles past max_seq_len (a violated contract) are not scheduled
-    const int nt = min((si.L + kBM - 1) / kBM, n_qt);
-    for (int t = 0; t < nt; ++t) atomicAdd(&cnt[min(tile_steps(si, t), cmax)], 1);
+    if (t * kBM < si.L) atomicAdd(&cnt[min(tile_steps(si, t), cmax)], 1);
   }
   __syncthreads();
   // exclusive scan in descending cost order: start(c) = items costing more than c
@@ -364,12 +366,12 @@ __global__ __launch_bounds__(1024) void attn_schedule_kernel(AttnArgs a, int n_q
     }
   if (tid == 1023) a.sched[0] = part[1023];
   __syncthreads();
-  for (int b = tid; b < a.num_seqs; b += 1024) {
+  for (int i = tid; i < items; i += 1024) {
+    const int b = i / n_qt, t = i - b * n_qt;
     const SeqInfo si = seq_info(a, b);
-    const int nt = min((si.L + kBM - 1) / kBM, n_qt);
-    for (int t = 0; t < nt; ++t) {
+    if (t * kBM < si.L) {
       const int pos = atomicAdd(&cnt[min(tile_steps(si, t), cmax)], 1);
-      a.sched[1 + pos] = b * n_qt + t;
+      a.sched[1 + pos] = i;
     }
   }
 }
