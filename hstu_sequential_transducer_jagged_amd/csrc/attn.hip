@@ -93,9 +93,13 @@ struct KeyData {
   alignas(16) float pos[kPosWin];   // raw position-bias window, entry e <-> dp = w0 + e
 };
 
+// Bytes per staged K / V row of HPB heads. The pads put the rows of one MFMA
+// operand read on distinct LDS banks: 16 B for the 16-lane b128 reads of K,
+// 64 B for the 32-lane transposing b64 reads of V.
 template <int HPB>
 struct Rows {
-  static constexpr int ROWB = HPB * kDH * 2 + 32;   // bytes per staged K/V row (+32 B pad)
+  static constexpr int ROWBK = HPB * kDH * 2 + 16;
+  static constexpr int ROWBV = HPB * kDH * 2 + 64;
 };
 
 // Position of key kk (block key index: cache rows first).
@@ -159,24 +163,39 @@ __device__ __forceinline__ void load_keydata(const Ctx& c, const int64_t* ts, co
 // rows w, w + HPB, ... of K and of V (rows past the last key repeat it; their
 // scores are masked). Row pointers are wave-uniform: block key kk lives at
 // base + kk*d for both the own rows (base shifted back by the cache length)
-// and the cache rows; only the lane's 16-byte column offset is per lane.
+// and the cache rows; only the lane's 16-byte column offset is per lane. A
+// tile that lies inside one source and before the last key takes its rows at
+// a fixed stride from one base.
 template <int HPB>
 __device__ __forceinline__ void load_kv(const Ctx& c, const uint16_t* kbase_o, const uint16_t* kbase_c,
                                         const uint16_t* vbase_o, const uint16_t* vbase_c, uint8_t* sk,
                                         uint8_t* sv, int tile, int wave, int lane) {
-  constexpr int ROWB = Rows<HPB>::ROWB;
+  constexpr int RK = Rows<HPB>::ROWBK;
+  constexpr int RV = Rows<HPB>::ROWBV;
   const int k0 = tile * kBN;
+  if (lane >= HPB * 8) return;
+  const bool uniform = (k0 + kBN <= c.nkeys) && (k0 >= c.nc || k0 + kBN <= c.nc);
+  if (uniform) {
+    const bool cached = k0 < c.nc;
+    const int64_t off = static_cast<int64_t>(k0) * c.d + lane * 8;
+    const uint16_t* kt = (cached ? kbase_c : kbase_o) + off;
+    const uint16_t* vt = (cached ? vbase_c : vbase_o) + off;
 #pragma unroll
-  for (int it = 0; it < kBN / HPB; ++it) {
-    const int r = wave + it * HPB;
-    const int kk = min(k0 + r, c.nkeys - 1);
-    const bool cached = kk < c.nc;
-    const int64_t off = static_cast<int64_t>(kk) * c.d;
-    const uint16_t* krow = (cached ? kbase_c : kbase_o) + off;
-    const uint16_t* vrow = (cached ? vbase_c : vbase_o) + off;
-    if (lane < HPB * 8) {
-      __builtin_amdgcn_global_load_lds(krow + lane * 8, LDS_PTR(void, sk + r * ROWB), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vrow + lane * 8, LDS_PTR(void, sv + r * ROWB), 16, 0, 0);
+    for (int it = 0; it < kBN / HPB; ++it) {
+      const int r = wave + it * HPB;
+      const int64_t ro = static_cast<int64_t>(r) * c.d;
+      __builtin_amdgcn_global_load_lds(kt + ro, LDS_PTR(void, sk + r * RK), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vt + ro, LDS_PTR(void, sv + r * RV), 16, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < kBN / HPB; ++it) {
+      const int r = wave + it * HPB;
+      const int kk = min(k0 + r, c.nkeys - 1);
+      const bool cached = kk < c.nc;
+      const int64_t off = static_cast<int64_t>(kk) * c.d + lane * 8;
+      __builtin_amdgcn_global_load_lds((cached ? kbase_c : kbase_o) + off, LDS_PTR(void, sk + r * RK), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((cached ? vbase_c : vbase_o) + off, LDS_PTR(void, sv + r * RV), 16, 0, 0);
     }
   }
 }
@@ -288,9 +307,8 @@ __device__ __forceinline__ void silu_pack(const f32x16& st, bf16x8 (&pa)[2]) {
 
 // V's B operands for both 16-key halves and both 32-dim blocks (transposing
 // 16-bit reads of the row-major tile).
-template <int HPB>
+template <int ROWB>
 __device__ __forceinline__ void load_v(const uint8_t* vb, int voff, bf16x8 (&vf)[2][2]) {
-  constexpr int ROWB = Rows<HPB>::ROWB;
 #pragma unroll
   for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -322,72 +340,107 @@ __device__ __forceinline__ int tile_steps(const SeqInfo& si, int qt) {
   return n_kt - (skip_b - skip_a);
 }
 
-constexpr int kSchedBuckets = 8192;
+constexpr int kNumXcd = 8;            // XCDs of the chip; workgroup id -> XCD id % 8
+constexpr int kCostBuckets = 1024;    // cost classes of the per-XCD sort
+constexpr int kSchedHead = kNumXcd + 1;
 
-// Work list of the bf16 attention: every non-empty (sequence, 64-query tile)
-// item, counting-sorted by its number of key steps, most expensive first.
-// sched[0] = number of items, sched[1 + i] = seq * n_qt + tile of item i.
-// One workgroup; cost buckets in LDS (costs above the last bucket share it).
-__global__ __launch_bounds__(1024) void attn_schedule_kernel(AttnArgs a, int n_qt, int cmax) {
-  __shared__ int cnt[kSchedBuckets];
-  __shared__ int part[1024];
+__device__ __forceinline__ int item_cost(const AttnArgs& a, int n_qt, int i) {
+  const int b = i / n_qt, t = i - b * n_qt;
+  const SeqInfo si = seq_info(a, b);
+  // tiles past max_seq_len (a violated contract) are never reached: t < n_qt
+  return t * kBM < si.L ? tile_steps(si, t) : 0;
+}
+
+// Work list of the bf16 attention. Items are the non-empty (sequence,
+// 64-query tile) pairs; an item's cost is its number of key steps.
+//  1. Items, in (sequence, tile) order, are cut into kNumXcd contiguous runs
+//     of equal total cost; run x goes to XCD x. The workgroups of one XCD
+//     then work on one or a few sequences at a time and share their K/V rows
+//     in that XCD's L2.
+//  2. Within a run, items are counting-sorted by cost, most expensive first,
+//     so that the XCD's compute units finish together.
+// sched[x] (x = 0..8): first list index of XCD x (sched[8] = item count);
+// sched[9 + k]: item (seq * n_qt + tile) at list index k.
+__global__ __launch_bounds__(1024) void attn_schedule_kernel(AttnArgs a, int n_qt) {
+  __shared__ int cnt[kNumXcd * kCostBuckets];
+  __shared__ long long part[1024];
   const int tid = threadIdx.x;
-  for (int i = tid; i <= cmax; i += 1024) cnt[i] = 0;
-  __syncthreads();
-  // One (sequence, tile) item per thread and pass. Tiles past max_seq_len (a
-  // violated contract) are not scheduled.
   const int items = a.num_seqs * n_qt;
-  for (int i = tid; i < items; i += 1024) {
-    const int b = i / n_qt, t = i - b * n_qt;
-    const SeqInfo si = seq_info(a, b);
-    if (t * kBM < si.L) atomicAdd(&cnt[min(tile_steps(si, t), cmax)], 1);
-  }
-  __syncthreads();
-  // exclusive scan in descending cost order: start(c) = items costing more than c
-  const int per = (cmax + 1 + 1023) / 1024;
-  const int lo = cmax - tid * per;   // this thread scans buckets lo, lo-1, ..., lo-per+1
-  int sum = 0;
-  for (int i = 0; i < per; ++i)
-    if (lo - i >= 0) sum += cnt[lo - i];
+  for (int i = tid; i < kNumXcd * kCostBuckets; i += 1024) cnt[i] = 0;
+  // each thread owns a contiguous chunk of items
+  const int per = (items + 1023) / 1024;
+  const int i0 = min(tid * per, items), i1 = min(i0 + per, items);
+  long long sum = 0;
+  for (int i = i0; i < i1; ++i) sum += item_cost(a, n_qt, i);
   part[tid] = sum;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
+    const long long v = tid >= off ? part[tid - off] : 0;
     __syncthreads();
     part[tid] += v;
     __syncthreads();
   }
-  int run = tid ? part[tid - 1] : 0;
-  for (int i = 0; i < per; ++i)
-    if (lo - i >= 0) {
-      const int c = cnt[lo - i];
-      cnt[lo - i] = run;
-      run += c;
-    }
-  if (tid == 1023) a.sched[0] = part[1023];
+  const long long total_cost = part[1023];
+  const long long run0 = tid ? part[tid - 1] : 0;
+  // sort key: XCD-major, cost descending; the item's XCD is the run holding
+  // the midpoint of its cost interval
+  auto key_of = [&](long long run, int c) __attribute__((always_inline)) {
+    const int x = static_cast<int>(min(static_cast<long long>(kNumXcd - 1),
+                                       ((2 * run + c) * kNumXcd) / (2 * total_cost)));
+    return x * kCostBuckets + (kCostBuckets - 1 - min(c, kCostBuckets - 1));
+  };
+  long long run = run0;
+  for (int i = i0; i < i1; ++i) {
+    const int c = item_cost(a, n_qt, i);
+    if (c > 0) atomicAdd(&cnt[key_of(run, c)], 1);
+    run += c;
+  }
   __syncthreads();
-  for (int i = tid; i < items; i += 1024) {
-    const int b = i / n_qt, t = i - b * n_qt;
-    const SeqInfo si = seq_info(a, b);
-    if (t * kBM < si.L) {
-      const int pos = atomicAdd(&cnt[min(tile_steps(si, t), cmax)], 1);
-      a.sched[1 + pos] = i;
-    }
+  // exclusive scan of the kNumXcd * kCostBuckets counters, 8 per thread
+  constexpr int kPer = kNumXcd * kCostBuckets / 1024;
+  int loc = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) loc += cnt[tid * kPer + i];
+  __syncthreads();
+  part[tid] = loc;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const long long v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int base = tid ? static_cast<int>(part[tid - 1]) : 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int c = cnt[tid * kPer + i];
+    cnt[tid * kPer + i] = base;
+    base += c;
+  }
+  __syncthreads();
+  if (tid < kNumXcd) a.sched[tid] = cnt[tid * kCostBuckets];
+  if (tid == kNumXcd) a.sched[kNumXcd] = static_cast<int>(part[1023]);
+  run = run0;
+  for (int i = i0; i < i1; ++i) {
+    const int c = item_cost(a, n_qt, i);
+    if (c > 0) a.sched[kSchedHead + atomicAdd(&cnt[key_of(run, c)], 1)] = i;
+    run += c;
   }
 }
 
 template <int HPB>
 __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
   constexpr int NT = 64 * HPB;
-  constexpr int ROWB = Rows<HPB>::ROWB;
+  constexpr int ROWBK = Rows<HPB>::ROWBK;
+  constexpr int ROWBV = Rows<HPB>::ROWBV;
   constexpr int SPT = 512 / NT;   // bias slots per thread (512 slots of 4 pairs)
   // Double buffers as distinct LDS objects: the compiler then knows that the
   // DMA filling one buffer cannot alias the reads of the other and does not
   // wait for it.
-  __shared__ __attribute__((aligned(16))) uint8_t sK0[kBN * ROWB];
-  __shared__ __attribute__((aligned(16))) uint8_t sK1[kBN * ROWB];
-  __shared__ __attribute__((aligned(16))) uint8_t sV0[kBN * ROWB];
-  __shared__ __attribute__((aligned(16))) uint8_t sV1[kBN * ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t sK0[kBN * ROWBK];
+  __shared__ __attribute__((aligned(16))) uint8_t sK1[kBN * ROWBK];
+  __shared__ __attribute__((aligned(16))) uint8_t sV0[kBN * ROWBV];
+  __shared__ __attribute__((aligned(16))) uint8_t sV1[kBN * ROWBV];
   __shared__ __attribute__((aligned(16))) float sB0[kBM * kBN];
   __shared__ __attribute__((aligned(16))) float sB1[kBM * kBN];
   __shared__ KeyData sD0, sD1;
@@ -395,11 +448,14 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
   __shared__ float tb_lin[64];   // base-2 time bias indexed by bucket
   __shared__ int64_t red_min[HPB], red_max[HPB];
 
-  // work item of this workgroup: the list is sorted heaviest first, so
-  // consecutive workgroups (dealt round-robin to the XCDs) carry equal work
-  const int total = a.sched[0];
-  const int item = a.sched[1 + blockIdx.x];
-  if (static_cast<int>(blockIdx.x) >= total) return;
+  // Work items of this workgroup: workgroup g runs on XCD g % 8 and takes
+  // that XCD's list entries g / 8, g / 8 + gridDim.x / 8, ...
+  const int xcd = blockIdx.x % kNumXcd;
+  const int list_end = a.sched[xcd + 1];
+  const int list_step = gridDim.x / kNumXcd;
+  for (int li = a.sched[xcd] + static_cast<int>(blockIdx.x) / kNumXcd; li < list_end; li += list_step) {
+  __syncthreads();   // the previous item's LDS reads are done
+  const int item = a.sched[kSchedHead + li];
   const int n_qt = (a.max_seq_len + kBM - 1) / kBM;
   const int seq = item / n_qt;
   const int qt = item - seq * n_qt;
@@ -421,7 +477,7 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
   c.q_hi = min(q0 + kBM, si.L);
   c.nkeys = c.nc + c.q_hi;
   c.d = a.d_model;
-  c.col0 = blockIdx.z * HPB * kDH;
+  c.col0 = blockIdx.y * HPB * kDH;
   c.pmin_q = c.nc + min(q0, c.first_tgt);
   c.pos_len = a.pos_len;
   c.pos_center = a.pos_center;
@@ -527,10 +583,10 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
   const int sl = lane & 15;
   const int h2 = lane >> 5;             // half of the wave
   // A operand K: row lane%32, dims 16c + 8*h2 of this head
-  const int koff = (lane & 31) * ROWB + (hcol + 8 * h2) * 2;
+  const int koff = (lane & 31) * ROWBK + (hcol + 8 * h2) * 2;
   // B operand V (transposing read): source lane sl reads row 4*h2 + sl/4
   // (+8, +16*kh), dims 32db + 16*(g16&1) + 4*(sl&3)
-  const int voff = (4 * h2 + (sl >> 2)) * ROWB + (hcol + 16 * (g16 & 1) + 4 * (sl & 3)) * 2;
+  const int voff = (4 * h2 + (sl >> 2)) * ROWBV + (hcol + 16 * (g16 & 1) + 4 * (sl & 3)) * 2;
 
   // ---- prologue: key data of tiles 0 and 1, K/V and bias of tile 0 ----
   load_keydata<HPB>(c, a.ts, a.c_ts, a.pos_bias, sD0, tile_of(0), wave, lane);
@@ -541,10 +597,11 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
   build_bias<HPB>(c, sq, sD0, sB0, tb_clz, tb_lin, a.nb, tile_of(0), tid);
   __syncthreads();
 
-  // Step `st` computes key tile st from buffer st&1. Meanwhile it loads the
-  // K/V rows of tile st+1 and the key data of tile st+2 by DMA into the other
-  // buffers, and builds the bias of tile st+1 from the key data that arrived
-  // a step earlier. Unrolled by two so that every buffer is a fixed LDS object.
+  // Step `st` computes key tile st from buffer st&1. After issuing its score
+  // MFMAs it starts the DMA of the K/V rows of tile st+1 and of the key data
+  // of tile st+2 into the other buffers, and builds the bias of tile st+1 from
+  // the key data that arrived a step earlier. Unrolled by two so that every
+  // buffer is a fixed LDS object.
 #define HSTU_ATTN_STEP(CUR_K, CUR_V, CUR_B, CUR_D, NXT_K, NXT_V, NXT_B, NXT_D)                    \
   {                                                                                              \
     const int nxt = st + 1;                                                                      \
@@ -557,7 +614,7 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
       build_bias<HPB>(c, sq, NXT_D, NXT_B, tb_clz, tb_lin, a.nb, tile_of(nxt), tid);             \
     }                                                                                            \
     bf16x8 vf[2][2];                                                                             \
-    load_v<HPB>(CUR_V, voff, vf);                                                                \
+    load_v<ROWBV>(CUR_V, voff, vf);                                                                \
     bf16x8 pa[2];                                                                                \
     silu_pack(sc[0], pa);                                                                        \
     pv(pa, vf, acc[0]);                                                                          \
@@ -586,6 +643,7 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
         for (int db = 0; db < 2; ++db) row[db * 32] = -kLn2 * acc[qb][db][r];
       }
     }
+  }   // work items
 }
 
 // fp32 kernel: one thread per query row, plain FMA loops, exact expf and IEEE
@@ -646,21 +704,22 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 
 size_t attn_workspace_bytes(int num_seqs, int max_seq_len) {
   const int64_t n_qt = (static_cast<int64_t>(max_seq_len) + kBM - 1) / kBM;
-  return static_cast<size_t>(1 + static_cast<int64_t>(num_seqs) * n_qt) * sizeof(int);
+  return static_cast<size_t>(kSchedHead + static_cast<int64_t>(num_seqs) * n_qt) * sizeof(int);
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   const int n_qt = (a.max_seq_len + kBM - 1) / kBM;
   if (a.num_seqs == 0 || n_qt == 0) return hipSuccess;
-  const int cmax = min((a.max_seq_len + a.max_cache_len) / kBN + 2, kSchedBuckets - 1);
-  hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, s, a, n_qt, cmax);
+  hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, s, a, n_qt);
   int hpb = 1;
   for (int c : {8, 4, 2, 1})
     if (a.num_heads % c == 0) {
       hpb = c;
       break;
     }
-  dim3 grid(a.num_seqs * n_qt, a.num_heads / hpb);
+  // a multiple of the XCD count, one workgroup per item on average
+  const int64_t items = static_cast<int64_t>(a.num_seqs) * n_qt;
+  dim3 grid(static_cast<unsigned>((items + kNumXcd - 1) / kNumXcd * kNumXcd), a.num_heads / hpb);
   switch (hpb) {
     case 8: hipLaunchKernelGGL(attn_bf16_kernel<8>, grid, dim3(512), 0, s, a); break;
     case 4: hipLaunchKernelGGL(attn_bf16_kernel<4>, grid, dim3(256), 0, s, a); break;

@@ -131,7 +131,7 @@ int hstu_proj_fwd(const hstu_layer_desc *desc, const hstu_layer_params *params, 
                   const void *x, void *u, void *v, void *q, void *k, void *stream);
 
 /* Workspace bytes hstu_attn_fwd needs for this batch (bf16: the work list
- * of its scheduling pass, 4 * (1 + num_seqs * ceil(max_seq_len / 64)) bytes
+ * of its scheduling pass, 4 * (9 + num_seqs * ceil(max_seq_len / 64)) bytes
  * rounded up to 256; f32: 0). */
 size_t hstu_attn_workspace_size(const hstu_layer_desc *desc, const hstu_jagged *jagged);
 

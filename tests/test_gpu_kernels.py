@@ -47,7 +47,7 @@ def _run_attn(hs, w, dtype, q, k, v, num_targets=None, cache=None, alpha=1.0):
     return to_np(av)[:w.total_tokens]
 
 
-@pytest.mark.parametrize("H", [8, 4, 2, 1])
+@pytest.mark.parametrize("H", [8, 4, 2, 1, 16, 12, 6])
 def test_attn_bf16_edge_lengths(gpu_lib, H):
     w = gen.make_custom(EDGE_LENGTHS, 64 * H, H, dtype="bf16", seed=100 + H, n_max=256)
     u, v, q, k = _qkv_inputs(w, "bf16")
@@ -56,6 +56,20 @@ def test_attn_bf16_edge_lengths(gpu_lib, H):
     ref = oracle.attention(q, k, v, w.offsets, w.timestamps, p.pos_bias, p.time_bias, H, w.n_max)
     err = row_rel_err(got, ref)
     print(f"attn bf16 H={H} T={w.total_tokens}: {err:.3e}")
+    assert err < TOL["bf16"]
+
+
+def test_attn_bf16_uneven_work_lists(gpu_lib):
+    """Equal-length sequences: the XCD whose cost share holds the cheap early
+    tiles gets more items than workgroups, which then take several items."""
+    H = 2
+    w = gen.make_custom([1024, 1024, 1024, 960], 64 * H, H, dtype="bf16", seed=150, n_max=1024)
+    u, v, q, k = _qkv_inputs(w, "bf16")
+    got = _run_attn(gpu_lib, w, "bf16", q, k, v)
+    p = w.layers[0]
+    ref = oracle.attention(q, k, v, w.offsets, w.timestamps, p.pos_bias, p.time_bias, H, w.n_max)
+    err = row_rel_err(got, ref)
+    print(f"attn bf16 uneven lists: {err:.3e}")
     assert err < TOL["bf16"]
 
 
