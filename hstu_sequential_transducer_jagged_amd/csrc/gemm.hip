@@ -24,7 +24,15 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // C^T[n][m] = sum_k W[n][k] X[m][k] (A operand = W rows, B operand = X rows),
 // so that a lane's accumulator holds 4 consecutive output columns of one row
 // and the epilogue stores 8-byte bf16 quads.
-constexpr int kGM = 256;
+//
+// Operand tiles reach LDS by direct global->LDS DMA (global_load_lds_dwordx4)
+// through a three-stage ring: the K step s+2 is requested while step s is
+// multiplied, so each load has two MFMA steps to land, and no staging
+// registers are used. A DMA instruction writes 1 KB of consecutive LDS (16
+// rows of 64 bytes); the bank swizzle is applied on the source side: the lane
+// that fills 16-byte slot p of row r fetches k-chunk p ^ ((r >> 2) & 3) of
+// that row, so the 16 rows one b128 MFMA-operand read serves hit 16 distinct
+// bank groups.
 constexpr int kGN = 128;
 constexpr int kGK = 32;
 constexpr int kRowB = kGK * 2;   // 64-byte LDS rows
@@ -33,13 +41,20 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// 16-byte chunk c (0..3) of LDS row r: XOR-swizzled so that the 8 rows one
-// ds_read_b128 cycle serves fall on distinct banks.
-__device__ __forceinline__ int swz(int r, int c) { return r * kRowB + ((c ^ ((r >> 1) & 3)) << 4); }
+// LDS byte offset of k-chunk c (0..3, 8 bf16 each) of tile row r.
+__device__ __forceinline__ int swz(int r, int c) { return r * kRowB + ((c ^ ((r >> 2) & 3)) << 4); }
 
 __device__ __forceinline__ float silu_fast(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
 }
+
+// Workgroup barrier ordering LDS accesses only (the DMA ring is waited for
+// explicitly; __syncthreads() would also drain it).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 // Epilogues receive one row m and 4 consecutive columns n..n+3.
 struct ProjEpi {
@@ -76,19 +91,100 @@ struct OutEpi {
   }
 };
 
+// One ring stage of DMA: wave w fills X rows 16i .. 16i+15 for i = w, w+4, ...
+// (NXI instructions) and W rows for i = w, w+4 (1 KB of LDS per instruction).
+template <int NXI>
+__device__ __forceinline__ void gemm_issue(const uint16_t* const (&xsrc)[NXI], const uint16_t* const (&wsrc)[2],
+                                           uint8_t* sx, uint8_t* sw, int k0, int wave) {
+#pragma unroll
+  for (int i = 0; i < NXI; ++i)
+    __builtin_amdgcn_global_load_lds(xsrc[i] + k0, LDS_PTR(void, sx + (wave + 4 * i) * 1024), 16, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    __builtin_amdgcn_global_load_lds(wsrc[i] + k0, LDS_PTR(void, sw + (wave + 4 * i) * 1024), 16, 0, 0);
+}
+
+// One 32-deep K step of a wave's (32 NJ) x 64 tile (C^T: 64 x 32 NJ).
+template <int NJ>
+__device__ __forceinline__ void gemm_compute(const uint8_t* sx, const uint8_t* sw, f32x16 (&acc)[2][NJ],
+                                             int wm, int wn, int l32, int h) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {     // two 16-deep MFMA steps
+    const int c = 2 * kk + h;          // 16-byte chunk of this lane's 8 k values
+    bf16x8 a[2], b[NJ];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sw[swz(wn * 64 + i * 32 + l32, c)]));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sx[swz(wm * 32 * NJ + j * 32 + l32, c)]));
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+  }
+}
+
+// The K loop over the three-stage ring. The stage buffers come in as
+// __restrict__ pointers: once inlined, every LDS access and DMA carries alias
+// scopes that tell the compiler's wait insertion that a DMA into one stage
+// does not alias reads of another, so it waits only for the stage it reads.
+// Step s: wait for this wave's DMA of stage s (the NJ + 2 instructions of
+// stage s+1 may stay in flight), barrier so that every wave's stage s is in LDS and
+// every wave is done with stage s-1, request stage s+2 into the buffer of
+// stage s-1, multiply stage s.
+template <int NJ>
+__device__ __forceinline__ void gemm_mainloop(uint8_t* __restrict__ sX0, uint8_t* __restrict__ sX1,
+                                              uint8_t* __restrict__ sX2, uint8_t* __restrict__ sW0,
+                                              uint8_t* __restrict__ sW1, uint8_t* __restrict__ sW2,
+                                              const uint16_t* const (&xsrc)[NJ],
+                                              const uint16_t* const (&wsrc)[2], f32x16 (&acc)[2][NJ],
+                                              int nsteps, int wave, int wm, int wn, int l32, int h) {
+  gemm_issue(xsrc, wsrc, sX0, sW0, 0, wave);
+  if (nsteps > 1) gemm_issue(xsrc, wsrc, sX1, sW1, kGK, wave);
+#define HSTU_GEMM_STEP(s, SX, SW, NX, NW)                                      \
+  {                                                                            \
+    if ((s) + 1 < nsteps)                                                      \
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NJ + 2) : "memory");            \
+    else                                                                       \
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                         \
+    lds_barrier();                                                             \
+    if ((s) + 2 < nsteps) gemm_issue(xsrc, wsrc, NX, NW, ((s) + 2) * kGK, wave); \
+    gemm_compute<NJ>(SX, SW, acc, wm, wn, l32, h);                             \
+  }
+  int s = 0;
+  for (; s + 3 <= nsteps; s += 3) {
+    HSTU_GEMM_STEP(s, sX0, sW0, sX2, sW2)
+    HSTU_GEMM_STEP(s + 1, sX1, sW1, sX0, sW0)
+    HSTU_GEMM_STEP(s + 2, sX2, sW2, sX1, sW1)
+  }
+  if (s < nsteps) {
+    HSTU_GEMM_STEP(s, sX0, sW0, sX2, sW2)
+    if (s + 1 < nsteps) HSTU_GEMM_STEP(s + 1, sX1, sW1, sX0, sW0)
+  }
+#undef HSTU_GEMM_STEP
+}
+
 // X [M, K] row-major, W [N, K] row-major (nn.Linear), K % 32 == 0,
 // N % 4 == 0. Grid: 8 * ceil(nm / 8) * nn workgroups (nm = ceil(M/256),
-// nn = N/128); workgroup id -> XCD id % 8 (round-robin dispatch); XCD x
+// nn = ceil(N/128)); workgroup id -> XCD id % 8 (round-robin dispatch); XCD x
 // takes row blocks x, x+8, ... and sweeps all nn column tiles of one row
 // block before the next, so each X row block is read from HBM once and W
 // stays in that XCD's L2.
-template <class Epi>
+template <int NJ, class Epi>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __restrict__ X,
                                                            const uint16_t* __restrict__ W,
                                                            int64_t M, int N, int K, int nm, int nn,
                                                            Epi epi) {
-  __shared__ __attribute__((aligned(16))) uint8_t sX[2][kGM * kRowB];
-  __shared__ __attribute__((aligned(16))) uint8_t sW[2][kGN * kRowB];
+  constexpr int BM = 64 * NJ;      // block rows; each wave owns BM/2 rows x 64 columns
+  // three ring stages as distinct LDS objects, so that a pending DMA into one
+  // stage does not make the compiler wait before reads of another
+  __shared__ __attribute__((aligned(16))) uint8_t sX0[BM * kRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t sX1[BM * kRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t sX2[BM * kRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t sW0[kGN * kRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t sW1[kGN * kRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t sW2[kGN * kRowB];
 
   const int id = blockIdx.x;
   const int xcd = id & 7;
@@ -96,89 +192,51 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
   const int mb = (slot / nn) * 8 + xcd;
   const int nb = slot - (slot / nn) * nn;
   if (mb >= nm) return;
-  const int64_t m0 = static_cast<int64_t>(mb) * kGM;
+  const int64_t m0 = static_cast<int64_t>(mb) * BM;
   const int n0 = nb * kGN;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int wm = wave & 1;         // 128-row half
+  const int wm = wave & 1;         // row half
   const int wn = wave >> 1;        // 64-column half
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
-  // staging: X tile 256 rows x 4 chunks (4 per thread), W tile 128 rows x 4 chunks (2 per thread)
-  uint4 rx[4], rw[2];
-  auto gload = [&](int k0) __attribute__((always_inline)) {
+  // DMA source rows of this lane: X instructions cover rows 16i + lane/4
+  // (i = wave, wave+4, ...), W instructions rows 16i + lane/4 (i = wave,
+  // wave+4). Rows past M or N repeat the last valid row: their products land
+  // only in outputs that are not stored.
+  const int lr = lane >> 2;
+  const int lp = lane & 3;
+  const uint16_t* xsrc[NJ];
+  const uint16_t* wsrc[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * 256;
-      const int r = c >> 2;
-      const int64_t gm = m0 + r;
-      rx[i] = gm < M ? *reinterpret_cast<const uint4*>(X + gm * K + k0 + (c & 3) * 8)
-                     : make_uint4(0, 0, 0, 0);
-    }
+  for (int i = 0; i < NJ; ++i) {
+    const int r = 16 * (wave + 4 * i) + lr;
+    const int64_t gm = min(m0 + r, M - 1);
+    xsrc[i] = X + gm * K + 8 * (lp ^ ((r >> 2) & 3));
+  }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + i * 256;
-      const int r = c >> 2;
-      rw[i] = n0 + r < N ? *reinterpret_cast<const uint4*>(W + static_cast<int64_t>(n0 + r) * K + k0 + (c & 3) * 8)
-                         : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto lstore = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * 256;
-      *reinterpret_cast<uint4*>(&sX[buf][swz(c >> 2, c & 3)]) = rx[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + i * 256;
-      *reinterpret_cast<uint4*>(&sW[buf][swz(c >> 2, c & 3)]) = rw[i];
-    }
-  };
-
-  f32x16 acc[2][4];
+  for (int i = 0; i < 2; ++i) {
+    const int r = 16 * (wave + 4 * i) + lr;
+    const int gn = min(n0 + r, N - 1);
+    wsrc[i] = W + static_cast<int64_t>(gn) * K + 8 * (lp ^ ((r >> 2) & 3));
+  }
+  f32x16 acc[2][NJ];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nsteps = K / kGK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nsteps) gload((st + 1) * kGK);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {     // two 16-deep MFMA steps
-      const int c = 2 * kk + h;          // 16-byte chunk of this lane's 8 k values
-      bf16x8 a[2], b[4];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
-                                              &sW[buf][swz(wn * 64 + i * 32 + l32, c)]));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
-                                              &sX[buf][swz(wm * 128 + j * 32 + l32, c)]));
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
-    }
-    if (st + 1 < nsteps) lstore(buf ^ 1);
-    __syncthreads();
-  }
+  gemm_mainloop<NJ>(sX0, sX1, sX2, sW0, sW1, sW2, xsrc, wsrc, acc, K / kGK, wave, wm, wn, l32, h);
 
   // C^T accumulator: lane -> m = j*32 + lane%32, n = i*32 + 8*(r/4) + 4*h + r%4
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t m = m0 + wm * 128 + j * 32 + l32;
+  for (int j = 0; j < NJ; ++j) {
+    const int64_t m = m0 + wm * 32 * NJ + j * 32 + l32;
     if (m >= M) continue;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -243,13 +301,23 @@ struct OutEpiF32 {
 
 }  // namespace
 
+// 256-row blocks (measured faster on long inputs), or 128-row blocks when
+// 256-row ones would leave the 256 compute units with under two rounds of
+// work.
 template <class Epi>
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, int64_t M, int N, int K, Epi epi,
                             hipStream_t s) {
-  const int nm = static_cast<int>((M + kGM - 1) / kGM);
   const int nn = (N + kGN - 1) / kGN;
-  const int grid = 8 * ((nm + 7) / 8) * nn;
-  hipLaunchKernelGGL(gemm_bf16_kernel<Epi>, dim3(grid), dim3(256), 0, s, x, w, M, N, K, nm, nn, epi);
+  const int64_t blocks256 = (M + 255) / 256 * nn;
+  if (blocks256 >= 2 * 512) {
+    const int nm = static_cast<int>((M + 255) / 256);
+    const int grid = 8 * ((nm + 7) / 8) * nn;
+    hipLaunchKernelGGL((gemm_bf16_kernel<4, Epi>), dim3(grid), dim3(256), 0, s, x, w, M, N, K, nm, nn, epi);
+  } else {
+    const int nm = static_cast<int>((M + 127) / 128);
+    const int grid = 8 * ((nm + 7) / 8) * nn;
+    hipLaunchKernelGGL((gemm_bf16_kernel<2, Epi>), dim3(grid), dim3(256), 0, s, x, w, M, N, K, nm, nn, epi);
+  }
   return hipGetLastError();
 }
 
