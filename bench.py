@@ -1,15 +1,21 @@
 #!/usr/bin/env python3
-"""Benchmark: one HSTU layer forward on the long jagged bf16 workload.
+"""Benchmark: the HSTU layer forward on seeded synthetic jagged workloads.
 
-Workload (default ``--workload 2``): 16 sequences with lengths uniform on
-[2048, 8192] (the first fixed at 8192), d_model 512, 8 heads of 64, bf16,
-seeded synthetic inputs (no dataset exists for it; see hstu_inputs.gen).
+Default (``--workload 2``, the headline line): 16 sequences with lengths
+uniform on [2048, 8192] (the first fixed at 8192), d_model 512, 8 heads of 64,
+bf16. A step is one pass of the whole layer path: projection (f1 + SiLU +
+split), jagged causal SiLU attention with the position/time bias,
+LayerNorm-gate and f2 + residual, each launched through its C-ABI entry point
+on one stream, inputs resident in HBM. Steps are timed with HIP events; each
+kernel's launches are bracketed by events inside the same timed region.
 
-A step is one pass of the whole layer path: projection (f1 + SiLU + split),
-jagged causal SiLU attention with the position/time bias, LayerNorm-gate and
-f2 + residual, each launched through its C-ABI entry point on one stream,
-inputs resident in HBM. Steps are timed with HIP events; the attention
-kernel's own launches are bracketed by events inside the same timed region.
+Other workloads (extra lines; parity is covered by the tests):
+  0, 1  one layer as above (fp32 64 tokens; bf16 64 sequences up to 512);
+  3     item/action embedding + an 8-layer stack over 128 Zipf-length
+        sequences (value = tokens through the whole stack per second);
+  4     ranking: 32 users x 4096 history tokens through 4 layers keeping K/V,
+        then 512 candidates per user in micro-batches of 128 against that
+        cache (value = history + candidate tokens per second).
 
 Prints ONE JSON line (rank 0, one GPU). Only N = 1 is supported.
 """
@@ -28,6 +34,7 @@ if ROOT not in sys.path:
 METRIC = "HSTU layer fwd tokens/s; jagged attn TFLOP/s and % of bf16 MFMA peak, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
 
 
 def parse():
@@ -35,7 +42,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2])
+    ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
                     help="approximate CPU seconds for the oracle sample")
@@ -87,11 +94,7 @@ def cpu_baseline(w, budget_s):
     import numpy as np
 
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+    threads = oracle_threads()
     p = w.layers[0]
     tokens = 0
     seqs = 0
@@ -110,21 +113,14 @@ def cpu_baseline(w, budget_s):
                       f"({tokens} tokens) of the same workload, {dt:.1f} s"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(sequences are independent; see the sharding note in the design notes).",
-              file=sys.stderr)
-        sys.exit(2)
-
+def run_layer(args):
+    """Workloads 0-2: one layer, kernel by kernel."""
     import numpy as np
     import torch
 
     from hstu_inputs import gen
     from hstu_sequential_transducer_jagged_amd import hstu, runner
 
-    hstu.load()
     w = gen.make_config(args.workload)
     dw = runner.DeviceWorkload(w)
     T, d, H = w.total_tokens, w.d_model, w.num_heads
@@ -191,19 +187,21 @@ def main():
     same = bool(torch.equal(y, y2))
 
     attn_tflops = attn_flop / (attn_ms * 1e-3) / 1e12
-    esz = 2
+    esz = 2 if w.dtype == "bf16" else 4
     proj_flop, out_flop = 8.0 * T * d * d, 2.0 * T * d * d
     ng_bytes = T * d * (4 + esz + esz)        # read AV (fp32) and U, write G
+    # the bf16 path runs on MFMA; the fp32 path on plain fp32 FMA (vector ALU)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     kernels = {
         "proj": {"ms": pct(per["proj"]), "tflops": proj_flop / np.mean(per["proj"]) / 1e9,
-                 "pct_bf16_peak": 100 * proj_flop / np.mean(per["proj"]) / 1e9 / PEAK_BF16_TFLOPS},
+                 "pct_peak": 100 * proj_flop / np.mean(per["proj"]) / 1e9 / peak},
         "attn": {"ms": pct(per["attn"]), "tflops": attn_tflops,
-                 "pct_bf16_peak": 100 * attn_tflops / PEAK_BF16_TFLOPS},
+                 "pct_peak": 100 * attn_tflops / peak},
         "norm_gate": {"ms": pct(per["norm_gate"]),
                       "gbs": ng_bytes / np.mean(per["norm_gate"]) / 1e6,
                       "pct_hbm_peak": 100 * ng_bytes / np.mean(per["norm_gate"]) / 1e6 / PEAK_HBM_GBS},
         "out": {"ms": pct(per["out"]), "tflops": out_flop / np.mean(per["out"]) / 1e9,
-                "pct_bf16_peak": 100 * out_flop / np.mean(per["out"]) / 1e9 / PEAK_BF16_TFLOPS},
+                "pct_peak": 100 * out_flop / np.mean(per["out"]) / 1e9 / peak},
         "step": {"ms": pct(steps_ms)},
     }
     src = os.path.join(ROOT, "hstu_sequential_transducer_jagged_amd", "csrc", "attn.hip")
@@ -218,19 +216,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic (seeded; no dataset)",
         "config": {"workload": gen.CONFIG_NAMES[args.workload], "total_tokens": T,
                    "num_seqs": w.num_seqs, "max_seq_len": w.max_seq_len, "d_model": d,
                    "num_heads": H, "head_dim": d // H, "visible_pairs": P},
-        "roofline": {"kernel": "attn_bf16", "bound": "mfma", "achieved": attn_tflops,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": attn_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": traffic_record("attn_bf16", src),
+        "roofline": {"kernel": "attn_" + w.dtype, "bound": "mfma" if w.dtype == "bf16" else "alu",
+                     "achieved": attn_tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": attn_tflops / peak,
+                     "traffic": traffic_record("attn_bf16", src) if args.workload == 2 else None,
                      "algorithmic_flop_per_launch": attn_flop,
                      "avg_launch_ms": attn_ms},
         "attn_tflops": attn_tflops,
-        "attn_pct_bf16_peak": 100.0 * attn_tflops / PEAK_BF16_TFLOPS,
+        "attn_pct_peak": 100.0 * attn_tflops / peak,
         "hstu_layer_fwd_ms": layer_ms,
         "hstu_layer_fwd_matches_steps": same,
         "kernels": kernels,
@@ -239,7 +237,225 @@ def main():
         rec["copy_calib"] = calib
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
-    print(json.dumps(rec), flush=True)
+    return rec
+
+
+def timed(step, stream, warmup, steps):
+    """Mean ms of `steps` calls of step() between HIP events on `stream`."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(steps):
+        step()
+    e.record(stream)
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def base_record(args, metric, value, unit, ms, dtype, config):
+    return {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+            "data": "synthetic (seeded; no dataset)", "config": config}
+
+
+def run_stack(args):
+    """Workload 3: embedding, then the 8-layer stack, through hstu_embed_fwd and
+    hstu_layer_fwd (one workspace, two ping-pong activation buffers)."""
+    import numpy as np
+    import torch
+
+    from hstu_inputs import gen
+    from hstu_sequential_transducer_jagged_amd import hstu, runner
+
+    w = gen.make_config(3)
+    dw = runner.DeviceWorkload(w)
+    T, d, L = w.total_tokens, w.d_model, len(w.layers)
+    x0 = dw.empty_act(T)
+    bufs = [dw.empty_act(T), dw.empty_act(T)]
+    ws = dw.workspace()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step():
+        hstu.hstu_embed_fwd(T, d, dw.dtype, dw.item_emb, dw.action_emb, dw.item_ids, dw.actions, x0, sh)
+        h = x0
+        for l in range(L):
+            y = bufs[l % 2]
+            hstu.hstu_layer_fwd(dw.desc, dw.layers[l].params, dw.jagged, None, h, y, None, None, ws, sh)
+            h = y
+
+    ms = timed(step, stream, args.warmup, args.steps)
+    P = visible_pairs(w.offsets)
+    rec = base_record(args, "HSTU stack fwd tokens/s (embedding + 8 layers), 1 GPU", T / (ms * 1e-3),
+                      "tokens/s", ms, w.dtype,
+                      {"workload": gen.CONFIG_NAMES[3], "total_tokens": T, "num_seqs": w.num_seqs,
+                       "max_seq_len": w.max_seq_len, "layers": L, "d_model": d,
+                       "num_heads": w.num_heads, "visible_pairs_per_layer": P})
+    rec["layer_tokens_per_s"] = T * L / (ms * 1e-3)
+    rec["attn_flop_per_layer"] = 4.0 * d * P
+    rec["roofline"] = None
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_stack(w, args.cpu_budget_s)
+    return rec
+
+
+def cpu_baseline_stack(w, budget_s):
+    """The CPU oracle (embedding + every layer) on the first sequences of the
+    same workload until ~budget_s of work is done."""
+    import numpy as np
+
+    import oracle
+    threads = oracle_threads()
+    tokens = seqs = 0
+    t0 = time.perf_counter()
+    for b in range(w.num_seqs):
+        s, e = int(w.offsets[b]), int(w.offsets[b + 1])
+        x = oracle.embed(w.item_emb, w.action_emb, w.item_ids[s:e], w.actions[s:e])
+        oracle.stack(x, w.layers, np.array([0, e - s]), w.timestamps[s:e], w.num_heads, w.n_max,
+                     w.alpha, w.ln_eps)
+        tokens += e - s
+        seqs += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"float64 NumPy oracle: embedding + {len(w.layers)} layers on the first "
+                      f"{seqs} sequence(s) ({tokens} tokens) of the same workload, {dt:.1f} s"}
+
+
+def run_ranking(args):
+    """Workload 4: history pass through every layer keeping K/V, then every
+    candidate micro-batch through every layer against that cache (all
+    device-resident; the micro-batch plan is built once, outside the timing)."""
+    import numpy as np
+    import torch
+
+    from hstu_inputs import gen
+    from hstu_sequential_transducer_jagged_amd import hstu, runner
+
+    w = gen.make_config(4)
+    dw = runner.DeviceWorkload(w)
+    Th, d, L = w.total_tokens, w.d_model, len(w.layers)
+    plan = runner.RankingPlan(w)
+    dev = dw.device
+    kc = [dw.empty_act(Th) for _ in range(L)]
+    vc = [dw.empty_act(Th) for _ in range(L)]
+    hbuf = [dw.empty_act(Th), dw.empty_act(Th)]
+    ws = dw.workspace()
+    cx = dw.upload_act(np.asarray(w.cand_x)[plan.order])
+    cts = torch.from_numpy(np.asarray(w.cand_timestamps, np.int64)[plan.order]).to(dev)
+    caches = [hstu.make_cache(dw.offsets, dw.timestamps, kc[l], vc[l], w.max_seq_len)
+              for l in range(L)]
+    mbs = []
+    for (start, offs, mlen) in plan.micro_batches:
+        n = int(offs[-1])
+        if n == 0:
+            continue
+        offs_d = torch.from_numpy(offs).to(dev)
+        tgt_d = torch.from_numpy(np.diff(offs).astype(np.int32)).to(dev)
+        jag = hstu.Jagged(len(offs) - 1, mlen, n, hstu.ptr(offs_d), hstu.ptr(cts) + 8 * start,
+                          hstu.ptr(tgt_d))
+        mbs.append((start, n, jag, offs_d, tgt_d, hstu.workspace_tensor(
+            hstu.hstu_layer_workspace_size(dw.desc, jag))))
+    Tc = sum(m[1] for m in mbs)
+    cbuf = [torch.empty_like(cx), torch.empty_like(cx)]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def history():
+        h = dw.x
+        for l in range(L):
+            y = hbuf[l % 2]
+            hstu.hstu_layer_fwd(dw.desc, dw.layers[l].params, dw.jagged, None, h, y, kc[l], vc[l], ws, sh)
+            h = y
+
+    def candidates():
+        for (start, n, jag, _, _, wsc) in mbs:
+            h = cx[start:start + n]
+            for l in range(L):
+                y = cbuf[l % 2][start:start + n]
+                hstu.hstu_layer_fwd(dw.desc, dw.layers[l].params, jag, caches[l], h, y, None, None,
+                                    wsc, sh)
+                h = y
+
+    def step():
+        history()
+        candidates()
+
+    ms = timed(step, stream, args.warmup, args.steps)
+    ms_h = timed(history, stream, 1, args.steps)
+    ms_c = timed(candidates, stream, 1, args.steps)
+    rec = base_record(args, "HSTU ranking fwd tokens/s (history + candidates, 4 layers), 1 GPU",
+                      (Th + Tc) / (ms * 1e-3), "tokens/s", ms, w.dtype,
+                      {"workload": gen.CONFIG_NAMES[4], "history_tokens": Th, "candidates": Tc,
+                       "users": w.num_seqs, "layers": L, "micro_batch": plan.b_m,
+                       "micro_batches": len(mbs), "d_model": d, "num_heads": w.num_heads})
+    rec["history_tokens_per_s"] = Th / (ms_h * 1e-3)
+    rec["history_ms"] = ms_h
+    rec["candidates_per_s"] = Tc / (ms_c * 1e-3)
+    rec["candidates_ms"] = ms_c
+    rec["roofline"] = None
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_ranking(w, args.cpu_budget_s)
+    return rec
+
+
+def cpu_baseline_ranking(w, budget_s):
+    """The CPU oracle's ranking (history through every layer, then every
+    candidate micro-batch against the cached history) on the first users of
+    the same workload until ~budget_s of work is done."""
+    import dataclasses
+
+    import numpy as np
+
+    import oracle
+    threads = oracle_threads()
+    tokens = users = 0
+    t0 = time.perf_counter()
+    for u in range(w.num_seqs):
+        s, e = int(w.offsets[u]), int(w.offsets[u + 1])
+        cs, ce = int(w.cand_offsets[u]), int(w.cand_offsets[u + 1])
+        sub = dataclasses.replace(
+            w, offsets=np.array([0, e - s], np.int64), timestamps=w.timestamps[s:e], x=w.x[s:e],
+            cand_offsets=np.array([0, ce - cs], np.int64),
+            cand_timestamps=w.cand_timestamps[cs:ce], cand_x=w.cand_x[cs:ce])
+        oracle.ranking(sub)
+        tokens += (e - s) + (ce - cs)
+        users += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"float64 NumPy oracle ranking (history + candidates, {len(w.layers)} layers) "
+                      f"for the first {users} user(s) ({tokens} tokens) of the same workload, "
+                      f"{dt:.1f} s"}
+
+
+def oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] + [1]))
+    except Exception:  # pragma: no cover
+        return os.cpu_count()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(sequences are independent; see the sharding note in the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch  # noqa: F401  (torch's HIP runtime first, then the library bound to it)
+
+    from hstu_sequential_transducer_jagged_amd import hstu
+    hstu.load()
+    run = {3: run_stack, 4: run_ranking}.get(args.workload, run_layer)
+    print(json.dumps(run(args)), flush=True)
 
 
 if __name__ == "__main__":

@@ -107,6 +107,11 @@ hstu::AttnArgs make_attn_args(const hstu_layer_desc* d, const hstu_jagged* j,
                               void* ws) {
   hstu::AttnArgs a{};
   a.sched = static_cast<int*>(ws);
+  a.total_tokens = j->total_tokens;
+  a.splits = d->dtype == HSTU_BF16 ? hstu::attn_splits(j->num_seqs, j->max_seq_len) : 1;
+  a.partial = a.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                                      hstu::attn_sched_bytes(j->num_seqs, j->max_seq_len))
+                           : nullptr;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -176,14 +181,15 @@ size_t round256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
 size_t attn_ws(const hstu_layer_desc* d, const hstu_jagged* j) {
   if (d->dtype != HSTU_BF16 || j->num_seqs <= 0 || j->max_seq_len <= 0) return 0;
-  return round256(hstu::attn_workspace_bytes(j->num_seqs, j->max_seq_len));
+  return round256(hstu::attn_workspace_bytes(j->num_seqs, j->max_seq_len, j->total_tokens, d->d_model));
 }
 
-// the work list indexes items as seq * n_tiles + tile in int32
+// the work list indexes (item, key chunk) units, item = seq * n_tiles + tile,
+// in int32
 int check_items(const hstu_jagged* j) {
   const int64_t n_qt = (static_cast<int64_t>(j->max_seq_len) + 63) / 64;
-  CHECK(static_cast<int64_t>(j->num_seqs) * n_qt < (int64_t{1} << 31) - 1, HSTU_E_UNSUPPORTED,
-        "num_seqs * ceil(max_seq_len / 64) must stay below 2^31");
+  CHECK(static_cast<int64_t>(j->num_seqs) * n_qt * 8 < (int64_t{1} << 31) - 1, HSTU_E_UNSUPPORTED,
+        "num_seqs * ceil(max_seq_len / 64) must stay below 2^28");
   return HSTU_OK;
 }
 

@@ -35,6 +35,8 @@
 #include "common.h"
 #include "internal.h"
 
+#include <algorithm>
+
 namespace hstu {
 namespace {
 
@@ -343,35 +345,55 @@ __device__ __forceinline__ int tile_steps(const SeqInfo& si, int qt) {
 constexpr int kNumXcd = 8;            // XCDs of the chip; workgroup id -> XCD id % 8
 constexpr int kCostBuckets = 1024;    // cost classes of the per-XCD sort
 constexpr int kSchedHead = kNumXcd + 1;
+constexpr int64_t kSplitMinUnits = 512;  // below this many items, key ranges are split
+constexpr int kMaxSplits = 8;
 
-__device__ __forceinline__ int item_cost(const AttnArgs& a, int n_qt, int i) {
+// Key steps [lo, hi) of chunk c of an item with n steps: chunks of ceil(n / S)
+// steps; trailing chunks may be empty.
+__device__ __forceinline__ void chunk_range(int n, int S, int c, int& lo, int& hi) {
+  const int per = (n + S - 1) / S;
+  lo = min(c * per, n);
+  hi = min(lo + per, n);
+}
+
+// Cost of work unit u = item * S + chunk: its key steps, at least 1 for a
+// non-empty item (an empty chunk still writes its zero partial); 0 for an
+// empty tile (never scheduled).
+__device__ __forceinline__ int unit_cost(const AttnArgs& a, int n_qt, int u) {
+  const int S = a.splits;
+  const int i = u / S, ch = u - i * S;
   const int b = i / n_qt, t = i - b * n_qt;
   const SeqInfo si = seq_info(a, b);
   // tiles past max_seq_len (a violated contract) are never reached: t < n_qt
-  return t * kBM < si.L ? tile_steps(si, t) : 0;
+  if (t * kBM >= si.L) return 0;
+  int lo, hi;
+  chunk_range(tile_steps(si, t), S, ch, lo, hi);
+  return max(hi - lo, 1);
 }
 
 // Work list of the bf16 attention. Items are the non-empty (sequence,
-// 64-query tile) pairs; an item's cost is its number of key steps.
-//  1. Items, in (sequence, tile) order, are cut into kNumXcd contiguous runs
+// 64-query tile) pairs, each cut into a.splits units of consecutive key steps
+// (one unit per item unless the batch has few items); a unit's cost is its
+// number of key steps.
+//  1. Units, in (sequence, tile, chunk) order, are cut into kNumXcd contiguous runs
 //     of equal total cost; run x goes to XCD x. The workgroups of one XCD
 //     then work on one or a few sequences at a time and share their K/V rows
 //     in that XCD's L2.
 //  2. Within a run, items are counting-sorted by cost, most expensive first,
 //     so that the XCD's compute units finish together.
-// sched[x] (x = 0..8): first list index of XCD x (sched[8] = item count);
-// sched[9 + k]: item (seq * n_qt + tile) at list index k.
+// sched[x] (x = 0..8): first list index of XCD x (sched[8] = unit count);
+// sched[9 + k]: unit ((seq * n_qt + tile) * splits + chunk) at list index k.
 __global__ __launch_bounds__(1024) void attn_schedule_kernel(AttnArgs a, int n_qt) {
   __shared__ int cnt[kNumXcd * kCostBuckets];
   __shared__ long long part[1024];
   const int tid = threadIdx.x;
-  const int items = a.num_seqs * n_qt;
+  const int items = a.num_seqs * n_qt * a.splits;
   for (int i = tid; i < kNumXcd * kCostBuckets; i += 1024) cnt[i] = 0;
   // each thread owns a contiguous chunk of items
   const int per = (items + 1023) / 1024;
   const int i0 = min(tid * per, items), i1 = min(i0 + per, items);
   long long sum = 0;
-  for (int i = i0; i < i1; ++i) sum += item_cost(a, n_qt, i);
+  for (int i = i0; i < i1; ++i) sum += unit_cost(a, n_qt, i);
   part[tid] = sum;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
@@ -391,7 +413,7 @@ __global__ __launch_bounds__(1024) void attn_schedule_kernel(AttnArgs a, int n_q
   };
   long long run = run0;
   for (int i = i0; i < i1; ++i) {
-    const int c = item_cost(a, n_qt, i);
+    const int c = unit_cost(a, n_qt, i);
     if (c > 0) atomicAdd(&cnt[key_of(run, c)], 1);
     run += c;
   }
@@ -422,7 +444,7 @@ __global__ __launch_bounds__(1024) void attn_schedule_kernel(AttnArgs a, int n_q
   if (tid == kNumXcd) a.sched[kNumXcd] = static_cast<int>(part[1023]);
   run = run0;
   for (int i = i0; i < i1; ++i) {
-    const int c = item_cost(a, n_qt, i);
+    const int c = unit_cost(a, n_qt, i);
     if (c > 0) a.sched[kSchedHead + atomicAdd(&cnt[key_of(run, c)], 1)] = i;
     run += c;
   }
@@ -455,7 +477,9 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
   const int list_step = gridDim.x / kNumXcd;
   for (int li = a.sched[xcd] + static_cast<int>(blockIdx.x) / kNumXcd; li < list_end; li += list_step) {
   __syncthreads();   // the previous item's LDS reads are done
-  const int item = a.sched[kSchedHead + li];
+  const int unit = a.sched[kSchedHead + li];
+  const int item = unit / a.splits;
+  const int chunk = unit - item * a.splits;
   const int n_qt = (a.max_seq_len + kBM - 1) / kBM;
   const int seq = item / n_qt;
   const int qt = item - seq * n_qt;
@@ -526,6 +550,12 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
   const int n_skip = skip_b - skip_a;
   const int n_steps = n_kt - n_skip;
   auto tile_of = [=](int st) { return st < skip_a ? st : st + n_skip; };
+  // key steps [st_lo, st_hi) of this unit's chunk
+  int st_lo, st_hi;
+  chunk_range(n_steps, a.splits, chunk, st_lo, st_hi);
+  // partial outputs of split items go to their chunk's slice of a.partial
+  float* __restrict__ out = a.splits > 1 ? a.partial + static_cast<int64_t>(chunk) * a.total_tokens * a.d_model
+                                         : a.av;
 
   // ---- per-slot query data of the bias builder ----
   SlotQ<SPT> sq;
@@ -588,13 +618,14 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
   // (+8, +16*kh), dims 32db + 16*(g16&1) + 4*(sl&3)
   const int voff = (4 * h2 + (sl >> 2)) * ROWBV + (hcol + 16 * (g16 & 1) + 4 * (sl & 3)) * 2;
 
-  // ---- prologue: key data of tiles 0 and 1, K/V and bias of tile 0 ----
-  load_keydata<HPB>(c, a.ts, a.c_ts, a.pos_bias, sD0, tile_of(0), wave, lane);
-  load_keydata<HPB>(c, a.ts, a.c_ts, a.pos_bias, sD1, tile_of(min(1, n_steps - 1)), wave, lane);
-  load_kv<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, sK0, sV0, tile_of(0), wave, lane);
+  if (st_lo < st_hi) {
+  // ---- prologue: key data of tiles lo and lo+1, K/V and bias of tile lo ----
+  load_keydata<HPB>(c, a.ts, a.c_ts, a.pos_bias, sD0, tile_of(st_lo), wave, lane);
+  load_keydata<HPB>(c, a.ts, a.c_ts, a.pos_bias, sD1, tile_of(min(st_lo + 1, st_hi - 1)), wave, lane);
+  load_kv<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, sK0, sV0, tile_of(st_lo), wave, lane);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  build_bias<HPB>(c, sq, sD0, sB0, tb_clz, tb_lin, a.nb, tile_of(0), tid);
+  build_bias<HPB>(c, sq, sD0, sB0, tb_clz, tb_lin, a.nb, tile_of(st_lo), tid);
   __syncthreads();
 
   // Step `st` computes key tile st from buffer st&1. After issuing its score
@@ -607,9 +638,9 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
     const int nxt = st + 1;                                                                      \
     f32x16 sc[2];                                                                                \
     scores<HPB>(CUR_K, CUR_B, qf, sc, koff, lane);                                               \
-    if (nxt < n_steps) {                                                                         \
+    if (nxt < st_hi) {                                                                         \
       load_kv<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, NXT_K, NXT_V, tile_of(nxt), wave, lane); \
-      if (st + 2 < n_steps)                                                                      \
+      if (st + 2 < st_hi)                                                                      \
         load_keydata<HPB>(c, a.ts, a.c_ts, a.pos_bias, CUR_D, tile_of(st + 2), wave, lane);      \
       build_bias<HPB>(c, sq, NXT_D, NXT_B, tb_clz, tb_lin, a.nb, tile_of(nxt), tid);             \
     }                                                                                            \
@@ -623,15 +654,15 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                             \
     __syncthreads();                                                                             \
   }
-  for (int st = 0; st < n_steps; ++st) {
+  for (int st = st_lo; st < st_hi; ++st) {
     HSTU_ATTN_STEP(sK0, sV0, sB0, sD0, sK1, sV1, sB1, sD1)
-    if (++st >= n_steps) break;
+    if (++st >= st_hi) break;
     HSTU_ATTN_STEP(sK1, sV1, sB1, sD1, sK0, sV0, sB0, sD0)
   }
+  }   // non-empty chunk
 #undef HSTU_ATTN_STEP
 
   // ---- AV = -ln2 * O: lane -> query qb*32 + 8(r/4) + 4*h2 + r%4, dim 32db + lane%32 ----
-  float* __restrict__ out = a.av;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -702,9 +733,43 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 
 }  // namespace
 
-size_t attn_workspace_bytes(int num_seqs, int max_seq_len) {
+int attn_splits(int num_seqs, int max_seq_len) {
+  const int64_t items = static_cast<int64_t>(num_seqs) * ((static_cast<int64_t>(max_seq_len) + kBM - 1) / kBM);
+  if (items <= 0 || items >= kSplitMinUnits) return 1;
+  return static_cast<int>(std::min<int64_t>(kMaxSplits, (kSplitMinUnits + items - 1) / items));
+}
+
+size_t attn_sched_bytes(int num_seqs, int max_seq_len) {
   const int64_t n_qt = (static_cast<int64_t>(max_seq_len) + kBM - 1) / kBM;
-  return static_cast<size_t>(kSchedHead + static_cast<int64_t>(num_seqs) * n_qt) * sizeof(int);
+  const int64_t units = static_cast<int64_t>(num_seqs) * n_qt * attn_splits(num_seqs, max_seq_len);
+  const size_t bytes = static_cast<size_t>(kSchedHead + units) * sizeof(int);
+  return (bytes + 255) & ~static_cast<size_t>(255);
+}
+
+size_t attn_workspace_bytes(int num_seqs, int max_seq_len, int64_t total_tokens, int d_model) {
+  const int S = attn_splits(num_seqs, max_seq_len);
+  const size_t partial = S > 1 ? static_cast<size_t>(S) * total_tokens * d_model * sizeof(float) : 0;
+  return attn_sched_bytes(num_seqs, max_seq_len) + partial;
+}
+
+// AV = sum over chunks of the partial outputs, in chunk order (deterministic).
+__global__ __launch_bounds__(256) void attn_reduce_kernel(const float* __restrict__ partial,
+                                                          float* __restrict__ av, int64_t n4,
+                                                          int64_t stride4, int splits) {
+  const float4* p = reinterpret_cast<const float4*>(partial);
+  float4* o = reinterpret_cast<float4*>(av);
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n4;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    float4 acc = p[i];
+    for (int c = 1; c < splits; ++c) {
+      const float4 v = p[c * stride4 + i];
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    o[i] = acc;
+  }
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
@@ -717,14 +782,21 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
       hpb = c;
       break;
     }
-  // a multiple of the XCD count, one workgroup per item on average
-  const int64_t items = static_cast<int64_t>(a.num_seqs) * n_qt;
-  dim3 grid(static_cast<unsigned>((items + kNumXcd - 1) / kNumXcd * kNumXcd), a.num_heads / hpb);
+  // a multiple of the XCD count, one workgroup per unit on average
+  const int64_t units = static_cast<int64_t>(a.num_seqs) * n_qt * a.splits;
+  dim3 grid(static_cast<unsigned>((units + kNumXcd - 1) / kNumXcd * kNumXcd), a.num_heads / hpb);
   switch (hpb) {
     case 8: hipLaunchKernelGGL(attn_bf16_kernel<8>, grid, dim3(512), 0, s, a); break;
     case 4: hipLaunchKernelGGL(attn_bf16_kernel<4>, grid, dim3(256), 0, s, a); break;
     case 2: hipLaunchKernelGGL(attn_bf16_kernel<2>, grid, dim3(128), 0, s, a); break;
     default: hipLaunchKernelGGL(attn_bf16_kernel<1>, grid, dim3(64), 0, s, a); break;
+  }
+  if (a.splits > 1) {
+    const int64_t n4 = a.total_tokens * a.d_model / 4;
+    const int blocks = static_cast<int>(std::min<int64_t>((n4 + 255) / 256, 4096));
+    if (n4 > 0)
+      hipLaunchKernelGGL(attn_reduce_kernel, dim3(blocks), dim3(256), 0, s, a.partial, a.av, n4, n4,
+                         a.splits);
   }
   return hipGetLastError();
 }

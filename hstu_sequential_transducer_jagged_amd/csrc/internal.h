@@ -33,11 +33,19 @@ struct AttnArgs {
   int num_seqs;
   int max_seq_len;
   int max_cache_len;
+  int64_t total_tokens;      // T
   int* sched;                // bf16 path: work list built by the scheduling pass
+  int splits;                // bf16 path: key-range chunks per (sequence, query tile)
+  float* partial;            // [splits, T, d] fp32 partial outputs when splits > 1
 };
 
-// Workspace bytes of the bf16 attention (its work list).
-size_t attn_workspace_bytes(int num_seqs, int max_seq_len);
+// bf16 attention: number of key-range chunks per work item (1 unless the
+// batch has too few (sequence, query tile) items to fill the chip).
+int attn_splits(int num_seqs, int max_seq_len);
+// Workspace bytes of the bf16 attention: the work list, then (splits > 1) the
+// partial outputs.
+size_t attn_sched_bytes(int num_seqs, int max_seq_len);
+size_t attn_workspace_bytes(int num_seqs, int max_seq_len, int64_t total_tokens, int d_model);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
 

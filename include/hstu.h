@@ -130,9 +130,12 @@ const char *hstu_last_error(void);
 int hstu_proj_fwd(const hstu_layer_desc *desc, const hstu_layer_params *params, int64_t T,
                   const void *x, void *u, void *v, void *q, void *k, void *stream);
 
-/* Workspace bytes hstu_attn_fwd needs for this batch (bf16: the work list
- * of its scheduling pass, 4 * (9 + num_seqs * ceil(max_seq_len / 64)) bytes
- * rounded up to 256; f32: 0). */
+/* Workspace bytes hstu_attn_fwd needs for this batch. bf16: the work list
+ * of its scheduling pass, 4 * (9 + U) bytes rounded up to 256, with
+ * U = I * S units, I = num_seqs * ceil(max_seq_len / 64) (sequence, query
+ * tile) items and S key-range splits per item (S = 1 when I >= 512, else
+ * min(8, ceil(512 / I)); then, when S > 1, S partial outputs of
+ * total_tokens x d_model fp32. f32: 0. */
 size_t hstu_attn_workspace_size(const hstu_layer_desc *desc, const hstu_jagged *jagged);
 
 /* Spatial aggregation, §2.1 second equation, with the visibility, position

@@ -114,7 +114,9 @@ def test_layer_workspace_checks(lib):
     d = _desc()
     need = lib.hstu_layer_workspace_size(ctypes.byref(d), ctypes.byref(_jag()))
     attn = lib.hstu_attn_workspace_size(ctypes.byref(d), ctypes.byref(_jag()))
-    assert attn == 256            # 4 * (9 + 2 sequences * 1 tile), rounded to 256
+    # 2 items (< 512) -> 8 key-range splits: work list 4 * (9 + 2 * 8) bytes
+    # rounded to 256, then 8 partial outputs of T x d fp32
+    assert attn == 256 + 8 * 10 * 512 * 4
     assert need == 4 * 10240 + 20480 + attn
     f = hstu.make_desc(64, 2, hstu.HSTU_F32, 255)
     assert lib.hstu_attn_workspace_size(ctypes.byref(f), ctypes.byref(_jag())) == 0
