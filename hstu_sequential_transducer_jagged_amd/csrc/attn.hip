@@ -29,6 +29,10 @@
 //    (lane = query, 16 keys) is the A-operand layout of the S.V MFMA, so P
 //    stays in registers; V's B operand is read with ds_read_b64_tr_b16
 //    (transposing 16-bit reads) from the row-major tile;
+//  * software pipeline in half tiles: while the score MFMAs of one 32-query
+//    block run, the SiLU and P.V of the previous block do, so the matrix
+//    cores and the vector ALUs of a wave overlap; the DMA of the next tile
+//    is spread over the step;
 //  * time buckets are exact integers: 32-bit |dt|+1 and a leading-zero count
 //    when every pair of the tile is within 2^30 s of the block's reference
 //    time, a 64-bit path otherwise.
@@ -161,44 +165,53 @@ __device__ __forceinline__ void load_keydata(const Ctx& c, const int64_t* ts, co
   }
 }
 
-// Direct global->LDS loads of the K and V rows of a key tile. Wave w loads
-// rows w, w + HPB, ... of K and of V (rows past the last key repeat it; their
-// scores are masked). Row pointers are wave-uniform: block key kk lives at
-// base + kk*d for both the own rows (base shifted back by the cache length)
-// and the cache rows; only the lane's 16-byte column offset is per lane. A
-// tile that lies inside one source and before the last key takes its rows at
-// a fixed stride from one base.
-template <int HPB>
-__device__ __forceinline__ void load_kv(const Ctx& c, const uint16_t* kbase_o, const uint16_t* kbase_c,
-                                        const uint16_t* vbase_o, const uint16_t* vbase_c, uint8_t* sk,
-                                        uint8_t* sv, int tile, int wave, int lane) {
-  constexpr int RK = Rows<HPB>::ROWBK;
-  constexpr int RV = Rows<HPB>::ROWBV;
-  const int k0 = tile * kBN;
-  if (lane >= HPB * 8) return;
-  const bool uniform = (k0 + kBN <= c.nkeys) && (k0 >= c.nc || k0 + kBN <= c.nc);
-  if (uniform) {
-    const bool cached = k0 < c.nc;
-    const int64_t off = static_cast<int64_t>(k0) * c.d + lane * 8;
-    const uint16_t* kt = (cached ? kbase_c : kbase_o) + off;
-    const uint16_t* vt = (cached ? vbase_c : vbase_o) + off;
+// One DMA row of a K or V tile: block key min(k0 + r, nkeys - 1) into LDS row
+// r. The source row is wave-uniform (scalar address arithmetic); the lane adds
+// its 16-byte column offset.
+template <int HPB, int ROWB>
+__device__ __forceinline__ void dma_row(const Ctx& c, const uint16_t* base_o, const uint16_t* base_c,
+                                        uint8_t* dst, int k0, int r, int lane) {
+  if (HPB < 8 && lane >= HPB * 8) return;
+  const int kk = min(k0 + r, c.nkeys - 1);
+  const uint16_t* src = (kk < c.nc ? base_c : base_o) + static_cast<int64_t>(kk) * c.d;
+  __builtin_amdgcn_global_load_lds(src + lane * 8, LDS_PTR(void, dst + r * ROWB), 16, 0, 0);
+}
+
+// P = S' / (1 + 2^S') for scores [8h, 8h + 8) of one accumulator, packed to
+// bf16 as one A operand of the P.V MFMA.
+__device__ __forceinline__ bf16x8 silu8(const f32x16& st, int h) {
+  uint32_t pk[4];
 #pragma unroll
-    for (int it = 0; it < kBN / HPB; ++it) {
-      const int r = wave + it * HPB;
-      const int64_t ro = static_cast<int64_t>(r) * c.d;
-      __builtin_amdgcn_global_load_lds(kt + ro, LDS_PTR(void, sk + r * RK), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vt + ro, LDS_PTR(void, sv + r * RV), 16, 0, 0);
-    }
-  } else {
+  for (int r = 0; r < 8; r += 2) {
+    const float x0 = st[8 * h + r], x1 = st[8 * h + r + 1];
+    const float p0 = x0 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x0));
+    const float p1 = x1 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x1));
+    pk[r >> 1] = pack_bf16x2(p0, p1);
+  }
+  return __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+}
+
+// P for scores [4q, 4q + 4) of one accumulator, as two packed bf16 pairs.
+__device__ __forceinline__ void silu4(const f32x16& st, int q, uint32_t& w0, uint32_t& w1) {
+  float p[4];
 #pragma unroll
-    for (int it = 0; it < kBN / HPB; ++it) {
-      const int r = wave + it * HPB;
-      const int kk = min(k0 + r, c.nkeys - 1);
-      const bool cached = kk < c.nc;
-      const int64_t off = static_cast<int64_t>(kk) * c.d + lane * 8;
-      __builtin_amdgcn_global_load_lds((cached ? kbase_c : kbase_o) + off, LDS_PTR(void, sk + r * RK), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((cached ? vbase_c : vbase_o) + off, LDS_PTR(void, sv + r * RV), 16, 0, 0);
-    }
+  for (int r = 0; r < 4; ++r) {
+    const float x = st[4 * q + r];
+    p[r] = x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
+  }
+  w0 = pack_bf16x2(p[0], p[1]);
+  w1 = pack_bf16x2(p[2], p[3]);
+}
+
+// Bias tile rows of one 32-query block as the initial S^T accumulator.
+__device__ __forceinline__ void load_bias_block(const float* bias, int qb, int lane, f32x16& st) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float4 bv = *reinterpret_cast<const float4*>(&bias[((qb * 4 + j) * 64 + lane) * 4]);
+    st[4 * j + 0] = bv.x;
+    st[4 * j + 1] = bv.y;
+    st[4 * j + 2] = bv.z;
+    st[4 * j + 3] = bv.w;
   }
 }
 
@@ -266,45 +279,68 @@ __device__ __forceinline__ void build_bias(const Ctx& c, const SlotQ<512 / (64 *
   }
 }
 
-// One wave's share of a key tile, in phases so that the step can interleave
-// other work between them: S^T = K Q^T + bias for both 32-query blocks
-// (two independent MFMA chains), then per block P = S' / (1 + 2^S') and
-// O += P V.
+// The full-tile bias of build_bias split in three pieces, so that its LDS
+// round trips overlap other work: issue the key-data reads, then (once they
+// are back) the time-bias lookups, then combine and store. Valid for tiles
+// whose keys are all visible non-targets and a 32-bit time span; on other
+// tiles it writes bounded garbage that build_bias then overwrites.
+template <int SPT>
+struct FastBias {
+  uint32_t tk[SPT][4];
+  float pw[SPT][4];
+  float tb[SPT][4];
+};
+
 template <int HPB>
-__device__ __forceinline__ void scores(const uint8_t* kb, const float* bias,
-                                       const bf16x8 (&qf)[2][4], f32x16 (&st)[2], int koff,
-                                       int lane) {
-  bf16x8 kf[4];
+__device__ __forceinline__ void fast_bias_issue(const Ctx& c, const SlotQ<512 / (64 * HPB)>& sq,
+                                                const KeyData& kd, int tile, int tid,
+                                                FastBias<512 / (64 * HPB)>& fb) {
+  constexpr int NT = 64 * HPB;
+  constexpr int SPT = 512 / NT;
+  const int k0 = tile * kBN;
+  const int w0 = window_origin(c, tile);
 #pragma unroll
-  for (int cc = 0; cc < 4; ++cc)
-    kf[cc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + koff + cc * 32));
+  for (int i = 0; i < SPT; ++i) {
+    const int slot = tid + i * NT;
+    const int kr = 8 * ((slot >> 6) & 3) + 4 * ((slot >> 5) & 1);
+    const uint4 t4 = *reinterpret_cast<const uint4*>(&kd.tlo[kr]);
+    fb.tk[i][0] = t4.x;
+    fb.tk[i][1] = t4.y;
+    fb.tk[i][2] = t4.z;
+    fb.tk[i][3] = t4.w;
+    int pb = sq.pq[i] - (k0 + kr) - w0;   // p_k = kk for non-target keys
+    pb = pb < 3 ? 3 : (pb > kPosWin - 1 ? kPosWin - 1 : pb);
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 bv = *reinterpret_cast<const float4*>(&bias[((qb * 4 + j) * 64 + lane) * 4]);
-      st[qb][4 * j + 0] = bv.x;
-      st[qb][4 * j + 1] = bv.y;
-      st[qb][4 * j + 2] = bv.z;
-      st[qb][4 * j + 3] = bv.w;
-    }
-#pragma unroll
-  for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) st[qb] = mfma32(kf[cc], qf[qb][cc], st[qb]);
+    for (int r = 0; r < 4; ++r) fb.pw[i][r] = kd.pos[pb - r];
+  }
 }
 
-__device__ __forceinline__ void silu_pack(const f32x16& st, bf16x8 (&pa)[2]) {
-  uint32_t pk[8];
+template <int HPB>
+__device__ __forceinline__ void fast_bias_lookup(const Ctx& c, const SlotQ<512 / (64 * HPB)>& sq,
+                                                 const float* tb_clz, FastBias<512 / (64 * HPB)>& fb) {
+  constexpr int SPT = 512 / (64 * HPB);
 #pragma unroll
-  for (int r = 0; r < 16; r += 2) {
-    const float x0 = st[r], x1 = st[r + 1];
-    const float p0 = x0 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x0));
-    const float p1 = x1 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x1));
-    pk[r >> 1] = pack_bf16x2(p0, p1);
+  for (int i = 0; i < SPT; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t x = sq.uq[i], y = fb.tk[i][r] - c.tb_lo;
+      const uint32_t ad = (x > y ? x - y : y - x) + 1u;   // |dt| + 1 >= 1
+      fb.tb[i][r] = tb_clz[__builtin_clz(ad)];
+    }
+}
+
+template <int HPB>
+__device__ __forceinline__ void fast_bias_store(const FastBias<512 / (64 * HPB)>& fb, float* bias, int tid) {
+  constexpr int NT = 64 * HPB;
+  constexpr int SPT = 512 / NT;
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    const int slot = tid + i * NT;
+    float b[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) b[r] = __builtin_fmaf(fb.pw[i][r], -kLog2e, fb.tb[i][r]);
+    *reinterpret_cast<float4*>(&bias[slot * 4]) = make_float4(b[0], b[1], b[2], b[3]);
   }
-  pa[0] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-  pa[1] = __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]));
 }
 
 // V's B operands for both 16-key halves and both 32-dim blocks (transposing
@@ -322,11 +358,112 @@ __device__ __forceinline__ void load_v(const uint8_t* vb, int voff, bf16x8 (&vf)
     }
 }
 
-__device__ __forceinline__ void pv(const bf16x8 (&pa)[2], const bf16x8 (&vf)[2][2], f32x16 (&acc)[2]) {
+// DMA slot `slot` (0..7) of a step: an eighth of the K and V rows of key
+// tile k0 / kBN (K rows in even slots, V rows in odd ones).
+template <int HPB>
+__device__ __forceinline__ void dma_slot(const Ctx& c, const uint16_t* kbase_o, const uint16_t* kbase_c,
+                                         const uint16_t* vbase_o, const uint16_t* vbase_c,
+                                         uint8_t* __restrict__ nk, uint8_t* __restrict__ nv, int k0, int slot,
+                                         int wave, int lane) {
+  constexpr int RPW = kBN / HPB;   // rows per wave of one tile
+  constexpr int RPS = RPW / 4;     // rows per slot
 #pragma unroll
-  for (int kh = 0; kh < 2; ++kh)
+  for (int it = 0; it < RPS; ++it) {
+    const int r = wave + ((slot >> 1) * RPS + it) * HPB;
+    if (slot & 1) dma_row<HPB, Rows<HPB>::ROWBV>(c, vbase_o, vbase_c, nv, k0, r, lane);
+    else dma_row<HPB, Rows<HPB>::ROWBK>(c, kbase_o, kbase_c, nk, k0, r, lane);
+  }
+}
+
+// One round of a step: SiLU of the previous 32-query score block `sp`, in
+// quarters, overlapped with the four score MFMAs of block `qb` into `sn` (in
+// the second half of the round, when its LDS operands have landed) and the
+// P.V MFMAs into `o`. `extra(sr)` runs after quarter sr.
+template <typename Extra>
+__device__ __forceinline__ void attn_round(const f32x16& sp, f32x16& sn, const bf16x8 (&kf)[4],
+                                           const bf16x8 (&q)[4], const bf16x8 (&vf)[2][2], f32x16 (&o)[2],
+                                           uint32_t (&w)[8], Extra extra) {
 #pragma unroll
-    for (int db = 0; db < 2; ++db) acc[db] = mfma32(pa[kh], vf[db][kh], acc[db]);
+  for (int sr = 0; sr < 4; ++sr) {
+    silu4(sp, sr, w[2 * sr], w[2 * sr + 1]);
+    extra(sr);
+    if (sr >= 2) {
+      sn = mfma32(kf[2 * (sr - 2)], q[2 * (sr - 2)], sn);
+      sn = mfma32(kf[2 * (sr - 2) + 1], q[2 * (sr - 2) + 1], sn);
+      const int kh = sr - 2;
+      const bf16x8 pk = __builtin_bit_cast(bf16x8, make_uint4(w[4 * kh], w[4 * kh + 1], w[4 * kh + 2], w[4 * kh + 3]));
+#pragma unroll
+      for (int db = 0; db < 2; ++db) o[db] = mfma32(pk, vf[db][kh], o[db]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One key step of the software pipeline (see the kernel). The LDS buffers
+// are distinct restrict-qualified arguments: the compiler can then tell that
+// a DMA into the next buffers does not alias the reads of the current ones,
+// and issues the DMA early without making those reads wait for it. MORE: a
+// later tile of the chunk follows (its DMA, key data and bias).
+template <int HPB, bool MORE>
+__device__ __forceinline__ void attn_step(
+    const Ctx& c, const SlotQ<512 / (64 * HPB)>& sq, const AttnArgs& a, int st, int st_hi, int skip_a,
+    int n_skip, const uint8_t* __restrict__ curK, const float* __restrict__ curB,
+    const uint8_t* __restrict__ curV, uint8_t* __restrict__ nxtK, uint8_t* __restrict__ nxtV,
+    float* __restrict__ nxtB, const KeyData* __restrict__ nxtD, KeyData* __restrict__ curD,
+    const float* __restrict__ tb_clz, const float* __restrict__ tb_lin, const uint16_t* kbase_o,
+    const uint16_t* kbase_c, const uint16_t* vbase_o, const uint16_t* vbase_c, const bf16x8 (&qf)[2][4],
+    f32x16 (&acc)[2][2], f32x16& s0, f32x16& s1, bf16x8 (&vf)[2][2], int koff, int voff, int wave, int lane,
+    int tid) {
+  constexpr int ROWBV = Rows<HPB>::ROWBV;
+  const int t1 = MORE ? (st + 1 < skip_a ? st + 1 : st + 1 + n_skip) : 0;
+  const int k1 = t1 * kBN;
+  // the bias of tile st+1 takes the split fast path when all its keys are
+  // visible non-targets for the whole block and times fit 32 bits
+  const bool fast1 = (k1 + kBN - 1 - c.nc <= c.q0) && (k1 + kBN - 1 - c.nc < c.first_tgt) && !c.wide;
+  FastBias<512 / (64 * HPB)> fb;
+  // A0: key data of tile st+2, key-data reads of tile st+1's bias
+  if (MORE && st + 2 < st_hi) {
+    const int t2 = st + 2 < skip_a ? st + 2 : st + 2 + n_skip;
+    load_keydata<HPB>(c, a.ts, a.c_ts, a.pos_bias, *curD, t2, wave, lane);
+  }
+  if (MORE) fast_bias_issue<HPB>(c, sq, *nxtD, t1, tid, fb);
+  __builtin_amdgcn_sched_barrier(0);
+  // R0: SiLU of block 1 of tile st-1 and its P.V; score MFMAs of block 0 of
+  // tile st (K and bias read at the end of the first quarter)
+  bf16x8 kf[4];
+  {
+    uint32_t w[8];
+    attn_round(s1, s0, kf, qf[0], vf, acc[1], w, [&](int sr) __attribute__((always_inline)) {
+      if (MORE) dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, nxtK, nxtV, k1, sr, wave, lane);
+      if (sr == 0) {
+        if (MORE) fast_bias_lookup<HPB>(c, sq, tb_clz, fb);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+          kf[cc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(curK + koff + cc * 32));
+        load_bias_block(curB, 0, lane, s0);
+      }
+      if (sr == 1 && MORE) fast_bias_store<HPB>(fb, nxtB, tid);
+    });
+  }
+  // A2: bias of block 1 into s1 (free now), V of tile st into vf
+  load_bias_block(curB, 1, lane, s1);
+  load_v<ROWBV>(curV, voff, vf);
+  __builtin_amdgcn_sched_barrier(0);
+  // R1: SiLU of block 0 of tile st and its P.V; score MFMAs of block 1
+  {
+    uint32_t w[8];
+    attn_round(s0, s1, kf, qf[1], vf, acc[0], w, [&](int sr) __attribute__((always_inline)) {
+      if (MORE) dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, nxtK, nxtV, k1, 4 + sr, wave, lane);
+    });
+    // keep the wait and the barrier after the SiLU of this step
+    asm volatile("" ::"v"(w[7]));
+  }
+  // tiles off the fast path: the full bias builder overwrites the tile
+  if (MORE && !fast1) build_bias<HPB>(c, sq, *nxtD, nxtB, tb_clz, tb_lin, a.nb, t1, tid);
+  if (MORE) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
 }
 
 // Number of key steps (32-key tiles visited) of query tile qt of a sequence:
@@ -619,47 +756,75 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
   const int voff = (4 * h2 + (sl >> 2)) * ROWBV + (hcol + 16 * (g16 & 1) + 4 * (sl & 3)) * 2;
 
   if (st_lo < st_hi) {
-  // ---- prologue: key data of tiles lo and lo+1, K/V and bias of tile lo ----
+  constexpr int RPW = kBN / HPB;   // DMA rows per wave of a K or V tile
+#define SK(i) ((i) ? sK1 : sK0)
+#define SV(i) ((i) ? sV1 : sV0)
+#define SB(i) ((i) ? sB1 : sB0)
+#define SD(i) ((i) ? &sD1 : &sD0)
+  // ---- prologue: key data of tiles lo and lo+1, K/V rows and bias of tile lo ----
   load_keydata<HPB>(c, a.ts, a.c_ts, a.pos_bias, sD0, tile_of(st_lo), wave, lane);
   load_keydata<HPB>(c, a.ts, a.c_ts, a.pos_bias, sD1, tile_of(min(st_lo + 1, st_hi - 1)), wave, lane);
-  load_kv<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, sK0, sV0, tile_of(st_lo), wave, lane);
+  {
+    const int k0 = tile_of(st_lo) * kBN;
+#pragma unroll
+    for (int it = 0; it < RPW; ++it) {
+      dma_row<HPB, ROWBK>(c, kbase_o, kbase_c, sK0, k0, wave + it * HPB, lane);
+      dma_row<HPB, ROWBV>(c, vbase_o, vbase_c, sV0, k0, wave + it * HPB, lane);
+    }
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   build_bias<HPB>(c, sq, sD0, sB0, tb_clz, tb_lin, a.nb, tile_of(st_lo), tid);
   __syncthreads();
 
-  // Step `st` computes key tile st from buffer st&1. After issuing its score
-  // MFMAs it starts the DMA of the K/V rows of tile st+1 and of the key data
-  // of tile st+2 into the other buffers, and builds the bias of tile st+1 from
-  // the key data that arrived a step earlier. Unrolled by two so that every
-  // buffer is a fixed LDS object.
-#define HSTU_ATTN_STEP(CUR_K, CUR_V, CUR_B, CUR_D, NXT_K, NXT_V, NXT_B, NXT_D)                    \
-  {                                                                                              \
-    const int nxt = st + 1;                                                                      \
-    f32x16 sc[2];                                                                                \
-    scores<HPB>(CUR_K, CUR_B, qf, sc, koff, lane);                                               \
-    if (nxt < st_hi) {                                                                         \
-      load_kv<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, NXT_K, NXT_V, tile_of(nxt), wave, lane); \
-      if (st + 2 < st_hi)                                                                      \
-        load_keydata<HPB>(c, a.ts, a.c_ts, a.pos_bias, CUR_D, tile_of(st + 2), wave, lane);      \
-      build_bias<HPB>(c, sq, NXT_D, NXT_B, tb_clz, tb_lin, a.nb, tile_of(nxt), tid);             \
-    }                                                                                            \
-    bf16x8 vf[2][2];                                                                             \
-    load_v<ROWBV>(CUR_V, voff, vf);                                                                \
-    bf16x8 pa[2];                                                                                \
-    silu_pack(sc[0], pa);                                                                        \
-    pv(pa, vf, acc[0]);                                                                          \
-    silu_pack(sc[1], pa);                                                                        \
-    pv(pa, vf, acc[1]);                                                                          \
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                             \
-    __syncthreads();                                                                             \
+  // Software pipeline in half tiles. Registers carried from step st-1 to
+  // step st: the scores of the second 32-query block of tile st-1 (s1) and
+  // the V operand of tile st-1 (vf). Step st (attn_step), buffers (st-lo)&1:
+  //  A0. DMA of the key data of tile st+2; LDS reads for the bias of st+1;
+  //  R0. SiLU of s1 and O1 += P V_{st-1}, overlapped with the score MFMAs of
+  //      block 0 of tile st into s0 (K and the bias as the initial value,
+  //      read from LDS early in the round); the bias of tile st+1 is
+  //      finished and stored; half of the K/V rows of tile st+1 by DMA;
+  //  A2. LDS: bias of block 1 into s1 (free now), V of tile st into vf;
+  //  R1. SiLU of s0 and O0 += P V_st, overlapped with the score MFMAs of
+  //      block 1 into s1; the other half of the DMA.
+  // After the last step, a drain runs the SiLU and P.V of s1.
+  // s1 and vf start at zero: the first step's R0 then adds exactly zero.
+  f32x16 s0, s1;
+  bf16x8 vf[2][2];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s1[r] = 0.f;
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) vf[db][kh] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+  // steps alternate between the two buffer sets
+#define HSTU_ATTN_STEP(MORE, K0, B0, V0, K1, V1, B1, D1, D0)                                          \
+  attn_step<HPB, MORE>(c, sq, a, st, st_hi, skip_a, n_skip, K0, B0, V0, K1, V1, B1, D1, D0, tb_clz,  \
+                       tb_lin, kbase_o, kbase_c, vbase_o, vbase_c, qf, acc, s0, s1, vf, koff, voff,      \
+                       wave, lane, tid)
+  int st = st_lo;
+#pragma clang loop unroll(disable)
+  for (; st + 1 < st_hi; ++st) {
+    const int p = (st - st_lo) & 1;
+    HSTU_ATTN_STEP(true, SK(p), SB(p), SV(p), SK(p ^ 1), SV(p ^ 1), SB(p ^ 1), SD(p ^ 1), SD(p));
   }
-  for (int st = st_lo; st < st_hi; ++st) {
-    HSTU_ATTN_STEP(sK0, sV0, sB0, sD0, sK1, sV1, sB1, sD1)
-    if (++st >= st_hi) break;
-    HSTU_ATTN_STEP(sK1, sV1, sB1, sD1, sK0, sV0, sB0, sD0)
+  {
+    const int p = (st - st_lo) & 1;
+    HSTU_ATTN_STEP(false, SK(p), SB(p), SV(p), SK(p ^ 1), SV(p ^ 1), SB(p ^ 1), SD(p ^ 1), SD(p));
+  }
+  // drain: SiLU and P.V of block 1 of the last tile
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    const bf16x8 pk = silu8(s1, kh);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) acc[1][db] = mfma32(pk, vf[db][kh], acc[1][db]);
   }
   }   // non-empty chunk
+#undef SK
+#undef SV
+#undef SB
+#undef SD
 #undef HSTU_ATTN_STEP
 
   // ---- AV = -ln2 * O: lane -> query qb*32 + 8(r/4) + 4*h2 + r%4, dim 32db + lane%32 ----
