@@ -203,6 +203,27 @@ __device__ __forceinline__ void silu4(const f32x16& st, int q, uint32_t& w0, uin
   w1 = pack_bf16x2(p[2], p[3]);
 }
 
+// One quarter (4 scores per lane) of load_bias_block.
+__device__ __forceinline__ void load_bias_quarter(const float* bias, int qb, int j, int lane, f32x16& st) {
+  const float4 bv = *reinterpret_cast<const float4*>(&bias[((qb * 4 + j) * 64 + lane) * 4]);
+  st[4 * j + 0] = bv.x;
+  st[4 * j + 1] = bv.y;
+  st[4 * j + 2] = bv.z;
+  st[4 * j + 3] = bv.w;
+}
+
+// V operands of one 16-key half (both 32-dim blocks).
+template <int ROWB>
+__device__ __forceinline__ void load_v_half(const uint8_t* vb, int voff, int kh, bf16x8 (&vf)[2][2]) {
+#pragma unroll
+  for (int db = 0; db < 2; ++db) {
+    const uint8_t* p = vb + voff + kh * 16 * ROWB + db * 64;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p + 8 * ROWB));
+    vf[db][kh] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+}
+
 // Bias tile rows of one 32-query block as the initial S^T accumulator.
 __device__ __forceinline__ void load_bias_block(const float* bias, int qb, int lane, f32x16& st) {
 #pragma unroll
@@ -338,24 +359,15 @@ __device__ __forceinline__ void fast_bias_store(const FastBias<512 / (64 * HPB)>
     const int slot = tid + i * NT;
     float b[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) b[r] = __builtin_fmaf(fb.pw[i][r], -kLog2e, fb.tb[i][r]);
+    for (int r = 0; r < 4; ++r) {
+      // pins the combine here: computed earlier, it would make the wave
+      // wait for every LDS read in flight
+      float tb = fb.tb[i][r];
+      asm volatile("" : "+v"(tb));
+      b[r] = __builtin_fmaf(fb.pw[i][r], -kLog2e, tb);
+    }
     *reinterpret_cast<float4*>(&bias[slot * 4]) = make_float4(b[0], b[1], b[2], b[3]);
   }
-}
-
-// V's B operands for both 16-key halves and both 32-dim blocks (transposing
-// 16-bit reads of the row-major tile).
-template <int ROWB>
-__device__ __forceinline__ void load_v(const uint8_t* vb, int voff, bf16x8 (&vf)[2][2]) {
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const uint8_t* p = vb + voff + kh * 16 * ROWB + db * 64;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p + 8 * ROWB));
-      vf[db][kh] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
 }
 
 // DMA slot `slot` (0..7) of a step: an eighth of the K and V rows of key
@@ -372,30 +384,6 @@ __device__ __forceinline__ void dma_slot(const Ctx& c, const uint16_t* kbase_o, 
     const int r = wave + ((slot >> 1) * RPS + it) * HPB;
     if (slot & 1) dma_row<HPB, Rows<HPB>::ROWBV>(c, vbase_o, vbase_c, nv, k0, r, lane);
     else dma_row<HPB, Rows<HPB>::ROWBK>(c, kbase_o, kbase_c, nk, k0, r, lane);
-  }
-}
-
-// One round of a step: SiLU of the previous 32-query score block `sp`, in
-// quarters, overlapped with the four score MFMAs of block `qb` into `sn` (in
-// the second half of the round, when its LDS operands have landed) and the
-// P.V MFMAs into `o`. `extra(sr)` runs after quarter sr.
-template <typename Extra>
-__device__ __forceinline__ void attn_round(const f32x16& sp, f32x16& sn, const bf16x8 (&kf)[4],
-                                           const bf16x8 (&q)[4], const bf16x8 (&vf)[2][2], f32x16 (&o)[2],
-                                           uint32_t (&w)[8], Extra extra) {
-#pragma unroll
-  for (int sr = 0; sr < 4; ++sr) {
-    silu4(sp, sr, w[2 * sr], w[2 * sr + 1]);
-    extra(sr);
-    if (sr >= 2) {
-      sn = mfma32(kf[2 * (sr - 2)], q[2 * (sr - 2)], sn);
-      sn = mfma32(kf[2 * (sr - 2) + 1], q[2 * (sr - 2) + 1], sn);
-      const int kh = sr - 2;
-      const bf16x8 pk = __builtin_bit_cast(bf16x8, make_uint4(w[4 * kh], w[4 * kh + 1], w[4 * kh + 2], w[4 * kh + 3]));
-#pragma unroll
-      for (int db = 0; db < 2; ++db) o[db] = mfma32(pk, vf[db][kh], o[db]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -421,40 +409,83 @@ __device__ __forceinline__ void attn_step(
   // visible non-targets for the whole block and times fit 32 bits
   const bool fast1 = (k1 + kBN - 1 - c.nc <= c.q0) && (k1 + kBN - 1 - c.nc < c.first_tgt) && !c.wide;
   FastBias<512 / (64 * HPB)> fb;
-  // A0: key data of tile st+2, key-data reads of tile st+1's bias
+  // A0: the key-data reads of tile st+1's bias go first, so that their
+  // dependent time-bias lookups are not queued behind this step's big LDS
+  // reads; DMA of the key data of tile st+2 and a quarter of the K/V rows
+  if (MORE) fast_bias_issue<HPB>(c, sq, *nxtD, t1, tid, fb);
   if (MORE && st + 2 < st_hi) {
     const int t2 = st + 2 < skip_a ? st + 2 : st + 2 + n_skip;
     load_keydata<HPB>(c, a.ts, a.c_ts, a.pos_bias, *curD, t2, wave, lane);
   }
-  if (MORE) fast_bias_issue<HPB>(c, sq, *nxtD, t1, tid, fb);
+  if (MORE) {
+    dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, nxtK, nxtV, k1, 0, wave, lane);
+    dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, nxtK, nxtV, k1, 1, wave, lane);
+  }
   __builtin_amdgcn_sched_barrier(0);
-  // R0: SiLU of block 1 of tile st-1 and its P.V; score MFMAs of block 0 of
-  // tile st (K and bias read at the end of the first quarter)
+  // R0: SiLU of block 1 of tile st-1 in quarters, each quarter's registers
+  // then refilled with the block-1 bias of tile st; P.V with V of tile
+  // st-1, each half of vf then refilled with V of tile st; the score MFMAs
+  // of block 0 in the second half; the rest of the DMA
   bf16x8 kf[4];
   {
     uint32_t w[8];
-    attn_round(s1, s0, kf, qf[0], vf, acc[1], w, [&](int sr) __attribute__((always_inline)) {
-      if (MORE) dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, nxtK, nxtV, k1, sr, wave, lane);
-      if (sr == 0) {
-        if (MORE) fast_bias_lookup<HPB>(c, sq, tb_clz, fb);
+    silu4(s1, 0, w[0], w[1]);
+    if (MORE) fast_bias_lookup<HPB>(c, sq, tb_clz, fb);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-          kf[cc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(curK + koff + cc * 32));
-        load_bias_block(curB, 0, lane, s0);
+    for (int cc = 0; cc < 4; ++cc)
+      kf[cc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(curK + koff + cc * 32));
+    load_bias_block(curB, 0, lane, s0);
+    load_bias_quarter(curB, 1, 0, lane, s1);
+    if (MORE) {
+      dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, nxtK, nxtV, k1, 2, wave, lane);
+      dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, nxtK, nxtV, k1, 3, wave, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int sr = 1; sr < 4; ++sr) {
+      silu4(s1, sr, w[2 * sr], w[2 * sr + 1]);
+      load_bias_quarter(curB, 1, sr, lane, s1);
+      if (MORE && sr < 3) {
+        dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, nxtK, nxtV, k1, 2 + 2 * sr, wave, lane);
+        dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, nxtK, nxtV, k1, 3 + 2 * sr, wave, lane);
       }
-      if (sr == 1 && MORE) fast_bias_store<HPB>(fb, nxtB, tid);
-    });
+      if (sr >= 2) {
+        s0 = mfma32(kf[2 * (sr - 2)], qf[0][2 * (sr - 2)], s0);
+        s0 = mfma32(kf[2 * (sr - 2) + 1], qf[0][2 * (sr - 2) + 1], s0);
+      }
+      // the store waits for every LDS read issued before it (the DMA keeps
+      // the compiler from counting partially): after the score MFMAs, which
+      // wait for K and the bias anyway
+      if (MORE && sr == 2) fast_bias_store<HPB>(fb, nxtB, tid);
+      if (sr & 1) {
+        const int kh = sr >> 1;
+        const bf16x8 pk = __builtin_bit_cast(bf16x8, make_uint4(w[4 * kh], w[4 * kh + 1], w[4 * kh + 2], w[4 * kh + 3]));
+#pragma unroll
+        for (int db = 0; db < 2; ++db) acc[1][db] = mfma32(pk, vf[db][kh], acc[1][db]);
+        load_v_half<ROWBV>(curV, voff, kh, vf);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  // A2: bias of block 1 into s1 (free now), V of tile st into vf
-  load_bias_block(curB, 1, lane, s1);
-  load_v<ROWBV>(curV, voff, vf);
-  __builtin_amdgcn_sched_barrier(0);
-  // R1: SiLU of block 0 of tile st and its P.V; score MFMAs of block 1
+  // R1: SiLU of block 0 of tile st and its P.V; the score MFMAs of block 1
   {
     uint32_t w[8];
-    attn_round(s0, s1, kf, qf[1], vf, acc[0], w, [&](int sr) __attribute__((always_inline)) {
-      if (MORE) dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, nxtK, nxtV, k1, 4 + sr, wave, lane);
-    });
+#pragma unroll
+    for (int sr = 0; sr < 4; ++sr) {
+      silu4(s0, sr, w[2 * sr], w[2 * sr + 1]);
+      // two score MFMAs every other quarter: the block-1 bias read last in
+      // R0 has time to land
+      if (sr & 1) {
+        s1 = mfma32(kf[sr - 1], qf[1][sr - 1], s1);
+        s1 = mfma32(kf[sr], qf[1][sr], s1);
+        const int kh = sr >> 1;
+        const bf16x8 pk = __builtin_bit_cast(bf16x8, make_uint4(w[4 * kh], w[4 * kh + 1], w[4 * kh + 2], w[4 * kh + 3]));
+#pragma unroll
+        for (int db = 0; db < 2; ++db) acc[0][db] = mfma32(pk, vf[db][kh], acc[0][db]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // keep the wait and the barrier after the SiLU of this step
     asm volatile("" ::"v"(w[7]));
   }
@@ -780,14 +811,17 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
   // Software pipeline in half tiles. Registers carried from step st-1 to
   // step st: the scores of the second 32-query block of tile st-1 (s1) and
   // the V operand of tile st-1 (vf). Step st (attn_step), buffers (st-lo)&1:
-  //  A0. DMA of the key data of tile st+2; LDS reads for the bias of st+1;
-  //  R0. SiLU of s1 and O1 += P V_{st-1}, overlapped with the score MFMAs of
-  //      block 0 of tile st into s0 (K and the bias as the initial value,
-  //      read from LDS early in the round); the bias of tile st+1 is
-  //      finished and stored; half of the K/V rows of tile st+1 by DMA;
-  //  A2. LDS: bias of block 1 into s1 (free now), V of tile st into vf;
+  //  A0. LDS reads for the bias of tile st+1 (first, so that their dependent
+  //      time-bias lookups are not queued behind the big reads); DMA of the
+  //      key data of tile st+2 and of the K/V rows of tile st+1 (over A0 and
+  //      the first half of R0);
+  //  R0. SiLU of s1 in quarters and O1 += P V_{st-1}; each consumed quarter of
+  //      s1 is refilled with the block-1 bias of tile st and each consumed
+  //      half of vf with V of tile st; the score MFMAs of block 0 of tile st
+  //      into s0 (K and its bias read in the first quarter) in the second
+  //      half; the bias of tile st+1 is finished and stored;
   //  R1. SiLU of s0 and O0 += P V_st, overlapped with the score MFMAs of
-  //      block 1 into s1; the other half of the DMA.
+  //      block 1 into s1.
   // After the last step, a drain runs the SiLU and P.V of s1.
   // s1 and vf start at zero: the first step's R0 then adds exactly zero.
   f32x16 s0, s1;
