@@ -877,9 +877,14 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
 }
 
 // fp32 kernel: one thread per query row, plain FMA loops, exact expf and IEEE
-// division. It serves the fp32 dtype (small workloads).
+// division. It serves the fp32 dtype (small workloads). Keys arrive in
+// chunks of 64 staged in LDS by the whole workgroup, so a thread's loop over
+// keys does not wait on global memory at every key.
 template <int DH>
 __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
+  __shared__ float sk[64][DH];
+  __shared__ float sv[64][DH];
+  __shared__ int64_t skt[64];
   const int seq = blockIdx.x;
   const int qt = blockIdx.y;
   const int h = blockIdx.z;
@@ -904,25 +909,44 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   const int64_t tq = qvalid ? a.ts[si.s + qi] : 0;
   const int q_hi = min(qt * 64 + 64, si.L);
   const int nkeys = si.nc + q_hi;
-  for (int kk = 0; kk < nkeys; ++kk) {
-    const bool cache = kk < si.nc;
-    const int j = kk - si.nc;
-    const bool vis = qvalid && (cache || ((j <= qi) && (j < first_tgt || j == qi)));
-    if (!vis) continue;
-    const int64_t row = cache ? (si.cs + kk) : (si.s + j);
-    const float* kr = (cache ? CK : K) + row * d + h * DH;
-    const float* vr = (cache ? CV : V) + row * d + h * DH;
-    float dot = 0.0f;
+  for (int k0 = 0; k0 < nkeys; k0 += 64) {
+    __syncthreads();   // the previous chunk's reads are done
+    for (int i = threadIdx.x; i < 64 * DH; i += 64) {
+      const int r = i / DH, cc = i - r * DH;
+      const int kk = k0 + r;
+      float kv = 0.0f, vv = 0.0f;
+      if (kk < nkeys) {
+        const bool cache = kk < si.nc;
+        const int64_t row = cache ? (si.cs + kk) : (si.s + kk - si.nc);
+        kv = (cache ? CK : K)[row * d + h * DH + cc];
+        vv = (cache ? CV : V)[row * d + h * DH + cc];
+      }
+      sk[r][cc] = kv;
+      sv[r][cc] = vv;
+    }
+    {
+      const int kk = k0 + threadIdx.x;
+      skt[threadIdx.x] = kk < nkeys ? (kk < si.nc ? a.c_ts[si.cs + kk] : a.ts[si.s + kk - si.nc]) : 0;
+    }
+    __syncthreads();
+    const int kend = min(64, nkeys - k0);
+    for (int r = 0; r < kend; ++r) {
+      const int kk = k0 + r;
+      const bool cache = kk < si.nc;
+      const int j = kk - si.nc;
+      const bool vis = qvalid && (cache || ((j <= qi) && (j < first_tgt || j == qi)));
+      if (!vis) continue;
+      float dot = 0.0f;
 #pragma unroll
-    for (int c = 0; c < DH; ++c) dot = fmaf(qv[c], kr[c], dot);
-    const int pk = cache ? kk : si.nc + (j < first_tgt ? j : first_tgt);
-    const int64_t tk = cache ? a.c_ts[si.cs + kk] : a.ts[si.s + j];
-    int pidx = pq - pk + a.pos_center;
-    pidx = pidx < 0 ? 0 : (pidx >= a.pos_len ? a.pos_len - 1 : pidx);
-    const float s = a.alpha * dot + a.pos_bias[pidx] + a.time_bias[time_bucket64(tq - tk, a.nb)];
-    const float w = s / (1.0f + expf(-s));
+      for (int c = 0; c < DH; ++c) dot = fmaf(qv[c], sk[r][c], dot);
+      const int pk = cache ? kk : si.nc + (j < first_tgt ? j : first_tgt);
+      int pidx = pq - pk + a.pos_center;
+      pidx = pidx < 0 ? 0 : (pidx >= a.pos_len ? a.pos_len - 1 : pidx);
+      const float s = a.alpha * dot + a.pos_bias[pidx] + a.time_bias[time_bucket64(tq - skt[r], a.nb)];
+      const float w = s / (1.0f + expf(-s));
 #pragma unroll
-    for (int c = 0; c < DH; ++c) acc[c] = fmaf(w, vr[c], acc[c]);
+      for (int c = 0; c < DH; ++c) acc[c] = fmaf(w, sv[r][c], acc[c]);
+    }
   }
   if (qvalid) {
 #pragma unroll

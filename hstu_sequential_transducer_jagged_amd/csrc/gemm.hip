@@ -36,6 +36,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kGN = 128;
 constexpr int kGK = 32;
 constexpr int kRowB = kGK * 2;   // 64-byte LDS rows
+constexpr int kOutRowB = kGN * 2 + 8;   // output tile row: 128 bf16 + 8-byte pad (conflict-free)
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -48,6 +49,11 @@ __device__ __forceinline__ float silu_fast(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
 }
 
+// s_waitcnt immediate with vmcnt = 0 and expcnt, lgkmcnt at their maxima
+// (vmcnt bits 3:0, expcnt 6:4, lgkmcnt 11:8); or in a vmcnt below 16. As a
+// builtin the wait is visible to the compiler's own wait insertion.
+constexpr int kWaitVm = 0x0F70;
+
 // Workgroup barrier ordering LDS accesses only (the DMA ring is waited for
 // explicitly; __syncthreads() would also drain it).
 __device__ __forceinline__ void lds_barrier() {
@@ -56,20 +62,26 @@ __device__ __forceinline__ void lds_barrier() {
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-// Epilogues receive one row m and 4 consecutive columns n..n+3.
+// Epilogues in two parts: pack() turns the 4 accumulators of row m,
+// columns n..n+3 into 4 bf16 outputs (bias, activation, residual), and
+// store8() writes 8 consecutive outputs of row m from column n (n % 8 == 0).
+// Between them the workgroup's tile passes through LDS, so that global
+// stores are whole 256-byte row segments instead of 16-byte pieces of 32
+// rows per instruction.
 struct ProjEpi {
   const float* bias;
   uint16_t* out[4];
   int K;   // d_model: width of each of U, V, Q, K
-  __device__ __forceinline__ void operator()(int64_t m, int n, const float (&v)[4]) const {
+  __device__ __forceinline__ uint2 pack(int64_t, int, const float (&v)[4], const float4& b) const {
+    const float bb[4] = {b.x, b.y, b.z, b.w};
     float z[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) z[e] = silu_fast(v[e] + (bias ? bias[n + e] : 0.0f));
+    for (int e = 0; e < 4; ++e) z[e] = silu_fast(v[e] + bb[e]);
+    return make_uint2(pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3]));
+  }
+  __device__ __forceinline__ void store8(int64_t m, int n, const uint4& o) const {
     const int chunk = n / K;
-    uint2 o;
-    o.x = pack_bf16x2(z[0], z[1]);
-    o.y = pack_bf16x2(z[2], z[3]);
-    *reinterpret_cast<uint2*>(out[chunk] + m * K + (n - chunk * K)) = o;
+    *reinterpret_cast<uint4*>(out[chunk] + m * K + (n - chunk * K)) = o;
   }
 };
 
@@ -78,23 +90,24 @@ struct OutEpi {
   const uint16_t* x;
   uint16_t* y;
   int K;
-  __device__ __forceinline__ void operator()(int64_t m, int n, const float (&v)[4]) const {
+  __device__ __forceinline__ uint2 pack(int64_t m, int n, const float (&v)[4], const float4& b) const {
     const uint2 xr = *reinterpret_cast<const uint2*>(x + m * K + n);
     const float xv[4] = {bf2f(xr.x & 0xffff), bf2f(xr.x >> 16), bf2f(xr.y & 0xffff), bf2f(xr.y >> 16)};
+    const float bb[4] = {b.x, b.y, b.z, b.w};
     float z[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) z[e] = v[e] + (bias ? bias[n + e] : 0.0f) + xv[e];
-    uint2 o;
-    o.x = pack_bf16x2(z[0], z[1]);
-    o.y = pack_bf16x2(z[2], z[3]);
-    *reinterpret_cast<uint2*>(y + m * K + n) = o;
+    for (int e = 0; e < 4; ++e) z[e] = v[e] + bb[e] + xv[e];
+    return make_uint2(pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3]));
+  }
+  __device__ __forceinline__ void store8(int64_t m, int n, const uint4& o) const {
+    *reinterpret_cast<uint4*>(y + m * K + n) = o;
   }
 };
 
 // One ring stage of DMA: wave w fills X rows 16i .. 16i+15 for i = w, w+4, ...
 // (NXI instructions) and W rows for i = w, w+4 (1 KB of LDS per instruction).
 template <int NXI>
-__device__ __forceinline__ void gemm_issue(const uint16_t* const (&xsrc)[NXI], const uint16_t* const (&wsrc)[2],
+__device__ __forceinline__ void gemm_issue(const uint16_t* const* xsrc, const uint16_t* const* wsrc,
                                            uint8_t* sx, uint8_t* sw, int k0, int wave) {
 #pragma unroll
   for (int i = 0; i < NXI; ++i)
@@ -133,26 +146,28 @@ __device__ __forceinline__ void gemm_compute(const uint8_t* sx, const uint8_t* s
 // stage s+1 may stay in flight), barrier so that every wave's stage s is in LDS and
 // every wave is done with stage s-1, request stage s+2 into the buffer of
 // stage s-1, multiply stage s.
-template <int NJ>
+template <int NJ, int NSTEPS>
 __device__ __forceinline__ void gemm_mainloop(uint8_t* __restrict__ sX0, uint8_t* __restrict__ sX1,
                                               uint8_t* __restrict__ sX2, uint8_t* __restrict__ sW0,
                                               uint8_t* __restrict__ sW1, uint8_t* __restrict__ sW2,
                                               const uint16_t* const (&xsrc)[NJ],
                                               const uint16_t* const (&wsrc)[2], f32x16 (&acc)[2][NJ],
-                                              int nsteps, int wave, int wm, int wn, int l32, int h) {
-  gemm_issue(xsrc, wsrc, sX0, sW0, 0, wave);
-  if (nsteps > 1) gemm_issue(xsrc, wsrc, sX1, sW1, kGK, wave);
+                                              int nsteps_rt, int wave, int wm, int wn, int l32, int h) {
+  const int nsteps = NSTEPS > 0 ? NSTEPS : nsteps_rt;
+  gemm_issue<NJ>(xsrc, wsrc, sX0, sW0, 0, wave);
+  if (nsteps > 1) gemm_issue<NJ>(xsrc, wsrc, sX1, sW1, kGK, wave);
 #define HSTU_GEMM_STEP(s, SX, SW, NX, NW)                                      \
   {                                                                            \
     if ((s) + 1 < nsteps)                                                      \
-      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NJ + 2) : "memory");            \
+      __builtin_amdgcn_s_waitcnt(kWaitVm | (NJ + 2));                          \
     else                                                                       \
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                         \
+      __builtin_amdgcn_s_waitcnt(kWaitVm);                                     \
     lds_barrier();                                                             \
-    if ((s) + 2 < nsteps) gemm_issue(xsrc, wsrc, NX, NW, ((s) + 2) * kGK, wave); \
+    if ((s) + 2 < nsteps) gemm_issue<NJ>(xsrc, wsrc, NX, NW, ((s) + 2) * kGK, wave); \
     gemm_compute<NJ>(SX, SW, acc, wm, wn, l32, h);                             \
   }
   int s = 0;
+#pragma unroll
   for (; s + 3 <= nsteps; s += 3) {
     HSTU_GEMM_STEP(s, sX0, sW0, sX2, sW2)
     HSTU_GEMM_STEP(s + 1, sX1, sW1, sX0, sW0)
@@ -177,14 +192,18 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
                                                            int64_t M, int N, int K, int nm, int nn,
                                                            Epi epi) {
   constexpr int BM = 64 * NJ;      // block rows; each wave owns BM/2 rows x 64 columns
-  // three ring stages as distinct LDS objects, so that a pending DMA into one
-  // stage does not make the compiler wait before reads of another
-  __shared__ __attribute__((aligned(16))) uint8_t sX0[BM * kRowB];
-  __shared__ __attribute__((aligned(16))) uint8_t sX1[BM * kRowB];
-  __shared__ __attribute__((aligned(16))) uint8_t sX2[BM * kRowB];
-  __shared__ __attribute__((aligned(16))) uint8_t sW0[kGN * kRowB];
-  __shared__ __attribute__((aligned(16))) uint8_t sW1[kGN * kRowB];
-  __shared__ __attribute__((aligned(16))) uint8_t sW2[kGN * kRowB];
+  // one LDS block: the three ring stages during the K loop (they reach the
+  // loop as distinct restrict-qualified pointers), the output tile after it
+  constexpr int kRing = 3 * (BM + kGN) * kRowB;
+  constexpr int kTile = BM * kOutRowB;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kRing > kTile ? kRing : kTile];
+  __shared__ __attribute__((aligned(16))) float sbias[kGN];   // bias of the tile's columns (0 past N)
+  uint8_t* const sX0 = smem;
+  uint8_t* const sX1 = smem + BM * kRowB;
+  uint8_t* const sX2 = smem + 2 * BM * kRowB;
+  uint8_t* const sW0 = smem + 3 * BM * kRowB;
+  uint8_t* const sW1 = sW0 + kGN * kRowB;
+  uint8_t* const sW2 = sW0 + 2 * kGN * kRowB;
 
   const int id = blockIdx.x;
   const int xcd = id & 7;
@@ -202,6 +221,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
   const int wn = wave >> 1;        // 64-column half
   const int l32 = lane & 31;
   const int h = lane >> 5;
+  if (tid < kGN) sbias[tid] = (epi.bias && n0 + tid < N) ? epi.bias[n0 + tid] : 0.0f;
 
   // DMA source rows of this lane: X instructions cover rows 16i + lane/4
   // (i = wave, wave+4, ...), W instructions rows 16i + lane/4 (i = wave,
@@ -231,23 +251,41 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  gemm_mainloop<NJ>(sX0, sX1, sX2, sW0, sW1, sW2, xsrc, wsrc, acc, K / kGK, wave, wm, wn, l32, h);
+  switch (K / kGK) {   // common widths (d_model 256, 512, 1024): unrolled
+    case 8: gemm_mainloop<NJ, 8>(sX0, sX1, sX2, sW0, sW1, sW2, xsrc, wsrc, acc, 8, wave, wm, wn, l32, h); break;
+    case 16: gemm_mainloop<NJ, 16>(sX0, sX1, sX2, sW0, sW1, sW2, xsrc, wsrc, acc, 16, wave, wm, wn, l32, h); break;
+    case 32: gemm_mainloop<NJ, 32>(sX0, sX1, sX2, sW0, sW1, sW2, xsrc, wsrc, acc, 32, wave, wm, wn, l32, h); break;
+    default: gemm_mainloop<NJ, 0>(sX0, sX1, sX2, sW0, sW1, sW2, xsrc, wsrc, acc, K / kGK, wave, wm, wn, l32, h);
+  }
 
-  // C^T accumulator: lane -> m = j*32 + lane%32, n = i*32 + 8*(r/4) + 4*h + r%4
+  // Output tile through LDS. C^T accumulator: lane -> row j*32 + lane%32,
+  // columns i*32 + 8*(r/4) + 4*h + r%4 of the wave's block.
+  lds_barrier();   // every wave is done reading the ring
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int64_t m = m0 + wm * 32 * NJ + j * 32 + l32;
-    if (m >= M) continue;
+    const int ml = wm * 32 * NJ + j * 32 + l32;
+    const int64_t m = m0 + ml;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * 64 + i * 32 + 8 * g + 4 * h;
-        if (n >= N) continue;
+        const int nl = wn * 64 + i * 32 + 8 * g + 4 * h;
         const float v[4] = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                             acc[i][j][4 * g + 3]};
-        epi(m, n, v);
+        const float4 b = *reinterpret_cast<const float4*>(&sbias[nl]);
+        const uint2 o = (m < M && n0 + nl < N) ? epi.pack(m, n0 + nl, v, b) : make_uint2(0, 0);
+        *reinterpret_cast<uint2*>(smem + ml * kOutRowB + nl * 2) = o;
       }
+  }
+  lds_barrier();
+  // 16 threads per 256-byte row segment, 16 rows per pass
+#pragma unroll
+  for (int it = 0; it < BM / 16; ++it) {
+    const int row = it * 16 + (tid >> 4);
+    const int nl = (tid & 15) * 8;
+    const int64_t m = m0 + row;
+    if (m < M && n0 + nl < N)
+      epi.store8(m, n0 + nl, *reinterpret_cast<const uint4*>(smem + row * kOutRowB + nl * 2));
   }
 }
 
