@@ -318,9 +318,25 @@ int hstu_layer_fwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
   hipStream_t s = as_stream(stream);
   st = do_proj(desc, params, T, x, u, v, q, k, s);
   if (st) return st;
-  st = do_attn(desc, jagged, cache, q, k, v, params->pos_bias, params->time_bias, av, attn_work, s);
-  if (st) return st;
-  st = do_norm_gate(desc, T, av, u, params->ln_gamma, params->ln_beta, u, s);
+  if (desc->dtype == HSTU_BF16 &&
+      hstu::attn_can_fuse_norm_gate(desc->num_heads, jagged->num_seqs, jagged->max_seq_len)) {
+    // one head group covers each row: the attention kernel finishes the rows
+    // into G = norm_gate(AV, U) itself (in place over U), with the same row
+    // code as hstu_norm_gate_fwd, so Y is bitwise that of the separate calls
+    hstu::AttnArgs a = make_attn_args(desc, jagged, cache, q, k, v, params->pos_bias, params->time_bias, av,
+                                      attn_work);
+    a.fuse_ng = 1;
+    a.ng_u = u;
+    a.ng_g = u;
+    a.ng_gamma = params->ln_gamma;
+    a.ng_beta = params->ln_beta;
+    a.ng_eps = desc->ln_eps;
+    st = device_status(hstu::launch_attn_bf16(a, s), "attention launch");
+  } else {
+    st = do_attn(desc, jagged, cache, q, k, v, params->pos_bias, params->time_bias, av, attn_work, s);
+    if (st) return st;
+    st = do_norm_gate(desc, T, av, u, params->ln_gamma, params->ln_beta, u, s);
+  }
   if (st) return st;
   return do_out(desc, T, u, x, params->w2, params->b2, y, s);
 }

@@ -618,19 +618,22 @@ __global__ __launch_bounds__(1024) void attn_schedule_kernel(AttnArgs a, int n_q
   }
 }
 
-template <int HPB>
+template <int HPB, bool FUSE_NG>
 __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
   constexpr int NT = 64 * HPB;
   constexpr int ROWBK = Rows<HPB>::ROWBK;
   constexpr int ROWBV = Rows<HPB>::ROWBV;
   constexpr int SPT = 512 / NT;   // bias slots per thread (512 slots of 4 pairs)
-  // Double buffers as distinct LDS objects: the compiler then knows that the
-  // DMA filling one buffer cannot alias the reads of the other and does not
-  // wait for it.
-  __shared__ __attribute__((aligned(16))) uint8_t sK0[kBN * ROWBK];
-  __shared__ __attribute__((aligned(16))) uint8_t sK1[kBN * ROWBK];
-  __shared__ __attribute__((aligned(16))) uint8_t sV0[kBN * ROWBV];
-  __shared__ __attribute__((aligned(16))) uint8_t sV1[kBN * ROWBV];
+  // K and V double buffers in one block: after the last step it holds the
+  // fp32 output tile of the fused norm_gate epilogue (64 x d floats fit:
+  // 64 * HPB * 256 bytes against 64 * (HPB * 256 + 80)). The steps receive
+  // the buffers as distinct restrict-qualified pointers, so a DMA into one
+  // does not make the compiler wait before reads of another.
+  __shared__ __attribute__((aligned(16))) uint8_t skv[2 * kBN * ROWBK + 2 * kBN * ROWBV];
+  uint8_t* const sK0 = skv;
+  uint8_t* const sK1 = skv + kBN * ROWBK;
+  uint8_t* const sV0 = skv + 2 * kBN * ROWBK;
+  uint8_t* const sV1 = sV0 + kBN * ROWBV;
   __shared__ __attribute__((aligned(16))) float sB0[kBM * kBN];
   __shared__ __attribute__((aligned(16))) float sB1[kBM * kBN];
   __shared__ KeyData sD0, sD1;
@@ -861,6 +864,51 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
 #undef SD
 #undef HSTU_ATTN_STEP
 
+  if constexpr (FUSE_NG) {
+    // ---- fused norm_gate: the 64 x d AV tile (AV = -ln2 * O) goes to LDS,
+    // then each wave turns whole rows into G with the norm_gate row code.
+    // U of a batch of up to 8 rows per wave is loaded ahead of the LDS pass,
+    // so its latency overlaps the tile transfer ----
+    constexpr int TD = HPB * kDH;   // = d_model: one head group covers the row
+    constexpr int RPW = kBM / HPB;  // rows per wave
+    constexpr int RB = RPW < 8 ? RPW : 8;
+    const uint16_t* __restrict__ ng_u = static_cast<const uint16_t*>(a.ng_u);
+    __syncthreads();   // every wave is done with the K/V buffers
+    uint2 ur[RB][kNgMaxChunks];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      const int qi = min(q0 + wave + b * HPB, si.L - 1);
+      load_u_chunks_bf16(ng_u + (si.s + qi) * TD, TD, lane, ur[b]);
+    }
+    float* tile = reinterpret_cast<float*>(skv);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = qb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+#pragma unroll
+        for (int db = 0; db < 2; ++db) tile[row * TD + hcol + db * 32 + (lane & 31)] = -kLn2 * acc[qb][db][r];
+      }
+    __syncthreads();
+    for (int b0 = 0; b0 < RPW; b0 += RB) {
+      if (b0 > 0) {
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+          const int qi = min(q0 + wave + (b0 + b) * HPB, si.L - 1);
+          load_u_chunks_bf16(ng_u + (si.s + qi) * TD, TD, lane, ur[b]);
+        }
+      }
+      const float* avr[RB];
+      uint16_t* g[RB];
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        const int rr = wave + (b0 + b) * HPB;
+        avr[b] = tile + rr * TD;
+        g[b] = q0 + rr < si.L ? static_cast<uint16_t*>(a.ng_g) + (si.s + q0 + rr) * TD : nullptr;
+      }
+      norm_gate_rows_bf16<RB>(avr, ur, g, TD, a.ng_eps, a.ng_gamma, a.ng_beta, lane);
+    }
+  } else {
   // ---- AV = -ln2 * O: lane -> query qb*32 + 8(r/4) + 4*h2 + r%4, dim 32db + lane%32 ----
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
@@ -873,6 +921,7 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
         for (int db = 0; db < 2; ++db) row[db * 32] = -kLn2 * acc[qb][db][r];
       }
     }
+  }
   }   // work items
 }
 
@@ -956,6 +1005,12 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 
 }  // namespace
 
+bool attn_can_fuse_norm_gate(int num_heads, int num_seqs, int max_seq_len) {
+  // one head group (8, 4, 2 or 1 heads) per row, and no key-range splits
+  return (num_heads == 8 || num_heads == 4 || num_heads == 2 || num_heads == 1) &&
+         attn_splits(num_seqs, max_seq_len) == 1;
+}
+
 int attn_splits(int num_seqs, int max_seq_len) {
   const int64_t items = static_cast<int64_t>(num_seqs) * ((static_cast<int64_t>(max_seq_len) + kBM - 1) / kBM);
   if (items <= 0 || items >= kSplitMinUnits) return 1;
@@ -1008,11 +1063,22 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   // a multiple of the XCD count, one workgroup per unit on average
   const int64_t units = static_cast<int64_t>(a.num_seqs) * n_qt * a.splits;
   dim3 grid(static_cast<unsigned>((units + kNumXcd - 1) / kNumXcd * kNumXcd), a.num_heads / hpb);
+  if (a.fuse_ng) {
+    if (!attn_can_fuse_norm_gate(a.num_heads, a.num_seqs, a.max_seq_len) || a.splits != 1)
+      return hipErrorInvalidValue;
+    switch (hpb) {
+      case 8: hipLaunchKernelGGL((attn_bf16_kernel<8, true>), grid, dim3(512), 0, s, a); break;
+      case 4: hipLaunchKernelGGL((attn_bf16_kernel<4, true>), grid, dim3(256), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((attn_bf16_kernel<2, true>), grid, dim3(128), 0, s, a); break;
+      default: hipLaunchKernelGGL((attn_bf16_kernel<1, true>), grid, dim3(64), 0, s, a); break;
+    }
+    return hipGetLastError();
+  }
   switch (hpb) {
-    case 8: hipLaunchKernelGGL(attn_bf16_kernel<8>, grid, dim3(512), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(attn_bf16_kernel<4>, grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(attn_bf16_kernel<2>, grid, dim3(128), 0, s, a); break;
-    default: hipLaunchKernelGGL(attn_bf16_kernel<1>, grid, dim3(64), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((attn_bf16_kernel<8, false>), grid, dim3(512), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((attn_bf16_kernel<4, false>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((attn_bf16_kernel<2, false>), grid, dim3(128), 0, s, a); break;
+    default: hipLaunchKernelGGL((attn_bf16_kernel<1, false>), grid, dim3(64), 0, s, a); break;
   }
   if (a.splits > 1) {
     const int64_t n4 = a.total_tokens * a.d_model / 4;

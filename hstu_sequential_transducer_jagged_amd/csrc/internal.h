@@ -37,6 +37,15 @@ struct AttnArgs {
   int* sched;                // bf16 path: work list built by the scheduling pass
   int splits;                // bf16 path: key-range chunks per (sequence, query tile)
   float* partial;            // [splits, T, d] fp32 partial outputs when splits > 1
+  // bf16 path, one head group covering d_model and splits == 1 only: when
+  // fuse_ng is set the kernel writes G = (LayerNorm(AV) * gamma + beta) (.) U
+  // to ng_g instead of AV (ng_g may alias ng_u)
+  int fuse_ng;
+  const void* ng_u;
+  void* ng_g;
+  const float* ng_gamma;
+  const float* ng_beta;
+  float ng_eps;
 };
 
 // bf16 attention: number of key-range chunks per work item (1 unless the
@@ -47,6 +56,9 @@ int attn_splits(int num_seqs, int max_seq_len);
 size_t attn_sched_bytes(int num_seqs, int max_seq_len);
 size_t attn_workspace_bytes(int num_seqs, int max_seq_len, int64_t total_tokens, int d_model);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
+// Whether launch_attn_bf16 can fuse norm_gate for this shape (one head group
+// per row, no key-range splits).
+bool attn_can_fuse_norm_gate(int num_heads, int num_seqs, int max_seq_len);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
 
 // C[M, N] = A[M, K] B[N, K]^T (+ epilogue). Both operands row-major with K

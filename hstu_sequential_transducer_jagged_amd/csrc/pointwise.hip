@@ -17,75 +17,21 @@
 namespace hstu {
 namespace {
 
-constexpr int kMaxChunks = 4;   // float4 chunks per lane: d <= 1024
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
 template <bool BF16>
 __global__ __launch_bounds__(256) void norm_gate_kernel(NormGateArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= a.M) return;
   const int d = a.d;
-  const int nchunk = d >> 2;
-  const float* avr = a.av + row * d;
-  float4 x[kMaxChunks];
-  float s = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
-    const int c = lane + 64 * i;
-    x[i] = c < nchunk ? reinterpret_cast<const float4*>(avr)[c] : make_float4(0, 0, 0, 0);
-    s += (x[i].x + x[i].y) + (x[i].z + x[i].w);
-  }
-  const float inv_d = 1.0f / static_cast<float>(d);
-  const float mean = wave_sum(s) * inv_d;
-  float ss = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
-    const int c = lane + 64 * i;
-    if (c < nchunk) {
-      const float a0 = x[i].x - mean, a1 = x[i].y - mean, a2 = x[i].z - mean, a3 = x[i].w - mean;
-      ss += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
-    }
-  }
-  const float var = wave_sum(ss) * inv_d;
-  const float rstd = 1.0f / sqrtf(var + a.eps);
-#pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
-    const int c = lane + 64 * i;
-    if (c >= nchunk) continue;
-    const int col = c * 4;
-    float gm[4] = {1.f, 1.f, 1.f, 1.f}, bt[4] = {0.f, 0.f, 0.f, 0.f};
-    if (a.gamma) {
-      const float4 t = *reinterpret_cast<const float4*>(a.gamma + col);
-      gm[0] = t.x; gm[1] = t.y; gm[2] = t.z; gm[3] = t.w;
-    }
-    if (a.beta) {
-      const float4 t = *reinterpret_cast<const float4*>(a.beta + col);
-      bt[0] = t.x; bt[1] = t.y; bt[2] = t.z; bt[3] = t.w;
-    }
-    const float xv[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
-    float n[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) n[e] = (xv[e] - mean) * rstd * gm[e] + bt[e];
-    if (BF16) {
-      const uint16_t* u = static_cast<const uint16_t*>(a.u) + row * d + col;
-      const uint2 ur = *reinterpret_cast<const uint2*>(u);
-      const float u0 = bf2f(ur.x & 0xffff), u1 = bf2f(ur.x >> 16);
-      const float u2 = bf2f(ur.y & 0xffff), u3 = bf2f(ur.y >> 16);
-      uint2 o;
-      o.x = pack_bf16x2(n[0] * u0, n[1] * u1);
-      o.y = pack_bf16x2(n[2] * u2, n[3] * u3);
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.g) + row * d + col) = o;
-    } else {
-      const float4 ur = *reinterpret_cast<const float4*>(static_cast<const float*>(a.u) + row * d + col);
-      *reinterpret_cast<float4*>(static_cast<float*>(a.g) + row * d + col) =
-          make_float4(n[0] * ur.x, n[1] * ur.y, n[2] * ur.z, n[3] * ur.w);
-    }
+  if (BF16) {
+    uint2 ur[1][kNgMaxChunks];
+    load_u_chunks_bf16(static_cast<const uint16_t*>(a.u) + row * d, d, lane, ur[0]);
+    const float* const avr[1] = {a.av + row * d};
+    uint16_t* const g[1] = {static_cast<uint16_t*>(a.g) + row * d};
+    norm_gate_rows_bf16<1>(avr, ur, g, d, a.eps, a.gamma, a.beta, lane);
+  } else {
+    norm_gate_row_f32(a.av + row * d, static_cast<const float*>(a.u) + row * d,
+                      static_cast<float*>(a.g) + row * d, d, a.eps, a.gamma, a.beta, lane);
   }
 }
 
