@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--spin-up-s", type=float, default=0.3,
+                    help="untimed seconds of back-to-back steps before the warm-up steps, so "
+                         "that the GPU clocks have settled under load when timing starts")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
                     help="approximate CPU seconds for the oracle sample")
@@ -211,6 +214,7 @@ def run_layer(args):
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "spin_up_s": args.spin_up_s,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -240,9 +244,27 @@ def run_layer(args):
     return rec
 
 
-def timed(step, stream, warmup, steps):
-    """Mean ms of `steps` calls of step() between HIP events on `stream`."""
+SPIN_UP_S = 0.3
+
+
+def spin_up(step, seconds):
+    """Untimed calls of step() for about `seconds` of wall time. Under a
+    sudden load the GPU needs some tens of milliseconds before its clocks
+    settle, and the first calls in a process also load code objects; a few
+    warm-up steps of ~1 ms do not cover that."""
     import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+
+
+def timed(step, stream, warmup, steps):
+    """Mean ms of `steps` calls of step() between HIP events on `stream`,
+    after the spin-up and `warmup` untimed calls."""
+    import torch
+    spin_up(step, SPIN_UP_S)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -257,7 +279,8 @@ def timed(step, stream, warmup, steps):
 
 def base_record(args, metric, value, unit, ms, dtype, config):
     return {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+            "warmup": args.warmup, "spin_up_s": args.spin_up_s, "ms_per_step": ms,
+            "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": dtype,
             "data": "synthetic (seeded; no dataset)", "config": config}
 
@@ -445,6 +468,8 @@ def oracle_threads():
 
 def main():
     args = parse()
+    global SPIN_UP_S
+    SPIN_UP_S = args.spin_up_s
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(sequences are independent; see the sharding note in the design notes).",
