@@ -9,8 +9,8 @@
 // Both are C[M, N] = A[M, K] B[N, K]^T with A and B row-major and K
 // contiguous, which is the operand layout of v_mfma_f32_32x32x16_bf16
 // (lane = row, 8 consecutive k), so tiles are staged through LDS unchanged
-// apart from a bank swizzle. The next K step's global loads are issued
-// before the current step's MFMAs (register staging, double-buffered LDS).
+// apart from a bank swizzle, by global->LDS DMA running up to three K steps
+// ahead of the MFMAs.
 #include "common.h"
 #include "internal.h"
 
@@ -26,8 +26,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // and the epilogue stores 8-byte bf16 quads.
 //
 // Operand tiles reach LDS by direct global->LDS DMA (global_load_lds_dwordx4)
-// through a three-stage ring: the K step s+2 is requested while step s is
-// multiplied, so each load has two MFMA steps to land, and no staging
+// through a three-stage ring: K step s+3 is requested during step s, so each
+// load has between two and three MFMA steps to land, and no staging
 // registers are used. A DMA instruction writes 1 KB of consecutive LDS (16
 // rows of 64 bytes); the bank swizzle is applied on the source side: the lane
 // that fills 16-byte slot p of row r fetches k-chunk p ^ ((r >> 2) & 3) of
@@ -36,7 +36,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kGN = 128;
 constexpr int kGK = 32;
 constexpr int kRowB = kGK * 2;   // 64-byte LDS rows
-constexpr int kOutRowB = kGN * 2 + 8;   // output tile row: 128 bf16 + 8-byte pad (conflict-free)
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -44,10 +43,6 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 
 // LDS byte offset of k-chunk c (0..3, 8 bf16 each) of tile row r.
 __device__ __forceinline__ int swz(int r, int c) { return r * kRowB + ((c ^ ((r >> 2) & 3)) << 4); }
-
-__device__ __forceinline__ float silu_fast(float z) {
-  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
-}
 
 // s_waitcnt immediate with vmcnt = 0 and expcnt, lgkmcnt at their maxima
 // (vmcnt bits 3:0, expcnt 6:4, lgkmcnt 11:8); or in a vmcnt below 16. As a
@@ -68,20 +63,44 @@ __device__ __forceinline__ void lds_barrier() {
 // Between them the workgroup's tile passes through LDS, so that global
 // stores are whole 256-byte row segments instead of 16-byte pieces of 32
 // rows per instruction.
+// A pointer that is the same in every lane, held in scalar registers.
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 struct ProjEpi {
   const float* bias;
-  uint16_t* out[4];
+  uint16_t* out0;   // U, V, Q, K: the four column blocks of width K
+  uint16_t* out1;
+  uint16_t* out2;
+  uint16_t* out3;
   int K;   // d_model: width of each of U, V, Q, K
-  __device__ __forceinline__ uint2 pack(int64_t, int, const float (&v)[4], const float4& b) const {
-    const float bb[4] = {b.x, b.y, b.z, b.w};
-    float z[4];
+  __device__ __forceinline__ uint2 load_extra(int64_t, int) const { return make_uint2(0, 0); }
+  // SiLU of 16 outputs (v + bias), each step over all 16 so that the
+  // transcendental latencies overlap
+  __device__ __forceinline__ void apply16(float (&z)[16], const uint2 (&)[4]) const {
+    float t[16];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) z[e] = silu_fast(v[e] + bb[e]);
-    return make_uint2(pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3]));
+    for (int e = 0; e < 16; ++e) t[e] = __builtin_amdgcn_exp2f(-1.4426950408889634f * z[e]);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) t[e] = __builtin_amdgcn_rcpf(1.0f + t[e]);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) z[e] *= t[e];
   }
+  // 8 columns from n (n % 8 == 0, K % 64 == 0) lie in one block; the block
+  // is picked by compares, so that the pointers stay in scalar registers
+  // (readfirstlane keeps the compiler from turning the select of kernel
+  // arguments into a per-lane load from the argument block)
   __device__ __forceinline__ void store8(int64_t m, int n, const uint4& o) const {
-    const int chunk = n / K;
-    *reinterpret_cast<uint4*>(out[chunk] + m * K + (n - chunk * K)) = o;
+    uint16_t* p = uniform_ptr(out0);
+    if (n >= K) { p = uniform_ptr(out1); n -= K; }
+    if (n >= K) { p = uniform_ptr(out2); n -= K; }
+    if (n >= K) { p = uniform_ptr(out3); n -= K; }
+    *reinterpret_cast<uint4*>(p + m * K + n) = o;
   }
 };
 
@@ -90,14 +109,19 @@ struct OutEpi {
   const uint16_t* x;
   uint16_t* y;
   int K;
-  __device__ __forceinline__ uint2 pack(int64_t m, int n, const float (&v)[4], const float4& b) const {
-    const uint2 xr = *reinterpret_cast<const uint2*>(x + m * K + n);
-    const float xv[4] = {bf2f(xr.x & 0xffff), bf2f(xr.x >> 16), bf2f(xr.y & 0xffff), bf2f(xr.y >> 16)};
-    const float bb[4] = {b.x, b.y, b.z, b.w};
-    float z[4];
+  // the residual X[m, n..n+3]
+  __device__ __forceinline__ uint2 load_extra(int64_t m, int n) const {
+    return *reinterpret_cast<const uint2*>(x + m * K + n);
+  }
+  // v + bias + X, the residual added in fp32 before the single rounding
+  __device__ __forceinline__ void apply16(float (&z)[16], const uint2 (&xr)[4]) const {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) z[e] = v[e] + bb[e] + xv[e];
-    return make_uint2(pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3]));
+    for (int g = 0; g < 4; ++g) {
+      z[4 * g + 0] += bf2f(xr[g].x & 0xffff);
+      z[4 * g + 1] += bf2f(xr[g].x >> 16);
+      z[4 * g + 2] += bf2f(xr[g].y & 0xffff);
+      z[4 * g + 3] += bf2f(xr[g].y >> 16);
+    }
   }
   __device__ __forceinline__ void store8(int64_t m, int n, const uint4& o) const {
     *reinterpret_cast<uint4*>(y + m * K + n) = o;
@@ -117,35 +141,37 @@ __device__ __forceinline__ void gemm_issue(const uint16_t* const* xsrc, const ui
     __builtin_amdgcn_global_load_lds(wsrc[i] + k0, LDS_PTR(void, sw + (wave + 4 * i) * 1024), 16, 0, 0);
 }
 
-// One 32-deep K step of a wave's (32 NJ) x 64 tile (C^T: 64 x 32 NJ).
+// LDS operand reads of one 16-deep half (kk) of a 32-deep K stage.
 template <int NJ>
-__device__ __forceinline__ void gemm_compute(const uint8_t* sx, const uint8_t* sw, f32x16 (&acc)[2][NJ],
-                                             int wm, int wn, int l32, int h) {
+__device__ __forceinline__ void gemm_ops(const uint8_t* sx, const uint8_t* sw, int kk, bf16x8 (&a)[2],
+                                         bf16x8 (&b)[NJ], int wm, int wn, int l32, int h) {
+  const int c = 2 * kk + h;          // 16-byte chunk of this lane's 8 k values
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {     // two 16-deep MFMA steps
-    const int c = 2 * kk + h;          // 16-byte chunk of this lane's 8 k values
-    bf16x8 a[2], b[NJ];
+  for (int i = 0; i < 2; ++i)
+    a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sw[swz(wn * 64 + i * 32 + l32, c)]));
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      a[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sw[swz(wn * 64 + i * 32 + l32, c)]));
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sx[swz(wm * 32 * NJ + j * 32 + l32, c)]));
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
-  }
+  for (int j = 0; j < NJ; ++j)
+    b[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sx[swz(wm * 32 * NJ + j * 32 + l32, c)]));
 }
 
-// The K loop over the three-stage ring. The stage buffers come in as
-// __restrict__ pointers: once inlined, every LDS access and DMA carries alias
-// scopes that tell the compiler's wait insertion that a DMA into one stage
-// does not alias reads of another, so it waits only for the stage it reads.
-// Step s: wait for this wave's DMA of stage s (the NJ + 2 instructions of
-// stage s+1 may stay in flight), barrier so that every wave's stage s is in LDS and
-// every wave is done with stage s-1, request stage s+2 into the buffer of
-// stage s-1, multiply stage s.
+template <int NJ>
+__device__ __forceinline__ void gemm_mma(const bf16x8 (&a)[2], const bf16x8 (&b)[NJ], f32x16 (&acc)[2][NJ]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+}
+
+// The K loop over the three-stage ring, with two operand register sets.
+// Step s: read the second half of stage s (set 1), multiply the first half
+// (set 0, read during step s-1); wait for this wave's DMA of stage s+1 and
+// barrier (stage s+1 is in LDS for every wave, and every wave has read all of
+// stage s); request stage s+3 into stage s's buffer; read the first half of
+// stage s+1 (set 0); multiply set 1. LDS reads thus overlap the MFMAs of the
+// other set, and each DMA has between two and three steps to land. The stage
+// buffers are separate LDS arrays, passed as distinct restrict-qualified
+// pointers, so the compiler's own waits leave the DMA in flight while other
+// stages are read.
 template <int NJ, int NSTEPS>
 __device__ __forceinline__ void gemm_mainloop(uint8_t* __restrict__ sX0, uint8_t* __restrict__ sX1,
                                               uint8_t* __restrict__ sX2, uint8_t* __restrict__ sW0,
@@ -156,29 +182,66 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t* __restrict__ sX0, uint8_t
   const int nsteps = NSTEPS > 0 ? NSTEPS : nsteps_rt;
   gemm_issue<NJ>(xsrc, wsrc, sX0, sW0, 0, wave);
   if (nsteps > 1) gemm_issue<NJ>(xsrc, wsrc, sX1, sW1, kGK, wave);
-#define HSTU_GEMM_STEP(s, SX, SW, NX, NW)                                      \
+  if (nsteps > 2) gemm_issue<NJ>(xsrc, wsrc, sX2, sW2, 2 * kGK, wave);
+  if (nsteps > 2)
+    __builtin_amdgcn_s_waitcnt(kWaitVm | (2 * (NJ + 2)));
+  else if (nsteps > 1)
+    __builtin_amdgcn_s_waitcnt(kWaitVm | (NJ + 2));
+  else
+    __builtin_amdgcn_s_waitcnt(kWaitVm);
+  lds_barrier();
+  bf16x8 a0[2], b0[NJ], a1[2], b1[NJ];
+  gemm_ops<NJ>(sX0, sW0, 0, a0, b0, wm, wn, l32, h);
+  // (scheduling fences keep each set's LDS reads ahead of the other set's
+  // MFMAs; left alone, the compiler sinks the reads to just before their use)
+#define HSTU_GEMM_STEP(s, CX, CW, NX, NW)                                      \
   {                                                                            \
-    if ((s) + 1 < nsteps)                                                      \
-      __builtin_amdgcn_s_waitcnt(kWaitVm | (NJ + 2));                          \
-    else                                                                       \
-      __builtin_amdgcn_s_waitcnt(kWaitVm);                                     \
-    lds_barrier();                                                             \
-    if ((s) + 2 < nsteps) gemm_issue<NJ>(xsrc, wsrc, NX, NW, ((s) + 2) * kGK, wave); \
-    gemm_compute<NJ>(SX, SW, acc, wm, wn, l32, h);                             \
+    gemm_ops<NJ>(CX, CW, 1, a1, b1, wm, wn, l32, h);                           \
+    __builtin_amdgcn_sched_barrier(0);                                         \
+    gemm_mma<NJ>(a0, b0, acc);                                                 \
+    if ((s) + 1 < nsteps) {                                                    \
+      if ((s) + 2 < nsteps)                                                    \
+        __builtin_amdgcn_s_waitcnt(kWaitVm | (NJ + 2));                        \
+      else                                                                     \
+        __builtin_amdgcn_s_waitcnt(kWaitVm);                                   \
+      lds_barrier();                                                           \
+      if ((s) + 3 < nsteps) gemm_issue<NJ>(xsrc, wsrc, CX, CW, ((s) + 3) * kGK, wave); \
+      gemm_ops<NJ>(NX, NW, 0, a0, b0, wm, wn, l32, h);                         \
+    }                                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                         \
+    gemm_mma<NJ>(a1, b1, acc);                                                 \
   }
   int s = 0;
 #pragma unroll
   for (; s + 3 <= nsteps; s += 3) {
-    HSTU_GEMM_STEP(s, sX0, sW0, sX2, sW2)
-    HSTU_GEMM_STEP(s + 1, sX1, sW1, sX0, sW0)
-    HSTU_GEMM_STEP(s + 2, sX2, sW2, sX1, sW1)
+    HSTU_GEMM_STEP(s, sX0, sW0, sX1, sW1)
+    HSTU_GEMM_STEP(s + 1, sX1, sW1, sX2, sW2)
+    HSTU_GEMM_STEP(s + 2, sX2, sW2, sX0, sW0)
   }
   if (s < nsteps) {
-    HSTU_GEMM_STEP(s, sX0, sW0, sX2, sW2)
-    if (s + 1 < nsteps) HSTU_GEMM_STEP(s + 1, sX1, sW1, sX0, sW0)
+    HSTU_GEMM_STEP(s, sX0, sW0, sX1, sW1)
+    if (s + 1 < nsteps) HSTU_GEMM_STEP(s + 1, sX1, sW1, sX2, sW2)
   }
 #undef HSTU_GEMM_STEP
 }
+
+// The output tile after the K loop: BM rows of 128 bf16 (256 B), in 32-row
+// blocks of 8 KB laid over the ring arrays (NJ/2 blocks per X stage, one per
+// W stage). The 16-byte chunk c of row r sits at chunk c ^ (r & 15), so that
+// the 32 rows one accumulator store covers spread over the banks.
+template <int NJ>
+__device__ __forceinline__ uint8_t* tile_block(int b, uint8_t* sX0, uint8_t* sX1, uint8_t* sX2,
+                                               uint8_t* sW0, uint8_t* sW1, uint8_t* sW2) {
+  constexpr int XB = NJ / 2;
+  if (b < XB) return sX0 + b * 8192;
+  if (b < 2 * XB) return sX1 + (b - XB) * 8192;
+  if (b < 3 * XB) return sX2 + (b - 2 * XB) * 8192;
+  if (b == 3 * XB) return sW0;
+  if (b == 3 * XB + 1) return sW1;
+  return sW2;
+}
+
+__device__ __forceinline__ int tile_off(int r, int c) { return (r & 31) * 256 + ((c ^ (r & 15)) << 4); }
 
 // X [M, K] row-major, W [N, K] row-major (nn.Linear), K % 32 == 0,
 // N % 4 == 0. Grid: 8 * ceil(nm / 8) * nn workgroups (nm = ceil(M/256),
@@ -192,18 +255,19 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
                                                            int64_t M, int N, int K, int nm, int nn,
                                                            Epi epi) {
   constexpr int BM = 64 * NJ;      // block rows; each wave owns BM/2 rows x 64 columns
-  // one LDS block: the three ring stages during the K loop (they reach the
-  // loop as distinct restrict-qualified pointers), the output tile after it
-  constexpr int kRing = 3 * (BM + kGN) * kRowB;
-  constexpr int kTile = BM * kOutRowB;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kRing > kTile ? kRing : kTile];
+  // The three ring stages are separate LDS arrays: the compiler's wait
+  // insertion tells DMA into one array apart from reads of another only for
+  // distinct arrays, and would otherwise wait for every DMA in flight before
+  // each stage's first read. After the K loop the same arrays hold the
+  // output tile (tile_block).
+  __shared__ __attribute__((aligned(16))) uint8_t sX0[BM * kRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t sX1[BM * kRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t sX2[BM * kRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t sW0[kGN * kRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t sW1[kGN * kRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t sW2[kGN * kRowB];
   __shared__ __attribute__((aligned(16))) float sbias[kGN];   // bias of the tile's columns (0 past N)
-  uint8_t* const sX0 = smem;
-  uint8_t* const sX1 = smem + BM * kRowB;
-  uint8_t* const sX2 = smem + 2 * BM * kRowB;
-  uint8_t* const sW0 = smem + 3 * BM * kRowB;
-  uint8_t* const sW1 = sW0 + kGN * kRowB;
-  uint8_t* const sW2 = sW0 + 2 * kGN * kRowB;
+  static_assert(3 * BM * kRowB + 3 * kGN * kRowB >= BM * 256, "output tile must fit the ring");
 
   const int id = blockIdx.x;
   const int xcd = id & 7;
@@ -260,22 +324,48 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
 
   // Output tile through LDS. C^T accumulator: lane -> row j*32 + lane%32,
   // columns i*32 + 8*(r/4) + 4*h + r%4 of the wave's block.
+  // Per-element epilogue inputs (the residual of f2) are loaded first, all
+  // at once and unconditionally (rows and columns clamped), so that their
+  // latencies overlap; loads behind a bounds branch would each be waited
+  // for on their own.
+  uint2 extra[NJ][2][4];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t m = min(m0 + wm * 32 * NJ + j * 32 + l32, M - 1);
+        const int n = min(n0 + wn * 64 + i * 32 + 8 * g + 4 * h, N - 4);
+        extra[j][i][g] = epi.load_extra(m, n);
+      }
   lds_barrier();   // every wave is done reading the ring
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int ml = wm * 32 * NJ + j * 32 + l32;
     const int64_t m = m0 + ml;
+    uint8_t* const blk = tile_block<NJ>(wm * NJ + j, sX0, sX1, sX2, sW0, sW1, sW2);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) {
+      float z[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 b = *reinterpret_cast<const float4*>(&sbias[wn * 64 + i * 32 + 8 * g + 4 * h]);
+        z[4 * g + 0] = acc[i][j][4 * g + 0] + b.x;
+        z[4 * g + 1] = acc[i][j][4 * g + 1] + b.y;
+        z[4 * g + 2] = acc[i][j][4 * g + 2] + b.z;
+        z[4 * g + 3] = acc[i][j][4 * g + 3] + b.w;
+      }
+      epi.apply16(z, extra[j][i]);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int nl = wn * 64 + i * 32 + 8 * g + 4 * h;
-        const float v[4] = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                            acc[i][j][4 * g + 3]};
-        const float4 b = *reinterpret_cast<const float4*>(&sbias[nl]);
-        const uint2 o = (m < M && n0 + nl < N) ? epi.pack(m, n0 + nl, v, b) : make_uint2(0, 0);
-        *reinterpret_cast<uint2*>(smem + ml * kOutRowB + nl * 2) = o;
+        const uint2 o = make_uint2(pack_bf16x2(z[4 * g + 0], z[4 * g + 1]),
+                                   pack_bf16x2(z[4 * g + 2], z[4 * g + 3]));
+        *reinterpret_cast<uint2*>(blk + tile_off(ml, nl >> 3) + 8 * h) =
+            (m < M && n0 + nl < N) ? o : make_uint2(0, 0);
       }
+    }
   }
   lds_barrier();
   // 16 threads per 256-byte row segment, 16 rows per pass
@@ -284,8 +374,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
     const int row = it * 16 + (tid >> 4);
     const int nl = (tid & 15) * 8;
     const int64_t m = m0 + row;
+    const uint8_t* const blk = tile_block<NJ>(it / 2, sX0, sX1, sX2, sW0, sW1, sW2);
     if (m < M && n0 + nl < N)
-      epi.store8(m, n0 + nl, *reinterpret_cast<const uint4*>(smem + row * kOutRowB + nl * 2));
+      epi.store8(m, n0 + nl, *reinterpret_cast<const uint4*>(blk + tile_off(row, tid & 15)));
   }
 }
 
@@ -361,10 +452,8 @@ hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, int64_t M, int
 
 hipError_t launch_proj_bf16(const ProjArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
-  ProjEpi epi{a.bias,
-              {static_cast<uint16_t*>(a.out[0]), static_cast<uint16_t*>(a.out[1]),
-               static_cast<uint16_t*>(a.out[2]), static_cast<uint16_t*>(a.out[3])},
-              a.K};
+  ProjEpi epi{a.bias, static_cast<uint16_t*>(a.out[0]), static_cast<uint16_t*>(a.out[1]),
+              static_cast<uint16_t*>(a.out[2]), static_cast<uint16_t*>(a.out[3]), a.K};
   return launch_gemm_bf16(static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.w), a.M,
                           4 * a.K, a.K, epi, s);
 }
