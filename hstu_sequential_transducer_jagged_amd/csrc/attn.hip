@@ -551,27 +551,54 @@ __device__ __forceinline__ int unit_cost(const AttnArgs& a, int n_qt, int u) {
 //     so that the XCD's compute units finish together.
 // sched[x] (x = 0..8): first list index of XCD x (sched[8] = unit count);
 // sched[9 + k]: unit ((seq * n_qt + tile) * splits + chunk) at list index k.
+// Exclusive prefix sum over the 1024 threads of the block (wave scans by
+// shuffles, then one pass over the 16 wave totals); *total receives the sum.
+__device__ __forceinline__ long long block_exclusive_scan(long long v, long long* wsum, long long* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  long long inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long t = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += t;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    long long w = lane < 16 ? wsum[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const long long t = __shfl_up(w, off, 64);
+      if (lane >= off) w += t;
+    }
+    if (lane < 16) wsum[lane] = w;
+  }
+  __syncthreads();
+  const long long excl = inc - v + (wave ? wsum[wave - 1] : 0);
+  *total = wsum[15];
+  __syncthreads();   // wsum may be reused by the next scan
+  return excl;
+}
+
 __global__ __launch_bounds__(1024) void attn_schedule_kernel(AttnArgs a, int n_qt) {
+  constexpr int kKeep = 8;   // unit costs per thread kept in registers between the passes
   __shared__ int cnt[kNumXcd * kCostBuckets];
-  __shared__ long long part[1024];
+  __shared__ long long wsum[16];
   const int tid = threadIdx.x;
   const int items = a.num_seqs * n_qt * a.splits;
   for (int i = tid; i < kNumXcd * kCostBuckets; i += 1024) cnt[i] = 0;
   // each thread owns a contiguous chunk of items
   const int per = (items + 1023) / 1024;
   const int i0 = min(tid * per, items), i1 = min(i0 + per, items);
+  int cst[kKeep];
   long long sum = 0;
-  for (int i = i0; i < i1; ++i) sum += unit_cost(a, n_qt, i);
-  part[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const long long v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kKeep; ++k) {
+    cst[k] = i0 + k < i1 ? unit_cost(a, n_qt, i0 + k) : 0;
+    sum += cst[k];
   }
-  const long long total_cost = part[1023];
-  const long long run0 = tid ? part[tid - 1] : 0;
+  for (int i = i0 + kKeep; i < i1; ++i) sum += unit_cost(a, n_qt, i);
+  long long total_cost;
+  const long long run0 = block_exclusive_scan(sum, wsum, &total_cost);   // also orders cnt's zeroing
   // sort key: XCD-major, cost descending; the item's XCD is the run holding
   // the midpoint of its cost interval
   auto key_of = [&](long long run, int c) __attribute__((always_inline)) {
@@ -580,7 +607,12 @@ __global__ __launch_bounds__(1024) void attn_schedule_kernel(AttnArgs a, int n_q
     return x * kCostBuckets + (kCostBuckets - 1 - min(c, kCostBuckets - 1));
   };
   long long run = run0;
-  for (int i = i0; i < i1; ++i) {
+#pragma unroll
+  for (int k = 0; k < kKeep; ++k) {
+    if (cst[k] > 0) atomicAdd(&cnt[key_of(run, cst[k])], 1);
+    run += cst[k];
+  }
+  for (int i = i0 + kKeep; i < i1; ++i) {
     const int c = unit_cost(a, n_qt, i);
     if (c > 0) atomicAdd(&cnt[key_of(run, c)], 1);
     run += c;
@@ -591,16 +623,8 @@ __global__ __launch_bounds__(1024) void attn_schedule_kernel(AttnArgs a, int n_q
   int loc = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) loc += cnt[tid * kPer + i];
-  __syncthreads();
-  part[tid] = loc;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const long long v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int base = tid ? static_cast<int>(part[tid - 1]) : 0;
+  long long units;
+  int base = static_cast<int>(block_exclusive_scan(loc, wsum, &units));
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int c = cnt[tid * kPer + i];
@@ -609,9 +633,14 @@ __global__ __launch_bounds__(1024) void attn_schedule_kernel(AttnArgs a, int n_q
   }
   __syncthreads();
   if (tid < kNumXcd) a.sched[tid] = cnt[tid * kCostBuckets];
-  if (tid == kNumXcd) a.sched[kNumXcd] = static_cast<int>(part[1023]);
+  if (tid == kNumXcd) a.sched[kNumXcd] = static_cast<int>(units);
   run = run0;
-  for (int i = i0; i < i1; ++i) {
+#pragma unroll
+  for (int k = 0; k < kKeep; ++k) {
+    if (cst[k] > 0) a.sched[kSchedHead + atomicAdd(&cnt[key_of(run, cst[k])], 1)] = i0 + k;
+    run += cst[k];
+  }
+  for (int i = i0 + kKeep; i < i1; ++i) {
     const int c = unit_cost(a, n_qt, i);
     if (c > 0) a.sched[kSchedHead + atomicAdd(&cnt[key_of(run, c)], 1)] = i;
     run += c;
