@@ -92,6 +92,12 @@ class LayerParams:
     beta: np.ndarray       # [d] float32
     pos_bias: np.ndarray   # [2*n_max-1] float32
     time_bias: np.ndarray  # [num_time_buckets] float32
+    # options (off by default): the input LayerNorm before f1, and the
+    # parameter-free position/time bias slopes (m_p, m_t) in place of tables
+    input_norm: bool = False
+    ln1_gamma: Optional[np.ndarray] = None   # [d] float32
+    ln1_beta: Optional[np.ndarray] = None    # [d] float32
+    linear_bias: Optional[tuple] = None
 
 
 @dataclasses.dataclass

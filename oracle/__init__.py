@@ -10,7 +10,9 @@ library.
 from .hstu_oracle import (  # noqa: F401
     attention,
     embed,
+    genrank_bias,
     layer,
+    layernorm,
     norm_gate,
     output,
     proj,

@@ -27,7 +27,12 @@ design notes of the repository):
   innovation 1);
 * the causal mask keeps the diagonal (j <= i);
 * the residual Y = X + f2(...) comes from the block diagram of [NOTES] §2.1
-  ("残差连接", residual connection); no LayerNorm before f1;
+  ("残差连接", residual connection); no LayerNorm before f1 by default (the
+  layer equations have none); the diagram's Norm1 is an option, and the
+  residual then still carries the raw X, since the skip leaves the input
+  ahead of Norm1;
+* the parameter-free bias of [GENRANK] eq. 6.2.6 is an option of the
+  attention (scalars m_p, m_t shared by all heads);
 * Norm is LayerNorm over all d features of the token, biased variance,
   eps from the caller (1e-5), affine gamma/beta;
 * Split order is U, V, Q, K, contiguous chunks of width d; head h owns
@@ -85,6 +90,34 @@ def time_bucket(dt, num_buckets: int = 32):
     return np.minimum(r, num_buckets - 1)
 
 
+def genrank_bias(dp, dt, m_p: float, m_t: float, num_buckets: int = 32):
+    """Parameter-free relative bias of [GENRANK] eq. 6.2.6:
+
+        bias(i, j) = -m_p * (p_i - p_j) - m_t * bucket(t_i - t_j)
+
+    with the slopes predefined (ALiBi-style, eq. 6.2.5, extended to time) and
+    bucket() the same integer floor(log2(|dt| + 1)) bucketing as the table
+    bias, so the two forms agree when the tables are filled linearly. m_p and
+    m_t are scalars shared by all heads, as the equation prints them."""
+    dp = np.asarray(dp, dtype=F64)
+    return -m_p * dp - m_t * time_bucket(dt, num_buckets).astype(F64)
+
+
+def layernorm(x, gamma, beta, eps: float):
+    """LayerNorm over the d features of each token row, biased variance,
+    affine gamma/beta (None: ones/zeros). Used for the optional input norm
+    (Norm1) that the block diagram of [NOTES] §2.1 draws before f1."""
+    x = np.asarray(x, F64)
+    mu = x.mean(axis=1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=1, keepdims=True)
+    n = (x - mu) / np.sqrt(var + eps)
+    if gamma is not None:
+        n = n * np.asarray(gamma, F64)
+    if beta is not None:
+        n = n + np.asarray(beta, F64)
+    return n
+
+
 # --------------------------------------------------------------------------
 # the three steps of the layer
 # --------------------------------------------------------------------------
@@ -123,7 +156,7 @@ def _visibility(L: int, m: int, n_cache: int, rows: np.ndarray) -> np.ndarray:
 
 def attention(q, k, v, offsets, timestamps, pos_bias, time_bias, num_heads: int,
               n_max: int, alpha: float = 1.0, num_targets=None, cache=None,
-              rows=None, row_chunk: int = 2048):
+              rows=None, row_chunk: int = 2048, linear_bias=None, num_time_buckets: int = 32):
     """Spatial aggregation, per head h of every sequence b:
 
         AV_h = (SiLU(alpha * Q_h K_h^T + rab_{p,t}) * Mask) V_h
@@ -140,6 +173,9 @@ def attention(q, k, v, offsets, timestamps, pos_bias, time_bias, num_heads: int,
           result then has one row per requested token. Query rows are
           evaluated in chunks of ``row_chunk`` (each row's value is its own
           dense definition; chunking only bounds memory).
+    linear_bias: None (rab from the tables), or (m_p, m_t): rab is then
+          genrank_bias() of every pair, evaluated directly with
+          ``num_time_buckets`` buckets; the tables are not used.
     Returns AV [T or len(rows), d] float64.
     """
     q = np.asarray(q, F64)
@@ -147,14 +183,15 @@ def attention(q, k, v, offsets, timestamps, pos_bias, time_bias, num_heads: int,
     v = np.asarray(v, F64)
     offsets = np.asarray(offsets, np.int64)
     timestamps = np.asarray(timestamps, np.int64)
-    pos_bias = np.asarray(pos_bias, F64)
-    time_bias = np.asarray(time_bias, F64)
+    if linear_bias is None:
+        pos_bias = np.asarray(pos_bias, F64)
+        time_bias = np.asarray(time_bias, F64)
     T, d = q.shape
     dh = d // num_heads
     B = offsets.shape[0] - 1
     want = np.arange(T) if rows is None else np.asarray(rows, np.int64)
     out = np.zeros((want.shape[0], d), dtype=F64)
-    nb = time_bias.shape[0]
+    nb = num_time_buckets if linear_bias is not None else time_bias.shape[0]
     for b in range(B):
         s, e = int(offsets[b]), int(offsets[b + 1])
         L = e - s
@@ -183,12 +220,15 @@ def attention(q, k, v, offsets, timestamps, pos_bias, time_bias, num_heads: int,
             qrows = want[csel] - s                      # own-token indices
             dp = own_p[qrows][:, None] - key_p[None, :]
             dt = timestamps[s + qrows][:, None] - key_t[None, :]
-            idx = dp + (n_max - 1)
             mask = _visibility(L, m, nc, qrows)
-            if np.any(mask & ((idx < 0) | (idx >= pos_bias.shape[0]))):
-                raise ValueError("position difference outside the position table")
-            idx = np.clip(idx, 0, pos_bias.shape[0] - 1)
-            rab = pos_bias[idx] + time_bias[time_bucket(dt, nb)]
+            if linear_bias is not None:
+                rab = genrank_bias(dp, dt, linear_bias[0], linear_bias[1], nb)
+            else:
+                idx = dp + (n_max - 1)
+                if np.any(mask & ((idx < 0) | (idx >= pos_bias.shape[0]))):
+                    raise ValueError("position difference outside the position table")
+                idx = np.clip(idx, 0, pos_bias.shape[0] - 1)
+                rab = pos_bias[idx] + time_bias[time_bucket(dt, nb)]
             for h in range(num_heads):
                 cols = slice(h * dh, (h + 1) * dh)
                 scores = alpha * (q[s + qrows, cols] @ keys_k[:, cols].T) + rab
@@ -243,6 +283,11 @@ def layer(x, p, offsets, timestamps, num_heads: int, n_max: int, alpha: float = 
     transformation ([NOTES] §2.1, all three equations, plus the residual).
 
     ``p`` has attributes w1, b1, w2, b2, gamma, beta, pos_bias, time_bias.
+    Optional attributes: ``ln1_gamma``/``ln1_beta`` with ``input_norm`` true
+    apply the input LayerNorm (Norm1 of the block diagram) to X before f1,
+    while the residual keeps the raw X (the skip connection leaves from the
+    input, ahead of Norm1); ``linear_bias`` = (m_p, m_t) replaces the table
+    rab by genrank_bias().
     With ``rows`` given, only those token rows are produced (their causal
     prefixes are projected as needed). Returns a dict with u, v, q, k (for
     the projected rows ``proj_rows``), av, g and y (for the output rows)."""
@@ -256,11 +301,16 @@ def layer(x, p, offsets, timestamps, num_heads: int, n_max: int, alpha: float = 
         orow = np.asarray(rows, np.int64)
         prow = _needed_prefix_rows(offsets, orow)
     u = np.zeros((T, d)); vv = np.zeros((T, d)); qq = np.zeros((T, d)); kk = np.zeros((T, d))
-    pu, pv, pq, pk = proj(x[prow], p.w1, p.b1, d)
+    xin = x[prow]
+    if getattr(p, "input_norm", False):
+        xin = layernorm(xin, getattr(p, "ln1_gamma", None), getattr(p, "ln1_beta", None), eps)
+    pu, pv, pq, pk = proj(xin, p.w1, p.b1, d)
     u[prow], vv[prow], qq[prow], kk[prow] = pu, pv, pq, pk
+    lin = getattr(p, "linear_bias", None)
     av = attention(qq, kk, vv, offsets, timestamps, p.pos_bias, p.time_bias, num_heads,
                    n_max, alpha, num_targets=num_targets, cache=cache,
-                   rows=None if rows is None else orow)
+                   rows=None if rows is None else orow, linear_bias=lin,
+                   num_time_buckets=len(p.time_bias) if p.time_bias is not None else 32)
     g = norm_gate(av, u[orow], p.gamma, p.beta, eps)
     y = output(x[orow], g, p.w2, p.b2)
     return dict(u=u, v=vv, q=qq, k=kk, av=av, g=g, y=y, proj_rows=prow, rows=orow)

@@ -545,3 +545,121 @@ def test_generator_recipe():
         if w.dtype == "bf16":
             np.testing.assert_array_equal(gen.bf16_round(w.x), w.x)
             np.testing.assert_array_equal(gen.bf16_round(w.layers[0].w1), w.layers[0].w1)
+
+
+# ---------------------------------------------------------------------------
+# options: parameter-free bias (GenRank eq. 6.2.6) and the input LayerNorm
+# ---------------------------------------------------------------------------
+
+def test_genrank_bias_worked_example():
+    """The worked example after GenRank eq. 6.2.6: the 7th, 5th and 1st of
+    seven past interactions, seen from the 8th, carry a small, a medium and a
+    large penalty. Any positive slopes must order them so; with m_t = 0 the
+    bias is ALiBi's -m (i - j) (eq. 6.2.5)."""
+    ex = json.load(open(os.path.join(HERE, "golden", "genrank_alibi_example.json")))
+    items = ex["interactions"]
+    assert [it["penalty"] for it in items] == ["small", "medium", "large"]
+    dp = np.array([it["position_distance"] for it in items])
+    dt = np.array([it["time_distance_s"] for it in items])
+    # bucket = bit length of |dt| + 1, minus one: 301 -> 8, 3601 -> 11, 86401 -> 16
+    assert list(oracle.time_bucket(dt)) == [8, 11, 16]
+    for mp, mt in [(0.5, 0.25), (0.01, 1.0), (2.0, 0.0), (0.0, 0.1)]:
+        b = oracle.genrank_bias(dp, dt, mp, mt)
+        assert np.all(b <= 0)
+        assert b[0] > b[1] > b[2]
+        if mt == 0.0:
+            np.testing.assert_array_equal(b, -mp * dp)
+
+
+def _with_targets_and_cache(seed):
+    w = _tiny([7, 1, 12, 5], d=8, H=2, seed=seed, n_max=24)
+    rng = np.random.default_rng(seed + 100)
+    q, k, v = (rng.standard_normal((int(w.offsets[-1]), 8)) for _ in range(3))
+    nt = np.array([2, 0, 3, 5])
+    coff = np.array([0, 3, 3, 9, 11])
+    cache = dict(offsets=coff, k=rng.standard_normal((11, 8)), v=rng.standard_normal((11, 8)),
+                 timestamps=1_500_000_000 + np.sort(rng.integers(0, 10**6, 11)))
+    return w, q, k, v, nt, cache
+
+
+def test_attention_linear_bias_matches_linear_tables():
+    """The direct eq. 6.2.6 path equals the table path with tables filled
+    linearly, with targets and a cache (two separate code paths)."""
+    w, q, k, v, nt, cache = _with_targets_and_cache(3)
+    mp, mt = 0.03125, 0.125
+    p = w.layers[0]
+    n = w.n_max
+    pb = -mp * (np.arange(2 * n - 1) - (n - 1))
+    tb = -mt * np.arange(32)
+    a = oracle.attention(q, k, v, w.offsets, w.timestamps, pb, tb, 2, n, w.alpha,
+                         num_targets=nt, cache=cache)
+    b = oracle.attention(q, k, v, w.offsets, w.timestamps, None, None, 2, n, w.alpha,
+                         num_targets=nt, cache=cache, linear_bias=(mp, mt))
+    np.testing.assert_allclose(b, a, rtol=1e-13, atol=1e-13)
+    c = oracle.attention(q, k, v, w.offsets, w.timestamps, p.pos_bias, p.time_bias, 2, n,
+                         w.alpha, num_targets=nt, cache=cache)
+    assert not np.allclose(b, c)
+
+
+def test_attention_linear_bias_shift_invariance():
+    """Eq. 6.2.6 depends on differences only: shifting every timestamp (own
+    and cached) by one constant leaves the output unchanged."""
+    w, q, k, v, nt, cache = _with_targets_and_cache(4)
+    kw = dict(num_targets=nt, linear_bias=(0.05, 0.2))
+    a = oracle.attention(q, k, v, w.offsets, w.timestamps, None, None, 2, w.n_max, w.alpha,
+                         cache=cache, **kw)
+    c2 = dict(cache, timestamps=cache["timestamps"] + 86_400 * 365)
+    b = oracle.attention(q, k, v, w.offsets, w.timestamps + 86_400 * 365, None, None, 2,
+                         w.n_max, w.alpha, cache=c2, **kw)
+    np.testing.assert_allclose(b, a, rtol=1e-14, atol=1e-14)
+
+
+def test_layernorm_against_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((37, 24)) * 3 + 1.5
+    g, b = rng.standard_normal(24), rng.standard_normal(24)
+    want = torch.nn.functional.layer_norm(torch.from_numpy(x), (24,), torch.from_numpy(g),
+                                          torch.from_numpy(b), eps=1e-5).numpy()
+    np.testing.assert_allclose(oracle.layernorm(x, g, b, 1e-5), want, rtol=1e-12, atol=1e-12)
+
+
+def _norm1_workload(seed, eps):
+    w = _tiny([6, 9, 1], d=8, H=2, seed=seed, n_max=9)
+    w.ln_eps = eps
+    rng = np.random.default_rng(seed + 7)
+    p = w.layers[0]
+    p.input_norm = True
+    p.ln1_gamma = 1.0 + 0.3 * rng.standard_normal(8)
+    p.ln1_beta = 0.2 * rng.standard_normal(8)
+    return w, p
+
+
+def _layer_y(w, x, p):
+    return oracle.layer(x, p, w.offsets, w.timestamps, w.num_heads, w.n_max, w.alpha,
+                        w.ln_eps)["y"]
+
+
+def test_layer_input_norm_residual_carries_raw_x():
+    """With Norm1, f1 sees LN(X) but the skip connection carries X: the
+    layer's update Y - X equals that of the plain layer run on LN(X)."""
+    import copy
+    w, p = _norm1_workload(5, 1e-5)
+    x = np.asarray(w.x, np.float64) * 2.0 + 0.7
+    y1 = _layer_y(w, x, p)
+    plain = copy.copy(p)
+    plain.input_norm = False
+    xn = oracle.layernorm(x, p.ln1_gamma, p.ln1_beta, w.ln_eps)
+    y0 = _layer_y(w, xn, plain)
+    np.testing.assert_allclose(y1 - x, y0 - xn, rtol=1e-12, atol=1e-12)
+    assert not np.allclose(y1, y0)
+
+
+def test_layer_input_norm_scale_shift_invariance():
+    """LayerNorm with eps = 0 ignores a positive scale and a shift of each
+    row, so with Norm1 the layer's update Y - X does too."""
+    w, p = _norm1_workload(6, 0.0)
+    x = np.asarray(w.x, np.float64)
+    base = _layer_y(w, x, p) - x
+    x2 = 3.5 * x - 1.25
+    np.testing.assert_allclose(_layer_y(w, x2, p) - x2, base, rtol=1e-9, atol=1e-9)
