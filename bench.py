@@ -308,7 +308,7 @@ def run_stack(args):
         h = x0
         for l in range(L):
             y = bufs[l % 2]
-            hstu.hstu_layer_fwd(dw.desc, dw.layers[l].params, dw.jagged, None, h, y, None, None, ws, sh)
+            hstu.hstu_layer_fwd(dw.layers[l].desc, dw.layers[l].params, dw.jagged, None, h, y, None, None, ws, sh)
             h = y
 
     ms = timed(step, stream, args.warmup, args.steps)
@@ -393,7 +393,7 @@ def run_ranking(args):
         h = dw.x
         for l in range(L):
             y = hbuf[l % 2]
-            hstu.hstu_layer_fwd(dw.desc, dw.layers[l].params, dw.jagged, None, h, y, kc[l], vc[l], ws, sh)
+            hstu.hstu_layer_fwd(dw.layers[l].desc, dw.layers[l].params, dw.jagged, None, h, y, kc[l], vc[l], ws, sh)
             h = y
 
     def candidates():
@@ -401,7 +401,7 @@ def run_ranking(args):
             h = cx[start:start + n]
             for l in range(L):
                 y = cbuf[l % 2][start:start + n]
-                hstu.hstu_layer_fwd(dw.desc, dw.layers[l].params, jag, caches[l], h, y, None, None,
+                hstu.hstu_layer_fwd(dw.layers[l].desc, dw.layers[l].params, jag, caches[l], h, y, None, None,
                                     wsc, sh)
                 h = y
 

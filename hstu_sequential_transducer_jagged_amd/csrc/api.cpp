@@ -68,6 +68,8 @@ int check_desc(const hstu_layer_desc* d) {
         "pos_table_len must be odd and positive (2*n_max-1), got %d", d->pos_table_len);
   CHECK(d->num_time_buckets >= 1 && d->num_time_buckets <= 64, HSTU_E_INVAL,
         "num_time_buckets must be in [1, 64] (got %d)", d->num_time_buckets);
+  CHECK(d->input_norm == 0 || d->input_norm == 1, HSTU_E_INVAL, "input_norm must be 0 or 1 (got %d)",
+        d->input_norm);
   return HSTU_OK;
 }
 
@@ -170,6 +172,14 @@ int do_norm_gate(const hstu_layer_desc* d, int64_t T, const float* av, const voi
                        "norm_gate launch");
 }
 
+int do_layernorm(const hstu_layer_desc* d, int64_t T, const void* x, const float* gamma,
+                 const float* beta, void* y, hipStream_t s) {
+  hstu::LayerNormArgs a{x, gamma, beta, y, T, d->d_model, d->ln_eps};
+  return device_status(d->dtype == HSTU_BF16 ? hstu::launch_layernorm_bf16(a, s)
+                                             : hstu::launch_layernorm_f32(a, s),
+                       "layernorm launch");
+}
+
 int do_out(const hstu_layer_desc* d, int64_t T, const void* g, const void* x, const void* w2,
            const float* b2, void* y, hipStream_t s) {
   hstu::OutArgs a{g, w2, b2, x, y, T, d->d_model};
@@ -257,6 +267,33 @@ int hstu_norm_gate_fwd(const hstu_layer_desc* desc, int64_t T, const float* av, 
   return do_norm_gate(desc, T, av, u, gamma, beta, g, as_stream(stream));
 }
 
+int hstu_layernorm_fwd(const hstu_layer_desc* desc, int64_t T, const void* x, const float* gamma,
+                       const float* beta, void* y, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  CHECK(T >= 0, HSTU_E_INVAL, "T must be >= 0");
+  if (T == 0) return ok();
+  CHECK(x && y, HSTU_E_INVAL, "x/y must not be NULL");
+  CHECK(x != y, HSTU_E_INVAL, "y must not alias x");
+  CHECK(aligned16(x) && aligned16(y), HSTU_E_INVAL, "x/y must be 16-byte aligned");
+  CHECK(!gamma || aligned16(gamma), HSTU_E_INVAL, "gamma must be 16-byte aligned");
+  CHECK(!beta || aligned16(beta), HSTU_E_INVAL, "beta must be 16-byte aligned");
+  return do_layernorm(desc, T, x, gamma, beta, y, as_stream(stream));
+}
+
+int hstu_linear_bias_tables(const hstu_layer_desc* desc, float m_p, float m_t, float* pos_bias,
+                            float* time_bias, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  CHECK(std::isfinite(m_p) && std::isfinite(m_t), HSTU_E_INVAL, "m_p and m_t must be finite");
+  CHECK(pos_bias && time_bias, HSTU_E_INVAL, "pos_bias/time_bias must not be NULL");
+  CHECK(pos_bias != time_bias, HSTU_E_INVAL, "pos_bias and time_bias must not alias");
+  return device_status(hstu::launch_linear_bias_tables(m_p, m_t, desc->pos_table_len,
+                                                       desc->num_time_buckets, pos_bias, time_bias,
+                                                       as_stream(stream)),
+                       "linear bias tables launch");
+}
+
 int hstu_out_fwd(const hstu_layer_desc* desc, int64_t T, const void* g, const void* x,
                  const void* w2, const float* b2, void* y, void* stream) {
   int st = check_desc(desc);
@@ -275,7 +312,8 @@ size_t hstu_layer_workspace_size(const hstu_layer_desc* desc, const hstu_jagged*
   const size_t T = static_cast<size_t>(jagged->total_tokens);
   const size_t act = round256(T * desc->d_model * elem_size(desc->dtype));
   const size_t av = round256(T * desc->d_model * sizeof(float));
-  return 4 * act + av + attn_ws(desc, jagged);  // U, V, Q, K (G overwrites U), AV, work list
+  // U, V, Q, K (G overwrites U), AV, work list, then LayerNorm(X) with input_norm
+  return 4 * act + av + attn_ws(desc, jagged) + (desc->input_norm ? act : 0);
 }
 
 int hstu_layer_fwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
@@ -300,6 +338,9 @@ int hstu_layer_fwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
         "k_out/v_out must be 16-byte aligned");
   CHECK(!params->ln_gamma || aligned16(params->ln_gamma), HSTU_E_INVAL, "ln_gamma must be 16-byte aligned");
   CHECK(!params->ln_beta || aligned16(params->ln_beta), HSTU_E_INVAL, "ln_beta must be 16-byte aligned");
+  CHECK(!desc->input_norm || ((!params->ln1_gamma || aligned16(params->ln1_gamma)) &&
+                              (!params->ln1_beta || aligned16(params->ln1_beta))),
+        HSTU_E_INVAL, "ln1_gamma/ln1_beta must be 16-byte aligned");
   const size_t need = hstu_layer_workspace_size(desc, jagged);
   CHECK(workspace != nullptr && workspace_bytes >= need, HSTU_E_WORKSPACE,
         "workspace too small: need %zu bytes, got %zu", need, workspace_bytes);
@@ -316,7 +357,15 @@ int hstu_layer_fwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
   if (k_out) k = k_out;
   if (v_out) v = v_out;
   hipStream_t s = as_stream(stream);
-  st = do_proj(desc, params, T, x, u, v, q, k, s);
+  const void* xin = x;   // what f1 reads; the residual below always adds the raw x
+  if (desc->input_norm) {
+    void* xn = ws + 4 * act + round256(static_cast<size_t>(T) * desc->d_model * sizeof(float)) +
+               attn_ws(desc, jagged);
+    st = do_layernorm(desc, T, x, params->ln1_gamma, params->ln1_beta, xn, s);
+    if (st) return st;
+    xin = xn;
+  }
+  st = do_proj(desc, params, T, xin, u, v, q, k, s);
   if (st) return st;
   if (desc->dtype == HSTU_BF16 &&
       hstu::attn_can_fuse_norm_gate(desc->num_heads, jagged->num_seqs, jagged->max_seq_len)) {

@@ -99,6 +99,24 @@ struct NormGateArgs {
 hipError_t launch_norm_gate_bf16(const NormGateArgs& a, hipStream_t s);
 hipError_t launch_norm_gate_f32(const NormGateArgs& a, hipStream_t s);
 
+// Y = LayerNorm_d(X) * gamma + beta, row by row (the optional input norm).
+struct LayerNormArgs {
+  const void* x;     // [M, d] dtype
+  const float* gamma;
+  const float* beta;
+  void* y;           // [M, d] dtype
+  int64_t M;
+  int d;
+  float eps;
+};
+hipError_t launch_layernorm_bf16(const LayerNormArgs& a, hipStream_t s);
+hipError_t launch_layernorm_f32(const LayerNormArgs& a, hipStream_t s);
+
+// pos[i] = -m_p * (i - (len - 1) / 2), time[b] = -m_t * b: the tables that
+// make the table bias equal the parameter-free position/time bias.
+hipError_t launch_linear_bias_tables(float m_p, float m_t, int pos_len, int num_buckets,
+                                     float* pos, float* time, hipStream_t s);
+
 struct EmbedArgs {
   const void* item;
   const void* action;

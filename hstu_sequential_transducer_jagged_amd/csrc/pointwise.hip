@@ -8,6 +8,13 @@
 //   16-byte (AV) or 8-byte (bf16 U/G) access; mean and variance are two
 //   register passes reduced with cross-lane shuffles (no LDS round trip).
 //
+// layernorm: the optional input norm before f1 (the block diagram's Norm1),
+//   Y = LayerNorm_d(X) * gamma + beta; same layout and reductions as
+//   norm_gate, reading bf16 or fp32 X.
+//
+// linear_bias_tables: the position and time tables of the parameter-free
+//   bias of "6.2. HSTU的工程突破" eq. 6.2.6, -m_p (p_i - p_j) - m_t bucket.
+//
 // embed: X[t] = item_emb[id_t] + action_emb[a_t], the action-oriented token
 //   of "6.2. HSTU的工程突破" eq. 6.2.2. One wavefront per token, 16-byte
 //   gathers of the two rows, fp32 add, one rounding.
@@ -33,6 +40,73 @@ __global__ __launch_bounds__(256) void norm_gate_kernel(NormGateArgs a) {
     norm_gate_row_f32(a.av + row * d, static_cast<const float*>(a.u) + row * d,
                       static_cast<float*>(a.g) + row * d, d, a.eps, a.gamma, a.beta, lane);
   }
+}
+
+// One wave per row: lane owns the 4-element chunks lane + 64 i (d <= 1024).
+template <bool BF16>
+__global__ __launch_bounds__(256) void layernorm_kernel(LayerNormArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= a.M) return;
+  const int d = a.d;
+  const int nchunk = d >> 2;
+  float4 x[kNgMaxChunks];
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kNgMaxChunks; ++i) {
+    const int c = lane + 64 * i;
+    x[i] = make_float4(0, 0, 0, 0);
+    if (c < nchunk) {
+      if (BF16) {
+        const uint2 r = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.x) + row * d)[c];
+        x[i] = make_float4(bf2f(r.x & 0xffff), bf2f(r.x >> 16), bf2f(r.y & 0xffff), bf2f(r.y >> 16));
+      } else {
+        x[i] = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + row * d)[c];
+      }
+    }
+    s += (x[i].x + x[i].y) + (x[i].z + x[i].w);
+  }
+  const float inv_d = 1.0f / static_cast<float>(d);
+  const float mean = wave_sum(s) * inv_d;
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kNgMaxChunks; ++i) {
+    if (lane + 64 * i < nchunk) {
+      const float a0 = x[i].x - mean, a1 = x[i].y - mean, a2 = x[i].z - mean, a3 = x[i].w - mean;
+      ss += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+    }
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(ss) * inv_d + a.eps);
+#pragma unroll
+  for (int i = 0; i < kNgMaxChunks; ++i) {
+    const int c = lane + 64 * i;
+    if (c >= nchunk) continue;
+    const int col = c * 4;
+    float4 gm = make_float4(1.f, 1.f, 1.f, 1.f), bt = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a.gamma) gm = *reinterpret_cast<const float4*>(a.gamma + col);
+    if (a.beta) bt = *reinterpret_cast<const float4*>(a.beta + col);
+    const float n0 = (x[i].x - mean) * rstd * gm.x + bt.x;
+    const float n1 = (x[i].y - mean) * rstd * gm.y + bt.y;
+    const float n2 = (x[i].z - mean) * rstd * gm.z + bt.z;
+    const float n3 = (x[i].w - mean) * rstd * gm.w + bt.w;
+    if (BF16) {
+      reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.y) + row * d)[c] =
+          make_uint2(pack_bf16x2(n0, n1), pack_bf16x2(n2, n3));
+    } else {
+      reinterpret_cast<float4*>(static_cast<float*>(a.y) + row * d)[c] = make_float4(n0, n1, n2, n3);
+    }
+  }
+}
+
+// pos_len = 2 n_max - 1 entries, entry i <-> p_i - p_j = i - (n_max - 1)
+__global__ __launch_bounds__(256) void linear_bias_tables_kernel(float m_p, float m_t, int pos_len,
+                                                                 int num_buckets, float* pos,
+                                                                 float* time) {
+  const int half = (pos_len - 1) / 2;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < pos_len; i += gridDim.x * 256)
+    pos[i] = -m_p * static_cast<float>(i - half);
+  if (blockIdx.x == 0)
+    for (int b = threadIdx.x; b < num_buckets; b += 256) time[b] = -m_t * static_cast<float>(b);
 }
 
 template <bool BF16>
@@ -98,6 +172,28 @@ hipError_t launch_norm_gate_f32(const NormGateArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
   hipLaunchKernelGGL(norm_gate_kernel<false>, dim3(static_cast<unsigned>((a.M + 3) / 4)),
                      dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_layernorm_bf16(const LayerNormArgs& a, hipStream_t s) {
+  if (a.M == 0) return hipSuccess;
+  hipLaunchKernelGGL(layernorm_kernel<true>, dim3(static_cast<unsigned>((a.M + 3) / 4)), dim3(256),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_layernorm_f32(const LayerNormArgs& a, hipStream_t s) {
+  if (a.M == 0) return hipSuccess;
+  hipLaunchKernelGGL(layernorm_kernel<false>, dim3(static_cast<unsigned>((a.M + 3) / 4)), dim3(256),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_bias_tables(float m_p, float m_t, int pos_len, int num_buckets, float* pos,
+                                     float* time, hipStream_t s) {
+  const int grid = (pos_len + 255) / 256;
+  hipLaunchKernelGGL(linear_bias_tables_kernel, dim3(grid > 0 ? grid : 1), dim3(256), 0, s, m_p, m_t,
+                     pos_len, num_buckets, pos, time);
   return hipGetLastError();
 }
 

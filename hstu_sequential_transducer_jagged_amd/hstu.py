@@ -28,7 +28,8 @@ HSTU_BF16 = 1
 
 EXPORTS = ("hstu_abi_version", "hstu_last_error", "hstu_proj_fwd", "hstu_attn_workspace_size",
            "hstu_attn_fwd",
-           "hstu_norm_gate_fwd", "hstu_out_fwd", "hstu_layer_workspace_size",
+           "hstu_norm_gate_fwd", "hstu_layernorm_fwd", "hstu_linear_bias_tables",
+           "hstu_out_fwd", "hstu_layer_workspace_size",
            "hstu_layer_fwd", "hstu_embed_fwd", "hstu_check_inputs")
 
 
@@ -42,7 +43,8 @@ class LayerDesc(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("alpha", ctypes.c_float), ("ln_eps", ctypes.c_float),
-                ("pos_table_len", ctypes.c_int32), ("num_time_buckets", ctypes.c_int32)]
+                ("pos_table_len", ctypes.c_int32), ("num_time_buckets", ctypes.c_int32),
+                ("input_norm", ctypes.c_int32)]
 
 
 class Jagged(ctypes.Structure):
@@ -61,7 +63,8 @@ class LayerParams(ctypes.Structure):
     _fields_ = [("w1", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("w2", ctypes.c_void_p),
                 ("b2", ctypes.c_void_p), ("ln_gamma", ctypes.c_void_p),
                 ("ln_beta", ctypes.c_void_p), ("pos_bias", ctypes.c_void_p),
-                ("time_bias", ctypes.c_void_p)]
+                ("time_bias", ctypes.c_void_p), ("ln1_gamma", ctypes.c_void_p),
+                ("ln1_beta", ctypes.c_void_p)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -86,6 +89,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "hstu_attn_workspace_size": (ctypes.c_size_t, [P, P]),
         "hstu_attn_fwd": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "hstu_norm_gate_fwd": (ctypes.c_int, [P, i64, P, P, P, P, P, P]),
+        "hstu_layernorm_fwd": (ctypes.c_int, [P, i64, P, P, P, P, P]),
+        "hstu_linear_bias_tables": (ctypes.c_int, [P, ctypes.c_float, ctypes.c_float, P, P, P]),
         "hstu_out_fwd": (ctypes.c_int, [P, i64, P, P, P, P, P, P]),
         "hstu_layer_workspace_size": (ctypes.c_size_t, [P, P]),
         "hstu_layer_fwd": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
@@ -124,9 +129,10 @@ def current_stream() -> int:
 # ---------------------------------------------------------------------------
 
 def make_desc(d_model: int, num_heads: int, dtype: int, pos_table_len: int,
-              alpha: float = 1.0, ln_eps: float = 1e-5, num_time_buckets: int = 32) -> LayerDesc:
+              alpha: float = 1.0, ln_eps: float = 1e-5, num_time_buckets: int = 32,
+              input_norm: bool = False) -> LayerDesc:
     return LayerDesc(d_model, num_heads, d_model // num_heads, dtype, alpha, ln_eps,
-                     pos_table_len, num_time_buckets)
+                     pos_table_len, num_time_buckets, int(bool(input_norm)))
 
 
 def make_jagged(offsets, timestamps, max_seq_len: int, num_targets=None) -> Jagged:
@@ -141,9 +147,10 @@ def make_cache(offsets, timestamps, k, v, max_len: int) -> KVCache:
     return KVCache(ptr(offsets), ptr(timestamps), ptr(k), ptr(v), int(max_len), T)
 
 
-def make_params(w1, b1, w2, b2, gamma, beta, pos_bias, time_bias) -> LayerParams:
+def make_params(w1, b1, w2, b2, gamma, beta, pos_bias, time_bias, ln1_gamma=None,
+                ln1_beta=None) -> LayerParams:
     return LayerParams(ptr(w1), ptr(b1), ptr(w2), ptr(b2), ptr(gamma), ptr(beta),
-                       ptr(pos_bias), ptr(time_bias))
+                       ptr(pos_bias), ptr(time_bias), ptr(ln1_gamma), ptr(ln1_beta))
 
 
 # ---------------------------------------------------------------------------
@@ -174,6 +181,17 @@ def hstu_attn_fwd(desc, jagged, cache, q, k, v, pos_bias, time_bias, av, workspa
 def hstu_norm_gate_fwd(desc, T, av, u, gamma, beta, g, stream=None) -> None:
     _check(load().hstu_norm_gate_fwd(_ref(desc), int(T), ptr(av), ptr(u), ptr(gamma), ptr(beta),
                                      ptr(g), stream if stream is not None else current_stream()))
+
+
+def hstu_layernorm_fwd(desc, T, x, gamma, beta, y, stream=None) -> None:
+    _check(load().hstu_layernorm_fwd(_ref(desc), int(T), ptr(x), ptr(gamma), ptr(beta), ptr(y),
+                                     stream if stream is not None else current_stream()))
+
+
+def hstu_linear_bias_tables(desc, m_p, m_t, pos_bias, time_bias, stream=None) -> None:
+    _check(load().hstu_linear_bias_tables(_ref(desc), float(m_p), float(m_t), ptr(pos_bias),
+                                          ptr(time_bias),
+                                          stream if stream is not None else current_stream()))
 
 
 def hstu_out_fwd(desc, T, g, x, w2, b2, y, stream=None) -> None:

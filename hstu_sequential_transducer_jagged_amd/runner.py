@@ -30,7 +30,12 @@ def _torch():
 
 
 class DeviceLayer:
-    def __init__(self, p, dtype: int, device):
+    """Device copy of one layer's parameters, with the layer's own descriptor
+    (``desc`` with input_norm set when the layer has the input LayerNorm).
+    A layer with ``linear_bias`` = (m_p, m_t) gets its position and time
+    tables filled on the device by ``hstu_linear_bias_tables``."""
+
+    def __init__(self, p, dtype: int, device, desc=None):
         torch = _torch()
         act = torch.bfloat16 if dtype == hstu.HSTU_BF16 else torch.float32
         f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
@@ -42,8 +47,18 @@ class DeviceLayer:
         self.beta = f32(p.beta)
         self.pos_bias = f32(p.pos_bias)
         self.time_bias = f32(p.time_bias)
+        norm1 = bool(getattr(p, "input_norm", False))
+        self.ln1_gamma = f32(p.ln1_gamma) if norm1 and getattr(p, "ln1_gamma", None) is not None else None
+        self.ln1_beta = f32(p.ln1_beta) if norm1 and getattr(p, "ln1_beta", None) is not None else None
+        self.desc = None
+        if desc is not None:
+            self.desc = hstu.LayerDesc.from_buffer_copy(desc)
+            self.desc.input_norm = int(norm1)
+            lin = getattr(p, "linear_bias", None)
+            if lin is not None:
+                hstu.hstu_linear_bias_tables(self.desc, lin[0], lin[1], self.pos_bias, self.time_bias)
         self.params = hstu.make_params(self.w1, self.b1, self.w2, self.b2, self.gamma, self.beta,
-                                       self.pos_bias, self.time_bias)
+                                       self.pos_bias, self.time_bias, self.ln1_gamma, self.ln1_beta)
 
 
 class DeviceWorkload:
@@ -64,7 +79,7 @@ class DeviceWorkload:
                                   hstu.ptr(self.offsets), hstu.ptr(self.timestamps), None)
         self.x = None if w.x is None else self.upload_act(w.x)
         idx = range(len(w.layers)) if layers is None else layers
-        self.layers = [DeviceLayer(w.layers[i], self.dtype, device) for i in idx]
+        self.layers = [DeviceLayer(w.layers[i], self.dtype, device, self.desc) for i in idx]
         if w.item_emb is not None:
             self.item_emb = self.upload_act(w.item_emb)
             self.action_emb = self.upload_act(w.action_emb)
@@ -80,8 +95,11 @@ class DeviceWorkload:
         return torch.empty((max(T, 1), self.w.d_model), dtype=self.act, device=self.device)
 
     def workspace(self, jagged=None):
-        return hstu.workspace_tensor(hstu.hstu_layer_workspace_size(self.desc, jagged or self.jagged),
-                                     self.device)
+        """A workspace large enough for every layer (with or without Norm1)."""
+        j = jagged or self.jagged
+        need = max([hstu.hstu_layer_workspace_size(self.desc, j)] +
+                   [hstu.hstu_layer_workspace_size(l.desc, j) for l in self.layers])
+        return hstu.workspace_tensor(need, self.device)
 
 
 def layer_forward(dw: DeviceWorkload, x, layer: int = 0, y=None, workspace=None, jagged=None,
@@ -90,7 +108,8 @@ def layer_forward(dw: DeviceWorkload, x, layer: int = 0, y=None, workspace=None,
     T = jagged.total_tokens
     y = dw.empty_act(T) if y is None else y
     ws = dw.workspace(jagged) if workspace is None else workspace
-    hstu.hstu_layer_fwd(dw.desc, dw.layers[layer].params, jagged, cache, x, y, k_out, v_out, ws)
+    hstu.hstu_layer_fwd(dw.layers[layer].desc, dw.layers[layer].params, jagged, cache, x, y, k_out,
+                        v_out, ws)
     return y
 
 
@@ -182,7 +201,7 @@ def ranking_forward(dw: DeviceWorkload, plan: RankingPlan, keep_history: bool = 
         xin = cx[start:start + n]
         for l in range(L):
             y = out[start:start + n] if l == L - 1 else dw.empty_act(n)
-            hstu.hstu_layer_fwd(dw.desc, dw.layers[l].params, jag, caches[l], xin, y, None, None,
+            hstu.hstu_layer_fwd(dw.layers[l].desc, dw.layers[l].params, jag, caches[l], xin, y, None, None,
                                 wsc)
             xin = y
     torch.cuda.current_stream().synchronize()

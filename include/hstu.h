@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 2
+#define HSTU_ABI_VERSION 3
 
 typedef enum {
   HSTU_OK = 0,
@@ -80,6 +80,10 @@ typedef struct {
   float ln_eps;             /* LayerNorm epsilon, >= 0 (1e-5 by default) */
   int32_t pos_table_len;    /* 2*n_max - 1 (odd); index = (p_i - p_j) + n_max - 1 */
   int32_t num_time_buckets; /* 1..64 (32 by default) */
+  int32_t input_norm;       /* 0 (default) or 1: hstu_layer_fwd first applies the input
+                               LayerNorm (params ln1_gamma/ln1_beta, eps ln_eps) to X,
+                               the Norm1 of the block diagram of "万亿参数推荐大模型…"
+                               §2.1; the residual still adds the raw X */
 } hstu_layer_desc;
 
 /* A jagged batch of the call's own tokens. */
@@ -114,6 +118,8 @@ typedef struct {
   const float *ln_beta;         /* [d] or NULL (zeros) */
   const float *pos_bias;        /* [pos_table_len] */
   const float *time_bias;       /* [num_time_buckets] */
+  const float *ln1_gamma;       /* [d] or NULL (ones): input LayerNorm, read if input_norm */
+  const float *ln1_beta;        /* [d] or NULL (zeros) */
 } hstu_layer_params;
 
 /* ABI version of the loaded library (HSTU_ABI_VERSION). */
@@ -166,16 +172,38 @@ int hstu_attn_fwd(const hstu_layer_desc *desc, const hstu_jagged *jagged,
 int hstu_norm_gate_fwd(const hstu_layer_desc *desc, int64_t T, const float *av, const void *u,
                        const float *gamma, const float *beta, void *g, void *stream);
 
+/* Input LayerNorm, the Norm1 that the block diagram of "万亿参数推荐大模型…"
+ * §2.1 draws before f1 (the layer equations have none; hstu_layer_fwd
+ * applies it when desc->input_norm is 1):
+ *   y = LayerNorm_d(x) * gamma + beta
+ * over all d features with the biased variance and desc->ln_eps. x, y
+ * [T, d] dtype (y must not alias x); gamma/beta [d] fp32 or NULL. */
+int hstu_layernorm_fwd(const hstu_layer_desc *desc, int64_t T, const void *x, const float *gamma,
+                       const float *beta, void *y, void *stream);
+
+/* Tables of the parameter-free relative bias of "6.2. HSTU的工程突破"
+ * eq. 6.2.6 (ALiBi's eq. 6.2.5 extended to time), with scalar slopes shared
+ * by all heads:
+ *   pos_bias[i]  = -m_p * (i - (n_max - 1))     i < pos_table_len
+ *   time_bias[b] = -m_t * b                     b < num_time_buckets
+ * With them, the table bias of every entry point equals
+ * -m_p (p_i - p_j) - m_t bucket(t_i - t_j) exactly up to one fp32 rounding
+ * of each product. pos_bias [pos_table_len], time_bias [num_time_buckets]:
+ * device fp32 outputs, overwritten. m_p, m_t finite. */
+int hstu_linear_bias_tables(const hstu_layer_desc *desc, float m_p, float m_t, float *pos_bias,
+                            float *time_bias, void *stream);
+
 /* Pointwise transformation, second half: y = x + g W2^T + b2
  * (f2 with the residual connection). g, x, y [T, d] dtype. */
 int hstu_out_fwd(const hstu_layer_desc *desc, int64_t T, const void *g, const void *x,
                  const void *w2, const float *b2, void *y, void *stream);
 
 /* Workspace bytes hstu_layer_fwd needs for this batch (host fields of
- * `jagged` only). */
+ * `jagged` only; one more [T, d] dtype buffer when desc->input_norm). */
 size_t hstu_layer_workspace_size(const hstu_layer_desc *desc, const hstu_jagged *jagged);
 
-/* One full layer: projection -> attention -> norm/gate -> f2 + residual.
+/* One full layer: [input LayerNorm ->] projection -> attention -> norm/gate
+ * -> f2 + residual (the residual adds the raw x).
  * x, y [T, d] dtype (y must not alias x). k_out / v_out: NULL, or [T, d]
  * dtype buffers that receive this call's K and V (to build a cache for later
  * calls). workspace: device, >= hstu_layer_workspace_size() bytes, 256-byte

@@ -35,7 +35,7 @@ def test_header_declares_the_binding_exports():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.hstu_abi_version() == 2
+    assert lib.hstu_abi_version() == 3
 
 
 def _desc(**kw):
@@ -135,6 +135,36 @@ def test_layer_workspace_checks(lib):
     st = lib.hstu_layer_fwd(ctypes.byref(d), ctypes.byref(params), ctypes.byref(_jag()), None,
                             P(FAKE), P(FAKE), None, None, P(FAKE), need, None)
     assert st == hstu.HSTU_E_INVAL                             # y aliases x
+
+
+def test_option_entry_points_validate(lib):
+    """The input LayerNorm and the parameter-free bias tables reject bad
+    arguments on the host; an input_norm flag other than 0/1 is refused by
+    every entry point, and the layer workspace grows by one [T, d] buffer."""
+    P = ctypes.c_void_p
+    d = _desc()
+    assert lib.hstu_layernorm_fwd(ctypes.byref(d), 0, None, None, None, None, None) == hstu.HSTU_OK
+    assert lib.hstu_layernorm_fwd(ctypes.byref(d), 4, P(FAKE), None, None, P(FAKE),
+                                  None) == hstu.HSTU_E_INVAL        # y aliases x
+    assert lib.hstu_layernorm_fwd(ctypes.byref(d), 4, P(FAKE), P(FAKE + 4), None, P(FAKE + 4096),
+                                  None) == hstu.HSTU_E_INVAL        # gamma misaligned
+    assert lib.hstu_layernorm_fwd(ctypes.byref(d), -1, P(FAKE), None, None, P(FAKE + 4096),
+                                  None) == hstu.HSTU_E_INVAL
+    for mp, mt in ((float("nan"), 0.1), (0.1, float("inf"))):
+        assert lib.hstu_linear_bias_tables(ctypes.byref(d), mp, mt, P(FAKE), P(FAKE + 4096),
+                                           None) == hstu.HSTU_E_INVAL
+    assert lib.hstu_linear_bias_tables(ctypes.byref(d), 0.1, 0.1, P(FAKE), P(FAKE),
+                                       None) == hstu.HSTU_E_INVAL   # tables alias
+    assert lib.hstu_linear_bias_tables(ctypes.byref(d), 0.1, 0.1, None, P(FAKE),
+                                       None) == hstu.HSTU_E_INVAL
+    bad = _desc()
+    bad.input_norm = 2
+    assert _attn(lib, bad, _jag()) == hstu.HSTU_E_INVAL
+    assert b"input_norm" in lib.hstu_last_error()
+    n1 = _desc()
+    n1.input_norm = 1
+    base = lib.hstu_layer_workspace_size(ctypes.byref(d), ctypes.byref(_jag()))
+    assert lib.hstu_layer_workspace_size(ctypes.byref(n1), ctypes.byref(_jag())) == base + 10240
 
 
 def test_binding_raises_with_message(lib):
