@@ -46,6 +46,12 @@ def parse():
     ap.add_argument("--spin-up-s", type=float, default=0.3,
                     help="untimed seconds of back-to-back steps before the warm-up steps, so "
                          "that the GPU clocks have settled under load when timing starts")
+    ap.add_argument("--input-norm", action="store_true",
+                    help="layer workloads: apply the input LayerNorm (Norm1) before f1 "
+                         "(gamma 1, beta 0, as the default affine recipe)")
+    ap.add_argument("--linear-bias", type=str, default=None, metavar="MP,MT",
+                    help="layer workloads: parameter-free position/time bias slopes in place "
+                         "of the drawn tables (tables filled by hstu_linear_bias_tables)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
                     help="approximate CPU seconds for the oracle sample")
@@ -129,6 +135,14 @@ def run_layer(args):
     from hstu_sequential_transducer_jagged_amd import hstu, runner
 
     w = gen.make_config(args.workload)
+    lin = tuple(float(t) for t in args.linear_bias.split(",")) if args.linear_bias else None
+    for p in w.layers:
+        if args.input_norm:
+            p.input_norm = True
+            p.ln1_gamma = np.ones(w.d_model, np.float32)
+            p.ln1_beta = np.zeros(w.d_model, np.float32)
+        if lin is not None:
+            p.linear_bias = lin
     dw = runner.DeviceWorkload(w)
     T, d, H = w.total_tokens, w.d_model, w.num_heads
     P = visible_pairs(w.offsets)
@@ -137,24 +151,32 @@ def run_layer(args):
     act = dw.act
     mk = lambda dt=act: torch.empty((T, d), dtype=dt, device="cuda")
     u, v, q, k, g, y = mk(), mk(), mk(), mk(), mk(), mk()
+    xn = mk() if args.input_norm else None
     av = mk(torch.float32)
     x = dw.x
-    desc, jag = dw.desc, dw.jagged
+    desc, jag = lay.desc, dw.jagged
     attn_ws = hstu.workspace_tensor(hstu.hstu_attn_workspace_size(desc, jag))
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
+    names = (["layernorm"] if args.input_norm else []) + ["proj", "attn", "norm_gate", "out"]
 
     def step(ev=None):
-        rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
-        rec(0)
-        hstu.hstu_proj_fwd(desc, lay.params, T, x, u, v, q, k, sh)
-        rec(1)
+        i = iter(range(len(names) + 1))
+        rec = (lambda: ev[next(i)].record(stream)) if ev is not None else (lambda: None)
+        rec()
+        xin = x
+        if args.input_norm:
+            hstu.hstu_layernorm_fwd(desc, T, x, lay.ln1_gamma, lay.ln1_beta, xn, sh)
+            rec()
+            xin = xn
+        hstu.hstu_proj_fwd(desc, lay.params, T, xin, u, v, q, k, sh)
+        rec()
         hstu.hstu_attn_fwd(desc, jag, None, q, k, v, lay.pos_bias, lay.time_bias, av, attn_ws, sh)
-        rec(2)
+        rec()
         hstu.hstu_norm_gate_fwd(desc, T, av, u, lay.gamma, lay.beta, g, sh)
-        rec(3)
+        rec()
         hstu.hstu_out_fwd(desc, T, g, x, lay.w2, lay.b2, y, sh)
-        rec(4)
+        rec()
 
     calib = copy_calibration(torch) if args.copy_calib else None
     K = args.steps
@@ -169,7 +191,7 @@ def run_layer(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -180,8 +202,8 @@ def run_layer(args):
     ms_separate = start.elapsed_time(end) / K
     # per-launch durations (ms) of each kernel, one sample per timed step
     per = {name: np.array([e[j].elapsed_time(e[j + 1]) for e in evs])
-           for j, name in enumerate(["proj", "attn", "norm_gate", "out"])}
-    steps_ms = np.array([e[0].elapsed_time(e[4]) for e in evs])
+           for j, name in enumerate(names)}
+    steps_ms = np.array([e[0].elapsed_time(e[len(names)]) for e in evs])
     attn_ms = float(np.mean(per["attn"]))
     pct = lambda a: {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
                      "p90": float(np.percentile(a, 90))}
@@ -205,6 +227,10 @@ def run_layer(args):
         "out": {"ms": pct(per["out"]), "tflops": out_flop / np.mean(per["out"]) / 1e9,
                 "pct_peak": 100 * out_flop / np.mean(per["out"]) / 1e9 / peak},
         "step": {"ms": pct(steps_ms)},
+        **({"layernorm": {"ms": pct(per["layernorm"]),
+                          "gbs": 2 * T * d * esz / np.mean(per["layernorm"]) / 1e6,
+                          "pct_hbm_peak": 100 * 2 * T * d * esz / np.mean(per["layernorm"]) / 1e6
+                                          / PEAK_HBM_GBS}} if args.input_norm else {}),
     }
     src = os.path.join(ROOT, "hstu_sequential_transducer_jagged_amd", "csrc", "attn.hip")
     rec = {
@@ -223,7 +249,9 @@ def run_layer(args):
         "data": "synthetic (seeded; no dataset)",
         "config": {"workload": gen.CONFIG_NAMES[args.workload], "total_tokens": T,
                    "num_seqs": w.num_seqs, "max_seq_len": w.max_seq_len, "d_model": d,
-                   "num_heads": H, "head_dim": d // H, "visible_pairs": P},
+                   "num_heads": H, "head_dim": d // H, "visible_pairs": P,
+                   "input_norm": bool(args.input_norm),
+                   "bias": ("parameter-free m_p=%g m_t=%g" % lin) if lin else "tables"},
         "roofline": {"kernel": "attn_" + w.dtype, "bound": "mfma" if w.dtype == "bf16" else "alu",
                      "achieved": attn_tflops, "peak": peak, "unit": "TFLOP/s",
                      "frac": attn_tflops / peak,
@@ -479,6 +507,10 @@ def main():
 
     from hstu_sequential_transducer_jagged_amd import hstu
     hstu.load()
+    if (args.input_norm or args.linear_bias) and args.workload in (3, 4):
+        print("--input-norm and --linear-bias apply to the single-layer workloads 0-2",
+              file=sys.stderr)
+        sys.exit(2)
     run = {3: run_stack, 4: run_ranking}.get(args.workload, run_layer)
     print(json.dumps(run(args)), flush=True)
 
