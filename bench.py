@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--linear-bias", type=str, default=None, metavar="MP,MT",
                     help="layer workloads: parameter-free position/time bias slopes in place "
                          "of the drawn tables (tables filled by hstu_linear_bias_tables)")
+    ap.add_argument("--b-m", type=int, default=None,
+                    help="ranking workload: candidates per user per micro-batch (default 128)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
                     help="approximate CPU seconds for the oracle sample")
@@ -391,7 +393,7 @@ def run_ranking(args):
     w = gen.make_config(4)
     dw = runner.DeviceWorkload(w)
     Th, d, L = w.total_tokens, w.d_model, len(w.layers)
-    plan = runner.RankingPlan(w)
+    plan = runner.RankingPlan(w, args.b_m)
     dev = dw.device
     kc = [dw.empty_act(Th) for _ in range(L)]
     vc = [dw.empty_act(Th) for _ in range(L)]
@@ -449,6 +451,7 @@ def run_ranking(args):
     rec["history_ms"] = ms_h
     rec["candidates_per_s"] = Tc / (ms_c * 1e-3)
     rec["candidates_ms"] = ms_c
+    rec["ms_per_micro_batch"] = ms_c / max(len(mbs), 1)   # all layers, all users
     rec["roofline"] = None
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline_ranking(w, args.cpu_budget_s)
