@@ -294,6 +294,37 @@ int hstu_linear_bias_tables(const hstu_layer_desc* desc, float m_p, float m_t, f
                        "linear bias tables launch");
 }
 
+int hstu_kv_cache_concat(const hstu_layer_desc* desc, int32_t num_seqs, const hstu_kv_cache* a,
+                         const hstu_kv_cache* n, int64_t* out_offsets, int64_t* out_timestamps,
+                         void* out_k, void* out_v, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  CHECK(num_seqs >= 0, HSTU_E_INVAL, "num_seqs must be >= 0");
+  CHECK(a && n, HSTU_E_INVAL, "a and n must not be NULL");
+  CHECK(a->total_tokens >= 0 && n->total_tokens >= 0, HSTU_E_INVAL, "total_tokens must be >= 0");
+  CHECK(a->offsets && n->offsets && out_offsets, HSTU_E_INVAL, "offsets must not be NULL");
+  const int64_t rows = a->total_tokens + n->total_tokens;
+  CHECK(num_seqs > 0 || rows == 0, HSTU_E_INVAL, "rows without sequences");
+  if (rows > 0) {
+    CHECK(out_timestamps && out_k && out_v, HSTU_E_INVAL, "outputs must not be NULL");
+    CHECK(aligned16(out_k) && aligned16(out_v), HSTU_E_INVAL, "out_k/out_v must be 16-byte aligned");
+    for (const hstu_kv_cache* c : {a, n}) {
+      if (c->total_tokens == 0) continue;
+      CHECK(c->timestamps && c->k && c->v, HSTU_E_INVAL, "cache timestamps/k/v must not be NULL");
+      CHECK(aligned16(c->k) && aligned16(c->v), HSTU_E_INVAL, "cache k/v must be 16-byte aligned");
+      CHECK(c->k != out_k && c->k != out_v && c->v != out_k && c->v != out_v &&
+                c->timestamps != out_timestamps && c->offsets != out_offsets,
+            HSTU_E_INVAL, "outputs must not alias the inputs");
+    }
+  }
+  const int row_bytes = desc->d_model * static_cast<int>(elem_size(desc->dtype));
+  hstu::CacheConcatArgs c{a->offsets, a->timestamps, a->k, a->v,
+                          n->offsets, n->timestamps, n->k, n->v,
+                          out_offsets, out_timestamps, out_k, out_v,
+                          rows, a->total_tokens, n->total_tokens, num_seqs, row_bytes};
+  return device_status(hstu::launch_cache_concat(c, as_stream(stream)), "cache concat launch");
+}
+
 int hstu_out_fwd(const hstu_layer_desc* desc, int64_t T, const void* g, const void* x,
                  const void* w2, const float* b2, void* y, void* stream) {
   int st = check_desc(desc);

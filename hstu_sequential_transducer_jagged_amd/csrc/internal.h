@@ -112,6 +112,29 @@ struct LayerNormArgs {
 hipError_t launch_layernorm_bf16(const LayerNormArgs& a, hipStream_t s);
 hipError_t launch_layernorm_f32(const LayerNormArgs& a, hipStream_t s);
 
+// Per-sequence concatenation of two K/V caches: rows of sequence b in out
+// are [a's rows of b, then n's rows of b]; out offsets = a + n offsets.
+struct CacheConcatArgs {
+  const int64_t* a_off;  // [B+1]
+  const int64_t* a_ts;
+  const void* a_k;
+  const void* a_v;
+  const int64_t* n_off;  // [B+1]
+  const int64_t* n_ts;
+  const void* n_k;
+  const void* n_v;
+  int64_t* out_off;      // [B+1]
+  int64_t* out_ts;
+  void* out_k;
+  void* out_v;
+  int64_t rows;          // a_T + n_T
+  int64_t a_T;           // rows of a and of n (source rows are clamped to them)
+  int64_t n_T;
+  int B;
+  int row_bytes;         // d * element size, a multiple of 16
+};
+hipError_t launch_cache_concat(const CacheConcatArgs& a, hipStream_t s);
+
 // pos[i] = -m_p * (i - (len - 1) / 2), time[b] = -m_t * b: the tables that
 // make the table bias equal the parameter-free position/time bias.
 hipError_t launch_linear_bias_tables(float m_p, float m_t, int pos_len, int num_buckets,

@@ -15,9 +15,15 @@
 // linear_bias_tables: the position and time tables of the parameter-free
 //   bias of "6.2. HSTU的工程突破" eq. 6.2.6, -m_p (p_i - p_j) - m_t bucket.
 //
+// cache_concat: appends a later request's K/V rows to a user's cached ones
+//   (M-FALCON caching across requests, "HSTU：Scaling Law 的首次探索"
+//   §7.1.5); one wave copies one output row with 16-byte accesses.
+//
 // embed: X[t] = item_emb[id_t] + action_emb[a_t], the action-oriented token
 //   of "6.2. HSTU的工程突破" eq. 6.2.2. One wavefront per token, 16-byte
 //   gathers of the two rows, fp32 add, one rounding.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -109,6 +115,37 @@ __global__ __launch_bounds__(256) void linear_bias_tables_kernel(float m_p, floa
     for (int b = threadIdx.x; b < num_buckets; b += 256) time[b] = -m_t * static_cast<float>(b);
 }
 
+__global__ __launch_bounds__(256) void cache_concat_kernel(CacheConcatArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (gid <= a.B) a.out_off[gid] = a.a_off[gid] + a.n_off[gid];
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= a.rows) return;
+  // sequence b of output row r: the last b with a_off[b] + n_off[b] <= r
+  int lo = 0, hi = a.B;   // invariant: start(lo) <= r < start(hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.a_off[mid] + a.n_off[mid] <= r) lo = mid; else hi = mid;
+  }
+  const int64_t k = r - (a.a_off[lo] + a.n_off[lo]);   // row within the sequence
+  const int64_t na = a.a_off[lo + 1] - a.a_off[lo];
+  bool from_a = k < na;
+  if (a.a_T == 0) from_a = false;   // an empty input may come with NULL pointers
+  if (a.n_T == 0) from_a = true;
+  // (clamped: offsets that break their contract never lead outside the inputs)
+  const int64_t src = from_a ? min(max(a.a_off[lo] + k, int64_t{0}), a.a_T - 1)
+                             : min(max(a.n_off[lo] + (k - na), int64_t{0}), a.n_T - 1);
+  const uint8_t* sk = static_cast<const uint8_t*>(from_a ? a.a_k : a.n_k) + src * a.row_bytes;
+  const uint8_t* sv = static_cast<const uint8_t*>(from_a ? a.a_v : a.n_v) + src * a.row_bytes;
+  uint8_t* dk = static_cast<uint8_t*>(a.out_k) + r * a.row_bytes;
+  uint8_t* dv = static_cast<uint8_t*>(a.out_v) + r * a.row_bytes;
+  for (int c = lane * 16; c < a.row_bytes; c += 64 * 16) {
+    *reinterpret_cast<uint4*>(dk + c) = *reinterpret_cast<const uint4*>(sk + c);
+    *reinterpret_cast<uint4*>(dv + c) = *reinterpret_cast<const uint4*>(sv + c);
+  }
+  if (lane == 0) a.out_ts[r] = from_a ? a.a_ts[src] : a.n_ts[src];
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
   const int lane = threadIdx.x & 63;
@@ -194,6 +231,13 @@ hipError_t launch_linear_bias_tables(float m_p, float m_t, int pos_len, int num_
   const int grid = (pos_len + 255) / 256;
   hipLaunchKernelGGL(linear_bias_tables_kernel, dim3(grid > 0 ? grid : 1), dim3(256), 0, s, m_p, m_t,
                      pos_len, num_buckets, pos, time);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_concat(const CacheConcatArgs& a, hipStream_t s) {
+  // enough blocks for every output row (4 per block) and for the B + 1 offsets
+  const int64_t blocks = std::max<int64_t>((a.rows + 3) / 4, (static_cast<int64_t>(a.B) + 1 + 255) / 256);
+  hipLaunchKernelGGL(cache_concat_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

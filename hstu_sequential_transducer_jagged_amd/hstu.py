@@ -29,6 +29,7 @@ HSTU_BF16 = 1
 EXPORTS = ("hstu_abi_version", "hstu_last_error", "hstu_proj_fwd", "hstu_attn_workspace_size",
            "hstu_attn_fwd",
            "hstu_norm_gate_fwd", "hstu_layernorm_fwd", "hstu_linear_bias_tables",
+           "hstu_kv_cache_concat",
            "hstu_out_fwd", "hstu_layer_workspace_size",
            "hstu_layer_fwd", "hstu_embed_fwd", "hstu_check_inputs")
 
@@ -91,6 +92,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "hstu_norm_gate_fwd": (ctypes.c_int, [P, i64, P, P, P, P, P, P]),
         "hstu_layernorm_fwd": (ctypes.c_int, [P, i64, P, P, P, P, P]),
         "hstu_linear_bias_tables": (ctypes.c_int, [P, ctypes.c_float, ctypes.c_float, P, P, P]),
+        "hstu_kv_cache_concat": (ctypes.c_int, [P, i32, P, P, P, P, P, P, P]),
         "hstu_out_fwd": (ctypes.c_int, [P, i64, P, P, P, P, P, P]),
         "hstu_layer_workspace_size": (ctypes.c_size_t, [P, P]),
         "hstu_layer_fwd": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
@@ -192,6 +194,13 @@ def hstu_linear_bias_tables(desc, m_p, m_t, pos_bias, time_bias, stream=None) ->
     _check(load().hstu_linear_bias_tables(_ref(desc), float(m_p), float(m_t), ptr(pos_bias),
                                           ptr(time_bias),
                                           stream if stream is not None else current_stream()))
+
+
+def hstu_kv_cache_concat(desc, num_seqs, a, n, out_offsets, out_timestamps, out_k, out_v,
+                         stream=None) -> None:
+    _check(load().hstu_kv_cache_concat(_ref(desc), int(num_seqs), _ref(a), _ref(n), ptr(out_offsets),
+                                       ptr(out_timestamps), ptr(out_k), ptr(out_v),
+                                       stream if stream is not None else current_stream()))
 
 
 def hstu_out_fwd(desc, T, g, x, w2, b2, y, stream=None) -> None:

@@ -163,6 +163,84 @@ class RankingPlan:
         self.micro_batches = mbs  # (first device row, offsets, max length)
 
 
+def request_forward(dw: DeviceWorkload, jagged, x, caches=None, workspace=None):
+    """One request's own tokens through every layer; layer l also attends to
+    ``caches[l]`` (a C cache descriptor) when given. Returns the last layer's
+    output and every layer's K and V of these tokens (to cache them)."""
+    T = jagged.total_tokens
+    L = len(dw.layers)
+    ks = [dw.empty_act(T) for _ in range(L)]
+    vs = [dw.empty_act(T) for _ in range(L)]
+    ws = dw.workspace(jagged) if workspace is None else workspace
+    h = x
+    for l in range(L):
+        y = dw.empty_act(T)
+        hstu.hstu_layer_fwd(dw.layers[l].desc, dw.layers[l].params, jagged,
+                            None if caches is None else caches[l], h, y, ks[l], vs[l], ws)
+        h = y
+    return h, ks, vs
+
+
+class DeviceCache:
+    """One layer's K/V cache on the device with its C descriptor (the tensors
+    stay referenced while the descriptor is in use)."""
+
+    def __init__(self, offsets, timestamps, k, v, max_len: int, total_tokens: int):
+        self.offsets, self.timestamps, self.k, self.v = offsets, timestamps, k, v
+        self.c = hstu.KVCache(hstu.ptr(offsets), hstu.ptr(timestamps), hstu.ptr(k), hstu.ptr(v),
+                              int(max_len), int(total_tokens))
+
+
+def concat_caches(dw: DeviceWorkload, a_caches, n_offsets, n_timestamps, n_ks, n_vs,
+                  n_total: int, max_len: int):
+    """Per layer, the earlier request's cache followed, user by user, by the
+    K/V rows of the tokens a later request added (hstu_kv_cache_concat).
+    ``max_len`` bounds every user's combined length."""
+    torch = _torch()
+    B = n_offsets.numel() - 1
+    out = []
+    for l, a in enumerate(a_caches):
+        n = hstu.KVCache(hstu.ptr(n_offsets), hstu.ptr(n_timestamps), hstu.ptr(n_ks[l]),
+                         hstu.ptr(n_vs[l]), 0, int(n_total))
+        rows = a.c.total_tokens + int(n_total)
+        off = torch.empty(B + 1, dtype=torch.int64, device=dw.device)
+        ts = torch.empty(max(rows, 1), dtype=torch.int64, device=dw.device)
+        k, v = dw.empty_act(rows), dw.empty_act(rows)
+        hstu.hstu_kv_cache_concat(dw.layers[l].desc, B, a.c, n, off, ts, k, v)
+        out.append(DeviceCache(off, ts, k, v, max_len, rows))
+    return out
+
+
+def score_candidates(dw: DeviceWorkload, plan: RankingPlan, caches, cand_x, cand_ts):
+    """Every micro-batch of the plan through all layers against the per-layer
+    caches (C descriptors). cand_x / cand_ts: device rows in the plan's
+    order. Returns the final outputs in that order."""
+    torch = _torch()
+    dev = dw.device
+    L = len(dw.layers)
+    out = torch.empty_like(cand_x)
+    keep = []
+    for (start, offs, mlen) in plan.micro_batches:
+        n = int(offs[-1])
+        if n == 0:
+            continue
+        offs_d = torch.from_numpy(offs).to(dev)
+        tgt_d = torch.from_numpy(np.diff(offs).astype(np.int32)).to(dev)
+        jag = hstu.Jagged(len(offs) - 1, mlen, n, hstu.ptr(offs_d),
+                          hstu.ptr(cand_ts) + 8 * start, hstu.ptr(tgt_d))
+        keep.append((offs_d, tgt_d))
+        wsc = dw.workspace(jag)
+        xin = cand_x[start:start + n]
+        for l in range(L):
+            y = out[start:start + n] if l == L - 1 else dw.empty_act(n)
+            hstu.hstu_layer_fwd(dw.layers[l].desc, dw.layers[l].params, jag, caches[l], xin, y,
+                                None, None, wsc)
+            xin = y
+    torch.cuda.current_stream().synchronize()
+    del keep
+    return out
+
+
 def ranking_forward(dw: DeviceWorkload, plan: RankingPlan, keep_history: bool = False):
     """History pass (keeps K, V per layer), then every micro-batch through all
     layers against the cached history. Returns the final candidate outputs in
@@ -184,26 +262,7 @@ def ranking_forward(dw: DeviceWorkload, plan: RankingPlan, keep_history: bool = 
         h = y
     cx = dw.upload_act(np.asarray(w.cand_x)[plan.order])
     cts = torch.from_numpy(np.asarray(w.cand_timestamps, np.int64)[plan.order]).to(dev)
-    out = torch.empty_like(cx)
     caches = [hstu.make_cache(dw.offsets, dw.timestamps, kc[l], vc[l], w.max_seq_len)
               for l in range(L)]
-    keep = []
-    for (start, offs, mlen) in plan.micro_batches:
-        n = int(offs[-1])
-        if n == 0:
-            continue
-        offs_d = torch.from_numpy(offs).to(dev)
-        tgt_d = torch.from_numpy(np.diff(offs).astype(np.int32)).to(dev)
-        jag = hstu.Jagged(len(offs) - 1, mlen, n, hstu.ptr(offs_d),
-                          hstu.ptr(cts) + 8 * start, hstu.ptr(tgt_d))
-        keep.append((offs_d, tgt_d))
-        wsc = dw.workspace(jag)
-        xin = cx[start:start + n]
-        for l in range(L):
-            y = out[start:start + n] if l == L - 1 else dw.empty_act(n)
-            hstu.hstu_layer_fwd(dw.layers[l].desc, dw.layers[l].params, jag, caches[l], xin, y, None, None,
-                                wsc)
-            xin = y
-    torch.cuda.current_stream().synchronize()
-    del keep
+    out = score_candidates(dw, plan, caches, cx, cts)
     return (out, hist) if keep_history else out

@@ -193,6 +193,23 @@ int hstu_layernorm_fwd(const hstu_layer_desc *desc, int64_t T, const void *x, co
 int hstu_linear_bias_tables(const hstu_layer_desc *desc, float m_p, float m_t, float *pos_bias,
                             float *time_bias, void *stream);
 
+/* Per-sequence concatenation of two K/V caches, for candidate scoring across
+ * requests (M-FALCON, "HSTU：Scaling Law 的首次探索" §7.1.5: a user's later
+ * request reuses the cached history and adds the tokens that arrived since
+ * it was cached):
+ *   rows of sequence b in out = [a's rows of b, then n's rows of b]
+ *   out_offsets[b] = a->offsets[b] + n->offsets[b]        (b = 0..num_seqs)
+ * a and n: num_seqs sequences each (offsets [num_seqs+1], timestamps, k, v
+ * [total_tokens, d] dtype; max_len unused). Typically a is the cache of the
+ * earlier request and n the K/V (hstu_layer_fwd k_out/v_out) of the new
+ * tokens, computed with a as their cache. Outputs: out_offsets
+ * [num_seqs+1], out_timestamps [a_T + n_T] int64, out_k/out_v
+ * [a_T + n_T, d] dtype; none may alias an input. Rows are read within
+ * each input's total_tokens even if its device offsets are inconsistent. */
+int hstu_kv_cache_concat(const hstu_layer_desc *desc, int32_t num_seqs, const hstu_kv_cache *a,
+                         const hstu_kv_cache *n, int64_t *out_offsets, int64_t *out_timestamps,
+                         void *out_k, void *out_v, void *stream);
+
 /* Pointwise transformation, second half: y = x + g W2^T + b2
  * (f2 with the residual connection). g, x, y [T, d] dtype. */
 int hstu_out_fwd(const hstu_layer_desc *desc, int64_t T, const void *g, const void *x,

@@ -167,6 +167,24 @@ def test_option_entry_points_validate(lib):
     assert lib.hstu_layer_workspace_size(ctypes.byref(n1), ctypes.byref(_jag())) == base + 10240
 
 
+def test_cache_concat_validates(lib):
+    P = ctypes.c_void_p
+    d = _desc()
+    a = hstu.KVCache(FAKE, FAKE, FAKE, FAKE, 8, 10)
+    n = hstu.KVCache(FAKE + 1024, FAKE + 2048, FAKE + 4096, FAKE + 8192, 8, 5)
+    cc = lambda B, a_, n_, o, t, k, v: lib.hstu_kv_cache_concat(
+        ctypes.byref(d), B, ctypes.byref(a_) if a_ else None, ctypes.byref(n_) if n_ else None,
+        P(o), P(t), P(k), P(v), None)
+    out = (FAKE + 65536, FAKE + 131072, FAKE + 262144, FAKE + 524288)
+    assert cc(-1, a, n, *out) == hstu.HSTU_E_INVAL
+    assert cc(2, None, n, *out) == hstu.HSTU_E_INVAL
+    assert cc(0, a, n, *out) == hstu.HSTU_E_INVAL                  # rows without sequences
+    assert cc(2, a, n, out[0], out[1], FAKE, out[3]) == hstu.HSTU_E_INVAL   # out_k aliases a.k
+    assert cc(2, a, n, out[0], out[1], out[2] + 8, out[3]) == hstu.HSTU_E_INVAL   # misaligned
+    bad = hstu.KVCache(FAKE, FAKE, FAKE, FAKE, 8, -1)
+    assert cc(2, bad, n, *out) == hstu.HSTU_E_INVAL
+
+
 def test_binding_raises_with_message(lib):
     with pytest.raises(hstu.HstuError) as e:
         hstu.hstu_attn_fwd(None, _jag(), None, None, None, None, None, None, None, None, stream=0)
