@@ -54,6 +54,10 @@ def parse():
                          "of the drawn tables (tables filled by hstu_linear_bias_tables)")
     ap.add_argument("--b-m", type=int, default=None,
                     help="ranking workload: candidates per user per micro-batch (default 128)")
+    ap.add_argument("--two-requests", type=float, default=None, metavar="F",
+                    help="ranking workload: also time a second request per user whose first "
+                         "fraction F of the history is already cached (new tokens against the "
+                         "cache, hstu_kv_cache_concat, candidates)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
                     help="approximate CPU seconds for the oracle sample")
@@ -356,6 +360,66 @@ def run_stack(args):
     return rec
 
 
+def two_requests(args, w, dw, stream, candidates, ms_recompute):
+    """Request 1 holds the first fraction F of every user's history (run
+    once, untimed, its K/V cached per layer). The timed request 2 runs the
+    remaining history tokens against that cache, appends their K/V to it
+    (hstu_kv_cache_concat) and scores the same candidates against the
+    combined cache; the alternative recomputes the whole history."""
+    import numpy as np
+    import torch
+
+    from hstu_inputs import gen
+    from hstu_sequential_transducer_jagged_amd import hstu, runner
+
+    f = float(args.two_requests)
+    L, B, dev = len(dw.layers), w.num_seqs, dw.device
+    hl = np.diff(w.offsets)
+    l1 = np.minimum((hl * f).astype(np.int64), hl)
+    l2 = hl - l1
+    r1 = np.concatenate([np.arange(w.offsets[u], w.offsets[u] + l1[u]) for u in range(B)])
+    r2 = np.concatenate([np.arange(w.offsets[u] + l1[u], w.offsets[u + 1]) for u in range(B)])
+    o1, o2 = gen.make_jagged(l1), gen.make_jagged(l2)
+    dev_i64 = lambda a: torch.from_numpy(np.asarray(a, np.int64)).to(dev)
+    off1, off2 = dev_i64(o1), dev_i64(o2)
+    ts1, ts2 = dev_i64(np.asarray(w.timestamps)[r1]), dev_i64(np.asarray(w.timestamps)[r2])
+    x1, x2 = dw.upload_act(np.asarray(w.x)[r1]), dw.upload_act(np.asarray(w.x)[r2])
+    T1, T2 = int(o1[-1]), int(o2[-1])
+    jag1 = hstu.Jagged(B, int(l1.max()), T1, hstu.ptr(off1), hstu.ptr(ts1), None)
+    jag2 = hstu.Jagged(B, int(l2.max()), T2, hstu.ptr(off2), hstu.ptr(ts2), None)
+    _, k1, v1 = runner.request_forward(dw, jag1, x1)
+    c1 = [runner.DeviceCache(off1, ts1, k1[l], v1[l], int(l1.max()), T1) for l in range(L)]
+    k2 = [dw.empty_act(T2) for _ in range(L)]
+    v2 = [dw.empty_act(T2) for _ in range(L)]
+    n2 = [hstu.KVCache(hstu.ptr(off2), hstu.ptr(ts2), hstu.ptr(k2[l]), hstu.ptr(v2[l]), 0, T2)
+          for l in range(L)]
+    rows = T1 + T2
+    c12 = [runner.DeviceCache(torch.empty(B + 1, dtype=torch.int64, device=dev),
+                              torch.empty(rows, dtype=torch.int64, device=dev),
+                              dw.empty_act(rows), dw.empty_act(rows), int(hl.max()), rows)
+           for _ in range(L)]
+    ybuf = [dw.empty_act(T2), dw.empty_act(T2)]
+    ws2 = dw.workspace(jag2)
+    sh = stream.cuda_stream
+
+    def request2():
+        h = x2
+        for l in range(L):
+            hstu.hstu_layer_fwd(dw.layers[l].desc, dw.layers[l].params, jag2, c1[l].c, h, ybuf[l % 2],
+                                k2[l], v2[l], ws2, sh)
+            h = ybuf[l % 2]
+        for l in range(L):
+            c = c12[l]
+            hstu.hstu_kv_cache_concat(dw.layers[l].desc, B, c1[l].c, n2[l], c.offsets, c.timestamps,
+                                      c.k, c.v, sh)
+        candidates([c.c for c in c12])
+
+    ms_reuse = timed(request2, stream, args.warmup, args.steps)
+    return {"cached_fraction": f, "new_history_tokens": T2, "cached_history_tokens": T1,
+            "request2_reuse_ms": ms_reuse, "request2_recompute_ms": ms_recompute,
+            "speedup": ms_recompute / ms_reuse}
+
+
 def cpu_baseline_stack(w, budget_s):
     """The CPU oracle (embedding + every layer) on the first sequences of the
     same workload until ~budget_s of work is done."""
@@ -426,12 +490,12 @@ def run_ranking(args):
             hstu.hstu_layer_fwd(dw.layers[l].desc, dw.layers[l].params, dw.jagged, None, h, y, kc[l], vc[l], ws, sh)
             h = y
 
-    def candidates():
+    def candidates(cs=caches):
         for (start, n, jag, _, _, wsc) in mbs:
             h = cx[start:start + n]
             for l in range(L):
                 y = cbuf[l % 2][start:start + n]
-                hstu.hstu_layer_fwd(dw.layers[l].desc, dw.layers[l].params, jag, caches[l], h, y, None, None,
+                hstu.hstu_layer_fwd(dw.layers[l].desc, dw.layers[l].params, jag, cs[l], h, y, None, None,
                                     wsc, sh)
                 h = y
 
@@ -452,6 +516,8 @@ def run_ranking(args):
     rec["candidates_per_s"] = Tc / (ms_c * 1e-3)
     rec["candidates_ms"] = ms_c
     rec["ms_per_micro_batch"] = ms_c / max(len(mbs), 1)   # all layers, all users
+    if args.two_requests is not None:
+        rec["two_requests"] = two_requests(args, w, dw, stream, candidates, ms)
     rec["roofline"] = None
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline_ranking(w, args.cpu_budget_s)
