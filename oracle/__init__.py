@@ -20,5 +20,6 @@ from .hstu_oracle import (  # noqa: F401
     ranking_independent,
     silu,
     stack,
+    stochastic_length,
     time_bucket,
 )

@@ -103,6 +103,41 @@ def genrank_bias(dp, dt, m_p: float, m_t: float, num_buckets: int = 32):
     return -m_p * dp - m_t * time_bucket(dt, num_buckets).astype(F64)
 
 
+def stochastic_length(offsets, alpha: float, n_max: int, u, keys):
+    """Stochastic Length ([GR-7.1] §7.1.5): a sequence of length n longer
+    than N^(alpha/2) is, with probability p = 1 - N^alpha / n^2, replaced by
+    a subsequence of k = floor(N^(alpha/2)) of its tokens; otherwise it is
+    kept whole (N = n_max; alpha = 2 never truncates).
+
+    The page prints N_{alpha/2} and N_alpha: read as powers. It says only
+    that the subsequence is sampled; here the k tokens with the smallest
+    keys are kept (ties to the earlier token), in their original order.
+    Randomness comes in: u [B] uniform in [0, 1) decides truncation
+    (truncate iff u_b < p_b); keys [T] rank the tokens. Everything is fp64.
+
+    Returns (new offsets [B+1], source rows [T'] sequence-major)."""
+    offsets = np.asarray(offsets, np.int64)
+    u = np.asarray(u, np.float64)
+    keys = np.asarray(keys, np.float64)
+    N = float(n_max)
+    k = int(np.floor(N ** (alpha / 2.0)))
+    rows, lens = [], []
+    for b in range(offsets.shape[0] - 1):
+        s, e = int(offsets[b]), int(offsets[b + 1])
+        n = e - s
+        keep = np.arange(s, e)
+        if n > N ** (alpha / 2.0):
+            p = 1.0 - N ** alpha / (float(n) * float(n))
+            if u[b] < p:
+                order = np.lexsort((np.arange(n), keys[s:e]))   # by key, then index
+                keep = s + np.sort(order[:k])
+        rows.append(keep)
+        lens.append(keep.shape[0])
+    new_off = np.zeros(len(lens) + 1, np.int64)
+    np.cumsum(lens, out=new_off[1:])
+    return new_off, (np.concatenate(rows) if rows else np.zeros(0, np.int64))
+
+
 def layernorm(x, gamma, beta, eps: float):
     """LayerNorm over the d features of each token row, biased variance,
     affine gamma/beta (None: ones/zeros). Used for the optional input norm

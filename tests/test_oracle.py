@@ -663,3 +663,57 @@ def test_layer_input_norm_scale_shift_invariance():
     base = _layer_y(w, x, p) - x
     x2 = 3.5 * x - 1.25
     np.testing.assert_allclose(_layer_y(w, x2, p) - x2, base, rtol=1e-9, atol=1e-9)
+
+
+# ---------------------------------------------------------------------------
+# Stochastic Length ([GR-7.1] §7.1.5)
+# ---------------------------------------------------------------------------
+
+def test_stochastic_length_alpha_two_keeps_everything():
+    """alpha = 2 degenerates to no truncation (stated on the page)."""
+    rng = np.random.default_rng(1)
+    off = gen.make_jagged([0, 1, 300, 4096, 8192])
+    new_off, rows = oracle.stochastic_length(off, 2.0, 8192, rng.random(5), rng.random(int(off[-1])))
+    np.testing.assert_array_equal(new_off, off)
+    np.testing.assert_array_equal(rows, np.arange(int(off[-1])))
+
+
+def test_stochastic_length_bruteforce_small():
+    """Short sequences stay whole; a truncated one keeps exactly floor(N^(a/2))
+    tokens, the ones with the smallest keys, in order (brute force over all
+    subsets of a tiny sequence)."""
+    import itertools
+    N, alpha = 16, 1.5                       # N^(a/2) = 8, N^a = 64
+    lens = [3, 8, 12]
+    off = gen.make_jagged(lens)
+    keys = np.array([0.5, 0.1, 0.9] + list(np.linspace(1, 0, 8)) +
+                    [0.3, 0.8, 0.1, 0.7, 0.2, 0.95, 0.05, 0.6, 0.4, 0.85, 0.15, 0.5])
+    u = np.array([0.0, 0.0, 0.0])           # truncate whenever allowed (p > 0)
+    new_off, rows = oracle.stochastic_length(off, alpha, N, u, keys)
+    assert list(np.diff(new_off)) == [3, 8, 8]   # 3, 8 <= 8 stay; 12 > 8, p = 1 - 64/144
+    np.testing.assert_array_equal(rows[:11], np.arange(11))
+    s = int(off[2])
+    best = min(itertools.combinations(range(12), 8), key=lambda c: sum(keys[s + j] for j in c))
+    np.testing.assert_array_equal(rows[11:], s + np.array(best))
+    u_hi = np.array([0.0, 0.0, 1.0 - 64 / 144])   # u = p: not truncated (strict u < p)
+    new_off, _ = oracle.stochastic_length(off, alpha, N, u_hi, keys)
+    assert list(np.diff(new_off)) == [3, 8, 12]
+
+
+def test_stochastic_length_frequency_matches_p():
+    """Over many draws the truncation frequency of a length-n sequence is
+    p = 1 - N^a / n^2 (binomial, 6 sigma)."""
+    N, alpha, n, draws = 8192, 1.6, 4096, 20000
+    off = gen.make_jagged([n] * draws)
+    rng = np.random.default_rng(7)
+    u = rng.random(draws)
+    p = 1.0 - N ** alpha / n ** 2
+    lens = []
+    for b0 in range(0, draws, 2000):          # one call per block keeps keys small
+        sub = gen.make_jagged([n] * 2000)
+        new_off, _ = oracle.stochastic_length(sub, alpha, N, u[b0:b0 + 2000],
+                                              np.zeros(int(sub[-1])))
+        lens.extend(np.diff(new_off))
+    frac = np.mean(np.asarray(lens) < n)
+    assert abs(frac - p) < 6 * math.sqrt(p * (1 - p) / draws), (frac, p)
+    assert set(lens) <= {n, int(N ** (alpha / 2))}
