@@ -33,6 +33,27 @@ int ok() {
   return HSTU_OK;
 }
 
+}  // namespace
+
+namespace hstu {
+
+// The error channel for entry points implemented in other files.
+int api_fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+void api_ok() { g_last_error.clear(); }
+
+}  // namespace hstu
+
+namespace {
+
 int device_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(HSTU_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
@@ -292,6 +313,20 @@ int hstu_linear_bias_tables(const hstu_layer_desc* desc, float m_p, float m_t, f
                                                        desc->num_time_buckets, pos_bias, time_bias,
                                                        as_stream(stream)),
                        "linear bias tables launch");
+}
+
+int hstu_gather_rows(int64_t n, int32_t row_bytes, const int64_t* rows, int64_t src_rows,
+                     const void* src, void* dst, void* stream) {
+  CHECK(n >= 0 && src_rows >= 0, HSTU_E_INVAL, "n and src_rows must be >= 0");
+  CHECK(row_bytes > 0 && row_bytes % 8 == 0, HSTU_E_INVAL, "row_bytes must be a positive multiple of 8");
+  if (n == 0) return ok();
+  CHECK(src_rows > 0, HSTU_E_INVAL, "gathering from an empty source");
+  CHECK(rows && src && dst, HSTU_E_INVAL, "rows/src/dst must not be NULL");
+  CHECK((reinterpret_cast<uintptr_t>(src) & 7u) == 0 && (reinterpret_cast<uintptr_t>(dst) & 7u) == 0,
+        HSTU_E_INVAL, "src/dst must be 8-byte aligned");
+  CHECK(src != dst, HSTU_E_INVAL, "dst must not alias src");
+  return device_status(hstu::launch_gather_rows(n, row_bytes, rows, src_rows, src, dst, as_stream(stream)),
+                       "gather launch");
 }
 
 int hstu_kv_cache_concat(const hstu_layer_desc* desc, int32_t num_seqs, const hstu_kv_cache* a,

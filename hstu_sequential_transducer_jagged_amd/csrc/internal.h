@@ -112,6 +112,16 @@ struct LayerNormArgs {
 hipError_t launch_layernorm_bf16(const LayerNormArgs& a, hipStream_t s);
 hipError_t launch_layernorm_f32(const LayerNormArgs& a, hipStream_t s);
 
+// Error channel of the C ABI (hstu_last_error), for entry points defined
+// outside api.cpp: api_fail records a message and returns code.
+int api_fail(int code, const char* fmt, ...);
+void api_ok();
+
+// dst[r] = src[rows[r]] for r < n, row_bytes per row (a multiple of 8);
+// rows are clamped to [0, src_rows).
+hipError_t launch_gather_rows(int64_t n, int row_bytes, const int64_t* rows, int64_t src_rows,
+                              const void* src, void* dst, hipStream_t s);
+
 // Per-sequence concatenation of two K/V caches: rows of sequence b in out
 // are [a's rows of b, then n's rows of b]; out offsets = a + n offsets.
 struct CacheConcatArgs {

@@ -146,6 +146,20 @@ __global__ __launch_bounds__(256) void cache_concat_kernel(CacheConcatArgs a) {
   if (lane == 0) a.out_ts[r] = from_a ? a.a_ts[src] : a.n_ts[src];
 }
 
+// One wave per row, 8-byte accesses.
+__global__ __launch_bounds__(256) void gather_rows_kernel(int64_t n, int row_bytes, const int64_t* rows,
+                                                          int64_t src_rows, const uint8_t* src,
+                                                          uint8_t* dst) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= n) return;
+  const int64_t sr = min(max(rows[r], int64_t{0}), src_rows - 1);
+  const uint8_t* s = src + sr * row_bytes;
+  uint8_t* d = dst + r * row_bytes;
+  for (int c = lane * 8; c < row_bytes; c += 64 * 8)
+    *reinterpret_cast<uint2*>(d + c) = *reinterpret_cast<const uint2*>(s + c);
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
   const int lane = threadIdx.x & 63;
@@ -231,6 +245,15 @@ hipError_t launch_linear_bias_tables(float m_p, float m_t, int pos_len, int num_
   const int grid = (pos_len + 255) / 256;
   hipLaunchKernelGGL(linear_bias_tables_kernel, dim3(grid > 0 ? grid : 1), dim3(256), 0, s, m_p, m_t,
                      pos_len, num_buckets, pos, time);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(int64_t n, int row_bytes, const int64_t* rows, int64_t src_rows,
+                              const void* src, void* dst, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(static_cast<unsigned>((n + 3) / 4)), dim3(256), 0, s, n,
+                     row_bytes, rows, src_rows, static_cast<const uint8_t*>(src),
+                     static_cast<uint8_t*>(dst));
   return hipGetLastError();
 }
 

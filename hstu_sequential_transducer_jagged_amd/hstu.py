@@ -29,7 +29,7 @@ HSTU_BF16 = 1
 EXPORTS = ("hstu_abi_version", "hstu_last_error", "hstu_proj_fwd", "hstu_attn_workspace_size",
            "hstu_attn_fwd",
            "hstu_norm_gate_fwd", "hstu_layernorm_fwd", "hstu_linear_bias_tables",
-           "hstu_kv_cache_concat",
+           "hstu_kv_cache_concat", "hstu_stochastic_length", "hstu_gather_rows",
            "hstu_out_fwd", "hstu_layer_workspace_size",
            "hstu_layer_fwd", "hstu_embed_fwd", "hstu_check_inputs")
 
@@ -93,6 +93,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "hstu_layernorm_fwd": (ctypes.c_int, [P, i64, P, P, P, P, P]),
         "hstu_linear_bias_tables": (ctypes.c_int, [P, ctypes.c_float, ctypes.c_float, P, P, P]),
         "hstu_kv_cache_concat": (ctypes.c_int, [P, i32, P, P, P, P, P, P, P]),
+        "hstu_stochastic_length": (ctypes.c_int, [i32, P, ctypes.c_double, i64, P, P, P, P, i64, P]),
+        "hstu_gather_rows": (ctypes.c_int, [i64, i32, P, i64, P, P, P]),
         "hstu_out_fwd": (ctypes.c_int, [P, i64, P, P, P, P, P, P]),
         "hstu_layer_workspace_size": (ctypes.c_size_t, [P, P]),
         "hstu_layer_fwd": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
@@ -201,6 +203,28 @@ def hstu_kv_cache_concat(desc, num_seqs, a, n, out_offsets, out_timestamps, out_
     _check(load().hstu_kv_cache_concat(_ref(desc), int(num_seqs), _ref(a), _ref(n), ptr(out_offsets),
                                        ptr(out_timestamps), ptr(out_k), ptr(out_v),
                                        stream if stream is not None else current_stream()))
+
+
+def hstu_stochastic_length(offsets, alpha, n_max, u, keys):
+    """Host arrays in, (out_offsets, rows) numpy int64 arrays out."""
+    import numpy as np
+    off = np.ascontiguousarray(offsets, np.int64)
+    B = off.shape[0] - 1
+    T = int(off[-1]) if B >= 0 else 0
+    uu = np.ascontiguousarray(u, np.float64)
+    kk = np.ascontiguousarray(keys, np.float64)
+    out_off = np.zeros(B + 1, np.int64)
+    rows = np.zeros(max(T, 1), np.int64)
+    total = ctypes.c_int64(0)
+    addr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    _check(load().hstu_stochastic_length(B, addr(off), float(alpha), int(n_max), addr(uu), addr(kk),
+                                         addr(out_off), addr(rows), T, ctypes.byref(total)))
+    return out_off, rows[:total.value].copy()
+
+
+def hstu_gather_rows(n, row_bytes, rows, src_rows, src, dst, stream=None) -> None:
+    _check(load().hstu_gather_rows(int(n), int(row_bytes), ptr(rows), int(src_rows), ptr(src), ptr(dst),
+                                   stream if stream is not None else current_stream()))
 
 
 def hstu_out_fwd(desc, T, g, x, w2, b2, y, stream=None) -> None:

@@ -210,6 +210,31 @@ int hstu_kv_cache_concat(const hstu_layer_desc *desc, int32_t num_seqs, const hs
                          const hstu_kv_cache *n, int64_t *out_offsets, int64_t *out_timestamps,
                          void *out_k, void *out_v, void *stream);
 
+/* Stochastic Length, "HSTU：Scaling Law 的首次探索" §7.1.5 (the page prints
+ * N_{alpha/2} and N_alpha; read as powers), on the HOST (a data-loader step):
+ * a sequence of length n > N^(alpha/2), N = n_max, is with probability
+ *   p = 1 - N^alpha / n^2        (truncated iff u[b] < p, fp64)
+ * replaced by k = floor(N^(alpha/2)) of its tokens: those with the smallest
+ * keys (ties to the earlier token), kept in their original order. The page
+ * does not say how the subsequence is sampled; this is the reading taken.
+ * Otherwise the sequence is kept whole; alpha = 2 never truncates.
+ * Host arrays: offsets [num_seqs+1] (start at 0, nondecreasing), u
+ * [num_seqs] in [0, 1], keys [T] finite (T = offsets[num_seqs]); outputs
+ * out_offsets [num_seqs+1] and rows (capacity rows_capacity >= T): the
+ * source row of every kept token, sequence-major; *out_total = kept rows.
+ * alpha in (0, 2], n_max >= 1. Deterministic for given inputs. */
+int hstu_stochastic_length(int32_t num_seqs, const int64_t *offsets, double alpha, int64_t n_max,
+                           const double *u, const double *keys, int64_t *out_offsets,
+                           int64_t *rows, int64_t rows_capacity, int64_t *out_total);
+
+/* Row gather (to build the sampled batch on the device):
+ *   dst[r] = src[rows[r]]   r < n, row_bytes bytes per row
+ * rows: device int64 [n], clamped to [0, src_rows); src, dst: device,
+ * 8-byte aligned, row_bytes a positive multiple of 8; dst must not alias
+ * src. */
+int hstu_gather_rows(int64_t n, int32_t row_bytes, const int64_t *rows, int64_t src_rows,
+                     const void *src, void *dst, void *stream);
+
 /* Pointwise transformation, second half: y = x + g W2^T + b2
  * (f2 with the residual connection). g, x, y [T, d] dtype. */
 int hstu_out_fwd(const hstu_layer_desc *desc, int64_t T, const void *g, const void *x,

@@ -120,3 +120,36 @@ def test_layer_input_norm(gpu_lib, dtype, lengths, H, d):
     assert row_rel_err(_oracle_y(w), ref) > 10 * TOL[dtype]
     print(f"input norm {dtype} {lengths} H={H}: {err:.3e}")
     assert err < TOL[dtype]
+
+
+def test_stochastic_length_layer(gpu_lib):
+    """Stochastic Length ("HSTU：Scaling Law 的首次探索" §7.1.5): the host
+    sampler picks the rows, hstu_gather_rows builds the shorter batch on the
+    device (bitwise copies of X rows and timestamps), and the layer over it
+    matches the oracle layer over the same sampled batch."""
+    import torch
+    from hstu_sequential_transducer_jagged_amd import hstu, runner
+    from tests.helpers import i64
+    w = gen.make_custom([900, 40, 1500, 0, 700, 1], 256, 4, dtype="bf16", seed=31,
+                        affine="random", n_max=1500)
+    rng = np.random.default_rng(32)
+    B, T = w.num_seqs, w.total_tokens
+    off, rows = hstu.hstu_stochastic_length(w.offsets, 1.6, 1500, rng.random(B), rng.random(T))
+    assert rows.size < T                      # some sequence was cut
+    dw = runner.DeviceWorkload(w)
+    n = int(rows.size)
+    rows_d, off_d = i64(rows), i64(off)
+    xs = dw.empty_act(n)
+    ts = torch.empty(n, dtype=torch.int64, device="cuda")
+    hstu.hstu_gather_rows(n, w.d_model * 2, rows_d, T, dw.x, xs)
+    hstu.hstu_gather_rows(n, 8, rows_d, T, dw.timestamps, ts)
+    jag = hstu.Jagged(B, int(np.diff(off).max()), n, hstu.ptr(off_d), hstu.ptr(ts), None)
+    y = runner.layer_forward(dw, xs, 0, jagged=jag)
+    _sync()
+    np.testing.assert_array_equal(to_np(xs)[:n], np.asarray(w.x, np.float64)[rows])
+    np.testing.assert_array_equal(ts.cpu().numpy(), np.asarray(w.timestamps)[rows])
+    ref = oracle.layer(np.asarray(w.x)[rows], w.layers[0], off, np.asarray(w.timestamps)[rows],
+                       w.num_heads, w.n_max, w.alpha, w.ln_eps)["y"]
+    err = row_rel_err(to_np(y)[:n], ref)
+    print(f"stochastic length: {n} of {T} rows, {err:.3e}")
+    assert err < TOL["bf16"]
