@@ -58,6 +58,9 @@ def parse():
                     help="ranking workload: also time a second request per user whose first "
                          "fraction F of the history is already cached (new tokens against the "
                          "cache, hstu_kv_cache_concat, candidates)")
+    ap.add_argument("--stochastic-length", type=float, default=None, metavar="ALPHA",
+                    help="layer workloads: sample the batch with Stochastic Length (N = n_max) and "
+                         "time the layer over the sampled batch against the full one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
                     help="approximate CPU seconds for the oracle sample")
@@ -360,6 +363,69 @@ def run_stack(args):
     return rec
 
 
+def run_stochastic_length(args):
+    """Stochastic Length on a layer workload: the host sampler
+    (hstu_stochastic_length, N = n_max, seeded draws) picks the kept rows,
+    hstu_gather_rows builds the sampled batch on the device, and one layer
+    runs over it. Timed against the same layer over the full batch."""
+    import numpy as np
+    import torch
+
+    from hstu_inputs import gen
+    from hstu_sequential_transducer_jagged_amd import hstu, runner
+
+    w = gen.make_config(args.workload)
+    alpha = float(args.stochastic_length)
+    dw = runner.DeviceWorkload(w)
+    lay = dw.layers[0]
+    T, B, d = w.total_tokens, w.num_seqs, w.d_model
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    ws = dw.workspace()
+    y_full = dw.empty_act(T)
+    ms_full = timed(lambda: hstu.hstu_layer_fwd(lay.desc, lay.params, dw.jagged, None, dw.x, y_full,
+                                                None, None, ws, sh), stream, args.warmup, args.steps)
+    rng = np.random.default_rng(np.random.SeedSequence(7000 + args.workload))
+    u, keys = rng.random(B), rng.random(T)
+    t0 = time.perf_counter()
+    off, rows = hstu.hstu_stochastic_length(w.offsets, alpha, w.n_max, u, keys)
+    ms_sampler = (time.perf_counter() - t0) * 1e3
+    n = int(rows.size)
+    rows_d = torch.from_numpy(rows).to("cuda")
+    off_d = torch.from_numpy(off).to("cuda")
+    xs = dw.empty_act(n)
+    ts = torch.empty(max(n, 1), dtype=torch.int64, device="cuda")
+    lens = np.diff(off)
+    jag = hstu.Jagged(B, int(lens.max()) if B else 0, n, hstu.ptr(off_d), hstu.ptr(ts), None)
+    ws_s = dw.workspace(jag)
+    ys = dw.empty_act(n)
+
+    def gather():
+        hstu.hstu_gather_rows(n, d * (2 if w.dtype == "bf16" else 4), rows_d, T, dw.x, xs, sh)
+        hstu.hstu_gather_rows(n, 8, rows_d, T, dw.timestamps, ts, sh)
+
+    ms_gather = timed(gather, stream, args.warmup, args.steps)
+    ms_sl = timed(lambda: hstu.hstu_layer_fwd(lay.desc, lay.params, jag, None, xs, ys, None, None,
+                                              ws_s, sh), stream, args.warmup, args.steps)
+    P, Ps = visible_pairs(w.offsets), visible_pairs(off)
+    ms = ms_gather + ms_sl
+    rec = base_record(args, METRIC + " (Stochastic Length)", n / (ms * 1e-3), "tokens/s", ms, w.dtype,
+                      {"workload": gen.CONFIG_NAMES[args.workload], "total_tokens": T,
+                       "num_seqs": B, "d_model": d, "num_heads": w.num_heads,
+                       "stochastic_length_alpha": alpha, "n_max": w.n_max,
+                       "kept_tokens": n, "kept_length": int(np.floor(w.n_max ** (alpha / 2)))})
+    rec["sparsity_pairs"] = 1.0 - Ps / P
+    rec["sparsity_tokens"] = 1.0 - n / T
+    rec["full_batch_ms"] = ms_full
+    rec["sampled_layer_ms"] = ms_sl
+    rec["gather_ms"] = ms_gather
+    rec["host_sampler_ms"] = ms_sampler
+    rec["speedup_vs_full"] = ms_full / ms
+    rec["input_tokens_per_s"] = T / (ms * 1e-3)
+    rec["roofline"] = None
+    return rec
+
+
 def two_requests(args, w, dw, stream, candidates, ms_recompute):
     """Request 1 holds the first fraction F of every user's history (run
     once, untimed, its K/V cached per layer). The timed request 2 runs the
@@ -580,7 +646,12 @@ def main():
         print("--input-norm and --linear-bias apply to the single-layer workloads 0-2",
               file=sys.stderr)
         sys.exit(2)
+    if args.stochastic_length is not None and args.workload in (3, 4):
+        print("--stochastic-length applies to the single-layer workloads 0-2", file=sys.stderr)
+        sys.exit(2)
     run = {3: run_stack, 4: run_ranking}.get(args.workload, run_layer)
+    if args.stochastic_length is not None:
+        run = run_stochastic_length
     print(json.dumps(run(args)), flush=True)
 
 
