@@ -12,6 +12,7 @@ from .hstu_oracle import (  # noqa: F401
     embed,
     genrank_bias,
     layer,
+    layer_backward,
     layernorm,
     norm_gate,
     output,
@@ -19,6 +20,7 @@ from .hstu_oracle import (  # noqa: F401
     ranking,
     ranking_independent,
     silu,
+    silu_grad,
     stack,
     stochastic_length,
     time_bucket,

@@ -351,6 +351,98 @@ def layer(x, p, offsets, timestamps, num_heads: int, n_max: int, alpha: float = 
     return dict(u=u, v=vv, q=qq, k=kk, av=av, g=g, y=y, proj_rows=prow, rows=orow)
 
 
+def silu_grad(z):
+    """d SiLU / dz = s (1 + z (1 - s)), s = sigmoid(z)."""
+    z = np.asarray(z, dtype=F64)
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-z))
+    return s * (1.0 + z * (1.0 - s))
+
+
+def layer_backward(x, p, offsets, timestamps, dy, num_heads: int, n_max: int,
+                   alpha: float = 1.0, eps: float = 1e-5) -> Dict[str, np.ndarray]:
+    """Gradients of <Y, dY> for one layer with plain causal attention (no
+    targets, no cache), the generative-training setting of [GR-7.1] §7.1.5:
+    dX, dW1, db1, dW2, db2, dgamma, dbeta and the gradients of the position
+    and time tables (the shared rab: every pair adds its score gradient,
+    summed over heads, to the entry it read). The chain rule applied to the
+    forward of layer() step by step, in float64."""
+    x = np.asarray(x, F64)
+    dy = np.asarray(dy, F64)
+    offsets = np.asarray(offsets, np.int64)
+    timestamps = np.asarray(timestamps, np.int64)
+    T, d = x.shape
+    dh = d // num_heads
+    w1, w2 = np.asarray(p.w1, F64), np.asarray(p.w2, F64)
+    gamma = np.ones(d) if p.gamma is None else np.asarray(p.gamma, F64)
+    beta = np.zeros(d) if p.beta is None else np.asarray(p.beta, F64)
+    pb, tb = np.asarray(p.pos_bias, F64), np.asarray(p.time_bias, F64)
+    nb = tb.shape[0]
+    # forward, keeping what the backward needs
+    z = x @ w1.T + (0.0 if p.b1 is None else np.asarray(p.b1, F64))
+    h = silu(z)
+    u, v, q, k = h[:, :d], h[:, d:2 * d], h[:, 2 * d:3 * d], h[:, 3 * d:]
+    av = np.zeros((T, d))
+    dq, dk, dv = np.zeros((T, d)), np.zeros((T, d)), np.zeros((T, d))
+    dpos, dtime = np.zeros_like(pb), np.zeros_like(tb)
+    seqs = []
+    for b in range(offsets.shape[0] - 1):
+        s, e = int(offsets[b]), int(offsets[b + 1])
+        if e == s:
+            continue
+        L = e - s
+        i = np.arange(L)
+        dp = i[:, None] - i[None, :]
+        dt = timestamps[s:e][:, None] - timestamps[s:e][None, :]
+        idx = np.clip(dp + (n_max - 1), 0, pb.shape[0] - 1)
+        bkt = time_bucket(dt, nb)
+        rab = pb[idx] + tb[bkt]
+        mask = dp >= 0
+        seqs.append((s, e, idx, bkt, rab, mask))
+        for hh in range(num_heads):
+            c = slice(hh * dh, (hh + 1) * dh)
+            sc = alpha * (q[s:e, c] @ k[s:e, c].T) + rab
+            av[s:e, c] = np.where(mask, silu(sc), 0.0) @ v[s:e, c]
+    mu = av.mean(axis=1, keepdims=True)
+    var = ((av - mu) ** 2).mean(axis=1, keepdims=True)
+    rstd = 1.0 / np.sqrt(var + eps)
+    nhat = (av - mu) * rstd
+    nrm = nhat * gamma + beta
+    g = nrm * u
+    # Y = X + G W2^T + b2
+    dg = dy @ w2
+    dw2 = dy.T @ g
+    db2 = dy.sum(axis=0)
+    # G = (nhat gamma + beta) * U
+    du = dg * nrm
+    dnrm = dg * u
+    dgamma = (dnrm * nhat).sum(axis=0)
+    dbeta = dnrm.sum(axis=0)
+    dnh = dnrm * gamma
+    dav = rstd * (dnh - dnh.mean(axis=1, keepdims=True)
+                  - nhat * (dnh * nhat).mean(axis=1, keepdims=True))
+    # AV_h = (SiLU(S_h) * Mask) V_h, S_h = alpha Q_h K_h^T + rab
+    for (s, e, idx, bkt, rab, mask) in seqs:
+        for hh in range(num_heads):
+            c = slice(hh * dh, (hh + 1) * dh)
+            sc = alpha * (q[s:e, c] @ k[s:e, c].T) + rab
+            pm = np.where(mask, silu(sc), 0.0)
+            dv[s:e, c] += pm.T @ dav[s:e, c]
+            dpm = dav[s:e, c] @ v[s:e, c].T
+            ds = np.where(mask, dpm * silu_grad(sc), 0.0)
+            dq[s:e, c] += alpha * (ds @ k[s:e, c])
+            dk[s:e, c] += alpha * (ds.T @ q[s:e, c])
+            np.add.at(dpos, idx[mask], ds[mask])
+            np.add.at(dtime, bkt[mask], ds[mask])
+    # U, V, Q, K = Split(SiLU(Z)), Z = X W1^T + b1
+    dz = np.concatenate([du, dv, dq, dk], axis=1) * silu_grad(z)
+    dw1 = dz.T @ x
+    db1 = dz.sum(axis=0)
+    dx = dy + dz @ w1
+    return dict(dx=dx, dw1=dw1, db1=db1, dw2=dw2, db2=db2, dgamma=dgamma, dbeta=dbeta,
+                dpos=dpos, dtime=dtime)
+
+
 def stack(x, layers: Sequence, offsets, timestamps, num_heads: int, n_max: int,
           alpha: float = 1.0, eps: float = 1e-5, return_all: bool = False):
     """L stacked layers: layer l's output is layer l+1's input ([GR-7.1]

@@ -717,3 +717,81 @@ def test_stochastic_length_frequency_matches_p():
     frac = np.mean(np.asarray(lens) < n)
     assert abs(frac - p) < 6 * math.sqrt(p * (1 - p) / draws), (frac, p)
     assert set(lens) <= {n, int(N ** (alpha / 2))}
+
+
+# ---------------------------------------------------------------------------
+# layer backward (generative training, plain causal attention)
+# ---------------------------------------------------------------------------
+
+def test_silu_grad_closed_form_and_difference():
+    z = np.linspace(-30, 30, 241)
+    h = 1e-6
+    num = (oracle.silu(z + h) - oracle.silu(z - h)) / (2 * h)
+    np.testing.assert_allclose(oracle.silu_grad(z), num, rtol=1e-6, atol=1e-9)
+    assert oracle.silu_grad(np.array([0.0]))[0] == 0.5          # sigma(0) = 1/2
+    np.testing.assert_allclose(oracle.silu_grad(np.array([60.0])), [1.0], atol=1e-20)
+
+
+def _bwd_case(seed):
+    w = _tiny([5, 1, 7, 0, 3], d=8, H=2, seed=seed, affine="random", n_max=7)
+    w.alpha = 0.7
+    rng = np.random.default_rng(seed + 1000)
+    dy = rng.standard_normal((w.total_tokens, 8))
+    return w, dy
+
+
+def _f(w, x, p, dy):
+    y = oracle.layer(x, p, w.offsets, w.timestamps, w.num_heads, w.n_max, w.alpha, w.ln_eps)["y"]
+    return float((y * dy).sum())
+
+
+@pytest.mark.parametrize("name", ["x", "w1", "b1", "w2", "b2", "gamma", "beta", "pos_bias",
+                                  "time_bias"])
+def test_layer_backward_matches_central_differences(name):
+    """<grad, v> equals the central difference of <Y, dY> along a random v,
+    for every input and parameter: the forward oracle checks the backward."""
+    import copy
+    w, dy = _bwd_case(3)
+    p = w.layers[0]
+    x = np.asarray(w.x, np.float64)
+    g = oracle.layer_backward(x, p, w.offsets, w.timestamps, dy, w.num_heads, w.n_max, w.alpha,
+                              w.ln_eps)
+    key = {"x": "dx", "w1": "dw1", "b1": "db1", "w2": "dw2", "b2": "db2", "gamma": "dgamma",
+           "beta": "dbeta", "pos_bias": "dpos", "time_bias": "dtime"}[name]
+    base = x if name == "x" else np.asarray(getattr(p, name), np.float64)
+    v = np.random.default_rng(99).standard_normal(base.shape)
+    eps = 1e-5
+
+    def at(t):
+        pp = copy.copy(p)
+        xx = x
+        if name == "x":
+            xx = x + t * v
+        else:
+            setattr(pp, name, base + t * v)
+        return _f(w, xx, pp, dy)
+
+    num = (at(eps) - at(-eps)) / (2 * eps)
+    ana = float((g[key] * v).sum())
+    assert abs(num - ana) <= 1e-6 * max(1.0, abs(ana)), (name, num, ana)
+
+
+def test_layer_backward_linear_in_dy_and_residual():
+    """Gradients are linear in dY; with W2 = 0 the only path to X is the
+    residual, so dX = dY and W1, b1, gamma, beta and the tables get nothing."""
+    w, dy = _bwd_case(4)
+    p = w.layers[0]
+    x = np.asarray(w.x, np.float64)
+    args = (w.offsets, w.timestamps)
+    kw = dict(num_heads=w.num_heads, n_max=w.n_max, alpha=w.alpha, eps=w.ln_eps)
+    g1 = oracle.layer_backward(x, p, *args, dy, **kw)
+    g2 = oracle.layer_backward(x, p, *args, -2.5 * dy, **kw)
+    for kk in g1:
+        np.testing.assert_allclose(g2[kk], -2.5 * g1[kk], rtol=1e-12, atol=1e-12)
+    import copy
+    p0 = copy.copy(p)
+    p0.w2 = np.zeros_like(p.w2)
+    g0 = oracle.layer_backward(x, p0, *args, dy, **kw)
+    np.testing.assert_array_equal(g0["dx"], dy)
+    for kk in ("dw1", "db1", "dgamma", "dbeta", "dpos", "dtime"):
+        assert np.all(g0[kk] == 0), kk
