@@ -4,6 +4,7 @@
 // on host scalars before anything is enqueued; no entry point allocates.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -454,6 +455,127 @@ int hstu_layer_fwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
   }
   if (st) return st;
   return do_out(desc, T, u, x, params->w2, params->b2, y, s);
+}
+
+size_t hstu_layer_bwd_workspace_size(const hstu_layer_desc* desc, const hstu_jagged* jagged) {
+  if (!desc || !jagged || jagged->total_tokens < 0 || desc->d_model <= 0) return 0;
+  const size_t T = static_cast<size_t>(jagged->total_tokens);
+  const size_t td = round256(T * desc->d_model * sizeof(float));
+  return 17 * td + round256(T * sizeof(float));
+}
+
+int hstu_layer_bwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
+                   const hstu_jagged* jagged, const void* x, const void* dy, void* dx,
+                   const hstu_layer_grads* grads, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  CHECK(desc->dtype == HSTU_F32, HSTU_E_UNSUPPORTED, "the backward pass supports dtype f32");
+  CHECK(desc->input_norm == 0, HSTU_E_UNSUPPORTED, "the backward pass does not support input_norm");
+  st = check_jagged(desc, jagged, nullptr);
+  if (st) return st;
+  CHECK(jagged->num_targets == nullptr, HSTU_E_UNSUPPORTED,
+        "the backward pass supports plain causal attention (no targets)");
+  CHECK(params && params->w1 && params->w2 && params->pos_bias && params->time_bias, HSTU_E_INVAL,
+        "params, w1, w2, pos_bias and time_bias must not be NULL");
+  CHECK(grads && grads->dw1 && grads->db1 && grads->dw2 && grads->db2 && grads->dgamma &&
+            grads->dbeta && grads->dpos && grads->dtime,
+        HSTU_E_INVAL, "every gradient pointer must be set");
+  const int64_t T = jagged->total_tokens;
+  const int d = desc->d_model;
+  const bool empty = T == 0 || jagged->num_seqs == 0;
+  if (!empty) {
+    CHECK(x && dy && dx, HSTU_E_INVAL, "x/dy/dx must not be NULL");
+    CHECK(dx != x && dx != dy, HSTU_E_INVAL, "dx must not alias x or dy");
+    CHECK(aligned16(x) && aligned16(dy) && aligned16(dx), HSTU_E_INVAL,
+          "x/dy/dx must be 16-byte aligned");
+    const size_t need = hstu_layer_bwd_workspace_size(desc, jagged);
+    CHECK(workspace != nullptr && workspace_bytes >= need, HSTU_E_WORKSPACE,
+          "workspace too small: need %zu bytes, got %zu", need, workspace_bytes);
+    CHECK((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, HSTU_E_INVAL,
+          "workspace must be 256-byte aligned");
+  }
+  hipStream_t s = as_stream(stream);
+  // gradients start at zero (also for an empty batch)
+  const struct { float* p; int64_t n; } zero[] = {
+      {grads->dw1, 4LL * d * d}, {grads->db1, 4LL * d}, {grads->dw2, 1LL * d * d}, {grads->db2, d},
+      {grads->dgamma, d}, {grads->dbeta, d}, {grads->dpos, desc->pos_table_len},
+      {grads->dtime, desc->num_time_buckets}};
+  for (const auto& z : zero) {
+    st = device_status(hstu::launch_fill_zero(z.p, z.n, s), "zero fill");
+    if (st) return st;
+  }
+  if (empty) return ok();
+  const size_t td = round256(static_cast<size_t>(T) * d * sizeof(float));
+  char* w = static_cast<char*>(workspace);
+  float* Z = reinterpret_cast<float*>(w);             // [T, 4d] pre-activation
+  float* U = reinterpret_cast<float*>(w + 4 * td);
+  float* V = reinterpret_cast<float*>(w + 5 * td);
+  float* Q = reinterpret_cast<float*>(w + 6 * td);
+  float* K = reinterpret_cast<float*>(w + 7 * td);
+  float* AV = reinterpret_cast<float*>(w + 8 * td);
+  float* NH = reinterpret_cast<float*>(w + 9 * td);
+  float* G = reinterpret_cast<float*>(w + 10 * td);
+  float* DG = reinterpret_cast<float*>(w + 11 * td);
+  float* DZ = reinterpret_cast<float*>(w + 12 * td);   // [T, 4d]: dU, dV, dQ, dK
+  float* DAV = reinterpret_cast<float*>(w + 16 * td);
+  float* RSTD = reinterpret_cast<float*>(w + 17 * td);
+  const float* X = static_cast<const float*>(x);
+  const float* DY = static_cast<const float*>(dy);
+  const float* W1 = static_cast<const float*>(params->w1);
+  const float* W2 = static_cast<const float*>(params->w2);
+  const int d4 = 4 * d;
+  // weight gradients reduce over T: split it so that the grid has ~2048 blocks
+  auto splits = [&](int M, int N) {
+    const int64_t tiles = static_cast<int64_t>((M + 63) / 64) * ((N + 63) / 64);
+    const int64_t sp = (2048 + tiles - 1) / tiles;
+    const int64_t cap = (T + 255) / 256;
+    return static_cast<int>(std::max<int64_t>(1, std::min(sp, cap)));
+  };
+#define HSTU_TRY(expr, what)                       \
+  do {                                             \
+    st = device_status((expr), what);              \
+    if (st) return st;                             \
+  } while (0)
+  // forward recompute
+  st = do_proj(desc, params, T, x, U, V, Q, K, s);
+  if (st) return st;
+  HSTU_TRY(hstu::launch_gemm_f32s(X, d, 1, W1, 1, d, Z, d4, nullptr, params->b1, static_cast<int>(T), d4, d,
+                                  1, s), "z gemm");
+  st = do_attn(desc, jagged, nullptr, Q, K, V, params->pos_bias, params->time_bias, AV, nullptr, s);
+  if (st) return st;
+  HSTU_TRY(hstu::launch_ln_gate_fwd(AV, U, params->ln_gamma, params->ln_beta, NH, RSTD, G, T, d,
+                                    desc->ln_eps, s), "ln/gate forward");
+  // Y = X + G W2^T + b2
+  HSTU_TRY(hstu::launch_gemm_f32s(DY, d, 1, W2, d, 1, DG, d, nullptr, nullptr, static_cast<int>(T), d, d, 1,
+                                  s), "dG gemm");
+  HSTU_TRY(hstu::launch_gemm_f32s(DY, 1, d, G, d, 1, grads->dw2, d, nullptr, nullptr, d, d, T,
+                                  splits(d, d), s), "dW2 gemm");
+  HSTU_TRY(hstu::launch_colsum(DY, d, T, d, grads->db2, s), "db2");
+  // G = (N^ gamma + beta) . U
+  HSTU_TRY(hstu::launch_ln_gate_bwd(DG, U, NH, RSTD, params->ln_gamma, params->ln_beta, DZ, d4, DAV,
+                                    grads->dgamma, grads->dbeta, T, d, s), "ln/gate backward");
+  // AV = (SiLU(a Q K^T + rab) . M) V, per head
+  hstu::BwdAttnArgs ba{};
+  ba.q = Q; ba.k = K; ba.v = V; ba.dav = DAV;
+  ba.offsets = jagged->offsets; ba.ts = jagged->timestamps;
+  ba.pos_bias = params->pos_bias; ba.time_bias = params->time_bias;
+  ba.dv = DZ + d; ba.dq = DZ + 2 * d; ba.dk = DZ + 3 * d; ba.ld_dz = d4;
+  ba.dpos = grads->dpos; ba.dtime = grads->dtime;
+  ba.d_model = d; ba.num_heads = desc->num_heads; ba.head_dim = desc->head_dim;
+  ba.pos_len = desc->pos_table_len; ba.pos_center = (desc->pos_table_len - 1) / 2;
+  ba.nb = desc->num_time_buckets; ba.alpha = desc->alpha;
+  ba.num_seqs = jagged->num_seqs; ba.max_seq_len = jagged->max_seq_len;
+  HSTU_TRY(hstu::launch_attn_bwd_f32(ba, s), "attention backward");
+  // [U V Q K] = SiLU(X W1^T + b1)
+  HSTU_TRY(hstu::launch_silu_bwd(DZ, Z, T * d4, s), "silu backward");
+  HSTU_TRY(hstu::launch_colsum(DZ, d4, T, d4, grads->db1, s), "db1");
+  HSTU_TRY(hstu::launch_gemm_f32s(DZ, 1, d4, X, d, 1, grads->dw1, d, nullptr, nullptr, d4, d, T,
+                                  splits(d4, d), s), "dW1 gemm");
+  HSTU_TRY(hstu::launch_gemm_f32s(DZ, d4, 1, W1, d, 1, static_cast<float*>(dx), d, DY, nullptr,
+                                  static_cast<int>(T), d, d4, 1, s), "dX gemm");
+#undef HSTU_TRY
+  return ok();
 }
 
 int hstu_embed_fwd(int64_t T, int32_t d_model, int32_t dtype, const void* item_emb,

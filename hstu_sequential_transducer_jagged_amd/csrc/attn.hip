@@ -61,13 +61,6 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ int time_bucket64(int64_t dt, int nb) {
-  uint64_t a = dt < 0 ? (0ull - static_cast<uint64_t>(dt)) : static_cast<uint64_t>(dt);
-  a += 1ull;
-  const int b = 63 - __clzll(static_cast<long long>(a));
-  return b < nb - 1 ? b : nb - 1;
-}
-
 struct SeqInfo {
   int64_t s;     // first own token row
   int L;         // own length

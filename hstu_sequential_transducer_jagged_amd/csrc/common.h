@@ -34,6 +34,14 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(const bf16x8& a, const bf16x8& b,
 }
 
 // Sum over the 64 lanes of a wave (butterfly; every lane gets the sum).
+// min(nb - 1, floor(log2(|dt| + 1))) in integers (the rab time bucket).
+__device__ __forceinline__ int time_bucket64(int64_t dt, int nb) {
+  uint64_t a = dt < 0 ? (0ull - static_cast<uint64_t>(dt)) : static_cast<uint64_t>(dt);
+  a += 1ull;
+  const int b = 63 - __clzll(static_cast<long long>(a));
+  return b < nb - 1 ? b : nb - 1;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);

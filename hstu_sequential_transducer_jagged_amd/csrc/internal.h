@@ -112,6 +112,43 @@ struct LayerNormArgs {
 hipError_t launch_layernorm_bf16(const LayerNormArgs& a, hipStream_t s);
 hipError_t launch_layernorm_f32(const LayerNormArgs& a, hipStream_t s);
 
+// ---- backward (fp32, plain causal attention) ----
+struct BwdAttnArgs {
+  const float* q;            // [T, d] (row stride d)
+  const float* k;
+  const float* v;
+  const float* dav;          // [T, d] gradient of AV
+  const int64_t* offsets;    // [B+1]
+  const int64_t* ts;         // [T]
+  const float* pos_bias;
+  const float* time_bias;
+  float* dq;                 // [T, ld_dz] blocks of dZ
+  float* dk;
+  float* dv;
+  float* dpos;               // [pos_len], accumulated
+  float* dtime;              // [nb], accumulated
+  int ld_dz;
+  int d_model, num_heads, head_dim, pos_len, pos_center, nb;
+  float alpha;
+  int num_seqs, max_seq_len;
+};
+hipError_t launch_attn_bwd_f32(const BwdAttnArgs& a, hipStream_t s);
+// C[m, n] = sum_k A[m sam + k sak] B[k sbk + n sbn] (+ bias[n] + addend[m, n]);
+// splits > 1: K split over blocks whose sums are added atomically into C
+// (zeroed beforehand, no bias or addend).
+hipError_t launch_gemm_f32s(const float* A, int64_t sam, int64_t sak, const float* B, int64_t sbk,
+                            int64_t sbn, float* C, int64_t ldc, const float* addend, const float* bias,
+                            int M, int N, int64_t K, int splits, hipStream_t s);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+hipError_t launch_colsum(const float* X, int64_t ldx, int64_t M, int N, float* out, hipStream_t s);
+hipError_t launch_ln_gate_fwd(const float* av, const float* u, const float* gamma, const float* beta,
+                              float* nhat, float* rstd, float* g, int64_t M, int d, float eps,
+                              hipStream_t s);
+hipError_t launch_ln_gate_bwd(const float* dg, const float* u, const float* nhat, const float* rstd,
+                              const float* gamma, const float* beta, float* du, int64_t ldu, float* dav,
+                              float* dgamma, float* dbeta, int64_t M, int d, hipStream_t s);
+hipError_t launch_silu_bwd(float* dz, const float* z, int64_t n, hipStream_t s);
+
 // Error channel of the C ABI (hstu_last_error), for entry points defined
 // outside api.cpp: api_fail records a message and returns code.
 int api_fail(int code, const char* fmt, ...);

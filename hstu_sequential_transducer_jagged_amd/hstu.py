@@ -31,7 +31,8 @@ EXPORTS = ("hstu_abi_version", "hstu_last_error", "hstu_proj_fwd", "hstu_attn_wo
            "hstu_norm_gate_fwd", "hstu_layernorm_fwd", "hstu_linear_bias_tables",
            "hstu_kv_cache_concat", "hstu_stochastic_length", "hstu_gather_rows",
            "hstu_out_fwd", "hstu_layer_workspace_size",
-           "hstu_layer_fwd", "hstu_embed_fwd", "hstu_check_inputs")
+           "hstu_layer_fwd", "hstu_layer_bwd_workspace_size", "hstu_layer_bwd",
+           "hstu_embed_fwd", "hstu_check_inputs")
 
 
 class HstuError(RuntimeError):
@@ -68,6 +69,12 @@ class LayerParams(ctypes.Structure):
                 ("ln1_beta", ctypes.c_void_p)]
 
 
+class LayerGrads(ctypes.Structure):
+    _fields_ = [("dw1", ctypes.c_void_p), ("db1", ctypes.c_void_p), ("dw2", ctypes.c_void_p),
+                ("db2", ctypes.c_void_p), ("dgamma", ctypes.c_void_p), ("dbeta", ctypes.c_void_p),
+                ("dpos", ctypes.c_void_p), ("dtime", ctypes.c_void_p)]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -98,6 +105,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "hstu_out_fwd": (ctypes.c_int, [P, i64, P, P, P, P, P, P]),
         "hstu_layer_workspace_size": (ctypes.c_size_t, [P, P]),
         "hstu_layer_fwd": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "hstu_layer_bwd_workspace_size": (ctypes.c_size_t, [P, P]),
+        "hstu_layer_bwd": (ctypes.c_int, [P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "hstu_embed_fwd": (ctypes.c_int, [i64, i32, i32, P, i64, P, i32, P, P, P, P]),
         "hstu_check_inputs": (ctypes.c_int, [P, P, P, P]),
     }
@@ -247,6 +256,22 @@ def hstu_layer_fwd(desc, params, jagged, cache, x, y, k_out, v_out, workspace,
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().hstu_layer_fwd(_ref(desc), _ref(params), _ref(jagged), _ref(cache), ptr(x),
                                  ptr(y), ptr(k_out), ptr(v_out), ptr(workspace), nbytes,
+                                 stream if stream is not None else current_stream()))
+
+
+def make_grads(dw1, db1, dw2, db2, dgamma, dbeta, dpos, dtime) -> LayerGrads:
+    return LayerGrads(ptr(dw1), ptr(db1), ptr(dw2), ptr(db2), ptr(dgamma), ptr(dbeta), ptr(dpos),
+                      ptr(dtime))
+
+
+def hstu_layer_bwd_workspace_size(desc, jagged) -> int:
+    return load().hstu_layer_bwd_workspace_size(_ref(desc), _ref(jagged))
+
+
+def hstu_layer_bwd(desc, params, jagged, x, dy, dx, grads, workspace, stream=None) -> None:
+    _check(load().hstu_layer_bwd(_ref(desc), _ref(params), _ref(jagged), ptr(x), ptr(dy), ptr(dx),
+                                 _ref(grads), ptr(workspace),
+                                 0 if workspace is None else workspace.numel() * workspace.element_size(),
                                  stream if stream is not None else current_stream()))
 
 

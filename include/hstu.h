@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 3
+#define HSTU_ABI_VERSION 4
 
 typedef enum {
   HSTU_OK = 0,
@@ -121,6 +121,18 @@ typedef struct {
   const float *ln1_gamma;       /* [d] or NULL (ones): input LayerNorm, read if input_norm */
   const float *ln1_beta;        /* [d] or NULL (zeros) */
 } hstu_layer_params;
+
+/* Gradients of one layer (hstu_layer_bwd): device fp32 buffers, overwritten. */
+typedef struct {
+  float *dw1;     /* [4d, d] */
+  float *db1;     /* [4d] */
+  float *dw2;     /* [d, d] */
+  float *db2;     /* [d] */
+  float *dgamma;  /* [d] */
+  float *dbeta;   /* [d] */
+  float *dpos;    /* [pos_table_len] */
+  float *dtime;   /* [num_time_buckets] */
+} hstu_layer_grads;
 
 /* ABI version of the loaded library (HSTU_ABI_VERSION). */
 int hstu_abi_version(void);
@@ -254,6 +266,27 @@ int hstu_layer_fwd(const hstu_layer_desc *desc, const hstu_layer_params *params,
                    const hstu_jagged *jagged, const hstu_kv_cache *cache, const void *x,
                    void *y, void *k_out, void *v_out, void *workspace,
                    size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of hstu_layer_bwd: 17 [T, d] fp32 buffers plus T floats
+ * (each rounded up to 256 bytes). */
+size_t hstu_layer_bwd_workspace_size(const hstu_layer_desc *desc, const hstu_jagged *jagged);
+
+/* Backward pass of one layer for generative training ("HSTU：Scaling Law 的
+ * 首次探索" §7.1.5: a causal forward over whole sequences), through the three
+ * equations of "万亿参数推荐大模型…" §2.1 and the residual: given dy =
+ * dL/dY, writes dx = dL/dX and every parameter gradient, including those of
+ * the position and time tables (each visible pair adds its score gradient,
+ * summed over heads, to the entries it read). Recomputes the forward.
+ * Supported: dtype HSTU_F32, input_norm 0, plain causal attention
+ * (jagged->num_targets NULL, no cache); else HSTU_E_UNSUPPORTED.
+ * x, dy, dx [T, d] fp32 (dx must not alias x or dy); grads: all eight
+ * pointers non-NULL. workspace: device, 256-byte aligned, >=
+ * hstu_layer_bwd_workspace_size(). Gradient sums use fp32 atomics, so
+ * their last bits may vary from run to run. */
+int hstu_layer_bwd(const hstu_layer_desc *desc, const hstu_layer_params *params,
+                   const hstu_jagged *jagged, const void *x, const void *dy, void *dx,
+                   const hstu_layer_grads *grads, void *workspace, size_t workspace_bytes,
+                   void *stream);
 
 /* Action-oriented token embedding, "6.2. HSTU的工程突破" eq. 6.2.2:
  *   x[t] = item_emb[item_ids[t]] + action_emb[actions[t]]

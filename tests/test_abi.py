@@ -35,7 +35,7 @@ def test_header_declares_the_binding_exports():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.hstu_abi_version() == 3
+    assert lib.hstu_abi_version() == 4
 
 
 def _desc(**kw):
@@ -183,6 +183,32 @@ def test_cache_concat_validates(lib):
     assert cc(2, a, n, out[0], out[1], out[2] + 8, out[3]) == hstu.HSTU_E_INVAL   # misaligned
     bad = hstu.KVCache(FAKE, FAKE, FAKE, FAKE, 8, -1)
     assert cc(2, bad, n, *out) == hstu.HSTU_E_INVAL
+
+
+def test_backward_validates(lib):
+    """hstu_layer_bwd supports fp32 plain causal layers; everything else is
+    refused on the host, before any launch."""
+    P = ctypes.c_void_p
+    f = hstu.make_desc(64, 2, hstu.HSTU_F32, 255)
+    params = hstu.LayerParams(FAKE, None, FAKE, None, None, None, FAKE, FAKE)
+    grads = hstu.LayerGrads(*([FAKE] * 8))
+    jag = _jag()
+    ws = lib.hstu_layer_bwd_workspace_size(ctypes.byref(f), ctypes.byref(jag))
+    assert ws == 17 * 2560 + 256
+    call = lambda desc, j=jag, g=grads, p=params, dx=FAKE + 4096, wsb=ws: lib.hstu_layer_bwd(
+        ctypes.byref(desc), ctypes.byref(p) if p else None, ctypes.byref(j),
+        P(FAKE), P(FAKE + 8192), P(dx), ctypes.byref(g) if g else None, P(FAKE), wsb, None)
+    assert call(_desc()) == hstu.HSTU_E_UNSUPPORTED                 # bf16
+    n1 = hstu.make_desc(64, 2, hstu.HSTU_F32, 255, input_norm=True)
+    assert call(n1) == hstu.HSTU_E_UNSUPPORTED
+    tj = hstu.Jagged(2, 6, 10, FAKE, FAKE, FAKE)                     # targets
+    assert call(f, j=tj) == hstu.HSTU_E_UNSUPPORTED
+    assert call(f, g=None) == hstu.HSTU_E_INVAL
+    half = hstu.LayerGrads(*([FAKE] * 7 + [None]))
+    assert call(f, g=half) == hstu.HSTU_E_INVAL
+    assert call(f, p=None) == hstu.HSTU_E_INVAL
+    assert call(f, dx=FAKE) == hstu.HSTU_E_INVAL                     # dx aliases x
+    assert call(f, wsb=ws - 1) == hstu.HSTU_E_WORKSPACE
 
 
 def test_binding_raises_with_message(lib):
