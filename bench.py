@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--stochastic-length", type=float, default=None, metavar="ALPHA",
                     help="layer workloads: sample the batch with Stochastic Length (N = n_max) and "
                          "time the layer over the sampled batch against the full one")
+    ap.add_argument("--backward", action="store_true",
+                    help="layer workloads: time the fp32 layer backward pass (hstu_layer_bwd) on the "
+                         "workload's shape in fp32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
                     help="approximate CPU seconds for the oracle sample")
@@ -363,6 +366,55 @@ def run_stack(args):
     return rec
 
 
+def run_backward(args):
+    """The layer backward pass (hstu_layer_bwd: forward recompute, then every
+    gradient) on a single-layer workload's shape, in fp32 (the backward's
+    dtype), against the fp32 forward of the same layer."""
+    import numpy as np
+    import torch
+
+    from hstu_inputs import gen
+    from hstu_sequential_transducer_jagged_amd import hstu, runner
+
+    w = gen.make_config(args.workload)
+    w.dtype = "f32"                      # bf16-valued inputs, held and computed in fp32
+    dw = runner.DeviceWorkload(w)
+    lay = dw.layers[0]
+    T, d = w.total_tokens, w.d_model
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    rng = np.random.default_rng(np.random.SeedSequence(8000 + args.workload))
+    dy = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to("cuda")
+    dx = torch.empty_like(dy)
+    g = [torch.empty(n, dtype=torch.float32, device="cuda") for n in
+         (4 * d * d, 4 * d, d * d, d, d, d, 2 * w.n_max - 1, w.num_time_buckets)]
+    grads = hstu.make_grads(*g)
+    ws = hstu.workspace_tensor(hstu.hstu_layer_bwd_workspace_size(lay.desc, dw.jagged))
+    ms = timed(lambda: hstu.hstu_layer_bwd(lay.desc, lay.params, dw.jagged, dw.x, dy, dx, grads, ws, sh),
+               stream, args.warmup, args.steps)
+    wsf = dw.workspace()
+    y = dw.empty_act(T)
+    ms_fwd = timed(lambda: hstu.hstu_layer_fwd(lay.desc, lay.params, dw.jagged, None, dw.x, y, None, None,
+                                               wsf, sh), stream, args.warmup, args.steps)
+    P = visible_pairs(w.offsets)
+    # algorithmic FLOPs: forward recompute (proj 8Td^2 + Z 8Td^2 + attention 4dP) and backward
+    # (dG, dW2 2Td^2 each; dW1, dX 8Td^2 each; attention 14dP: dQ 6dP, dK/dV 8dP)
+    flop = 16.0 * T * d * d + 4.0 * d * P + 20.0 * T * d * d + 14.0 * d * P
+    rec = base_record(args, "HSTU layer backward tokens/s (fp32, forward recompute included), 1 GPU",
+                      T / (ms * 1e-3), "tokens/s", ms, "f32",
+                      {"workload": gen.CONFIG_NAMES[args.workload] + ", held in fp32", "total_tokens": T,
+                       "num_seqs": w.num_seqs, "d_model": d, "num_heads": w.num_heads,
+                       "visible_pairs": P})
+    rec["forward_fp32_ms"] = ms_fwd
+    rec["backward_over_forward"] = ms / ms_fwd
+    rec["algorithmic_flop"] = flop
+    rec["roofline"] = {"kernel": "layer backward (all kernels)", "bound": "alu",
+                       "achieved": flop / (ms * 1e-3) / 1e12, "peak": PEAK_F32_TFLOPS,
+                       "unit": "TFLOP/s", "frac": flop / (ms * 1e-3) / 1e12 / PEAK_F32_TFLOPS,
+                       "traffic": None}
+    return rec
+
+
 def run_stochastic_length(args):
     """Stochastic Length on a layer workload: the host sampler
     (hstu_stochastic_length, N = n_max, seeded draws) picks the kept rows,
@@ -652,6 +704,11 @@ def main():
     run = {3: run_stack, 4: run_ranking}.get(args.workload, run_layer)
     if args.stochastic_length is not None:
         run = run_stochastic_length
+    if args.backward:
+        if args.workload in (3, 4):
+            print("--backward applies to the single-layer workloads 0-2", file=sys.stderr)
+            sys.exit(2)
+        run = run_backward
     print(json.dumps(run(args)), flush=True)
 
 
