@@ -178,9 +178,30 @@ int do_proj(const hstu_layer_desc* d, const hstu_layer_params* p, int64_t T, con
                        "proj launch");
 }
 
+hstu::BwdAttnArgs make_train_args(const hstu_layer_desc* d, const hstu_jagged* j, const float* q,
+                                  const float* k, const float* v, const float* pb, const float* tb) {
+  hstu::BwdAttnArgs a{};
+  a.q = q; a.k = k; a.v = v;
+  a.offsets = j->offsets; a.ts = j->timestamps;
+  a.pos_bias = pb; a.time_bias = tb;
+  a.d_model = d->d_model; a.num_heads = d->num_heads; a.head_dim = d->head_dim;
+  a.pos_len = d->pos_table_len; a.pos_center = (d->pos_table_len - 1) / 2;
+  a.nb = d->num_time_buckets; a.alpha = d->alpha;
+  a.num_seqs = j->num_seqs; a.max_seq_len = j->max_seq_len;
+  return a;
+}
+
 int do_attn(const hstu_layer_desc* d, const hstu_jagged* j, const hstu_kv_cache* c, const void* q,
             const void* k, const void* v, const float* pb, const float* tb, float* av, void* ws,
             hipStream_t s) {
+  if (d->dtype == HSTU_F32 && c == nullptr && j->num_targets == nullptr &&
+      hstu::attn_train_supported(d->head_dim)) {
+    // plain causal fp32: the matrix-core kernel
+    hstu::BwdAttnArgs ta = make_train_args(d, j, static_cast<const float*>(q), static_cast<const float*>(k),
+                                           static_cast<const float*>(v), pb, tb);
+    ta.av = av;
+    return device_status(hstu::launch_attn_train_fwd(ta, s), "attention launch");
+  }
   const hstu::AttnArgs a = make_attn_args(d, j, c, q, k, v, pb, tb, av, ws);
   return device_status(d->dtype == HSTU_BF16 ? hstu::launch_attn_bf16(a, s) : hstu::launch_attn_f32(a, s),
                        "attention launch");
@@ -542,8 +563,9 @@ int hstu_layer_bwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
   if (st) return st;
   HSTU_TRY(hstu::launch_gemm_f32s(X, d, 1, W1, 1, d, Z, d4, nullptr, params->b1, static_cast<int>(T), d4, d,
                                   1, s), "z gemm");
-  st = do_attn(desc, jagged, nullptr, Q, K, V, params->pos_bias, params->time_bias, AV, nullptr, s);
-  if (st) return st;
+  hstu::BwdAttnArgs ba = make_train_args(desc, jagged, Q, K, V, params->pos_bias, params->time_bias);
+  ba.av = AV;
+  HSTU_TRY(hstu::launch_attn_train_fwd(ba, s), "attention forward");
   HSTU_TRY(hstu::launch_ln_gate_fwd(AV, U, params->ln_gamma, params->ln_beta, NH, RSTD, G, T, d,
                                     desc->ln_eps, s), "ln/gate forward");
   // Y = X + G W2^T + b2
@@ -556,16 +578,9 @@ int hstu_layer_bwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
   HSTU_TRY(hstu::launch_ln_gate_bwd(DG, U, NH, RSTD, params->ln_gamma, params->ln_beta, DZ, d4, DAV,
                                     grads->dgamma, grads->dbeta, T, d, s), "ln/gate backward");
   // AV = (SiLU(a Q K^T + rab) . M) V, per head
-  hstu::BwdAttnArgs ba{};
-  ba.q = Q; ba.k = K; ba.v = V; ba.dav = DAV;
-  ba.offsets = jagged->offsets; ba.ts = jagged->timestamps;
-  ba.pos_bias = params->pos_bias; ba.time_bias = params->time_bias;
+  ba.dav = DAV;
   ba.dv = DZ + d; ba.dq = DZ + 2 * d; ba.dk = DZ + 3 * d; ba.ld_dz = d4;
   ba.dpos = grads->dpos; ba.dtime = grads->dtime;
-  ba.d_model = d; ba.num_heads = desc->num_heads; ba.head_dim = desc->head_dim;
-  ba.pos_len = desc->pos_table_len; ba.pos_center = (desc->pos_table_len - 1) / 2;
-  ba.nb = desc->num_time_buckets; ba.alpha = desc->alpha;
-  ba.num_seqs = jagged->num_seqs; ba.max_seq_len = jagged->max_seq_len;
   HSTU_TRY(hstu::launch_attn_bwd_f32(ba, s), "attention backward");
   // [U V Q K] = SiLU(X W1^T + b1)
   HSTU_TRY(hstu::launch_silu_bwd(DZ, Z, T * d4, s), "silu backward");

@@ -1,0 +1,466 @@
+// Attention of one HSTU layer for training, fp32 on the matrix cores
+// (v_mfma_f32_16x16x4_f32). Plain causal attention over the batch's own
+// tokens, as "HSTU：Scaling Law 的首次探索" §7.1.5 trains it: per head
+//   S = alpha Q K^T + rab,  P = SiLU(S) . M,  AV = P V
+// ("万亿参数推荐大模型…" §2.1 second equation), and its backward
+//   dP = dAV V^T,  dS = dP . SiLU'(S) . M,  dV = P^T dAV,
+//   dQ = alpha dS K,  dK = alpha dS^T Q,  d rab(i, j) += dS(i, j).
+//
+// Three kernels share one structure. A wave owns 32 rows of one head (query
+// rows for the forward and dQ, key rows for dK/dV), keeps their operands in
+// registers, and walks the visible 32-row blocks of the other side:
+//   * score-shaped products over the 32x32 block (S, and dP for the
+//     backward), as 2x2 tiles of 16x16, whose accumulators put one query
+//     or key per lane and 4 rows of the other side in each tile's registers;
+//   * the pointwise step in those registers (bias, SiLU, mask, dS);
+//   * the second product(s), where each accumulator register is exactly the
+//     B operand of a 16x16x4 step over 4 rows of that side.
+// The contraction order of every product is free, so each operand is loaded
+// in the order that suits its layout: float4 runs along the head dimension
+// for the row-per-lane operands, and whole rows across the lanes for the
+// dimension-per-lane ones. A workgroup holds one wave per head of the same
+// 32 rows, so its waves have identical trip counts.
+#include "common.h"
+#include "internal.h"
+
+namespace hstu {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2eT = 1.4426950408889634f;
+// Entries of the workgroup's LDS accumulator of position-bias gradients
+// (position differences -31 .. kPosCap-32); larger differences are added to
+// global memory directly.
+constexpr int kPosCap = 16384 + 64;
+
+// 16x16x4: lane l supplies A[l%16][l/16] and B[l/16][l%16]; accumulator
+// register r of lane l is D[4 (l/16) + r][l%16]. (The 32x32x2 form runs at
+// half this rate on gfx950.)
+__device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float sigmoid_t(float s) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2eT * s));
+}
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+__device__ __forceinline__ float comp(const float4& v, int e) {
+  return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
+}
+
+// Row-per-lane operand of a product over the head dimension: lane (row, g)
+// holds columns 16u + 4g + e (u < DH/16, e < 4) of its row, so that step
+// t = 4u + e contracts columns 16u + 4g' + e over the lane groups g'.
+template <int DH>
+__device__ __forceinline__ void load_rowop(const float* row, int g, float4 (&o)[DH / 16]) {
+#pragma unroll
+  for (int u = 0; u < DH / 16; ++u) o[u] = *reinterpret_cast<const float4*>(row + 16 * u + 4 * g);
+}
+
+// Dimension-per-lane operand: the NCT = DH/16 columns NCT*lc .. NCT*lc+NCT-1
+// of one row, so that output tile ct, row lc is column NCT*lc + ct.
+template <int NCT>
+struct ColOp {
+  float v[NCT];
+};
+template <int NCT>
+__device__ __forceinline__ ColOp<NCT> load_colop(const float* row, int lc) {
+  ColOp<NCT> o;
+  if constexpr (NCT == 4) {
+    const float4 x = *reinterpret_cast<const float4*>(row + 4 * lc);
+    o.v[0] = x.x; o.v[1] = x.y; o.v[2] = x.z; o.v[3] = x.w;
+  } else {
+    const float2 x = *reinterpret_cast<const float2*>(row + 2 * lc);
+    o.v[0] = x.x; o.v[1] = x.y;
+  }
+  return o;
+}
+
+// Stores the NCT x 2 output tiles of one lane: tile (ct, bt), register r is
+// output row i = 4g + r -> column NCT*i + ct, of the lane's row 16 bt + lc.
+// out points at row 16*0 + lc, head column 0; ld is the row stride.
+template <int NCT>
+__device__ __forceinline__ void store_tiles(float* out, int64_t ld, const f32x4 (&acc)[NCT][2], int g,
+                                            float scale, bool ok0, bool ok1) {
+#pragma unroll
+  for (int bt = 0; bt < 2; ++bt) {
+    if (!(bt == 0 ? ok0 : ok1)) continue;
+    float* row = out + bt * 16 * ld;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int c = NCT * (4 * g + r);
+      if constexpr (NCT == 4) {
+        float4 x;
+        x.x = acc[0][bt][r] * scale; x.y = acc[1][bt][r] * scale;
+        x.z = acc[2][bt][r] * scale; x.w = acc[3][bt][r] * scale;
+        *reinterpret_cast<float4*>(row + c) = x;
+      } else {
+        float2 x;
+        x.x = acc[0][bt][r] * scale; x.y = acc[1][bt][r] * scale;
+        *reinterpret_cast<float2*>(row + c) = x;
+      }
+    }
+  }
+}
+
+struct Place {
+  int seq, blk, h;
+};
+
+// Workgroup -> (sequence, 32-row block, head of this wave). Blocks are taken
+// heaviest first: descending for query blocks (more keys below them),
+// ascending for key blocks (more queries above them). Workgroups go to the
+// XCDs round-robin, so with the (sequence, head group) index alone each XCD
+// would keep the same few sequences for the whole launch, and the cost of a
+// sequence grows with its squared length; the index is rotated by the block
+// row so that every sequence's rows spread over all XCDs.
+__device__ __forceinline__ Place place(const BwdAttnArgs& a, bool descending, int wave, int nw) {
+  const int hgs = a.num_heads / nw;
+  const int nblk = (a.max_seq_len + 31) >> 5;
+  const int per = a.num_seqs * hgs;
+  const int b = static_cast<int>(blockIdx.x) / per;
+  int rem = static_cast<int>(blockIdx.x) - b * per;
+  rem = (rem + b) % per;
+  Place p;
+  p.blk = descending ? nblk - 1 - b : b;
+  p.seq = rem / hgs;
+  p.h = (rem - p.seq * hgs) * nw + wave;
+  return p;
+}
+
+// Forward (FWD: AV) or dQ with the bias-table gradients, for the 32 query
+// rows of one block (two 16-row tiles) and one head per wave.
+template <int DH, bool FWD>
+__global__ __launch_bounds__(512) void attn_train_q_kernel(BwdAttnArgs a) {
+  constexpr int NU = DH / 16, NCT = DH / 16;
+  __shared__ float s_gpos[FWD ? 1 : kPosCap];
+  __shared__ float s_tval[64], s_tgrad[64];
+  __shared__ float s_win[8][64];
+  __shared__ int64_t s_ts[8][32];
+  const int nw = blockDim.x >> 6;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lc = lane & 15, g = lane >> 4;
+  const Place pl = place(a, true, wave, nw);
+  const int64_t s0 = a.offsets[pl.seq];
+  const int L = static_cast<int>(a.offsets[pl.seq + 1] - s0);
+  const int q0 = pl.blk * 32;
+  if (q0 >= L) return;   // the whole workgroup: same sequence and block
+  const int range = min(q0 + 63, kPosCap);   // LDS entries d + 31 this block can touch
+  if (!FWD) {
+    for (int e = tid; e < range; e += blockDim.x) s_gpos[e] = 0.0f;
+    if (tid < 64) s_tgrad[tid] = 0.0f;
+  }
+  if (tid < 64) s_tval[tid] = tid < a.nb ? a.time_bias[tid] : 0.0f;
+  __syncthreads();
+
+  const int d = a.d_model;
+  // this sequence's rows of the head; row offsets within a sequence are int32
+  const int64_t base = s0 * d + pl.h * DH;
+  const float* Ks = a.k + base;
+  const float* Vs = a.v + base;
+  const float* Cs = FWD ? Vs : Ks;   // operand of the second product
+  const int64_t* Ts = a.ts + s0;
+  // query tiles: rows q0 + lc and q0 + 16 + lc
+  float4 qr[2][NU], dr[2][NU];
+  int64_t tq[2];
+  bool qv[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int qrow = min(q0 + 16 * qt + lc, L - 1);
+    qv[qt] = q0 + 16 * qt + lc < L;
+    load_rowop<DH>(a.q + base + qrow * d, g, qr[qt]);
+    if (!FWD) load_rowop<DH>(a.dav + base + qrow * d, g, dr[qt]);
+    tq[qt] = Ts[qrow];
+  }
+  float* win = s_win[wave];
+  int64_t* kts = s_ts[wave];
+  f32x4 acc[NCT][2];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) acc[ct][0] = acc[ct][1] = f32x4{};
+  int tb_cur = -1;
+  float tg_cur = 0.0f;
+  // position-bias window of block kb: entry e <-> difference q0 - 32 kb - 31 + e;
+  // the window value and the key timestamp of this lane are fetched a block ahead
+  float wv = a.pos_bias[clampi(a.pos_center + q0 - 31 + lane, 0, a.pos_len - 1)];
+  int64_t tsv = Ts[min(lane & 31, L - 1)];
+
+  for (int kb = 0; kb <= pl.blk; ++kb) {
+    const int j0 = kb * 32, D = q0 - j0;
+    win[lane] = wv;
+    if (lane < 32) kts[lane] = tsv;
+    wv = a.pos_bias[clampi(a.pos_center + D - 63 + lane, 0, a.pos_len - 1)];
+    tsv = Ts[min(j0 + 32 + (lane & 31), L - 1)];
+    float4 kr[2][NU], vr[2][NU];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int krow = min(j0 + 16 * kt + lc, L - 1);
+      load_rowop<DH>(Ks + krow * d, g, kr[kt]);
+      if (!FWD) load_rowop<DH>(Vs + krow * d, g, vr[kt]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // S^T = K Q^T (rows: keys, columns: queries); dP^T = V dAV^T
+    f32x4 sacc[2][2], pacc[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) sacc[kt][qt] = pacc[kt][qt] = f32x4{};
+#pragma unroll
+    for (int t = 0; t < DH / 4; ++t)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          sacc[kt][qt] = mma(comp(kr[kt][t >> 2], t & 3), comp(qr[qt][t >> 2], t & 3), sacc[kt][qt]);
+          if (!FWD)
+            pacc[kt][qt] = mma(comp(vr[kt][t >> 2], t & 3), comp(dr[qt][t >> 2], t & 3), pacc[kt][qt]);
+        }
+    // the second product's operand, requested while the scores finish (it
+    // takes the registers of K and V above): key row 16 kt + 4g + r
+    ColOp<NCT> kc[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) kc[kt][r] = load_colop<NCT>(Cs + min(j0 + 16 * kt + 4 * g + r, L - 1) * d, lc);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int jr = 16 * kt + 4 * g + r;   // key row in the block
+        const int64_t tk = kts[jr];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          const int ir = 16 * qt + lc;        // query row in the block
+          const bool vis = qv[qt] && (j0 + jr <= q0 + ir);
+          const int tb = time_bucket64(tq[qt] - tk, a.nb);
+          const float sc = a.alpha * sacc[kt][qt][r] + win[ir - jr + 31] + s_tval[tb];
+          const float sg = sigmoid_t(sc);
+          if (FWD) {
+            sacc[kt][qt][r] = vis ? sc * sg : 0.0f;
+          } else {
+            const float ds = vis ? pacc[kt][qt][r] * sg * (1.0f + sc * (1.0f - sg)) : 0.0f;
+            sacc[kt][qt][r] = ds;
+            if (vis) {
+              const int gi = D + ir - jr + 31;
+              if (gi < kPosCap)
+                atomicAdd(&s_gpos[gi], ds);
+              else
+                atomicAdd(&a.dpos[clampi(a.pos_center + gi - 31, 0, a.pos_len - 1)], ds);
+            }
+          }
+        }
+      }
+    if (!FWD) {
+      // time-bucket gradients: per lane and query tile the keys ascend, so
+      // runs of one bucket are summed in registers before an LDS add
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int jr = 16 * kt + 4 * g + r;
+            if (qv[qt] && j0 + jr <= q0 + 16 * qt + lc) {
+              const int tb = time_bucket64(tq[qt] - kts[jr], a.nb);
+              if (tb != tb_cur) {
+                if (tb_cur >= 0) atomicAdd(&s_tgrad[tb_cur], tg_cur);
+                tb_cur = tb;
+                tg_cur = 0.0f;
+              }
+              tg_cur += sacc[kt][qt][r];
+            }
+          }
+    }
+    // dQ^T += K^T dS^T (AV^T += V^T P^T): step (kt, r) contracts keys 16 kt + 4g' + r
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) acc[ct][qt] = mma(kc[kt][r].v[ct], sacc[kt][qt][r], acc[ct][qt]);
+  }
+
+  if (FWD)
+    store_tiles<NCT>(a.av + (s0 + q0 + lc) * d + pl.h * DH, d, acc, g, 1.0f, qv[0], qv[1]);
+  else
+    store_tiles<NCT>(a.dq + (s0 + q0 + lc) * a.ld_dz + pl.h * DH, a.ld_dz, acc, g, a.alpha, qv[0], qv[1]);
+  if (!FWD) {
+    if (tb_cur >= 0) atomicAdd(&s_tgrad[tb_cur], tg_cur);
+    __syncthreads();
+    for (int e = tid; e < range; e += blockDim.x) {
+      const float gsum = s_gpos[e];
+      if (gsum != 0.0f) atomicAdd(&a.dpos[clampi(a.pos_center + e - 31, 0, a.pos_len - 1)], gsum);
+    }
+    if (tid < a.nb && s_tgrad[tid] != 0.0f) atomicAdd(&a.dtime[tid], s_tgrad[tid]);
+  }
+}
+
+// dK and dV for the 32 key rows of one block (two 16-row tiles) and one
+// head per wave.
+template <int DH>
+__global__ __launch_bounds__(512) void attn_train_kv_kernel(BwdAttnArgs a) {
+  constexpr int NU = DH / 16, NCT = DH / 16;
+  __shared__ float s_tval[64];
+  __shared__ float s_win[8][64];
+  __shared__ int64_t s_ts[8][32];
+  // V rows of each wave, parked in LDS by the lane that reads them back
+  // (registers are the limit here); 16-byte padding per lane
+  __shared__ float4 s_v[8][2][NU][64 + 1];
+  __shared__ int64_t s_kts[8][32];
+  const int nw = blockDim.x >> 6;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lc = lane & 15, g = lane >> 4;
+  const Place pl = place(a, false, wave, nw);
+  const int64_t s0 = a.offsets[pl.seq];
+  const int L = static_cast<int>(a.offsets[pl.seq + 1] - s0);
+  const int j0 = pl.blk * 32;
+  if (j0 >= L) return;
+  if (tid < 64) s_tval[tid] = tid < a.nb ? a.time_bias[tid] : 0.0f;
+  __syncthreads();
+
+  const int d = a.d_model;
+  const int64_t base = s0 * d + pl.h * DH;
+  const float* Qs = a.q + base;
+  const float* Ds = a.dav + base;
+  const int64_t* Ts = a.ts + s0;
+  float4 kr[2][NU];
+  bool kv[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int krow = min(j0 + 16 * kt + lc, L - 1);
+    kv[kt] = j0 + 16 * kt + lc < L;
+    load_rowop<DH>(a.k + base + krow * d, g, kr[kt]);
+    float4 vr[NU];
+    load_rowop<DH>(a.v + base + krow * d, g, vr);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) s_v[wave][kt][u][lane] = vr[u];
+  }
+  if (lane < 32) s_kts[wave][lane] = Ts[min(j0 + lane, L - 1)];
+  float* win = s_win[wave];
+  int64_t* qts = s_ts[wave];
+  f32x4 dk[NCT][2], dv[NCT][2];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) dk[ct][0] = dk[ct][1] = dv[ct][0] = dv[ct][1] = f32x4{};
+  const int nblk = (L + 31) >> 5;
+  // window entry e <-> difference 32 qb - j0 - 31 + e; fetched a block ahead
+  float wv = a.pos_bias[clampi(a.pos_center - 31 + lane, 0, a.pos_len - 1)];
+  int64_t tsv = Ts[min(j0 + (lane & 31), L - 1)];
+  for (int qb = pl.blk; qb < nblk; ++qb) {
+    const int q0 = qb * 32, D = q0 - j0;
+    win[lane] = wv;
+    if (lane < 32) qts[lane] = tsv;
+    wv = a.pos_bias[clampi(a.pos_center + D + 1 + lane, 0, a.pos_len - 1)];
+    tsv = Ts[min(q0 + 32 + (lane & 31), L - 1)];
+    float4 qa[2][NU], da[2][NU], vr[2][NU];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int qrow = min(q0 + 16 * qt + lc, L - 1);
+      load_rowop<DH>(Qs + qrow * d, g, qa[qt]);
+      load_rowop<DH>(Ds + qrow * d, g, da[qt]);
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int u = 0; u < NU; ++u) vr[kt][u] = s_v[wave][kt][u][lane];
+    __builtin_amdgcn_sched_barrier(0);
+    // S = Q K^T (rows: queries, columns: keys); dP = dAV V^T
+    f32x4 sacc[2][2], pacc[2][2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) sacc[qt][kt] = pacc[qt][kt] = f32x4{};
+#pragma unroll
+    for (int t = 0; t < DH / 4; ++t)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          sacc[qt][kt] = mma(comp(qa[qt][t >> 2], t & 3), comp(kr[kt][t >> 2], t & 3), sacc[qt][kt]);
+          pacc[qt][kt] = mma(comp(da[qt][t >> 2], t & 3), comp(vr[kt][t >> 2], t & 3), pacc[qt][kt]);
+        }
+    // the second products' operands (in the registers of qa/da): query row 16 qt + 4g + r
+    ColOp<NCT> qc[2][4], dc[2][4];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = min(q0 + 16 * qt + 4 * g + r, L - 1) * d;
+        qc[qt][r] = load_colop<NCT>(Qs + row, lc);
+        dc[qt][r] = load_colop<NCT>(Ds + row, lc);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t tk[2] = {s_kts[wave][lc], s_kts[wave][16 + lc]};
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ir = 16 * qt + 4 * g + r;   // query row in the block
+        const int64_t tqr = qts[ir];
+        const bool qok = q0 + ir < L;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const int jr = 16 * kt + lc;        // key row in the block
+          const bool vis = kv[kt] && qok && (j0 + jr <= q0 + ir);
+          const int tb = time_bucket64(tqr - tk[kt], a.nb);
+          const float sc = a.alpha * sacc[qt][kt][r] + win[ir - jr + 31] + s_tval[tb];
+          const float sg = sigmoid_t(sc);
+          sacc[qt][kt][r] = vis ? sc * sg : 0.0f;
+          pacc[qt][kt][r] = vis ? pacc[qt][kt][r] * sg * (1.0f + sc * (1.0f - sg)) : 0.0f;
+        }
+      }
+    // dV^T += dAV^T P, dK^T += Q^T dS: step (qt, r) contracts queries 16 qt + 4g' + r
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            dv[ct][kt] = mma(dc[qt][r].v[ct], sacc[qt][kt][r], dv[ct][kt]);
+            dk[ct][kt] = mma(qc[qt][r].v[ct], pacc[qt][kt][r], dk[ct][kt]);
+          }
+  }
+  store_tiles<NCT>(a.dk + (s0 + j0 + lc) * a.ld_dz + pl.h * DH, a.ld_dz, dk, g, a.alpha, kv[0], kv[1]);
+  store_tiles<NCT>(a.dv + (s0 + j0 + lc) * a.ld_dz + pl.h * DH, a.ld_dz, dv, g, 1.0f, kv[0], kv[1]);
+}
+
+// Waves per workgroup: the largest divisor of num_heads up to 8.
+int waves_for(int num_heads) {
+  for (int w = 8; w > 1; --w)
+    if (num_heads % w == 0) return w;
+  return 1;
+}
+
+template <typename K>
+hipError_t launch_train(K kernel, const BwdAttnArgs& a, hipStream_t s) {
+  const int nw = waves_for(a.num_heads);
+  const int64_t nblk = (static_cast<int64_t>(a.max_seq_len) + 31) / 32;
+  const int64_t grid = nblk * a.num_seqs * (a.num_heads / nw);
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(64 * nw), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attn_train_supported(int head_dim) { return head_dim == 32 || head_dim == 64; }
+
+hipError_t launch_attn_train_fwd(const BwdAttnArgs& a, hipStream_t s) {
+  return a.head_dim == 32 ? launch_train(attn_train_q_kernel<32, true>, a, s)
+                          : launch_train(attn_train_q_kernel<64, true>, a, s);
+}
+
+hipError_t launch_attn_bwd_f32(const BwdAttnArgs& a, hipStream_t s) {
+  hipError_t e = a.head_dim == 32 ? launch_train(attn_train_q_kernel<32, false>, a, s)
+                                  : launch_train(attn_train_q_kernel<64, false>, a, s);
+  if (e != hipSuccess) return e;
+  return a.head_dim == 32 ? launch_train(attn_train_kv_kernel<32>, a, s)
+                          : launch_train(attn_train_kv_kernel<64>, a, s);
+}
+
+}  // namespace hstu

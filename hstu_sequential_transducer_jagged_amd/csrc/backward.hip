@@ -12,10 +12,8 @@
 //   [U V Q K] = SiLU(X W1^T + b1) dZ = d[U V Q K] . SiLU'(Z), dW1, db1, dX
 //
 // Kernels here are plain fp32: a strided tiled GEMM (split-K with atomics
-// for the weight gradients), row kernels for the LayerNorm/gate step, and
-// two attention kernels that recompute the scores, one over queries (dQ
-// and the bias-table gradients, accumulated in LDS and flushed with
-// atomics) and one over keys (dK, dV).
+// for the weight gradients) and row kernels for the LayerNorm/gate step.
+// The attention backward is in attn_train.hip.
 #include "common.h"
 #include "internal.h"
 
@@ -205,159 +203,6 @@ __global__ __launch_bounds__(256) void silu_bwd_kernel(float* dz, const float* _
   }
 }
 
-// rab of one (query, key) pair, as the fp32 forward computes it.
-__device__ __forceinline__ int pos_index(const BwdAttnArgs& a, int qi, int j) {
-  int p = qi - j + a.pos_center;
-  return p < 0 ? 0 : (p >= a.pos_len ? a.pos_len - 1 : p);
-}
-
-// One thread per query row of head h: recomputes the scores of its visible
-// keys (j <= i), accumulates dQ, and the table gradients of the block: a
-// 127-entry window of position differences per key chunk and the time
-// buckets, summed in LDS and flushed with atomics.
-template <int DH>
-__global__ __launch_bounds__(64) void attn_bwd_q_kernel(BwdAttnArgs a) {
-  __shared__ float sk[64][DH];
-  __shared__ float sv[64][DH];
-  __shared__ int64_t skt[64];
-  __shared__ float spos[128];
-  __shared__ float stime[64];
-  const int seq = blockIdx.x, qt = blockIdx.y, h = blockIdx.z;
-  const int64_t s0 = a.offsets[seq];
-  const int L = static_cast<int>(a.offsets[seq + 1] - s0);
-  if (qt * 64 >= L) return;
-  const int qi = qt * 64 + threadIdx.x;
-  const bool qvalid = qi < L;
-  const int d = a.d_model;
-  const int ld = a.ld_dz;
-  float qv[DH], dv_[DH], dq[DH];
-#pragma unroll
-  for (int c = 0; c < DH; ++c) {
-    qv[c] = qvalid ? a.q[(s0 + qi) * d + h * DH + c] : 0.0f;
-    dv_[c] = qvalid ? a.dav[(s0 + qi) * d + h * DH + c] : 0.0f;
-    dq[c] = 0.0f;
-  }
-  const int64_t tq = qvalid ? a.ts[s0 + qi] : 0;
-  stime[threadIdx.x] = 0.0f;
-  const int q_hi = min(qt * 64 + 64, L);
-  for (int k0 = 0; k0 < q_hi; k0 += 64) {
-    __syncthreads();   // previous chunk's reads and flush are done
-    for (int i = threadIdx.x; i < 64 * DH; i += 64) {
-      const int r = i / DH, cc = i - r * DH;
-      const int kk = k0 + r;
-      const bool in = kk < q_hi;
-      sk[r][cc] = in ? a.k[(s0 + kk) * d + h * DH + cc] : 0.0f;
-      sv[r][cc] = in ? a.v[(s0 + kk) * d + h * DH + cc] : 0.0f;
-    }
-    skt[threadIdx.x] = k0 + static_cast<int>(threadIdx.x) < q_hi ? a.ts[s0 + k0 + threadIdx.x] : 0;
-    spos[threadIdx.x] = 0.0f;
-    spos[threadIdx.x + 64] = 0.0f;
-    __syncthreads();
-    const int base = qt * 64 - k0 - 63;   // position difference of window entry 0
-    const int kend = min(64, q_hi - k0);
-    for (int r = 0; r < kend; ++r) {
-      const int j = k0 + r;
-      if (!qvalid || j > qi) continue;
-      float dot = 0.0f, dp = 0.0f;
-#pragma unroll
-      for (int c = 0; c < DH; ++c) {
-        dot = fmaf(qv[c], sk[r][c], dot);
-        dp = fmaf(dv_[c], sv[r][c], dp);
-      }
-      const int pidx = pos_index(a, qi, j);
-      const int tbk = time_bucket64(tq - skt[r], a.nb);
-      const float sc = a.alpha * dot + a.pos_bias[pidx] + a.time_bias[tbk];
-      const float sg = sigmoid_f(sc);
-      const float ds = dp * sg * (1.0f + sc * (1.0f - sg));
-#pragma unroll
-      for (int c = 0; c < DH; ++c) dq[c] = fmaf(a.alpha * ds, sk[r][c], dq[c]);
-      atomicAdd(&spos[qi - j - base], ds);
-      atomicAdd(&stime[tbk], ds);
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < 127; e += 64) {
-      const float g = spos[e];
-      if (g != 0.0f) {
-        int p = base + e + a.pos_center;
-        p = p < 0 ? 0 : (p >= a.pos_len ? a.pos_len - 1 : p);
-        atomicAdd(&a.dpos[p], g);
-      }
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x < a.nb && stime[threadIdx.x] != 0.0f) atomicAdd(&a.dtime[threadIdx.x], stime[threadIdx.x]);
-  if (qvalid) {
-#pragma unroll
-    for (int c = 0; c < DH; ++c) a.dq[(s0 + qi) * ld + h * DH + c] = dq[c];
-  }
-}
-
-// One thread per key row j of head h: recomputes the scores of the queries
-// that see it (i >= j) and accumulates dK and dV.
-template <int DH>
-__global__ __launch_bounds__(64) void attn_bwd_kv_kernel(BwdAttnArgs a) {
-  __shared__ float sq[64][DH];
-  __shared__ float sd[64][DH];
-  __shared__ int64_t sqt[64];
-  const int seq = blockIdx.x, kt = blockIdx.y, h = blockIdx.z;
-  const int64_t s0 = a.offsets[seq];
-  const int L = static_cast<int>(a.offsets[seq + 1] - s0);
-  if (kt * 64 >= L) return;
-  const int j = kt * 64 + threadIdx.x;
-  const bool kvalid = j < L;
-  const int d = a.d_model;
-  const int ld = a.ld_dz;
-  float kv[DH], vv[DH], dk[DH], dv[DH];
-#pragma unroll
-  for (int c = 0; c < DH; ++c) {
-    kv[c] = kvalid ? a.k[(s0 + j) * d + h * DH + c] : 0.0f;
-    vv[c] = kvalid ? a.v[(s0 + j) * d + h * DH + c] : 0.0f;
-    dk[c] = 0.0f;
-    dv[c] = 0.0f;
-  }
-  const int64_t tk = kvalid ? a.ts[s0 + j] : 0;
-  for (int q0 = kt * 64; q0 < L; q0 += 64) {
-    __syncthreads();
-    for (int i = threadIdx.x; i < 64 * DH; i += 64) {
-      const int r = i / DH, cc = i - r * DH;
-      const int qq = q0 + r;
-      const bool in = qq < L;
-      sq[r][cc] = in ? a.q[(s0 + qq) * d + h * DH + cc] : 0.0f;
-      sd[r][cc] = in ? a.dav[(s0 + qq) * d + h * DH + cc] : 0.0f;
-    }
-    sqt[threadIdx.x] = q0 + static_cast<int>(threadIdx.x) < L ? a.ts[s0 + q0 + threadIdx.x] : 0;
-    __syncthreads();
-    const int qend = min(64, L - q0);
-    for (int r = 0; r < qend; ++r) {
-      const int qi = q0 + r;
-      if (!kvalid || qi < j) continue;
-      float dot = 0.0f, dp = 0.0f;
-#pragma unroll
-      for (int c = 0; c < DH; ++c) {
-        dot = fmaf(sq[r][c], kv[c], dot);
-        dp = fmaf(sd[r][c], vv[c], dp);
-      }
-      const int pidx = pos_index(a, qi, j);
-      const float sc = a.alpha * dot + a.pos_bias[pidx] + a.time_bias[time_bucket64(sqt[r] - tk, a.nb)];
-      const float sg = sigmoid_f(sc);
-      const float p = sc * sg;
-      const float ds = dp * sg * (1.0f + sc * (1.0f - sg));
-#pragma unroll
-      for (int c = 0; c < DH; ++c) {
-        dk[c] = fmaf(a.alpha * ds, sq[r][c], dk[c]);
-        dv[c] = fmaf(p, sd[r][c], dv[c]);
-      }
-    }
-  }
-  if (kvalid) {
-#pragma unroll
-    for (int c = 0; c < DH; ++c) {
-      a.dk[(s0 + j) * ld + h * DH + c] = dk[c];
-      a.dv[(s0 + j) * ld + h * DH + c] = dv[c];
-    }
-  }
-}
-
 int blocks_for(int64_t n) {
   const int64_t b = (n + 255) / 256;
   return static_cast<int>(b < 4096 ? (b > 0 ? b : 1) : 4096);
@@ -421,18 +266,5 @@ hipError_t launch_silu_bwd(float* dz, const float* z, int64_t n, hipStream_t s) 
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd_f32(const BwdAttnArgs& a, hipStream_t s) {
-  const int nt = (a.max_seq_len + 63) / 64;
-  if (a.num_seqs == 0 || nt == 0) return hipSuccess;
-  dim3 grid(a.num_seqs, nt, a.num_heads);
-  if (a.head_dim == 32) {
-    hipLaunchKernelGGL(attn_bwd_q_kernel<32>, grid, dim3(64), 0, s, a);
-    hipLaunchKernelGGL(attn_bwd_kv_kernel<32>, grid, dim3(64), 0, s, a);
-  } else {
-    hipLaunchKernelGGL(attn_bwd_q_kernel<64>, grid, dim3(64), 0, s, a);
-    hipLaunchKernelGGL(attn_bwd_kv_kernel<64>, grid, dim3(64), 0, s, a);
-  }
-  return hipGetLastError();
-}
 
 }  // namespace hstu

@@ -127,11 +127,17 @@ struct BwdAttnArgs {
   float* dv;
   float* dpos;               // [pos_len], accumulated
   float* dtime;              // [nb], accumulated
+  float* av;                 // [T, d] forward output (launch_attn_train_fwd)
   int ld_dz;
   int d_model, num_heads, head_dim, pos_len, pos_center, nb;
   float alpha;
   int num_seqs, max_seq_len;
 };
+// fp32 attention on the matrix cores, plain causal (no targets, no cache),
+// head_dim 32 or 64: the forward AV, and the backward (dQ, dK, dV, table
+// gradients accumulated into dpos/dtime).
+bool attn_train_supported(int head_dim);
+hipError_t launch_attn_train_fwd(const BwdAttnArgs& a, hipStream_t s);
 hipError_t launch_attn_bwd_f32(const BwdAttnArgs& a, hipStream_t s);
 // C[m, n] = sum_k A[m sam + k sak] B[k sbk + n sbn] (+ bias[n] + addend[m, n]);
 // splits > 1: K split over blocks whose sums are added atomically into C
