@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhstu.so")
-SOURCES = ["api.cpp", "attn.hip", "attn_train.hip", "backward.hip", "gemm.hip", "pointwise.hip", "sampler.cpp"]
+SOURCES = ["api.cpp", "attn.hip", "attn_train.hip", "backward.hip", "gemm.hip", "gemm_f32.hip", "pointwise.hip", "sampler.cpp"]
 ARCH = "gfx950"
 
 

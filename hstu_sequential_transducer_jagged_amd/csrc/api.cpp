@@ -558,11 +558,24 @@ int hstu_layer_bwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
     st = device_status((expr), what);              \
     if (st) return st;                             \
   } while (0)
-  // forward recompute
-  st = do_proj(desc, params, T, x, U, V, Q, K, s);
-  if (st) return st;
-  HSTU_TRY(hstu::launch_gemm_f32s(X, d, 1, W1, 1, d, Z, d4, nullptr, params->b1, static_cast<int>(T), d4, d,
-                                  1, s), "z gemm");
+  // forward recompute: Z = X W1^T + b1 and [U V Q K] = SiLU(Z) in one pass
+  {
+    hstu::GemmF32Args g{};
+    g.A = X; g.sam = d; g.sak = 1;
+    g.B = W1; g.sbk = 1; g.sbn = d;
+    g.C = Z; g.ldc = d4; g.bias = params->b1;
+    g.outs[0] = U; g.outs[1] = V; g.outs[2] = Q; g.outs[3] = K;
+    g.split = d; g.M = static_cast<int>(T); g.N = d4; g.K = d;
+    const hipError_t e = hstu::launch_gemm_f32_mma(g, 2, 1, s);
+    if (e == hipErrorNotSupported) {
+      st = do_proj(desc, params, T, x, U, V, Q, K, s);
+      if (st) return st;
+      HSTU_TRY(hstu::launch_gemm_f32s(X, d, 1, W1, 1, d, Z, d4, nullptr, params->b1, static_cast<int>(T), d4,
+                                      d, 1, s), "z gemm");
+    } else {
+      HSTU_TRY(e, "projection");
+    }
+  }
   hstu::BwdAttnArgs ba = make_train_args(desc, jagged, Q, K, V, params->pos_bias, params->time_bias);
   ba.av = AV;
   HSTU_TRY(hstu::launch_attn_train_fwd(ba, s), "attention forward");

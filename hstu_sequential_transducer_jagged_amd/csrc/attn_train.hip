@@ -132,8 +132,10 @@ __device__ __forceinline__ Place place(const BwdAttnArgs& a, bool descending, in
 }
 
 // Forward (FWD: AV) or dQ with the bias-table gradients, for the 32 query
-// rows of one block (two 16-row tiles) and one head per wave.
-template <int DH, bool FWD>
+// rows of one block (two 16-row tiles) and one head per wave. LONG: some
+// position differences may lie beyond the LDS accumulator (sequences longer
+// than kPosCap - 64); those are added to global memory one by one.
+template <int DH, bool FWD, bool LONG = false>
 __global__ __launch_bounds__(512) void attn_train_q_kernel(BwdAttnArgs a) {
   constexpr int NU = DH / 16, NCT = DH / 16;
   __shared__ float s_gpos[FWD ? 1 : kPosCap];
@@ -179,8 +181,11 @@ __global__ __launch_bounds__(512) void attn_train_q_kernel(BwdAttnArgs a) {
   f32x4 acc[NCT][2];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) acc[ct][0] = acc[ct][1] = f32x4{};
-  int tb_cur = -1;
-  float tg_cur = 0.0f;
+  // time-bucket gradients: per lane and query tile the keys ascend, so runs
+  // of one bucket are summed in registers and added to LDS when the bucket
+  // changes (starting from bucket 0 with nothing summed)
+  int tb_cur[2] = {0, 0};
+  float tg_cur[2] = {0.0f, 0.0f};
   // position-bias window of block kb: entry e <-> difference q0 - 32 kb - 31 + e;
   // the window value and the key timestamp of this lane are fetched a block ahead
   float wv = a.pos_bias[clampi(a.pos_center + q0 - 31 + lane, 0, a.pos_len - 1)];
@@ -242,37 +247,19 @@ __global__ __launch_bounds__(512) void attn_train_q_kernel(BwdAttnArgs a) {
           } else {
             const float ds = vis ? pacc[kt][qt][r] * sg * (1.0f + sc * (1.0f - sg)) : 0.0f;
             sacc[kt][qt][r] = ds;
-            if (vis) {
-              const int gi = D + ir - jr + 31;
-              if (gi < kPosCap)
-                atomicAdd(&s_gpos[gi], ds);
-              else
-                atomicAdd(&a.dpos[clampi(a.pos_center + gi - 31, 0, a.pos_len - 1)], ds);
-            }
+            // hidden pairs add zero (their index D + ir - jr + 31 >= 0 is in range)
+            const int gi = D + ir - jr + 31;
+            if (!LONG || gi < kPosCap)
+              atomicAdd(&s_gpos[gi], ds);
+            else if (vis)
+              atomicAdd(&a.dpos[clampi(a.pos_center + gi - 31, 0, a.pos_len - 1)], ds);
+            const bool flush = vis && tb != tb_cur[qt];
+            if (flush) atomicAdd(&s_tgrad[tb_cur[qt]], tg_cur[qt]);
+            tg_cur[qt] = (flush ? 0.0f : tg_cur[qt]) + ds;
+            tb_cur[qt] = flush ? tb : tb_cur[qt];
           }
         }
       }
-    if (!FWD) {
-      // time-bucket gradients: per lane and query tile the keys ascend, so
-      // runs of one bucket are summed in registers before an LDS add
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int jr = 16 * kt + 4 * g + r;
-            if (qv[qt] && j0 + jr <= q0 + 16 * qt + lc) {
-              const int tb = time_bucket64(tq[qt] - kts[jr], a.nb);
-              if (tb != tb_cur) {
-                if (tb_cur >= 0) atomicAdd(&s_tgrad[tb_cur], tg_cur);
-                tb_cur = tb;
-                tg_cur = 0.0f;
-              }
-              tg_cur += sacc[kt][qt][r];
-            }
-          }
-    }
     // dQ^T += K^T dS^T (AV^T += V^T P^T): step (kt, r) contracts keys 16 kt + 4g' + r
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -289,7 +276,8 @@ __global__ __launch_bounds__(512) void attn_train_q_kernel(BwdAttnArgs a) {
   else
     store_tiles<NCT>(a.dq + (s0 + q0 + lc) * a.ld_dz + pl.h * DH, a.ld_dz, acc, g, a.alpha, qv[0], qv[1]);
   if (!FWD) {
-    if (tb_cur >= 0) atomicAdd(&s_tgrad[tb_cur], tg_cur);
+    atomicAdd(&s_tgrad[tb_cur[0]], tg_cur[0]);
+    atomicAdd(&s_tgrad[tb_cur[1]], tg_cur[1]);
     __syncthreads();
     for (int e = tid; e < range; e += blockDim.x) {
       const float gsum = s_gpos[e];
@@ -456,8 +444,14 @@ hipError_t launch_attn_train_fwd(const BwdAttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_attn_bwd_f32(const BwdAttnArgs& a, hipStream_t s) {
-  hipError_t e = a.head_dim == 32 ? launch_train(attn_train_q_kernel<32, false>, a, s)
-                                  : launch_train(attn_train_q_kernel<64, false>, a, s);
+  const bool lng = static_cast<int64_t>(a.max_seq_len) + 64 > kPosCap;
+  hipError_t e;
+  if (a.head_dim == 32)
+    e = lng ? launch_train(attn_train_q_kernel<32, false, true>, a, s)
+            : launch_train(attn_train_q_kernel<32, false, false>, a, s);
+  else
+    e = lng ? launch_train(attn_train_q_kernel<64, false, true>, a, s)
+            : launch_train(attn_train_q_kernel<64, false, false>, a, s);
   if (e != hipSuccess) return e;
   return a.head_dim == 32 ? launch_train(attn_train_kv_kernel<32>, a, s)
                           : launch_train(attn_train_kv_kernel<64>, a, s);

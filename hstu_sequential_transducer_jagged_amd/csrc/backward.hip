@@ -214,6 +214,21 @@ hipError_t launch_gemm_f32s(const float* A, int64_t sam, int64_t sak, const floa
                             int64_t sbn, float* C, int64_t ldc, const float* addend, const float* bias,
                             int M, int N, int64_t K, int splits, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
+  {
+    GemmF32Args g{};
+    g.A = A; g.sam = sam; g.sak = sak;
+    g.B = B; g.sbk = sbk; g.sbn = sbn;
+    g.C = C; g.ldc = ldc;
+    g.M = M; g.N = N; g.K = K;
+    if (splits > 1) {
+      const hipError_t e = launch_gemm_f32_mma(g, 1, splits, s);
+      if (e != hipErrorNotSupported) return e;
+    } else {
+      g.addend = addend; g.bias = bias;
+      const hipError_t e = launch_gemm_f32_mma(g, 0, 1, s);
+      if (e != hipErrorNotSupported) return e;
+    }
+  }
   if (splits > 1) {
     int64_t kchunk = (K + splits - 1) / splits;
     kchunk = (kchunk + 15) / 16 * 16;

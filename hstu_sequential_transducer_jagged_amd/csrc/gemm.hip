@@ -382,6 +382,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
 
 // ---------------------------------------------------------------------------
 // fp32: 16 x 16 output tile per block, K staged through LDS in steps of 16.
+// Used where the matrix-core kernel (gemm_f32.hip) refuses the layout.
 // ---------------------------------------------------------------------------
 template <class Epi>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A,
@@ -468,6 +469,16 @@ hipError_t launch_out_bf16(const OutArgs& a, hipStream_t s) {
 hipError_t launch_proj_f32(const ProjArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
   const int N = 4 * a.K;
+  if (a.M < (int64_t{1} << 31)) {
+    GemmF32Args g{};
+    g.A = static_cast<const float*>(a.x); g.sam = a.K; g.sak = 1;
+    g.B = static_cast<const float*>(a.w); g.sbk = 1; g.sbn = a.K;
+    g.bias = a.bias;
+    for (int i = 0; i < 4; ++i) g.outs[i] = static_cast<float*>(a.out[i]);
+    g.split = a.K; g.M = static_cast<int>(a.M); g.N = N; g.K = a.K;
+    const hipError_t e = launch_gemm_f32_mma(g, 2, 1, s);
+    if (e != hipErrorNotSupported) return e;
+  }
   ProjEpiF32 epi{a.bias,
                  {static_cast<float*>(a.out[0]), static_cast<float*>(a.out[1]),
                   static_cast<float*>(a.out[2]), static_cast<float*>(a.out[3])},
@@ -481,6 +492,16 @@ hipError_t launch_proj_f32(const ProjArgs& a, hipStream_t s) {
 
 hipError_t launch_out_f32(const OutArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
+  if (a.M < (int64_t{1} << 31)) {
+    GemmF32Args g{};
+    g.A = static_cast<const float*>(a.g); g.sam = a.K; g.sak = 1;
+    g.B = static_cast<const float*>(a.w); g.sbk = 1; g.sbn = a.K;
+    g.C = static_cast<float*>(a.y); g.ldc = a.K;
+    g.addend = static_cast<const float*>(a.x); g.bias = a.bias;
+    g.M = static_cast<int>(a.M); g.N = a.K; g.K = a.K;
+    const hipError_t e = launch_gemm_f32_mma(g, 0, 1, s);
+    if (e != hipErrorNotSupported) return e;
+  }
   OutEpiF32 epi{a.bias, static_cast<const float*>(a.x), static_cast<float*>(a.y), a.K};
   dim3 grid(static_cast<unsigned>((a.M + 15) / 16), (a.K + 15) / 16);
   hipLaunchKernelGGL(gemm_f32_kernel<OutEpiF32>, grid, dim3(256), 0, s,

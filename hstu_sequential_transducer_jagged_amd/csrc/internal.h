@@ -81,6 +81,30 @@ struct OutArgs {
   int K;
 };
 
+// fp32 GEMM on the matrix cores: C[m, n] = sum_k A[m sam + k sak] B[k sbk + n sbn].
+// epi 0: C = acc + bias[n] + addend[m, n] (each optional; addend row stride ldc);
+// epi 1: C += acc atomically, K split over `splits` chunks (C zeroed by the caller);
+// epi 2: outs[n / split][m * split + n % split] = SiLU(acc + bias[n]), and
+//        C[m, n] = acc + bias[n] when C is set (split % 16 == 0, N <= 4 split).
+// Returns hipErrorNotSupported, launching nothing, for operand layouts it does
+// not take (each operand needs its k index or its m / n index contiguous,
+// the other stride a multiple of 4, 16-byte aligned bases).
+struct GemmF32Args {
+  const float* A;
+  int64_t sam, sak;
+  const float* B;
+  int64_t sbk, sbn;
+  float* C;
+  int64_t ldc;
+  const float* addend;
+  const float* bias;
+  float* outs[4];
+  int split;
+  int M, N;
+  int64_t K, kchunk;
+};
+hipError_t launch_gemm_f32_mma(const GemmF32Args& a, int epi, int splits, hipStream_t s);
+
 hipError_t launch_proj_bf16(const ProjArgs& a, hipStream_t s);
 hipError_t launch_proj_f32(const ProjArgs& a, hipStream_t s);
 hipError_t launch_out_bf16(const OutArgs& a, hipStream_t s);
