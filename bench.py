@@ -34,7 +34,7 @@ if ROOT not in sys.path:
 METRIC = "HSTU layer fwd tokens/s; jagged attn TFLOP/s and % of bf16 MFMA peak, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
-PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32, matrix cores (dense) and vector alike
 
 
 def parse():
@@ -226,7 +226,7 @@ def run_layer(args):
     esz = 2 if w.dtype == "bf16" else 4
     proj_flop, out_flop = 8.0 * T * d * d, 2.0 * T * d * d
     ng_bytes = T * d * (4 + esz + esz)        # read AV (fp32) and U, write G
-    # the bf16 path runs on MFMA; the fp32 path on plain fp32 FMA (vector ALU)
+    # both paths run on the matrix cores: bf16 MFMA, and fp32 16x16x4 MFMA
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     kernels = {
         "proj": {"ms": pct(per["proj"]), "tflops": proj_flop / np.mean(per["proj"]) / 1e9,
@@ -264,7 +264,7 @@ def run_layer(args):
                    "num_heads": H, "head_dim": d // H, "visible_pairs": P,
                    "input_norm": bool(args.input_norm),
                    "bias": ("parameter-free m_p=%g m_t=%g" % lin) if lin else "tables"},
-        "roofline": {"kernel": "attn_" + w.dtype, "bound": "mfma" if w.dtype == "bf16" else "alu",
+        "roofline": {"kernel": "attn_" + w.dtype, "bound": "mfma",
                      "achieved": attn_tflops, "peak": peak, "unit": "TFLOP/s",
                      "frac": attn_tflops / peak,
                      "traffic": traffic_record("attn_bf16", src) if args.workload == 2 else None,
@@ -397,9 +397,11 @@ def run_backward(args):
     ms_fwd = timed(lambda: hstu.hstu_layer_fwd(lay.desc, lay.params, dw.jagged, None, dw.x, y, None, None,
                                                wsf, sh), stream, args.warmup, args.steps)
     P = visible_pairs(w.offsets)
-    # algorithmic FLOPs: forward recompute (proj 8Td^2 + Z 8Td^2 + attention 4dP) and backward
-    # (dG, dW2 2Td^2 each; dW1, dX 8Td^2 each; attention 14dP: dQ 6dP, dK/dV 8dP)
-    flop = 16.0 * T * d * d + 4.0 * d * P + 20.0 * T * d * d + 14.0 * d * P
+    # algorithmic FLOPs: the forward recompute (f1 8Td^2, attention S and AV 4dP) and the
+    # backward (dG, dW2 2Td^2 each; dW1, dX 8Td^2 each; attention dP, dV, dQ, dK 8dP)
+    flop = 8.0 * T * d * d + 4.0 * d * P + 20.0 * T * d * d + 8.0 * d * P
+    # executed: the dQ and the dK/dV kernels each recompute S and dP (another 6dP)
+    flop_exec = flop + 6.0 * d * P
     rec = base_record(args, "HSTU layer backward tokens/s (fp32, forward recompute included), 1 GPU",
                       T / (ms * 1e-3), "tokens/s", ms, "f32",
                       {"workload": gen.CONFIG_NAMES[args.workload] + ", held in fp32", "total_tokens": T,
@@ -408,7 +410,9 @@ def run_backward(args):
     rec["forward_fp32_ms"] = ms_fwd
     rec["backward_over_forward"] = ms / ms_fwd
     rec["algorithmic_flop"] = flop
-    rec["roofline"] = {"kernel": "layer backward (all kernels)", "bound": "alu",
+    rec["executed_flop"] = flop_exec
+    rec["executed_tflops"] = flop_exec / (ms * 1e-3) / 1e12
+    rec["roofline"] = {"kernel": "layer backward (all kernels)", "bound": "mfma",
                        "achieved": flop / (ms * 1e-3) / 1e12, "peak": PEAK_F32_TFLOPS,
                        "unit": "TFLOP/s", "frac": flop / (ms * 1e-3) / 1e12 / PEAK_F32_TFLOPS,
                        "traffic": None}
