@@ -195,7 +195,8 @@ int do_attn(const hstu_layer_desc* d, const hstu_jagged* j, const hstu_kv_cache*
             const void* k, const void* v, const float* pb, const float* tb, float* av, void* ws,
             hipStream_t s) {
   if (d->dtype == HSTU_F32 && c == nullptr && j->num_targets == nullptr &&
-      hstu::attn_train_supported(d->head_dim)) {
+      hstu::attn_train_supported(d->head_dim) &&
+      static_cast<int64_t>(j->max_seq_len) * d->d_model < (int64_t{1} << 31)) {
     // plain causal fp32: the matrix-core kernel
     hstu::BwdAttnArgs ta = make_train_args(d, j, static_cast<const float*>(q), static_cast<const float*>(k),
                                            static_cast<const float*>(v), pb, tb);
@@ -497,6 +498,9 @@ int hstu_layer_bwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
   if (st) return st;
   CHECK(jagged->num_targets == nullptr, HSTU_E_UNSUPPORTED,
         "the backward pass supports plain causal attention (no targets)");
+  CHECK(jagged->total_tokens < (int64_t{1} << 31) &&
+            static_cast<int64_t>(jagged->max_seq_len) * desc->d_model < (int64_t{1} << 31),
+        HSTU_E_UNSUPPORTED, "the backward pass needs total_tokens and max_seq_len * d_model below 2^31");
   CHECK(params && params->w1 && params->w2 && params->pos_bias && params->time_bias, HSTU_E_INVAL,
         "params, w1, w2, pos_bias and time_bias must not be NULL");
   CHECK(grads && grads->dw1 && grads->db1 && grads->dw2 && grads->db2 && grads->dgamma &&

@@ -429,6 +429,8 @@ hipError_t launch_train(K kernel, const BwdAttnArgs& a, hipStream_t s) {
   const int64_t nblk = (static_cast<int64_t>(a.max_seq_len) + 31) / 32;
   const int64_t grid = nblk * a.num_seqs * (a.num_heads / nw);
   if (grid == 0) return hipSuccess;
+  // row offsets inside one sequence are int32
+  if (static_cast<int64_t>(a.max_seq_len) * a.d_model >= (int64_t{1} << 31)) return hipErrorInvalidValue;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(64 * nw), 0, s, a);
   return hipGetLastError();

@@ -278,7 +278,8 @@ size_t hstu_layer_bwd_workspace_size(const hstu_layer_desc *desc, const hstu_jag
  * the position and time tables (each visible pair adds its score gradient,
  * summed over heads, to the entries it read). Recomputes the forward.
  * Supported: dtype HSTU_F32, input_norm 0, plain causal attention
- * (jagged->num_targets NULL, no cache); else HSTU_E_UNSUPPORTED.
+ * (jagged->num_targets NULL, no cache), total_tokens and
+ * max_seq_len * d_model below 2^31; else HSTU_E_UNSUPPORTED.
  * x, dy, dx [T, d] fp32 (dx must not alias x or dy); grads: all eight
  * pointers non-NULL. workspace: device, 256-byte aligned, >=
  * hstu_layer_bwd_workspace_size(). Gradient sums use fp32 atomics, so

@@ -21,12 +21,16 @@ def _rel(g, r):
     return float(np.abs(g - r).max() / max(np.abs(r).max(), 1e-6))
 
 
-@pytest.mark.parametrize("lengths,d,H,alpha", [
-    ([1, 5, 64, 65, 0, 130], 64, 2, 0.7),      # head_dim 32, ragged tails, an empty sequence
-    ([200, 3, 64], 128, 2, 1.0),               # head_dim 64
-    (None, None, None, None),                  # the 1 x 64 fp32 workload
+@pytest.mark.parametrize("lengths,d,H,alpha,shuffle_ts", [
+    ([1, 5, 64, 65, 0, 130], 64, 2, 0.7, False),   # head_dim 32, ragged tails, an empty sequence
+    ([200, 3, 64], 128, 2, 1.0, False),            # head_dim 64
+    ([100, 33, 257], 512, 8, 1.0, False),          # 8 heads: one 8-wave workgroup per block row
+    ([40, 75, 2], 96, 3, 1.0, False),              # 3 heads of 32: a 3-wave workgroup
+    ([65, 1, 31], 1024, 16, 0.5, False),           # 16 heads: two head groups per block row
+    ([90, 140], 128, 2, 1.0, True),                # timestamps out of order: buckets change often
+    (None, None, None, None, False),               # the 1 x 64 fp32 workload
 ])
-def test_layer_backward_matches_oracle(gpu_lib, lengths, d, H, alpha):
+def test_layer_backward_matches_oracle(gpu_lib, lengths, d, H, alpha, shuffle_ts):
     import torch
     from hstu_sequential_transducer_jagged_amd import hstu, runner
     if lengths is None:
@@ -34,6 +38,11 @@ def test_layer_backward_matches_oracle(gpu_lib, lengths, d, H, alpha):
     else:
         w = gen.make_custom(lengths, d, H, dtype="f32", seed=61, affine="random")
         w.alpha = alpha
+        if shuffle_ts:
+            rng = np.random.default_rng(63)
+            for b in range(len(lengths)):
+                s0, s1 = int(w.offsets[b]), int(w.offsets[b + 1])
+                w.timestamps[s0:s1] = rng.permutation(w.timestamps[s0:s1])
     d, T = w.d_model, w.total_tokens
     p = w.layers[0]
     dy = np.random.default_rng(62).standard_normal((T, d)).astype(np.float32)

@@ -73,13 +73,13 @@ def test_attn_bf16_uneven_work_lists(gpu_lib):
     assert err < TOL["bf16"]
 
 
-@pytest.mark.parametrize("dh", [32, 64])
-def test_attn_f32_edge_lengths(gpu_lib, dh):
-    w = gen.make_custom(EDGE_LENGTHS, 2 * dh, 2, dtype="f32", seed=200 + dh, n_max=256)
+@pytest.mark.parametrize("dh,H", [(32, 2), (64, 2), (64, 8), (32, 3), (64, 16), (64, 1)])
+def test_attn_f32_edge_lengths(gpu_lib, dh, H):
+    w = gen.make_custom(EDGE_LENGTHS, H * dh, H, dtype="f32", seed=200 + dh + H, n_max=256)
     u, v, q, k = _qkv_inputs(w, "f32")
     got = _run_attn(gpu_lib, w, "f32", q, k, v)
     p = w.layers[0]
-    ref = oracle.attention(q, k, v, w.offsets, w.timestamps, p.pos_bias, p.time_bias, 2, w.n_max)
+    ref = oracle.attention(q, k, v, w.offsets, w.timestamps, p.pos_bias, p.time_bias, H, w.n_max)
     err = row_rel_err(got, ref)
     print(f"attn f32 dh={dh}: {err:.3e}")
     assert err < TOL["f32"]
