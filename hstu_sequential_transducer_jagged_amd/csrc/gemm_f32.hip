@@ -219,6 +219,9 @@ hipError_t launch_gemm_f32_mma(const GemmF32Args& a, int epi, int splits, hipStr
   const int64_t gm = (static_cast<int64_t>(a.M) + kBM - 1) / kBM;
   if (gm > 65535) return hipErrorNotSupported;
   dim3 grid((a.N + kBN - 1) / kBN, static_cast<unsigned>(gm), z);
+  // under 8 workgroups each K chunk's load latency is exposed: the plain
+  // kernels, with many small blocks, are faster there
+  if (static_cast<int64_t>(grid.x) * grid.y * grid.z < 8) return hipErrorNotSupported;
   if (epi == 0) return dispatch<0>(p, grid, s);
   if (epi == 1) return dispatch<1>(p, grid, s);
   if (!(p.sak == 1 && p.sbk == 1)) return hipErrorNotSupported;

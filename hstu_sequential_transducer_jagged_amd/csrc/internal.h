@@ -88,7 +88,8 @@ struct OutArgs {
 //        C[m, n] = acc + bias[n] when C is set (split % 16 == 0, N <= 4 split).
 // Returns hipErrorNotSupported, launching nothing, for operand layouts it does
 // not take (each operand needs its k index or its m / n index contiguous,
-// the other stride a multiple of 4, 16-byte aligned bases).
+// the other stride a multiple of 4, 16-byte aligned bases) and for products
+// of fewer than 8 workgroups (128 x 128 tiles times K chunks).
 struct GemmF32Args {
   const float* A;
   int64_t sam, sak;

@@ -84,3 +84,36 @@ def test_layer_backward_empty_batch_zeroes_gradients(gpu_lib):
     hstu.hstu_layer_bwd(desc, params, jag, None, None, None, grads, None)
     torch.cuda.synchronize()
     assert all(float(t.abs().max()) == 0.0 for t in g)
+
+
+def test_layer_backward_long_sequence_tables_balance(gpu_lib):
+    """A sequence longer than the LDS accumulator of position gradients
+    (differences up to 16 384): the excess goes to global memory directly.
+    Every visible pair adds its score gradient once to the position table and
+    once to the time table, so the two tables' sums agree, and the entries
+    beyond the accumulator receive their share."""
+    import torch
+    from hstu_sequential_transducer_jagged_amd import hstu, runner
+    L = 16500
+    w = gen.make_custom([L], 32, 1, dtype="f32", seed=71, n_max=L)
+    d, T = w.d_model, w.total_tokens
+    dy = np.random.default_rng(72).standard_normal((T, d)).astype(np.float32)
+    dw = runner.DeviceWorkload(w)
+    lay = dw.layers[0]
+    g = [torch.empty(n, dtype=torch.float32, device="cuda") for n in
+         (4 * d * d, 4 * d, d * d, d, d, d, 2 * w.n_max - 1, w.num_time_buckets)]
+    grads = hstu.make_grads(*g)
+    dx = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    ws = hstu.workspace_tensor(hstu.hstu_layer_bwd_workspace_size(lay.desc, dw.jagged))
+    hstu.hstu_layer_bwd(lay.desc, lay.params, dw.jagged, dw.x, f32(dy), dx, grads, ws)
+    torch.cuda.synchronize()
+    dpos = to_np(g[6]).astype(np.float64)
+    dtime = to_np(g[7]).astype(np.float64)
+    assert np.all(np.isfinite(dpos)) and np.all(np.isfinite(dtime))
+    center = w.n_max - 1
+    # differences below zero are never visible
+    assert np.all(dpos[:center] == 0.0)
+    scale = np.abs(dpos).sum()
+    assert abs(dpos.sum() - dtime.sum()) <= 1e-4 * scale, (dpos.sum(), dtime.sum(), scale)
+    # differences 16 384 .. L-1 exist and received gradient
+    assert np.count_nonzero(dpos[center + 16384:center + L]) > 0
