@@ -19,7 +19,7 @@
 // in the order that suits its layout: float4 runs along the head dimension
 // for the row-per-lane operands, and whole rows across the lanes for the
 // dimension-per-lane ones. A workgroup holds one wave per head of the same
-// 32 rows, so its waves have identical trip counts.
+// 32 rows (up to four heads), so its waves have identical trip counts.
 #include "common.h"
 #include "internal.h"
 
@@ -29,6 +29,13 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2eT = 1.4426950408889634f;
+// Waves (heads) per workgroup, at most. Four-wave workgroups let two or three
+// of them share a CU and drift out of step, so that one's matrix work
+// overlaps another's pointwise step; with one eight-wave workgroup per CU
+// the forward ran 18 % and the backward 10 % slower.
+// (The kernels keep a 512-thread launch bound all the same: it holds them to
+// 256 registers, two waves per SIMD.)
+constexpr int kMaxWaves = 4;
 // Entries of the workgroup's LDS accumulator of position-bias gradients
 // (position differences -31 .. kPosCap-32); larger differences are added to
 // global memory directly.
@@ -140,8 +147,8 @@ __global__ __launch_bounds__(512) void attn_train_q_kernel(BwdAttnArgs a) {
   constexpr int NU = DH / 16, NCT = DH / 16;
   __shared__ float s_gpos[FWD ? 1 : kPosCap];
   __shared__ float s_tval[64], s_tgrad[64];
-  __shared__ float s_win[8][64];
-  __shared__ int64_t s_ts[8][32];
+  __shared__ float s_win[kMaxWaves][64];
+  __shared__ int64_t s_ts[kMaxWaves][32];
   const int nw = blockDim.x >> 6;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lc = lane & 15, g = lane >> 4;
   const Place pl = place(a, true, wave, nw);
@@ -293,12 +300,12 @@ template <int DH>
 __global__ __launch_bounds__(512) void attn_train_kv_kernel(BwdAttnArgs a) {
   constexpr int NU = DH / 16, NCT = DH / 16;
   __shared__ float s_tval[64];
-  __shared__ float s_win[8][64];
-  __shared__ int64_t s_ts[8][32];
+  __shared__ float s_win[kMaxWaves][64];
+  __shared__ int64_t s_ts[kMaxWaves][32];
   // V rows of each wave, parked in LDS by the lane that reads them back
   // (registers are the limit here); 16-byte padding per lane
-  __shared__ float4 s_v[8][2][NU][64 + 1];
-  __shared__ int64_t s_kts[8][32];
+  __shared__ float4 s_v[kMaxWaves][2][NU][64 + 1];
+  __shared__ int64_t s_kts[kMaxWaves][32];
   const int nw = blockDim.x >> 6;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lc = lane & 15, g = lane >> 4;
   const Place pl = place(a, false, wave, nw);
@@ -416,9 +423,9 @@ __global__ __launch_bounds__(512) void attn_train_kv_kernel(BwdAttnArgs a) {
   store_tiles<NCT>(a.dv + (s0 + j0 + lc) * a.ld_dz + pl.h * DH, a.ld_dz, dv, g, 1.0f, kv[0], kv[1]);
 }
 
-// Waves per workgroup: the largest divisor of num_heads up to 8.
+// Waves per workgroup: the largest divisor of num_heads up to kMaxWaves.
 int waves_for(int num_heads) {
-  for (int w = 8; w > 1; --w)
+  for (int w = kMaxWaves; w > 1; --w)
     if (num_heads % w == 0) return w;
   return 1;
 }
