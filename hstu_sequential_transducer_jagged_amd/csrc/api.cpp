@@ -486,10 +486,18 @@ size_t hstu_layer_bwd_workspace_size(const hstu_layer_desc* desc, const hstu_jag
   return 17 * td + round256(T * sizeof(float));
 }
 
-int hstu_layer_bwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
-                   const hstu_jagged* jagged, const void* x, const void* dy, void* dx,
-                   const hstu_layer_grads* grads, void* workspace, size_t workspace_bytes,
-                   void* stream) {
+namespace {
+
+// The fp32 training layer. kTrainFull: forward recompute, then the backward
+// (hstu_layer_bwd). kTrainForward: the forward with Y, keeping in the
+// workspace what the backward reads (hstu_layer_fwd_train). kTrainBackward:
+// the backward from such a workspace (hstu_layer_bwd_after_fwd).
+enum { kTrainFull = 0, kTrainForward = 1, kTrainBackward = 2 };
+
+int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, const hstu_jagged* jagged,
+                const void* x, const void* dy, void* dx, void* y, const hstu_layer_grads* grads,
+                void* workspace, size_t workspace_bytes, void* stream, int mode) {
+  const bool fwd = mode != kTrainBackward, bwd = mode != kTrainForward;
   int st = check_desc(desc);
   if (st) return st;
   CHECK(desc->dtype == HSTU_F32, HSTU_E_UNSUPPORTED, "the backward pass supports dtype f32");
@@ -503,17 +511,23 @@ int hstu_layer_bwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
         HSTU_E_UNSUPPORTED, "the backward pass needs total_tokens and max_seq_len * d_model below 2^31");
   CHECK(params && params->w1 && params->w2 && params->pos_bias && params->time_bias, HSTU_E_INVAL,
         "params, w1, w2, pos_bias and time_bias must not be NULL");
-  CHECK(grads && grads->dw1 && grads->db1 && grads->dw2 && grads->db2 && grads->dgamma &&
-            grads->dbeta && grads->dpos && grads->dtime,
+  CHECK(!bwd || (grads && grads->dw1 && grads->db1 && grads->dw2 && grads->db2 && grads->dgamma &&
+                  grads->dbeta && grads->dpos && grads->dtime),
         HSTU_E_INVAL, "every gradient pointer must be set");
   const int64_t T = jagged->total_tokens;
   const int d = desc->d_model;
   const bool empty = T == 0 || jagged->num_seqs == 0;
   if (!empty) {
-    CHECK(x && dy && dx, HSTU_E_INVAL, "x/dy/dx must not be NULL");
-    CHECK(dx != x && dx != dy, HSTU_E_INVAL, "dx must not alias x or dy");
-    CHECK(aligned16(x) && aligned16(dy) && aligned16(dx), HSTU_E_INVAL,
-          "x/dy/dx must be 16-byte aligned");
+    if (bwd) {
+      CHECK(x && dy && dx, HSTU_E_INVAL, "x/dy/dx must not be NULL");
+      CHECK(dx != x && dx != dy, HSTU_E_INVAL, "dx must not alias x or dy");
+      CHECK(aligned16(x) && aligned16(dy) && aligned16(dx), HSTU_E_INVAL,
+            "x/dy/dx must be 16-byte aligned");
+    } else {
+      CHECK(x && y, HSTU_E_INVAL, "x/y must not be NULL");
+      CHECK(y != x, HSTU_E_INVAL, "y must not alias x");
+      CHECK(aligned16(x) && aligned16(y), HSTU_E_INVAL, "x/y must be 16-byte aligned");
+    }
     const size_t need = hstu_layer_bwd_workspace_size(desc, jagged);
     CHECK(workspace != nullptr && workspace_bytes >= need, HSTU_E_WORKSPACE,
           "workspace too small: need %zu bytes, got %zu", need, workspace_bytes);
@@ -521,14 +535,16 @@ int hstu_layer_bwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
           "workspace must be 256-byte aligned");
   }
   hipStream_t s = as_stream(stream);
-  // gradients start at zero (also for an empty batch)
-  const struct { float* p; int64_t n; } zero[] = {
-      {grads->dw1, 4LL * d * d}, {grads->db1, 4LL * d}, {grads->dw2, 1LL * d * d}, {grads->db2, d},
-      {grads->dgamma, d}, {grads->dbeta, d}, {grads->dpos, desc->pos_table_len},
-      {grads->dtime, desc->num_time_buckets}};
-  for (const auto& z : zero) {
-    st = device_status(hstu::launch_fill_zero(z.p, z.n, s), "zero fill");
-    if (st) return st;
+  if (bwd) {
+    // gradients start at zero (also for an empty batch)
+    const struct { float* p; int64_t n; } zero[] = {
+        {grads->dw1, 4LL * d * d}, {grads->db1, 4LL * d}, {grads->dw2, 1LL * d * d}, {grads->db2, d},
+        {grads->dgamma, d}, {grads->dbeta, d}, {grads->dpos, desc->pos_table_len},
+        {grads->dtime, desc->num_time_buckets}};
+    for (const auto& z : zero) {
+      st = device_status(hstu::launch_fill_zero(z.p, z.n, s), "zero fill");
+      if (st) return st;
+    }
   }
   if (empty) return ok();
   const size_t td = round256(static_cast<size_t>(T) * d * sizeof(float));
@@ -562,8 +578,10 @@ int hstu_layer_bwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
     st = device_status((expr), what);              \
     if (st) return st;                             \
   } while (0)
-  // forward recompute: Z = X W1^T + b1 and [U V Q K] = SiLU(Z) in one pass
-  {
+  hstu::BwdAttnArgs ba = make_train_args(desc, jagged, Q, K, V, params->pos_bias, params->time_bias);
+  ba.av = AV;
+  // forward: Z = X W1^T + b1 and [U V Q K] = SiLU(Z) in one pass
+  if (fwd) {
     hstu::GemmF32Args g{};
     g.A = X; g.sam = d; g.sak = 1;
     g.B = W1; g.sbk = 1; g.sbn = d;
@@ -580,11 +598,18 @@ int hstu_layer_bwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
       HSTU_TRY(e, "projection");
     }
   }
-  hstu::BwdAttnArgs ba = make_train_args(desc, jagged, Q, K, V, params->pos_bias, params->time_bias);
-  ba.av = AV;
-  HSTU_TRY(hstu::launch_attn_train_fwd(ba, s), "attention forward");
-  HSTU_TRY(hstu::launch_ln_gate_fwd(AV, U, params->ln_gamma, params->ln_beta, NH, RSTD, G, T, d,
-                                    desc->ln_eps, s), "ln/gate forward");
+  if (fwd) {
+    HSTU_TRY(hstu::launch_attn_train_fwd(ba, s), "attention forward");
+    HSTU_TRY(hstu::launch_ln_gate_fwd(AV, U, params->ln_gamma, params->ln_beta, NH, RSTD, G, T, d,
+                                      desc->ln_eps, s), "ln/gate forward");
+  }
+  if (!bwd) {
+    // Y = X + G W2^T + b2
+    HSTU_TRY(hstu::launch_gemm_f32s(G, d, 1, W2, 1, d, static_cast<float*>(y), d, X,
+                                    static_cast<const float*>(params->b2), static_cast<int>(T), d, d, 1, s),
+             "output gemm");
+    return ok();
+  }
   // Y = X + G W2^T + b2
   HSTU_TRY(hstu::launch_gemm_f32s(DY, d, 1, W2, d, 1, DG, d, nullptr, nullptr, static_cast<int>(T), d, d, 1,
                                   s), "dG gemm");
@@ -608,6 +633,31 @@ int hstu_layer_bwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
                                   static_cast<int>(T), d, d4, 1, s), "dX gemm");
 #undef HSTU_TRY
   return ok();
+}
+
+}  // namespace
+
+int hstu_layer_bwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
+                   const hstu_jagged* jagged, const void* x, const void* dy, void* dx,
+                   const hstu_layer_grads* grads, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  return layer_train(desc, params, jagged, x, dy, dx, nullptr, grads, workspace, workspace_bytes, stream,
+                     kTrainFull);
+}
+
+int hstu_layer_fwd_train(const hstu_layer_desc* desc, const hstu_layer_params* params,
+                         const hstu_jagged* jagged, const void* x, void* y, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return layer_train(desc, params, jagged, x, nullptr, nullptr, y, nullptr, workspace, workspace_bytes,
+                     stream, kTrainForward);
+}
+
+int hstu_layer_bwd_after_fwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
+                             const hstu_jagged* jagged, const void* x, const void* dy, void* dx,
+                             const hstu_layer_grads* grads, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return layer_train(desc, params, jagged, x, dy, dx, nullptr, grads, workspace, workspace_bytes, stream,
+                     kTrainBackward);
 }
 
 int hstu_embed_fwd(int64_t T, int32_t d_model, int32_t dtype, const void* item_emb,

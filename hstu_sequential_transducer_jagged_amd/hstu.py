@@ -32,6 +32,7 @@ EXPORTS = ("hstu_abi_version", "hstu_last_error", "hstu_proj_fwd", "hstu_attn_wo
            "hstu_kv_cache_concat", "hstu_stochastic_length", "hstu_gather_rows",
            "hstu_out_fwd", "hstu_layer_workspace_size",
            "hstu_layer_fwd", "hstu_layer_bwd_workspace_size", "hstu_layer_bwd",
+           "hstu_layer_fwd_train", "hstu_layer_bwd_after_fwd",
            "hstu_embed_fwd", "hstu_check_inputs")
 
 
@@ -107,6 +108,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "hstu_layer_fwd": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "hstu_layer_bwd_workspace_size": (ctypes.c_size_t, [P, P]),
         "hstu_layer_bwd": (ctypes.c_int, [P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "hstu_layer_fwd_train": (ctypes.c_int, [P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "hstu_layer_bwd_after_fwd": (ctypes.c_int, [P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "hstu_embed_fwd": (ctypes.c_int, [i64, i32, i32, P, i64, P, i32, P, P, P, P]),
         "hstu_check_inputs": (ctypes.c_int, [P, P, P, P]),
     }
@@ -273,6 +276,20 @@ def hstu_layer_bwd(desc, params, jagged, x, dy, dx, grads, workspace, stream=Non
                                  _ref(grads), ptr(workspace),
                                  0 if workspace is None else workspace.numel() * workspace.element_size(),
                                  stream if stream is not None else current_stream()))
+
+
+def hstu_layer_fwd_train(desc, params, jagged, x, y, workspace, stream=None) -> None:
+    _check(load().hstu_layer_fwd_train(_ref(desc), _ref(params), _ref(jagged), ptr(x), ptr(y),
+                                       ptr(workspace),
+                                       0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                       stream if stream is not None else current_stream()))
+
+
+def hstu_layer_bwd_after_fwd(desc, params, jagged, x, dy, dx, grads, workspace, stream=None) -> None:
+    _check(load().hstu_layer_bwd_after_fwd(_ref(desc), _ref(params), _ref(jagged), ptr(x), ptr(dy),
+                                           ptr(dx), _ref(grads), ptr(workspace),
+                                           0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                           stream if stream is not None else current_stream()))
 
 
 def hstu_embed_fwd(T, d_model, dtype, item_emb, action_emb, item_ids, actions, x,

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 4
+#define HSTU_ABI_VERSION 5
 
 typedef enum {
   HSTU_OK = 0,
@@ -288,6 +288,25 @@ int hstu_layer_bwd(const hstu_layer_desc *desc, const hstu_layer_params *params,
                    const hstu_jagged *jagged, const void *x, const void *dy, void *dx,
                    const hstu_layer_grads *grads, void *workspace, size_t workspace_bytes,
                    void *stream);
+
+/* A training step in two calls, without the backward's forward recompute.
+ * hstu_layer_fwd_train: the layer forward in fp32 (same equations and
+ * support as hstu_layer_bwd: HSTU_F32, no input_norm, plain causal
+ * attention), writing y [T, d] (must not alias x) and keeping in `workspace`
+ * (hstu_layer_bwd_workspace_size() bytes, 256-byte aligned) the activations
+ * the backward reads: Z, U, V, Q, K, AV, the normalised AV, 1/sigma and G.
+ * hstu_layer_bwd_after_fwd: the backward of hstu_layer_bwd, reading those
+ * activations instead of recomputing them; desc, params, jagged, x and the
+ * workspace must be those of the hstu_layer_fwd_train call, with the
+ * workspace untouched in between (it is not checked). Same errors as
+ * hstu_layer_bwd. */
+int hstu_layer_fwd_train(const hstu_layer_desc *desc, const hstu_layer_params *params,
+                         const hstu_jagged *jagged, const void *x, void *y, void *workspace,
+                         size_t workspace_bytes, void *stream);
+int hstu_layer_bwd_after_fwd(const hstu_layer_desc *desc, const hstu_layer_params *params,
+                             const hstu_jagged *jagged, const void *x, const void *dy, void *dx,
+                             const hstu_layer_grads *grads, void *workspace, size_t workspace_bytes,
+                             void *stream);
 
 /* Action-oriented token embedding, "6.2. HSTU的工程突破" eq. 6.2.2:
  *   x[t] = item_emb[item_ids[t]] + action_emb[actions[t]]

@@ -35,7 +35,7 @@ def test_header_declares_the_binding_exports():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.hstu_abi_version() == 4
+    assert lib.hstu_abi_version() == 5
 
 
 def _desc(**kw):
@@ -209,6 +209,32 @@ def test_backward_validates(lib):
     assert call(f, p=None) == hstu.HSTU_E_INVAL
     assert call(f, dx=FAKE) == hstu.HSTU_E_INVAL                     # dx aliases x
     assert call(f, wsb=ws - 1) == hstu.HSTU_E_WORKSPACE
+
+
+def test_train_pair_validates(lib):
+    """hstu_layer_fwd_train and hstu_layer_bwd_after_fwd take what
+    hstu_layer_bwd takes, and refuse the same layers on the host."""
+    P = ctypes.c_void_p
+    f = hstu.make_desc(64, 2, hstu.HSTU_F32, 255)
+    params = hstu.LayerParams(FAKE, None, FAKE, None, None, None, FAKE, FAKE)
+    grads = hstu.LayerGrads(*([FAKE] * 8))
+    jag = _jag()
+    ws = lib.hstu_layer_bwd_workspace_size(ctypes.byref(f), ctypes.byref(jag))
+    fwd = lambda desc, y=FAKE + 4096, wsb=ws, p=params: lib.hstu_layer_fwd_train(
+        ctypes.byref(desc), ctypes.byref(p) if p else None, ctypes.byref(jag), P(FAKE), P(y), P(FAKE), wsb,
+        None)
+    assert fwd(_desc()) == hstu.HSTU_E_UNSUPPORTED                  # bf16
+    assert fwd(hstu.make_desc(64, 2, hstu.HSTU_F32, 255, input_norm=True)) == hstu.HSTU_E_UNSUPPORTED
+    assert fwd(f, y=FAKE) == hstu.HSTU_E_INVAL                       # y aliases x
+    assert fwd(f, y=None) == hstu.HSTU_E_INVAL
+    assert fwd(f, p=None) == hstu.HSTU_E_INVAL
+    assert fwd(f, wsb=ws - 1) == hstu.HSTU_E_WORKSPACE
+    bwd = lambda desc, g=grads, dx=FAKE + 4096: lib.hstu_layer_bwd_after_fwd(
+        ctypes.byref(desc), ctypes.byref(params), ctypes.byref(jag), P(FAKE), P(FAKE + 8192), P(dx),
+        ctypes.byref(g) if g else None, P(FAKE), ws, None)
+    assert bwd(_desc()) == hstu.HSTU_E_UNSUPPORTED
+    assert bwd(f, g=None) == hstu.HSTU_E_INVAL
+    assert bwd(f, dx=FAKE) == hstu.HSTU_E_INVAL
 
 
 def test_binding_raises_with_message(lib):

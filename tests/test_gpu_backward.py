@@ -117,3 +117,36 @@ def test_layer_backward_long_sequence_tables_balance(gpu_lib):
     assert abs(dpos.sum() - dtime.sum()) <= 1e-4 * scale, (dpos.sum(), dtime.sum(), scale)
     # differences 16 384 .. L-1 exist and received gradient
     assert np.count_nonzero(dpos[center + 16384:center + L]) > 0
+
+
+def test_training_step_in_two_calls(gpu_lib):
+    """hstu_layer_fwd_train gives the layer's Y and leaves the activations in
+    the workspace; hstu_layer_bwd_after_fwd then gives the gradients of
+    hstu_layer_bwd without recomputing the forward."""
+    import torch
+    from hstu_sequential_transducer_jagged_amd import hstu, runner
+    w = gen.make_custom([300, 7, 129], 256, 4, dtype="f32", seed=81, affine="random")
+    d, T = w.d_model, w.total_tokens
+    p = w.layers[0]
+    dy = np.random.default_rng(82).standard_normal((T, d)).astype(np.float32)
+    dw = runner.DeviceWorkload(w)
+    lay = dw.layers[0]
+    ws = hstu.workspace_tensor(hstu.hstu_layer_bwd_workspace_size(lay.desc, dw.jagged))
+    y = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    hstu.hstu_layer_fwd_train(lay.desc, lay.params, dw.jagged, dw.x, y, ws)
+    ref_y = oracle.layer(w.x, p, w.offsets, w.timestamps, w.num_heads, w.n_max, w.alpha, w.ln_eps)["y"]
+    assert _rel(to_np(y), ref_y) < TOL_BWD
+    sizes = [4 * d * d, 4 * d, d * d, d, d, d, 2 * w.n_max - 1, w.num_time_buckets]
+    g = [torch.empty(n, dtype=torch.float32, device="cuda") for n in sizes]
+    dx = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    hstu.hstu_layer_bwd_after_fwd(lay.desc, lay.params, dw.jagged, dw.x, f32(dy), dx, hstu.make_grads(*g), ws)
+    torch.cuda.synchronize()
+    ref = oracle.layer_backward(w.x, p, w.offsets, w.timestamps, dy, w.num_heads, w.n_max, w.alpha, w.ln_eps)
+    names = ["dw1", "db1", "dw2", "db2", "dgamma", "dbeta", "dpos", "dtime"]
+    got = {"dx": to_np(dx), **{k: to_np(t) for k, t in zip(names, g)}}
+    got["dw1"] = got["dw1"].reshape(4 * d, d)
+    got["dw2"] = got["dw2"].reshape(d, d)
+    errs = {k: _rel(got[k], ref[k]) for k in got}
+    print("two calls", {k: f"{v:.1e}" for k, v in errs.items()})
+    for k, e in errs.items():
+        assert e < TOL_BWD, (k, e)
