@@ -34,9 +34,13 @@ __device__ __forceinline__ float comp4(const float4& v, int e) {
 }
 
 // One operand chunk: rows [row0, row0 + 128) x k [k0, k0 + 16) of
-// X[row][k] = P[row * s_row + k * s_k], two float4 per thread, zero outside
-// rows < nrows and k < kend. KC: s_k == 1 (float4 along k); else s_row == 1
-// (float4 along rows).
+// X[row][k] = P[row * s_row + k * s_k], two float4 of four k values per
+// thread, zero outside rows < nrows and k < kend. KC: s_k == 1 (one float4
+// load); else s_row == 1 (four scalar loads, each coalesced over the lanes'
+// consecutive rows). Either way a thread's float4 is one conflict-free LDS
+// write; transposing four-row float4s with scalar LDS writes instead put 32
+// lanes on 4 banks and cost the products with such operands 4 % of the
+// backward pass.
 template <bool KC>
 __device__ __forceinline__ void chunk_load(const float* __restrict__ P, int64_t s_row, int64_t s_k, int row0,
                                            int nrows, int64_t k0, int64_t kend, int tid, float4 (&r)[2]) {
@@ -55,16 +59,19 @@ __device__ __forceinline__ void chunk_load(const float* __restrict__ P, int64_t 
         r[i] = make_float4(t[0], t[1], t[2], t[3]);
       }
     } else {
-      const int64_t k = k0 + (idx >> 5);
-      const int row = row0 + 4 * (idx & 31);
-      if (k < kend && row + 3 < nrows) {
-        r[i] = *reinterpret_cast<const float4*>(P + row + k * s_k);
-      } else {
-        float t[4];
+      // four k values of one row: each is a coalesced scalar load across the
+      // lanes (consecutive rows), and the float4 goes to LDS in one write
+      const int row = row0 + (idx & 127);
+      const int64_t k = k0 + 4 * (idx >> 7);
+      float t[4];
+      if (row < nrows && k + 3 < kend) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) t[e] = (k < kend && row + e < nrows) ? P[row + e + k * s_k] : 0.0f;
-        r[i] = make_float4(t[0], t[1], t[2], t[3]);
+        for (int e = 0; e < 4; ++e) t[e] = P[row + (k + e) * s_k];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[e] = (row < nrows && k + e < kend) ? P[row + (k + e) * s_k] : 0.0f;
       }
+      r[i] = make_float4(t[0], t[1], t[2], t[3]);
     }
   }
 }
@@ -77,11 +84,7 @@ __device__ __forceinline__ void chunk_store(float (*S)[kLd], int tid, const floa
     if constexpr (KC) {
       *reinterpret_cast<float4*>(&S[idx >> 2][4 * (idx & 3)]) = r[i];
     } else {
-      const int kk = idx >> 5, row = 4 * (idx & 31);
-      S[row][kk] = r[i].x;
-      S[row + 1][kk] = r[i].y;
-      S[row + 2][kk] = r[i].z;
-      S[row + 3][kk] = r[i].w;
+      *reinterpret_cast<float4*>(&S[idx & 127][4 * (idx >> 7)]) = r[i];
     }
   }
 }
