@@ -198,6 +198,9 @@ def run_layer(args):
     y2 = mk()
     ms_step = timed(lambda: hstu.hstu_layer_fwd(desc, lay.params, jag, None, x, y2, None, None, ws, sh),
                     stream, args.warmup, K)
+    # the same step replayed from a HIP graph (host launch cost removed)
+    graph, y3 = runner.capture(runner.layer_forward, dw, x, 0)
+    ms_graph = timed(graph.replay, stream, args.warmup, K)
 
     # breakdown: the four per-kernel entry points, HIP events between them
     for _ in range(args.warmup):
@@ -275,6 +278,8 @@ def run_layer(args):
         "step_entry_point": "hstu_layer_fwd",
         "separate_entry_points_ms_per_step": ms_separate,
         "separate_entry_points_match_bitwise": same,
+        "graph_ms_per_step": ms_graph,
+        "graph_matches_bitwise": bool(torch.equal(y3, y2)),
         "kernels": kernels,
     }
     if calib is not None:

@@ -135,6 +135,26 @@ def stack_forward(dw: DeviceWorkload, x=None, return_all: bool = False):
     return outs if return_all else h
 
 
+def capture(fn, *args, **kwargs):
+    """Records fn(*args, **kwargs), a sequence of the library's calls on the
+    current stream, into a HIP graph (torch.cuda.CUDAGraph), after one eager
+    run on a side stream. Returns (graph, result): graph.replay() re-runs
+    every kernel with the same device pointers, so `result` (and any buffer fn
+    allocated) holds each replay's output. The calls must not synchronise
+    (hstu_check_inputs does); the library's entry points allocate nothing and
+    clear memory with kernels, never with memset nodes."""
+    torch = _torch()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(*args, **kwargs)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = fn(*args, **kwargs)
+    return graph, out
+
+
 class RankingPlan:
     """Candidate rows re-laid out micro-batch-major so that each micro-batch
     is one contiguous jagged batch: [mb0: user0 rows, user1 rows, ...; mb1:
