@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--stochastic-length", type=float, default=None, metavar="ALPHA",
                     help="layer workloads: sample the batch with Stochastic Length (N = n_max) and "
                          "time the layer over the sampled batch against the full one")
+    ap.add_argument("--diag-lengths", default=None,
+                    help="attention diagnostic: COUNTxLENGTH (e.g. 16x8192, 1x8192), the workload-2 layer "
+                         "(bf16, d_model 512, 8 heads, same seeded recipe) on sequences of those lengths")
     ap.add_argument("--backward", action="store_true",
                     help="layer workloads: time the fp32 layer backward pass (hstu_layer_bwd) on the "
                          "workload's shape in fp32")
@@ -146,7 +149,12 @@ def run_layer(args):
     from hstu_inputs import gen
     from hstu_sequential_transducer_jagged_amd import hstu, runner
 
-    w = gen.make_config(args.workload)
+    if args.diag_lengths:
+        cnt, ln = (int(t) for t in args.diag_lengths.lower().split("x"))
+        w = gen.make_custom([ln] * cnt, 512, 8, dtype="bf16", seed=1002 + 100_000, n_max=ln,
+                            name="bf16 %d x %d (attention diagnostic) d512 h8" % (cnt, ln))
+    else:
+        w = gen.make_config(args.workload)
     lin = tuple(float(t) for t in args.linear_bias.split(",")) if args.linear_bias else None
     for p in w.layers:
         if args.input_norm:
@@ -262,7 +270,8 @@ def run_layer(args):
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded; no dataset)",
-        "config": {"workload": gen.CONFIG_NAMES[args.workload], "total_tokens": T,
+        "config": {"workload": w.name if args.diag_lengths else gen.CONFIG_NAMES[args.workload],
+                   "total_tokens": T,
                    "num_seqs": w.num_seqs, "max_seq_len": w.max_seq_len, "d_model": d,
                    "num_heads": H, "head_dim": d // H, "visible_pairs": P,
                    "input_norm": bool(args.input_norm),
@@ -270,7 +279,8 @@ def run_layer(args):
         "roofline": {"kernel": "attn_" + w.dtype, "bound": "mfma",
                      "achieved": attn_tflops, "peak": peak, "unit": "TFLOP/s",
                      "frac": attn_tflops / peak,
-                     "traffic": traffic_record("attn_bf16", src) if args.workload == 2 else None,
+                     "traffic": (traffic_record("attn_bf16", src)
+                                 if args.workload == 2 and not args.diag_lengths else None),
                      "algorithmic_flop_per_launch": attn_flop,
                      "avg_launch_ms": attn_ms},
         "attn_tflops": attn_tflops,
