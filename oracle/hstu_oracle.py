@@ -179,19 +179,24 @@ def _positions(L: int, m: int, n_cache: int) -> np.ndarray:
     return p
 
 
-def _visibility(L: int, m: int, n_cache: int, rows: np.ndarray) -> np.ndarray:
+def _visibility(L: int, m: int, n_cache: int, rows: np.ndarray, target_no_self: bool = False) -> np.ndarray:
     """Boolean [len(rows), n_cache + L] mask of visible keys for the given
-    own-token query rows."""
+    own-token query rows. target_no_self: a target (one of the last m
+    tokens) does not see itself either, only the history and the
+    non-targets (the literal reading of [GR-7.1] §7.1.5's M-FALCON: a
+    candidate attends to the user history)."""
     j = np.arange(L)
     i = rows[:, None]
-    own = (j[None, :] <= i) & ((j[None, :] < L - m) | (j[None, :] == i))
+    self_ok = (j[None, :] == i) & ~(target_no_self & (i >= L - m))
+    own = (j[None, :] <= i) & ((j[None, :] < L - m) | self_ok)
     cache = np.ones((rows.shape[0], n_cache), dtype=bool)
     return np.concatenate([cache, own], axis=1)
 
 
 def attention(q, k, v, offsets, timestamps, pos_bias, time_bias, num_heads: int,
               n_max: int, alpha: float = 1.0, num_targets=None, cache=None,
-              rows=None, row_chunk: int = 2048, linear_bias=None, num_time_buckets: int = 32):
+              rows=None, row_chunk: int = 2048, linear_bias=None, num_time_buckets: int = 32,
+              target_no_self: bool = False):
     """Spatial aggregation, per head h of every sequence b:
 
         AV_h = (SiLU(alpha * Q_h K_h^T + rab_{p,t}) * Mask) V_h
@@ -211,6 +216,7 @@ def attention(q, k, v, offsets, timestamps, pos_bias, time_bias, num_heads: int,
     linear_bias: None (rab from the tables), or (m_p, m_t): rab is then
           genrank_bias() of every pair, evaluated directly with
           ``num_time_buckets`` buckets; the tables are not used.
+    target_no_self: targets do not see themselves (_visibility).
     Returns AV [T or len(rows), d] float64.
     """
     q = np.asarray(q, F64)
@@ -255,7 +261,7 @@ def attention(q, k, v, offsets, timestamps, pos_bias, time_bias, num_heads: int,
             qrows = want[csel] - s                      # own-token indices
             dp = own_p[qrows][:, None] - key_p[None, :]
             dt = timestamps[s + qrows][:, None] - key_t[None, :]
-            mask = _visibility(L, m, nc, qrows)
+            mask = _visibility(L, m, nc, qrows, target_no_self)
             if linear_bias is not None:
                 rab = genrank_bias(dp, dt, linear_bias[0], linear_bias[1], nb)
             else:

@@ -209,6 +209,60 @@ def test_attention_bruteforce_targets_and_cache():
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
 
 
+def test_attention_targets_without_self_closed_forms():
+    """target_no_self: Q = K = 0 and rab == c. With no cache, a sequence of
+    targets only sees nothing (AV = 0); with a cache, every target sees just
+    the cache, AV = SiLU(c) * sum of the cache's V rows; non-targets keep
+    their causal sums."""
+    w = _tiny([5, 4], d=4, H=1, seed=3)
+    p = w.layers[0]
+    p.pos_bias[:] = 0.6
+    p.time_bias[:] = 0.0
+    c = float(p.pos_bias[0])      # the table's (float32) value
+    z = np.zeros((w.total_tokens, 4))
+    v = np.random.default_rng(4).standard_normal((w.total_tokens, 4))
+    m = np.array([5, 2])          # sequence 0: all targets; sequence 1: 2 non-targets, 2 targets
+    got = oracle.attention(z, z, v, w.offsets, w.timestamps, p.pos_bias, p.time_bias, 1, w.n_max,
+                           num_targets=m, target_no_self=True)
+    sc = c / (1 + math.exp(-c))
+    assert np.all(got[0:5] == 0.0)
+    np.testing.assert_allclose(got[5], sc * v[5], rtol=1e-14)
+    np.testing.assert_allclose(got[6], sc * (v[5] + v[6]), rtol=1e-14)
+    np.testing.assert_allclose(got[7], sc * (v[5] + v[6]), rtol=1e-14)   # targets: non-targets only
+    np.testing.assert_allclose(got[8], sc * (v[5] + v[6]), rtol=1e-14)
+    hv = np.random.default_rng(5).standard_normal((3, 4))
+    cache = dict(k=np.zeros((3, 4)), v=hv, offsets=np.array([0, 3, 3]),
+                 timestamps=np.array([1, 2, 3], np.int64))
+    got = oracle.attention(z, z, v, w.offsets, w.timestamps, p.pos_bias, p.time_bias, 1, w.n_max,
+                           num_targets=m, cache=cache, target_no_self=True)
+    np.testing.assert_allclose(got[0:5], np.tile(sc * hv.sum(axis=0), (5, 1)), rtol=1e-14)
+
+
+def test_attention_targets_without_self_drop_the_self_term():
+    """A target's output without itself is its output with itself minus
+    SiLU(S_ii) v_i, S_ii = alpha q_i.k_i + pos_bias[center] + time_bias[0]
+    (targets share a position, and the time difference to itself is 0);
+    other rows are unchanged."""
+    w = _tiny([6, 7], d=8, H=2, seed=9, n_max=16)
+    p = w.layers[0]
+    u, v, q, k = _qkv(w)
+    m = np.array([3, 7])
+    a = oracle.attention(q, k, v, w.offsets, w.timestamps, p.pos_bias, p.time_bias, 2, w.n_max,
+                         alpha=0.8, num_targets=m)
+    b = oracle.attention(q, k, v, w.offsets, w.timestamps, p.pos_bias, p.time_bias, 2, w.n_max,
+                         alpha=0.8, num_targets=m, target_no_self=True)
+    targets = {3, 4, 5} | set(range(6, 13))
+    for i in range(w.total_tokens):
+        if i not in targets:
+            np.testing.assert_array_equal(a[i], b[i])
+            continue
+        for h in range(2):
+            cols = slice(4 * h, 4 * h + 4)
+            s_ii = 0.8 * float(np.dot(q[i, cols], k[i, cols])) + float(p.pos_bias[w.n_max - 1]) + float(p.time_bias[0])
+            self_term = s_ii / (1 + math.exp(-s_ii)) * v[i, cols]
+            np.testing.assert_allclose(b[i, cols], a[i, cols] - self_term, rtol=1e-12, atol=1e-12)
+
+
 def test_attention_closed_form_zero():
     w = _tiny([7, 3], d=8, H=2)
     p = w.layers[0]
