@@ -92,6 +92,8 @@ int check_desc(const hstu_layer_desc* d) {
         "num_time_buckets must be in [1, 64] (got %d)", d->num_time_buckets);
   CHECK(d->input_norm == 0 || d->input_norm == 1, HSTU_E_INVAL, "input_norm must be 0 or 1 (got %d)",
         d->input_norm);
+  CHECK(d->target_no_self == 0 || d->target_no_self == 1, HSTU_E_INVAL,
+        "target_no_self must be 0 or 1 (got %d)", d->target_no_self);
   return HSTU_OK;
 }
 
@@ -144,6 +146,7 @@ hstu::AttnArgs make_attn_args(const hstu_layer_desc* d, const hstu_jagged* j,
   a.offsets = j->offsets;
   a.ts = j->timestamps;
   a.num_targets = j->num_targets;
+  a.no_self = d->target_no_self;
   a.c_offsets = c ? c->offsets : nullptr;
   a.c_ts = c ? c->timestamps : nullptr;
   a.pos_bias = pb;

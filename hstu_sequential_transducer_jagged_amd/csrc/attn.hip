@@ -110,6 +110,7 @@ __device__ __forceinline__ int key_pos(int kk, int nc, int first_tgt) {
 struct Ctx {
   int64_t s, cs;
   int L, nc, first_tgt, q0, q_hi, nkeys, d, col0, pmin_q, pos_len, pos_center;
+  int no_self;        // targets do not see themselves
   uint32_t tb_lo;     // low word of the block's reference time (minimum timestamp)
   int wide;           // the block's timestamps span >= 2^31 s: 64-bit bucket path
 };
@@ -273,7 +274,8 @@ __device__ __forceinline__ void build_bias(const Ctx& c, const SlotQ<512 / (64 *
         const int kk = kbase + r;
         const int jo = kk - c.nc;
         const bool vis = qi < c.L && kk < c.nkeys &&
-                         (kk < c.nc || (jo <= qi && (jo < c.first_tgt || jo == qi)));
+                         (kk < c.nc ||
+                          (jo <= qi && (jo < c.first_tgt || (jo == qi && !(c.no_self && qi >= c.first_tgt)))));
         int pidx = sq.pq[i] - key_pos(kk, c.nc, c.first_tgt) - w0;
         pidx = pidx < 0 ? 0 : (pidx >= kPosWin ? kPosWin - 1 : pidx);
         float tbv;
@@ -690,6 +692,7 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
   c.L = si.L;
   c.nc = si.nc;
   c.first_tgt = si.L - si.m;
+  c.no_self = a.no_self;
   c.q0 = q0;
   c.q_hi = min(q0 + kBM, si.L);
   c.nkeys = c.nc + c.q_hi;
@@ -1005,7 +1008,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
       const int kk = k0 + r;
       const bool cache = kk < si.nc;
       const int j = kk - si.nc;
-      const bool vis = qvalid && (cache || ((j <= qi) && (j < first_tgt || j == qi)));
+      const bool vis = qvalid && (cache || ((j <= qi) && (j < first_tgt ||
+                                                        (j == qi && !(a.no_self && qi >= first_tgt)))));
       if (!vis) continue;
       float dot = 0.0f;
 #pragma unroll

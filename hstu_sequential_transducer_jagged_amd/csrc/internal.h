@@ -33,6 +33,7 @@ struct AttnArgs {
   int num_seqs;
   int max_seq_len;
   int max_cache_len;
+  int no_self;               // targets do not see themselves
   int64_t total_tokens;      // T
   int* sched;                // bf16 path: work list built by the scheduling pass
   int splits;                // bf16 path: key-range chunks per (sequence, query tile)

@@ -47,7 +47,7 @@ class LayerDesc(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("alpha", ctypes.c_float), ("ln_eps", ctypes.c_float),
                 ("pos_table_len", ctypes.c_int32), ("num_time_buckets", ctypes.c_int32),
-                ("input_norm", ctypes.c_int32)]
+                ("input_norm", ctypes.c_int32), ("target_no_self", ctypes.c_int32)]
 
 
 class Jagged(ctypes.Structure):
@@ -146,9 +146,9 @@ def current_stream() -> int:
 
 def make_desc(d_model: int, num_heads: int, dtype: int, pos_table_len: int,
               alpha: float = 1.0, ln_eps: float = 1e-5, num_time_buckets: int = 32,
-              input_norm: bool = False) -> LayerDesc:
+              input_norm: bool = False, target_no_self: bool = False) -> LayerDesc:
     return LayerDesc(d_model, num_heads, d_model // num_heads, dtype, alpha, ln_eps,
-                     pos_table_len, num_time_buckets, int(bool(input_norm)))
+                     pos_table_len, num_time_buckets, int(bool(input_norm)), int(bool(target_no_self)))
 
 
 def make_jagged(offsets, timestamps, max_seq_len: int, num_targets=None) -> Jagged:

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 5
+#define HSTU_ABI_VERSION 6
 
 typedef enum {
   HSTU_OK = 0,
@@ -84,6 +84,10 @@ typedef struct {
                                LayerNorm (params ln1_gamma/ln1_beta, eps ln_eps) to X,
                                the Norm1 of the block diagram of "万亿参数推荐大模型…"
                                §2.1; the residual still adds the raw X */
+  int32_t target_no_self;   /* 0 (default) or 1: a target then sees the cache and the
+                               non-targets only, not itself (the literal reading of the
+                               M-FALCON mask of "HSTU：Scaling Law 的首次探索" §7.1.5:
+                               a candidate attends to the user history) */
 } hstu_layer_desc;
 
 /* A jagged batch of the call's own tokens. */

@@ -35,7 +35,7 @@ def test_header_declares_the_binding_exports():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.hstu_abi_version() == 5
+    assert lib.hstu_abi_version() == 6
 
 
 def _desc(**kw):

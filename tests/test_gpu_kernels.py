@@ -21,10 +21,10 @@ def _qkv_inputs(w, dtype):
     return [round_like(a, dtype) for a in (u, v, q, k)]
 
 
-def _run_attn(hs, w, dtype, q, k, v, num_targets=None, cache=None, alpha=1.0):
+def _run_attn(hs, w, dtype, q, k, v, num_targets=None, cache=None, alpha=1.0, no_self=False):
     import torch
     desc = hs.make_desc(w.d_model, w.num_heads, hs.HSTU_BF16 if dtype == "bf16" else hs.HSTU_F32,
-                        2 * w.n_max - 1, alpha=alpha)
+                        2 * w.n_max - 1, alpha=alpha, target_no_self=no_self)
     offs, ts = i64(w.offsets), i64(w.timestamps)
     nt = None if num_targets is None else i32(num_targets)
     jag = hs.make_jagged(offs, ts, w.max_seq_len, nt)
@@ -98,9 +98,10 @@ def test_attn_alpha(gpu_lib, dtype, alpha):
     assert row_rel_err(got, ref) < TOL[dtype]
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_attn_targets_and_cache(gpu_lib, dtype):
-    """Own tokens = some non-targets then targets, plus a cached history."""
+@pytest.mark.parametrize("dtype,no_self", [("bf16", False), ("f32", False), ("bf16", True), ("f32", True)])
+def test_attn_targets_and_cache(gpu_lib, dtype, no_self):
+    """Own tokens = some non-targets then targets, plus a cached history;
+    no_self: targets do not see themselves."""
     H = 2
     rng = np.random.default_rng(5)
     w = gen.make_ranking(seed=31, users=5, history=[70, 0, 129, 1, 64],
@@ -120,12 +121,15 @@ def test_attn_targets_and_cache(gpu_lib, dtype):
                        layers=[gen.make_layer_params(
                            {n: np.random.default_rng(i) for i, n in enumerate(
                                ["w1", "w2", "pos", "time"])}, d, w.n_max + 130, dtype)])
-    got = _run_attn(gpu_lib, own, dtype, cq, ck, cv, num_targets=m, cache=cache)
+    got = _run_attn(gpu_lib, own, dtype, cq, ck, cv, num_targets=m, cache=cache, no_self=no_self)
     p = own.layers[0]
     ref = oracle.attention(cq, ck, cv, own.offsets, own.timestamps, p.pos_bias, p.time_bias, H,
-                           own.n_max, num_targets=m, cache=cache)
-    err = row_rel_err(got, ref)
-    print(f"attn {dtype} targets+cache: {err:.3e}")
+                           own.n_max, num_targets=m, cache=cache, target_no_self=no_self)
+    # a target of a user with no history and no self sees nothing: AV = 0
+    empty = np.abs(ref).max(axis=1) == 0
+    assert np.all(got[empty] == 0.0)
+    err = row_rel_err(got[~empty], ref[~empty])
+    print(f"attn {dtype} targets+cache no_self={no_self}: {err:.3e}")
     assert err < TOL[dtype]
 
 
