@@ -713,9 +713,9 @@ def main():
     global SPIN_UP_S
     SPIN_UP_S = args.spin_up_s
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(sequences are independent; see the sharding note in the design notes).",
-              file=sys.stderr)
+        print("bench.py runs on one GPU only: there is no multi-GPU path (the sequences of a "
+              "batch are independent, so a data-parallel split of the forward needs no "
+              "communication between GPUs).", file=sys.stderr)
         sys.exit(2)
     import torch  # noqa: F401  (torch's HIP runtime first, then the library bound to it)
 

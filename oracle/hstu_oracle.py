@@ -14,8 +14,7 @@ cited (by title; section, equation or figure):
 [GENRANK]  "6.2. HSTU的工程突破" (fun-rec, chapter 6.2, GenRank)
 [SA2HSTU]  "从自注意力到 HSTU：解构下一代推荐系统引擎"
 
-Readings taken where the pages leave a step open (each also listed in the
-design notes of the repository):
+Readings taken where the pages leave a step open:
 
 * score scale alpha defaults to 1: the layer equations in [NOTES] §2.1 and
   [SA2HSTU] step 2 carry no 1/sqrt(d) (only [GENRANK] eq. 6.2.3 restates the
