@@ -1,4 +1,4 @@
-"""Device-side drivers that compose the C-ABI entry points.
+"""Helpers that compose the C-ABI entry points on the device.
 
 * ``DeviceWorkload``: uploads a workload's arrays (numpy) into device tensors
   (bf16 or fp32 activations and weights, fp32 tables, int64 offsets and
