@@ -431,6 +431,37 @@ def run_backward(args):
                        "visible_pairs": P})
     rec["forward_fp32_ms"] = ms_fwd
     rec["train_step_two_calls_ms"] = ms_step
+    if args.stochastic_length is not None:
+        # Stochastic Length on the training pass: the sampler's kept rows of
+        # X, dY and the timestamps, gathered on the device, then the same
+        # backward over the sampled batch
+        alpha = float(args.stochastic_length)
+        B = w.num_seqs
+        rng = np.random.default_rng(np.random.SeedSequence(7000 + args.workload))
+        u, keys = rng.random(B), rng.random(T)
+        off, rows = hstu.hstu_stochastic_length(w.offsets, alpha, w.n_max, u, keys)
+        n = int(rows.size)
+        rows_d = torch.from_numpy(rows).to("cuda")
+        off_d = torch.from_numpy(off).to("cuda")
+        xs, dys, dxs = (torch.empty((max(n, 1), d), dtype=torch.float32, device="cuda") for _ in range(3))
+        tss = torch.empty(max(n, 1), dtype=torch.int64, device="cuda")
+        lens = np.diff(off)
+        jag_s = hstu.Jagged(B, int(lens.max()) if B else 0, n, hstu.ptr(off_d), hstu.ptr(tss), None)
+        ws_s = hstu.workspace_tensor(hstu.hstu_layer_bwd_workspace_size(lay.desc, jag_s))
+
+        def gather():
+            hstu.hstu_gather_rows(n, 4 * d, rows_d, T, dw.x, xs, sh)
+            hstu.hstu_gather_rows(n, 4 * d, rows_d, T, dy, dys, sh)
+            hstu.hstu_gather_rows(n, 8, rows_d, T, dw.timestamps, tss, sh)
+
+        ms_gather = timed(gather, stream, args.warmup, args.steps)
+        ms_sl = timed(lambda: hstu.hstu_layer_bwd(lay.desc, lay.params, jag_s, xs, dys, dxs, grads, ws_s, sh),
+                      stream, args.warmup, args.steps)
+        Ps = visible_pairs(off)
+        rec["stochastic_length"] = {"alpha": alpha, "kept_tokens": n, "sparsity_tokens": 1.0 - n / T,
+                                    "sparsity_pairs": 1.0 - Ps / P, "gather_ms": ms_gather,
+                                    "sampled_backward_ms": ms_sl,
+                                    "speedup_vs_full": ms / (ms_sl + ms_gather)}
     rec["backward_over_forward"] = ms / ms_fwd
     rec["algorithmic_flop"] = flop
     rec["executed_flop"] = flop_exec
