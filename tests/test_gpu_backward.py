@@ -150,3 +150,45 @@ def test_training_step_in_two_calls(gpu_lib):
     print("two calls", {k: f"{v:.1e}" for k, v in errs.items()})
     for k, e in errs.items():
         assert e < TOL_BWD, (k, e)
+
+
+def test_layer_backward_over_a_stochastic_length_sample(gpu_lib):
+    """Generative training with Stochastic Length ("HSTU：Scaling Law 的首次
+    探索" §7.1.5): the sampler's rows of X, dY and the timestamps gathered on
+    the device, then the backward over the shorter batch, against the
+    oracle's backward over the same sampled sequences."""
+    import torch
+    from hstu_sequential_transducer_jagged_amd import hstu, runner
+    from tests.helpers import i64
+    w = gen.make_custom([400, 40, 520, 0, 260], 128, 2, dtype="f32", seed=85, affine="random", n_max=520)
+    d, B, T = w.d_model, w.num_seqs, w.total_tokens
+    rng = np.random.default_rng(86)
+    off, rows = hstu.hstu_stochastic_length(w.offsets, 1.6, w.n_max, rng.random(B), rng.random(T))
+    assert rows.size < T
+    n = int(rows.size)
+    dy = rng.standard_normal((T, d)).astype(np.float32)
+    dw = runner.DeviceWorkload(w)
+    lay = dw.layers[0]
+    rows_d, off_d = i64(rows), i64(off)
+    dyt = f32(dy)
+    xs, dys, dxs = (torch.empty((n, d), dtype=torch.float32, device="cuda") for _ in range(3))
+    ts = torch.empty(n, dtype=torch.int64, device="cuda")
+    hstu.hstu_gather_rows(n, 4 * d, rows_d, T, dw.x, xs)
+    hstu.hstu_gather_rows(n, 4 * d, rows_d, T, dyt, dys)
+    hstu.hstu_gather_rows(n, 8, rows_d, T, dw.timestamps, ts)
+    jag = hstu.Jagged(B, int(np.diff(off).max()), n, hstu.ptr(off_d), hstu.ptr(ts), None)
+    sizes = [4 * d * d, 4 * d, d * d, d, d, d, 2 * w.n_max - 1, w.num_time_buckets]
+    g = [torch.empty(k, dtype=torch.float32, device="cuda") for k in sizes]
+    ws = hstu.workspace_tensor(hstu.hstu_layer_bwd_workspace_size(lay.desc, jag))
+    hstu.hstu_layer_bwd(lay.desc, lay.params, jag, xs, dys, dxs, hstu.make_grads(*g), ws)
+    torch.cuda.synchronize()
+    ref = oracle.layer_backward(np.asarray(w.x)[rows], w.layers[0], off, np.asarray(w.timestamps)[rows],
+                                dy[rows], w.num_heads, w.n_max, w.alpha, w.ln_eps)
+    names = ["dw1", "db1", "dw2", "db2", "dgamma", "dbeta", "dpos", "dtime"]
+    got = {"dx": to_np(dxs), **{k: to_np(t) for k, t in zip(names, g)}}
+    got["dw1"] = got["dw1"].reshape(4 * d, d)
+    got["dw2"] = got["dw2"].reshape(d, d)
+    errs = {k: _rel(got[k], ref[k]) for k in got}
+    print("stochastic length backward", n, "of", T, {k: f"{v:.1e}" for k, v in errs.items()})
+    for k, e in errs.items():
+        assert e < TOL_BWD, (k, e)
