@@ -370,7 +370,8 @@ def layer_backward(x, p, offsets, timestamps, dy, num_heads: int, n_max: int,
     targets, no cache), the generative-training setting of [GR-7.1] §7.1.5:
     dX, dW1, db1, dW2, db2, dgamma, dbeta and the gradients of the position
     and time tables (the shared rab: every pair adds its score gradient,
-    summed over heads, to the entry it read). The chain rule applied to the
+    summed over heads, to the entry it read); with ``p.input_norm`` also
+    dln1_gamma and dln1_beta of the input LayerNorm. The chain rule applied to the
     forward of layer() step by step, in float64."""
     x = np.asarray(x, F64)
     dy = np.asarray(dy, F64)
@@ -384,7 +385,17 @@ def layer_backward(x, p, offsets, timestamps, dy, num_heads: int, n_max: int,
     pb, tb = np.asarray(p.pos_bias, F64), np.asarray(p.time_bias, F64)
     nb = tb.shape[0]
     # forward, keeping what the backward needs
-    z = x @ w1.T + (0.0 if p.b1 is None else np.asarray(p.b1, F64))
+    norm1 = bool(getattr(p, "input_norm", False))
+    xin = x
+    if norm1:
+        # the input LayerNorm (Norm1 of [NOTES] §2.1's block diagram) before f1
+        g1 = getattr(p, "ln1_gamma", None)
+        g1 = np.ones(d) if g1 is None else np.asarray(g1, F64)
+        mu1 = x.mean(axis=1, keepdims=True)
+        rstd1 = 1.0 / np.sqrt(((x - mu1) ** 2).mean(axis=1, keepdims=True) + eps)
+        xhat1 = (x - mu1) * rstd1
+        xin = layernorm(x, getattr(p, "ln1_gamma", None), getattr(p, "ln1_beta", None), eps)
+    z = xin @ w1.T + (0.0 if p.b1 is None else np.asarray(p.b1, F64))
     h = silu(z)
     u, v, q, k = h[:, :d], h[:, d:2 * d], h[:, 2 * d:3 * d], h[:, 3 * d:]
     av = np.zeros((T, d))
@@ -441,10 +452,19 @@ def layer_backward(x, p, offsets, timestamps, dy, num_heads: int, n_max: int,
             np.add.at(dtime, bkt[mask], ds[mask])
     # U, V, Q, K = Split(SiLU(Z)), Z = X W1^T + b1
     dz = np.concatenate([du, dv, dq, dk], axis=1) * silu_grad(z)
-    dw1 = dz.T @ x
+    dw1 = dz.T @ xin
     db1 = dz.sum(axis=0)
-    dx = dy + dz @ w1
-    return dict(dx=dx, dw1=dw1, db1=db1, dw2=dw2, db2=db2, dgamma=dgamma, dbeta=dbeta,
+    dxin = dz @ w1
+    extra = {}
+    if norm1:
+        # xin = xhat1 gamma1 + beta1, xhat1 = (x - mean) / sigma over the d features
+        extra["dln1_gamma"] = (dxin * xhat1).sum(axis=0)
+        extra["dln1_beta"] = dxin.sum(axis=0)
+        dxh = dxin * g1
+        dxin = rstd1 * (dxh - dxh.mean(axis=1, keepdims=True)
+                        - xhat1 * (dxh * xhat1).mean(axis=1, keepdims=True))
+    dx = dy + dxin
+    return dict(**extra, dx=dx, dw1=dw1, db1=db1, dw2=dw2, db2=db2, dgamma=dgamma, dbeta=dbeta,
                 dpos=dpos, dtime=dtime)
 
 

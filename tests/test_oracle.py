@@ -830,6 +830,40 @@ def test_layer_backward_matches_central_differences(name):
     assert abs(num - ana) <= 1e-6 * max(1.0, abs(ana)), (name, num, ana)
 
 
+@pytest.mark.parametrize("name", ["x", "w1", "ln1_gamma", "ln1_beta", "time_bias"])
+def test_layer_backward_with_input_norm_matches_central_differences(name):
+    """The same check with the input LayerNorm before f1 (its gamma and beta
+    random): the gradient reaches X through the residual and through Norm1."""
+    import copy
+    w, dy = _bwd_case(5)
+    p = copy.copy(w.layers[0])
+    rng = np.random.default_rng(55)
+    p.input_norm = True
+    p.ln1_gamma = 1.0 + 0.3 * rng.standard_normal(8)
+    p.ln1_beta = 0.2 * rng.standard_normal(8)
+    x = np.asarray(w.x, np.float64)
+    g = oracle.layer_backward(x, p, w.offsets, w.timestamps, dy, w.num_heads, w.n_max, w.alpha,
+                              w.ln_eps)
+    key = {"x": "dx", "w1": "dw1", "ln1_gamma": "dln1_gamma", "ln1_beta": "dln1_beta",
+           "time_bias": "dtime"}[name]
+    base = x if name == "x" else np.asarray(getattr(p, name), np.float64)
+    v = np.random.default_rng(98).standard_normal(base.shape)
+    eps = 1e-5
+
+    def at(t):
+        pp = copy.copy(p)
+        xx = x
+        if name == "x":
+            xx = x + t * v
+        else:
+            setattr(pp, name, base + t * v)
+        return _f(w, xx, pp, dy)
+
+    num = (at(eps) - at(-eps)) / (2 * eps)
+    ana = float((g[key] * v).sum())
+    assert abs(num - ana) <= 1e-6 * max(1.0, abs(ana)), (name, num, ana)
+
+
 def test_layer_backward_linear_in_dy_and_residual():
     """Gradients are linear in dY; with W2 = 0 the only path to X is the
     residual, so dX = dY and W1, b1, gamma, beta and the tables get nothing."""
