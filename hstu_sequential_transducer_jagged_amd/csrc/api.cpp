@@ -486,7 +486,7 @@ size_t hstu_layer_bwd_workspace_size(const hstu_layer_desc* desc, const hstu_jag
   if (!desc || !jagged || jagged->total_tokens < 0 || desc->d_model <= 0) return 0;
   const size_t T = static_cast<size_t>(jagged->total_tokens);
   const size_t td = round256(T * desc->d_model * sizeof(float));
-  return 17 * td + round256(T * sizeof(float));
+  return (desc->input_norm ? 18 : 17) * td + round256(T * sizeof(float));
 }
 
 namespace {
@@ -504,7 +504,6 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
   int st = check_desc(desc);
   if (st) return st;
   CHECK(desc->dtype == HSTU_F32, HSTU_E_UNSUPPORTED, "the backward pass supports dtype f32");
-  CHECK(desc->input_norm == 0, HSTU_E_UNSUPPORTED, "the backward pass does not support input_norm");
   st = check_jagged(desc, jagged, nullptr);
   if (st) return st;
   CHECK(jagged->num_targets == nullptr, HSTU_E_UNSUPPORTED,
@@ -517,6 +516,12 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
   CHECK(!bwd || (grads && grads->dw1 && grads->db1 && grads->dw2 && grads->db2 && grads->dgamma &&
                   grads->dbeta && grads->dpos && grads->dtime),
         HSTU_E_INVAL, "every gradient pointer must be set");
+  const bool norm1 = desc->input_norm != 0;
+  CHECK(!bwd || !norm1 || (grads->dln1_gamma && grads->dln1_beta), HSTU_E_INVAL,
+        "with input_norm, dln1_gamma and dln1_beta must be set");
+  CHECK(!norm1 || ((!params->ln1_gamma || aligned16(params->ln1_gamma)) &&
+                   (!params->ln1_beta || aligned16(params->ln1_beta))),
+        HSTU_E_INVAL, "ln1_gamma/ln1_beta must be 16-byte aligned");
   const int64_t T = jagged->total_tokens;
   const int d = desc->d_model;
   const bool empty = T == 0 || jagged->num_seqs == 0;
@@ -543,8 +548,11 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
     const struct { float* p; int64_t n; } zero[] = {
         {grads->dw1, 4LL * d * d}, {grads->db1, 4LL * d}, {grads->dw2, 1LL * d * d}, {grads->db2, d},
         {grads->dgamma, d}, {grads->dbeta, d}, {grads->dpos, desc->pos_table_len},
-        {grads->dtime, desc->num_time_buckets}};
+        {grads->dtime, desc->num_time_buckets},
+        {norm1 ? grads->dln1_gamma : nullptr, norm1 ? d : 0},
+        {norm1 ? grads->dln1_beta : nullptr, norm1 ? d : 0}};
     for (const auto& z : zero) {
+      if (z.n == 0) continue;
       st = device_status(hstu::launch_fill_zero(z.p, z.n, s), "zero fill");
       if (st) return st;
     }
@@ -564,6 +572,9 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
   float* DZ = reinterpret_cast<float*>(w + 12 * td);   // [T, 4d]: dU, dV, dQ, dK
   float* DAV = reinterpret_cast<float*>(w + 16 * td);
   float* RSTD = reinterpret_cast<float*>(w + 17 * td);
+  // LayerNorm(X) with input_norm: the input of f1
+  float* XN = norm1 ? reinterpret_cast<float*>(w + 17 * td + round256(static_cast<size_t>(T) * sizeof(float)))
+                    : nullptr;
   const float* X = static_cast<const float*>(x);
   const float* DY = static_cast<const float*>(dy);
   const float* W1 = static_cast<const float*>(params->w1);
@@ -583,19 +594,24 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
   } while (0)
   hstu::BwdAttnArgs ba = make_train_args(desc, jagged, Q, K, V, params->pos_bias, params->time_bias);
   ba.av = AV;
+  const float* XIN = norm1 ? XN : X;   // the input of f1
   // forward: Z = X W1^T + b1 and [U V Q K] = SiLU(Z) in one pass
   if (fwd) {
+    if (norm1) {
+      st = do_layernorm(desc, T, x, params->ln1_gamma, params->ln1_beta, XN, s);
+      if (st) return st;
+    }
     hstu::GemmF32Args g{};
-    g.A = X; g.sam = d; g.sak = 1;
+    g.A = XIN; g.sam = d; g.sak = 1;
     g.B = W1; g.sbk = 1; g.sbn = d;
     g.C = Z; g.ldc = d4; g.bias = params->b1;
     g.outs[0] = U; g.outs[1] = V; g.outs[2] = Q; g.outs[3] = K;
     g.split = d; g.M = static_cast<int>(T); g.N = d4; g.K = d;
     const hipError_t e = hstu::launch_gemm_f32_mma(g, 2, 1, s);
     if (e == hipErrorNotSupported) {
-      st = do_proj(desc, params, T, x, U, V, Q, K, s);
+      st = do_proj(desc, params, T, XIN, U, V, Q, K, s);
       if (st) return st;
-      HSTU_TRY(hstu::launch_gemm_f32s(X, d, 1, W1, 1, d, Z, d4, nullptr, params->b1, static_cast<int>(T), d4,
+      HSTU_TRY(hstu::launch_gemm_f32s(XIN, d, 1, W1, 1, d, Z, d4, nullptr, params->b1, static_cast<int>(T), d4,
                                       d, 1, s), "z gemm");
     } else {
       HSTU_TRY(e, "projection");
@@ -630,10 +646,18 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
   // [U V Q K] = SiLU(X W1^T + b1)
   HSTU_TRY(hstu::launch_silu_bwd(DZ, Z, T * d4, s), "silu backward");
   HSTU_TRY(hstu::launch_colsum(DZ, d4, T, d4, grads->db1, s), "db1");
-  HSTU_TRY(hstu::launch_gemm_f32s(DZ, 1, d4, X, d, 1, grads->dw1, d, nullptr, nullptr, d4, d, T,
+  HSTU_TRY(hstu::launch_gemm_f32s(DZ, 1, d4, XIN, d, 1, grads->dw1, d, nullptr, nullptr, d4, d, T,
                                   splits(d4, d), s), "dW1 gemm");
-  HSTU_TRY(hstu::launch_gemm_f32s(DZ, d4, 1, W1, d, 1, static_cast<float*>(dx), d, DY, nullptr,
-                                  static_cast<int>(T), d, d4, 1, s), "dX gemm");
+  if (norm1) {
+    // d LayerNorm(X) = dZ W1 (into DG, free by now), then back through the LayerNorm, plus dY
+    HSTU_TRY(hstu::launch_gemm_f32s(DZ, d4, 1, W1, d, 1, DG, d, nullptr, nullptr, static_cast<int>(T), d, d4, 1,
+                                    s), "dXn gemm");
+    HSTU_TRY(hstu::launch_ln1_bwd(X, DG, DY, params->ln1_gamma, static_cast<float*>(dx), grads->dln1_gamma,
+                                  grads->dln1_beta, T, d, desc->ln_eps, s), "input LayerNorm backward");
+  } else {
+    HSTU_TRY(hstu::launch_gemm_f32s(DZ, d4, 1, W1, d, 1, static_cast<float*>(dx), d, DY, nullptr,
+                                    static_cast<int>(T), d, d4, 1, s), "dX gemm");
+  }
 #undef HSTU_TRY
   return ok();
 }

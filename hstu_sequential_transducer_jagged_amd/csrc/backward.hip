@@ -193,6 +193,60 @@ __global__ __launch_bounds__(256) void ln_gate_bwd_kernel(const float* __restric
   }
 }
 
+// Input LayerNorm backward, per row (one wave): xhat = (x - mean) / sigma
+// recomputed from x; dxh = dxn . gamma;
+// dx = dy + (dxh - mean(dxh) - xhat mean(dxh . xhat)) / sigma; this block's
+// partial column sums of dxn . xhat (dgamma) and dxn (dbeta).
+__global__ __launch_bounds__(256) void ln1_bwd_kernel(const float* __restrict__ x, const float* __restrict__ dxn,
+                                                      const float* __restrict__ dy, const float* gamma,
+                                                      float* dx, float* dgamma, float* dbeta, int64_t M, int d,
+                                                      float eps) {
+  __shared__ float sg[4][1024];
+  __shared__ float sb[4][1024];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int c = lane; c < d; c += 64) {
+    sg[wave][c] = 0.0f;
+    sb[wave][c] = 0.0f;
+  }
+  const float inv_d = 1.0f / static_cast<float>(d);
+  for (int64_t row = static_cast<int64_t>(blockIdx.x) * 16 + wave; row < M &&
+       row < static_cast<int64_t>(blockIdx.x) * 16 + 16; row += 4) {
+    const float* xr = x + row * d;
+    const float* gr = dxn + row * d;
+    float sx = 0.0f;
+    for (int c = lane; c < d; c += 64) sx += xr[c];
+    const float mean = wave_sum(sx) * inv_d;
+    float sv = 0.0f;
+    for (int c = lane; c < d; c += 64) {
+      const float t = xr[c] - mean;
+      sv += t * t;
+    }
+    const float rstd = 1.0f / sqrtf(wave_sum(sv) * inv_d + eps);
+    float s1 = 0.0f, s2 = 0.0f;
+    for (int c = lane; c < d; c += 64) {
+      const float xh = (xr[c] - mean) * rstd;
+      const float g = gr[c];
+      sg[wave][c] += g * xh;
+      sb[wave][c] += g;
+      const float dxh = g * (gamma ? gamma[c] : 1.0f);
+      s1 += dxh;
+      s2 += dxh * xh;
+    }
+    const float m1 = wave_sum(s1) * inv_d;
+    const float m2 = wave_sum(s2) * inv_d;
+    for (int c = lane; c < d; c += 64) {
+      const float xh = (xr[c] - mean) * rstd;
+      const float dxh = gr[c] * (gamma ? gamma[c] : 1.0f);
+      dx[row * d + c] = dy[row * d + c] + rstd * (dxh - m1 - xh * m2);
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < d; c += 256) {
+    atomicAdd(&dgamma[c], (sg[0][c] + sg[1][c]) + (sg[2][c] + sg[3][c]));
+    atomicAdd(&dbeta[c], (sb[0][c] + sb[1][c]) + (sb[2][c] + sb[3][c]));
+  }
+}
+
 // dz *= SiLU'(z), elementwise over [M, n4].
 __global__ __launch_bounds__(256) void silu_bwd_kernel(float* dz, const float* __restrict__ z, int64_t n) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
@@ -241,6 +295,14 @@ hipError_t launch_gemm_f32s(const float* A, int64_t sam, int64_t sak, const floa
     hipLaunchKernelGGL(gemm_f32s_kernel<false>, grid, dim3(256), 0, s, A, sam, sak, B, sbk, sbn, C, ldc,
                        addend, bias, M, N, K, K);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_ln1_bwd(const float* x, const float* dxn, const float* dy, const float* gamma, float* dx,
+                          float* dgamma, float* dbeta, int64_t M, int d, float eps, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  hipLaunchKernelGGL(ln1_bwd_kernel, dim3(static_cast<unsigned>((M + 15) / 16)), dim3(256), 0, s, x, dxn, dy,
+                     gamma, dx, dgamma, dbeta, M, d, eps);
   return hipGetLastError();
 }
 

@@ -172,6 +172,11 @@ hipError_t launch_gemm_f32s(const float* A, int64_t sam, int64_t sak, const floa
                             int64_t sbn, float* C, int64_t ldc, const float* addend, const float* bias,
                             int M, int N, int64_t K, int splits, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+// Input LayerNorm backward (d <= 1024): dx = dy + LN'(x)^T dxn, with the
+// statistics recomputed from x; dgamma/dbeta += column sums of dxn * xhat
+// and dxn.
+hipError_t launch_ln1_bwd(const float* x, const float* dxn, const float* dy, const float* gamma, float* dx,
+                          float* dgamma, float* dbeta, int64_t M, int d, float eps, hipStream_t s);
 hipError_t launch_colsum(const float* X, int64_t ldx, int64_t M, int N, float* out, hipStream_t s);
 hipError_t launch_ln_gate_fwd(const float* av, const float* u, const float* gamma, const float* beta,
                               float* nhat, float* rstd, float* g, int64_t M, int d, float eps,

@@ -73,7 +73,8 @@ class LayerParams(ctypes.Structure):
 class LayerGrads(ctypes.Structure):
     _fields_ = [("dw1", ctypes.c_void_p), ("db1", ctypes.c_void_p), ("dw2", ctypes.c_void_p),
                 ("db2", ctypes.c_void_p), ("dgamma", ctypes.c_void_p), ("dbeta", ctypes.c_void_p),
-                ("dpos", ctypes.c_void_p), ("dtime", ctypes.c_void_p)]
+                ("dpos", ctypes.c_void_p), ("dtime", ctypes.c_void_p),
+                ("dln1_gamma", ctypes.c_void_p), ("dln1_beta", ctypes.c_void_p)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -262,9 +263,10 @@ def hstu_layer_fwd(desc, params, jagged, cache, x, y, k_out, v_out, workspace,
                                  stream if stream is not None else current_stream()))
 
 
-def make_grads(dw1, db1, dw2, db2, dgamma, dbeta, dpos, dtime) -> LayerGrads:
+def make_grads(dw1, db1, dw2, db2, dgamma, dbeta, dpos, dtime, dln1_gamma=None,
+               dln1_beta=None) -> LayerGrads:
     return LayerGrads(ptr(dw1), ptr(db1), ptr(dw2), ptr(db2), ptr(dgamma), ptr(dbeta), ptr(dpos),
-                      ptr(dtime))
+                      ptr(dtime), ptr(dln1_gamma), ptr(dln1_beta))
 
 
 def hstu_layer_bwd_workspace_size(desc, jagged) -> int:

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 6
+#define HSTU_ABI_VERSION 7
 
 typedef enum {
   HSTU_OK = 0,
@@ -136,6 +136,8 @@ typedef struct {
   float *dbeta;   /* [d] */
   float *dpos;    /* [pos_table_len] */
   float *dtime;   /* [num_time_buckets] */
+  float *dln1_gamma; /* [d], with desc->input_norm (else unused, may be NULL) */
+  float *dln1_beta;  /* [d], likewise */
 } hstu_layer_grads;
 
 /* ABI version of the loaded library (HSTU_ABI_VERSION). */
@@ -271,8 +273,8 @@ int hstu_layer_fwd(const hstu_layer_desc *desc, const hstu_layer_params *params,
                    void *y, void *k_out, void *v_out, void *workspace,
                    size_t workspace_bytes, void *stream);
 
-/* Workspace bytes of hstu_layer_bwd: 17 [T, d] fp32 buffers plus T floats
- * (each rounded up to 256 bytes). */
+/* Workspace bytes of hstu_layer_bwd: 17 [T, d] fp32 buffers (18 with
+ * desc->input_norm) plus T floats (each rounded up to 256 bytes). */
 size_t hstu_layer_bwd_workspace_size(const hstu_layer_desc *desc, const hstu_jagged *jagged);
 
 /* Backward pass of one layer for generative training ("HSTU：Scaling Law 的
@@ -281,9 +283,12 @@ size_t hstu_layer_bwd_workspace_size(const hstu_layer_desc *desc, const hstu_jag
  * dL/dY, writes dx = dL/dX and every parameter gradient, including those of
  * the position and time tables (each visible pair adds its score gradient,
  * summed over heads, to the entries it read). Recomputes the forward.
- * Supported: dtype HSTU_F32, input_norm 0, plain causal attention
- * (jagged->num_targets NULL, no cache), total_tokens and
- * max_seq_len * d_model below 2^31; else HSTU_E_UNSUPPORTED.
+ * With desc->input_norm the gradient also runs through the input LayerNorm
+ * (params ln1_gamma/ln1_beta, NULL meaning ones/zeros) into dx, and
+ * grads->dln1_gamma/dln1_beta must be set.
+ * Supported: dtype HSTU_F32, plain causal attention (jagged->num_targets
+ * NULL, no cache), total_tokens and max_seq_len * d_model below 2^31,
+ * d_model <= 1024; else HSTU_E_UNSUPPORTED.
  * x, dy, dx [T, d] fp32 (dx must not alias x or dy); grads: all eight
  * pointers non-NULL. workspace: device, 256-byte aligned, >=
  * hstu_layer_bwd_workspace_size(). Gradient sums use fp32 atomics, so
@@ -295,10 +300,10 @@ int hstu_layer_bwd(const hstu_layer_desc *desc, const hstu_layer_params *params,
 
 /* A training step in two calls, without the backward's forward recompute.
  * hstu_layer_fwd_train: the layer forward in fp32 (same equations and
- * support as hstu_layer_bwd: HSTU_F32, no input_norm, plain causal
- * attention), writing y [T, d] (must not alias x) and keeping in `workspace`
+ * support as hstu_layer_bwd: HSTU_F32, plain causal attention), writing y [T, d] (must not alias x) and keeping in `workspace`
  * (hstu_layer_bwd_workspace_size() bytes, 256-byte aligned) the activations
- * the backward reads: Z, U, V, Q, K, AV, the normalised AV, 1/sigma and G.
+ * the backward reads: Z, U, V, Q, K, AV, the normalised AV, 1/sigma and G
+ * (and LayerNorm(X) with input_norm).
  * hstu_layer_bwd_after_fwd: the backward of hstu_layer_bwd, reading those
  * activations instead of recomputing them; desc, params, jagged, x and the
  * workspace must be those of the hstu_layer_fwd_train call, with the

@@ -35,7 +35,7 @@ def test_header_declares_the_binding_exports():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.hstu_abi_version() == 6
+    assert lib.hstu_abi_version() == 7
 
 
 def _desc(**kw):
@@ -200,7 +200,7 @@ def test_backward_validates(lib):
         P(FAKE), P(FAKE + 8192), P(dx), ctypes.byref(g) if g else None, P(FAKE), wsb, None)
     assert call(_desc()) == hstu.HSTU_E_UNSUPPORTED                 # bf16
     n1 = hstu.make_desc(64, 2, hstu.HSTU_F32, 255, input_norm=True)
-    assert call(n1) == hstu.HSTU_E_UNSUPPORTED
+    assert call(n1) == hstu.HSTU_E_INVAL                          # dln1_gamma/dln1_beta unset
     tj = hstu.Jagged(2, 6, 10, FAKE, FAKE, FAKE)                     # targets
     assert call(f, j=tj) == hstu.HSTU_E_UNSUPPORTED
     assert call(f, g=None) == hstu.HSTU_E_INVAL
@@ -224,7 +224,6 @@ def test_train_pair_validates(lib):
         ctypes.byref(desc), ctypes.byref(p) if p else None, ctypes.byref(jag), P(FAKE), P(y), P(FAKE), wsb,
         None)
     assert fwd(_desc()) == hstu.HSTU_E_UNSUPPORTED                  # bf16
-    assert fwd(hstu.make_desc(64, 2, hstu.HSTU_F32, 255, input_norm=True)) == hstu.HSTU_E_UNSUPPORTED
     assert fwd(f, y=FAKE) == hstu.HSTU_E_INVAL                       # y aliases x
     assert fwd(f, y=None) == hstu.HSTU_E_INVAL
     assert fwd(f, p=None) == hstu.HSTU_E_INVAL

@@ -192,3 +192,47 @@ def test_layer_backward_over_a_stochastic_length_sample(gpu_lib):
     print("stochastic length backward", n, "of", T, {k: f"{v:.1e}" for k, v in errs.items()})
     for k, e in errs.items():
         assert e < TOL_BWD, (k, e)
+
+
+@pytest.mark.parametrize("two_calls", [False, True])
+def test_layer_backward_with_input_norm(gpu_lib, two_calls):
+    """With the input LayerNorm before f1 (random gamma1, beta1) the gradient
+    reaches X through the residual and through the LayerNorm; dln1_gamma and
+    dln1_beta come back too. Both the recomputing call and the two-call
+    training step, against the oracle."""
+    import torch
+    from hstu_sequential_transducer_jagged_amd import hstu, runner
+    w = gen.make_custom([130, 7, 64, 0, 33], 128, 2, dtype="f32", seed=87, affine="random")
+    d, T = w.d_model, w.total_tokens
+    p = w.layers[0]
+    rng = np.random.default_rng(88)
+    p.input_norm = True
+    p.ln1_gamma = (1.0 + 0.3 * rng.standard_normal(d)).astype(np.float32)
+    p.ln1_beta = (0.2 * rng.standard_normal(d)).astype(np.float32)
+    dy = rng.standard_normal((T, d)).astype(np.float32)
+    dw = runner.DeviceWorkload(w)
+    lay = dw.layers[0]
+    assert lay.desc.input_norm == 1
+    sizes = [4 * d * d, 4 * d, d * d, d, d, d, 2 * w.n_max - 1, w.num_time_buckets, d, d]
+    g = [torch.empty(k, dtype=torch.float32, device="cuda") for k in sizes]
+    grads = hstu.make_grads(*g)
+    dx = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    ws = hstu.workspace_tensor(hstu.hstu_layer_bwd_workspace_size(lay.desc, dw.jagged))
+    if two_calls:
+        y = torch.empty((T, d), dtype=torch.float32, device="cuda")
+        hstu.hstu_layer_fwd_train(lay.desc, lay.params, dw.jagged, dw.x, y, ws)
+        hstu.hstu_layer_bwd_after_fwd(lay.desc, lay.params, dw.jagged, dw.x, f32(dy), dx, grads, ws)
+        ref_y = oracle.layer(w.x, p, w.offsets, w.timestamps, w.num_heads, w.n_max, w.alpha, w.ln_eps)["y"]
+        assert _rel(to_np(y), ref_y) < TOL_BWD
+    else:
+        hstu.hstu_layer_bwd(lay.desc, lay.params, dw.jagged, dw.x, f32(dy), dx, grads, ws)
+    torch.cuda.synchronize()
+    ref = oracle.layer_backward(w.x, p, w.offsets, w.timestamps, dy, w.num_heads, w.n_max, w.alpha, w.ln_eps)
+    names = ["dw1", "db1", "dw2", "db2", "dgamma", "dbeta", "dpos", "dtime", "dln1_gamma", "dln1_beta"]
+    got = {"dx": to_np(dx), **{k: to_np(t) for k, t in zip(names, g)}}
+    got["dw1"] = got["dw1"].reshape(4 * d, d)
+    got["dw2"] = got["dw2"].reshape(d, d)
+    errs = {k: _rel(got[k], ref[k]) for k in got}
+    print("backward with input norm", two_calls, {k: f"{v:.1e}" for k, v in errs.items()})
+    for k, e in errs.items():
+        assert e < TOL_BWD, (k, e)
