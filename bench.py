@@ -393,6 +393,11 @@ def run_backward(args):
 
     w = gen.make_config(args.workload)
     w.dtype = "f32"                      # bf16-valued inputs, held and computed in fp32
+    if args.input_norm:
+        for p in w.layers:
+            p.input_norm = True
+            p.ln1_gamma = np.ones(w.d_model, np.float32)
+            p.ln1_beta = np.zeros(w.d_model, np.float32)
     dw = runner.DeviceWorkload(w)
     lay = dw.layers[0]
     T, d = w.total_tokens, w.d_model
@@ -402,7 +407,7 @@ def run_backward(args):
     dy = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to("cuda")
     dx = torch.empty_like(dy)
     g = [torch.empty(n, dtype=torch.float32, device="cuda") for n in
-         (4 * d * d, 4 * d, d * d, d, d, d, 2 * w.n_max - 1, w.num_time_buckets)]
+         (4 * d * d, 4 * d, d * d, d, d, d, 2 * w.n_max - 1, w.num_time_buckets, d, d)]
     grads = hstu.make_grads(*g)
     ws = hstu.workspace_tensor(hstu.hstu_layer_bwd_workspace_size(lay.desc, dw.jagged))
     ms = timed(lambda: hstu.hstu_layer_bwd(lay.desc, lay.params, dw.jagged, dw.x, dy, dx, grads, ws, sh),
@@ -427,6 +432,7 @@ def run_backward(args):
     rec = base_record(args, "HSTU layer backward tokens/s (fp32, forward recompute included), 1 GPU",
                       T / (ms * 1e-3), "tokens/s", ms, "f32",
                       {"workload": gen.CONFIG_NAMES[args.workload] + ", held in fp32", "total_tokens": T,
+                       "input_norm": bool(args.input_norm),
                        "num_seqs": w.num_seqs, "d_model": d, "num_heads": w.num_heads,
                        "visible_pairs": P})
     rec["forward_fp32_ms"] = ms_fwd
