@@ -53,3 +53,25 @@ def i32(a, device="cuda"):
 def f32(a, device="cuda"):
     import torch
     return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+
+
+def oracle_pool_map(fn, args, workers=8):
+    """fn(*a) for each a in args, in a pool of CPU worker processes (spawned,
+    so they never inherit a GPU context; they run the float64 oracle only).
+    Results come back in the order of args."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import os
+    n = max(1, min(workers, len(args), os.cpu_count() or 1))
+    if n == 1:
+        return [fn(*a) for a in args]
+    with cf.ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn"),
+                                initializer=_one_blas_thread) as ex:
+        return list(ex.map(fn, *zip(*args)))
+
+
+def _one_blas_thread():
+    """Pool workers keep to one BLAS thread each: the pool supplies the
+    parallelism, and nested thread pools would oversubscribe the cores."""
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)

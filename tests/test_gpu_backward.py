@@ -1,24 +1,41 @@
 """The layer backward pass on the GPU (hstu_layer_bwd, fp32, plain causal
 attention) against the oracle's float64 backward, itself pinned by finite
-differences of the forward. Every gradient is compared as a whole tensor:
-max |g - r| / max |r| below 1e-4, the fp32 bound of the forward tests."""
+differences of the forward.
+
+Metric, below 1e-4 (the fp32 bound of the forward tests):
+* matrices (dX [T, d], dW1 [4d, d], dW2 [d, d]) row by row, as the forward
+  tests do: max_t ||g_t - r_t||_inf / max(||r_t||_inf, 1e-6);
+* vectors (db1, db2, dgamma, dbeta, the position and time tables' gradients,
+  dln1_gamma, dln1_beta) entry by entry: |g_i - r_i| / max(|r_i|, FLOOR *
+  max |r|). FLOOR = 1e-2: with the 1e-4 bound an entry is then allowed an
+  absolute error of at least 1e-6 max |r|, about 8 fp32 ulps of the tensor's
+  largest entry. Entries far below the largest are sums that cancelled down
+  to their size, and fp32 accumulation resolves them only to the ulp of the
+  terms they cancelled from."""
 
 import numpy as np
 import pytest
 
 import oracle
 from hstu_inputs import gen
-from tests.helpers import f32, i64, to_np
+from tests.helpers import f32, i64, row_rel_err, to_np
 
 pytestmark = pytest.mark.gpu
 
 TOL_BWD = 1e-4
+FLOOR = 1e-2
 
 
 def _rel(g, r):
+    """Row-normalised for matrices, per entry above the floor for vectors."""
     g, r = np.asarray(g, np.float64), np.asarray(r, np.float64)
     assert g.shape == r.shape and np.all(np.isfinite(g))
-    return float(np.abs(g - r).max() / max(np.abs(r).max(), 1e-6))
+    if g.size == 0:
+        return 0.0
+    if g.ndim == 2:
+        return row_rel_err(g, r)
+    den = np.maximum(np.abs(r), max(FLOOR * np.abs(r).max(), 1e-12))
+    return float((np.abs(g - r) / den).max())
 
 
 @pytest.mark.parametrize("lengths,d,H,alpha,shuffle_ts", [
@@ -28,6 +45,7 @@ def _rel(g, r):
     ([40, 75, 2], 96, 3, 1.0, False),              # 3 heads of 32: a 3-wave workgroup
     ([65, 1, 31], 1024, 16, 0.5, False),           # 16 heads: two head groups per block row
     ([90, 140], 128, 2, 1.0, True),                # timestamps out of order: buckets change often
+    ([120, 64, 9], 128, 2, 1.0, "wide"),           # clocks spanning far more than 2^31 units
     (None, None, None, None, False),               # the 1 x 64 fp32 workload
 ])
 def test_layer_backward_matches_oracle(gpu_lib, lengths, d, H, alpha, shuffle_ts):
@@ -38,7 +56,11 @@ def test_layer_backward_matches_oracle(gpu_lib, lengths, d, H, alpha, shuffle_ts
     else:
         w = gen.make_custom(lengths, d, H, dtype="f32", seed=61, affine="random")
         w.alpha = alpha
-        if shuffle_ts:
+        if shuffle_ts == "wide":
+            from tests.test_gpu_time_buckets import _timestamps
+            w.timestamps = _timestamps("wide", lengths, np.random.default_rng(64))
+            w.layers[0].time_bias = np.random.default_rng(65).standard_normal(32).astype(np.float32)
+        elif shuffle_ts:
             rng = np.random.default_rng(63)
             for b in range(len(lengths)):
                 s0, s1 = int(w.offsets[b]), int(w.offsets[b + 1])
