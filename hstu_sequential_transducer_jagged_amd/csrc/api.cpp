@@ -134,10 +134,17 @@ hstu::AttnArgs make_attn_args(const hstu_layer_desc* d, const hstu_jagged* j,
   hstu::AttnArgs a{};
   a.sched = static_cast<int*>(ws);
   a.total_tokens = j->total_tokens;
-  a.splits = d->dtype == HSTU_BF16 ? hstu::attn_splits(j->num_seqs, j->max_seq_len) : 1;
-  a.partial = a.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                                      hstu::attn_sched_bytes(j->num_seqs, j->max_seq_len))
-                           : nullptr;
+  if (d->dtype == HSTU_BF16) {
+    const hstu::AttnPlan plan = hstu::attn_plan(j->num_seqs, j->max_seq_len, d->num_heads, j->total_tokens,
+                                                d->d_model);
+    a.bm = plan.bm;
+    a.splits = plan.splits;
+    a.partial = plan.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + plan.sched_bytes) : nullptr;
+  } else {
+    a.bm = 64;
+    a.splits = 1;
+    a.partial = nullptr;
+  }
   a.q = q;
   a.k = k;
   a.v = v;
@@ -238,7 +245,8 @@ size_t round256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
 size_t attn_ws(const hstu_layer_desc* d, const hstu_jagged* j) {
   if (d->dtype != HSTU_BF16 || j->num_seqs <= 0 || j->max_seq_len <= 0) return 0;
-  return round256(hstu::attn_workspace_bytes(j->num_seqs, j->max_seq_len, j->total_tokens, d->d_model));
+  return round256(
+      hstu::attn_plan(j->num_seqs, j->max_seq_len, d->num_heads, j->total_tokens, d->d_model).workspace_bytes);
 }
 
 // the work list indexes (item, key chunk) units, item = seq * n_tiles + tile,
@@ -460,7 +468,8 @@ int hstu_layer_fwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
   st = do_proj(desc, params, T, xin, u, v, q, k, s);
   if (st) return st;
   if (desc->dtype == HSTU_BF16 &&
-      hstu::attn_can_fuse_norm_gate(desc->num_heads, jagged->num_seqs, jagged->max_seq_len)) {
+      hstu::attn_can_fuse_norm_gate(jagged->num_seqs, jagged->max_seq_len, desc->num_heads, jagged->total_tokens,
+                                    desc->d_model)) {
     // one head group covers each row: the attention kernel finishes the rows
     // into G = norm_gate(AV, U) itself (in place over U), with the same row
     // code as hstu_norm_gate_fwd, so Y is bitwise that of the separate calls

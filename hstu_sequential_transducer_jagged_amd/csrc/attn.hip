@@ -425,7 +425,6 @@ __device__ __forceinline__ void attn_step(
   {
     uint32_t w[8];
     silu4(s1, 0, w[0], w[1]);
-    if (MORE) fast_bias_lookup<HPB>(c, sq, tb_clz, fb);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
@@ -449,10 +448,6 @@ __device__ __forceinline__ void attn_step(
         s0 = mfma32(kf[2 * (sr - 2)], qf[0][2 * (sr - 2)], s0);
         s0 = mfma32(kf[2 * (sr - 2) + 1], qf[0][2 * (sr - 2) + 1], s0);
       }
-      // the store waits for every LDS read issued before it (the DMA keeps
-      // the compiler from counting partially): after the score MFMAs, which
-      // wait for K and the bias anyway
-      if (MORE && sr == 2) fast_bias_store<HPB>(fb, nxtB, tid);
       if (sr & 1) {
         const int kh = sr >> 1;
         const bf16x8 pk = __builtin_bit_cast(bf16x8, make_uint4(w[4 * kh], w[4 * kh + 1], w[4 * kh + 2], w[4 * kh + 3]));
@@ -463,12 +458,19 @@ __device__ __forceinline__ void attn_step(
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // R1: SiLU of block 0 of tile st and its P.V; the score MFMAs of block 1
+  // R1: SiLU of block 0 of tile st and its P.V; the score MFMAs of block 1;
+  // the time-bias lookups of tile st+1 after the first quarter and their
+  // combine and store after the last, so that each LDS round trip of the
+  // bias has most of a round to land
   {
     uint32_t w[8];
 #pragma unroll
     for (int sr = 0; sr < 4; ++sr) {
       silu4(s0, sr, w[2 * sr], w[2 * sr + 1]);
+      if (MORE && sr == 0) fast_bias_lookup<HPB>(c, sq, tb_clz, fb);
+      // the store waits for every LDS read issued before it (the DMA keeps
+      // the compiler from counting partially): last, after the MFMAs
+      if (MORE && sr == 3) fast_bias_store<HPB>(fb, nxtB, tid);
       // two score MFMAs every other quarter: the block-1 bias read last in
       // R0 has time to land
       if (sr & 1) {
@@ -494,9 +496,9 @@ __device__ __forceinline__ void attn_step(
 
 // Number of key steps (32-key tiles visited) of query tile qt of a sequence:
 // the cost the schedule sorts by.
-__device__ __forceinline__ int tile_steps(const SeqInfo& si, int qt) {
-  const int q0 = qt * kBM;
-  const int q_hi = min(q0 + kBM, si.L);
+__device__ __forceinline__ int tile_steps(const SeqInfo& si, int qt, int bm) {
+  const int q0 = qt * bm;
+  const int q_hi = min(q0 + bm, si.L);
   const int nkeys = si.nc + q_hi;
   const int n_kt = (nkeys + kBN - 1) / kBN;
   const int first_tgt = si.L - si.m;
@@ -528,9 +530,9 @@ __device__ __forceinline__ int unit_cost(const AttnArgs& a, int n_qt, int u) {
   const int b = i / n_qt, t = i - b * n_qt;
   const SeqInfo si = seq_info(a, b);
   // tiles past max_seq_len (a violated contract) are never reached: t < n_qt
-  if (t * kBM >= si.L) return 0;
+  if (t * a.bm >= si.L) return 0;
   int lo, hi;
-  chunk_range(tile_steps(si, t), S, ch, lo, hi);
+  chunk_range(tile_steps(si, t, a.bm), S, ch, lo, hi);
   return max(hi - lo, 1);
 }
 
@@ -675,7 +677,7 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
   const int unit = a.sched[kSchedHead + li];
   const int item = unit / a.splits;
   const int chunk = unit - item * a.splits;
-  const int n_qt = (a.max_seq_len + kBM - 1) / kBM;
+  const int n_qt = (a.max_seq_len + a.bm - 1) / a.bm;
   const int seq = item / n_qt;
   const int qt = item - seq * n_qt;
   const SeqInfo si = seq_info(a, seq);
@@ -1031,29 +1033,38 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 
 }  // namespace
 
-bool attn_can_fuse_norm_gate(int num_heads, int num_seqs, int max_seq_len) {
-  // one head group (8, 4, 2 or 1 heads) per row, and no key-range splits
-  return (num_heads == 8 || num_heads == 4 || num_heads == 2 || num_heads == 1) &&
-         attn_splits(num_seqs, max_seq_len) == 1;
+namespace {
+// Heads per workgroup of the 64-query kernel: the largest of 8, 4, 2, 1
+// dividing the head count.
+int v1_heads_per_group(int num_heads) {
+  for (int c : {8, 4, 2, 1})
+    if (num_heads % c == 0) return c;
+  return 1;
+}
+}  // namespace
+
+AttnPlan attn_plan(int num_seqs, int max_seq_len, int num_heads, int64_t total_tokens, int d_model) {
+  AttnPlan p{};
+  p.bm = kBM;
+  p.heads_per_group = v1_heads_per_group(num_heads);
+  const int64_t n_qt = (static_cast<int64_t>(max_seq_len) + p.bm - 1) / p.bm;
+  const int64_t items = static_cast<int64_t>(num_seqs) * n_qt;
+  p.splits = (items <= 0 || items >= kSplitMinUnits)
+                 ? 1
+                 : static_cast<int>(std::min<int64_t>(kMaxSplits, (kSplitMinUnits + items - 1) / items));
+  const size_t sched = static_cast<size_t>(kSchedHead + items * p.splits) * sizeof(int);
+  p.sched_bytes = (sched + 255) & ~static_cast<size_t>(255);
+  const size_t partial =
+      p.splits > 1 ? static_cast<size_t>(p.splits) * total_tokens * d_model * sizeof(float) : 0;
+  p.workspace_bytes = p.sched_bytes + partial;
+  return p;
 }
 
-int attn_splits(int num_seqs, int max_seq_len) {
-  const int64_t items = static_cast<int64_t>(num_seqs) * ((static_cast<int64_t>(max_seq_len) + kBM - 1) / kBM);
-  if (items <= 0 || items >= kSplitMinUnits) return 1;
-  return static_cast<int>(std::min<int64_t>(kMaxSplits, (kSplitMinUnits + items - 1) / items));
-}
-
-size_t attn_sched_bytes(int num_seqs, int max_seq_len) {
-  const int64_t n_qt = (static_cast<int64_t>(max_seq_len) + kBM - 1) / kBM;
-  const int64_t units = static_cast<int64_t>(num_seqs) * n_qt * attn_splits(num_seqs, max_seq_len);
-  const size_t bytes = static_cast<size_t>(kSchedHead + units) * sizeof(int);
-  return (bytes + 255) & ~static_cast<size_t>(255);
-}
-
-size_t attn_workspace_bytes(int num_seqs, int max_seq_len, int64_t total_tokens, int d_model) {
-  const int S = attn_splits(num_seqs, max_seq_len);
-  const size_t partial = S > 1 ? static_cast<size_t>(S) * total_tokens * d_model * sizeof(float) : 0;
-  return attn_sched_bytes(num_seqs, max_seq_len) + partial;
+bool attn_can_fuse_norm_gate(int num_seqs, int max_seq_len, int num_heads, int64_t total_tokens,
+                             int d_model) {
+  // one head group covers each row, and no key-range splits
+  const AttnPlan p = attn_plan(num_seqs, max_seq_len, num_heads, total_tokens, d_model);
+  return p.heads_per_group == num_heads && num_heads <= 8 && p.splits == 1;
 }
 
 // AV = sum over chunks of the partial outputs, in chunk order (deterministic).
@@ -1079,32 +1090,30 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(const float* __restric
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   const int n_qt = (a.max_seq_len + kBM - 1) / kBM;
   if (a.num_seqs == 0 || n_qt == 0) return hipSuccess;
+  if (a.bm != kBM) return hipErrorInvalidValue;
   hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, s, a, n_qt);
-  int hpb = 1;
-  for (int c : {8, 4, 2, 1})
-    if (a.num_heads % c == 0) {
-      hpb = c;
-      break;
-    }
   // a multiple of the XCD count, one workgroup per unit on average
   const int64_t units = static_cast<int64_t>(a.num_seqs) * n_qt * a.splits;
-  dim3 grid(static_cast<unsigned>((units + kNumXcd - 1) / kNumXcd * kNumXcd), a.num_heads / hpb);
+  const unsigned gx = static_cast<unsigned>((units + kNumXcd - 1) / kNumXcd * kNumXcd);
+  if (a.fuse_ng && (a.splits != 1 || !attn_can_fuse_norm_gate(a.num_seqs, a.max_seq_len, a.num_heads,
+                                                              a.total_tokens, a.d_model)))
+    return hipErrorInvalidValue;
+  const int hpb = v1_heads_per_group(a.num_heads);
+  const dim3 grid(gx, a.num_heads / hpb);
   if (a.fuse_ng) {
-    if (!attn_can_fuse_norm_gate(a.num_heads, a.num_seqs, a.max_seq_len) || a.splits != 1)
-      return hipErrorInvalidValue;
     switch (hpb) {
       case 8: hipLaunchKernelGGL((attn_bf16_kernel<8, true>), grid, dim3(512), 0, s, a); break;
       case 4: hipLaunchKernelGGL((attn_bf16_kernel<4, true>), grid, dim3(256), 0, s, a); break;
       case 2: hipLaunchKernelGGL((attn_bf16_kernel<2, true>), grid, dim3(128), 0, s, a); break;
       default: hipLaunchKernelGGL((attn_bf16_kernel<1, true>), grid, dim3(64), 0, s, a); break;
     }
-    return hipGetLastError();
-  }
-  switch (hpb) {
-    case 8: hipLaunchKernelGGL((attn_bf16_kernel<8, false>), grid, dim3(512), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((attn_bf16_kernel<4, false>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((attn_bf16_kernel<2, false>), grid, dim3(128), 0, s, a); break;
-    default: hipLaunchKernelGGL((attn_bf16_kernel<1, false>), grid, dim3(64), 0, s, a); break;
+  } else {
+    switch (hpb) {
+      case 8: hipLaunchKernelGGL((attn_bf16_kernel<8, false>), grid, dim3(512), 0, s, a); break;
+      case 4: hipLaunchKernelGGL((attn_bf16_kernel<4, false>), grid, dim3(256), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((attn_bf16_kernel<2, false>), grid, dim3(128), 0, s, a); break;
+      default: hipLaunchKernelGGL((attn_bf16_kernel<1, false>), grid, dim3(64), 0, s, a); break;
+    }
   }
   if (a.splits > 1) {
     const int64_t n4 = a.total_tokens * a.d_model / 4;

@@ -36,6 +36,7 @@ struct AttnArgs {
   int no_self;               // targets do not see themselves
   int64_t total_tokens;      // T
   int* sched;                // bf16 path: work list built by the scheduling pass
+  int bm;                    // bf16 path: queries per work item (64)
   int splits;                // bf16 path: key-range chunks per (sequence, query tile)
   float* partial;            // [splits, T, d] fp32 partial outputs when splits > 1
   // bf16 path, one head group covering d_model and splits == 1 only: when
@@ -49,17 +50,23 @@ struct AttnArgs {
   float ng_eps;
 };
 
-// bf16 attention: number of key-range chunks per work item (1 unless the
-// batch has too few (sequence, query tile) items to fill the chip).
-int attn_splits(int num_seqs, int max_seq_len);
-// Workspace bytes of the bf16 attention: the work list, then (splits > 1) the
-// partial outputs.
-size_t attn_sched_bytes(int num_seqs, int max_seq_len);
-size_t attn_workspace_bytes(int num_seqs, int max_seq_len, int64_t total_tokens, int d_model);
+// Launch plan of the bf16 attention for a batch shape: queries per work
+// item, heads per workgroup, key-range chunks per item (1 unless the batch has
+// too few items to fill the chip), and the workspace layout (the work list,
+// then with splits > 1 the fp32 partial outputs).
+struct AttnPlan {
+  int bm;
+  int heads_per_group;
+  int splits;
+  size_t sched_bytes;
+  size_t workspace_bytes;
+};
+AttnPlan attn_plan(int num_seqs, int max_seq_len, int num_heads, int64_t total_tokens, int d_model);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 // Whether launch_attn_bf16 can fuse norm_gate for this shape (one head group
 // per row, no key-range splits).
-bool attn_can_fuse_norm_gate(int num_heads, int num_seqs, int max_seq_len);
+bool attn_can_fuse_norm_gate(int num_seqs, int max_seq_len, int num_heads, int64_t total_tokens,
+                             int d_model);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
 
 // C[M, N] = A[M, K] B[N, K]^T (+ epilogue). Both operands row-major with K
