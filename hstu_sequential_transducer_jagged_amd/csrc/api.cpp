@@ -130,13 +130,13 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 hstu::AttnArgs make_attn_args(const hstu_layer_desc* d, const hstu_jagged* j,
                               const hstu_kv_cache* c, const void* q, const void* k,
                               const void* v, const float* pb, const float* tb, float* av,
-                              void* ws) {
+                              void* ws, int max_splits = 8) {
   hstu::AttnArgs a{};
   a.sched = static_cast<int*>(ws);
   a.total_tokens = j->total_tokens;
   if (d->dtype == HSTU_BF16) {
     const hstu::AttnPlan plan = hstu::attn_plan(j->num_seqs, j->max_seq_len, d->num_heads, j->total_tokens,
-                                                d->d_model);
+                                                d->d_model, max_splits);
     a.bm = plan.bm;
     a.splits = plan.splits;
     a.partial = plan.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + plan.sched_bytes) : nullptr;
@@ -203,7 +203,7 @@ hstu::BwdAttnArgs make_train_args(const hstu_layer_desc* d, const hstu_jagged* j
 
 int do_attn(const hstu_layer_desc* d, const hstu_jagged* j, const hstu_kv_cache* c, const void* q,
             const void* k, const void* v, const float* pb, const float* tb, float* av, void* ws,
-            hipStream_t s) {
+            hipStream_t s, int max_splits = 8) {
   if (d->dtype == HSTU_F32 && c == nullptr && j->num_targets == nullptr &&
       hstu::attn_train_supported(d->head_dim) &&
       static_cast<int64_t>(j->max_seq_len) * d->d_model < (int64_t{1} << 31)) {
@@ -213,7 +213,7 @@ int do_attn(const hstu_layer_desc* d, const hstu_jagged* j, const hstu_kv_cache*
     ta.av = av;
     return device_status(hstu::launch_attn_train_fwd(ta, s), "attention launch");
   }
-  const hstu::AttnArgs a = make_attn_args(d, j, c, q, k, v, pb, tb, av, ws);
+  const hstu::AttnArgs a = make_attn_args(d, j, c, q, k, v, pb, tb, av, ws, max_splits);
   return device_status(d->dtype == HSTU_BF16 ? hstu::launch_attn_bf16(a, s) : hstu::launch_attn_f32(a, s),
                        "attention launch");
 }
@@ -307,6 +307,41 @@ int hstu_attn_fwd(const hstu_layer_desc* desc, const hstu_jagged* jagged,
         "workspace must be 256-byte aligned");
   return do_attn(desc, jagged, cache, q, k, v, pos_bias, time_bias, av, workspace,
                  as_stream(stream));
+}
+
+int hstu_attn_fwd_noalloc(const hstu_layer_desc* desc, const hstu_jagged* jagged,
+                          const hstu_kv_cache* cache, const void* q, const void* k, const void* v,
+                          const float* pos_bias, const float* time_bias, float* av, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  st = check_jagged(desc, jagged, cache);
+  if (st) return st;
+  st = check_items(jagged);
+  if (st) return st;
+  if (jagged->num_seqs == 0 || jagged->total_tokens == 0) return ok();
+  CHECK(q && k && v && av, HSTU_E_INVAL, "q/k/v/av must not be NULL");
+  CHECK(pos_bias && time_bias, HSTU_E_INVAL, "pos_bias/time_bias must not be NULL");
+  CHECK(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(av), HSTU_E_INVAL,
+        "q/k/v/av must be 16-byte aligned");
+  void* ws = nullptr;
+  int max_splits = 8;
+  if (desc->dtype == HSTU_BF16) {
+    // the most key-range splits whose work list and partial outputs fit the
+    // static scratch (fewer splits only change the order of the fp32 sums)
+    const size_t cap = hstu::kAttnStaticScratchBytes;
+    for (;;) {
+      const hstu::AttnPlan p = hstu::attn_plan(jagged->num_seqs, jagged->max_seq_len, desc->num_heads,
+                                               jagged->total_tokens, desc->d_model, max_splits);
+      if (p.workspace_bytes <= cap) break;
+      CHECK(p.splits > 1, HSTU_E_WORKSPACE,
+            "batch too large for the static scratch: its work list needs %zu bytes, the scratch holds %zu",
+            p.workspace_bytes, cap);
+      max_splits = p.splits - 1;
+    }
+    CHECK(hstu::attn_static_scratch(&ws) == hipSuccess, HSTU_E_DEVICE,
+          "could not resolve the static scratch on the current device");
+  }
+  return do_attn(desc, jagged, cache, q, k, v, pos_bias, time_bias, av, ws, as_stream(stream), max_splits);
 }
 
 int hstu_norm_gate_fwd(const hstu_layer_desc* desc, int64_t T, const float* av, const void* u,

@@ -40,6 +40,7 @@
 #include "internal.h"
 
 #include <algorithm>
+#include <mutex>
 
 namespace hstu {
 namespace {
@@ -1043,7 +1044,8 @@ int v1_heads_per_group(int num_heads) {
 }
 }  // namespace
 
-AttnPlan attn_plan(int num_seqs, int max_seq_len, int num_heads, int64_t total_tokens, int d_model) {
+AttnPlan attn_plan(int num_seqs, int max_seq_len, int num_heads, int64_t total_tokens, int d_model,
+                   int max_splits) {
   AttnPlan p{};
   p.bm = kBM;
   p.heads_per_group = v1_heads_per_group(num_heads);
@@ -1052,6 +1054,7 @@ AttnPlan attn_plan(int num_seqs, int max_seq_len, int num_heads, int64_t total_t
   p.splits = (items <= 0 || items >= kSplitMinUnits)
                  ? 1
                  : static_cast<int>(std::min<int64_t>(kMaxSplits, (kSplitMinUnits + items - 1) / items));
+  p.splits = std::max(1, std::min(p.splits, max_splits));
   const size_t sched = static_cast<size_t>(kSchedHead + items * p.splits) * sizeof(int);
   p.sched_bytes = (sched + 255) & ~static_cast<size_t>(255);
   const size_t partial =
@@ -1123,6 +1126,33 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
                          a.splits);
   }
   return hipGetLastError();
+}
+
+// Device scratch of the allocation-free attention entry point: the work
+// list and the partial outputs of hstu_attn_fwd_noalloc. One copy per device
+// (each device's code object holds its own), kept until the process ends.
+// Host code never uses the array's name as an address: the device address
+// comes from hipGetSymbolAddress, resolved once per device.
+static __device__ __align__(256) unsigned char scratch[kAttnStaticScratchBytes];
+
+hipError_t attn_static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s) {

@@ -61,7 +61,14 @@ struct AttnPlan {
   size_t sched_bytes;
   size_t workspace_bytes;
 };
-AttnPlan attn_plan(int num_seqs, int max_seq_len, int num_heads, int64_t total_tokens, int d_model);
+// max_splits caps the key-range splits (the allocation-free entry point
+// lowers it until its workspace fits the static scratch).
+AttnPlan attn_plan(int num_seqs, int max_seq_len, int num_heads, int64_t total_tokens, int d_model,
+                   int max_splits = 8);
+// Bytes of the static device scratch behind hstu_attn_fwd_noalloc, and its
+// device address on the current device (resolved once per device).
+constexpr size_t kAttnStaticScratchBytes = size_t{32} << 20;
+hipError_t attn_static_scratch(void** ptr);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 // Whether launch_attn_bf16 can fuse norm_gate for this shape (one head group
 // per row, no key-range splits).

@@ -27,7 +27,7 @@ HSTU_F32 = 0
 HSTU_BF16 = 1
 
 EXPORTS = ("hstu_abi_version", "hstu_last_error", "hstu_proj_fwd", "hstu_attn_workspace_size",
-           "hstu_attn_fwd",
+           "hstu_attn_fwd", "hstu_attn_fwd_noalloc",
            "hstu_norm_gate_fwd", "hstu_layernorm_fwd", "hstu_linear_bias_tables",
            "hstu_kv_cache_concat", "hstu_stochastic_length", "hstu_gather_rows",
            "hstu_out_fwd", "hstu_layer_workspace_size",
@@ -98,6 +98,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "hstu_proj_fwd": (ctypes.c_int, [P, P, i64, P, P, P, P, P, P]),
         "hstu_attn_workspace_size": (ctypes.c_size_t, [P, P]),
         "hstu_attn_fwd": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "hstu_attn_fwd_noalloc": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P]),
         "hstu_norm_gate_fwd": (ctypes.c_int, [P, i64, P, P, P, P, P, P]),
         "hstu_layernorm_fwd": (ctypes.c_int, [P, i64, P, P, P, P, P]),
         "hstu_linear_bias_tables": (ctypes.c_int, [P, ctypes.c_float, ctypes.c_float, P, P, P]),
@@ -193,6 +194,12 @@ def hstu_attn_fwd(desc, jagged, cache, q, k, v, pos_bias, time_bias, av, workspa
     _check(load().hstu_attn_fwd(_ref(desc), _ref(jagged), _ref(cache), ptr(q), ptr(k), ptr(v),
                                 ptr(pos_bias), ptr(time_bias), ptr(av), ptr(workspace), nbytes,
                                 stream if stream is not None else current_stream()))
+
+
+def hstu_attn_fwd_noalloc(desc, jagged, cache, q, k, v, pos_bias, time_bias, av, stream=None) -> None:
+    _check(load().hstu_attn_fwd_noalloc(_ref(desc), _ref(jagged), _ref(cache), ptr(q), ptr(k), ptr(v),
+                                        ptr(pos_bias), ptr(time_bias), ptr(av),
+                                        stream if stream is not None else current_stream()))
 
 
 def hstu_norm_gate_fwd(desc, T, av, u, gamma, beta, g, stream=None) -> None:

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 7
+#define HSTU_ABI_VERSION 8
 
 typedef enum {
   HSTU_OK = 0,
@@ -181,6 +181,23 @@ int hstu_attn_fwd(const hstu_layer_desc *desc, const hstu_jagged *jagged,
                   const hstu_kv_cache *cache, const void *q, const void *k, const void *v,
                   const float *pos_bias, const float *time_bias, float *av, void *workspace,
                   size_t workspace_bytes, void *stream);
+
+/* hstu_attn_fwd without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The work list and the partial outputs
+ * live in a static device array of HSTU_ATTN_STATIC_SCRATCH_BYTES (32 MiB),
+ * one per device, held until the process ends. Arguments and results are
+ * those of hstu_attn_fwd; the key-range splits are capped so that they fit
+ * the array, and where the cap applies the fp32 partial sums are added in a
+ * different grouping (results agree to rounding; bitwise otherwise). A batch
+ * whose work list alone exceeds the array returns HSTU_E_WORKSPACE. Every
+ * call on a device shares that device's array, so calls that overlap on one
+ * device race; every call overwrites all it reads, nothing needs clearing.
+ * Allocates nothing. */
+#define HSTU_ATTN_STATIC_SCRATCH_BYTES (32u << 20)
+int hstu_attn_fwd_noalloc(const hstu_layer_desc *desc, const hstu_jagged *jagged,
+                          const hstu_kv_cache *cache, const void *q, const void *k, const void *v,
+                          const float *pos_bias, const float *time_bias, float *av, void *stream);
 
 /* Pointwise transformation, first half (§2.1 third equation and the block
  * diagram: LayerNorm, then the product with U):

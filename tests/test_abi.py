@@ -35,7 +35,7 @@ def test_header_declares_the_binding_exports():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.hstu_abi_version() == 7
+    assert lib.hstu_abi_version() == 8
 
 
 def _desc(**kw):
@@ -249,3 +249,16 @@ def test_product_path_does_not_use_the_oracle():
             if f.endswith((".py", ".cpp", ".hip", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
+
+
+def test_noalloc_rejects_a_work_list_larger_than_its_scratch(lib):
+    """hstu_attn_fwd_noalloc: a batch whose work list alone exceeds the
+    static scratch (100 000 sequences of up to 8192 tokens: 12.8 M work
+    units) is refused with HSTU_E_WORKSPACE before anything is enqueued."""
+    P = ctypes.c_void_p
+    d = hstu.make_desc(512, 8, hstu.HSTU_BF16, 2 * 8192 - 1)
+    jag = hstu.Jagged(100_000, 8192, 200_000, FAKE, FAKE, None)
+    st = lib.hstu_attn_fwd_noalloc(ctypes.byref(d), ctypes.byref(jag), None, P(FAKE), P(FAKE), P(FAKE),
+                                   P(FAKE), P(FAKE), P(FAKE), None)
+    assert st == hstu.HSTU_E_WORKSPACE
+    assert b"static scratch" in lib.hstu_last_error()
