@@ -41,6 +41,11 @@ Readings taken where the pages leave a step open:
   shared by all heads ([GR-7.1] §7.1.4 innovation 2 names the position and
   time differences; the bucketed time difference follows [GENRANK] eq.
   6.2.6's bucket(t_i - t_j)); the floor(log2) is taken in integers;
+* the type-aware term of rab ([GR-7.1] §7.1.4 innovation 2, an option):
+  with nt token types, the time table is one table per ordered pair of
+  (query type, key type), time_bias[(type_i * nt + type_j) * nb + bucket],
+  so each type pair has its own time decay; the position table is shared;
+  nt = 1 is the untyped rab;
 * targets (ranking candidates, [GR-7.1] §7.1.5 M-FALCON and [GENRANK]
   §6.2.2 Fig. 6.2.2): history is causal, a candidate sees the whole history
   and itself but no other candidate; all candidates of a sequence share the
@@ -195,7 +200,7 @@ def _visibility(L: int, m: int, n_cache: int, rows: np.ndarray, target_no_self: 
 def attention(q, k, v, offsets, timestamps, pos_bias, time_bias, num_heads: int,
               n_max: int, alpha: float = 1.0, num_targets=None, cache=None,
               rows=None, row_chunk: int = 2048, linear_bias=None, num_time_buckets: int = 32,
-              target_no_self: bool = False):
+              target_no_self: bool = False, token_types=None, num_token_types: int = 1):
     """Spatial aggregation, per head h of every sequence b:
 
         AV_h = (SiLU(alpha * Q_h K_h^T + rab_{p,t}) * Mask) V_h
@@ -216,6 +221,15 @@ def attention(q, k, v, offsets, timestamps, pos_bias, time_bias, num_heads: int,
           genrank_bias() of every pair, evaluated directly with
           ``num_time_buckets`` buckets; the tables are not used.
     target_no_self: targets do not see themselves (_visibility).
+    token_types, num_token_types: the type-aware term of rab ([GR-7.1]
+          §7.1.4, innovation 2: the bias is a function of the position
+          difference, the time difference and the two tokens' types, so that
+          different behaviours can decay at different rates). token_types
+          [T] holds each own token's type in [0, nt); the cache dict then
+          carries "types" [Tc]. time_bias is then nt * nt tables of nb
+          buckets, flat: the pair (query type a, key type b) uses
+          time_bias[(a * nt + b) * nb + bucket]; the position table stays
+          shared. nt = 1 (or token_types None) is the untyped rab.
     Returns AV [T or len(rows), d] float64.
     """
     q = np.asarray(q, F64)
@@ -231,7 +245,16 @@ def attention(q, k, v, offsets, timestamps, pos_bias, time_bias, num_heads: int,
     B = offsets.shape[0] - 1
     want = np.arange(T) if rows is None else np.asarray(rows, np.int64)
     out = np.zeros((want.shape[0], d), dtype=F64)
-    nb = num_time_buckets if linear_bias is not None else time_bias.shape[0]
+    nt = int(num_token_types) if token_types is not None else 1
+    if nt < 1:
+        raise ValueError("num_token_types must be >= 1")
+    if linear_bias is not None:
+        nb = num_time_buckets
+    else:
+        if time_bias.shape[0] % (nt * nt):
+            raise ValueError("time_bias must hold num_token_types^2 tables")
+        nb = time_bias.shape[0] // (nt * nt)
+    types = None if token_types is None else np.asarray(token_types, np.int64)
     for b in range(B):
         s, e = int(offsets[b]), int(offsets[b + 1])
         L = e - s
@@ -250,6 +273,9 @@ def attention(q, k, v, offsets, timestamps, pos_bias, time_bias, num_heads: int,
             vc = np.zeros((0, d))
             tc = np.zeros(0, np.int64)
         nc = ce - cs
+        if types is not None:
+            ty_c = np.zeros(0, np.int64) if nc == 0 else np.asarray(cache["types"][cs:ce], np.int64)
+            key_ty = np.concatenate([ty_c, types[s:e]])
         keys_k = np.concatenate([kc, k[s:e]], axis=0)
         keys_v = np.concatenate([vc, v[s:e]], axis=0)
         key_t = np.concatenate([tc, timestamps[s:e]])
@@ -268,7 +294,13 @@ def attention(q, k, v, offsets, timestamps, pos_bias, time_bias, num_heads: int,
                 if np.any(mask & ((idx < 0) | (idx >= pos_bias.shape[0]))):
                     raise ValueError("position difference outside the position table")
                 idx = np.clip(idx, 0, pos_bias.shape[0] - 1)
-                rab = pos_bias[idx] + time_bias[time_bucket(dt, nb)]
+                tbi = time_bucket(dt, nb)
+                if types is not None:
+                    if np.any((types[s + qrows] < 0) | (types[s + qrows] >= nt)) or \
+                            np.any((key_ty < 0) | (key_ty >= nt)):
+                        raise ValueError("token type outside [0, num_token_types)")
+                    tbi = (types[s + qrows][:, None] * nt + key_ty[None, :]) * nb + tbi
+                rab = pos_bias[idx] + time_bias[tbi]
             for h in range(num_heads):
                 cols = slice(h * dh, (h + 1) * dh)
                 scores = alpha * (q[s + qrows, cols] @ keys_k[:, cols].T) + rab
@@ -318,7 +350,8 @@ def _needed_prefix_rows(offsets, rows):
 
 
 def layer(x, p, offsets, timestamps, num_heads: int, n_max: int, alpha: float = 1.0,
-          eps: float = 1e-5, num_targets=None, cache=None, rows=None) -> Dict[str, np.ndarray]:
+          eps: float = 1e-5, num_targets=None, cache=None, rows=None, token_types=None,
+          num_token_types: int = 1) -> Dict[str, np.ndarray]:
     """One HSTU layer: projection, spatial aggregation, pointwise
     transformation ([NOTES] §2.1, all three equations, plus the residual).
 
@@ -347,10 +380,12 @@ def layer(x, p, offsets, timestamps, num_heads: int, n_max: int, alpha: float = 
     pu, pv, pq, pk = proj(xin, p.w1, p.b1, d)
     u[prow], vv[prow], qq[prow], kk[prow] = pu, pv, pq, pk
     lin = getattr(p, "linear_bias", None)
+    nt = int(num_token_types) if token_types is not None else 1
     av = attention(qq, kk, vv, offsets, timestamps, p.pos_bias, p.time_bias, num_heads,
                    n_max, alpha, num_targets=num_targets, cache=cache,
                    rows=None if rows is None else orow, linear_bias=lin,
-                   num_time_buckets=len(p.time_bias) if p.time_bias is not None else 32)
+                   num_time_buckets=len(p.time_bias) // (nt * nt) if p.time_bias is not None else 32,
+                   token_types=token_types, num_token_types=nt)
     g = norm_gate(av, u[orow], p.gamma, p.beta, eps)
     y = output(x[orow], g, p.w2, p.b2)
     return dict(u=u, v=vv, q=qq, k=kk, av=av, g=g, y=y, proj_rows=prow, rows=orow)

@@ -39,8 +39,11 @@ def _qkv(w, l=0):
 
 
 def _brute_attention(q, k, v, offsets, ts, pb, tb, H, n_max, alpha, num_targets=None,
-                     cache=None):
-    """Scalar triple loop straight from the definition (pure Python floats)."""
+                     cache=None, types=None, nt=1):
+    """Scalar triple loop straight from the definition (pure Python floats).
+    With types: the time table is nt x nt tables of nb buckets (query type
+    first)."""
+    nb = len(tb) // (nt * nt)
     T, d = len(q), len(q[0])
     dh = d // H
     out = [[0.0] * d for _ in range(T)]
@@ -54,22 +57,25 @@ def _brute_attention(q, k, v, offsets, ts, pb, tb, H, n_max, alpha, num_targets=
             cs, ce = int(cache["offsets"][b]), int(cache["offsets"][b + 1])
             nc = ce - cs
             for c in range(nc):
+                ty = int(cache["types"][cs + c]) if types is not None else 0
                 keys.append((cache["k"][cs + c], cache["v"][cs + c], c,
-                             int(cache["timestamps"][cs + c]), "cache", -1))
+                             int(cache["timestamps"][cs + c]), "cache", -1, ty))
         for j in range(L):
             pos = nc + (j if j < L - m else L - m)
-            keys.append((k[s + j], v[s + j], pos, int(ts[s + j]), "own", j))
+            ty = int(types[s + j]) if types is not None else 0
+            keys.append((k[s + j], v[s + j], pos, int(ts[s + j]), "own", j, ty))
         for i in range(L):
             p_i = nc + (i if i < L - m else L - m)
             t_i = int(ts[s + i])
-            for (kr, vr, p_j, t_j, kind, j) in keys:
+            ty_i = int(types[s + i]) if types is not None else 0
+            for (kr, vr, p_j, t_j, kind, j, ty_j) in keys:
                 if kind == "own":
                     if j > i:
                         continue
                     if j >= L - m and j != i:
                         continue
-                bucket = min(len(tb) - 1, (abs(t_i - t_j) + 1).bit_length() - 1)
-                rab = float(pb[p_i - p_j + n_max - 1]) + float(tb[bucket])
+                bucket = min(nb - 1, (abs(t_i - t_j) + 1).bit_length() - 1)
+                rab = float(pb[p_i - p_j + n_max - 1]) + float(tb[(ty_i * nt + ty_j) * nb + bucket])
                 for h in range(H):
                     dot = 0.0
                     for c in range(h * dh, (h + 1) * dh):
@@ -883,3 +889,109 @@ def test_layer_backward_linear_in_dy_and_residual():
     np.testing.assert_array_equal(g0["dx"], dy)
     for kk in ("dw1", "db1", "dgamma", "dbeta", "dpos", "dtime"):
         assert np.all(g0[kk] == 0), kk
+
+
+# ---------------------------------------------------------------------------
+# type-aware rab ("HSTU：Scaling Law 的首次探索" §7.1.4, innovation 2)
+# ---------------------------------------------------------------------------
+
+def _typed(lengths, nt, seed, d=8, H=2, nb=32):
+    w = _tiny(lengths, d=d, H=H, seed=seed, n_max=max(lengths))
+    rng = np.random.default_rng(seed + 1)
+    types = rng.integers(0, nt, size=w.total_tokens)
+    tb = rng.standard_normal(nt * nt * nb) * 0.5
+    w.timestamps = w.timestamps + np.arange(w.total_tokens) ** 3   # many buckets
+    return w, types, tb
+
+
+@pytest.mark.parametrize("nt", [2, 3])
+def test_attention_types_bruteforce(nt):
+    w, types, tb = _typed([5, 1, 9], nt, seed=40 + nt)
+    p = w.layers[0]
+    u, v, q, k = _qkv(w)
+    got = oracle.attention(q, k, v, w.offsets, w.timestamps, p.pos_bias, tb, w.num_heads, w.n_max,
+                           w.alpha, token_types=types, num_token_types=nt)
+    want = _brute_attention(q, k, v, w.offsets, w.timestamps, p.pos_bias, tb, w.num_heads,
+                            w.n_max, w.alpha, types=types, nt=nt)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_types_targets_and_cache_bruteforce():
+    w = gen.make_ranking(seed=12, users=3, history=[4, 0, 6], candidates=[3, 2, 1],
+                         micro_batch=2, d_model=8, num_heads=2, num_layers=1, affine="random",
+                         dtype="f32")
+    p = w.layers[0]
+    rng = np.random.default_rng(5)
+    nt = 2
+    tb = rng.standard_normal(nt * nt * 32)
+    cache = dict(k=rng.standard_normal((w.total_tokens, 8)), v=rng.standard_normal((w.total_tokens, 8)),
+                 offsets=w.offsets, timestamps=w.timestamps,
+                 types=rng.integers(0, nt, size=w.total_tokens))
+    Tc = int(w.cand_offsets[-1])
+    cq, ck, cv = (rng.standard_normal((Tc, 8)) for _ in range(3))
+    ctypes_ = rng.integers(0, nt, size=Tc)
+    m = np.diff(w.cand_offsets)
+    got = oracle.attention(cq, ck, cv, w.cand_offsets, w.cand_timestamps, p.pos_bias, tb, 2, w.n_max,
+                           num_targets=m, cache=cache, token_types=ctypes_, num_token_types=nt)
+    want = _brute_attention(cq, ck, cv, w.cand_offsets, w.cand_timestamps, p.pos_bias, tb, 2, w.n_max,
+                            1.0, num_targets=m, cache=cache, types=ctypes_, nt=nt)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_types_single_type_is_the_untyped_rab():
+    """Every token of type 0 with the (0, 0) table equal to the untyped one:
+    bitwise the untyped result, whatever the other type pairs hold."""
+    w, _, _ = _typed([7, 3], 3, seed=50)
+    p = w.layers[0]
+    u, v, q, k = _qkv(w)
+    tb3 = np.random.default_rng(51).standard_normal(9 * 32)
+    tb3[:32] = p.time_bias
+    got = oracle.attention(q, k, v, w.offsets, w.timestamps, p.pos_bias, tb3, 2, w.n_max, w.alpha,
+                           token_types=np.zeros(w.total_tokens, np.int64), num_token_types=3)
+    np.testing.assert_array_equal(got, _attn(w, q, k, v))
+
+
+def test_attention_types_constant_pair_tables_closed_form():
+    """Q = K = 0, no position bias, and each pair's time table a constant
+    c[a, b] (asymmetric): AV_i = sum over key types b of
+    SiLU(c[type_i, b]) * (prefix sum of v over the keys of type b up to i),
+    a per-type np.cumsum. A transposed (key type, query type) lookup fails."""
+    nt = 3
+    w, types, _ = _typed([11, 6], nt, seed=60)
+    p = w.layers[0]
+    p.pos_bias[:] = 0.0
+    c = np.array([[0.3, -1.2, 2.0], [0.9, 0.1, -0.4], [-2.5, 1.7, 0.6]])
+    tb = np.repeat(c.reshape(-1), 32)
+    v = np.random.default_rng(61).standard_normal((w.total_tokens, 8))
+    z = np.zeros_like(v)
+    got = oracle.attention(z, z, v, w.offsets, w.timestamps, p.pos_bias, tb, 2, w.n_max,
+                           token_types=types, num_token_types=nt)
+    silu = lambda x: x / (1.0 + math.exp(-x))
+    for b0 in range(2):
+        s, e = int(w.offsets[b0]), int(w.offsets[b0 + 1])
+        ty = types[s:e]
+        want = np.zeros((e - s, 8))
+        for tb_ in range(nt):
+            pref = np.cumsum(np.where((ty == tb_)[:, None], v[s:e], 0.0), axis=0)
+            want += np.array([silu(c[a, tb_]) for a in ty])[:, None] * pref
+        np.testing.assert_allclose(got[s:e], want, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_types_relabel_equivariance():
+    """Renaming the types by a permutation, with the pair tables moved
+    accordingly, leaves every output unchanged."""
+    nt = 3
+    w, types, tb = _typed([8, 5, 2], nt, seed=70)
+    p = w.layers[0]
+    u, v, q, k = _qkv(w)
+    perm = np.array([2, 0, 1])
+    tb3 = tb.reshape(nt, nt, 32)
+    tb_new = np.empty_like(tb3)
+    for a in range(nt):
+        for b in range(nt):
+            tb_new[perm[a], perm[b]] = tb3[a, b]
+    base = oracle.attention(q, k, v, w.offsets, w.timestamps, p.pos_bias, tb, 2, w.n_max, w.alpha,
+                            token_types=types, num_token_types=nt)
+    moved = oracle.attention(q, k, v, w.offsets, w.timestamps, p.pos_bias, tb_new.reshape(-1), 2,
+                             w.n_max, w.alpha, token_types=perm[types], num_token_types=nt)
+    np.testing.assert_allclose(moved, base, rtol=0, atol=0)
