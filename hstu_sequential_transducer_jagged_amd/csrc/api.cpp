@@ -94,8 +94,21 @@ int check_desc(const hstu_layer_desc* d) {
         d->input_norm);
   CHECK(d->target_no_self == 0 || d->target_no_self == 1, HSTU_E_INVAL,
         "target_no_self must be 0 or 1 (got %d)", d->target_no_self);
+  CHECK(d->num_token_types >= 0 && d->num_token_types <= HSTU_MAX_TOKEN_TYPES, HSTU_E_INVAL,
+        "num_token_types must be in [0, %d] (got %d)", HSTU_MAX_TOKEN_TYPES, d->num_token_types);
+  CHECK(d->bias_mode == HSTU_BIAS_TABLES || d->bias_mode == HSTU_BIAS_LINEAR, HSTU_E_INVAL,
+        "unknown bias_mode %d", d->bias_mode);
+  if (d->bias_mode == HSTU_BIAS_LINEAR) {
+    CHECK(std::isfinite(d->linear_m_p) && std::isfinite(d->linear_m_t), HSTU_E_INVAL,
+          "linear_m_p and linear_m_t must be finite");
+    CHECK(d->num_token_types <= 1, HSTU_E_UNSUPPORTED,
+          "the parameter-free bias has no token types (num_token_types %d)", d->num_token_types);
+  }
   return HSTU_OK;
 }
+
+bool typed(const hstu_layer_desc* d) { return d->num_token_types > 1; }
+bool linear_bias(const hstu_layer_desc* d) { return d->bias_mode == HSTU_BIAS_LINEAR; }
 
 int check_jagged(const hstu_layer_desc* d, const hstu_jagged* j, const hstu_kv_cache* c) {
   CHECK(j != nullptr, HSTU_E_INVAL, "jagged is NULL");
@@ -117,8 +130,14 @@ int check_jagged(const hstu_layer_desc* d, const hstu_jagged* j, const hstu_kv_c
   // bounded by the host scalars. With targets it depends on device data
   // (targets share one position); the kernels clamp table indices, and
   // hstu_check_inputs() checks the exact bound.
+  if (typed(d)) {
+    CHECK(j->total_tokens == 0 || j->token_types != nullptr, HSTU_E_INVAL,
+          "jagged token_types is NULL with num_token_types %d", d->num_token_types);
+    CHECK(!c || c->total_tokens == 0 || c->token_types != nullptr, HSTU_E_INVAL,
+          "cache token_types is NULL with num_token_types %d", d->num_token_types);
+  }
   const int64_t n_max = (static_cast<int64_t>(d->pos_table_len) + 1) / 2;
-  if (j->num_targets == nullptr)
+  if (j->num_targets == nullptr && !linear_bias(d))
     CHECK(static_cast<int64_t>(j->max_seq_len) + cache_max <= n_max, HSTU_E_INVAL,
           "position table too small: max_seq_len (%d) + cache max_len (%lld) > n_max (%lld)",
           j->max_seq_len, static_cast<long long>(cache_max), static_cast<long long>(n_max));
@@ -158,6 +177,12 @@ hstu::AttnArgs make_attn_args(const hstu_layer_desc* d, const hstu_jagged* j,
   a.c_ts = c ? c->timestamps : nullptr;
   a.pos_bias = pb;
   a.time_bias = tb;
+  a.types = typed(d) ? j->token_types : nullptr;
+  a.c_types = typed(d) && c ? c->token_types : nullptr;
+  a.ntypes = typed(d) ? d->num_token_types : 1;
+  a.linear = linear_bias(d) ? 1 : 0;
+  a.m_p = d->linear_m_p;
+  a.m_t = d->linear_m_t;
   a.av = av;
   a.d_model = d->d_model;
   a.num_heads = d->num_heads;
@@ -204,7 +229,7 @@ hstu::BwdAttnArgs make_train_args(const hstu_layer_desc* d, const hstu_jagged* j
 int do_attn(const hstu_layer_desc* d, const hstu_jagged* j, const hstu_kv_cache* c, const void* q,
             const void* k, const void* v, const float* pb, const float* tb, float* av, void* ws,
             hipStream_t s, int max_splits = 8) {
-  if (d->dtype == HSTU_F32 && c == nullptr && j->num_targets == nullptr &&
+  if (d->dtype == HSTU_F32 && c == nullptr && j->num_targets == nullptr && !typed(d) && !linear_bias(d) &&
       hstu::attn_train_supported(d->head_dim) &&
       static_cast<int64_t>(j->max_seq_len) * d->d_model < (int64_t{1} << 31)) {
     // plain causal fp32: the matrix-core kernel
@@ -297,7 +322,7 @@ int hstu_attn_fwd(const hstu_layer_desc* desc, const hstu_jagged* jagged,
   if (st) return st;
   if (jagged->num_seqs == 0 || jagged->total_tokens == 0) return ok();
   CHECK(q && k && v && av, HSTU_E_INVAL, "q/k/v/av must not be NULL");
-  CHECK(pos_bias && time_bias, HSTU_E_INVAL, "pos_bias/time_bias must not be NULL");
+  CHECK(linear_bias(desc) || (pos_bias && time_bias), HSTU_E_INVAL, "pos_bias/time_bias must not be NULL");
   CHECK(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(av), HSTU_E_INVAL,
         "q/k/v/av must be 16-byte aligned");
   const size_t need = attn_ws(desc, jagged);
@@ -320,7 +345,7 @@ int hstu_attn_fwd_noalloc(const hstu_layer_desc* desc, const hstu_jagged* jagged
   if (st) return st;
   if (jagged->num_seqs == 0 || jagged->total_tokens == 0) return ok();
   CHECK(q && k && v && av, HSTU_E_INVAL, "q/k/v/av must not be NULL");
-  CHECK(pos_bias && time_bias, HSTU_E_INVAL, "pos_bias/time_bias must not be NULL");
+  CHECK(linear_bias(desc) || (pos_bias && time_bias), HSTU_E_INVAL, "pos_bias/time_bias must not be NULL");
   CHECK(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(av), HSTU_E_INVAL,
         "q/k/v/av must be 16-byte aligned");
   void* ws = nullptr;
@@ -378,8 +403,9 @@ int hstu_linear_bias_tables(const hstu_layer_desc* desc, float m_p, float m_t, f
   CHECK(std::isfinite(m_p) && std::isfinite(m_t), HSTU_E_INVAL, "m_p and m_t must be finite");
   CHECK(pos_bias && time_bias, HSTU_E_INVAL, "pos_bias/time_bias must not be NULL");
   CHECK(pos_bias != time_bias, HSTU_E_INVAL, "pos_bias and time_bias must not alias");
+  const int pairs = typed(desc) ? desc->num_token_types * desc->num_token_types : 1;
   return device_status(hstu::launch_linear_bias_tables(m_p, m_t, desc->pos_table_len,
-                                                       desc->num_time_buckets, pos_bias, time_bias,
+                                                       desc->num_time_buckets, pairs, pos_bias, time_bias,
                                                        as_stream(stream)),
                        "linear bias tables launch");
 }
@@ -459,8 +485,8 @@ int hstu_layer_fwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
   if (st) return st;
   st = check_jagged(desc, jagged, cache);
   if (st) return st;
-  CHECK(params && params->w1 && params->w2 && params->pos_bias && params->time_bias, HSTU_E_INVAL,
-        "params, w1, w2, pos_bias and time_bias must not be NULL");
+  CHECK(params && params->w1 && params->w2 && (linear_bias(desc) || (params->pos_bias && params->time_bias)),
+        HSTU_E_INVAL, "params, w1, w2, pos_bias and time_bias must not be NULL");
   st = check_items(jagged);
   if (st) return st;
   const int64_t T = jagged->total_tokens;
@@ -552,6 +578,8 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
   if (st) return st;
   CHECK(jagged->num_targets == nullptr, HSTU_E_UNSUPPORTED,
         "the backward pass supports plain causal attention (no targets)");
+  CHECK(!typed(desc) && !linear_bias(desc), HSTU_E_UNSUPPORTED,
+        "the backward pass supports the untyped table bias");
   CHECK(jagged->total_tokens < (int64_t{1} << 31) &&
             static_cast<int64_t>(jagged->max_seq_len) * desc->d_model < (int64_t{1} << 31),
         HSTU_E_UNSUPPORTED, "the backward pass needs total_tokens and max_seq_len * d_model below 2^31");
@@ -768,6 +796,15 @@ int hstu_check_inputs(const hstu_layer_desc* desc, const hstu_jagged* jagged,
     coff.resize(B + 1);
     e = hipMemcpyAsync(coff.data(), cache->offsets, sizeof(int64_t) * (B + 1), hipMemcpyDeviceToHost, s);
   }
+  std::vector<int32_t> ty, cty;
+  if (e == hipSuccess && typed(desc) && jagged->total_tokens > 0) {
+    ty.resize(static_cast<size_t>(jagged->total_tokens));
+    e = hipMemcpyAsync(ty.data(), jagged->token_types, sizeof(int32_t) * ty.size(), hipMemcpyDeviceToHost, s);
+  }
+  if (e == hipSuccess && typed(desc) && cache && cache->total_tokens > 0) {
+    cty.resize(static_cast<size_t>(cache->total_tokens));
+    e = hipMemcpyAsync(cty.data(), cache->token_types, sizeof(int32_t) * cty.size(), hipMemcpyDeviceToHost, s);
+  }
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return device_status(e, "check_inputs copy");
   CHECK(B == 0 || off[0] == 0, HSTU_E_DATA, "offsets[0] = %lld, expected 0", static_cast<long long>(off[0]));
@@ -790,7 +827,7 @@ int hstu_check_inputs(const hstu_layer_desc* desc, const hstu_jagged* jagged,
     const int64_t m = tgt.empty() ? 0 : tgt[b];
     const int64_t max_dp = L == 0 ? 0 : (m > 0 ? C + (L - m) : C + L - 1);
     const int64_t n_max = (static_cast<int64_t>(desc->pos_table_len) + 1) / 2;
-    CHECK(max_dp <= n_max - 1, HSTU_E_DATA,
+    CHECK(linear_bias(desc) || max_dp <= n_max - 1, HSTU_E_DATA,
           "sequence %d needs position differences up to %lld but the table covers %lld", b,
           static_cast<long long>(max_dp), static_cast<long long>(n_max - 1));
   }
@@ -800,6 +837,12 @@ int hstu_check_inputs(const hstu_layer_desc* desc, const hstu_jagged* jagged,
     CHECK(coff[0] == 0 && coff[B] == cache->total_tokens, HSTU_E_DATA,
           "cache offsets must start at 0 and end at cache total_tokens");
   }
+  for (size_t i = 0; i < ty.size(); ++i)
+    CHECK(ty[i] >= 0 && ty[i] < desc->num_token_types, HSTU_E_DATA, "token_types[%zu] = %d outside [0, %d)", i,
+          ty[i], desc->num_token_types);
+  for (size_t i = 0; i < cty.size(); ++i)
+    CHECK(cty[i] >= 0 && cty[i] < desc->num_token_types, HSTU_E_DATA,
+          "cache token_types[%zu] = %d outside [0, %d)", i, cty[i], desc->num_token_types);
   return ok();
 }
 

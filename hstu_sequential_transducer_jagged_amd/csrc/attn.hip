@@ -86,11 +86,20 @@ __device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b) {
   return si;
 }
 
+// Bias modes of the bf16 kernel (template parameter): the position and time
+// tables; the tables with one time table per (query type, key type) pair;
+// the parameter-free bias -m_p dp - m_t bucket computed from the two slopes.
+constexpr int kBiasTables = 0;
+constexpr int kBiasTyped = 1;
+constexpr int kBiasLinear = 2;
+constexpr int kMaxTypePairs = 16;    // up to 4 token types
+
 // Per-key data of one key tile, delivered to LDS by DMA two tiles ahead.
 struct KeyData {
   alignas(16) uint32_t tlo[kBN];    // low words of the key timestamps
   alignas(16) uint32_t thi[kBN];    // high words (64-bit path)
   alignas(16) float pos[kPosWin];   // raw position-bias window, entry e <-> dp = w0 + e
+  alignas(16) int32_t ty[kBN];      // key token types (typed mode)
 };
 
 // Bytes per staged K / V row of HPB heads. The pads put the rows of one MFMA
@@ -127,35 +136,34 @@ __device__ __forceinline__ int64_t key_row(const Ctx& c, int kk) {
   return kk < c.nc ? (c.cs + kk) : (c.s + kk - c.nc);
 }
 
-// DMA of a tile's key data: wave 0 the timestamps (lanes 0..31 low words,
-// 32..63 high words), waves 1 and 2 the two halves of the position window.
-template <int HPB>
-__device__ __forceinline__ void load_keydata(const Ctx& c, const int64_t* ts, const int64_t* c_ts,
-                                             const float* pos_bias, KeyData& kd, int tile, int wave,
+// DMA of a tile's key data, four items: 0 the timestamps (lanes 0..31 low
+// words, 32..63 high words), 1 and 2 the halves of the position window
+// (table modes), 3 the key types (typed mode); item i is issued by wave
+// i % HPB. Key types outside [0, nt) are clamped where they are used.
+template <int HPB, int MODE>
+__device__ __forceinline__ void load_keydata(const Ctx& c, const AttnArgs& a, KeyData& kd, int tile, int wave,
                                              int lane) {
-  if (wave == 0) {
-    const int kk = min(tile * kBN + (lane & (kBN - 1)), c.nkeys - 1);
-    const int64_t* tp = kk < c.nc ? c_ts + (c.cs + kk) : ts + (c.s + kk - c.nc);
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(tp) + (lane >> 5);
-    __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, kd.tlo), 4, 0, 0);
-  } else if (wave <= 2 || HPB < 4) {
-    // with fewer than 3 waves, wave 0 / 1 issue the window halves too
-    const int w0 = window_origin(c, tile);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      if (HPB >= 4 && half != wave - 1) continue;
-      int idx = c.pos_center + w0 + half * 64 + lane;
+  for (int item = 0; item < 4; ++item) {
+    if (item % HPB != wave) continue;
+    if (item == 0) {
+      const int kk = min(tile * kBN + (lane & (kBN - 1)), c.nkeys - 1);
+      const int64_t* tp = kk < c.nc ? a.c_ts + (c.cs + kk) : a.ts + (c.s + kk - c.nc);
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(tp) + (lane >> 5);
+      __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, kd.tlo), 4, 0, 0);
+    } else if (item <= 2) {
+      if (MODE == kBiasLinear) continue;
+      const int half = item - 1;
+      int idx = c.pos_center + window_origin(c, tile) + half * 64 + lane;
       idx = idx < 0 ? 0 : (idx >= c.pos_len ? c.pos_len - 1 : idx);
-      __builtin_amdgcn_global_load_lds(pos_bias + idx, LDS_PTR(void, kd.pos + half * 64), 4, 0, 0);
-    }
-  }
-  if (HPB < 4 && wave == 0) {
-    const int w0 = window_origin(c, tile);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      int idx = c.pos_center + w0 + half * 64 + lane;
-      idx = idx < 0 ? 0 : (idx >= c.pos_len ? c.pos_len - 1 : idx);
-      __builtin_amdgcn_global_load_lds(pos_bias + idx, LDS_PTR(void, kd.pos + half * 64), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.pos_bias + idx, LDS_PTR(void, kd.pos + half * 64), 4, 0, 0);
+    } else {
+      if (MODE != kBiasTyped) continue;
+      if (lane < kBN) {
+        const int kk = min(tile * kBN + lane, c.nkeys - 1);
+        const int32_t* src = kk < c.nc ? a.c_types + (c.cs + kk) : a.types + (c.s + kk - c.nc);
+        __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, kd.ty), 4, 0, 0);
+      }
     }
   }
 }
@@ -239,19 +247,37 @@ struct SlotQ {
   int qi[SPT], pq[SPT];
   uint32_t uq[SPT];     // query time relative to the block reference (32-bit path)
   int64_t tq[SPT];      // raw query time (64-bit path)
+  int ty[SPT];          // query token type x nt (typed mode)
 };
 
+// Base-2 bias of one pair from its time bucket (as the clz of |dt|+1 on the
+// 32-bit path, or the bucket itself on the 64-bit one) and, per mode, the
+// position-table value or the position difference:
+//   tables: -log2(e) (pb + tb[type pair][bucket]);
+//   linear: log2(e) (m_p dp + m_t bucket).
+// tb_clz / tb_lin hold -log2(e) times the time tables, indexed by
+// (type pair) * 32 + clz and (type pair) * 64 + bucket.
+template <int MODE>
+__device__ __forceinline__ float pair_bias_clz(const AttnArgs& a, const float* tb_clz, int tp, uint32_t clz,
+                                               float pb_or_dp) {
+  if constexpr (MODE == kBiasLinear) {
+    const int bucket = min(31 - static_cast<int>(clz), a.nb - 1);
+    return kLog2e * __builtin_fmaf(a.m_p, pb_or_dp, a.m_t * static_cast<float>(bucket));
+  } else {
+    return __builtin_fmaf(pb_or_dp, -kLog2e, tb_clz[tp * 32 + clz]);
+  }
+}
+
 // Bias tile (base-2 domain) of key tile `tile` from its key data.
-template <int HPB>
-__device__ __forceinline__ void build_bias(const Ctx& c, const SlotQ<512 / (64 * HPB)>& sq,
+template <int HPB, int MODE>
+__device__ __forceinline__ void build_bias(const Ctx& c, const AttnArgs& a, const SlotQ<512 / (64 * HPB)>& sq,
                                            const KeyData& kd, float* bias, const float* tb_clz,
-                                           const float* tb_lin, int nb, int tile, int tid) {
+                                           const float* tb_lin, int tile, int tid) {
   constexpr int NT = 64 * HPB;
   constexpr int SPT = 512 / NT;
   const int k0 = tile * kBN;
   const int w0 = window_origin(c, tile);
-  // all keys are non-targets visible to every query of the block
-  const bool full = (k0 + kBN - 1 - c.nc <= c.q0) && (k0 + kBN - 1 - c.nc < c.first_tgt);
+  const int nb = a.nb, nt = a.ntypes;
 #pragma unroll
   for (int i = 0; i < SPT; ++i) {
     const int slot = tid + i * NT;
@@ -259,38 +285,38 @@ __device__ __forceinline__ void build_bias(const Ctx& c, const SlotQ<512 / (64 *
     const int kbase = k0 + kr;
     const int qi = sq.qi[i];
     float b[4];
-    if (full && !c.wide) {
-      const uint4 t4 = *reinterpret_cast<const uint4*>(&kd.tlo[kr]);
-      const uint32_t tk[4] = {t4.x, t4.y, t4.z, t4.w};
-      const float* pw = kd.pos + (sq.pq[i] - kbase - w0);   // p_k = kk for non-target keys
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t x = sq.uq[i], y = tk[r] - c.tb_lo;
-        const uint32_t ad = (x > y ? x - y : y - x) + 1u;   // |dt| + 1 >= 1
-        b[r] = __builtin_fmaf(pw[-r], -kLog2e, tb_clz[__builtin_clz(ad)]);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kk = kbase + r;
-        const int jo = kk - c.nc;
-        const bool vis = qi < c.L && kk < c.nkeys &&
-                         (kk < c.nc ||
-                          (jo <= qi && (jo < c.first_tgt || (jo == qi && !(c.no_self && qi >= c.first_tgt)))));
-        int pidx = sq.pq[i] - key_pos(kk, c.nc, c.first_tgt) - w0;
+    for (int r = 0; r < 4; ++r) {
+      const int kk = kbase + r;
+      const int jo = kk - c.nc;
+      const bool vis = qi < c.L && kk < c.nkeys &&
+                       (kk < c.nc ||
+                        (jo <= qi && (jo < c.first_tgt || (jo == qi && !(c.no_self && qi >= c.first_tgt)))));
+      const int dp = sq.pq[i] - key_pos(kk, c.nc, c.first_tgt);
+      int tp = 0;
+      if constexpr (MODE == kBiasTyped) tp = sq.ty[i] + min(max(kd.ty[kr + r], 0), nt - 1);
+      float pv;
+      if constexpr (MODE == kBiasLinear) {
+        pv = static_cast<float>(dp);
+      } else {
+        int pidx = dp - w0;
         pidx = pidx < 0 ? 0 : (pidx >= kPosWin ? kPosWin - 1 : pidx);
-        float tbv;
-        if (!c.wide) {
-          const uint32_t x = sq.uq[i], y = kd.tlo[kr + r] - c.tb_lo;
-          const uint32_t ad = (x > y ? x - y : y - x) + 1u;
-          tbv = tb_clz[__builtin_clz(ad)];
-        } else {
-          const int64_t tk = static_cast<int64_t>((static_cast<uint64_t>(kd.thi[kr + r]) << 32) |
-                                                  kd.tlo[kr + r]);
-          tbv = tb_lin[time_bucket64(sq.tq[i] - tk, nb)];
-        }
-        b[r] = vis ? __builtin_fmaf(kd.pos[pidx], -kLog2e, tbv) : kMaskBias;
+        pv = kd.pos[pidx];
       }
+      float bv;
+      if (!c.wide) {
+        const uint32_t x = sq.uq[i], y = kd.tlo[kr + r] - c.tb_lo;
+        const uint32_t ad = (x > y ? x - y : y - x) + 1u;
+        bv = pair_bias_clz<MODE>(a, tb_clz, tp, __builtin_clz(ad), pv);
+      } else {
+        const int64_t tk = static_cast<int64_t>((static_cast<uint64_t>(kd.thi[kr + r]) << 32) | kd.tlo[kr + r]);
+        const int bucket = time_bucket64(sq.tq[i] - tk, nb);
+        if constexpr (MODE == kBiasLinear)
+          bv = kLog2e * __builtin_fmaf(a.m_p, pv, a.m_t * static_cast<float>(bucket));
+        else
+          bv = __builtin_fmaf(pv, -kLog2e, tb_lin[tp * 64 + bucket]);
+      }
+      b[r] = vis ? bv : kMaskBias;
     }
     *reinterpret_cast<float4*>(&bias[slot * 4]) = make_float4(b[0], b[1], b[2], b[3]);
   }
@@ -304,11 +330,12 @@ __device__ __forceinline__ void build_bias(const Ctx& c, const SlotQ<512 / (64 *
 template <int SPT>
 struct FastBias {
   uint32_t tk[SPT][4];
-  float pw[SPT][4];
+  float pw[SPT][4];     // position-table values (table modes) or position differences (linear)
   float tb[SPT][4];
+  int ty[SPT][4];       // key types (typed mode)
 };
 
-template <int HPB>
+template <int HPB, int MODE>
 __device__ __forceinline__ void fast_bias_issue(const Ctx& c, const SlotQ<512 / (64 * HPB)>& sq,
                                                 const KeyData& kd, int tile, int tid,
                                                 FastBias<512 / (64 * HPB)>& fb) {
@@ -325,15 +352,27 @@ __device__ __forceinline__ void fast_bias_issue(const Ctx& c, const SlotQ<512 / 
     fb.tk[i][1] = t4.y;
     fb.tk[i][2] = t4.z;
     fb.tk[i][3] = t4.w;
-    int pb = sq.pq[i] - (k0 + kr) - w0;   // p_k = kk for non-target keys
-    pb = pb < 3 ? 3 : (pb > kPosWin - 1 ? kPosWin - 1 : pb);
+    if constexpr (MODE == kBiasTyped) {
+      const int4 y4 = *reinterpret_cast<const int4*>(&kd.ty[kr]);
+      fb.ty[i][0] = y4.x;
+      fb.ty[i][1] = y4.y;
+      fb.ty[i][2] = y4.z;
+      fb.ty[i][3] = y4.w;
+    }
+    if constexpr (MODE == kBiasLinear) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) fb.pw[i][r] = kd.pos[pb - r];
+      for (int r = 0; r < 4; ++r) fb.pw[i][r] = static_cast<float>(sq.pq[i] - (k0 + kr + r));   // p_k = kk
+    } else {
+      int pb = sq.pq[i] - (k0 + kr) - w0;   // p_k = kk for non-target keys
+      pb = pb < 3 ? 3 : (pb > kPosWin - 1 ? kPosWin - 1 : pb);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) fb.pw[i][r] = kd.pos[pb - r];
+    }
   }
 }
 
-template <int HPB>
-__device__ __forceinline__ void fast_bias_lookup(const Ctx& c, const SlotQ<512 / (64 * HPB)>& sq,
+template <int HPB, int MODE>
+__device__ __forceinline__ void fast_bias_lookup(const Ctx& c, const AttnArgs& a, const SlotQ<512 / (64 * HPB)>& sq,
                                                  const float* tb_clz, FastBias<512 / (64 * HPB)>& fb) {
   constexpr int SPT = 512 / (64 * HPB);
 #pragma unroll
@@ -342,12 +381,20 @@ __device__ __forceinline__ void fast_bias_lookup(const Ctx& c, const SlotQ<512 /
     for (int r = 0; r < 4; ++r) {
       const uint32_t x = sq.uq[i], y = fb.tk[i][r] - c.tb_lo;
       const uint32_t ad = (x > y ? x - y : y - x) + 1u;   // |dt| + 1 >= 1
-      fb.tb[i][r] = tb_clz[__builtin_clz(ad)];
+      const uint32_t clz = __builtin_clz(ad);
+      if constexpr (MODE == kBiasLinear) {
+        fb.tb[i][r] = a.m_t * static_cast<float>(min(31 - static_cast<int>(clz), a.nb - 1));
+      } else {
+        int tp = 0;
+        if constexpr (MODE == kBiasTyped) tp = sq.ty[i] + min(max(fb.ty[i][r], 0), a.ntypes - 1);
+        fb.tb[i][r] = tb_clz[tp * 32 + clz];
+      }
     }
 }
 
-template <int HPB>
-__device__ __forceinline__ void fast_bias_store(const FastBias<512 / (64 * HPB)>& fb, float* bias, int tid) {
+template <int HPB, int MODE>
+__device__ __forceinline__ void fast_bias_store(const AttnArgs& a, const FastBias<512 / (64 * HPB)>& fb, float* bias,
+                                                int tid) {
   constexpr int NT = 64 * HPB;
   constexpr int SPT = 512 / NT;
 #pragma unroll
@@ -360,7 +407,10 @@ __device__ __forceinline__ void fast_bias_store(const FastBias<512 / (64 * HPB)>
       // wait for every LDS read in flight
       float tb = fb.tb[i][r];
       asm volatile("" : "+v"(tb));
-      b[r] = __builtin_fmaf(fb.pw[i][r], -kLog2e, tb);
+      if constexpr (MODE == kBiasLinear)
+        b[r] = kLog2e * __builtin_fmaf(a.m_p, fb.pw[i][r], tb);
+      else
+        b[r] = __builtin_fmaf(fb.pw[i][r], -kLog2e, tb);
     }
     *reinterpret_cast<float4*>(&bias[slot * 4]) = make_float4(b[0], b[1], b[2], b[3]);
   }
@@ -388,7 +438,7 @@ __device__ __forceinline__ void dma_slot(const Ctx& c, const uint16_t* kbase_o, 
 // a DMA into the next buffers does not alias the reads of the current ones,
 // and issues the DMA early without making those reads wait for it. MORE: a
 // later tile of the chunk follows (its DMA, key data and bias).
-template <int HPB, bool MORE>
+template <int HPB, bool MORE, int MODE>
 __device__ __forceinline__ void attn_step(
     const Ctx& c, const SlotQ<512 / (64 * HPB)>& sq, const AttnArgs& a, int st, int st_hi, int skip_a,
     int n_skip, const uint8_t* __restrict__ curK, const float* __restrict__ curB,
@@ -408,10 +458,10 @@ __device__ __forceinline__ void attn_step(
   // A0: the key-data reads of tile st+1's bias go first, so that their
   // dependent time-bias lookups are not queued behind this step's big LDS
   // reads; DMA of the key data of tile st+2 and a quarter of the K/V rows
-  if (MORE) fast_bias_issue<HPB>(c, sq, *nxtD, t1, tid, fb);
+  if (MORE) fast_bias_issue<HPB, MODE>(c, sq, *nxtD, t1, tid, fb);
   if (MORE && st + 2 < st_hi) {
     const int t2 = st + 2 < skip_a ? st + 2 : st + 2 + n_skip;
-    load_keydata<HPB>(c, a.ts, a.c_ts, a.pos_bias, *curD, t2, wave, lane);
+    load_keydata<HPB, MODE>(c, a, *curD, t2, wave, lane);
   }
   if (MORE) {
     dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, nxtK, nxtV, k1, 0, wave, lane);
@@ -468,10 +518,10 @@ __device__ __forceinline__ void attn_step(
 #pragma unroll
     for (int sr = 0; sr < 4; ++sr) {
       silu4(s0, sr, w[2 * sr], w[2 * sr + 1]);
-      if (MORE && sr == 0) fast_bias_lookup<HPB>(c, sq, tb_clz, fb);
+      if (MORE && sr == 0) fast_bias_lookup<HPB, MODE>(c, a, sq, tb_clz, fb);
       // the store waits for every LDS read issued before it (the DMA keeps
       // the compiler from counting partially): last, after the MFMAs
-      if (MORE && sr == 3) fast_bias_store<HPB>(fb, nxtB, tid);
+      if (MORE && sr == 3) fast_bias_store<HPB, MODE>(a, fb, nxtB, tid);
       // two score MFMAs every other quarter: the block-1 bias read last in
       // R0 has time to land
       if (sr & 1) {
@@ -488,7 +538,7 @@ __device__ __forceinline__ void attn_step(
     asm volatile("" ::"v"(w[7]));
   }
   // tiles off the fast path: the full bias builder overwrites the tile
-  if (MORE && !fast1) build_bias<HPB>(c, sq, *nxtD, nxtB, tb_clz, tb_lin, a.nb, t1, tid);
+  if (MORE && !fast1) build_bias<HPB, MODE>(c, a, sq, *nxtD, nxtB, tb_clz, tb_lin, t1, tid);
   if (MORE) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -645,7 +695,7 @@ __global__ __launch_bounds__(1024) void attn_schedule_kernel(AttnArgs a, int n_q
   }
 }
 
-template <int HPB, bool FUSE_NG>
+template <int HPB, bool FUSE_NG, int MODE>
 __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
   constexpr int NT = 64 * HPB;
   constexpr int ROWBK = Rows<HPB>::ROWBK;
@@ -664,8 +714,10 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float sB0[kBM * kBN];
   __shared__ __attribute__((aligned(16))) float sB1[kBM * kBN];
   __shared__ KeyData sD0, sD1;
-  __shared__ float tb_clz[32];   // base-2 time bias indexed by clz(|dt|+1)
-  __shared__ float tb_lin[64];   // base-2 time bias indexed by bucket
+  // base-2 time tables: (type pair) * 32 + clz(|dt|+1) and (type pair) * 64 + bucket
+  constexpr int kPairs = MODE == kBiasTyped ? kMaxTypePairs : 1;
+  __shared__ float tb_clz[kPairs * 32];
+  __shared__ float tb_lin[kPairs * 64];
   __shared__ int64_t red_min[HPB], red_max[HPB];
 
   // Work items of this workgroup: workgroup g runs on XCD g % 8 and takes
@@ -724,9 +776,14 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
       red_max[wave] = tmax;
     }
     // time tables in the base-2 domain
-    for (int i = tid; i < 64; i += NT) {
-      tb_lin[i] = -kLog2e * a.time_bias[min(i, a.nb - 1)];
-      if (i < 32) tb_clz[i] = -kLog2e * a.time_bias[min(31 - i, a.nb - 1)];  // clz i <=> bucket 31-i
+    if (MODE != kBiasLinear) {
+      const int pairs = MODE == kBiasTyped ? a.ntypes * a.ntypes : 1;
+      for (int i = tid; i < pairs * 64; i += NT) {
+        const int tp = i >> 6, b = i & 63;
+        tb_lin[i] = -kLog2e * a.time_bias[tp * a.nb + min(b, a.nb - 1)];
+        if (b < 32)   // clz b <=> bucket 31 - b
+          tb_clz[tp * 32 + b] = -kLog2e * a.time_bias[tp * a.nb + min(31 - b, a.nb - 1)];
+      }
     }
     __syncthreads();
     tmin = red_min[0];
@@ -766,6 +823,7 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
     sq.pq[i] = c.nc + min(qi, c.first_tgt);
     const int64_t tq = a.ts[si.s + min(qi, si.L - 1)];
     sq.tq[i] = tq;
+    sq.ty[i] = MODE == kBiasTyped ? min(max(a.types[si.s + min(qi, si.L - 1)], 0), a.ntypes - 1) * a.ntypes : 0;
     sq.uq[i] = static_cast<uint32_t>(tq) - c.tb_lo;
   }
 
@@ -824,8 +882,8 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
 #define SB(i) ((i) ? sB1 : sB0)
 #define SD(i) ((i) ? &sD1 : &sD0)
   // ---- prologue: key data of tiles lo and lo+1, K/V rows and bias of tile lo ----
-  load_keydata<HPB>(c, a.ts, a.c_ts, a.pos_bias, sD0, tile_of(st_lo), wave, lane);
-  load_keydata<HPB>(c, a.ts, a.c_ts, a.pos_bias, sD1, tile_of(min(st_lo + 1, st_hi - 1)), wave, lane);
+  load_keydata<HPB, MODE>(c, a, sD0, tile_of(st_lo), wave, lane);
+  load_keydata<HPB, MODE>(c, a, sD1, tile_of(min(st_lo + 1, st_hi - 1)), wave, lane);
   {
     const int k0 = tile_of(st_lo) * kBN;
 #pragma unroll
@@ -836,7 +894,7 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  build_bias<HPB>(c, sq, sD0, sB0, tb_clz, tb_lin, a.nb, tile_of(st_lo), tid);
+  build_bias<HPB, MODE>(c, a, sq, sD0, sB0, tb_clz, tb_lin, tile_of(st_lo), tid);
   __syncthreads();
 
   // Software pipeline in half tiles. Registers carried from step st-1 to
@@ -865,7 +923,7 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
     for (int kh = 0; kh < 2; ++kh) vf[db][kh] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
   // steps alternate between the two buffer sets
 #define HSTU_ATTN_STEP(MORE, K0, B0, V0, K1, V1, B1, D1, D0)                                          \
-  attn_step<HPB, MORE>(c, sq, a, st, st_hi, skip_a, n_skip, K0, B0, V0, K1, V1, B1, D1, D0, tb_clz,  \
+  attn_step<HPB, MORE, MODE>(c, sq, a, st, st_hi, skip_a, n_skip, K0, B0, V0, K1, V1, B1, D1, D0, tb_clz,  \
                        tb_lin, kbase_o, kbase_c, vbase_o, vbase_c, qf, acc, s0, s1, vf, koff, voff,      \
                        wave, lane, tid)
   int st = st_lo;
@@ -962,6 +1020,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   __shared__ float sk[64][DH];
   __shared__ float sv[64][DH];
   __shared__ int64_t skt[64];
+  __shared__ int sty[64];
   const int seq = blockIdx.x;
   const int qt = blockIdx.y;
   const int h = blockIdx.z;
@@ -984,6 +1043,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   }
   const int pq = si.nc + (qi < first_tgt ? qi : first_tgt);
   const int64_t tq = qvalid ? a.ts[si.s + qi] : 0;
+  const int nt = a.ntypes;
+  // token types outside [0, nt) are clamped (hstu_check_inputs reports them)
+  const int tyq = nt > 1 && qvalid ? min(max(a.types[si.s + qi], 0), nt - 1) : 0;
   const int q_hi = min(qt * 64 + 64, si.L);
   const int nkeys = si.nc + q_hi;
   for (int k0 = 0; k0 < nkeys; k0 += 64) {
@@ -1004,6 +1066,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
     {
       const int kk = k0 + threadIdx.x;
       skt[threadIdx.x] = kk < nkeys ? (kk < si.nc ? a.c_ts[si.cs + kk] : a.ts[si.s + kk - si.nc]) : 0;
+      sty[threadIdx.x] = nt > 1 && kk < nkeys
+                             ? min(max(kk < si.nc ? a.c_types[si.cs + kk] : a.types[si.s + kk - si.nc], 0), nt - 1)
+                             : 0;
     }
     __syncthreads();
     const int kend = min(64, nkeys - k0);
@@ -1018,9 +1083,17 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 #pragma unroll
       for (int c = 0; c < DH; ++c) dot = fmaf(qv[c], sk[r][c], dot);
       const int pk = cache ? kk : si.nc + (j < first_tgt ? j : first_tgt);
-      int pidx = pq - pk + a.pos_center;
-      pidx = pidx < 0 ? 0 : (pidx >= a.pos_len ? a.pos_len - 1 : pidx);
-      const float s = a.alpha * dot + a.pos_bias[pidx] + a.time_bias[time_bucket64(tq - skt[r], a.nb)];
+      const int bucket = time_bucket64(tq - skt[r], a.nb);
+      float rab;
+      if (a.linear) {
+        // the parameter-free bias -m_p (p_i - p_j) - m_t bucket
+        rab = -a.m_p * static_cast<float>(pq - pk) - a.m_t * static_cast<float>(bucket);
+      } else {
+        int pidx = pq - pk + a.pos_center;
+        pidx = pidx < 0 ? 0 : (pidx >= a.pos_len ? a.pos_len - 1 : pidx);
+        rab = a.pos_bias[pidx] + a.time_bias[(tyq * nt + sty[r]) * a.nb + bucket];
+      }
+      const float s = a.alpha * dot + rab;
       const float w = s / (1.0f + expf(-s));
 #pragma unroll
       for (int c = 0; c < DH; ++c) acc[c] = fmaf(w, sv[r][c], acc[c]);
@@ -1090,6 +1163,18 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(const float* __restric
   }
 }
 
+namespace {
+template <bool FUSE_NG, int MODE>
+void launch_attn_kernel(int hpb, dim3 grid, const AttnArgs& a, hipStream_t s) {
+  switch (hpb) {
+    case 8: hipLaunchKernelGGL((attn_bf16_kernel<8, FUSE_NG, MODE>), grid, dim3(512), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((attn_bf16_kernel<4, FUSE_NG, MODE>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((attn_bf16_kernel<2, FUSE_NG, MODE>), grid, dim3(128), 0, s, a); break;
+    default: hipLaunchKernelGGL((attn_bf16_kernel<1, FUSE_NG, MODE>), grid, dim3(64), 0, s, a); break;
+  }
+}
+}  // namespace
+
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   const int n_qt = (a.max_seq_len + kBM - 1) / kBM;
   if (a.num_seqs == 0 || n_qt == 0) return hipSuccess;
@@ -1103,19 +1188,18 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   const int hpb = v1_heads_per_group(a.num_heads);
   const dim3 grid(gx, a.num_heads / hpb);
+  const int mode = a.linear ? kBiasLinear : (a.ntypes > 1 ? kBiasTyped : kBiasTables);
   if (a.fuse_ng) {
-    switch (hpb) {
-      case 8: hipLaunchKernelGGL((attn_bf16_kernel<8, true>), grid, dim3(512), 0, s, a); break;
-      case 4: hipLaunchKernelGGL((attn_bf16_kernel<4, true>), grid, dim3(256), 0, s, a); break;
-      case 2: hipLaunchKernelGGL((attn_bf16_kernel<2, true>), grid, dim3(128), 0, s, a); break;
-      default: hipLaunchKernelGGL((attn_bf16_kernel<1, true>), grid, dim3(64), 0, s, a); break;
+    switch (mode) {
+      case kBiasTyped: launch_attn_kernel<true, kBiasTyped>(hpb, grid, a, s); break;
+      case kBiasLinear: launch_attn_kernel<true, kBiasLinear>(hpb, grid, a, s); break;
+      default: launch_attn_kernel<true, kBiasTables>(hpb, grid, a, s); break;
     }
   } else {
-    switch (hpb) {
-      case 8: hipLaunchKernelGGL((attn_bf16_kernel<8, false>), grid, dim3(512), 0, s, a); break;
-      case 4: hipLaunchKernelGGL((attn_bf16_kernel<4, false>), grid, dim3(256), 0, s, a); break;
-      case 2: hipLaunchKernelGGL((attn_bf16_kernel<2, false>), grid, dim3(128), 0, s, a); break;
-      default: hipLaunchKernelGGL((attn_bf16_kernel<1, false>), grid, dim3(64), 0, s, a); break;
+    switch (mode) {
+      case kBiasTyped: launch_attn_kernel<false, kBiasTyped>(hpb, grid, a, s); break;
+      case kBiasLinear: launch_attn_kernel<false, kBiasLinear>(hpb, grid, a, s); break;
+      default: launch_attn_kernel<false, kBiasTables>(hpb, grid, a, s); break;
     }
   }
   if (a.splits > 1) {

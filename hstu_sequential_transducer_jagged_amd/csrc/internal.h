@@ -21,7 +21,12 @@ struct AttnArgs {
   const int64_t* c_offsets;  // [B+1] or null
   const int64_t* c_ts;       // [Tc] or null
   const float* pos_bias;     // [pos_len]
-  const float* time_bias;    // [nb]
+  const float* time_bias;    // [ntypes^2 * nb]: one table per (query type, key type) pair
+  const int32_t* types;      // [T] token types (ntypes > 1) or null
+  const int32_t* c_types;    // [Tc] cached token types (ntypes > 1) or null
+  int ntypes;                // 1: untyped rab
+  int linear;                // 1: parameter-free bias -m_p dp - m_t bucket, no tables
+  float m_p, m_t;
   float* av;                 // [T, d] fp32 out
   int d_model;
   int num_heads;
@@ -233,9 +238,10 @@ struct CacheConcatArgs {
 };
 hipError_t launch_cache_concat(const CacheConcatArgs& a, hipStream_t s);
 
-// pos[i] = -m_p * (i - (len - 1) / 2), time[b] = -m_t * b: the tables that
-// make the table bias equal the parameter-free position/time bias.
-hipError_t launch_linear_bias_tables(float m_p, float m_t, int pos_len, int num_buckets,
+// pos[i] = -m_p * (i - (len - 1) / 2), time[p * nb + b] = -m_t * b for each
+// of `pairs` type-pair tables: the tables that make the table bias equal the
+// parameter-free position/time bias.
+hipError_t launch_linear_bias_tables(float m_p, float m_t, int pos_len, int num_buckets, int pairs,
                                      float* pos, float* time, hipStream_t s);
 
 struct EmbedArgs {

@@ -106,13 +106,14 @@ __global__ __launch_bounds__(256) void layernorm_kernel(LayerNormArgs a) {
 
 // pos_len = 2 n_max - 1 entries, entry i <-> p_i - p_j = i - (n_max - 1)
 __global__ __launch_bounds__(256) void linear_bias_tables_kernel(float m_p, float m_t, int pos_len,
-                                                                 int num_buckets, float* pos,
+                                                                 int num_buckets, int pairs, float* pos,
                                                                  float* time) {
   const int half = (pos_len - 1) / 2;
   for (int i = blockIdx.x * 256 + threadIdx.x; i < pos_len; i += gridDim.x * 256)
     pos[i] = -m_p * static_cast<float>(i - half);
   if (blockIdx.x == 0)
-    for (int b = threadIdx.x; b < num_buckets; b += 256) time[b] = -m_t * static_cast<float>(b);
+    for (int i = threadIdx.x; i < pairs * num_buckets; i += 256)
+      time[i] = -m_t * static_cast<float>(i % num_buckets);
 }
 
 __global__ __launch_bounds__(256) void cache_concat_kernel(CacheConcatArgs a) {
@@ -240,11 +241,11 @@ hipError_t launch_layernorm_f32(const LayerNormArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_linear_bias_tables(float m_p, float m_t, int pos_len, int num_buckets, float* pos,
-                                     float* time, hipStream_t s) {
+hipError_t launch_linear_bias_tables(float m_p, float m_t, int pos_len, int num_buckets, int pairs,
+                                     float* pos, float* time, hipStream_t s) {
   const int grid = (pos_len + 255) / 256;
   hipLaunchKernelGGL(linear_bias_tables_kernel, dim3(grid > 0 ? grid : 1), dim3(256), 0, s, m_p, m_t,
-                     pos_len, num_buckets, pos, time);
+                     pos_len, num_buckets, pairs, pos, time);
   return hipGetLastError();
 }
 

@@ -25,6 +25,9 @@ HSTU_E_DEVICE = -4
 HSTU_E_DATA = -5
 HSTU_F32 = 0
 HSTU_BF16 = 1
+HSTU_BIAS_TABLES = 0
+HSTU_BIAS_LINEAR = 1
+HSTU_MAX_TOKEN_TYPES = 4
 
 EXPORTS = ("hstu_abi_version", "hstu_last_error", "hstu_proj_fwd", "hstu_attn_workspace_size",
            "hstu_attn_fwd", "hstu_attn_fwd_noalloc",
@@ -47,19 +50,23 @@ class LayerDesc(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("alpha", ctypes.c_float), ("ln_eps", ctypes.c_float),
                 ("pos_table_len", ctypes.c_int32), ("num_time_buckets", ctypes.c_int32),
-                ("input_norm", ctypes.c_int32), ("target_no_self", ctypes.c_int32)]
+                ("input_norm", ctypes.c_int32), ("target_no_self", ctypes.c_int32),
+                ("num_token_types", ctypes.c_int32), ("bias_mode", ctypes.c_int32),
+                ("linear_m_p", ctypes.c_float), ("linear_m_t", ctypes.c_float)]
 
 
 class Jagged(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
                 ("total_tokens", ctypes.c_int64), ("offsets", ctypes.c_void_p),
-                ("timestamps", ctypes.c_void_p), ("num_targets", ctypes.c_void_p)]
+                ("timestamps", ctypes.c_void_p), ("num_targets", ctypes.c_void_p),
+                ("token_types", ctypes.c_void_p)]
 
 
 class KVCache(ctypes.Structure):
     _fields_ = [("offsets", ctypes.c_void_p), ("timestamps", ctypes.c_void_p),
                 ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
-                ("max_len", ctypes.c_int32), ("total_tokens", ctypes.c_int64)]
+                ("max_len", ctypes.c_int32), ("total_tokens", ctypes.c_int64),
+                ("token_types", ctypes.c_void_p)]
 
 
 class LayerParams(ctypes.Structure):
@@ -148,21 +155,28 @@ def current_stream() -> int:
 
 def make_desc(d_model: int, num_heads: int, dtype: int, pos_table_len: int,
               alpha: float = 1.0, ln_eps: float = 1e-5, num_time_buckets: int = 32,
-              input_norm: bool = False, target_no_self: bool = False) -> LayerDesc:
+              input_norm: bool = False, target_no_self: bool = False,
+              num_token_types: int = 0, bias_mode: int = HSTU_BIAS_TABLES,
+              linear_m_p: float = 0.0, linear_m_t: float = 0.0) -> LayerDesc:
     return LayerDesc(d_model, num_heads, d_model // num_heads, dtype, alpha, ln_eps,
-                     pos_table_len, num_time_buckets, int(bool(input_norm)), int(bool(target_no_self)))
+                     pos_table_len, num_time_buckets, int(bool(input_norm)), int(bool(target_no_self)),
+                     int(num_token_types), int(bias_mode), float(linear_m_p), float(linear_m_t))
 
 
-def make_jagged(offsets, timestamps, max_seq_len: int, num_targets=None) -> Jagged:
-    """offsets: int64 device tensor [B+1]; timestamps: int64 device [T]."""
+def make_jagged(offsets, timestamps, max_seq_len: int, num_targets=None,
+                token_types=None) -> Jagged:
+    """offsets: int64 device tensor [B+1]; timestamps: int64 device [T];
+    num_targets: int32 device [B] or None; token_types: int32 device [T] or None."""
     B = offsets.numel() - 1
     T = int(offsets[-1].item()) if B > 0 else 0
-    return Jagged(B, int(max_seq_len), T, ptr(offsets), ptr(timestamps), ptr(num_targets))
+    return Jagged(B, int(max_seq_len), T, ptr(offsets), ptr(timestamps), ptr(num_targets),
+                  ptr(token_types))
 
 
-def make_cache(offsets, timestamps, k, v, max_len: int) -> KVCache:
+def make_cache(offsets, timestamps, k, v, max_len: int, token_types=None) -> KVCache:
     T = int(offsets[-1].item()) if offsets.numel() > 1 else 0
-    return KVCache(ptr(offsets), ptr(timestamps), ptr(k), ptr(v), int(max_len), T)
+    return KVCache(ptr(offsets), ptr(timestamps), ptr(k), ptr(v), int(max_len), T,
+                   ptr(token_types))
 
 
 def make_params(w1, b1, w2, b2, gamma, beta, pos_bias, time_bias, ln1_gamma=None,

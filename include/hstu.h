@@ -18,6 +18,10 @@
  * is shared by all heads; position and real-time differences follow
  * §7.1.4 innovation 2 of the chapter-7.1 page, the bucketed time difference
  * eq. 6.2.6 of "6.2. HSTU的工程突破". The floor(log2) is exact (integer).
+ * Two options of the same term (hstu_layer_desc): token types, where the
+ * time table is one table per ordered (query type, key type) pair, the
+ * type-aware bias of §7.1.4 innovation 2; and the parameter-free bias of
+ * eq. 6.2.6, -m_p (p_i - p_j) - m_t bucket, computed in the kernels.
  *
  * Visibility. Within sequence b the keys are [the cache rows of b, then the
  * call's own tokens of b]. Key j is visible to query i iff j is a cache row,
@@ -57,7 +61,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 8
+#define HSTU_ABI_VERSION 9
 
 typedef enum {
   HSTU_OK = 0,
@@ -69,6 +73,11 @@ typedef enum {
 } hstu_status;
 
 typedef enum { HSTU_F32 = 0, HSTU_BF16 = 1 } hstu_dtype;
+
+/* Source of rab (hstu_layer_desc.bias_mode). */
+typedef enum { HSTU_BIAS_TABLES = 0, HSTU_BIAS_LINEAR = 1 } hstu_bias_mode;
+
+#define HSTU_MAX_TOKEN_TYPES 4
 
 /* Host-side layer description, passed by pointer, read during the call only. */
 typedef struct {
@@ -88,6 +97,21 @@ typedef struct {
                                non-targets only, not itself (the literal reading of the
                                M-FALCON mask of "HSTU：Scaling Law 的首次探索" §7.1.5:
                                a candidate attends to the user history) */
+  int32_t num_token_types;  /* 0 or 1 (default): untyped rab. 2..HSTU_MAX_TOKEN_TYPES: the
+                               type-aware rab of "HSTU：Scaling Law 的首次探索" §7.1.4
+                               innovation 2 (content and action tokens decay differently):
+                               time_bias then holds num_token_types^2 tables of
+                               num_time_buckets entries, the pair (query type a, key type b)
+                               at offset (a * num_token_types + b) * num_time_buckets; the
+                               position table stays shared. Token types come from
+                               hstu_jagged.token_types (and the cache's); forward only */
+  int32_t bias_mode;        /* hstu_bias_mode. HSTU_BIAS_LINEAR: rab(i, j) = -linear_m_p
+                               (p_i - p_j) - linear_m_t bucket(t_i - t_j), the parameter-free
+                               bias of "6.2. HSTU的工程突破" eq. 6.2.6 (slopes shared by all
+                               heads), computed by the kernels with no tables: pos_bias and
+                               time_bias are not read (may be NULL). Untyped, forward only */
+  float linear_m_p;         /* slopes of HSTU_BIAS_LINEAR, finite */
+  float linear_m_t;
 } hstu_layer_desc;
 
 /* A jagged batch of the call's own tokens. */
@@ -99,6 +123,8 @@ typedef struct {
   const int64_t *timestamps;    /* device [T], int64 seconds (any order) */
   const int32_t *num_targets;   /* device [B] or NULL: the last m_b tokens of b are targets,
                                    0 <= m_b <= L_b */
+  const int32_t *token_types;   /* device [T] with num_token_types > 1 (each in
+                                   [0, num_token_types)), else unused (may be NULL) */
 } hstu_jagged;
 
 /* Optional cached history (keys/values visible to every own token of the
@@ -110,6 +136,7 @@ typedef struct {
   const void *v;                /* device [cache_T, d_model], dtype */
   int32_t max_len;              /* >= every cache length (host) */
   int64_t total_tokens;         /* cache_T (host) */
+  const int32_t *token_types;   /* device [cache_T] with num_token_types > 1, else unused */
 } hstu_kv_cache;
 
 /* Layer parameters: device pointers, caller-owned. */
@@ -120,8 +147,9 @@ typedef struct {
   const float *b2;              /* [d] or NULL (zeros) */
   const float *ln_gamma;        /* [d] or NULL (ones) */
   const float *ln_beta;         /* [d] or NULL (zeros) */
-  const float *pos_bias;        /* [pos_table_len] */
-  const float *time_bias;       /* [num_time_buckets] */
+  const float *pos_bias;        /* [pos_table_len]; unused with HSTU_BIAS_LINEAR */
+  const float *time_bias;       /* [num_time_buckets], or [T^2 * num_time_buckets] with
+                                   T = num_token_types > 1; unused with HSTU_BIAS_LINEAR */
   const float *ln1_gamma;       /* [d] or NULL (ones): input LayerNorm, read if input_norm */
   const float *ln1_beta;        /* [d] or NULL (zeros) */
 } hstu_layer_params;
@@ -166,7 +194,10 @@ size_t hstu_attn_workspace_size(const hstu_layer_desc *desc, const hstu_jagged *
  * and bias rules above:
  *   av[i, h*dh:(h+1)*dh] = sum_{j visible} SiLU(alpha q_i.k_j + rab(i, j)) v_j
  * q, k, v [T, d] (dtype, own tokens of `jagged`); cache may be NULL;
- * pos_bias [pos_table_len], time_bias [num_time_buckets] (fp32);
+ * pos_bias [pos_table_len], time_bias [num_time_buckets], or
+ * [num_token_types^2 * num_time_buckets] with token types (fp32; neither is
+ * read with HSTU_BIAS_LINEAR); token types outside [0, num_token_types) are
+ * clamped by the kernels (hstu_check_inputs() reports them);
  * av [T, d] fp32 output. workspace: device, 256-byte aligned, at least
  * hstu_attn_workspace_size() bytes (may be NULL when that is 0); its
  * contents are scratch. Every visible position difference must lie in
@@ -223,8 +254,11 @@ int hstu_layernorm_fwd(const hstu_layer_desc *desc, int64_t T, const void *x, co
  *   time_bias[b] = -m_t * b                     b < num_time_buckets
  * With them, the table bias of every entry point equals
  * -m_p (p_i - p_j) - m_t bucket(t_i - t_j) exactly up to one fp32 rounding
- * of each product. pos_bias [pos_table_len], time_bias [num_time_buckets]:
- * device fp32 outputs, overwritten. m_p, m_t finite. */
+ * of each product. pos_bias [pos_table_len], time_bias [num_time_buckets]
+ * (with num_token_types > 1, every one of the T^2 pair tables gets the same
+ * values): device fp32 outputs, overwritten. m_p, m_t finite.
+ * desc->bias_mode = HSTU_BIAS_LINEAR computes the same bias inside the
+ * attention kernels instead, with no tables. */
 int hstu_linear_bias_tables(const hstu_layer_desc *desc, float m_p, float m_t, float *pos_bias,
                             float *time_bias, void *stream);
 
@@ -304,7 +338,8 @@ size_t hstu_layer_bwd_workspace_size(const hstu_layer_desc *desc, const hstu_jag
  * (params ln1_gamma/ln1_beta, NULL meaning ones/zeros) into dx, and
  * grads->dln1_gamma/dln1_beta must be set.
  * Supported: dtype HSTU_F32, plain causal attention (jagged->num_targets
- * NULL, no cache), total_tokens and max_seq_len * d_model below 2^31,
+ * NULL, no cache), the untyped table bias (num_token_types <= 1,
+ * HSTU_BIAS_TABLES), total_tokens and max_seq_len * d_model below 2^31,
  * d_model <= 1024; else HSTU_E_UNSUPPORTED.
  * x, dy, dx [T, d] fp32 (dx must not alias x or dy); grads: all eight
  * pointers non-NULL. workspace: device, 256-byte aligned, >=
@@ -346,8 +381,9 @@ int hstu_embed_fwd(int64_t T, int32_t d_model, int32_t dtype, const void *item_e
 /* Debug validation of device-resident index data (copies it to the host and
  * synchronises `stream`): offsets start at 0, do not decrease and end at T;
  * max_seq_len bounds every length; 0 <= num_targets[b] <= L_b; the cache
- * offsets likewise; every visible position difference fits the table. Returns
- * HSTU_OK or HSTU_E_DATA (with a message). */
+ * offsets likewise; every visible position difference fits the table; with
+ * num_token_types > 1 every token type (own and cached) lies in
+ * [0, num_token_types). Returns HSTU_OK or HSTU_E_DATA (with a message). */
 int hstu_check_inputs(const hstu_layer_desc *desc, const hstu_jagged *jagged,
                       const hstu_kv_cache *cache, void *stream);
 

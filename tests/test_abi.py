@@ -35,7 +35,7 @@ def test_header_declares_the_binding_exports():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.hstu_abi_version() == 8
+    assert lib.hstu_abi_version() == 9
 
 
 def _desc(**kw):
@@ -262,3 +262,55 @@ def test_noalloc_rejects_a_work_list_larger_than_its_scratch(lib):
                                    P(FAKE), P(FAKE), P(FAKE), None)
     assert st == hstu.HSTU_E_WORKSPACE
     assert b"static scratch" in lib.hstu_last_error()
+
+
+def test_bias_mode_and_token_type_validation(lib):
+    """The type-aware rab and the in-kernel parameter-free bias: descriptor
+    and pointer checks made on the host before any launch."""
+    P = ctypes.c_void_p
+    d = _desc()
+    d.num_token_types = hstu.HSTU_MAX_TOKEN_TYPES + 1
+    assert _attn(lib, d, _jag()) == hstu.HSTU_E_INVAL
+    d = _desc()
+    d.num_token_types = -1
+    assert _attn(lib, d, _jag()) == hstu.HSTU_E_INVAL
+    d = _desc()
+    d.bias_mode = 2
+    assert _attn(lib, d, _jag()) == hstu.HSTU_E_INVAL
+    d = _desc()
+    d.bias_mode = hstu.HSTU_BIAS_LINEAR
+    d.linear_m_p = float("inf")
+    assert _attn(lib, d, _jag()) == hstu.HSTU_E_INVAL
+    d = _desc()
+    d.bias_mode = hstu.HSTU_BIAS_LINEAR
+    d.num_token_types = 2
+    assert _attn(lib, d, _jag()) == hstu.HSTU_E_UNSUPPORTED
+    # typed: token types must be given for own tokens and for a non-empty cache
+    d = _desc()
+    d.num_token_types = 3
+    assert _attn(lib, d, _jag()) == hstu.HSTU_E_INVAL
+    assert b"token_types" in lib.hstu_last_error()
+    j = _jag()
+    j.token_types = FAKE
+    cache = hstu.KVCache(FAKE, FAKE, FAKE, FAKE, 8, 100)
+    d.pos_table_len = 255
+    assert _attn(lib, d, j, cache) == hstu.HSTU_E_INVAL
+    assert b"cache token_types" in lib.hstu_last_error()
+    # the parameter-free bias reads no tables and no position bound applies
+    d = _desc(pos_table_len=3)
+    d.bias_mode = hstu.HSTU_BIAS_LINEAR
+    st = lib.hstu_attn_fwd(ctypes.byref(d), ctypes.byref(_jag(B=0, T=0, mx=0)), None, P(FAKE),
+                           P(FAKE), P(FAKE), None, None, P(FAKE), None, 0, None)
+    assert st == hstu.HSTU_OK
+    d = _desc(pos_table_len=3)                                 # tables: n_max 2 < 6
+    assert _attn(lib, d, _jag()) == hstu.HSTU_E_INVAL
+    # the backward pass takes the untyped table bias only
+    f = hstu.make_desc(64, 1, hstu.HSTU_F32, 255, num_token_types=2)
+    params = hstu.LayerParams(*([FAKE] * 8))
+    grads = hstu.LayerGrads(*([FAKE] * 10))
+    j = _jag()
+    j.token_types = FAKE
+    assert lib.hstu_layer_bwd(ctypes.byref(f), ctypes.byref(params), ctypes.byref(j), P(FAKE),
+                              P(FAKE), P(FAKE + 4096), ctypes.byref(grads), P(FAKE), 1 << 30,
+                              None) == hstu.HSTU_E_UNSUPPORTED
+    assert b"untyped table bias" in lib.hstu_last_error()
