@@ -70,6 +70,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
                     help="approximate CPU seconds for the oracle sample")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the measured MFMA-loop, copy and clock probes")
     ap.add_argument("--copy-calib", action="store_true",
                     help="first run a plain elementwise copy of known size (512 MiB read, "
                          "512 MiB written) so that HBM counters can be scaled against it")
@@ -91,6 +93,23 @@ def copy_calibration(torch):
     del src, dst
     return {"kernel": "torch.neg bf16", "bytes_read": COPY_CALIB_BYTES,
             "bytes_written": COPY_CALIB_BYTES}
+
+
+def measured_peaks():
+    """What this GPU reaches beside the published peaks, measured before the
+    timed region: a loop of independent bf16 MFMAs with no memory traffic,
+    a 1 GiB streaming copy, and the shader clock under the MFMA load
+    (libhstu_probe.so)."""
+    from hstu_sequential_transducer_jagged_amd import probe
+    m = probe.mfma_bf16()
+    c = probe.copy_hbm()
+    return {"mfma_bf16_tflops": m["tflops"], "mfma_bf16_frac_of_spec": m["tflops"] / PEAK_BF16_TFLOPS,
+            "hbm_copy_gbs": c["gbs"], "hbm_copy_frac_of_spec": c["gbs"] / PEAK_HBM_GBS,
+            "shader_ghz_under_mfma": m["shader_ghz"],
+            "spec": {"mfma_bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS, "ghz": 2.4},
+            "probes": "MFMA loop: %d workgroups x 4 waves x %d rounds of four independent "
+                      "32x32x16 bf16 MFMAs; copy: %d MiB read + written, 16-byte vectors"
+                      % (m["groups"], m["iters"], c["bytes"] >> 20)}
 
 
 def visible_pairs(offsets):
@@ -199,6 +218,7 @@ def run_layer(args):
         rec()
 
     calib = copy_calibration(torch) if args.copy_calib else None
+    peaks = None if args.no_probes else measured_peaks()
     K = args.steps
 
     # the timed step: the whole layer through hstu_layer_fwd
@@ -235,6 +255,10 @@ def run_layer(args):
 
     attn_tflops = attn_flop / (attn_ms * 1e-3) / 1e12
     esz = 2 if w.dtype == "bf16" else 4
+    # the attention's compulsory HBM traffic: Q, K, V and the timestamps read
+    # once, AV (fp32) written once; the bias tables and offsets are noise
+    attn_bytes = T * d * 3 * esz + 8 * T + 4 * T * d
+    attn_gbs = attn_bytes / (attn_ms * 1e-3) / 1e9
     proj_flop, out_flop = 8.0 * T * d * d, 2.0 * T * d * d
     ng_bytes = T * d * (4 + esz + esz)        # read AV (fp32) and U, write G
     # both paths run on the matrix cores: bf16 MFMA, and fp32 16x16x4 MFMA
@@ -243,7 +267,9 @@ def run_layer(args):
         "proj": {"ms": pct(per["proj"]), "tflops": proj_flop / np.mean(per["proj"]) / 1e9,
                  "pct_peak": 100 * proj_flop / np.mean(per["proj"]) / 1e9 / peak},
         "attn": {"ms": pct(per["attn"]), "tflops": attn_tflops,
-                 "pct_peak": 100 * attn_tflops / peak},
+                 "pct_peak": 100 * attn_tflops / peak,
+                 "algorithmic_bytes": attn_bytes, "gbs": attn_gbs,
+                 "pct_hbm_peak": 100 * attn_gbs / PEAK_HBM_GBS},
         "norm_gate": {"ms": pct(per["norm_gate"]),
                       "gbs": ng_bytes / np.mean(per["norm_gate"]) / 1e6,
                       "pct_hbm_peak": 100 * ng_bytes / np.mean(per["norm_gate"]) / 1e6 / PEAK_HBM_GBS},
@@ -276,13 +302,21 @@ def run_layer(args):
                    "num_heads": H, "head_dim": d // H, "visible_pairs": P,
                    "input_norm": bool(args.input_norm),
                    "bias": ("parameter-free m_p=%g m_t=%g" % lin) if lin else "tables"},
-        "roofline": {"kernel": "attn_" + w.dtype, "bound": "mfma",
-                     "achieved": attn_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": attn_tflops / peak,
-                     "traffic": (traffic_record("attn_bf16", src)
-                                 if args.workload == 2 and not args.diag_lengths else None),
-                     "algorithmic_flop_per_launch": attn_flop,
-                     "avg_launch_ms": attn_ms},
+        "roofline": (
+            # short sequences (workload 1): each key tile serves few queries, so the
+            # attention is bound by its compulsory HBM traffic, not the matrix cores
+            {"kernel": "attn_" + w.dtype, "bound": "hbm", "achieved": attn_gbs,
+             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": attn_gbs / PEAK_HBM_GBS,
+             "traffic": None, "algorithmic_bytes_per_launch": attn_bytes,
+             "avg_launch_ms": attn_ms}
+            if args.workload == 1 and not args.diag_lengths else
+            {"kernel": "attn_" + w.dtype, "bound": "mfma",
+             "achieved": attn_tflops, "peak": peak, "unit": "TFLOP/s",
+             "frac": attn_tflops / peak,
+             "traffic": (traffic_record("attn_bf16", src)
+                         if args.workload == 2 and not args.diag_lengths else None),
+             "algorithmic_flop_per_launch": attn_flop,
+             "avg_launch_ms": attn_ms}),
         "attn_tflops": attn_tflops,
         "attn_pct_peak": 100.0 * attn_tflops / peak,
         "step_entry_point": "hstu_layer_fwd",
@@ -292,6 +326,12 @@ def run_layer(args):
         "graph_matches_bitwise": bool(torch.equal(y3, y2)),
         "kernels": kernels,
     }
+    if peaks is not None:
+        rec["measured_peaks"] = peaks
+        if w.dtype == "bf16":
+            rec["roofline"]["frac_of_measured_peak"] = (
+                attn_gbs / peaks["hbm_copy_gbs"] if rec["roofline"]["bound"] == "hbm"
+                else attn_tflops / peaks["mfma_bf16_tflops"])
     if calib is not None:
         rec["copy_calib"] = calib
     if not args.no_cpu_baseline:

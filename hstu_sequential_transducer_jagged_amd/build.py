@@ -14,7 +14,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhstu.so")
-SOURCES = ["api.cpp", "attn.hip", "attn_train.hip", "backward.hip", "gemm.hip", "gemm_f32.hip", "pointwise.hip", "sampler.cpp"]
+SOURCES = ["api.cpp", "plan.cpp", "attn.hip", "attn_train.hip", "backward.hip", "gemm.hip", "gemm_f32.hip",
+           "pointwise.hip", "sampler.cpp"]
+# measurement probes for the benchmark (include/hstu_probe.h), a library of their own
+PROBE_LIB = os.path.join(PKG, "libhstu_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"
 
 
@@ -42,18 +46,23 @@ def compile_one(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 4, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
+def link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int = 4, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(compile_one, SOURCES + PROBE_SOURCES))
+    link(objs[:len(SOURCES)], LIB)
+    link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

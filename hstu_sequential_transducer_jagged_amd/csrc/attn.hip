@@ -45,7 +45,7 @@
 namespace hstu {
 namespace {
 
-constexpr int kBM = 64;   // query rows per workgroup
+constexpr int kBM = kAttnBM;   // query rows per workgroup
 constexpr int kBN = 32;   // keys per step
 constexpr int kDH = 64;   // head dim of the bf16 kernel
 constexpr float kLog2e = 1.4426950408889634f;
@@ -560,9 +560,8 @@ __device__ __forceinline__ int tile_steps(const SeqInfo& si, int qt, int bm) {
 
 constexpr int kNumXcd = 8;            // XCDs of the chip; workgroup id -> XCD id % 8
 constexpr int kCostBuckets = 1024;    // cost classes of the per-XCD sort
-constexpr int kSchedHead = kNumXcd + 1;
-constexpr int64_t kSplitMinUnits = 512;  // below this many items, key ranges are split
-constexpr int kMaxSplits = 8;
+constexpr int kSchedHead = kAttnSchedHead;
+static_assert(kSchedHead == kNumXcd + 1, "work list header: one counter per XCD, then the total");
 
 // Key steps [lo, hi) of chunk c of an item with n steps: chunks of ceil(n / S)
 // steps; trailing chunks may be empty.
@@ -1107,42 +1106,6 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 
 }  // namespace
 
-namespace {
-// Heads per workgroup of the 64-query kernel: the largest of 8, 4, 2, 1
-// dividing the head count.
-int v1_heads_per_group(int num_heads) {
-  for (int c : {8, 4, 2, 1})
-    if (num_heads % c == 0) return c;
-  return 1;
-}
-}  // namespace
-
-AttnPlan attn_plan(int num_seqs, int max_seq_len, int num_heads, int64_t total_tokens, int d_model,
-                   int max_splits) {
-  AttnPlan p{};
-  p.bm = kBM;
-  p.heads_per_group = v1_heads_per_group(num_heads);
-  const int64_t n_qt = (static_cast<int64_t>(max_seq_len) + p.bm - 1) / p.bm;
-  const int64_t items = static_cast<int64_t>(num_seqs) * n_qt;
-  p.splits = (items <= 0 || items >= kSplitMinUnits)
-                 ? 1
-                 : static_cast<int>(std::min<int64_t>(kMaxSplits, (kSplitMinUnits + items - 1) / items));
-  p.splits = std::max(1, std::min(p.splits, max_splits));
-  const size_t sched = static_cast<size_t>(kSchedHead + items * p.splits) * sizeof(int);
-  p.sched_bytes = (sched + 255) & ~static_cast<size_t>(255);
-  const size_t partial =
-      p.splits > 1 ? static_cast<size_t>(p.splits) * total_tokens * d_model * sizeof(float) : 0;
-  p.workspace_bytes = p.sched_bytes + partial;
-  return p;
-}
-
-bool attn_can_fuse_norm_gate(int num_seqs, int max_seq_len, int num_heads, int64_t total_tokens,
-                             int d_model) {
-  // one head group covers each row, and no key-range splits
-  const AttnPlan p = attn_plan(num_seqs, max_seq_len, num_heads, total_tokens, d_model);
-  return p.heads_per_group == num_heads && num_heads <= 8 && p.splits == 1;
-}
-
 // AV = sum over chunks of the partial outputs, in chunk order (deterministic).
 __global__ __launch_bounds__(256) void attn_reduce_kernel(const float* __restrict__ partial,
                                                           float* __restrict__ av, int64_t n4,
@@ -1186,7 +1149,7 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.fuse_ng && (a.splits != 1 || !attn_can_fuse_norm_gate(a.num_seqs, a.max_seq_len, a.num_heads,
                                                               a.total_tokens, a.d_model)))
     return hipErrorInvalidValue;
-  const int hpb = v1_heads_per_group(a.num_heads);
+  const int hpb = attn_heads_per_group(a.num_heads);
   const dim3 grid(gx, a.num_heads / hpb);
   const int mode = a.linear ? kBiasLinear : (a.ntypes > 1 ? kBiasTyped : kBiasTables);
   if (a.fuse_ng) {

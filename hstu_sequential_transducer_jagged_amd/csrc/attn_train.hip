@@ -445,7 +445,6 @@ hipError_t launch_train(K kernel, const BwdAttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
-bool attn_train_supported(int head_dim) { return head_dim == 32 || head_dim == 64; }
 
 hipError_t launch_attn_train_fwd(const BwdAttnArgs& a, hipStream_t s) {
   return a.head_dim == 32 ? launch_train(attn_train_q_kernel<32, true>, a, s)

@@ -55,6 +55,17 @@ struct AttnArgs {
   float ng_eps;
 };
 
+// Work decomposition of the bf16 attention (shared by the host plan and the
+// kernels): queries per work item; the work list's header (one counter per
+// XCD, then the total) ahead of the item ids; below kAttnSplitMinUnits items
+// the key range of each item is split into up to kAttnMaxSplits chunks.
+constexpr int kAttnBM = 64;
+constexpr int kAttnSchedHead = 9;
+constexpr int64_t kAttnSplitMinUnits = 512;
+constexpr int kAttnMaxSplits = 8;
+// Heads per workgroup: the largest of 8, 4, 2, 1 dividing the head count.
+int attn_heads_per_group(int num_heads);
+
 // Launch plan of the bf16 attention for a batch shape: queries per work
 // item, heads per workgroup, key-range chunks per item (1 unless the batch has
 // too few items to fill the chip), and the workspace layout (the work list,

@@ -314,3 +314,23 @@ def test_bias_mode_and_token_type_validation(lib):
                               P(FAKE), P(FAKE + 4096), ctypes.byref(grads), P(FAKE), 1 << 30,
                               None) == hstu.HSTU_E_UNSUPPORTED
     assert b"untyped table bias" in lib.hstu_last_error()
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "hstu_probe.h")
+
+
+def test_probe_library_exports_its_header():
+    from hstu_sequential_transducer_jagged_amd import probe
+    text = open(PROBE_HEADER).read()
+    declared = sorted(set(re.findall(r"^\s*int\s*(hstu_probe_\w+)\s*\(", text, re.MULTILINE)))
+    assert declared == sorted(probe.EXPORTS)
+    if not os.path.exists(probe.LIB_PATH):
+        from hstu_sequential_transducer_jagged_amd import build
+        build.build()
+    lib = probe.load()
+    for name in declared:
+        assert hasattr(lib, name), name
+    # invalid arguments are refused before any launch (hipErrorInvalidValue = 1)
+    assert lib.hstu_probe_copy(ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 8), 16, None) == 1
+    assert lib.hstu_probe_copy(ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 64), 24, None) == 1
+    assert lib.hstu_probe_mfma_bf16(0, 1, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None) == 1
