@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="layer workloads: time the fp32 layer backward pass (hstu_layer_bwd) on the "
                          "workload's shape in fp32")
+    ap.add_argument("--attn-bwd-bf16", action="store_true",
+                    help="with --backward: the attention backward on the bf16 matrix cores "
+                         "(desc.attn_bwd_bf16); the all-fp32 backward is timed beside it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
                     help="approximate CPU seconds for the oracle sample")
@@ -449,6 +452,14 @@ def run_backward(args):
     g = [torch.empty(n, dtype=torch.float32, device="cuda") for n in
          (4 * d * d, 4 * d, d * d, d, d, d, 2 * w.n_max - 1, w.num_time_buckets, d, d)]
     grads = hstu.make_grads(*g)
+    ms_f32_bwd = None
+    if args.attn_bwd_bf16:
+        # the fp32 backward first, for comparison; then the timed one with the flag
+        ws32 = hstu.workspace_tensor(hstu.hstu_layer_bwd_workspace_size(lay.desc, dw.jagged))
+        ms_f32_bwd = timed(lambda: hstu.hstu_layer_bwd(lay.desc, lay.params, dw.jagged, dw.x, dy, dx, grads,
+                                                       ws32, sh), stream, args.warmup, args.steps)
+        del ws32
+        lay.desc.attn_bwd_bf16 = 1
     ws = hstu.workspace_tensor(hstu.hstu_layer_bwd_workspace_size(lay.desc, dw.jagged))
     ms = timed(lambda: hstu.hstu_layer_bwd(lay.desc, lay.params, dw.jagged, dw.x, dy, dx, grads, ws, sh),
                stream, args.warmup, args.steps)
@@ -469,13 +480,17 @@ def run_backward(args):
     flop = 8.0 * T * d * d + 4.0 * d * P + 20.0 * T * d * d + 8.0 * d * P
     # executed: the dQ and the dK/dV kernels each recompute S and dP (another 6dP)
     flop_exec = flop + 6.0 * d * P
-    rec = base_record(args, "HSTU layer backward tokens/s (fp32, forward recompute included), 1 GPU",
+    rec = base_record(args, "HSTU layer backward tokens/s (fp32, forward recompute included"
+                      + (", attention backward on bf16 matrix cores" if args.attn_bwd_bf16 else "") + "), 1 GPU",
                       T / (ms * 1e-3), "tokens/s", ms, "f32",
                       {"workload": gen.CONFIG_NAMES[args.workload] + ", held in fp32", "total_tokens": T,
                        "input_norm": bool(args.input_norm),
                        "num_seqs": w.num_seqs, "d_model": d, "num_heads": w.num_heads,
                        "visible_pairs": P})
     rec["forward_fp32_ms"] = ms_fwd
+    if ms_f32_bwd is not None:
+        rec["attn_bwd_bf16"] = True
+        rec["backward_all_fp32_ms"] = ms_f32_bwd
     rec["train_step_two_calls_ms"] = ms_step
     if args.stochastic_length is not None:
         # Stochastic Length on the training pass: the sampler's kept rows of

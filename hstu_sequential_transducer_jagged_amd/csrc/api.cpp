@@ -98,6 +98,8 @@ int check_desc(const hstu_layer_desc* d) {
         "num_token_types must be in [0, %d] (got %d)", HSTU_MAX_TOKEN_TYPES, d->num_token_types);
   CHECK(d->bias_mode == HSTU_BIAS_TABLES || d->bias_mode == HSTU_BIAS_LINEAR, HSTU_E_INVAL,
         "unknown bias_mode %d", d->bias_mode);
+  CHECK(d->attn_bwd_bf16 == 0 || d->attn_bwd_bf16 == 1, HSTU_E_INVAL, "attn_bwd_bf16 must be 0 or 1 (got %d)",
+        d->attn_bwd_bf16);
   if (d->bias_mode == HSTU_BIAS_LINEAR) {
     CHECK(std::isfinite(d->linear_m_p) && std::isfinite(d->linear_m_t), HSTU_E_INVAL,
           "linear_m_p and linear_m_t must be finite");
@@ -556,7 +558,9 @@ size_t hstu_layer_bwd_workspace_size(const hstu_layer_desc* desc, const hstu_jag
   if (!desc || !jagged || jagged->total_tokens < 0 || desc->d_model <= 0) return 0;
   const size_t T = static_cast<size_t>(jagged->total_tokens);
   const size_t td = round256(T * desc->d_model * sizeof(float));
-  return (desc->input_norm ? 18 : 17) * td + round256(T * sizeof(float));
+  // with the bf16 attention backward: bf16 copies of Q, K, V and dAV
+  const size_t bf = desc->attn_bwd_bf16 == 1 ? 4 * round256(T * desc->d_model * sizeof(uint16_t)) : 0;
+  return (desc->input_norm ? 18 : 17) * td + round256(T * sizeof(float)) + bf;
 }
 
 namespace {
@@ -647,6 +651,16 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
   // LayerNorm(X) with input_norm: the input of f1
   float* XN = norm1 ? reinterpret_cast<float*>(w + 17 * td + round256(static_cast<size_t>(T) * sizeof(float)))
                     : nullptr;
+  // bf16 copies of Q, K, V, dAV for the bf16 attention backward
+  const bool bf16_bwd = desc->attn_bwd_bf16 == 1;
+  const size_t tb16 = round256(static_cast<size_t>(T) * d * sizeof(uint16_t));
+  uint16_t* B16 = reinterpret_cast<uint16_t*>(w + (norm1 ? 18 : 17) * td +
+                                              round256(static_cast<size_t>(T) * sizeof(float)));
+  uint16_t* Q16 = B16;
+  uint16_t* K16 = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(B16) + tb16);
+  uint16_t* V16 = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(B16) + 2 * tb16);
+  uint16_t* DAV16 = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(B16) + 3 * tb16);
+
   const float* X = static_cast<const float*>(x);
   const float* DY = static_cast<const float*>(dy);
   const float* W1 = static_cast<const float*>(params->w1);
@@ -714,7 +728,17 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
   ba.dav = DAV;
   ba.dv = DZ + d; ba.dq = DZ + 2 * d; ba.dk = DZ + 3 * d; ba.ld_dz = d4;
   ba.dpos = grads->dpos; ba.dtime = grads->dtime;
-  HSTU_TRY(hstu::launch_attn_bwd_f32(ba, s), "attention backward");
+  if (bf16_bwd) {
+    const int64_t n = T * d;
+    HSTU_TRY(hstu::launch_to_bf16(Q, Q16, n, s), "bf16 copy");
+    HSTU_TRY(hstu::launch_to_bf16(K, K16, n, s), "bf16 copy");
+    HSTU_TRY(hstu::launch_to_bf16(V, V16, n, s), "bf16 copy");
+    HSTU_TRY(hstu::launch_to_bf16(DAV, DAV16, n, s), "bf16 copy");
+    ba.q16 = Q16; ba.k16 = K16; ba.v16 = V16; ba.dav16 = DAV16;
+    HSTU_TRY(hstu::launch_attn_bwd_bf16(ba, s), "attention backward (bf16)");
+  } else {
+    HSTU_TRY(hstu::launch_attn_bwd_f32(ba, s), "attention backward");
+  }
   // [U V Q K] = SiLU(X W1^T + b1)
   HSTU_TRY(hstu::launch_silu_bwd(DZ, Z, T * d4, s), "silu backward");
   HSTU_TRY(hstu::launch_colsum(DZ, d4, T, d4, grads->db1, s), "db1");

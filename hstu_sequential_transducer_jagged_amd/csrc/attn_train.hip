@@ -20,6 +20,8 @@
 // for the row-per-lane operands, and whole rows across the lanes for the
 // dimension-per-lane ones. A workgroup holds one wave per head of the same
 // 32 rows (up to four heads), so its waves have identical trip counts.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -423,6 +425,394 @@ __global__ __launch_bounds__(512) void attn_train_kv_kernel(BwdAttnArgs a) {
   store_tiles<NCT>(a.dv + (s0 + j0 + lc) * a.ld_dz + pl.h * DH, a.ld_dz, dv, g, 1.0f, kv[0], kv[1]);
 }
 
+// ---------------------------------------------------------------------------
+// The backward on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16): the same
+// products, pointwise step and table gradients as above, from bf16 copies
+// of Q, K, V and dAV, with P and dS rounded to bf16 as the operands of their
+// products and every sum in fp32.
+//
+// 16x16x32: lane l supplies A[l%16][8 (l/16) + e] and B[8 (l/16) + e][l%16]
+// (e < 8); accumulator register r of lane l is D[4 (l/16) + r][l%16], the
+// layout of the 16x16x4 fp32 form. The score-shaped products contract the
+// head dimension, so their operands are rows read straight from memory (8
+// consecutive dims per lane). The second products contract the 32 rows of
+// the block walked: their B operand is the accumulator itself, lane group g
+// holding rows 4g + r of the first and the second 16-row tile (slots
+// e = 4 t + r), and their A operand is the other side's 32 x DH block read
+// back transposed from the wave's LDS copy (ds_read_b64_tr_b16: within 16
+// lanes, source lane 4a + b addresses dims 4b .. 4b+3 of row a, and lane i
+// receives dim i of rows 0 .. 3), which yields the same slot order.
+// ---------------------------------------------------------------------------
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define HSTU_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// LDS accumulator of position-bias gradients of the bf16 dQ kernel:
+// differences -31 .. kPosCapB - 32; larger ones go to global memory.
+constexpr int kPosCapB = 8192 + 64;
+
+// Row-per-lane bf16 operand over the head dimension: lane (row, g) holds
+// dims 32c + 8g .. 32c + 8g + 7 of its row (c < DH / 32).
+template <int NC>
+__device__ __forceinline__ void load_row16(const uint16_t* row, int g, bf16x8 (&o)[NC]) {
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    o[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(row + 32 * c + 8 * g));
+}
+
+// The wave's 32 x DH block in LDS (row stride DH + 8 bf16: the four rows one
+// transposing read touches start in different banks), from the row operands
+// of its two 16-row tiles.
+template <int DH>
+__device__ __forceinline__ void stash_block(uint16_t* blk, const bf16x8 (&o)[2][DH / 32], int lc, int g) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int c = 0; c < DH / 32; ++c)
+      *reinterpret_cast<uint4*>(blk + (16 * t + lc) * (DH + 8) + 32 * c + 8 * g) =
+          __builtin_bit_cast(uint4, o[t][c]);
+}
+
+// A operand of a second product, for output dims 16 ct .. 16 ct + 15: lane
+// (lc, g) gets dim 16 ct + lc of block rows 4g .. 4g+3 (slots 0..3) and
+// 16 + 4g .. 16 + 4g + 3 (slots 4..7).
+template <int DH>
+__device__ __forceinline__ bf16x8 load_block_tr(const uint16_t* blk, int ct, int lc, int g) {
+  const uint16_t* p = blk + (4 * g + (lc >> 2)) * (DH + 8) + 16 * ct + 4 * (lc & 3);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(HSTU_LDS(i16x4, p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(HSTU_LDS(i16x4, p + 16 * (DH + 8)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// B operand of a second product from two accumulator tiles (slots 4t + r).
+__device__ __forceinline__ bf16x8 pack_slots(const f32x4& t0, const f32x4& t1) {
+  const uint4 u = make_uint4(pack_bf16x2(t0[0], t0[1]), pack_bf16x2(t0[2], t0[3]), pack_bf16x2(t1[0], t1[1]),
+                             pack_bf16x2(t1[2], t1[3]));
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// Output tile of a second product: accumulator register r of lane (lc, g) is
+// dim 16 ct + 4g + r of row lc of the 16-row tile; one float4 per tile.
+template <int NCT>
+__device__ __forceinline__ void store_tiles16(float* out, int64_t ld, const f32x4 (&acc)[NCT][2], int lc, int g,
+                                              float scale, bool ok0, bool ok1) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (!(t == 0 ? ok0 : ok1)) continue;
+    float* row = out + (16 * t + lc) * ld;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+      *reinterpret_cast<float4*>(row + 16 * ct + 4 * g) =
+          make_float4(acc[ct][t][0] * scale, acc[ct][t][1] * scale, acc[ct][t][2] * scale, acc[ct][t][3] * scale);
+  }
+}
+
+// dQ with the bias-table gradients for the 32 query rows of one block and one
+// head per wave. The table gradients sum dS over the workgroup's heads
+// before anything is added: each wave parks its dS block in LDS, then lane
+// l of every wave takes diagonal l (query row - key row = l - 31) of the
+// rows it owns, sums it over the heads, adds the sum to the position
+// accumulator once, and sums runs of one time bucket along the diagonal in
+// registers. LONG: some position differences lie beyond the LDS
+// accumulator; those are added to global memory.
+template <int DH, bool LONG>
+__global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) {
+  constexpr int NC = DH / 32, NCT = DH / 16;
+  constexpr int DSR = 36;   // row stride of a parked dS block (16-byte rows, spread over the banks)
+  __shared__ float s_gpos[kPosCapB];
+  __shared__ float s_tval[64], s_tgrad[64];
+  __shared__ float s_win[kMaxWaves][64];
+  __shared__ int64_t s_ts[kMaxWaves][32];
+  __shared__ int64_t s_qts[32];
+  __shared__ __attribute__((aligned(16))) float s_ds[kMaxWaves][32 * DSR];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[kMaxWaves][32 * (DH + 8)];
+  const int nw = blockDim.x >> 6;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lc = lane & 15, g = lane >> 4;
+  const Place pl = place(a, true, wave, nw);
+  const int64_t s0 = a.offsets[pl.seq];
+  const int L = static_cast<int>(a.offsets[pl.seq + 1] - s0);
+  const int q0 = pl.blk * 32;
+  if (q0 >= L) return;   // the whole workgroup: same sequence and block
+  const int range = min(q0 + 63, kPosCapB);   // LDS entries d + 31 this block can touch
+  const int64_t* Ts = a.ts + s0;
+  for (int e = tid; e < range; e += blockDim.x) s_gpos[e] = 0.0f;
+  if (tid < 64) {
+    s_tgrad[tid] = 0.0f;
+    s_tval[tid] = tid < a.nb ? a.time_bias[tid] : 0.0f;
+  }
+  if (tid < 32) s_qts[tid] = Ts[min(q0 + tid, L - 1)];
+  __syncthreads();
+
+  const int d = a.d_model;
+  const int64_t base = s0 * d + pl.h * DH;
+  const uint16_t* Ks = a.k16 + base;
+  const uint16_t* Vs = a.v16 + base;
+  uint16_t* kblk = s_k[wave];
+  bf16x8 qf[2][NC], df[2][NC];
+  int64_t tq[2];
+  bool qv[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int qrow = min(q0 + 16 * qt + lc, L - 1);
+    qv[qt] = q0 + 16 * qt + lc < L;
+    load_row16<NC>(a.q16 + base + qrow * d, g, qf[qt]);
+    load_row16<NC>(a.dav16 + base + qrow * d, g, df[qt]);
+    tq[qt] = Ts[qrow];
+  }
+  float* win = s_win[wave];
+  int64_t* kts = s_ts[wave];
+  f32x4 acc[NCT][2];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) acc[ct][0] = acc[ct][1] = f32x4{};
+  // time-bucket run of this lane's diagonal (bucket, sum)
+  int run_tb = 0;
+  float run_sum = 0.0f;
+  float wv = a.pos_bias[clampi(a.pos_center + q0 - 31 + lane, 0, a.pos_len - 1)];
+  int64_t tsv = Ts[min(lane & 31, L - 1)];
+  // the next block's K and V rows, requested one block ahead
+  bf16x8 kn[2][NC], vn[2][NC];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int krow = min(16 * kt + lc, L - 1);
+    load_row16<NC>(Ks + krow * d, g, kn[kt]);
+    load_row16<NC>(Vs + krow * d, g, vn[kt]);
+  }
+
+  for (int kb = 0; kb <= pl.blk; ++kb) {
+    const int j0 = kb * 32, D = q0 - j0;
+    win[lane] = wv;
+    if (lane < 32) kts[lane] = tsv;
+    wv = a.pos_bias[clampi(a.pos_center + D - 63 + lane, 0, a.pos_len - 1)];
+    tsv = Ts[min(j0 + 32 + (lane & 31), L - 1)];
+    bf16x8 kf[2][NC], vf[2][NC];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        kf[kt][c] = kn[kt][c];
+        vf[kt][c] = vn[kt][c];
+      }
+    if (kb < pl.blk) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int krow = min(j0 + 32 + 16 * kt + lc, L - 1);
+        load_row16<NC>(Ks + krow * d, g, kn[kt]);
+        load_row16<NC>(Vs + krow * d, g, vn[kt]);
+      }
+    }
+    // S^T = K Q^T (rows: keys, columns: queries); dP^T = V dAV^T
+    f32x4 sacc[2][2], pacc[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        sacc[kt][qt] = pacc[kt][qt] = f32x4{};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          sacc[kt][qt] = mfma_16x16x32(kf[kt][c], qf[qt][c], sacc[kt][qt]);
+          pacc[kt][qt] = mfma_16x16x32(vf[kt][c], df[qt][c], pacc[kt][qt]);
+        }
+      }
+    // this block's keys, for the transposed reads of the second product
+    stash_block<DH>(kblk, kf, lc, g);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int jr = 16 * kt + 4 * g + r;   // key row in the block
+        const int64_t tk = kts[jr];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          const int ir = 16 * qt + lc;        // query row in the block
+          const bool vis = qv[qt] && (j0 + jr <= q0 + ir);
+          const int tb = time_bucket64(tq[qt] - tk, a.nb);
+          const float sc = a.alpha * sacc[kt][qt][r] + win[ir - jr + 31] + s_tval[tb];
+          const float sg = sigmoid_t(sc);
+          sacc[kt][qt][r] = vis ? pacc[kt][qt][r] * sg * (1.0f + sc * (1.0f - sg)) : 0.0f;
+        }
+      }
+    // park dS (query row ir = 16 qt + lc, key rows 16 kt + 4g .. +3)
+    float* dsw = s_ds[wave];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        *reinterpret_cast<float4*>(dsw + (16 * qt + lc) * DSR + 16 * kt + 4 * g) =
+            make_float4(sacc[kt][qt][0], sacc[kt][qt][1], sacc[kt][qt][2], sacc[kt][qt][3]);
+    // dQ^T += K^T dS^T over the block's 32 keys
+    bf16x8 bs[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) bs[qt] = pack_slots(sacc[0][qt], sacc[1][qt]);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const bf16x8 kt_op = load_block_tr<DH>(kblk, ct, lc, g);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) acc[ct][qt] = mfma_16x16x32(kt_op, bs[qt], acc[ct][qt]);
+    }
+    __syncthreads();   // every wave's dS block is parked
+    // table gradients: lane l takes diagonal l of rows wave, wave + nw, ...
+    float pos_sum = 0.0f;
+    for (int ir = wave; ir < 32; ir += nw) {
+      const int jr = ir - lane + 31;
+      if (lane >= 63 || jr < 0 || jr >= 32 || j0 + jr > q0 + ir || q0 + ir >= L) continue;
+      float v = 0.0f;
+      for (int w2 = 0; w2 < nw; ++w2) v += s_ds[w2][ir * DSR + jr];
+      pos_sum += v;
+      const int tb = time_bucket64(s_qts[ir] - kts[jr], a.nb);
+      if (tb != run_tb) {
+        atomicAdd(&s_tgrad[run_tb], run_sum);
+        run_sum = 0.0f;
+        run_tb = tb;
+      }
+      run_sum += v;
+    }
+    if (lane < 63 && pos_sum != 0.0f) {
+      const int gi = D + lane;   // difference D + lane - 31
+      if (!LONG || gi < kPosCapB)
+        atomicAdd(&s_gpos[gi], pos_sum);
+      else
+        atomicAdd(&a.dpos[clampi(a.pos_center + gi - 31, 0, a.pos_len - 1)], pos_sum);
+    }
+    __syncthreads();   // the parked blocks are read before the next block overwrites them
+  }
+
+  store_tiles16<NCT>(a.dq + (s0 + q0) * a.ld_dz + pl.h * DH, a.ld_dz, acc, lc, g, a.alpha, qv[0], qv[1]);
+  atomicAdd(&s_tgrad[run_tb], run_sum);
+  __syncthreads();
+  for (int e = tid; e < range; e += blockDim.x) {
+    const float gsum = s_gpos[e];
+    if (gsum != 0.0f) atomicAdd(&a.dpos[clampi(a.pos_center + e - 31, 0, a.pos_len - 1)], gsum);
+  }
+  if (tid < a.nb && s_tgrad[tid] != 0.0f) atomicAdd(&a.dtime[tid], s_tgrad[tid]);
+}
+
+// dK and dV for the 32 key rows of one block and one head per wave.
+template <int DH>
+__global__ __launch_bounds__(512) void attn_train_kv_bf16_kernel(BwdAttnArgs a) {
+  constexpr int NC = DH / 32, NCT = DH / 16;
+  __shared__ float s_tval[64];
+  __shared__ float s_win[kMaxWaves][64];
+  __shared__ int64_t s_ts[kMaxWaves][32];
+  __shared__ int64_t s_kts[kMaxWaves][32];
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[kMaxWaves][32 * (DH + 8)];
+  __shared__ __attribute__((aligned(16))) uint16_t s_d[kMaxWaves][32 * (DH + 8)];
+  const int nw = blockDim.x >> 6;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lc = lane & 15, g = lane >> 4;
+  const Place pl = place(a, false, wave, nw);
+  const int64_t s0 = a.offsets[pl.seq];
+  const int L = static_cast<int>(a.offsets[pl.seq + 1] - s0);
+  const int j0 = pl.blk * 32;
+  if (j0 >= L) return;
+  if (tid < 64) s_tval[tid] = tid < a.nb ? a.time_bias[tid] : 0.0f;
+  __syncthreads();
+
+  const int d = a.d_model;
+  const int64_t base = s0 * d + pl.h * DH;
+  const uint16_t* Qs = a.q16 + base;
+  const uint16_t* Ds = a.dav16 + base;
+  const int64_t* Ts = a.ts + s0;
+  uint16_t* qblk = s_q[wave];
+  uint16_t* dblk = s_d[wave];
+  bf16x8 kf[2][NC], vf[2][NC];
+  bool kv[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int krow = min(j0 + 16 * kt + lc, L - 1);
+    kv[kt] = j0 + 16 * kt + lc < L;
+    load_row16<NC>(a.k16 + base + krow * d, g, kf[kt]);
+    load_row16<NC>(a.v16 + base + krow * d, g, vf[kt]);
+  }
+  if (lane < 32) s_kts[wave][lane] = Ts[min(j0 + lane, L - 1)];
+  float* win = s_win[wave];
+  int64_t* qts = s_ts[wave];
+  f32x4 dk[NCT][2], dv[NCT][2];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) dk[ct][0] = dk[ct][1] = dv[ct][0] = dv[ct][1] = f32x4{};
+  const int nblk = (L + 31) >> 5;
+  // window entry e <-> difference 32 qb - j0 - 31 + e; fetched a block ahead
+  float wv = a.pos_bias[clampi(a.pos_center - 31 + lane, 0, a.pos_len - 1)];
+  int64_t tsv = Ts[min(j0 + (lane & 31), L - 1)];
+  for (int qb = pl.blk; qb < nblk; ++qb) {
+    const int q0 = qb * 32, D = q0 - j0;
+    win[lane] = wv;
+    if (lane < 32) qts[lane] = tsv;
+    wv = a.pos_bias[clampi(a.pos_center + D + 1 + lane, 0, a.pos_len - 1)];
+    tsv = Ts[min(q0 + 32 + (lane & 31), L - 1)];
+    bf16x8 qf[2][NC], df[2][NC];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int qrow = min(q0 + 16 * qt + lc, L - 1);
+      load_row16<NC>(Qs + qrow * d, g, qf[qt]);
+      load_row16<NC>(Ds + qrow * d, g, df[qt]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // S = Q K^T (rows: queries, columns: keys); dP = dAV V^T
+    f32x4 sacc[2][2], pacc[2][2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        sacc[qt][kt] = pacc[qt][kt] = f32x4{};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          sacc[qt][kt] = mfma_16x16x32(qf[qt][c], kf[kt][c], sacc[qt][kt]);
+          pacc[qt][kt] = mfma_16x16x32(df[qt][c], vf[kt][c], pacc[qt][kt]);
+        }
+      }
+    // this block's queries and dAV rows, for the transposed reads
+    stash_block<DH>(qblk, qf, lc, g);
+    stash_block<DH>(dblk, df, lc, g);
+    const int64_t tk[2] = {s_kts[wave][lc], s_kts[wave][16 + lc]};
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ir = 16 * qt + 4 * g + r;   // query row in the block
+        const int64_t tqr = qts[ir];
+        const bool qok = q0 + ir < L;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const int jr = 16 * kt + lc;        // key row in the block
+          const bool vis = kv[kt] && qok && (j0 + jr <= q0 + ir);
+          const int tb = time_bucket64(tqr - tk[kt], a.nb);
+          const float sc = a.alpha * sacc[qt][kt][r] + win[ir - jr + 31] + s_tval[tb];
+          const float sg = sigmoid_t(sc);
+          sacc[qt][kt][r] = vis ? sc * sg : 0.0f;
+          pacc[qt][kt][r] = vis ? pacc[qt][kt][r] * sg * (1.0f + sc * (1.0f - sg)) : 0.0f;
+        }
+      }
+    // dV^T += dAV^T P and dK^T += Q^T dS over the block's 32 queries
+    bf16x8 bp[2], bs[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      bp[kt] = pack_slots(sacc[0][kt], sacc[1][kt]);
+      bs[kt] = pack_slots(pacc[0][kt], pacc[1][kt]);
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const bf16x8 dt_op = load_block_tr<DH>(dblk, ct, lc, g);
+      const bf16x8 qt_op = load_block_tr<DH>(qblk, ct, lc, g);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        dv[ct][kt] = mfma_16x16x32(dt_op, bp[kt], dv[ct][kt]);
+        dk[ct][kt] = mfma_16x16x32(qt_op, bs[kt], dk[ct][kt]);
+      }
+    }
+  }
+  store_tiles16<NCT>(a.dk + (s0 + j0) * a.ld_dz + pl.h * DH, a.ld_dz, dk, lc, g, a.alpha, kv[0], kv[1]);
+  store_tiles16<NCT>(a.dv + (s0 + j0) * a.ld_dz + pl.h * DH, a.ld_dz, dv, lc, g, 1.0f, kv[0], kv[1]);
+}
+
+// fp32 -> bf16 (round to nearest even), n a multiple of 4.
+__global__ __launch_bounds__(256) void to_bf16_kernel(const float4* __restrict__ src, uint2* __restrict__ dst,
+                                                      int64_t n4) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const float4 v = src[i];
+    dst[i] = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+  }
+}
+
 // Waves per workgroup: the largest divisor of num_heads up to kMaxWaves.
 int waves_for(int num_heads) {
   for (int w = kMaxWaves; w > 1; --w)
@@ -449,6 +839,31 @@ hipError_t launch_train(K kernel, const BwdAttnArgs& a, hipStream_t s) {
 hipError_t launch_attn_train_fwd(const BwdAttnArgs& a, hipStream_t s) {
   return a.head_dim == 32 ? launch_train(attn_train_q_kernel<32, true>, a, s)
                           : launch_train(attn_train_q_kernel<64, true>, a, s);
+}
+
+hipError_t launch_attn_bwd_bf16(const BwdAttnArgs& a, hipStream_t s) {
+  if (!a.q16 || !a.k16 || !a.v16 || !a.dav16) return hipErrorInvalidValue;
+  const bool lng = static_cast<int64_t>(a.max_seq_len) + 64 > kPosCapB;
+  hipError_t e;
+  if (a.head_dim == 32)
+    e = lng ? launch_train(attn_train_dq_bf16_kernel<32, true>, a, s)
+            : launch_train(attn_train_dq_bf16_kernel<32, false>, a, s);
+  else
+    e = lng ? launch_train(attn_train_dq_bf16_kernel<64, true>, a, s)
+            : launch_train(attn_train_dq_bf16_kernel<64, false>, a, s);
+  if (e != hipSuccess) return e;
+  return a.head_dim == 32 ? launch_train(attn_train_kv_bf16_kernel<32>, a, s)
+                          : launch_train(attn_train_kv_bf16_kernel<64>, a, s);
+}
+
+hipError_t launch_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s) {
+  if (n % 4 != 0) return hipErrorInvalidValue;
+  const int64_t n4 = n / 4;
+  if (n4 == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 8192);
+  hipLaunchKernelGGL(to_bf16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     reinterpret_cast<const float4*>(src), reinterpret_cast<uint2*>(dst), n4);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_bwd_f32(const BwdAttnArgs& a, hipStream_t s) {

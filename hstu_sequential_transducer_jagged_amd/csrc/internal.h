@@ -174,6 +174,11 @@ struct BwdAttnArgs {
   const float* k;
   const float* v;
   const float* dav;          // [T, d] gradient of AV
+  // bf16 copies of q, k, v, dav (the bf16 backward reads these instead)
+  const uint16_t* q16;
+  const uint16_t* k16;
+  const uint16_t* v16;
+  const uint16_t* dav16;
   const int64_t* offsets;    // [B+1]
   const int64_t* ts;         // [T]
   const float* pos_bias;
@@ -195,6 +200,11 @@ struct BwdAttnArgs {
 bool attn_train_supported(int head_dim);
 hipError_t launch_attn_train_fwd(const BwdAttnArgs& a, hipStream_t s);
 hipError_t launch_attn_bwd_f32(const BwdAttnArgs& a, hipStream_t s);
+// The same backward on the bf16 matrix cores, from a.q16/k16/v16/dav16
+// (head_dim 32 or 64); the outputs and table gradients as above.
+hipError_t launch_attn_bwd_bf16(const BwdAttnArgs& a, hipStream_t s);
+// dst[i] = bf16(src[i]) (round to nearest even), n a multiple of 4.
+hipError_t launch_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
 // C[m, n] = sum_k A[m sam + k sak] B[k sbk + n sbn] (+ bias[n] + addend[m, n]);
 // splits > 1: K split over blocks whose sums are added atomically into C
 // (zeroed beforehand, no bias or addend).

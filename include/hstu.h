@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 9
+#define HSTU_ABI_VERSION 10
 
 typedef enum {
   HSTU_OK = 0,
@@ -112,6 +112,14 @@ typedef struct {
                                time_bias are not read (may be NULL). Untyped, forward only */
   float linear_m_p;         /* slopes of HSTU_BIAS_LINEAR, finite */
   float linear_m_t;
+  int32_t attn_bwd_bf16;    /* 0 (default) or 1, read by the backward entry points
+                               (hstu_layer_bwd, hstu_layer_bwd_after_fwd): the attention
+                               backward runs on the bf16 matrix cores. Q, K, V and dAV are
+                               rounded to bf16 once, P and dS as the operands of their
+                               products; every sum is fp32, and every other step of the
+                               layer (its forward recompute included) stays fp32. Gradients
+                               then agree with the fp32 ones to the bf16 tolerance (2e-2),
+                               not the fp32 one */
 } hstu_layer_desc;
 
 /* A jagged batch of the call's own tokens. */

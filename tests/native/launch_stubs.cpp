@@ -28,6 +28,8 @@ hipError_t launch_layernorm_bf16(const LayerNormArgs&, hipStream_t) { reached("l
 hipError_t launch_layernorm_f32(const LayerNormArgs&, hipStream_t) { reached("launch_layernorm_f32"); }
 hipError_t launch_attn_train_fwd(const BwdAttnArgs&, hipStream_t) { reached("launch_attn_train_fwd"); }
 hipError_t launch_attn_bwd_f32(const BwdAttnArgs&, hipStream_t) { reached("launch_attn_bwd_f32"); }
+hipError_t launch_attn_bwd_bf16(const BwdAttnArgs&, hipStream_t) { reached("launch_attn_bwd_bf16"); }
+hipError_t launch_to_bf16(const float*, uint16_t*, int64_t, hipStream_t) { reached("launch_to_bf16"); }
 hipError_t launch_gemm_f32s(const float*, int64_t, int64_t, const float*, int64_t, int64_t, float*, int64_t,
                             const float*, const float*, int, int, int64_t, int, hipStream_t) {
   reached("launch_gemm_f32s");

@@ -1,0 +1,146 @@
+"""The layer backward with the attention backward on the bf16 matrix cores
+(desc.attn_bwd_bf16 = 1) against the oracle's float64 backward.
+
+Q, K, V and dAV are rounded to bf16 once, P and dS as the operands of their
+products, and every sum is fp32. The bound is the bf16 one of the forward
+tests, 2e-2. Matrices (dX, dW1, dW2) are compared row by row, vectors entry
+by entry above a floor, as in test_gpu_backward.py. The floor is 0.2 of the
+vector's largest entry, so an entry may be off by 2e-2 of itself, or by
+4e-3 of the largest entry: about one bf16 ulp (2^-8) of it.
+
+The floor follows from the arithmetic. A vector entry sums over many
+tokens or pairs (db1 over T rows of dZ, a table-gradient entry over the dS
+of every pair at one position difference or time bucket). Each term carries
+the relative error of its bf16 operands, about 2^-9 to 2^-8. An entry whose
+terms cancel down to a small fraction of the largest keeps the absolute
+error of the terms it cancelled from, not one relative to its own size."""
+
+import numpy as np
+import pytest
+
+import oracle
+from hstu_inputs import gen
+from tests.helpers import f32, row_rel_err, to_np
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+FLOOR = 0.2
+
+
+def _rel(g, r):
+    g, r = np.asarray(g, np.float64), np.asarray(r, np.float64)
+    assert g.shape == r.shape and np.all(np.isfinite(g))
+    if g.size == 0:
+        return 0.0
+    if g.ndim == 2:
+        return row_rel_err(g, r)
+    den = np.maximum(np.abs(r), max(FLOOR * np.abs(r).max(), 1e-12))
+    return float((np.abs(g - r) / den).max())
+
+
+def _grads(d, w):
+    import torch
+    from hstu_sequential_transducer_jagged_amd import hstu
+    g = {k: torch.empty(n, dtype=torch.float32, device="cuda") for k, n in [
+        ("dw1", 4 * d * d), ("db1", 4 * d), ("dw2", d * d), ("db2", d), ("dgamma", d),
+        ("dbeta", d), ("dpos", 2 * w.n_max - 1), ("dtime", w.num_time_buckets)]}
+    return g, hstu.make_grads(g["dw1"], g["db1"], g["dw2"], g["db2"], g["dgamma"], g["dbeta"],
+                              g["dpos"], g["dtime"])
+
+
+def _backward(w, dy, two_calls=False):
+    import torch
+    from hstu_sequential_transducer_jagged_amd import hstu, runner
+    d, T = w.d_model, w.total_tokens
+    dw = runner.DeviceWorkload(w)
+    lay = dw.layers[0]
+    desc = hstu.LayerDesc.from_buffer_copy(lay.desc)
+    desc.attn_bwd_bf16 = 1
+    g, grads = _grads(d, w)
+    dyt = f32(dy)
+    dx = torch.empty_like(dyt)
+    ws = hstu.workspace_tensor(hstu.hstu_layer_bwd_workspace_size(desc, dw.jagged))
+    out = {}
+    if two_calls:
+        y = torch.empty_like(dyt)
+        hstu.hstu_layer_fwd_train(desc, lay.params, dw.jagged, dw.x, y, ws)
+        torch.cuda.synchronize()
+        out["y"] = to_np(y)
+        hstu.hstu_layer_bwd_after_fwd(desc, lay.params, dw.jagged, dw.x, dyt, dx, grads, ws)
+    else:
+        hstu.hstu_layer_bwd(desc, lay.params, dw.jagged, dw.x, dyt, dx, grads, ws)
+    torch.cuda.synchronize()
+    return out, {"dx": to_np(dx), "dw1": to_np(g["dw1"]).reshape(4 * d, d),
+            "dw2": to_np(g["dw2"]).reshape(d, d),
+            **{k: to_np(g[k]) for k in ("db1", "db2", "dgamma", "dbeta", "dpos", "dtime")}}
+
+
+@pytest.mark.parametrize("lengths,d,H,alpha,ts_kind", [
+    ([1, 5, 64, 65, 0, 130], 64, 2, 0.7, None),    # head_dim 32, ragged tails, an empty sequence
+    ([200, 3, 64], 128, 2, 1.0, None),             # head_dim 64
+    ([100, 33, 257], 512, 8, 1.0, None),           # 8 heads: two 4-wave workgroups per block row
+    ([40, 75, 2], 96, 3, 1.0, None),               # 3 heads of 32: a 3-wave workgroup
+    ([65, 1, 31], 1024, 16, 0.5, None),            # 16 heads
+    ([90, 140], 128, 2, 1.0, "shuffled"),          # timestamps out of order
+    ([120, 64, 9], 128, 2, 1.0, "wide"),           # clocks spanning far more than 2^31 units
+])
+def test_bf16_attention_backward_matches_oracle(gpu_lib, lengths, d, H, alpha, ts_kind):
+    w = gen.make_custom(lengths, d, H, dtype="f32", seed=81, affine="random")
+    w.alpha = alpha
+    if ts_kind == "wide":
+        from tests.test_gpu_time_buckets import _timestamps
+        w.timestamps = _timestamps("wide", lengths, np.random.default_rng(84))
+        w.layers[0].time_bias = np.random.default_rng(85).standard_normal(32).astype(np.float32)
+    elif ts_kind == "shuffled":
+        rng = np.random.default_rng(83)
+        for b in range(len(lengths)):
+            s0, s1 = int(w.offsets[b]), int(w.offsets[b + 1])
+            w.timestamps[s0:s1] = rng.permutation(w.timestamps[s0:s1])
+    dy = np.random.default_rng(82).standard_normal((w.total_tokens, w.d_model)).astype(np.float32)
+    _, got = _backward(w, dy)
+    ref = oracle.layer_backward(w.x, w.layers[0], w.offsets, w.timestamps, dy, w.num_heads, w.n_max,
+                                w.alpha, w.ln_eps)
+    errs = {k: _rel(got[k], ref[k]) for k in got}
+    print("bf16 backward", lengths, {k: f"{v:.1e}" for k, v in errs.items()})
+    for k, e in errs.items():
+        assert e < TOL, (k, e)
+
+
+def test_bf16_backward_in_two_calls(gpu_lib):
+    """hstu_layer_fwd_train then hstu_layer_bwd_after_fwd with the flag: dX
+    exactly as in one call (no atomics on its path), the gradients that sum
+    with fp32 atomics (weights, biases, tables) to their rounding order, and
+    everything against the oracle."""
+    w = gen.make_custom([150, 7, 64], 128, 2, dtype="f32", seed=86, affine="random")
+    dy = np.random.default_rng(87).standard_normal((w.total_tokens, w.d_model)).astype(np.float32)
+    _, one = _backward(w, dy)
+    fwd, two = _backward(w, dy, two_calls=True)
+    ref_y = oracle.layer(w.x, w.layers[0], w.offsets, w.timestamps, w.num_heads, w.n_max, w.alpha,
+                         w.ln_eps)["y"]
+    assert row_rel_err(fwd["y"], ref_y) < TOL
+    np.testing.assert_array_equal(one["dx"], two["dx"])
+    for k in one:
+        assert _rel(two[k], one[k]) < 1e-5, k
+    ref = oracle.layer_backward(w.x, w.layers[0], w.offsets, w.timestamps, dy, w.num_heads, w.n_max,
+                                w.alpha, w.ln_eps)
+    for k in two:
+        assert _rel(two[k], ref[k]) < TOL, k
+
+
+def test_bf16_backward_long_sequence_tables_balance(gpu_lib):
+    """A sequence longer than the bf16 kernel's LDS accumulator of position
+    gradients (differences up to 8 192): the excess goes to global memory.
+    Every visible pair adds its dS once to each table, so the two tables'
+    sums agree, and the far entries receive their share."""
+    L = 8400
+    w = gen.make_custom([L], 64, 1, dtype="f32", seed=88, n_max=L)
+    dy = np.random.default_rng(89).standard_normal((w.total_tokens, w.d_model)).astype(np.float32)
+    _, got = _backward(w, dy)
+    dpos, dtime = got["dpos"].astype(np.float64), got["dtime"].astype(np.float64)
+    assert np.all(np.isfinite(dpos)) and np.all(np.isfinite(dtime))
+    center = w.n_max - 1
+    assert np.all(dpos[:center] == 0.0)
+    scale = np.abs(dpos).sum()
+    assert abs(dpos.sum() - dtime.sum()) <= 1e-4 * scale, (dpos.sum(), dtime.sum(), scale)
+    assert np.count_nonzero(dpos[center + 8192:center + L]) > 0
