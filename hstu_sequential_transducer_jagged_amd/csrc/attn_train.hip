@@ -508,13 +508,13 @@ __device__ __forceinline__ void store_tiles16(float* out, int64_t ld, const f32x
 }
 
 // dQ with the bias-table gradients for the 32 query rows of one block and one
-// head per wave. The table gradients sum dS over the workgroup's heads
-// before anything is added: each wave parks its dS block in LDS, then lane
-// l of every wave takes diagonal l (query row - key row = l - 31) of the
-// rows it owns, sums it over the heads, adds the sum to the position
-// accumulator once, and sums runs of one time bucket along the diagonal in
-// registers. LONG: some position differences lie beyond the LDS
-// accumulator; those are added to global memory.
+// head per wave. The position gradient sums each diagonal of a block before
+// anything is added: the wave parks its dS block in LDS, lane l sums
+// diagonal l (query row - key row = l - 31) and adds the sum to the position
+// accumulator once. The time-bucket gradient sums runs of one bucket per
+// lane in registers, as the fp32 kernel does. LONG: some position
+// differences lie beyond the LDS accumulator; those are added to global
+// memory.
 template <int DH, bool LONG>
 __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) {
   constexpr int NC = DH / 32, NCT = DH / 16;
@@ -523,7 +523,6 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
   __shared__ float s_tval[64], s_tgrad[64];
   __shared__ float s_win[kMaxWaves][64];
   __shared__ int64_t s_ts[kMaxWaves][32];
-  __shared__ int64_t s_qts[32];
   __shared__ __attribute__((aligned(16))) float s_ds[kMaxWaves][32 * DSR];
   __shared__ __attribute__((aligned(16))) uint16_t s_k[kMaxWaves][32 * (DH + 8)];
   const int nw = blockDim.x >> 6;
@@ -540,7 +539,6 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
     s_tgrad[tid] = 0.0f;
     s_tval[tid] = tid < a.nb ? a.time_bias[tid] : 0.0f;
   }
-  if (tid < 32) s_qts[tid] = Ts[min(q0 + tid, L - 1)];
   __syncthreads();
 
   const int d = a.d_model;
@@ -564,9 +562,11 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
   f32x4 acc[NCT][2];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) acc[ct][0] = acc[ct][1] = f32x4{};
-  // time-bucket run of this lane's diagonal (bucket, sum)
-  int run_tb = 0;
-  float run_sum = 0.0f;
+  // time-bucket gradients: per lane and query tile the keys ascend, so runs
+  // of one bucket are summed in registers and added to LDS when the bucket
+  // changes (starting from bucket 0 with nothing summed)
+  int tb_cur[2] = {0, 0};
+  float tg_cur[2] = {0.0f, 0.0f};
   float wv = a.pos_bias[clampi(a.pos_center + q0 - 31 + lane, 0, a.pos_len - 1)];
   int64_t tsv = Ts[min(lane & 31, L - 1)];
   // the next block's K and V rows, requested one block ahead
@@ -628,7 +628,12 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
           const int tb = time_bucket64(tq[qt] - tk, a.nb);
           const float sc = a.alpha * sacc[kt][qt][r] + win[ir - jr + 31] + s_tval[tb];
           const float sg = sigmoid_t(sc);
-          sacc[kt][qt][r] = vis ? pacc[kt][qt][r] * sg * (1.0f + sc * (1.0f - sg)) : 0.0f;
+          const float ds = vis ? pacc[kt][qt][r] * sg * (1.0f + sc * (1.0f - sg)) : 0.0f;
+          sacc[kt][qt][r] = ds;
+          const bool flush = vis && tb != tb_cur[qt];
+          if (flush) atomicAdd(&s_tgrad[tb_cur[qt]], tg_cur[qt]);
+          tg_cur[qt] = (flush ? 0.0f : tg_cur[qt]) + ds;
+          tb_cur[qt] = flush ? tb : tb_cur[qt];
         }
       }
     // park dS (query row ir = 16 qt + lc, key rows 16 kt + 4g .. +3)
@@ -649,22 +654,16 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) acc[ct][qt] = mfma_16x16x32(kt_op, bs[qt], acc[ct][qt]);
     }
-    __syncthreads();   // every wave's dS block is parked
-    // table gradients: lane l takes diagonal l of rows wave, wave + nw, ...
+    // position gradient: lane l sums diagonal l of this wave's parked block
+    // (rows ir with key row jr = ir - l + 31 in the block; hidden pairs hold
+    // dS = 0). LDS accesses of one wave complete in order, so the block is
+    // read back without a barrier.
     float pos_sum = 0.0f;
-    for (int ir = wave; ir < 32; ir += nw) {
-      const int jr = ir - lane + 31;
-      if (lane >= 63 || jr < 0 || jr >= 32 || j0 + jr > q0 + ir || q0 + ir >= L) continue;
-      float v = 0.0f;
-      for (int w2 = 0; w2 < nw; ++w2) v += s_ds[w2][ir * DSR + jr];
-      pos_sum += v;
-      const int tb = time_bucket64(s_qts[ir] - kts[jr], a.nb);
-      if (tb != run_tb) {
-        atomicAdd(&s_tgrad[run_tb], run_sum);
-        run_sum = 0.0f;
-        run_tb = tb;
-      }
-      run_sum += v;
+#pragma unroll
+    for (int ir = 0; ir < 32; ++ir) {
+      const int jr = ir - lane + 31;   // in the block for ir in [lane - 31, lane]
+      const float v = dsw[ir * DSR + min(max(jr, 0), 31)];
+      pos_sum += (jr >= 0 && jr < 32) ? v : 0.0f;
     }
     if (lane < 63 && pos_sum != 0.0f) {
       const int gi = D + lane;   // difference D + lane - 31
@@ -673,11 +672,11 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
       else
         atomicAdd(&a.dpos[clampi(a.pos_center + gi - 31, 0, a.pos_len - 1)], pos_sum);
     }
-    __syncthreads();   // the parked blocks are read before the next block overwrites them
   }
 
   store_tiles16<NCT>(a.dq + (s0 + q0) * a.ld_dz + pl.h * DH, a.ld_dz, acc, lc, g, a.alpha, qv[0], qv[1]);
-  atomicAdd(&s_tgrad[run_tb], run_sum);
+  atomicAdd(&s_tgrad[tb_cur[0]], tg_cur[0]);
+  atomicAdd(&s_tgrad[tb_cur[1]], tg_cur[1]);
   __syncthreads();
   for (int e = tid; e < range; e += blockDim.x) {
     const float gsum = s_gpos[e];
