@@ -731,6 +731,14 @@ __global__ __launch_bounds__(512) void attn_train_kv_bf16_kernel(BwdAttnArgs a) 
   // window entry e <-> difference 32 qb - j0 - 31 + e; fetched a block ahead
   float wv = a.pos_bias[clampi(a.pos_center - 31 + lane, 0, a.pos_len - 1)];
   int64_t tsv = Ts[min(j0 + (lane & 31), L - 1)];
+  // the next block's Q and dAV rows, requested one block ahead
+  bf16x8 qn[2][NC], dn[2][NC];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int qrow = min(j0 + 16 * qt + lc, L - 1);
+    load_row16<NC>(Qs + qrow * d, g, qn[qt]);
+    load_row16<NC>(Ds + qrow * d, g, dn[qt]);
+  }
   for (int qb = pl.blk; qb < nblk; ++qb) {
     const int q0 = qb * 32, D = q0 - j0;
     win[lane] = wv;
@@ -739,12 +747,20 @@ __global__ __launch_bounds__(512) void attn_train_kv_bf16_kernel(BwdAttnArgs a) 
     tsv = Ts[min(q0 + 32 + (lane & 31), L - 1)];
     bf16x8 qf[2][NC], df[2][NC];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const int qrow = min(q0 + 16 * qt + lc, L - 1);
-      load_row16<NC>(Qs + qrow * d, g, qf[qt]);
-      load_row16<NC>(Ds + qrow * d, g, df[qt]);
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        qf[qt][c] = qn[qt][c];
+        df[qt][c] = dn[qt][c];
+      }
+    if (qb + 1 < nblk) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const int qrow = min(q0 + 32 + 16 * qt + lc, L - 1);
+        load_row16<NC>(Qs + qrow * d, g, qn[qt]);
+        load_row16<NC>(Ds + qrow * d, g, dn[qt]);
+      }
     }
-    __builtin_amdgcn_sched_barrier(0);
     // S = Q K^T (rows: queries, columns: keys); dP = dAV V^T
     f32x4 sacc[2][2], pacc[2][2];
 #pragma unroll
