@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--attn-bwd-bf16", action="store_true",
                     help="with --backward: the attention backward on the bf16 matrix cores "
                          "(desc.attn_bwd_bf16); the all-fp32 backward is timed beside it")
+    ap.add_argument("--gemm-bwd-bf16", action="store_true",
+                    help="with --backward: the backward's products dW2, dW1 and dX on the bf16 "
+                         "matrix cores (desc.gemm_bwd_bf16); the all-fp32 backward is timed beside it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
                     help="approximate CPU seconds for the oracle sample")
@@ -453,13 +456,14 @@ def run_backward(args):
          (4 * d * d, 4 * d, d * d, d, d, d, 2 * w.n_max - 1, w.num_time_buckets, d, d)]
     grads = hstu.make_grads(*g)
     ms_f32_bwd = None
-    if args.attn_bwd_bf16:
-        # the fp32 backward first, for comparison; then the timed one with the flag
+    if args.attn_bwd_bf16 or args.gemm_bwd_bf16:
+        # the fp32 backward first, for comparison; then the timed one with the flags
         ws32 = hstu.workspace_tensor(hstu.hstu_layer_bwd_workspace_size(lay.desc, dw.jagged))
         ms_f32_bwd = timed(lambda: hstu.hstu_layer_bwd(lay.desc, lay.params, dw.jagged, dw.x, dy, dx, grads,
                                                        ws32, sh), stream, args.warmup, args.steps)
         del ws32
-        lay.desc.attn_bwd_bf16 = 1
+        lay.desc.attn_bwd_bf16 = int(bool(args.attn_bwd_bf16))
+        lay.desc.gemm_bwd_bf16 = int(bool(args.gemm_bwd_bf16))
     ws = hstu.workspace_tensor(hstu.hstu_layer_bwd_workspace_size(lay.desc, dw.jagged))
     ms = timed(lambda: hstu.hstu_layer_bwd(lay.desc, lay.params, dw.jagged, dw.x, dy, dx, grads, ws, sh),
                stream, args.warmup, args.steps)
@@ -480,8 +484,10 @@ def run_backward(args):
     flop = 8.0 * T * d * d + 4.0 * d * P + 20.0 * T * d * d + 8.0 * d * P
     # executed: the dQ and the dK/dV kernels each recompute S and dP (another 6dP)
     flop_exec = flop + 6.0 * d * P
+    on16 = [n for n, f in (("attention backward", args.attn_bwd_bf16),
+                           ("backward products", args.gemm_bwd_bf16)) if f]
     rec = base_record(args, "HSTU layer backward tokens/s (fp32, forward recompute included"
-                      + (", attention backward on bf16 matrix cores" if args.attn_bwd_bf16 else "") + "), 1 GPU",
+                      + (", " + " and ".join(on16) + " on bf16 matrix cores" if on16 else "") + "), 1 GPU",
                       T / (ms * 1e-3), "tokens/s", ms, "f32",
                       {"workload": gen.CONFIG_NAMES[args.workload] + ", held in fp32", "total_tokens": T,
                        "input_norm": bool(args.input_norm),
@@ -489,7 +495,8 @@ def run_backward(args):
                        "visible_pairs": P})
     rec["forward_fp32_ms"] = ms_fwd
     if ms_f32_bwd is not None:
-        rec["attn_bwd_bf16"] = True
+        rec["attn_bwd_bf16"] = bool(args.attn_bwd_bf16)
+        rec["gemm_bwd_bf16"] = bool(args.gemm_bwd_bf16)
         rec["backward_all_fp32_ms"] = ms_f32_bwd
     rec["train_step_two_calls_ms"] = ms_step
     if args.stochastic_length is not None:

@@ -100,6 +100,8 @@ int check_desc(const hstu_layer_desc* d) {
         "unknown bias_mode %d", d->bias_mode);
   CHECK(d->attn_bwd_bf16 == 0 || d->attn_bwd_bf16 == 1, HSTU_E_INVAL, "attn_bwd_bf16 must be 0 or 1 (got %d)",
         d->attn_bwd_bf16);
+  CHECK(d->gemm_bwd_bf16 == 0 || d->gemm_bwd_bf16 == 1, HSTU_E_INVAL, "gemm_bwd_bf16 must be 0 or 1 (got %d)",
+        d->gemm_bwd_bf16);
   if (d->bias_mode == HSTU_BIAS_LINEAR) {
     CHECK(std::isfinite(d->linear_m_p) && std::isfinite(d->linear_m_t), HSTU_E_INVAL,
           "linear_m_p and linear_m_t must be finite");
@@ -554,13 +556,67 @@ int hstu_layer_fwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
   return do_out(desc, T, u, x, params->w2, params->b2, y, s);
 }
 
-size_t hstu_layer_bwd_workspace_size(const hstu_layer_desc* desc, const hstu_jagged* jagged) {
-  if (!desc || !jagged || jagged->total_tokens < 0 || desc->d_model <= 0) return 0;
-  const size_t T = static_cast<size_t>(jagged->total_tokens);
+namespace {
+
+// The weight gradients of the bf16 backward contract over the T tokens: S
+// splits of kc tokens each (kc % 32 == 0), the transposed operand copies
+// zero-padded to tp = S * kc columns. Up to 32 splits, so that a product with
+// 16 to 32 output tiles fills the chip.
+struct TokSplit {
+  int S;
+  int kc;
+  int64_t tp;
+};
+TokSplit tok_split(int64_t T) {
+  const int64_t steps = std::max<int64_t>(1, (T + 31) / 32);
+  const int64_t S = std::min<int64_t>(32, steps);
+  const int64_t kc = (steps + S - 1) / S * 32;
+  return {static_cast<int>(S), static_cast<int>(kc), S * kc};
+}
+
+// Byte offsets of the bf16 backward products' buffers, from the start of
+// their region: dZ in bf16; dY^T, G^T, Xin^T and dZ^T in bf16 with tp
+// columns; W1^T in bf16; the split partial sums of dW1 or dW2.
+struct GemmBf16Ws {
+  size_t dz16, dyt, gt, xint, dzt, w1t, part, bytes;
+};
+GemmBf16Ws gemm_bf16_ws(int64_t T, int d) {
+  const TokSplit ts = tok_split(T);
+  const size_t t = static_cast<size_t>(T), dd = static_cast<size_t>(d), tp = static_cast<size_t>(ts.tp);
+  GemmBf16Ws w{};
+  size_t o = 0;
+  auto take = [&](size_t n) {
+    const size_t at = o;
+    o += round256(n);
+    return at;
+  };
+  w.dz16 = take(t * 4 * dd * 2);
+  w.dyt = take(dd * tp * 2);
+  w.gt = take(dd * tp * 2);
+  w.xint = take(dd * tp * 2);
+  w.dzt = take(4 * dd * tp * 2);
+  w.w1t = take(4 * dd * dd * 2);
+  w.part = take(static_cast<size_t>(ts.S) * 4 * dd * dd * 4);
+  w.bytes = o;
+  return w;
+}
+
+// Bytes of the fp32 layout and the bf16 attention copies: where the bf16
+// products' region starts.
+size_t train_ws_base(const hstu_layer_desc* desc, size_t T) {
   const size_t td = round256(T * desc->d_model * sizeof(float));
   // with the bf16 attention backward: bf16 copies of Q, K, V and dAV
   const size_t bf = desc->attn_bwd_bf16 == 1 ? 4 * round256(T * desc->d_model * sizeof(uint16_t)) : 0;
   return (desc->input_norm ? 18 : 17) * td + round256(T * sizeof(float)) + bf;
+}
+
+}  // namespace
+
+size_t hstu_layer_bwd_workspace_size(const hstu_layer_desc* desc, const hstu_jagged* jagged) {
+  if (!desc || !jagged || jagged->total_tokens < 0 || desc->d_model <= 0) return 0;
+  const size_t T = static_cast<size_t>(jagged->total_tokens);
+  const size_t g16 = desc->gemm_bwd_bf16 == 1 ? gemm_bf16_ws(jagged->total_tokens, desc->d_model).bytes : 0;
+  return train_ws_base(desc, T) + g16;
 }
 
 namespace {
@@ -661,6 +717,19 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
   uint16_t* V16 = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(B16) + 2 * tb16);
   uint16_t* DAV16 = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(B16) + 3 * tb16);
 
+  // bf16 operand copies and split partials of the backward's products
+  const bool g16 = desc->gemm_bwd_bf16 == 1;
+  const TokSplit ts = tok_split(T);
+  const GemmBf16Ws gw = gemm_bf16_ws(T, d);
+  char* const g16w = w + train_ws_base(desc, static_cast<size_t>(T));
+  uint16_t* const DZ16 = reinterpret_cast<uint16_t*>(g16w + gw.dz16);
+  uint16_t* const DYT = reinterpret_cast<uint16_t*>(g16w + gw.dyt);
+  uint16_t* const GT = reinterpret_cast<uint16_t*>(g16w + gw.gt);
+  uint16_t* const XINT = reinterpret_cast<uint16_t*>(g16w + gw.xint);
+  uint16_t* const DZT = reinterpret_cast<uint16_t*>(g16w + gw.dzt);
+  uint16_t* const W1T = reinterpret_cast<uint16_t*>(g16w + gw.w1t);
+  float* const PART = reinterpret_cast<float*>(g16w + gw.part);
+
   const float* X = static_cast<const float*>(x);
   const float* DY = static_cast<const float*>(dy);
   const float* W1 = static_cast<const float*>(params->w1);
@@ -715,11 +784,27 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
              "output gemm");
     return ok();
   }
+  // C[M, N] = A[M, K] B[N, K]^T on bf16 copies (K = S * kc with splits)
+  auto gemm16 = [&](const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb, float* c, int64_t ldc,
+                    const float* addend, int64_t M, int N, int kc, int S) {
+    hstu::GemmBf16Args g{a, lda, b, ldb, c, ldc, addend, M, N, kc, S};
+    return hstu::launch_gemm_bf16_f32(g, s);
+  };
   // Y = X + G W2^T + b2
+  // dG stays fp32 in both modes: it feeds dAV, which the bf16 attention
+  // backward rounds again, and the table gradients would carry both roundings
   HSTU_TRY(hstu::launch_gemm_f32s(DY, d, 1, W2, d, 1, DG, d, nullptr, nullptr, static_cast<int>(T), d, d, 1,
                                   s), "dG gemm");
-  HSTU_TRY(hstu::launch_gemm_f32s(DY, 1, d, G, d, 1, grads->dw2, d, nullptr, nullptr, d, d, T,
-                                  splits(d, d), s), "dW2 gemm");
+  if (g16) {
+    // dW2 = dY^T G over the tokens, in splits
+    HSTU_TRY(hstu::launch_to_bf16_t(DY, d, T, d, DYT, ts.tp, s), "bf16 transpose");
+    HSTU_TRY(hstu::launch_to_bf16_t(G, d, T, d, GT, ts.tp, s), "bf16 transpose");
+    HSTU_TRY(gemm16(DYT, ts.tp, GT, ts.tp, PART, d, nullptr, d, d, ts.kc, ts.S), "dW2 gemm (bf16)");
+    HSTU_TRY(hstu::launch_sum_splits(PART, ts.S, static_cast<int64_t>(d) * d, grads->dw2, s), "dW2 sum");
+  } else {
+    HSTU_TRY(hstu::launch_gemm_f32s(DY, 1, d, G, d, 1, grads->dw2, d, nullptr, nullptr, d, d, T,
+                                    splits(d, d), s), "dW2 gemm");
+  }
   HSTU_TRY(hstu::launch_colsum(DY, d, T, d, grads->db2, s), "db2");
   // G = (N^ gamma + beta) . U
   HSTU_TRY(hstu::launch_ln_gate_bwd(DG, U, NH, RSTD, params->ln_gamma, params->ln_beta, DZ, d4, DAV,
@@ -742,6 +827,23 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
   // [U V Q K] = SiLU(X W1^T + b1)
   HSTU_TRY(hstu::launch_silu_bwd(DZ, Z, T * d4, s), "silu backward");
   HSTU_TRY(hstu::launch_colsum(DZ, d4, T, d4, grads->db1, s), "db1");
+  if (g16) {
+    // dW1 = dZ^T Xin over the tokens, in splits; dX (or dXn) = dZ W1 (B = W1^T)
+    HSTU_TRY(hstu::launch_to_bf16(DZ, DZ16, T * d4, s), "bf16 copy");
+    HSTU_TRY(hstu::launch_to_bf16_t(DZ, d4, T, d4, DZT, ts.tp, s), "bf16 transpose");
+    HSTU_TRY(hstu::launch_to_bf16_t(XIN, d, T, d, XINT, ts.tp, s), "bf16 transpose");
+    HSTU_TRY(hstu::launch_to_bf16_t(W1, d, d4, d, W1T, d4, s), "bf16 transpose");
+    HSTU_TRY(gemm16(DZT, ts.tp, XINT, ts.tp, PART, d, nullptr, d4, d, ts.kc, ts.S), "dW1 gemm (bf16)");
+    HSTU_TRY(hstu::launch_sum_splits(PART, ts.S, static_cast<int64_t>(d4) * d, grads->dw1, s), "dW1 sum");
+    if (norm1) {
+      HSTU_TRY(gemm16(DZ16, d4, W1T, d4, DG, d, nullptr, T, d, d4, 1), "dXn gemm (bf16)");
+      HSTU_TRY(hstu::launch_ln1_bwd(X, DG, DY, params->ln1_gamma, static_cast<float*>(dx), grads->dln1_gamma,
+                                    grads->dln1_beta, T, d, desc->ln_eps, s), "input LayerNorm backward");
+    } else {
+      HSTU_TRY(gemm16(DZ16, d4, W1T, d4, static_cast<float*>(dx), d, DY, T, d, d4, 1), "dX gemm (bf16)");
+    }
+    return ok();
+  }
   HSTU_TRY(hstu::launch_gemm_f32s(DZ, 1, d4, XIN, d, 1, grads->dw1, d, nullptr, nullptr, d4, d, T,
                                   splits(d4, d), s), "dW1 gemm");
   if (norm1) {

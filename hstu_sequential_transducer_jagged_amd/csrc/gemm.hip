@@ -6,11 +6,17 @@
 //   out:  Y = X + G W2^T + b2, bias and residual are the epilogue (third
 //         equation plus the block diagram's skip connection).
 //
-// Both are C[M, N] = A[M, K] B[N, K]^T with A and B row-major and K
+// The same kernel, with an fp32 epilogue and optional split-K, runs the
+// products of the training backward (dG, dW2, dW1, dX) on bf16 operand
+// copies (launch_gemm_bf16_f32).
+//
+// All are C[M, N] = A[M, K] B[N, K]^T with A and B row-major and K
 // contiguous, which is the operand layout of v_mfma_f32_32x32x16_bf16
 // (lane = row, 8 consecutive k), so tiles are staged through LDS unchanged
 // apart from a bank swizzle, by global->LDS DMA running up to three K steps
 // ahead of the MFMAs.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -73,6 +79,7 @@ __device__ __forceinline__ T* uniform_ptr(T* p) {
 }
 
 struct ProjEpi {
+  static constexpr bool kF32 = false;
   const float* bias;
   uint16_t* out0;   // U, V, Q, K: the four column blocks of width K
   uint16_t* out1;
@@ -105,6 +112,7 @@ struct ProjEpi {
 };
 
 struct OutEpi {
+  static constexpr bool kF32 = false;
   const float* bias;
   const uint16_t* x;
   uint16_t* y;
@@ -126,6 +134,18 @@ struct OutEpi {
   __device__ __forceinline__ void store8(int64_t m, int n, const uint4& o) const {
     *reinterpret_cast<uint4*>(y + m * K + n) = o;
   }
+};
+
+// fp32 output straight from the accumulators (16-byte stores of 4 columns),
+// plus an fp32 addend; split s of a split-K product writes to
+// out + s * split_stride. No bias.
+struct F32Epi {
+  static constexpr bool kF32 = true;
+  const float* bias;      // always nullptr
+  float* out;
+  const float* addend;    // or nullptr
+  int64_t ld;             // row stride of out and addend
+  int64_t split_stride;
 };
 
 // One ring stage of DMA: wave w fills X rows 16i .. 16i+15 for i = w, w+4, ...
@@ -243,16 +263,19 @@ __device__ __forceinline__ uint8_t* tile_block(int b, uint8_t* sX0, uint8_t* sX1
 
 __device__ __forceinline__ int tile_off(int r, int c) { return (r & 31) * 256 + ((c ^ (r & 15)) << 4); }
 
-// X [M, K] row-major, W [N, K] row-major (nn.Linear), K % 32 == 0,
-// N % 4 == 0. Grid: 8 * ceil(nm / 8) * nn workgroups (nm = ceil(M/256),
-// nn = ceil(N/128)); workgroup id -> XCD id % 8 (round-robin dispatch); XCD x
-// takes row blocks x, x+8, ... and sweeps all nn column tiles of one row
-// block before the next, so each X row block is read from HBM once and W
-// stays in that XCD's L2.
+// X [M, ldx] row-major, W [N, ldw] row-major (nn.Linear), contracted over
+// K columns (K % 32 == 0), N % 4 == 0. Grid, with splits == 1:
+// 8 * ceil(nm / 8) * nn workgroups (nm = ceil(M/BM), nn = ceil(N/128));
+// workgroup id -> XCD id % 8 (round-robin dispatch); XCD x takes row blocks
+// x, x+8, ... and sweeps all nn column tiles of one row block before the
+// next, so each X row block is read from HBM once and W stays in that XCD's
+// L2. With splits > 1 (split-K, few tiles): splits * nm * nn workgroups,
+// tile-major within a split; split s contracts columns s*K .. s*K + K - 1.
 template <int NJ, class Epi>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __restrict__ X,
                                                            const uint16_t* __restrict__ W,
-                                                           int64_t M, int N, int K, int nm, int nn,
+                                                           int64_t M, int N, int K, int64_t ldx,
+                                                           int64_t ldw, int nm, int nn, int splits,
                                                            Epi epi) {
   constexpr int BM = 64 * NJ;      // block rows; each wave owns BM/2 rows x 64 columns
   // The three ring stages are separate LDS arrays: the compiler's wait
@@ -270,11 +293,20 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
   static_assert(3 * BM * kRowB + 3 * kGN * kRowB >= BM * 256, "output tile must fit the ring");
 
   const int id = blockIdx.x;
-  const int xcd = id & 7;
-  const int slot = id >> 3;
-  const int mb = (slot / nn) * 8 + xcd;
-  const int nb = slot - (slot / nn) * nn;
-  if (mb >= nm) return;
+  int mb, nb, sp = 0;
+  if (splits == 1) {
+    const int xcd = id & 7;
+    const int slot = id >> 3;
+    mb = (slot / nn) * 8 + xcd;
+    nb = slot - (slot / nn) * nn;
+    if (mb >= nm) return;
+  } else {
+    const int nt = nm * nn;
+    sp = id / nt;
+    const int t = id - sp * nt;
+    mb = t / nn;
+    nb = t - mb * nn;
+  }
   const int64_t m0 = static_cast<int64_t>(mb) * BM;
   const int n0 = nb * kGN;
 
@@ -299,13 +331,13 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
   for (int i = 0; i < NJ; ++i) {
     const int r = 16 * (wave + 4 * i) + lr;
     const int64_t gm = min(m0 + r, M - 1);
-    xsrc[i] = X + gm * K + 8 * (lp ^ ((r >> 2) & 3));
+    xsrc[i] = X + gm * ldx + static_cast<int64_t>(sp) * K + 8 * (lp ^ ((r >> 2) & 3));
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int r = 16 * (wave + 4 * i) + lr;
     const int gn = min(n0 + r, N - 1);
-    wsrc[i] = W + static_cast<int64_t>(gn) * K + 8 * (lp ^ ((r >> 2) & 3));
+    wsrc[i] = W + gn * ldw + static_cast<int64_t>(sp) * K + 8 * (lp ^ ((r >> 2) & 3));
   }
   f32x16 acc[2][NJ];
 #pragma unroll
@@ -322,6 +354,33 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
     default: gemm_mainloop<NJ, 0>(sX0, sX1, sX2, sW0, sW1, sW2, xsrc, wsrc, acc, K / kGK, wave, wm, wn, l32, h);
   }
 
+  if constexpr (Epi::kF32) {
+    // C^T accumulator: lane -> row j*32 + lane%32, columns
+    // i*32 + 8*(r/4) + 4*h + r%4 of the wave's block
+    float* const out = epi.out + sp * epi.split_stride;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t m = m0 + wm * 32 * NJ + j * 32 + l32;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * 64 + i * 32 + 8 * g + 4 * h;
+          if (m < M && n < N) {
+            float4 v = make_float4(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                   acc[i][j][4 * g + 3]);
+            if (epi.addend) {
+              const float4 r = *reinterpret_cast<const float4*>(epi.addend + m * epi.ld + n);
+              v.x += r.x;
+              v.y += r.y;
+              v.z += r.z;
+              v.w += r.w;
+            }
+            *reinterpret_cast<float4*>(out + m * epi.ld + n) = v;
+          }
+        }
+    }
+  } else {
   // Output tile through LDS. C^T accumulator: lane -> row j*32 + lane%32,
   // columns i*32 + 8*(r/4) + 4*h + r%4 of the wave's block.
   // Per-element epilogue inputs (the residual of f2) are loaded first, all
@@ -377,6 +436,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
     const uint8_t* const blk = tile_block<NJ>(it / 2, sX0, sX1, sX2, sW0, sW1, sW2);
     if (m < M && n0 + nl < N)
       epi.store8(m, n0 + nl, *reinterpret_cast<const uint4*>(blk + tile_off(row, tid & 15)));
+  }
   }
 }
 
@@ -442,12 +502,122 @@ hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, int64_t M, int
   if (blocks256 >= 2 * 512) {
     const int nm = static_cast<int>((M + 255) / 256);
     const int grid = 8 * ((nm + 7) / 8) * nn;
-    hipLaunchKernelGGL((gemm_bf16_kernel<4, Epi>), dim3(grid), dim3(256), 0, s, x, w, M, N, K, nm, nn, epi);
+    hipLaunchKernelGGL((gemm_bf16_kernel<4, Epi>), dim3(grid), dim3(256), 0, s, x, w, M, N, K,
+                       static_cast<int64_t>(K), static_cast<int64_t>(K), nm, nn, 1, epi);
   } else {
     const int nm = static_cast<int>((M + 127) / 128);
     const int grid = 8 * ((nm + 7) / 8) * nn;
-    hipLaunchKernelGGL((gemm_bf16_kernel<2, Epi>), dim3(grid), dim3(256), 0, s, x, w, M, N, K, nm, nn, epi);
+    hipLaunchKernelGGL((gemm_bf16_kernel<2, Epi>), dim3(grid), dim3(256), 0, s, x, w, M, N, K,
+                       static_cast<int64_t>(K), static_cast<int64_t>(K), nm, nn, 1, epi);
   }
+  return hipGetLastError();
+}
+
+namespace {
+
+__global__ __launch_bounds__(256) void sum_splits_kernel(const float4* __restrict__ part, int splits,
+                                                         int64_t n4, float4* __restrict__ out) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    float4 a = part[i];
+    for (int sp = 1; sp < splits; ++sp) {
+      const float4 b = part[sp * n4 + i];
+      a.x += b.x;
+      a.y += b.y;
+      a.z += b.z;
+      a.w += b.w;
+    }
+    out[i] = a;
+  }
+}
+
+// 64 x 64 tiles: coalesced float4 row reads into LDS, then 16-byte bf16
+// writes of the transposed rows (8 consecutive source rows per thread). The
+// 65-float LDS rows make both the stores and the column reads conflict-free.
+__global__ __launch_bounds__(256) void to_bf16_t_kernel(const float* __restrict__ src, int64_t ld_src,
+                                                        int64_t rows, int cols, uint16_t* __restrict__ dst,
+                                                        int64_t ld_dst) {
+  __shared__ float t[64][65];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int c0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int r = it * 16 + (tid >> 4);
+    const int c = (tid & 15) * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r0 + r < rows && c0 + c < cols) v = *reinterpret_cast<const float4*>(src + (r0 + r) * ld_src + c0 + c);
+    t[r][c + 0] = v.x;
+    t[r][c + 1] = v.y;
+    t[r][c + 2] = v.z;
+    t[r][c + 3] = v.w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int idx = it * 256 + tid;
+    const int cc = idx >> 3;
+    const int ch = idx & 7;
+    if (c0 + cc < cols && r0 + ch * 8 < ld_dst) {
+      uint4 o;
+      o.x = pack_bf16x2(t[ch * 8 + 0][cc], t[ch * 8 + 1][cc]);
+      o.y = pack_bf16x2(t[ch * 8 + 2][cc], t[ch * 8 + 3][cc]);
+      o.z = pack_bf16x2(t[ch * 8 + 4][cc], t[ch * 8 + 5][cc]);
+      o.w = pack_bf16x2(t[ch * 8 + 6][cc], t[ch * 8 + 7][cc]);
+      *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(c0 + cc) * ld_dst + r0 + ch * 8) = o;
+    }
+  }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+// Split-K products (the weight gradients, few output tiles) take 256-row
+// blocks from M = 2048 up; single products the forward's rule.
+hipError_t launch_gemm_bf16_f32(const GemmBf16Args& g, hipStream_t s) {
+  if (g.M == 0 || g.N == 0) return hipSuccess;
+  if (g.kc <= 0 || g.kc % kGK != 0 || g.splits < 1 || g.lda % 8 != 0 || g.ldb % 8 != 0 || g.N % 4 != 0 ||
+      g.ldc % 4 != 0 || g.ldc < g.N || g.lda < static_cast<int64_t>(g.splits) * g.kc ||
+      g.ldb < static_cast<int64_t>(g.splits) * g.kc || (g.splits > 1 && g.addend) || !aligned16(g.a) ||
+      !aligned16(g.b) || !aligned16(g.c) || (g.addend && !aligned16(g.addend)))
+    return hipErrorInvalidValue;
+  const F32Epi epi{nullptr, g.c, g.addend, g.ldc, g.M * g.ldc};
+  const int nn = (g.N + kGN - 1) / kGN;
+  const bool big = g.splits > 1 ? g.M >= 2048 : (g.M + 255) / 256 * nn >= 2 * 512;
+  const int bm = big ? 256 : 128;
+  const int64_t nm = (g.M + bm - 1) / bm;
+  const int64_t grid = g.splits > 1 ? g.splits * nm * nn : 8 * ((nm + 7) / 8) * nn;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  if (big)
+    hipLaunchKernelGGL((gemm_bf16_kernel<4, F32Epi>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, g.a,
+                       g.b, g.M, g.N, g.kc, g.lda, g.ldb, static_cast<int>(nm), nn, g.splits, epi);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<2, F32Epi>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, g.a,
+                       g.b, g.M, g.N, g.kc, g.lda, g.ldb, static_cast<int>(nm), nn, g.splits, epi);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_splits(const float* part, int splits, int64_t n, float* out, hipStream_t s) {
+  if (n % 4 != 0 || splits < 1 || !aligned16(part) || !aligned16(out)) return hipErrorInvalidValue;
+  const int64_t n4 = n / 4;
+  if (n4 == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 4096);
+  hipLaunchKernelGGL(sum_splits_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     reinterpret_cast<const float4*>(part), splits, n4, reinterpret_cast<float4*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_to_bf16_t(const float* src, int64_t ld_src, int64_t rows, int cols, uint16_t* dst,
+                            int64_t ld_dst, hipStream_t s) {
+  if (cols % 4 != 0 || ld_src % 4 != 0 || ld_src < cols || ld_dst % 8 != 0 || ld_dst < rows || !aligned16(src) ||
+      !aligned16(dst))
+    return hipErrorInvalidValue;
+  if (cols == 0 || ld_dst == 0) return hipSuccess;
+  const int64_t gx = (ld_dst + 63) / 64;
+  if (gx > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(to_bf16_t_kernel, dim3(static_cast<unsigned>(gx), (cols + 63) / 64), dim3(256), 0, s,
+                     src, ld_src, rows, cols, dst, ld_dst);
   return hipGetLastError();
 }
 

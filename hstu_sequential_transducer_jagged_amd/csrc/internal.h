@@ -137,6 +137,33 @@ struct GemmF32Args {
 };
 hipError_t launch_gemm_f32_mma(const GemmF32Args& a, int epi, int splits, hipStream_t s);
 
+// bf16 products of the training backward: C[M, N] (fp32) = A[M, K] B[N, K]^T,
+// A and B row-major bf16 with row strides lda, ldb (% 8 == 0) and K
+// contiguous. K = splits * kc (kc % 32 == 0; rows zero-padded to that
+// length). splits == 1: C (+ addend, [M, ldc] fp32 or nullptr) is written;
+// splits > 1: split s writes its partial product to c + s * M * ldc, and
+// launch_sum_splits adds them up. N % 4 == 0, ldc % 4 == 0.
+struct GemmBf16Args {
+  const uint16_t* a;
+  int64_t lda;
+  const uint16_t* b;
+  int64_t ldb;
+  float* c;
+  int64_t ldc;
+  const float* addend;
+  int64_t M;
+  int N;
+  int kc;
+  int splits;
+};
+hipError_t launch_gemm_bf16_f32(const GemmBf16Args& g, hipStream_t s);
+// out[i] = sum over s < splits of part[s * n + i] (n % 4 == 0)
+hipError_t launch_sum_splits(const float* part, int splits, int64_t n, float* out, hipStream_t s);
+// dst[c * ld_dst + r] = bf16(src[r * ld_src + c]) for r < rows, c < cols, and
+// 0 for rows <= r < ld_dst: the transposed bf16 copy, zero-padded along r
+// (cols % 4 == 0, ld_src % 4 == 0, ld_dst % 8 == 0).
+hipError_t launch_to_bf16_t(const float* src, int64_t ld_src, int64_t rows, int cols, uint16_t* dst,
+                            int64_t ld_dst, hipStream_t s);
 hipError_t launch_proj_bf16(const ProjArgs& a, hipStream_t s);
 hipError_t launch_proj_f32(const ProjArgs& a, hipStream_t s);
 hipError_t launch_out_bf16(const OutArgs& a, hipStream_t s);

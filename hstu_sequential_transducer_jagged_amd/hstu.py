@@ -53,7 +53,7 @@ class LayerDesc(ctypes.Structure):
                 ("input_norm", ctypes.c_int32), ("target_no_self", ctypes.c_int32),
                 ("num_token_types", ctypes.c_int32), ("bias_mode", ctypes.c_int32),
                 ("linear_m_p", ctypes.c_float), ("linear_m_t", ctypes.c_float),
-                ("attn_bwd_bf16", ctypes.c_int32)]
+                ("attn_bwd_bf16", ctypes.c_int32), ("gemm_bwd_bf16", ctypes.c_int32)]
 
 
 class Jagged(ctypes.Structure):
@@ -159,11 +159,11 @@ def make_desc(d_model: int, num_heads: int, dtype: int, pos_table_len: int,
               input_norm: bool = False, target_no_self: bool = False,
               num_token_types: int = 0, bias_mode: int = HSTU_BIAS_TABLES,
               linear_m_p: float = 0.0, linear_m_t: float = 0.0,
-              attn_bwd_bf16: bool = False) -> LayerDesc:
+              attn_bwd_bf16: bool = False, gemm_bwd_bf16: bool = False) -> LayerDesc:
     return LayerDesc(d_model, num_heads, d_model // num_heads, dtype, alpha, ln_eps,
                      pos_table_len, num_time_buckets, int(bool(input_norm)), int(bool(target_no_self)),
                      int(num_token_types), int(bias_mode), float(linear_m_p), float(linear_m_t),
-                     int(bool(attn_bwd_bf16)))
+                     int(bool(attn_bwd_bf16)), int(bool(gemm_bwd_bf16)))
 
 
 def make_jagged(offsets, timestamps, max_seq_len: int, num_targets=None,

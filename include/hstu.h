@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 10
+#define HSTU_ABI_VERSION 11
 
 typedef enum {
   HSTU_OK = 0,
@@ -120,6 +120,16 @@ typedef struct {
                                layer (its forward recompute included) stays fp32. Gradients
                                then agree with the fp32 ones to the bf16 tolerance (2e-2),
                                not the fp32 one */
+  int32_t gemm_bwd_bf16;    /* 0 (default) or 1, read by the backward entry points: three
+                               products of the backward (dW2 = dY^T G, dW1 = dZ^T Xin and
+                               dX = dZ W1, with Xin the input of f1) run on the bf16
+                               matrix cores. Their operands are rounded to bf16 once, the
+                               sums are fp32; the weight gradients sum over the tokens in
+                               fixed splits (no atomics). dG = dY W2 stays fp32 (it feeds
+                               the attention gradients), and so does the forward
+                               recompute. Independent of attn_bwd_bf16. Gradients agree
+                               with the fp32 ones to the bf16 tolerance (2e-2). The
+                               workspace grows by the bf16 operand copies */
 } hstu_layer_desc;
 
 /* A jagged batch of the call's own tokens. */

@@ -30,6 +30,11 @@ hipError_t launch_attn_train_fwd(const BwdAttnArgs&, hipStream_t) { reached("lau
 hipError_t launch_attn_bwd_f32(const BwdAttnArgs&, hipStream_t) { reached("launch_attn_bwd_f32"); }
 hipError_t launch_attn_bwd_bf16(const BwdAttnArgs&, hipStream_t) { reached("launch_attn_bwd_bf16"); }
 hipError_t launch_to_bf16(const float*, uint16_t*, int64_t, hipStream_t) { reached("launch_to_bf16"); }
+hipError_t launch_to_bf16_t(const float*, int64_t, int64_t, int, uint16_t*, int64_t, hipStream_t) {
+  reached("launch_to_bf16_t");
+}
+hipError_t launch_gemm_bf16_f32(const GemmBf16Args&, hipStream_t) { reached("launch_gemm_bf16_f32"); }
+hipError_t launch_sum_splits(const float*, int, int64_t, float*, hipStream_t) { reached("launch_sum_splits"); }
 hipError_t launch_gemm_f32s(const float*, int64_t, int64_t, const float*, int64_t, int64_t, float*, int64_t,
                             const float*, const float*, int, int, int64_t, int, hipStream_t) {
   reached("launch_gemm_f32s");

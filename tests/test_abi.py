@@ -35,7 +35,7 @@ def test_header_declares_the_binding_exports():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.hstu_abi_version() == 10
+    assert lib.hstu_abi_version() == 11
 
 
 def _desc(**kw):
@@ -209,6 +209,17 @@ def test_backward_validates(lib):
     assert call(f, p=None) == hstu.HSTU_E_INVAL
     assert call(f, dx=FAKE) == hstu.HSTU_E_INVAL                     # dx aliases x
     assert call(f, wsb=ws - 1) == hstu.HSTU_E_WORKSPACE
+    # bf16 backward products: bf16 dZ (T x 4d), the transposed dY, G, Xin
+    # (d x 32) and dZ (4d x 32) padded to one 32-token split, W1^T and one
+    # split's partial dW1, each rounded up to 256 bytes
+    g16 = hstu.make_desc(64, 2, hstu.HSTU_F32, 255, gemm_bwd_bf16=True)
+    extra = 5120 + 3 * 4096 + 16384 + 32768 + 65536
+    assert lib.hstu_layer_bwd_workspace_size(ctypes.byref(g16), ctypes.byref(jag)) == ws + extra
+    assert call(g16) == hstu.HSTU_E_WORKSPACE
+    bad = hstu.make_desc(64, 2, hstu.HSTU_F32, 255)
+    bad.gemm_bwd_bf16 = 2
+    assert call(bad) == hstu.HSTU_E_INVAL
+    assert b"gemm_bwd_bf16" in lib.hstu_last_error()
 
 
 def test_train_pair_validates(lib):
