@@ -71,7 +71,7 @@ def parse():
                     help="with --backward: the attention backward on the bf16 matrix cores "
                          "(desc.attn_bwd_bf16); the all-fp32 backward is timed beside it")
     ap.add_argument("--gemm-bwd-bf16", action="store_true",
-                    help="with --backward: the backward's products dW2, dW1 and dX on the bf16 "
+                    help="with --backward: the backward's products dG, dW2, dW1 and dX on the bf16 "
                          "matrix cores (desc.gemm_bwd_bf16); the all-fp32 backward is timed beside it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,

@@ -575,10 +575,10 @@ TokSplit tok_split(int64_t T) {
 }
 
 // Byte offsets of the bf16 backward products' buffers, from the start of
-// their region: dZ in bf16; dY^T, G^T, Xin^T and dZ^T in bf16 with tp
-// columns; W1^T in bf16; the split partial sums of dW1 or dW2.
+// their region: dY and dZ in bf16; dY^T, G^T, Xin^T and dZ^T in bf16 with tp
+// columns; W1^T and W2^T in bf16; the split partial sums of dW1 or dW2.
 struct GemmBf16Ws {
-  size_t dz16, dyt, gt, xint, dzt, w1t, part, bytes;
+  size_t dy16, dz16, dyt, gt, xint, dzt, w1t, w2t, part, bytes;
 };
 GemmBf16Ws gemm_bf16_ws(int64_t T, int d) {
   const TokSplit ts = tok_split(T);
@@ -590,12 +590,14 @@ GemmBf16Ws gemm_bf16_ws(int64_t T, int d) {
     o += round256(n);
     return at;
   };
+  w.dy16 = take(t * dd * 2);
   w.dz16 = take(t * 4 * dd * 2);
   w.dyt = take(dd * tp * 2);
   w.gt = take(dd * tp * 2);
   w.xint = take(dd * tp * 2);
   w.dzt = take(4 * dd * tp * 2);
   w.w1t = take(4 * dd * dd * 2);
+  w.w2t = take(dd * dd * 2);
   w.part = take(static_cast<size_t>(ts.S) * 4 * dd * dd * 4);
   w.bytes = o;
   return w;
@@ -610,13 +612,27 @@ size_t train_ws_base(const hstu_layer_desc* desc, size_t T) {
   return (desc->input_norm ? 18 : 17) * td + round256(T * sizeof(float)) + bf;
 }
 
+// With attn_bwd_bf16 and head_dim 64 the attention forward of the training
+// layer also runs on the bf16 kernel (from the bf16 copies of Q, K, V); its
+// work list and partial outputs follow the bf16 products' region.
+bool train_fwd_bf16(const hstu_layer_desc* desc) {
+  return desc->attn_bwd_bf16 == 1 && desc->head_dim == 64 && desc->d_model <= 1024;
+}
+size_t train_attn16_bytes(const hstu_layer_desc* desc, const hstu_jagged* j) {
+  if (!train_fwd_bf16(desc)) return 0;
+  return round256(hstu::attn_plan(j->num_seqs, j->max_seq_len, desc->num_heads, j->total_tokens,
+                                  desc->d_model).workspace_bytes);
+}
+
 }  // namespace
 
 size_t hstu_layer_bwd_workspace_size(const hstu_layer_desc* desc, const hstu_jagged* jagged) {
-  if (!desc || !jagged || jagged->total_tokens < 0 || desc->d_model <= 0) return 0;
+  if (!desc || !jagged || jagged->total_tokens < 0 || desc->d_model <= 0 || jagged->num_seqs < 0 ||
+      jagged->max_seq_len < 0)
+    return 0;
   const size_t T = static_cast<size_t>(jagged->total_tokens);
   const size_t g16 = desc->gemm_bwd_bf16 == 1 ? gemm_bf16_ws(jagged->total_tokens, desc->d_model).bytes : 0;
-  return train_ws_base(desc, T) + g16;
+  return train_ws_base(desc, T) + g16 + train_attn16_bytes(desc, jagged);
 }
 
 namespace {
@@ -717,17 +733,23 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
   uint16_t* V16 = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(B16) + 2 * tb16);
   uint16_t* DAV16 = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(B16) + 3 * tb16);
 
+  // the attention forward on the bf16 kernel: its work list and partials
+  const bool fwd16 = train_fwd_bf16(desc);
+  void* const attn16_ws = w + train_ws_base(desc, static_cast<size_t>(T)) +
+                          (desc->gemm_bwd_bf16 == 1 ? gemm_bf16_ws(T, d).bytes : 0);
   // bf16 operand copies and split partials of the backward's products
   const bool g16 = desc->gemm_bwd_bf16 == 1;
   const TokSplit ts = tok_split(T);
   const GemmBf16Ws gw = gemm_bf16_ws(T, d);
   char* const g16w = w + train_ws_base(desc, static_cast<size_t>(T));
+  uint16_t* const DY16 = reinterpret_cast<uint16_t*>(g16w + gw.dy16);
   uint16_t* const DZ16 = reinterpret_cast<uint16_t*>(g16w + gw.dz16);
   uint16_t* const DYT = reinterpret_cast<uint16_t*>(g16w + gw.dyt);
   uint16_t* const GT = reinterpret_cast<uint16_t*>(g16w + gw.gt);
   uint16_t* const XINT = reinterpret_cast<uint16_t*>(g16w + gw.xint);
   uint16_t* const DZT = reinterpret_cast<uint16_t*>(g16w + gw.dzt);
   uint16_t* const W1T = reinterpret_cast<uint16_t*>(g16w + gw.w1t);
+  uint16_t* const W2T = reinterpret_cast<uint16_t*>(g16w + gw.w2t);
   float* const PART = reinterpret_cast<float*>(g16w + gw.part);
 
   const float* X = static_cast<const float*>(x);
@@ -773,7 +795,24 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
     }
   }
   if (fwd) {
-    HSTU_TRY(hstu::launch_attn_train_fwd(ba, s), "attention forward");
+    if (bf16_bwd) {
+      // the bf16 copies of Q, K, V that the attention backward reads (kept
+      // in the workspace for the two-call step)
+      const int64_t n = T * d;
+      HSTU_TRY(hstu::launch_to_bf16(Q, Q16, n, s), "bf16 copy");
+      HSTU_TRY(hstu::launch_to_bf16(K, K16, n, s), "bf16 copy");
+      HSTU_TRY(hstu::launch_to_bf16(V, V16, n, s), "bf16 copy");
+    }
+    if (fwd16) {
+      // AV = (SiLU(a Q K^T + rab) . M) V on the bf16 kernel, fp32 out
+      hstu_layer_desc d16 = *desc;
+      d16.dtype = HSTU_BF16;
+      const hstu::AttnArgs a = make_attn_args(&d16, jagged, nullptr, Q16, K16, V16, params->pos_bias,
+                                              params->time_bias, AV, attn16_ws);
+      HSTU_TRY(hstu::launch_attn_bf16(a, s), "attention forward (bf16)");
+    } else {
+      HSTU_TRY(hstu::launch_attn_train_fwd(ba, s), "attention forward");
+    }
     HSTU_TRY(hstu::launch_ln_gate_fwd(AV, U, params->ln_gamma, params->ln_beta, NH, RSTD, G, T, d,
                                       desc->ln_eps, s), "ln/gate forward");
   }
@@ -791,17 +830,18 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
     return hstu::launch_gemm_bf16_f32(g, s);
   };
   // Y = X + G W2^T + b2
-  // dG stays fp32 in both modes: it feeds dAV, which the bf16 attention
-  // backward rounds again, and the table gradients would carry both roundings
-  HSTU_TRY(hstu::launch_gemm_f32s(DY, d, 1, W2, d, 1, DG, d, nullptr, nullptr, static_cast<int>(T), d, d, 1,
-                                  s), "dG gemm");
   if (g16) {
-    // dW2 = dY^T G over the tokens, in splits
+    // dG = dY W2 (B = W2^T); dW2 = dY^T G over the tokens, in splits
+    HSTU_TRY(hstu::launch_to_bf16(DY, DY16, T * d, s), "bf16 copy");
+    HSTU_TRY(hstu::launch_to_bf16_t(W2, d, d, d, W2T, d, s), "bf16 transpose");
     HSTU_TRY(hstu::launch_to_bf16_t(DY, d, T, d, DYT, ts.tp, s), "bf16 transpose");
     HSTU_TRY(hstu::launch_to_bf16_t(G, d, T, d, GT, ts.tp, s), "bf16 transpose");
+    HSTU_TRY(gemm16(DY16, d, W2T, d, DG, d, nullptr, T, d, d, 1), "dG gemm (bf16)");
     HSTU_TRY(gemm16(DYT, ts.tp, GT, ts.tp, PART, d, nullptr, d, d, ts.kc, ts.S), "dW2 gemm (bf16)");
     HSTU_TRY(hstu::launch_sum_splits(PART, ts.S, static_cast<int64_t>(d) * d, grads->dw2, s), "dW2 sum");
   } else {
+    HSTU_TRY(hstu::launch_gemm_f32s(DY, d, 1, W2, d, 1, DG, d, nullptr, nullptr, static_cast<int>(T), d, d, 1,
+                                    s), "dG gemm");
     HSTU_TRY(hstu::launch_gemm_f32s(DY, 1, d, G, d, 1, grads->dw2, d, nullptr, nullptr, d, d, T,
                                     splits(d, d), s), "dW2 gemm");
   }
@@ -814,11 +854,7 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
   ba.dv = DZ + d; ba.dq = DZ + 2 * d; ba.dk = DZ + 3 * d; ba.ld_dz = d4;
   ba.dpos = grads->dpos; ba.dtime = grads->dtime;
   if (bf16_bwd) {
-    const int64_t n = T * d;
-    HSTU_TRY(hstu::launch_to_bf16(Q, Q16, n, s), "bf16 copy");
-    HSTU_TRY(hstu::launch_to_bf16(K, K16, n, s), "bf16 copy");
-    HSTU_TRY(hstu::launch_to_bf16(V, V16, n, s), "bf16 copy");
-    HSTU_TRY(hstu::launch_to_bf16(DAV, DAV16, n, s), "bf16 copy");
+    HSTU_TRY(hstu::launch_to_bf16(DAV, DAV16, T * d, s), "bf16 copy");
     ba.q16 = Q16; ba.k16 = K16; ba.v16 = V16; ba.dav16 = DAV16;
     HSTU_TRY(hstu::launch_attn_bwd_bf16(ba, s), "attention backward (bf16)");
   } else {

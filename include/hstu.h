@@ -112,24 +112,30 @@ typedef struct {
                                time_bias are not read (may be NULL). Untyped, forward only */
   float linear_m_p;         /* slopes of HSTU_BIAS_LINEAR, finite */
   float linear_m_t;
-  int32_t attn_bwd_bf16;    /* 0 (default) or 1, read by the backward entry points
-                               (hstu_layer_bwd, hstu_layer_bwd_after_fwd): the attention
-                               backward runs on the bf16 matrix cores. Q, K, V and dAV are
-                               rounded to bf16 once, P and dS as the operands of their
-                               products; every sum is fp32, and every other step of the
-                               layer (its forward recompute included) stays fp32. Gradients
-                               then agree with the fp32 ones to the bf16 tolerance (2e-2),
-                               not the fp32 one */
-  int32_t gemm_bwd_bf16;    /* 0 (default) or 1, read by the backward entry points: three
-                               products of the backward (dW2 = dY^T G, dW1 = dZ^T Xin and
-                               dX = dZ W1, with Xin the input of f1) run on the bf16
-                               matrix cores. Their operands are rounded to bf16 once, the
-                               sums are fp32; the weight gradients sum over the tokens in
-                               fixed splits (no atomics). dG = dY W2 stays fp32 (it feeds
-                               the attention gradients), and so does the forward
-                               recompute. Independent of attn_bwd_bf16. Gradients agree
-                               with the fp32 ones to the bf16 tolerance (2e-2). The
-                               workspace grows by the bf16 operand copies */
+  int32_t attn_bwd_bf16;    /* 0 (default) or 1, read by the training entry points
+                               (hstu_layer_bwd, hstu_layer_fwd_train,
+                               hstu_layer_bwd_after_fwd): the attention backward runs on
+                               the bf16 matrix cores, and with head_dim 64 so does the
+                               attention forward of the training layer (the recompute, and
+                               hstu_layer_fwd_train's), on the forward path's kernel with
+                               fp32 AV. Q, K, V and dAV are rounded to bf16 once, P and dS
+                               as the operands of their products; every sum is fp32. Other
+                               steps stay fp32 (see gemm_bwd_bf16 for the products).
+                               Gradients then agree with the fp32 ones to the bf16
+                               tolerance: matrices per row to 2e-2, vector entries to 2e-2
+                               of themselves or 2^-7 of the magnitude of the terms they
+                               sum */
+  int32_t gemm_bwd_bf16;    /* 0 (default) or 1, read by the backward entry points: the four
+                               products of the backward (dG = dY W2, dW2 = dY^T G,
+                               dW1 = dZ^T Xin, dX = dZ W1 with Xin the input of f1) run on
+                               the bf16 matrix cores. Their operands are rounded to bf16
+                               once, the sums are fp32; the weight gradients sum over the
+                               tokens in fixed splits (no atomics). Independent of
+                               attn_bwd_bf16. Gradients then agree with the fp32 ones to
+                               the bf16 tolerance: matrices per row to 2e-2, vector
+                               entries to 2e-2 of themselves or 2^-7 of the magnitude of
+                               the terms they sum. The workspace grows by the bf16
+                               operand copies */
 } hstu_layer_desc;
 
 /* A jagged batch of the call's own tokens. */
@@ -370,7 +376,8 @@ int hstu_layer_bwd(const hstu_layer_desc *desc, const hstu_layer_params *params,
 
 /* A training step in two calls, without the backward's forward recompute.
  * hstu_layer_fwd_train: the layer forward in fp32 (same equations and
- * support as hstu_layer_bwd: HSTU_F32, plain causal attention), writing y [T, d] (must not alias x) and keeping in `workspace`
+ * support as hstu_layer_bwd: HSTU_F32, plain causal attention; the attention
+ * on bf16 with desc->attn_bwd_bf16), writing y [T, d] (must not alias x) and keeping in `workspace`
  * (hstu_layer_bwd_workspace_size() bytes, 256-byte aligned) the activations
  * the backward reads: Z, U, V, Q, K, AV, the normalised AV, 1/sigma and G
  * (and LayerNorm(X) with input_norm).

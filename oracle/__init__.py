@@ -21,6 +21,7 @@ from .hstu_oracle import (  # noqa: F401
     ranking_independent,
     silu,
     silu_grad,
+    silu_grad2,
     stack,
     stochastic_length,
     time_bucket,

@@ -399,15 +399,36 @@ def silu_grad(z):
     return s * (1.0 + z * (1.0 - s))
 
 
+def silu_grad2(z):
+    """d^2 SiLU / dz^2 = s (1 - s) (2 + z (1 - 2 s)), s = sigmoid(z)."""
+    z = np.asarray(z, dtype=F64)
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-z))
+    return s * (1.0 - s) * (2.0 + z * (1.0 - 2.0 * s))
+
+
 def layer_backward(x, p, offsets, timestamps, dy, num_heads: int, n_max: int,
-                   alpha: float = 1.0, eps: float = 1e-5) -> Dict[str, np.ndarray]:
+                   alpha: float = 1.0, eps: float = 1e-5,
+                   magnitudes: bool = False) -> Dict[str, np.ndarray]:
     """Gradients of <Y, dY> for one layer with plain causal attention (no
     targets, no cache), the generative-training setting of [GR-7.1] §7.1.5:
     dX, dW1, db1, dW2, db2, dgamma, dbeta and the gradients of the position
     and time tables (the shared rab: every pair adds its score gradient,
     summed over heads, to the entry it read); with ``p.input_norm`` also
     dln1_gamma and dln1_beta of the input LayerNorm. The chain rule applied to the
-    forward of layer() step by step, in float64."""
+    forward of layer() step by step, in float64.
+
+    With ``magnitudes``, the result also holds ``mag``: for each vector
+    gradient, the sum of the absolute values of the terms it adds up (the
+    scale of the rounding error of a sum whose terms are computed in lower
+    precision). The terms are the rows summed over tokens for db1, db2,
+    dgamma, dbeta, dln1_gamma and dln1_beta. For the two tables a pair's
+    term is its score gradient dS = SiLU'(S) dP with dP = dAV_i . V_j and
+    S = alpha Q_i . K_j + rab, two dot products over the head's dh features;
+    its magnitude is the first-order change of dS when every product in
+    those dot products moves by its own size:
+    |SiLU'(S)| (|dAV_i| . |V_j|) + |SiLU''(S)| |dP| |alpha| (|Q_i| . |K_j|).
+    Test scaffolding: not a gradient."""
     x = np.asarray(x, F64)
     dy = np.asarray(dy, F64)
     offsets = np.asarray(offsets, np.int64)
@@ -436,6 +457,7 @@ def layer_backward(x, p, offsets, timestamps, dy, num_heads: int, n_max: int,
     av = np.zeros((T, d))
     dq, dk, dv = np.zeros((T, d)), np.zeros((T, d)), np.zeros((T, d))
     dpos, dtime = np.zeros_like(pb), np.zeros_like(tb)
+    mpos, mtime = np.zeros_like(pb), np.zeros_like(tb)
     seqs = []
     for b in range(offsets.shape[0] - 1):
         s, e = int(offsets[b]), int(offsets[b + 1])
@@ -485,20 +507,33 @@ def layer_backward(x, p, offsets, timestamps, dy, num_heads: int, n_max: int,
             dk[s:e, c] += alpha * (ds.T @ q[s:e, c])
             np.add.at(dpos, idx[mask], ds[mask])
             np.add.at(dtime, bkt[mask], ds[mask])
+            if magnitudes:
+                mds = (np.abs(silu_grad(sc)) * (np.abs(dav[s:e, c]) @ np.abs(v[s:e, c]).T)
+                       + np.abs(silu_grad2(sc)) * np.abs(dpm) * abs(alpha)
+                       * (np.abs(q[s:e, c]) @ np.abs(k[s:e, c]).T))
+                np.add.at(mpos, idx[mask], mds[mask])
+                np.add.at(mtime, bkt[mask], mds[mask])
     # U, V, Q, K = Split(SiLU(Z)), Z = X W1^T + b1
     dz = np.concatenate([du, dv, dq, dk], axis=1) * silu_grad(z)
     dw1 = dz.T @ xin
     db1 = dz.sum(axis=0)
     dxin = dz @ w1
     extra = {}
+    mag = dict(db1=np.abs(dz).sum(axis=0), db2=np.abs(dy).sum(axis=0),
+               dgamma=np.abs(dnrm * nhat).sum(axis=0), dbeta=np.abs(dnrm).sum(axis=0),
+               dpos=mpos, dtime=mtime)
     if norm1:
         # xin = xhat1 gamma1 + beta1, xhat1 = (x - mean) / sigma over the d features
         extra["dln1_gamma"] = (dxin * xhat1).sum(axis=0)
         extra["dln1_beta"] = dxin.sum(axis=0)
+        mag["dln1_gamma"] = np.abs(dxin * xhat1).sum(axis=0)
+        mag["dln1_beta"] = np.abs(dxin).sum(axis=0)
         dxh = dxin * g1
         dxin = rstd1 * (dxh - dxh.mean(axis=1, keepdims=True)
                         - xhat1 * (dxh * xhat1).mean(axis=1, keepdims=True))
     dx = dy + dxin
+    if magnitudes:
+        extra["mag"] = mag
     return dict(**extra, dx=dx, dw1=dw1, db1=db1, dw2=dw2, db2=db2, dgamma=dgamma, dbeta=dbeta,
                 dpos=dpos, dtime=dtime)
 

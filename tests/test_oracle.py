@@ -891,6 +891,80 @@ def test_layer_backward_linear_in_dy_and_residual():
         assert np.all(g0[kk] == 0), kk
 
 
+def test_silu_grad2_matches_central_differences():
+    """SiLU'' against the central difference of SiLU', its value 1/2 at 0
+    and its decay far from 0."""
+    z = np.linspace(-12.0, 12.0, 97)
+    h = 1e-5
+    num = (oracle.silu_grad(z + h) - oracle.silu_grad(z - h)) / (2 * h)
+    np.testing.assert_allclose(oracle.silu_grad2(z), num, rtol=1e-6, atol=1e-9)
+    assert oracle.silu_grad2(np.array([0.0]))[0] == 0.5
+    assert abs(oracle.silu_grad2(np.array([60.0]))[0]) < 1e-20
+
+
+def _mag_case(seed, norm1):
+    import copy
+    w, dy = _bwd_case(seed)
+    p = copy.copy(w.layers[0])
+    if norm1:
+        rng = np.random.default_rng(seed + 7)
+        p.input_norm = True
+        p.ln1_gamma = 1.0 + 0.3 * rng.standard_normal(8)
+        p.ln1_beta = 0.2 * rng.standard_normal(8)
+    return w, p, dy
+
+
+@pytest.mark.parametrize("norm1", [False, True])
+def test_backward_magnitudes_bound_and_balance(norm1):
+    """The term magnitudes of the vector gradients: the gradients are the
+    same with and without them; each entry is at most its magnitude
+    (triangle inequality); every visible pair and head adds its magnitude to
+    one entry of each table, so the two tables' magnitudes have equal sums;
+    and they scale with |c| when dY is multiplied by c (every term is linear
+    in dY)."""
+    w, p, dy = _mag_case(11, norm1)
+    x = np.asarray(w.x, np.float64)
+    args = (x, p, w.offsets, w.timestamps)
+    kw = dict(num_heads=w.num_heads, n_max=w.n_max, alpha=w.alpha, eps=w.ln_eps)
+    g = oracle.layer_backward(*args, dy, **kw, magnitudes=True)
+    plain = oracle.layer_backward(*args, dy, **kw)
+    assert "mag" not in plain
+    for k in plain:
+        np.testing.assert_array_equal(g[k], plain[k])
+    mag = g["mag"]
+    names = ["db1", "db2", "dgamma", "dbeta", "dpos", "dtime"] + (["dln1_gamma", "dln1_beta"] if norm1 else [])
+    assert sorted(mag) == sorted(names)
+    for k in names:
+        assert mag[k].shape == g[k].shape
+        assert np.all(mag[k] >= np.abs(g[k]) * (1 - 1e-12)), k
+    assert mag["dpos"].sum() > 0
+    np.testing.assert_allclose(mag["dpos"].sum(), mag["dtime"].sum(), rtol=1e-12)
+    g3 = oracle.layer_backward(*args, -3.0 * dy, **kw, magnitudes=True)
+    for k in names:
+        np.testing.assert_allclose(g3["mag"][k], 3.0 * mag[k], rtol=1e-12, atol=1e-300)
+
+
+def test_backward_magnitudes_special_cases():
+    """With dY >= 0 every term of db2 is non-negative, so its magnitude is
+    db2 itself; with W2 = 0 no gradient reaches G's producers, and every
+    magnitude but db2's is zero; with dY = 0 all are zero."""
+    import copy
+    w, p, dy = _mag_case(12, False)
+    x = np.asarray(w.x, np.float64)
+    kw = dict(num_heads=w.num_heads, n_max=w.n_max, alpha=w.alpha, eps=w.ln_eps, magnitudes=True)
+    g = oracle.layer_backward(x, p, w.offsets, w.timestamps, np.abs(dy), **kw)
+    np.testing.assert_allclose(g["mag"]["db2"], g["db2"], rtol=1e-12)
+    p0 = copy.copy(p)
+    p0.w2 = np.zeros_like(p.w2)
+    g0 = oracle.layer_backward(x, p0, w.offsets, w.timestamps, dy, **kw)
+    for k, m in g0["mag"].items():
+        if k != "db2":
+            assert np.all(m == 0), k
+    gz = oracle.layer_backward(x, p, w.offsets, w.timestamps, np.zeros_like(dy), **kw)
+    for k, m in gz["mag"].items():
+        assert np.all(m == 0), k
+
+
 # ---------------------------------------------------------------------------
 # type-aware rab ("HSTU：Scaling Law 的首次探索" §7.1.4, innovation 2)
 # ---------------------------------------------------------------------------
