@@ -71,8 +71,9 @@ def parse():
                     help="with --backward: the attention backward on the bf16 matrix cores "
                          "(desc.attn_bwd_bf16); the all-fp32 backward is timed beside it")
     ap.add_argument("--gemm-bwd-bf16", action="store_true",
-                    help="with --backward: the backward's products dG, dW2, dW1 and dX on the bf16 "
-                         "matrix cores (desc.gemm_bwd_bf16); the all-fp32 backward is timed beside it")
+                    help="with --backward: every product of the training layer (f1, and dG, dW2, dW1, dX "
+                         "of the backward) on the bf16 matrix cores (desc.gemm_bwd_bf16); the all-fp32 "
+                         "backward is timed beside it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
                     help="approximate CPU seconds for the oracle sample")
@@ -484,8 +485,8 @@ def run_backward(args):
     flop = 8.0 * T * d * d + 4.0 * d * P + 20.0 * T * d * d + 8.0 * d * P
     # executed: the dQ and the dK/dV kernels each recompute S and dP (another 6dP)
     flop_exec = flop + 6.0 * d * P
-    on16 = [n for n, f in (("attention backward", args.attn_bwd_bf16),
-                           ("backward products", args.gemm_bwd_bf16)) if f]
+    on16 = [n for n, f in (("attention", args.attn_bwd_bf16),
+                           ("products", args.gemm_bwd_bf16)) if f]
     rec = base_record(args, "HSTU layer backward tokens/s (fp32, forward recompute included"
                       + (", " + " and ".join(on16) + " on bf16 matrix cores" if on16 else "") + "), 1 GPU",
                       T / (ms * 1e-3), "tokens/s", ms, "f32",

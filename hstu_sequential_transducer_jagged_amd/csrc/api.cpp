@@ -574,11 +574,13 @@ TokSplit tok_split(int64_t T) {
   return {static_cast<int>(S), static_cast<int>(kc), S * kc};
 }
 
-// Byte offsets of the bf16 backward products' buffers, from the start of
-// their region: dY and dZ in bf16; dY^T, G^T, Xin^T and dZ^T in bf16 with tp
-// columns; W1^T and W2^T in bf16; the split partial sums of dW1 or dW2.
+// Byte offsets of the bf16 products' buffers, from the start of their
+// region: the operands of f1 as bf16 hi/lo splits (Xin [T, 3d], W1 [4d, 3d]),
+// those of f2 (G, W2) in bf16; dY and dZ in
+// bf16; dY^T, G^T, Xin^T and dZ^T in bf16 with tp columns; W1^T and W2^T in
+// bf16; the split partial sums of dW1 or dW2.
 struct GemmBf16Ws {
-  size_t dy16, dz16, dyt, gt, xint, dzt, w1t, w2t, part, bytes;
+  size_t xin16, w1_16, g16, w2_16, dy16, dz16, dyt, gt, xint, dzt, w1t, w2t, part, bytes;
 };
 GemmBf16Ws gemm_bf16_ws(int64_t T, int d) {
   const TokSplit ts = tok_split(T);
@@ -590,6 +592,10 @@ GemmBf16Ws gemm_bf16_ws(int64_t T, int d) {
     o += round256(n);
     return at;
   };
+  w.xin16 = take(t * 3 * dd * 2);
+  w.w1_16 = take(4 * dd * 3 * dd * 2);
+  w.g16 = take(t * dd * 2);
+  w.w2_16 = take(dd * dd * 2);
   w.dy16 = take(t * dd * 2);
   w.dz16 = take(t * 4 * dd * 2);
   w.dyt = take(dd * tp * 2);
@@ -742,6 +748,10 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
   const TokSplit ts = tok_split(T);
   const GemmBf16Ws gw = gemm_bf16_ws(T, d);
   char* const g16w = w + train_ws_base(desc, static_cast<size_t>(T));
+  uint16_t* const XIN16 = reinterpret_cast<uint16_t*>(g16w + gw.xin16);
+  uint16_t* const W1_16 = reinterpret_cast<uint16_t*>(g16w + gw.w1_16);
+  uint16_t* const G16 = reinterpret_cast<uint16_t*>(g16w + gw.g16);
+  uint16_t* const W2_16 = reinterpret_cast<uint16_t*>(g16w + gw.w2_16);
   uint16_t* const DY16 = reinterpret_cast<uint16_t*>(g16w + gw.dy16);
   uint16_t* const DZ16 = reinterpret_cast<uint16_t*>(g16w + gw.dz16);
   uint16_t* const DYT = reinterpret_cast<uint16_t*>(g16w + gw.dyt);
@@ -772,12 +782,30 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
   hstu::BwdAttnArgs ba = make_train_args(desc, jagged, Q, K, V, params->pos_bias, params->time_bias);
   ba.av = AV;
   const float* XIN = norm1 ? XN : X;   // the input of f1
+  // C[M, N] = A[M, K] B[N, K]^T on bf16 copies (K = S * kc with splits)
+  auto gemm16 = [&](const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb, float* c, int64_t ldc,
+                    const float* addend, int64_t M, int N, int kc, int S) {
+    hstu::GemmBf16Args g{a, lda, b, ldb, c, ldc, addend, M, N, kc, S};
+    return hstu::launch_gemm_bf16_f32(g, s);
+  };
   // forward: Z = X W1^T + b1 and [U V Q K] = SiLU(Z) in one pass
   if (fwd) {
     if (norm1) {
       st = do_layernorm(desc, T, x, params->ln1_gamma, params->ln1_beta, XN, s);
       if (st) return st;
     }
+  }
+  if (fwd && g16) {
+    // f1 feeds every gradient: its operands are split into bf16 hi and lo
+    // parts, [Xh | Xl | Xh] [Wh | Wh | Wl]^T over 3d, fp32-like products
+    HSTU_TRY(hstu::launch_to_bf16x3(XIN, T, d, XIN16, 0, s), "bf16 split");
+    HSTU_TRY(hstu::launch_to_bf16x3(W1, d4, d, W1_16, 1, s), "bf16 split");
+    hstu::GemmBf16Args g{XIN16, 3 * d, W1_16, 3 * d, Z, d4, nullptr, T, d4, 3 * d, 1};
+    g.bias = params->b1;
+    g.act[0] = U; g.act[1] = V; g.act[2] = Q; g.act[3] = K;
+    g.act_w = d;
+    HSTU_TRY(hstu::launch_gemm_bf16_f32(g, s), "projection (bf16)");
+  } else if (fwd) {
     hstu::GemmF32Args g{};
     g.A = XIN; g.sam = d; g.sak = 1;
     g.B = W1; g.sbk = 1; g.sbn = d;
@@ -818,17 +846,19 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
   }
   if (!bwd) {
     // Y = X + G W2^T + b2
-    HSTU_TRY(hstu::launch_gemm_f32s(G, d, 1, W2, 1, d, static_cast<float*>(y), d, X,
-                                    static_cast<const float*>(params->b2), static_cast<int>(T), d, d, 1, s),
-             "output gemm");
+    if (g16) {
+      HSTU_TRY(hstu::launch_to_bf16(G, G16, T * d, s), "bf16 copy");
+      HSTU_TRY(hstu::launch_to_bf16(W2, W2_16, static_cast<int64_t>(d) * d, s), "bf16 copy");
+      hstu::GemmBf16Args g{G16, d, W2_16, d, static_cast<float*>(y), d, X, T, d, d, 1};
+      g.bias = params->b2;
+      HSTU_TRY(hstu::launch_gemm_bf16_f32(g, s), "output gemm (bf16)");
+    } else {
+      HSTU_TRY(hstu::launch_gemm_f32s(G, d, 1, W2, 1, d, static_cast<float*>(y), d, X,
+                                      static_cast<const float*>(params->b2), static_cast<int>(T), d, d, 1, s),
+               "output gemm");
+    }
     return ok();
   }
-  // C[M, N] = A[M, K] B[N, K]^T on bf16 copies (K = S * kc with splits)
-  auto gemm16 = [&](const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb, float* c, int64_t ldc,
-                    const float* addend, int64_t M, int N, int kc, int S) {
-    hstu::GemmBf16Args g{a, lda, b, ldb, c, ldc, addend, M, N, kc, S};
-    return hstu::launch_gemm_bf16_f32(g, s);
-  };
   // Y = X + G W2^T + b2
   if (g16) {
     // dG = dY W2 (B = W2^T); dW2 = dY^T G over the tokens, in splits

@@ -136,16 +136,19 @@ struct OutEpi {
   }
 };
 
-// fp32 output straight from the accumulators (16-byte stores of 4 columns),
-// plus an fp32 addend; split s of a split-K product writes to
-// out + s * split_stride. No bias.
+// fp32 output straight from the accumulators (16-byte stores of 4 columns):
+// v = acc + bias (+ addend) to out, and optionally SiLU(v) split by columns
+// into act[0..3] (blocks of act_w columns, row stride act_w). Split s of a
+// split-K product writes to out + s * split_stride (no bias, addend or act).
 struct F32Epi {
   static constexpr bool kF32 = true;
-  const float* bias;      // always nullptr
-  float* out;
+  const float* bias;      // [N] or nullptr
+  float* out;             // or nullptr
   const float* addend;    // or nullptr
   int64_t ld;             // row stride of out and addend
   int64_t split_stride;
+  float* act[4];          // act[0] nullptr: no activation output
+  int act_w;
 };
 
 // One ring stage of DMA: wave w fills X rows 16i .. 16i+15 for i = w, w+4, ...
@@ -357,7 +360,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
   if constexpr (Epi::kF32) {
     // C^T accumulator: lane -> row j*32 + lane%32, columns
     // i*32 + 8*(r/4) + 4*h + r%4 of the wave's block
-    float* const out = epi.out + sp * epi.split_stride;
+    float* const out = epi.out ? epi.out + sp * epi.split_stride : nullptr;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int64_t m = m0 + wm * 32 * NJ + j * 32 + l32;
@@ -365,10 +368,12 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * 64 + i * 32 + 8 * g + 4 * h;
+          const int nl = wn * 64 + i * 32 + 8 * g + 4 * h;
+          const int n = n0 + nl;
           if (m < M && n < N) {
-            float4 v = make_float4(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                   acc[i][j][4 * g + 3]);
+            const float4 b = *reinterpret_cast<const float4*>(&sbias[nl]);
+            float4 v = make_float4(acc[i][j][4 * g + 0] + b.x, acc[i][j][4 * g + 1] + b.y,
+                                   acc[i][j][4 * g + 2] + b.z, acc[i][j][4 * g + 3] + b.w);
             if (epi.addend) {
               const float4 r = *reinterpret_cast<const float4*>(epi.addend + m * epi.ld + n);
               v.x += r.x;
@@ -376,7 +381,21 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
               v.z += r.z;
               v.w += r.w;
             }
-            *reinterpret_cast<float4*>(out + m * epi.ld + n) = v;
+            if (out) *reinterpret_cast<float4*>(out + m * epi.ld + n) = v;
+            if (epi.act[0]) {
+              // the 4 columns lie in one block (act_w % 4 == 0)
+              int c = n;
+              float* p = epi.act[0];
+              if (c >= epi.act_w) { p = epi.act[1]; c -= epi.act_w; }
+              if (c >= epi.act_w) { p = epi.act[2]; c -= epi.act_w; }
+              if (c >= epi.act_w) { p = epi.act[3]; c -= epi.act_w; }
+              float4 a;
+              a.x = v.x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * v.x));
+              a.y = v.y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * v.y));
+              a.z = v.z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * v.z));
+              a.w = v.w * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * v.w));
+              *reinterpret_cast<float4*>(p + m * epi.act_w + c) = a;
+            }
           }
         }
     }
@@ -569,20 +588,60 @@ __global__ __launch_bounds__(256) void to_bf16_t_kernel(const float* __restrict_
   }
 }
 
+// Row r of src (cols floats) -> row r of dst (3 cols bf16): x = hi + lo with
+// hi = bf16(x) and lo = bf16(x - hi); the three column blocks are
+// [hi | lo | hi] (lo_last == 0) or [hi | hi | lo] (lo_last == 1), so that
+// [A_hi | A_lo | A_hi] [B_hi | B_hi | B_lo]^T = A_hi B_hi^T + A_lo B_hi^T +
+// A_hi B_lo^T: the product of the two fp32 matrices up to the lo*lo term.
+__global__ __launch_bounds__(256) void to_bf16x3_kernel(const float4* __restrict__ src, int64_t rows, int cols4,
+                                                        uint2* __restrict__ dst, int lo_last) {
+  const int64_t n4 = rows * cols4;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t r = i / cols4;
+    const int64_t c = i - r * cols4;
+    const float4 v = src[i];
+    const uint2 hi = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+    const float4 l = make_float4(v.x - bf2f(hi.x & 0xffff), v.y - bf2f(hi.x >> 16), v.z - bf2f(hi.y & 0xffff),
+                                 v.w - bf2f(hi.y >> 16));
+    const uint2 lo = make_uint2(pack_bf16x2(l.x, l.y), pack_bf16x2(l.z, l.w));
+    uint2* const row = dst + r * 3 * cols4;
+    row[c] = hi;
+    row[cols4 + c] = lo_last ? hi : lo;
+    row[2 * cols4 + c] = lo_last ? lo : hi;
+  }
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
+
+hipError_t launch_to_bf16x3(const float* src, int64_t rows, int cols, uint16_t* dst, int lo_last, hipStream_t s) {
+  if (cols % 4 != 0 || !aligned16(src) || !aligned16(dst)) return hipErrorInvalidValue;
+  const int64_t n4 = rows * (cols / 4);
+  if (n4 == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 8192);
+  hipLaunchKernelGGL(to_bf16x3_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     reinterpret_cast<const float4*>(src), rows, cols / 4, reinterpret_cast<uint2*>(dst), lo_last);
+  return hipGetLastError();
+}
 
 // Split-K products (the weight gradients, few output tiles) take 256-row
 // blocks from M = 2048 up; single products the forward's rule.
 hipError_t launch_gemm_bf16_f32(const GemmBf16Args& g, hipStream_t s) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
+  const bool act = g.act[0] != nullptr;
   if (g.kc <= 0 || g.kc % kGK != 0 || g.splits < 1 || g.lda % 8 != 0 || g.ldb % 8 != 0 || g.N % 4 != 0 ||
       g.ldc % 4 != 0 || g.ldc < g.N || g.lda < static_cast<int64_t>(g.splits) * g.kc ||
-      g.ldb < static_cast<int64_t>(g.splits) * g.kc || (g.splits > 1 && g.addend) || !aligned16(g.a) ||
-      !aligned16(g.b) || !aligned16(g.c) || (g.addend && !aligned16(g.addend)))
+      g.ldb < static_cast<int64_t>(g.splits) * g.kc ||
+      (g.splits > 1 && (g.addend || g.bias || act || !g.c)) || !aligned16(g.a) || !aligned16(g.b) ||
+      (g.c && !aligned16(g.c)) || (g.addend && !aligned16(g.addend)) ||
+      (act && (g.act_w <= 0 || g.act_w % 4 != 0 || static_cast<int64_t>(g.act_w) * 4 != g.N)))
     return hipErrorInvalidValue;
-  const F32Epi epi{nullptr, g.c, g.addend, g.ldc, g.M * g.ldc};
+  for (int i = 0; act && i < 4; ++i)
+    if (!g.act[i] || !aligned16(g.act[i])) return hipErrorInvalidValue;
+  const F32Epi epi{g.bias, g.c, g.addend, g.ldc, g.M * g.ldc, {g.act[0], g.act[1], g.act[2], g.act[3]},
+                   g.act_w};
   const int nn = (g.N + kGN - 1) / kGN;
   const bool big = g.splits > 1 ? g.M >= 2048 : (g.M + 255) / 256 * nn >= 2 * 512;
   const int bm = big ? 256 : 128;

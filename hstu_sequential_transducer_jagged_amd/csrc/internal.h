@@ -137,12 +137,15 @@ struct GemmF32Args {
 };
 hipError_t launch_gemm_f32_mma(const GemmF32Args& a, int epi, int splits, hipStream_t s);
 
-// bf16 products of the training backward: C[M, N] (fp32) = A[M, K] B[N, K]^T,
+// bf16 products of the training layer: C[M, N] (fp32) = A[M, K] B[N, K]^T,
 // A and B row-major bf16 with row strides lda, ldb (% 8 == 0) and K
 // contiguous. K = splits * kc (kc % 32 == 0; rows zero-padded to that
-// length). splits == 1: C (+ addend, [M, ldc] fp32 or nullptr) is written;
-// splits > 1: split s writes its partial product to c + s * M * ldc, and
-// launch_sum_splits adds them up. N % 4 == 0, ldc % 4 == 0.
+// length). splits == 1: C + bias (+ addend, [M, ldc] fp32 or nullptr) is
+// written to c (if not nullptr), and with act[0] set also SiLU of it split
+// into the four [M, act_w] arrays act[0..3] (N == 4 act_w); splits > 1 (no
+// bias, addend or act): split s writes its partial product to
+// c + s * M * ldc, and launch_sum_splits adds them up. N % 4 == 0,
+// ldc % 4 == 0.
 struct GemmBf16Args {
   const uint16_t* a;
   int64_t lda;
@@ -155,8 +158,17 @@ struct GemmBf16Args {
   int N;
   int kc;
   int splits;
+  const float* bias = nullptr;
+  float* act[4] = {nullptr, nullptr, nullptr, nullptr};
+  int act_w = 0;
 };
 hipError_t launch_gemm_bf16_f32(const GemmBf16Args& g, hipStream_t s);
+// dst [rows, 3 cols] bf16 from src [rows, cols] fp32 (cols % 4 == 0): each
+// value split as hi = bf16(x), lo = bf16(x - hi), the column blocks
+// [hi | lo | hi] (lo_last 0) or [hi | hi | lo] (lo_last 1). A bf16 product of
+// an lo_last-0 copy of A with an lo_last-1 copy of B, contracted over the
+// 3 cols, is A B^T up to the lo*lo term (about 2^-16 relative per product).
+hipError_t launch_to_bf16x3(const float* src, int64_t rows, int cols, uint16_t* dst, int lo_last, hipStream_t s);
 // out[i] = sum over s < splits of part[s * n + i] (n % 4 == 0)
 hipError_t launch_sum_splits(const float* part, int splits, int64_t n, float* out, hipStream_t s);
 // dst[c * ld_dst + r] = bf16(src[r * ld_src + c]) for r < rows, c < cols, and

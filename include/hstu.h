@@ -125,12 +125,16 @@ typedef struct {
                                tolerance: matrices per row to 2e-2, vector entries to 2e-2
                                of themselves or 2^-7 of the magnitude of the terms they
                                sum */
-  int32_t gemm_bwd_bf16;    /* 0 (default) or 1, read by the backward entry points: the four
-                               products of the backward (dG = dY W2, dW2 = dY^T G,
-                               dW1 = dZ^T Xin, dX = dZ W1 with Xin the input of f1) run on
-                               the bf16 matrix cores. Their operands are rounded to bf16
-                               once, the sums are fp32; the weight gradients sum over the
-                               tokens in fixed splits (no atomics). Independent of
+  int32_t gemm_bwd_bf16;    /* 0 (default) or 1, read by the training entry points: every
+                               product of the training layer runs on the bf16 matrix cores:
+                               f1 (Z = Xin W1^T + b1 with the SiLU split, Xin the input of
+                               f1), f2 of hstu_layer_fwd_train, and the backward's
+                               dG = dY W2, dW2 = dY^T G, dW1 = dZ^T Xin and dX = dZ W1.
+                               Their operands are rounded to bf16 once (f1's are split
+                               into bf16 hi and lo parts, three products contracted
+                               together, since f1 feeds every gradient), the sums and
+                               outputs are fp32; the weight gradients sum over the tokens
+                               in fixed splits (no atomics). Independent of
                                attn_bwd_bf16. Gradients then agree with the fp32 ones to
                                the bf16 tolerance: matrices per row to 2e-2, vector
                                entries to 2e-2 of themselves or 2^-7 of the magnitude of

@@ -34,6 +34,9 @@ hipError_t launch_to_bf16_t(const float*, int64_t, int64_t, int, uint16_t*, int6
   reached("launch_to_bf16_t");
 }
 hipError_t launch_gemm_bf16_f32(const GemmBf16Args&, hipStream_t) { reached("launch_gemm_bf16_f32"); }
+hipError_t launch_to_bf16x3(const float*, int64_t, int, uint16_t*, int, hipStream_t) {
+  reached("launch_to_bf16x3");
+}
 hipError_t launch_sum_splits(const float*, int, int64_t, float*, hipStream_t) { reached("launch_sum_splits"); }
 hipError_t launch_gemm_f32s(const float*, int64_t, int64_t, const float*, int64_t, int64_t, float*, int64_t,
                             const float*, const float*, int, int, int64_t, int, hipStream_t) {

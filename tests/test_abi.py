@@ -209,11 +209,13 @@ def test_backward_validates(lib):
     assert call(f, p=None) == hstu.HSTU_E_INVAL
     assert call(f, dx=FAKE) == hstu.HSTU_E_INVAL                     # dx aliases x
     assert call(f, wsb=ws - 1) == hstu.HSTU_E_WORKSPACE
-    # bf16 backward products: bf16 dY, dZ (T x d, T x 4d), the transposed
-    # dY, G, Xin (d x 32) and dZ (4d x 32) padded to one 32-token split,
-    # W1^T, W2^T and one split's partial dW1, each rounded up to 256 bytes
+    # bf16 products: Xin and W1 as bf16 hi/lo splits (3 columns per value),
+    # bf16 G, W2 (f2), dY, dZ (T x d, T x 4d),
+    # the transposed dY, G, Xin (d x 32) and dZ (4d x 32) padded to one
+    # 32-token split, W1^T, W2^T and one split's partial dW1, each rounded up
+    # to 256 bytes
     g16 = hstu.make_desc(64, 2, hstu.HSTU_F32, 255, gemm_bwd_bf16=True)
-    extra = 1280 + 5120 + 3 * 4096 + 16384 + 32768 + 8192 + 65536
+    extra = (3 * 1280 + 3 * 32768 + 1280 + 8192) + 1280 + 5120 + 3 * 4096 + 16384 + 32768 + 8192 + 65536
     assert lib.hstu_layer_bwd_workspace_size(ctypes.byref(g16), ctypes.byref(jag)) == ws + extra
     assert call(g16) == hstu.HSTU_E_WORKSPACE
     bad = hstu.make_desc(64, 2, hstu.HSTU_F32, 255)

@@ -227,6 +227,9 @@ def test_bf16_products_backward_with_input_norm(gpu_lib, two_calls, attn):
         hstu.hstu_layer_bwd_after_fwd(desc, lay.params, dw.jagged, dw.x, f32(dy), dx, grads, ws)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(to_np(dx), dx_one)
+        # y of the forward call (f1 and f2 on bf16)
+        ref_y = oracle.layer(w.x, p, w.offsets, w.timestamps, w.num_heads, w.n_max, w.alpha, w.ln_eps)["y"]
+        assert row_rel_err(to_np(y), ref_y) < TOL
     ref = oracle.layer_backward(w.x, p, w.offsets, w.timestamps, dy, w.num_heads, w.n_max, w.alpha, w.ln_eps,
                                 magnitudes=True)
     names = ["dw1", "db1", "dw2", "db2", "dgamma", "dbeta", "dpos", "dtime", "dln1_gamma", "dln1_beta"]
