@@ -804,6 +804,10 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
     g.bias = params->b1;
     g.act[0] = U; g.act[1] = V; g.act[2] = Q; g.act[3] = K;
     g.act_w = d;
+    if (bf16_bwd) {
+      // the bf16 copies of V, Q, K the bf16 attention reads
+      g.act16[1] = V16; g.act16[2] = Q16; g.act16[3] = K16;
+    }
     HSTU_TRY(hstu::launch_gemm_bf16_f32(g, s), "projection (bf16)");
   } else if (fwd) {
     hstu::GemmF32Args g{};
@@ -823,9 +827,9 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
     }
   }
   if (fwd) {
-    if (bf16_bwd) {
-      // the bf16 copies of Q, K, V that the attention backward reads (kept
-      // in the workspace for the two-call step)
+    if (bf16_bwd && !g16) {
+      // the bf16 copies of Q, K, V that the attention reads (kept in the
+      // workspace for the two-call step; with g16 the projection wrote them)
       const int64_t n = T * d;
       HSTU_TRY(hstu::launch_to_bf16(Q, Q16, n, s), "bf16 copy");
       HSTU_TRY(hstu::launch_to_bf16(K, K16, n, s), "bf16 copy");
@@ -891,12 +895,10 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
     HSTU_TRY(hstu::launch_attn_bwd_f32(ba, s), "attention backward");
   }
   // [U V Q K] = SiLU(X W1^T + b1)
-  HSTU_TRY(hstu::launch_silu_bwd(DZ, Z, T * d4, s), "silu backward");
-  HSTU_TRY(hstu::launch_colsum(DZ, d4, T, d4, grads->db1, s), "db1");
   if (g16) {
-    // dW1 = dZ^T Xin over the tokens, in splits; dX (or dXn) = dZ W1 (B = W1^T)
-    HSTU_TRY(hstu::launch_to_bf16(DZ, DZ16, T * d4, s), "bf16 copy");
-    HSTU_TRY(hstu::launch_to_bf16_t(DZ, d4, T, d4, DZT, ts.tp, s), "bf16 transpose");
+    // dZ in bf16 (row-major and transposed) and db1 in one pass; dW1 = dZ^T
+    // Xin over the tokens, in splits; dX (or dXn) = dZ W1 (B = W1^T)
+    HSTU_TRY(hstu::launch_silu_bwd_bf16(DZ, Z, T, d4, DZ16, DZT, ts.tp, grads->db1, s), "silu backward (bf16)");
     HSTU_TRY(hstu::launch_to_bf16_t(XIN, d, T, d, XINT, ts.tp, s), "bf16 transpose");
     HSTU_TRY(hstu::launch_to_bf16_t(W1, d, d4, d, W1T, d4, s), "bf16 transpose");
     HSTU_TRY(gemm16(DZT, ts.tp, XINT, ts.tp, PART, d, nullptr, d4, d, ts.kc, ts.S), "dW1 gemm (bf16)");
@@ -910,6 +912,8 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
     }
     return ok();
   }
+  HSTU_TRY(hstu::launch_silu_bwd(DZ, Z, T * d4, s), "silu backward");
+  HSTU_TRY(hstu::launch_colsum(DZ, d4, T, d4, grads->db1, s), "db1");
   HSTU_TRY(hstu::launch_gemm_f32s(DZ, 1, d4, XIN, d, 1, grads->dw1, d, nullptr, nullptr, d4, d, T,
                                   splits(d4, d), s), "dW1 gemm");
   if (norm1) {

@@ -257,6 +257,63 @@ __global__ __launch_bounds__(256) void silu_bwd_kernel(float* dz, const float* _
   }
 }
 
+// dZ = d[U V Q K] . SiLU'(Z) for the bf16 products, in 64 x 64 tiles: dZ in
+// bf16 row-major (dz16 [T, n], the A operand of dX = dZ W1), dZ^T in bf16
+// with tp columns, zero past T (dzt [n, tp], the A operand of
+// dW1 = dZ^T Xin), and the column sums of dZ in fp32 added to db1 (one
+// atomic per column and tile). The fp32 dZ is not written back.
+__global__ __launch_bounds__(256) void silu_bwd_bf16_kernel(const float* __restrict__ dz,
+                                                            const float* __restrict__ z, int64_t T, int n,
+                                                            uint16_t* __restrict__ dz16,
+                                                            uint16_t* __restrict__ dzt, int64_t tp,
+                                                            float* db1) {
+  __shared__ float t[64][65];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int c0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int r = it * 16 + (tid >> 4);
+    const int c = (tid & 15) * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r0 + r < T && c0 + c < n) {
+      const int64_t o = (r0 + r) * n + c0 + c;
+      const float4 g = *reinterpret_cast<const float4*>(dz + o);
+      const float4 zz = *reinterpret_cast<const float4*>(z + o);
+      float sg;
+      sg = sigmoid_f(zz.x); v.x = g.x * sg * (1.0f + zz.x * (1.0f - sg));
+      sg = sigmoid_f(zz.y); v.y = g.y * sg * (1.0f + zz.y * (1.0f - sg));
+      sg = sigmoid_f(zz.z); v.z = g.z * sg * (1.0f + zz.z * (1.0f - sg));
+      sg = sigmoid_f(zz.w); v.w = g.w * sg * (1.0f + zz.w * (1.0f - sg));
+      *reinterpret_cast<uint2*>(dz16 + o) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+    }
+    t[r][c + 0] = v.x;
+    t[r][c + 1] = v.y;
+    t[r][c + 2] = v.z;
+    t[r][c + 3] = v.w;
+  }
+  __syncthreads();
+  if (tid < 64 && c0 + tid < n && r0 < T) {
+    float sum = 0.0f;
+    for (int r = 0; r < 64; ++r) sum += t[r][tid];
+    atomicAdd(&db1[c0 + tid], sum);
+  }
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int idx = it * 256 + tid;
+    const int cc = idx >> 3;
+    const int ch = idx & 7;
+    if (c0 + cc < n && r0 + ch * 8 < tp) {
+      uint4 o;
+      o.x = pack_bf16x2(t[ch * 8 + 0][cc], t[ch * 8 + 1][cc]);
+      o.y = pack_bf16x2(t[ch * 8 + 2][cc], t[ch * 8 + 3][cc]);
+      o.z = pack_bf16x2(t[ch * 8 + 4][cc], t[ch * 8 + 5][cc]);
+      o.w = pack_bf16x2(t[ch * 8 + 6][cc], t[ch * 8 + 7][cc]);
+      *reinterpret_cast<uint4*>(dzt + static_cast<int64_t>(c0 + cc) * tp + r0 + ch * 8) = o;
+    }
+  }
+}
+
 int blocks_for(int64_t n) {
   const int64_t b = (n + 255) / 256;
   return static_cast<int>(b < 4096 ? (b > 0 ? b : 1) : 4096);
@@ -340,6 +397,18 @@ hipError_t launch_ln_gate_bwd(const float* dg, const float* u, const float* nhat
 hipError_t launch_silu_bwd(float* dz, const float* z, int64_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(silu_bwd_kernel, dim3(blocks_for(n)), dim3(256), 0, s, dz, z, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_bwd_bf16(const float* dz, const float* z, int64_t T, int n, uint16_t* dz16,
+                                uint16_t* dzt, int64_t tp, float* db1, hipStream_t s) {
+  const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  if (n % 4 != 0 || tp % 8 != 0 || tp < T || !a16(dz) || !a16(z) || !a16(dz16) || !a16(dzt)) return hipErrorInvalidValue;
+  if (n == 0 || tp == 0) return hipSuccess;
+  const int64_t gx = (tp + 63) / 64;
+  if (gx > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(silu_bwd_bf16_kernel, dim3(static_cast<unsigned>(gx), (n + 63) / 64), dim3(256), 0, s, dz,
+                     z, T, n, dz16, dzt, tp, db1);
   return hipGetLastError();
 }
 

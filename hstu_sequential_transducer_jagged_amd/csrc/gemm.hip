@@ -149,6 +149,7 @@ struct F32Epi {
   int64_t split_stride;
   float* act[4];          // act[0] nullptr: no activation output
   int act_w;
+  uint16_t* act16[4];     // bf16 copies of the act blocks, each nullptr or [M, act_w]
 };
 
 // One ring stage of DMA: wave w fills X rows 16i .. 16i+15 for i = w, w+4, ...
@@ -386,15 +387,19 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
               // the 4 columns lie in one block (act_w % 4 == 0)
               int c = n;
               float* p = epi.act[0];
-              if (c >= epi.act_w) { p = epi.act[1]; c -= epi.act_w; }
-              if (c >= epi.act_w) { p = epi.act[2]; c -= epi.act_w; }
-              if (c >= epi.act_w) { p = epi.act[3]; c -= epi.act_w; }
+              uint16_t* p16 = epi.act16[0];
+              if (c >= epi.act_w) { p = epi.act[1]; p16 = epi.act16[1]; c -= epi.act_w; }
+              if (c >= epi.act_w) { p = epi.act[2]; p16 = epi.act16[2]; c -= epi.act_w; }
+              if (c >= epi.act_w) { p = epi.act[3]; p16 = epi.act16[3]; c -= epi.act_w; }
               float4 a;
               a.x = v.x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * v.x));
               a.y = v.y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * v.y));
               a.z = v.z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * v.z));
               a.w = v.w * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * v.w));
               *reinterpret_cast<float4*>(p + m * epi.act_w + c) = a;
+              if (p16)
+                *reinterpret_cast<uint2*>(p16 + m * epi.act_w + c) =
+                    make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
             }
           }
         }
@@ -638,10 +643,11 @@ hipError_t launch_gemm_bf16_f32(const GemmBf16Args& g, hipStream_t s) {
       (g.c && !aligned16(g.c)) || (g.addend && !aligned16(g.addend)) ||
       (act && (g.act_w <= 0 || g.act_w % 4 != 0 || static_cast<int64_t>(g.act_w) * 4 != g.N)))
     return hipErrorInvalidValue;
-  for (int i = 0; act && i < 4; ++i)
-    if (!g.act[i] || !aligned16(g.act[i])) return hipErrorInvalidValue;
+  for (int i = 0; i < 4; ++i)
+    if ((act && (!g.act[i] || !aligned16(g.act[i]))) || (g.act16[i] && (!act || !aligned16(g.act16[i]))))
+      return hipErrorInvalidValue;
   const F32Epi epi{g.bias, g.c, g.addend, g.ldc, g.M * g.ldc, {g.act[0], g.act[1], g.act[2], g.act[3]},
-                   g.act_w};
+                   g.act_w, {g.act16[0], g.act16[1], g.act16[2], g.act16[3]}};
   const int nn = (g.N + kGN - 1) / kGN;
   const bool big = g.splits > 1 ? g.M >= 2048 : (g.M + 255) / 256 * nn >= 2 * 512;
   const int bm = big ? 256 : 128;

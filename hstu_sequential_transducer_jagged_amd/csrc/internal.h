@@ -142,7 +142,8 @@ hipError_t launch_gemm_f32_mma(const GemmF32Args& a, int epi, int splits, hipStr
 // contiguous. K = splits * kc (kc % 32 == 0; rows zero-padded to that
 // length). splits == 1: C + bias (+ addend, [M, ldc] fp32 or nullptr) is
 // written to c (if not nullptr), and with act[0] set also SiLU of it split
-// into the four [M, act_w] arrays act[0..3] (N == 4 act_w); splits > 1 (no
+// into the four [M, act_w] arrays act[0..3] (N == 4 act_w), and into bf16
+// copies act16[i] where those are set; splits > 1 (no
 // bias, addend or act): split s writes its partial product to
 // c + s * M * ldc, and launch_sum_splits adds them up. N % 4 == 0,
 // ldc % 4 == 0.
@@ -161,6 +162,7 @@ struct GemmBf16Args {
   const float* bias = nullptr;
   float* act[4] = {nullptr, nullptr, nullptr, nullptr};
   int act_w = 0;
+  uint16_t* act16[4] = {nullptr, nullptr, nullptr, nullptr};
 };
 hipError_t launch_gemm_bf16_f32(const GemmBf16Args& g, hipStream_t s);
 // dst [rows, 3 cols] bf16 from src [rows, cols] fp32 (cols % 4 == 0): each
@@ -264,6 +266,11 @@ hipError_t launch_ln_gate_bwd(const float* dg, const float* u, const float* nhat
                               const float* gamma, const float* beta, float* du, int64_t ldu, float* dav,
                               float* dgamma, float* dbeta, int64_t M, int d, hipStream_t s);
 hipError_t launch_silu_bwd(float* dz, const float* z, int64_t n, hipStream_t s);
+// dZ = dz . SiLU'(z) over [T, n] fp32 (not written back): dz16 [T, n] bf16,
+// dzt [n, tp] bf16 (dZ^T, zero for T <= t < tp), and db1[c] += sum_t dZ[t, c]
+// (n % 4 == 0, tp % 8 == 0, tp >= T).
+hipError_t launch_silu_bwd_bf16(const float* dz, const float* z, int64_t T, int n, uint16_t* dz16,
+                                uint16_t* dzt, int64_t tp, float* db1, hipStream_t s);
 
 // Error channel of the C ABI (hstu_last_error), for entry points defined
 // outside api.cpp: api_fail records a message and returns code.

@@ -57,6 +57,10 @@ hipError_t launch_ln_gate_bwd(const float*, const float*, const float*, const fl
   reached("launch_ln_gate_bwd");
 }
 hipError_t launch_silu_bwd(float*, const float*, int64_t, hipStream_t) { reached("launch_silu_bwd"); }
+hipError_t launch_silu_bwd_bf16(const float*, const float*, int64_t, int, uint16_t*, uint16_t*, int64_t, float*,
+                                hipStream_t) {
+  reached("launch_silu_bwd_bf16");
+}
 hipError_t launch_gather_rows(int64_t, int, const int64_t*, int64_t, const void*, void*, hipStream_t) {
   reached("launch_gather_rows");
 }
