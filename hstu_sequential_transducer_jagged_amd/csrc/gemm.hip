@@ -24,6 +24,7 @@ namespace hstu {
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Block tile: 256 rows (M) x 128 output columns (N), K staged 32 at a time.
 // Four waves, each 128 rows x 64 columns; the product is formed transposed,
@@ -101,13 +102,16 @@ struct ProjEpi {
   // 8 columns from n (n % 8 == 0, K % 64 == 0) lie in one block; the block
   // is picked by compares, so that the pointers stay in scalar registers
   // (readfirstlane keeps the compiler from turning the select of kernel
-  // arguments into a per-lane load from the argument block)
+  // arguments into a per-lane load from the argument block). Nontemporal
+  // stores: the 8 d bytes per token leave the caches to the operand tiles
+  // (f1 0.24 -> 0.19 ms, the layer 2 % faster, measured on the 16 x
+  // U[2048, 8192] workload).
   __device__ __forceinline__ void store8(int64_t m, int n, const uint4& o) const {
     uint16_t* p = uniform_ptr(out0);
     if (n >= K) { p = uniform_ptr(out1); n -= K; }
     if (n >= K) { p = uniform_ptr(out2); n -= K; }
     if (n >= K) { p = uniform_ptr(out3); n -= K; }
-    *reinterpret_cast<uint4*>(p + m * K + n) = o;
+    __builtin_nontemporal_store(u32x4{o.x, o.y, o.z, o.w}, reinterpret_cast<u32x4*>(p + m * K + n));
   }
 };
 
