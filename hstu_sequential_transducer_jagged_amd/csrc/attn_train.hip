@@ -615,20 +615,41 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
       }
     // this block's keys, for the transposed reads of the second product
     stash_block<DH>(kblk, kf, lc, g);
+    // per 16-key half: every LDS read first (key times and position-window
+    // entries, then the time-table entries of the buckets), then the
+    // arithmetic for every pair, masked by a select; read behind the
+    // visibility test, each pair's lookups were waited for on their own
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt) {
+      int64_t tk[4];
+      float wq[4][2], tvq[4][2];
+      int tbq[4][2];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tk[r] = kts[16 * kt + 4 * g + r];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) wq[r][qt] = win[16 * qt + lc - (16 * kt + 4 * g + r) + 31];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) tbq[r][qt] = time_bucket64(tq[qt] - tk[r], a.nb);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) tvq[r][qt] = s_tval[tbq[r][qt]];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int jr = 16 * kt + 4 * g + r;   // key row in the block
-        const int64_t tk = kts[jr];
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
           const int ir = 16 * qt + lc;        // query row in the block
           const bool vis = qv[qt] && (j0 + jr <= q0 + ir);
-          const int tb = time_bucket64(tq[qt] - tk, a.nb);
-          const float sc = a.alpha * sacc[kt][qt][r] + win[ir - jr + 31] + s_tval[tb];
+          const int tb = tbq[r][qt];
+          const float sc = a.alpha * sacc[kt][qt][r] + wq[r][qt] + tvq[r][qt];
           const float sg = sigmoid_t(sc);
-          const float ds = vis ? pacc[kt][qt][r] * sg * (1.0f + sc * (1.0f - sg)) : 0.0f;
+          const float dsv = pacc[kt][qt][r] * sg * (1.0f + sc * (1.0f - sg));
+          const float ds = vis ? dsv : 0.0f;
           sacc[kt][qt][r] = ds;
           const bool flush = vis && tb != tb_cur[qt];
           if (flush) atomicAdd(&s_tgrad[tb_cur[qt]], tg_cur[qt]);
@@ -636,6 +657,7 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
           tb_cur[qt] = flush ? tb : tb_cur[qt];
         }
       }
+    }
     // park dS (query row ir = 16 qt + lc, key rows 16 kt + 4g .. +3)
     float* dsw = s_ds[wave];
 #pragma unroll
@@ -658,12 +680,23 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
     // (rows ir with key row jr = ir - l + 31 in the block; hidden pairs hold
     // dS = 0). LDS accesses of one wave complete in order, so the block is
     // read back without a barrier.
+    // The reads go out eight at a time into distinct registers: left to
+    // itself the compiler reuses one register and waits for each read.
     float pos_sum = 0.0f;
 #pragma unroll
-    for (int ir = 0; ir < 32; ++ir) {
-      const int jr = ir - lane + 31;   // in the block for ir in [lane - 31, lane]
-      const float v = dsw[ir * DSR + min(max(jr, 0), 31)];
-      pos_sum += (jr >= 0 && jr < 32) ? v : 0.0f;
+    for (int b = 0; b < 4; ++b) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int ir = 8 * b + e, jr = ir - lane + 31;   // in the block for ir in [lane - 31, lane]
+        v[e] = dsw[ir * DSR + min(max(jr, 0), 31)];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int ir = 8 * b + e, jr = ir - lane + 31;
+        pos_sum += (jr >= 0 && jr < 32) ? v[e] : 0.0f;
+      }
     }
     if (lane < 63 && pos_sum != 0.0f) {
       const int gi = D + lane;   // difference D + lane - 31
