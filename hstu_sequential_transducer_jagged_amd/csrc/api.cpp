@@ -676,6 +676,8 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
   CHECK(!norm1 || ((!params->ln1_gamma || aligned16(params->ln1_gamma)) &&
                    (!params->ln1_beta || aligned16(params->ln1_beta))),
         HSTU_E_INVAL, "ln1_gamma/ln1_beta must be 16-byte aligned");
+  CHECK((!params->ln_gamma || aligned16(params->ln_gamma)) && (!params->ln_beta || aligned16(params->ln_beta)),
+        HSTU_E_INVAL, "ln_gamma/ln_beta must be 16-byte aligned");
   const int64_t T = jagged->total_tokens;
   const int d = desc->d_model;
   const bool empty = T == 0 || jagged->num_seqs == 0;

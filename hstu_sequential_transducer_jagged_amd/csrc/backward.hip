@@ -115,8 +115,20 @@ __global__ __launch_bounds__(256) void colsum_kernel(const float* __restrict__ X
   }
 }
 
+// The row kernels below hold a row of d <= 1024 floats in registers, as up
+// to four float4 per lane (float4 i of lane l covers columns 4 (l + 64 i) ..
+// +3), read once with 16-byte loads.
+constexpr int kRow4 = 4;
+
+__device__ __forceinline__ float4 ld4(const float* p, int c4, int n4) {
+  return c4 < n4 ? *reinterpret_cast<const float4*>(p + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+__device__ __forceinline__ float4 ld4_or(const float* p, int c4, float v) {
+  return p ? *reinterpret_cast<const float4*>(p + 4 * c4) : make_float4(v, v, v, v);
+}
+
 // Per row (one wave): N^ = (AV - mean) * rstd, G = (N^ gamma + beta) . U.
-// Keeps N^ and rstd for the backward.
+// Keeps N^ and rstd for the backward. d % 4 == 0.
 __global__ __launch_bounds__(256) void ln_gate_fwd_kernel(const float* __restrict__ av,
                                                           const float* __restrict__ u,
                                                           const float* gamma, const float* beta,
@@ -125,27 +137,43 @@ __global__ __launch_bounds__(256) void ln_gate_fwd_kernel(const float* __restric
   const int lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
+  const int n4 = d >> 2;
   const float* x = av + row * d;
+  float4 xv[kRow4];
   float s = 0.0f;
-  for (int c = lane; c < d; c += 64) s += x[c];
+#pragma unroll
+  for (int i = 0; i < kRow4; ++i) {
+    xv[i] = ld4(x, lane + 64 * i, n4);
+    s += (xv[i].x + xv[i].y) + (xv[i].z + xv[i].w);
+  }
   const float mean = wave_sum(s) / static_cast<float>(d);
   float ss = 0.0f;
-  for (int c = lane; c < d; c += 64) {
-    const float t = x[c] - mean;
-    ss += t * t;
+#pragma unroll
+  for (int i = 0; i < kRow4; ++i) {
+    if (lane + 64 * i >= n4) continue;
+    const float a0 = xv[i].x - mean, a1 = xv[i].y - mean, a2 = xv[i].z - mean, a3 = xv[i].w - mean;
+    ss += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
   }
   const float rstd = 1.0f / sqrtf(wave_sum(ss) / static_cast<float>(d) + eps);
-  for (int c = lane; c < d; c += 64) {
-    const float n = (x[c] - mean) * rstd;
-    nhat[row * d + c] = n;
-    const float gm = gamma ? gamma[c] : 1.0f, bt = beta ? beta[c] : 0.0f;
-    g[row * d + c] = (n * gm + bt) * u[row * d + c];
+#pragma unroll
+  for (int i = 0; i < kRow4; ++i) {
+    const int c4 = lane + 64 * i;
+    if (c4 >= n4) continue;
+    const float4 gm = ld4_or(gamma, c4, 1.0f), bt = ld4_or(beta, c4, 0.0f);
+    const float4 uv = *reinterpret_cast<const float4*>(u + row * d + 4 * c4);
+    const float4 n = make_float4((xv[i].x - mean) * rstd, (xv[i].y - mean) * rstd, (xv[i].z - mean) * rstd,
+                                 (xv[i].w - mean) * rstd);
+    *reinterpret_cast<float4*>(nhat + row * d + 4 * c4) = n;
+    *reinterpret_cast<float4*>(g + row * d + 4 * c4) =
+        make_float4((n.x * gm.x + bt.x) * uv.x, (n.y * gm.y + bt.y) * uv.y, (n.z * gm.z + bt.z) * uv.z,
+                    (n.w * gm.w + bt.w) * uv.w);
   }
   if (lane == 0) rstd_out[row] = rstd;
 }
 
 // Per row (one wave), from dG: dU (into dz's U block), dAV, and this
 // block's partial column sums of dN . N^ (dgamma) and dN (dbeta), dN = dG . U.
+// d % 4 == 0, ldu % 4 == 0.
 __global__ __launch_bounds__(256) void ln_gate_bwd_kernel(const float* __restrict__ dg,
                                                           const float* __restrict__ u,
                                                           const float* __restrict__ nhat,
@@ -154,36 +182,58 @@ __global__ __launch_bounds__(256) void ln_gate_bwd_kernel(const float* __restric
                                                           float* du, int64_t ldu, float* dav,
                                                           float* dgamma, float* dbeta, int64_t M,
                                                           int d) {
-  __shared__ float sg[4][1024];
-  __shared__ float sb[4][1024];
+  __shared__ __attribute__((aligned(16))) float sg[4][1024];
+  __shared__ __attribute__((aligned(16))) float sb[4][1024];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int c = lane; c < d; c += 64) {
-    sg[wave][c] = 0.0f;
-    sb[wave][c] = 0.0f;
-  }
+  const int n4 = d >> 2;
+  float4 gsum[kRow4], bsum[kRow4];
+#pragma unroll
+  for (int i = 0; i < kRow4; ++i) gsum[i] = bsum[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int64_t row = static_cast<int64_t>(blockIdx.x) * 16 + wave; row < M &&
        row < static_cast<int64_t>(blockIdx.x) * 16 + 16; row += 4) {
+    float4 dnh[kRow4], nh[kRow4];
     float s1 = 0.0f, s2 = 0.0f;
-    for (int c = lane; c < d; c += 64) {
-      const int64_t i = row * d + c;
-      const float gm = gamma ? gamma[c] : 1.0f, bt = beta ? beta[c] : 0.0f;
-      const float nh = nhat[i];
-      du[row * ldu + c] = dg[i] * (nh * gm + bt);
-      const float dn = dg[i] * u[i];
-      sg[wave][c] += dn * nh;
-      sb[wave][c] += dn;
-      const float dnh = dn * gm;
-      s1 += dnh;
-      s2 += dnh * nh;
+#pragma unroll
+    for (int i = 0; i < kRow4; ++i) {
+      const int c4 = lane + 64 * i;
+      if (c4 >= n4) {
+        dnh[i] = nh[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        continue;
+      }
+      const int64_t o = row * d + 4 * c4;
+      const float4 gm = ld4_or(gamma, c4, 1.0f), bt = ld4_or(beta, c4, 0.0f);
+      const float4 g4 = *reinterpret_cast<const float4*>(dg + o);
+      const float4 u4 = *reinterpret_cast<const float4*>(u + o);
+      nh[i] = *reinterpret_cast<const float4*>(nhat + o);
+      *reinterpret_cast<float4*>(du + row * ldu + 4 * c4) =
+          make_float4(g4.x * (nh[i].x * gm.x + bt.x), g4.y * (nh[i].y * gm.y + bt.y),
+                      g4.z * (nh[i].z * gm.z + bt.z), g4.w * (nh[i].w * gm.w + bt.w));
+      const float4 dn = make_float4(g4.x * u4.x, g4.y * u4.y, g4.z * u4.z, g4.w * u4.w);
+      gsum[i].x += dn.x * nh[i].x; gsum[i].y += dn.y * nh[i].y;
+      gsum[i].z += dn.z * nh[i].z; gsum[i].w += dn.w * nh[i].w;
+      bsum[i].x += dn.x; bsum[i].y += dn.y; bsum[i].z += dn.z; bsum[i].w += dn.w;
+      dnh[i] = make_float4(dn.x * gm.x, dn.y * gm.y, dn.z * gm.z, dn.w * gm.w);
+      s1 += (dnh[i].x + dnh[i].y) + (dnh[i].z + dnh[i].w);
+      s2 += (dnh[i].x * nh[i].x + dnh[i].y * nh[i].y) + (dnh[i].z * nh[i].z + dnh[i].w * nh[i].w);
     }
     const float m1 = wave_sum(s1) / static_cast<float>(d);
     const float m2 = wave_sum(s2) / static_cast<float>(d);
     const float r = rstd[row];
-    for (int c = lane; c < d; c += 64) {
-      const int64_t i = row * d + c;
-      const float gm = gamma ? gamma[c] : 1.0f;
-      const float dnh = dg[i] * u[i] * gm;
-      dav[i] = r * (dnh - m1 - nhat[i] * m2);
+#pragma unroll
+    for (int i = 0; i < kRow4; ++i) {
+      const int c4 = lane + 64 * i;
+      if (c4 >= n4) continue;
+      *reinterpret_cast<float4*>(dav + row * d + 4 * c4) =
+          make_float4(r * (dnh[i].x - m1 - nh[i].x * m2), r * (dnh[i].y - m1 - nh[i].y * m2),
+                      r * (dnh[i].z - m1 - nh[i].z * m2), r * (dnh[i].w - m1 - nh[i].w * m2));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kRow4; ++i) {
+    const int c4 = lane + 64 * i;
+    if (c4 < n4) {
+      *reinterpret_cast<float4*>(&sg[wave][4 * c4]) = gsum[i];
+      *reinterpret_cast<float4*>(&sb[wave][4 * c4]) = bsum[i];
     }
   }
   __syncthreads();
@@ -380,6 +430,10 @@ hipError_t launch_ln_gate_fwd(const float* av, const float* u, const float* gamm
                               float* nhat, float* rstd, float* g, int64_t M, int d, float eps,
                               hipStream_t s) {
   if (M == 0) return hipSuccess;
+  const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  if (d % 4 != 0 || d > 64 * 4 * kRow4 || !a16(av) || !a16(u) || !a16(nhat) || !a16(g) || !a16(gamma) ||
+      !a16(beta))
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(ln_gate_fwd_kernel, dim3(static_cast<unsigned>((M + 3) / 4)), dim3(256), 0, s, av, u,
                      gamma, beta, nhat, rstd, g, M, d, eps);
   return hipGetLastError();
@@ -389,6 +443,10 @@ hipError_t launch_ln_gate_bwd(const float* dg, const float* u, const float* nhat
                               const float* gamma, const float* beta, float* du, int64_t ldu, float* dav,
                               float* dgamma, float* dbeta, int64_t M, int d, hipStream_t s) {
   if (M == 0) return hipSuccess;
+  const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  if (d % 4 != 0 || d > 64 * 4 * kRow4 || ldu % 4 != 0 || !a16(dg) || !a16(u) || !a16(nhat) || !a16(du) ||
+      !a16(dav) || !a16(gamma) || !a16(beta))
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(ln_gate_bwd_kernel, dim3(static_cast<unsigned>((M + 15) / 16)), dim3(256), 0, s, dg,
                      u, nhat, rstd, gamma, beta, du, ldu, dav, dgamma, dbeta, M, d);
   return hipGetLastError();
