@@ -546,9 +546,13 @@ def run_backward(args):
     rec["algorithmic_flop"] = flop
     rec["executed_flop"] = flop_exec
     rec["executed_tflops"] = flop_exec / (ms * 1e-3) / 1e12
+    # the matrix work runs on the fp32 matrix cores, or with both bf16 flags on
+    # the bf16 ones (f1 on hi/lo splits included); with one flag it is mixed
+    # and is priced against the bf16 peak, the higher of the two
+    peak = PEAK_BF16_TFLOPS if (args.attn_bwd_bf16 or args.gemm_bwd_bf16) else PEAK_F32_TFLOPS
     rec["roofline"] = {"kernel": "layer backward (all kernels)", "bound": "mfma",
-                       "achieved": flop / (ms * 1e-3) / 1e12, "peak": PEAK_F32_TFLOPS,
-                       "unit": "TFLOP/s", "frac": flop / (ms * 1e-3) / 1e12 / PEAK_F32_TFLOPS,
+                       "achieved": flop / (ms * 1e-3) / 1e12, "peak": peak,
+                       "unit": "TFLOP/s", "frac": flop / (ms * 1e-3) / 1e12 / peak,
                        "traffic": None}
     return rec
 
