@@ -56,6 +56,30 @@ __device__ __forceinline__ float sigmoid_t(float s) {
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// Time bucket in 32-bit arithmetic. A time t is kept as its offset from a
+// reference time, biased by 2^31 (mod 2^64). When every time a block uses
+// gives an offset below 2^32 - 1, the difference of two offsets is the
+// wrapped 64-bit difference of their times, and its magnitude plus one fits
+// in 32 bits, so time_bucket32 returns what time_bucket64 returns for that
+// difference. The test is made per block for the whole wave.
+__device__ __forceinline__ uint64_t time_off(int64_t t, int64_t tref) {
+  return static_cast<uint64_t>(t) - static_cast<uint64_t>(tref) + (uint64_t{1} << 31);
+}
+__device__ __forceinline__ bool time_fits32(uint64_t off) { return off < 0xffffffffull; }
+// The bf16 kernels look the time table up by a key, 31 - floor(log2(|dt| + 1))
+// in -32 .. 31, from which the bucket is min(31 - key, nb - 1): LDS tables
+// indexed by key + 32 hold the clamp, so the 32-bit path costs an absolute
+// difference and a leading-zero count per pair.
+__device__ __forceinline__ int time_key32(uint32_t x, uint32_t y) {
+  const uint32_t m = (x > y ? x - y : y - x) + 1u;   // |dt| + 1 <= 2^32 - 1
+  return __builtin_clz(m);
+}
+__device__ __forceinline__ int time_key64(int64_t dt) {
+  uint64_t m = dt < 0 ? (0ull - static_cast<uint64_t>(dt)) : static_cast<uint64_t>(dt);
+  m += 1ull;
+  return __clzll(static_cast<long long>(m)) - 32;
+}
+
 __device__ __forceinline__ float comp(const float4& v, int e) {
   return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
 }
@@ -520,9 +544,10 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
   constexpr int NC = DH / 32, NCT = DH / 16;
   constexpr int DSR = 36;   // row stride of a parked dS block (16-byte rows, spread over the banks)
   __shared__ float s_gpos[kPosCapB];
-  __shared__ float s_tval[64], s_tgrad[64];
+  __shared__ float s_tvk[64], s_tgk[64];   // by time key + 32
   __shared__ float s_win[kMaxWaves][64];
   __shared__ int64_t s_ts[kMaxWaves][32];
+  __shared__ uint32_t s_ts32[kMaxWaves][32];
   __shared__ __attribute__((aligned(16))) float s_ds[kMaxWaves][32 * DSR];
   __shared__ __attribute__((aligned(16))) uint16_t s_k[kMaxWaves][32 * (DH + 8)];
   const int nw = blockDim.x >> 6;
@@ -536,8 +561,8 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
   const int64_t* Ts = a.ts + s0;
   for (int e = tid; e < range; e += blockDim.x) s_gpos[e] = 0.0f;
   if (tid < 64) {
-    s_tgrad[tid] = 0.0f;
-    s_tval[tid] = tid < a.nb ? a.time_bias[tid] : 0.0f;
+    s_tgk[tid] = 0.0f;
+    s_tvk[tid] = a.time_bias[min(63 - tid, a.nb - 1)];
   }
   __syncthreads();
 
@@ -548,7 +573,11 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
   uint16_t* kblk = s_k[wave];
   bf16x8 qf[2][NC], df[2][NC];
   int64_t tq[2];
+  uint32_t tq32[2];
   bool qv[2];
+  // times as 32-bit offsets from the block's first query time where they fit
+  const int64_t tref = Ts[q0];
+  bool fq = true;
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     const int qrow = min(q0 + 16 * qt + lc, L - 1);
@@ -556,16 +585,24 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
     load_row16<NC>(a.q16 + base + qrow * d, g, qf[qt]);
     load_row16<NC>(a.dav16 + base + qrow * d, g, df[qt]);
     tq[qt] = Ts[qrow];
+    const uint64_t off = time_off(tq[qt], tref);
+    fq = fq && time_fits32(off);
+    tq32[qt] = static_cast<uint32_t>(off);
   }
+  const bool fast_q = __builtin_amdgcn_ballot_w64(!fq) == 0;
   float* win = s_win[wave];
   int64_t* kts = s_ts[wave];
+  uint32_t* kts32 = s_ts32[wave];
   f32x4 acc[NCT][2];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) acc[ct][0] = acc[ct][1] = f32x4{};
   // time-bucket gradients: per lane and query tile the keys ascend, so runs
-  // of one bucket are summed in registers and added to LDS when the bucket
-  // changes (starting from bucket 0 with nothing summed)
-  int tb_cur[2] = {0, 0};
+  // of one time key are summed in registers and added to LDS when the key
+  // changes (starting from key 31, bucket 0, with nothing summed); the
+  // entries go to their buckets at the end
+  const float* tvk = s_tvk + 32;
+  float* tgk = s_tgk + 32;
+  int tb_cur[2] = {31, 31};   // time keys
   float tg_cur[2] = {0.0f, 0.0f};
   float wv = a.pos_bias[clampi(a.pos_center + q0 - 31 + lane, 0, a.pos_len - 1)];
   int64_t tsv = Ts[min(lane & 31, L - 1)];
@@ -581,7 +618,12 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
   for (int kb = 0; kb <= pl.blk; ++kb) {
     const int j0 = kb * 32, D = q0 - j0;
     win[lane] = wv;
-    if (lane < 32) kts[lane] = tsv;
+    const uint64_t koff = time_off(tsv, tref);
+    const bool fast = fast_q && __builtin_amdgcn_ballot_w64(!time_fits32(koff)) == 0;
+    if (lane < 32) {
+      kts[lane] = tsv;
+      kts32[lane] = static_cast<uint32_t>(koff);
+    }
     wv = a.pos_bias[clampi(a.pos_center + D - 63 + lane, 0, a.pos_len - 1)];
     tsv = Ts[min(j0 + 32 + (lane & 31), L - 1)];
     bf16x8 kf[2][NC], vf[2][NC];
@@ -621,11 +663,25 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
     // visibility test, each pair's lookups were waited for on their own
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      int64_t tk[4];
       float wq[4][2], tvq[4][2];
       int tbq[4][2];
+      if (fast) {
+        uint32_t tk[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) tk[r] = kts[16 * kt + 4 * g + r];
+        for (int r = 0; r < 4; ++r) tk[r] = kts32[16 * kt + 4 * g + r];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) tbq[r][qt] = time_key32(tq32[qt], tk[r]);
+      } else {
+        int64_t tk[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tk[r] = kts[16 * kt + 4 * g + r];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) tbq[r][qt] = time_key64(tq[qt] - tk[r]);
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -633,11 +689,7 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) tbq[r][qt] = time_bucket64(tq[qt] - tk[r], a.nb);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) tvq[r][qt] = s_tval[tbq[r][qt]];
+        for (int qt = 0; qt < 2; ++qt) tvq[r][qt] = tvk[tbq[r][qt]];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int jr = 16 * kt + 4 * g + r;   // key row in the block
@@ -648,11 +700,11 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
           const int tb = tbq[r][qt];
           const float sc = a.alpha * sacc[kt][qt][r] + wq[r][qt] + tvq[r][qt];
           const float sg = sigmoid_t(sc);
-          const float dsv = pacc[kt][qt][r] * sg * (1.0f + sc * (1.0f - sg));
+          const float dsv = pacc[kt][qt][r] * __builtin_fmaf(sc, __builtin_fmaf(-sg, sg, sg), sg);
           const float ds = vis ? dsv : 0.0f;
           sacc[kt][qt][r] = ds;
           const bool flush = vis && tb != tb_cur[qt];
-          if (flush) atomicAdd(&s_tgrad[tb_cur[qt]], tg_cur[qt]);
+          if (flush) atomicAdd(&tgk[tb_cur[qt]], tg_cur[qt]);
           tg_cur[qt] = (flush ? 0.0f : tg_cur[qt]) + ds;
           tb_cur[qt] = flush ? tb : tb_cur[qt];
         }
@@ -682,6 +734,8 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
     // read back without a barrier.
     // The reads go out eight at a time into distinct registers: left to
     // itself the compiler reuses one register and waits for each read.
+    // (Adding each pair's dS to the accumulator with an LDS atomic instead,
+    // sixteen per lane and step, ran 3.4 times slower.)
     float pos_sum = 0.0f;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -708,24 +762,24 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
   }
 
   store_tiles16<NCT>(a.dq + (s0 + q0) * a.ld_dz + pl.h * DH, a.ld_dz, acc, lc, g, a.alpha, qv[0], qv[1]);
-  atomicAdd(&s_tgrad[tb_cur[0]], tg_cur[0]);
-  atomicAdd(&s_tgrad[tb_cur[1]], tg_cur[1]);
+  atomicAdd(&tgk[tb_cur[0]], tg_cur[0]);
+  atomicAdd(&tgk[tb_cur[1]], tg_cur[1]);
   __syncthreads();
   for (int e = tid; e < range; e += blockDim.x) {
     const float gsum = s_gpos[e];
     if (gsum != 0.0f) atomicAdd(&a.dpos[clampi(a.pos_center + e - 31, 0, a.pos_len - 1)], gsum);
   }
-  if (tid < a.nb && s_tgrad[tid] != 0.0f) atomicAdd(&a.dtime[tid], s_tgrad[tid]);
+  if (tid < 64 && s_tgk[tid] != 0.0f) atomicAdd(&a.dtime[min(63 - tid, a.nb - 1)], s_tgk[tid]);
 }
 
 // dK and dV for the 32 key rows of one block and one head per wave.
 template <int DH>
 __global__ __launch_bounds__(512) void attn_train_kv_bf16_kernel(BwdAttnArgs a) {
   constexpr int NC = DH / 32, NCT = DH / 16;
-  __shared__ float s_tval[64];
+  __shared__ float s_tvk[64];   // by time key + 32
   __shared__ float s_win[kMaxWaves][64];
   __shared__ int64_t s_ts[kMaxWaves][32];
-  __shared__ int64_t s_kts[kMaxWaves][32];
+  __shared__ uint32_t s_ts32[kMaxWaves][32];
   __shared__ __attribute__((aligned(16))) uint16_t s_q[kMaxWaves][32 * (DH + 8)];
   __shared__ __attribute__((aligned(16))) uint16_t s_d[kMaxWaves][32 * (DH + 8)];
   const int nw = blockDim.x >> 6;
@@ -735,7 +789,8 @@ __global__ __launch_bounds__(512) void attn_train_kv_bf16_kernel(BwdAttnArgs a) 
   const int L = static_cast<int>(a.offsets[pl.seq + 1] - s0);
   const int j0 = pl.blk * 32;
   if (j0 >= L) return;
-  if (tid < 64) s_tval[tid] = tid < a.nb ? a.time_bias[tid] : 0.0f;
+  if (tid < 64) s_tvk[tid] = a.time_bias[min(63 - tid, a.nb - 1)];
+  const float* tvk = s_tvk + 32;
   __syncthreads();
 
   const int d = a.d_model;
@@ -754,9 +809,22 @@ __global__ __launch_bounds__(512) void attn_train_kv_bf16_kernel(BwdAttnArgs a) 
     load_row16<NC>(a.k16 + base + krow * d, g, kf[kt]);
     load_row16<NC>(a.v16 + base + krow * d, g, vf[kt]);
   }
-  if (lane < 32) s_kts[wave][lane] = Ts[min(j0 + lane, L - 1)];
   float* win = s_win[wave];
   int64_t* qts = s_ts[wave];
+  uint32_t* qts32 = s_ts32[wave];
+  // times as 32-bit offsets from the block's first key time where they fit
+  const int64_t tref = Ts[j0];
+  int64_t tk[2];
+  uint32_t tk32[2];
+  bool fk = true;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    tk[kt] = Ts[min(j0 + 16 * kt + lc, L - 1)];
+    const uint64_t off = time_off(tk[kt], tref);
+    fk = fk && time_fits32(off);
+    tk32[kt] = static_cast<uint32_t>(off);
+  }
+  const bool fast_k = __builtin_amdgcn_ballot_w64(!fk) == 0;
   f32x4 dk[NCT][2], dv[NCT][2];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) dk[ct][0] = dk[ct][1] = dv[ct][0] = dv[ct][1] = f32x4{};
@@ -775,7 +843,12 @@ __global__ __launch_bounds__(512) void attn_train_kv_bf16_kernel(BwdAttnArgs a) 
   for (int qb = pl.blk; qb < nblk; ++qb) {
     const int q0 = qb * 32, D = q0 - j0;
     win[lane] = wv;
-    if (lane < 32) qts[lane] = tsv;
+    const uint64_t qoff = time_off(tsv, tref);
+    const bool fast = fast_k && __builtin_amdgcn_ballot_w64(!time_fits32(qoff)) == 0;
+    if (lane < 32) {
+      qts[lane] = tsv;
+      qts32[lane] = static_cast<uint32_t>(qoff);
+    }
     wv = a.pos_bias[clampi(a.pos_center + D + 1 + lane, 0, a.pos_len - 1)];
     tsv = Ts[min(q0 + 32 + (lane & 31), L - 1)];
     bf16x8 qf[2][NC], df[2][NC];
@@ -810,20 +883,39 @@ __global__ __launch_bounds__(512) void attn_train_kv_bf16_kernel(BwdAttnArgs a) 
     // this block's queries and dAV rows, for the transposed reads
     stash_block<DH>(qblk, qf, lc, g);
     stash_block<DH>(dblk, df, lc, g);
-    const int64_t tk[2] = {s_kts[wave][lc], s_kts[wave][16 + lc]};
+    // time buckets of the block's pairs, in 32 bits where the times allow
+    int tbq[2][4][2];
+    if (fast) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t tqr = qts32[16 * qt + 4 * g + r];
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) tbq[qt][r][kt] = time_key32(tqr, tk32[kt]);
+        }
+    } else {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t tqr = qts[16 * qt + 4 * g + r];
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) tbq[qt][r][kt] = time_key64(tqr - tk[kt]);
+        }
+    }
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int ir = 16 * qt + 4 * g + r;   // query row in the block
-        const int64_t tqr = qts[ir];
         const bool qok = q0 + ir < L;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
           const int jr = 16 * kt + lc;        // key row in the block
           const bool vis = kv[kt] && qok && (j0 + jr <= q0 + ir);
-          const int tb = time_bucket64(tqr - tk[kt], a.nb);
-          const float sc = a.alpha * sacc[qt][kt][r] + win[ir - jr + 31] + s_tval[tb];
+          const int tb = tbq[qt][r][kt];
+          const float sc = a.alpha * sacc[qt][kt][r] + win[ir - jr + 31] + tvk[tb];
           const float sg = sigmoid_t(sc);
           sacc[qt][kt][r] = vis ? sc * sg : 0.0f;
           pacc[qt][kt][r] = vis ? pacc[qt][kt][r] * sg * (1.0f + sc * (1.0f - sg)) : 0.0f;

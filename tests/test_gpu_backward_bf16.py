@@ -102,13 +102,14 @@ def _backward(w, dy, two_calls=False, attn=True, gemm=False):
     ([65, 1, 31], 1024, 16, 0.5, None),            # 16 heads
     ([90, 140], 128, 2, 1.0, "shuffled"),          # timestamps out of order
     ([120, 64, 9], 128, 2, 1.0, "wide"),           # clocks spanning far more than 2^31 units
+    ([150, 70], 128, 2, 1.0, "b32-high"),          # spans just under 2^31: buckets to 30 in 32 bits
 ])
 def test_bf16_attention_backward_matches_oracle(gpu_lib, lengths, d, H, alpha, ts_kind):
     w = gen.make_custom(lengths, d, H, dtype="f32", seed=81, affine="random")
     w.alpha = alpha
-    if ts_kind == "wide":
+    if ts_kind in ("wide", "b32-high"):
         from tests.test_gpu_time_buckets import _timestamps
-        w.timestamps = _timestamps("wide", lengths, np.random.default_rng(84))
+        w.timestamps = _timestamps(ts_kind, lengths, np.random.default_rng(84))
         w.layers[0].time_bias = np.random.default_rng(85).standard_normal(32).astype(np.float32)
     elif ts_kind == "shuffled":
         rng = np.random.default_rng(83)
