@@ -76,7 +76,8 @@ int check_desc(const hstu_layer_desc* d) {
   CHECK(d->d_model == d->num_heads * d->head_dim, HSTU_E_INVAL,
         "d_model (%d) != num_heads (%d) * head_dim (%d)", d->d_model, d->num_heads, d->head_dim);
   if (d->dtype == HSTU_BF16) {
-    CHECK(d->head_dim == 64, HSTU_E_UNSUPPORTED, "bf16 supports head_dim 64 (got %d)", d->head_dim);
+    CHECK(d->head_dim == 32 || d->head_dim == 64, HSTU_E_UNSUPPORTED,
+          "bf16 supports head_dim 32 or 64 (got %d)", d->head_dim);
     CHECK(d->d_model <= 1024, HSTU_E_UNSUPPORTED, "d_model %d > 1024", d->d_model);
   } else {
     CHECK(d->head_dim == 32 || d->head_dim == 64, HSTU_E_UNSUPPORTED,
@@ -150,6 +151,11 @@ int check_jagged(const hstu_layer_desc* d, const hstu_jagged* j, const hstu_kv_c
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// The tiled bf16 attention kernel (work list, key-range splits, the fused
+// norm_gate epilogue) takes head_dim 64; bf16 with head_dim 32 runs on the
+// row-structured matrix-core kernel (plain causal) or the per-row kernel.
+bool tiled_bf16(const hstu_layer_desc* d) { return d->dtype == HSTU_BF16 && d->head_dim == 64; }
+
 hstu::AttnArgs make_attn_args(const hstu_layer_desc* d, const hstu_jagged* j,
                               const hstu_kv_cache* c, const void* q, const void* k,
                               const void* v, const float* pb, const float* tb, float* av,
@@ -157,7 +163,8 @@ hstu::AttnArgs make_attn_args(const hstu_layer_desc* d, const hstu_jagged* j,
   hstu::AttnArgs a{};
   a.sched = static_cast<int*>(ws);
   a.total_tokens = j->total_tokens;
-  if (d->dtype == HSTU_BF16) {
+  a.in_bf16 = d->dtype == HSTU_BF16 && !tiled_bf16(d);
+  if (tiled_bf16(d)) {
     const hstu::AttnPlan plan = hstu::attn_plan(j->num_seqs, j->max_seq_len, d->num_heads, j->total_tokens,
                                                 d->d_model, max_splits);
     a.bm = plan.bm;
@@ -242,8 +249,18 @@ int do_attn(const hstu_layer_desc* d, const hstu_jagged* j, const hstu_kv_cache*
     ta.av = av;
     return device_status(hstu::launch_attn_train_fwd(ta, s), "attention launch");
   }
+  if (d->dtype == HSTU_BF16 && !tiled_bf16(d) && c == nullptr && j->num_targets == nullptr && !typed(d) &&
+      !linear_bias(d) && static_cast<int64_t>(j->max_seq_len) * d->d_model < (int64_t{1} << 31)) {
+    // plain causal bf16 with head_dim 32: the row-structured matrix-core kernel
+    hstu::BwdAttnArgs ta = make_train_args(d, j, nullptr, nullptr, nullptr, pb, tb);
+    ta.q16 = static_cast<const uint16_t*>(q);
+    ta.k16 = static_cast<const uint16_t*>(k);
+    ta.v16 = static_cast<const uint16_t*>(v);
+    ta.av = av;
+    return device_status(hstu::launch_attn_fwd_bf16_rows(ta, s), "attention launch");
+  }
   const hstu::AttnArgs a = make_attn_args(d, j, c, q, k, v, pb, tb, av, ws, max_splits);
-  return device_status(d->dtype == HSTU_BF16 ? hstu::launch_attn_bf16(a, s) : hstu::launch_attn_f32(a, s),
+  return device_status(tiled_bf16(d) ? hstu::launch_attn_bf16(a, s) : hstu::launch_attn_f32(a, s),
                        "attention launch");
 }
 
@@ -273,7 +290,7 @@ int do_out(const hstu_layer_desc* d, int64_t T, const void* g, const void* x, co
 size_t round256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
 size_t attn_ws(const hstu_layer_desc* d, const hstu_jagged* j) {
-  if (d->dtype != HSTU_BF16 || j->num_seqs <= 0 || j->max_seq_len <= 0) return 0;
+  if (!tiled_bf16(d) || j->num_seqs <= 0 || j->max_seq_len <= 0) return 0;
   return round256(
       hstu::attn_plan(j->num_seqs, j->max_seq_len, d->num_heads, j->total_tokens, d->d_model).workspace_bytes);
 }
@@ -354,7 +371,7 @@ int hstu_attn_fwd_noalloc(const hstu_layer_desc* desc, const hstu_jagged* jagged
         "q/k/v/av must be 16-byte aligned");
   void* ws = nullptr;
   int max_splits = 8;
-  if (desc->dtype == HSTU_BF16) {
+  if (tiled_bf16(desc)) {
     // the most key-range splits whose work list and partial outputs fit the
     // static scratch (fewer splits only change the order of the fp32 sums)
     const size_t cap = hstu::kAttnStaticScratchBytes;
@@ -532,7 +549,7 @@ int hstu_layer_fwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
   }
   st = do_proj(desc, params, T, xin, u, v, q, k, s);
   if (st) return st;
-  if (desc->dtype == HSTU_BF16 &&
+  if (tiled_bf16(desc) &&
       hstu::attn_can_fuse_norm_gate(jagged->num_seqs, jagged->max_seq_len, desc->num_heads, jagged->total_tokens,
                                     desc->d_model)) {
     // one head group covers each row: the attention kernel finishes the rows

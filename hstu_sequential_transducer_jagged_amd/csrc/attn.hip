@@ -1010,11 +1010,22 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
   }   // work items
 }
 
+// Input element as fp32: fp32 as is, bf16 (raw 16-bit pattern) widened.
+template <bool BF16>
+__device__ __forceinline__ float ld_in(const void* p, int64_t i) {
+  if constexpr (BF16)
+    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
+  else
+    return static_cast<const float*>(p)[i];
+}
+
 // fp32 kernel: one thread per query row, plain FMA loops, exact expf and IEEE
-// division. It serves the fp32 dtype (small workloads). Keys arrive in
-// chunks of 64 staged in LDS by the whole workgroup, so a thread's loop over
-// keys does not wait on global memory at every key.
-template <int DH>
+// division. It serves the fp32 dtype (small workloads) and, reading bf16
+// inputs (BF16), the bf16 cases no matrix-core kernel takes: head_dim 32
+// with targets, a cache, token types or the parameter-free bias. Keys arrive
+// in chunks of 64 staged in LDS by the whole workgroup, so a thread's loop
+// over keys does not wait on global memory at every key.
+template <int DH, bool BF16>
 __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   __shared__ float sk[64][DH];
   __shared__ float sv[64][DH];
@@ -1028,16 +1039,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   if (qt * 64 >= si.L) return;
   const bool qvalid = qi < si.L;
   const int d = a.d_model;
-  const float* Q = static_cast<const float*>(a.q);
-  const float* K = static_cast<const float*>(a.k);
-  const float* V = static_cast<const float*>(a.v);
-  const float* CK = static_cast<const float*>(a.ck);
-  const float* CV = static_cast<const float*>(a.cv);
   const int first_tgt = si.L - si.m;
   float qv[DH], acc[DH];
 #pragma unroll
   for (int c = 0; c < DH; ++c) {
-    qv[c] = qvalid ? Q[(si.s + qi) * d + h * DH + c] : 0.0f;
+    qv[c] = qvalid ? ld_in<BF16>(a.q, (si.s + qi) * d + h * DH + c) : 0.0f;
     acc[c] = 0.0f;
   }
   const int pq = si.nc + (qi < first_tgt ? qi : first_tgt);
@@ -1056,8 +1062,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
       if (kk < nkeys) {
         const bool cache = kk < si.nc;
         const int64_t row = cache ? (si.cs + kk) : (si.s + kk - si.nc);
-        kv = (cache ? CK : K)[row * d + h * DH + cc];
-        vv = (cache ? CV : V)[row * d + h * DH + cc];
+        kv = ld_in<BF16>(cache ? a.ck : a.k, row * d + h * DH + cc);
+        vv = ld_in<BF16>(cache ? a.cv : a.v, row * d + h * DH + cc);
       }
       sk[r][cc] = kv;
       sv[r][cc] = vv;
@@ -1206,10 +1212,13 @@ hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s) {
   const int n_qt = (a.max_seq_len + 63) / 64;
   if (a.num_seqs == 0 || n_qt == 0) return hipSuccess;
   dim3 grid(a.num_seqs, n_qt, a.num_heads);
-  if (a.head_dim == 32)
-    hipLaunchKernelGGL(attn_f32_kernel<32>, grid, dim3(64), 0, s, a);
+  if (a.in_bf16 && a.head_dim != 32) return hipErrorInvalidValue;
+  if (a.in_bf16)
+    hipLaunchKernelGGL((attn_f32_kernel<32, true>), grid, dim3(64), 0, s, a);
+  else if (a.head_dim == 32)
+    hipLaunchKernelGGL((attn_f32_kernel<32, false>), grid, dim3(64), 0, s, a);
   else
-    hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, s, a);
+    hipLaunchKernelGGL((attn_f32_kernel<64, false>), grid, dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

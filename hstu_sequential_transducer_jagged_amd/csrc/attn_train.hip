@@ -943,6 +943,165 @@ __global__ __launch_bounds__(512) void attn_train_kv_bf16_kernel(BwdAttnArgs a) 
   store_tiles16<NCT>(a.dv + (s0 + j0) * a.ld_dz + pl.h * DH, a.ld_dz, dv, lc, g, 1.0f, kv[0], kv[1]);
 }
 
+// AV for the 32 query rows of one block and one head per wave, from bf16
+// Q, K and V on the bf16 matrix cores (plain causal attention, the layer's
+// forward where no other bf16 kernel serves the head dimension): per 32-key
+// block S^T = K Q^T, P = SiLU(S) masked, AV^T += V^T P^T. The bias, the
+// 32-bit time keys and the operand layouts are those of the dQ kernel above,
+// with V stashed for the transposed reads in place of K.
+template <int DH>
+__global__ __launch_bounds__(512) void attn_fwd_bf16_rows_kernel(BwdAttnArgs a) {
+  constexpr int NC = DH / 32, NCT = DH / 16;
+  __shared__ float s_tvk[64];   // by time key + 32
+  __shared__ float s_win[kMaxWaves][64];
+  __shared__ int64_t s_ts[kMaxWaves][32];
+  __shared__ uint32_t s_ts32[kMaxWaves][32];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[kMaxWaves][32 * (DH + 8)];
+  const int nw = blockDim.x >> 6;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lc = lane & 15, g = lane >> 4;
+  const Place pl = place(a, true, wave, nw);
+  const int64_t s0 = a.offsets[pl.seq];
+  const int L = static_cast<int>(a.offsets[pl.seq + 1] - s0);
+  const int q0 = pl.blk * 32;
+  if (q0 >= L) return;   // the whole workgroup: same sequence and block
+  if (tid < 64) s_tvk[tid] = a.time_bias[min(63 - tid, a.nb - 1)];
+  __syncthreads();
+
+  const int d = a.d_model;
+  const int64_t base = s0 * d + pl.h * DH;
+  const uint16_t* Ks = a.k16 + base;
+  const uint16_t* Vs = a.v16 + base;
+  const int64_t* Ts = a.ts + s0;
+  uint16_t* vblk = s_v[wave];
+  bf16x8 qf[2][NC];
+  int64_t tq[2];
+  uint32_t tq32[2];
+  bool qv[2];
+  const int64_t tref = Ts[q0];
+  bool fq = true;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int qrow = min(q0 + 16 * qt + lc, L - 1);
+    qv[qt] = q0 + 16 * qt + lc < L;
+    load_row16<NC>(a.q16 + base + qrow * d, g, qf[qt]);
+    tq[qt] = Ts[qrow];
+    const uint64_t off = time_off(tq[qt], tref);
+    fq = fq && time_fits32(off);
+    tq32[qt] = static_cast<uint32_t>(off);
+  }
+  const bool fast_q = __builtin_amdgcn_ballot_w64(!fq) == 0;
+  float* win = s_win[wave];
+  int64_t* kts = s_ts[wave];
+  uint32_t* kts32 = s_ts32[wave];
+  const float* tvk = s_tvk + 32;
+  f32x4 acc[NCT][2];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) acc[ct][0] = acc[ct][1] = f32x4{};
+  float wv = a.pos_bias[clampi(a.pos_center + q0 - 31 + lane, 0, a.pos_len - 1)];
+  int64_t tsv = Ts[min(lane & 31, L - 1)];
+  bf16x8 kn[2][NC], vn[2][NC];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int krow = min(16 * kt + lc, L - 1);
+    load_row16<NC>(Ks + krow * d, g, kn[kt]);
+    load_row16<NC>(Vs + krow * d, g, vn[kt]);
+  }
+
+  for (int kb = 0; kb <= pl.blk; ++kb) {
+    const int j0 = kb * 32, D = q0 - j0;
+    win[lane] = wv;
+    const uint64_t koff = time_off(tsv, tref);
+    const bool fast = fast_q && __builtin_amdgcn_ballot_w64(!time_fits32(koff)) == 0;
+    if (lane < 32) {
+      kts[lane] = tsv;
+      kts32[lane] = static_cast<uint32_t>(koff);
+    }
+    wv = a.pos_bias[clampi(a.pos_center + D - 63 + lane, 0, a.pos_len - 1)];
+    tsv = Ts[min(j0 + 32 + (lane & 31), L - 1)];
+    bf16x8 kf[2][NC], vf[2][NC];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        kf[kt][c] = kn[kt][c];
+        vf[kt][c] = vn[kt][c];
+      }
+    if (kb < pl.blk) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int krow = min(j0 + 32 + 16 * kt + lc, L - 1);
+        load_row16<NC>(Ks + krow * d, g, kn[kt]);
+        load_row16<NC>(Vs + krow * d, g, vn[kt]);
+      }
+    }
+    // S^T = K Q^T (rows: keys, columns: queries)
+    f32x4 sacc[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        sacc[kt][qt] = f32x4{};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) sacc[kt][qt] = mfma_16x16x32(kf[kt][c], qf[qt][c], sacc[kt][qt]);
+      }
+    // this block's values, for the transposed reads of the second product
+    stash_block<DH>(vblk, vf, lc, g);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      float wq[4][2], tvq[4][2];
+      int tbq[4][2];
+      if (fast) {
+        uint32_t tk[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tk[r] = kts32[16 * kt + 4 * g + r];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) tbq[r][qt] = time_key32(tq32[qt], tk[r]);
+      } else {
+        int64_t tk[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tk[r] = kts[16 * kt + 4 * g + r];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) tbq[r][qt] = time_key64(tq[qt] - tk[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) wq[r][qt] = win[16 * qt + lc - (16 * kt + 4 * g + r) + 31];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) tvq[r][qt] = tvk[tbq[r][qt]];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int jr = 16 * kt + 4 * g + r;   // key row in the block
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          const int ir = 16 * qt + lc;        // query row in the block
+          const bool vis = qv[qt] && (j0 + jr <= q0 + ir);
+          const float sc = a.alpha * sacc[kt][qt][r] + wq[r][qt] + tvq[r][qt];
+          const float pv = sc * sigmoid_t(sc);
+          sacc[kt][qt][r] = vis ? pv : 0.0f;
+        }
+      }
+    }
+    // AV^T += V^T P^T over the block's 32 keys
+    bf16x8 bp[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) bp[qt] = pack_slots(sacc[0][qt], sacc[1][qt]);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const bf16x8 vt_op = load_block_tr<DH>(vblk, ct, lc, g);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) acc[ct][qt] = mfma_16x16x32(vt_op, bp[qt], acc[ct][qt]);
+    }
+  }
+  store_tiles16<NCT>(a.av + (s0 + q0) * a.d_model + pl.h * DH, a.d_model, acc, lc, g, 1.0f, qv[0], qv[1]);
+}
+
 // fp32 -> bf16 (round to nearest even), n a multiple of 4.
 __global__ __launch_bounds__(256) void to_bf16_kernel(const float4* __restrict__ src, uint2* __restrict__ dst,
                                                       int64_t n4) {
@@ -994,6 +1153,12 @@ hipError_t launch_attn_bwd_bf16(const BwdAttnArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   return a.head_dim == 32 ? launch_train(attn_train_kv_bf16_kernel<32>, a, s)
                           : launch_train(attn_train_kv_bf16_kernel<64>, a, s);
+}
+
+hipError_t launch_attn_fwd_bf16_rows(const BwdAttnArgs& a, hipStream_t s) {
+  if (!a.q16 || !a.k16 || !a.v16 || !a.av) return hipErrorInvalidValue;
+  return a.head_dim == 32 ? launch_train(attn_fwd_bf16_rows_kernel<32>, a, s)
+                          : launch_train(attn_fwd_bf16_rows_kernel<64>, a, s);
 }
 
 hipError_t launch_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s) {

@@ -39,6 +39,7 @@ struct AttnArgs {
   int max_seq_len;
   int max_cache_len;
   int no_self;               // targets do not see themselves
+  int in_bf16;               // per-row kernel: q/k/v/ck/cv are bf16 (else fp32)
   int64_t total_tokens;      // T
   int* sched;                // bf16 path: work list built by the scheduling pass
   int bm;                    // bf16 path: queries per work item (64)
@@ -90,6 +91,8 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 // per row, no key-range splits).
 bool attn_can_fuse_norm_gate(int num_seqs, int max_seq_len, int num_heads, int64_t total_tokens,
                              int d_model);
+// Per-row attention (one thread per query row), every option; fp32 inputs,
+// or bf16 ones with head_dim 32 when a.in_bf16 is set.
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
 
 // C[M, N] = A[M, K] B[N, K]^T (+ epilogue). Both operands row-major with K
@@ -244,6 +247,10 @@ hipError_t launch_attn_bwd_f32(const BwdAttnArgs& a, hipStream_t s);
 // The same backward on the bf16 matrix cores, from a.q16/k16/v16/dav16
 // (head_dim 32 or 64); the outputs and table gradients as above.
 hipError_t launch_attn_bwd_bf16(const BwdAttnArgs& a, hipStream_t s);
+// Plain causal AV (fp32, row stride d_model) from a.q16/k16/v16 on the bf16
+// matrix cores, head_dim 32 or 64: the bf16 forward for head dimensions the
+// tiled bf16 kernel does not take.
+hipError_t launch_attn_fwd_bf16_rows(const BwdAttnArgs& a, hipStream_t s);
 // dst[i] = bf16(src[i]) (round to nearest even), n a multiple of 4.
 hipError_t launch_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
 // C[m, n] = sum_k A[m sam + k sak] B[k sbk + n sbn] (+ bias[n] + addend[m, n]);

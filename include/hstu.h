@@ -83,7 +83,7 @@ typedef enum { HSTU_BIAS_TABLES = 0, HSTU_BIAS_LINEAR = 1 } hstu_bias_mode;
 typedef struct {
   int32_t d_model;          /* == num_heads * head_dim */
   int32_t num_heads;
-  int32_t head_dim;         /* bf16: 64; f32: 32 or 64 */
+  int32_t head_dim;         /* 32 or 64 (bf16 head_dim 32: see hstu_attn_fwd) */
   int32_t dtype;            /* hstu_dtype */
   float alpha;              /* score scale, 1e-6 <= |alpha| <= 1e6 (1.0 by default) */
   float ln_eps;             /* LayerNorm epsilon, >= 0 (1e-5 by default) */
@@ -210,12 +210,12 @@ const char *hstu_last_error(void);
 int hstu_proj_fwd(const hstu_layer_desc *desc, const hstu_layer_params *params, int64_t T,
                   const void *x, void *u, void *v, void *q, void *k, void *stream);
 
-/* Workspace bytes hstu_attn_fwd needs for this batch. bf16: the work list
+/* Workspace bytes hstu_attn_fwd needs for this batch. bf16, head_dim 64: the work list
  * of its scheduling pass, 4 * (9 + U) bytes rounded up to 256, with
  * U = I * S units, I = num_seqs * ceil(max_seq_len / 64) (sequence, query
  * tile) items and S key-range splits per item (S = 1 when I >= 512, else
  * min(8, ceil(512 / I)); then, when S > 1, S partial outputs of
- * total_tokens x d_model fp32. f32: 0. */
+ * total_tokens x d_model fp32. f32, and bf16 with head_dim 32: 0. */
 size_t hstu_attn_workspace_size(const hstu_layer_desc *desc, const hstu_jagged *jagged);
 
 /* Spatial aggregation, §2.1 second equation, with the visibility, position
@@ -235,7 +235,11 @@ size_t hstu_attn_workspace_size(const hstu_layer_desc *desc, const hstu_jagged *
  * (HSTU_E_INVAL); with targets the bound depends on device data and only
  * hstu_check_inputs() checks it (the kernels clamp table indices, so a
  * violation never reads out of bounds). Lengths above max_seq_len are a
- * contract violation: their query tiles past max_seq_len are not computed. */
+ * contract violation: their query tiles past max_seq_len are not computed.
+ * bf16 with head_dim 32 runs plain causal batches on the bf16 matrix cores
+ * (32-query blocks per head); with targets, a cache, token types or
+ * HSTU_BIAS_LINEAR it runs on a per-row kernel with fp32 arithmetic, which
+ * is correct at any size but not tuned for speed. */
 int hstu_attn_fwd(const hstu_layer_desc *desc, const hstu_jagged *jagged,
                   const hstu_kv_cache *cache, const void *q, const void *k, const void *v,
                   const float *pos_bias, const float *time_bias, float *av, void *workspace,

@@ -68,7 +68,7 @@ void attention_validation() {
   hstu_layer_desc d = desc();
   d.head_dim = 32;
   EXPECT(attn(&d, &j) == HSTU_E_INVAL);
-  d = desc(256, 8);
+  d = desc(256, 16);   // head_dim 16
   EXPECT(attn(&d, &j) == HSTU_E_UNSUPPORTED);
   for (float a : {0.0f, NAN, 1e9f, -INFINITY}) {
     d = desc();

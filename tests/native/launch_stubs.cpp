@@ -29,6 +29,7 @@ hipError_t launch_layernorm_f32(const LayerNormArgs&, hipStream_t) { reached("la
 hipError_t launch_attn_train_fwd(const BwdAttnArgs&, hipStream_t) { reached("launch_attn_train_fwd"); }
 hipError_t launch_attn_bwd_f32(const BwdAttnArgs&, hipStream_t) { reached("launch_attn_bwd_f32"); }
 hipError_t launch_attn_bwd_bf16(const BwdAttnArgs&, hipStream_t) { reached("launch_attn_bwd_bf16"); }
+hipError_t launch_attn_fwd_bf16_rows(const BwdAttnArgs&, hipStream_t) { reached("launch_attn_fwd_bf16_rows"); }
 hipError_t launch_to_bf16(const float*, uint16_t*, int64_t, hipStream_t) { reached("launch_to_bf16"); }
 hipError_t launch_to_bf16_t(const float*, int64_t, int64_t, int, uint16_t*, int64_t, hipStream_t) {
   reached("launch_to_bf16_t");

@@ -66,7 +66,7 @@ def test_validation_errors(lib):
     d = _desc()
     d.head_dim = 32
     assert _attn(lib, d, _jag()) == hstu.HSTU_E_INVAL          # d_model != H * dh
-    d = hstu.make_desc(256, 8, hstu.HSTU_BF16, 255)            # dh = 32 in bf16
+    d = hstu.make_desc(256, 16, hstu.HSTU_BF16, 255)           # dh = 16
     assert _attn(lib, d, _jag()) == hstu.HSTU_E_UNSUPPORTED
     d = _desc()
     d.dtype = 7
