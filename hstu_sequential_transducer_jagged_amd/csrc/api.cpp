@@ -635,9 +635,10 @@ size_t train_ws_base(const hstu_layer_desc* desc, size_t T) {
   return (desc->input_norm ? 18 : 17) * td + round256(T * sizeof(float)) + bf;
 }
 
-// With attn_bwd_bf16 and head_dim 64 the attention forward of the training
-// layer also runs on the bf16 kernel (from the bf16 copies of Q, K, V); its
-// work list and partial outputs follow the bf16 products' region.
+// With attn_bwd_bf16 the attention forward of the training layer also runs
+// on bf16 (from the bf16 copies of Q, K, V): head_dim 64 on the tiled kernel,
+// whose work list and partial outputs follow the bf16 products' region, and
+// head_dim 32 on the row-structured kernel, which needs no workspace.
 bool train_fwd_bf16(const hstu_layer_desc* desc) {
   return desc->attn_bwd_bf16 == 1 && desc->head_dim == 64 && desc->d_model <= 1024;
 }
@@ -861,6 +862,11 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
       const hstu::AttnArgs a = make_attn_args(&d16, jagged, nullptr, Q16, K16, V16, params->pos_bias,
                                               params->time_bias, AV, attn16_ws);
       HSTU_TRY(hstu::launch_attn_bf16(a, s), "attention forward (bf16)");
+    } else if (bf16_bwd) {
+      // head_dim 32: the row-structured bf16 kernel, from the same copies
+      hstu::BwdAttnArgs fa = ba;
+      fa.q16 = Q16; fa.k16 = K16; fa.v16 = V16;
+      HSTU_TRY(hstu::launch_attn_fwd_bf16_rows(fa, s), "attention forward (bf16)");
     } else {
       HSTU_TRY(hstu::launch_attn_train_fwd(ba, s), "attention forward");
     }

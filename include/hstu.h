@@ -115,10 +115,10 @@ typedef struct {
   int32_t attn_bwd_bf16;    /* 0 (default) or 1, read by the training entry points
                                (hstu_layer_bwd, hstu_layer_fwd_train,
                                hstu_layer_bwd_after_fwd): the attention backward runs on
-                               the bf16 matrix cores, and with head_dim 64 so does the
-                               attention forward of the training layer (the recompute, and
-                               hstu_layer_fwd_train's), on the forward path's kernel with
-                               fp32 AV. Q, K, V and dAV are rounded to bf16 once, P and dS
+                               the bf16 matrix cores, and so does the attention forward
+                               of the training layer (the recompute, and
+                               hstu_layer_fwd_train's), on the forward path's kernels
+                               with fp32 AV. Q, K, V and dAV are rounded to bf16 once, P and dS
                                as the operands of their products; every sum is fp32. Other
                                steps stay fp32 (see gemm_bwd_bf16 for the products).
                                Gradients then agree with the fp32 ones to the bf16
