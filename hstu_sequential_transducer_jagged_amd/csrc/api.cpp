@@ -891,9 +891,9 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
   // Y = X + G W2^T + b2
   if (g16) {
     // dG = dY W2 (B = W2^T); dW2 = dY^T G over the tokens, in splits
-    HSTU_TRY(hstu::launch_to_bf16(DY, DY16, T * d, s), "bf16 copy");
     HSTU_TRY(hstu::launch_to_bf16_t(W2, d, d, d, W2T, d, s), "bf16 transpose");
-    HSTU_TRY(hstu::launch_to_bf16_t(DY, d, T, d, DYT, ts.tp, s), "bf16 transpose");
+    // dY^T and the row-major dY copy in one pass over dY
+    HSTU_TRY(hstu::launch_to_bf16_t(DY, d, T, d, DYT, ts.tp, s, DY16, d), "bf16 transpose");
     HSTU_TRY(hstu::launch_to_bf16_t(G, d, T, d, GT, ts.tp, s), "bf16 transpose");
     HSTU_TRY(gemm16(DY16, d, W2T, d, DG, d, nullptr, T, d, d, 1), "dG gemm (bf16)");
     HSTU_TRY(gemm16(DYT, ts.tp, GT, ts.tp, PART, d, nullptr, d, d, ts.kc, ts.S), "dW2 gemm (bf16)");
@@ -906,14 +906,15 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
   }
   HSTU_TRY(hstu::launch_colsum(DY, d, T, d, grads->db2, s), "db2");
   // G = (N^ gamma + beta) . U
-  HSTU_TRY(hstu::launch_ln_gate_bwd(DG, U, NH, RSTD, params->ln_gamma, params->ln_beta, DZ, d4, DAV,
-                                    grads->dgamma, grads->dbeta, T, d, s), "ln/gate backward");
+  // (with the bf16 attention backward, dAV goes out in bf16 only: its one reader)
+  HSTU_TRY(hstu::launch_ln_gate_bwd(DG, U, NH, RSTD, params->ln_gamma, params->ln_beta, DZ, d4,
+                                    bf16_bwd ? nullptr : DAV, bf16_bwd ? DAV16 : nullptr, grads->dgamma,
+                                    grads->dbeta, T, d, s), "ln/gate backward");
   // AV = (SiLU(a Q K^T + rab) . M) V, per head
-  ba.dav = DAV;
+  ba.dav = bf16_bwd ? nullptr : DAV;
   ba.dv = DZ + d; ba.dq = DZ + 2 * d; ba.dk = DZ + 3 * d; ba.ld_dz = d4;
   ba.dpos = grads->dpos; ba.dtime = grads->dtime;
   if (bf16_bwd) {
-    HSTU_TRY(hstu::launch_to_bf16(DAV, DAV16, T * d, s), "bf16 copy");
     ba.q16 = Q16; ba.k16 = K16; ba.v16 = V16; ba.dav16 = DAV16;
     HSTU_TRY(hstu::launch_attn_bwd_bf16(ba, s), "attention backward (bf16)");
   } else {

@@ -180,8 +180,8 @@ __global__ __launch_bounds__(256) void ln_gate_bwd_kernel(const float* __restric
                                                           const float* __restrict__ rstd,
                                                           const float* gamma, const float* beta,
                                                           float* du, int64_t ldu, float* dav,
-                                                          float* dgamma, float* dbeta, int64_t M,
-                                                          int d) {
+                                                          uint16_t* dav16, float* dgamma, float* dbeta,
+                                                          int64_t M, int d) {
   __shared__ __attribute__((aligned(16))) float sg[4][1024];
   __shared__ __attribute__((aligned(16))) float sb[4][1024];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -223,9 +223,12 @@ __global__ __launch_bounds__(256) void ln_gate_bwd_kernel(const float* __restric
     for (int i = 0; i < kRow4; ++i) {
       const int c4 = lane + 64 * i;
       if (c4 >= n4) continue;
-      *reinterpret_cast<float4*>(dav + row * d + 4 * c4) =
-          make_float4(r * (dnh[i].x - m1 - nh[i].x * m2), r * (dnh[i].y - m1 - nh[i].y * m2),
-                      r * (dnh[i].z - m1 - nh[i].z * m2), r * (dnh[i].w - m1 - nh[i].w * m2));
+      const float4 o = make_float4(r * (dnh[i].x - m1 - nh[i].x * m2), r * (dnh[i].y - m1 - nh[i].y * m2),
+                                   r * (dnh[i].z - m1 - nh[i].z * m2), r * (dnh[i].w - m1 - nh[i].w * m2));
+      if (dav16)
+        *reinterpret_cast<uint2*>(dav16 + row * d + 4 * c4) = make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
+      else
+        *reinterpret_cast<float4*>(dav + row * d + 4 * c4) = o;
     }
   }
 #pragma unroll
@@ -441,14 +444,15 @@ hipError_t launch_ln_gate_fwd(const float* av, const float* u, const float* gamm
 
 hipError_t launch_ln_gate_bwd(const float* dg, const float* u, const float* nhat, const float* rstd,
                               const float* gamma, const float* beta, float* du, int64_t ldu, float* dav,
-                              float* dgamma, float* dbeta, int64_t M, int d, hipStream_t s) {
+                              uint16_t* dav16, float* dgamma, float* dbeta, int64_t M, int d, hipStream_t s) {
   if (M == 0) return hipSuccess;
   const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
   if (d % 4 != 0 || d > 64 * 4 * kRow4 || ldu % 4 != 0 || !a16(dg) || !a16(u) || !a16(nhat) || !a16(du) ||
-      !a16(dav) || !a16(gamma) || !a16(beta))
+      !a16(dav) || !a16(gamma) || !a16(beta) || (reinterpret_cast<uintptr_t>(dav16) & 7u) != 0 ||
+      (dav == nullptr && dav16 == nullptr))
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(ln_gate_bwd_kernel, dim3(static_cast<unsigned>((M + 15) / 16)), dim3(256), 0, s, dg,
-                     u, nhat, rstd, gamma, beta, du, ldu, dav, dgamma, dbeta, M, d);
+                     u, nhat, rstd, gamma, beta, du, ldu, dav, dav16, dgamma, dbeta, M, d);
   return hipGetLastError();
 }
 

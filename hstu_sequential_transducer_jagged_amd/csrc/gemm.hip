@@ -564,9 +564,12 @@ __global__ __launch_bounds__(256) void sum_splits_kernel(const float4* __restric
 // 64 x 64 tiles: coalesced float4 row reads into LDS, then 16-byte bf16
 // writes of the transposed rows (8 consecutive source rows per thread). The
 // 65-float LDS rows make both the stores and the column reads conflict-free.
+// With dst_rows the same rounded values also go out untransposed (row
+// stride ld_rows), from the row reads.
 __global__ __launch_bounds__(256) void to_bf16_t_kernel(const float* __restrict__ src, int64_t ld_src,
                                                         int64_t rows, int cols, uint16_t* __restrict__ dst,
-                                                        int64_t ld_dst) {
+                                                        int64_t ld_dst, uint16_t* __restrict__ dst_rows,
+                                                        int64_t ld_rows) {
   __shared__ float t[64][65];
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 64;
   const int c0 = blockIdx.y * 64;
@@ -576,7 +579,12 @@ __global__ __launch_bounds__(256) void to_bf16_t_kernel(const float* __restrict_
     const int r = it * 16 + (tid >> 4);
     const int c = (tid & 15) * 4;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (r0 + r < rows && c0 + c < cols) v = *reinterpret_cast<const float4*>(src + (r0 + r) * ld_src + c0 + c);
+    if (r0 + r < rows && c0 + c < cols) {
+      v = *reinterpret_cast<const float4*>(src + (r0 + r) * ld_src + c0 + c);
+      if (dst_rows)
+        *reinterpret_cast<uint2*>(dst_rows + (r0 + r) * ld_rows + c0 + c) =
+            make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+    }
     t[r][c + 0] = v.x;
     t[r][c + 1] = v.y;
     t[r][c + 2] = v.z;
@@ -680,15 +688,17 @@ hipError_t launch_sum_splits(const float* part, int splits, int64_t n, float* ou
 }
 
 hipError_t launch_to_bf16_t(const float* src, int64_t ld_src, int64_t rows, int cols, uint16_t* dst,
-                            int64_t ld_dst, hipStream_t s) {
+                            int64_t ld_dst, hipStream_t s, uint16_t* dst_rows, int64_t ld_rows) {
   if (cols % 4 != 0 || ld_src % 4 != 0 || ld_src < cols || ld_dst % 8 != 0 || ld_dst < rows || !aligned16(src) ||
       !aligned16(dst))
+    return hipErrorInvalidValue;
+  if (dst_rows && (ld_rows % 4 != 0 || ld_rows < cols || (reinterpret_cast<uintptr_t>(dst_rows) & 7u) != 0))
     return hipErrorInvalidValue;
   if (cols == 0 || ld_dst == 0) return hipSuccess;
   const int64_t gx = (ld_dst + 63) / 64;
   if (gx > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(to_bf16_t_kernel, dim3(static_cast<unsigned>(gx), (cols + 63) / 64), dim3(256), 0, s,
-                     src, ld_src, rows, cols, dst, ld_dst);
+                     src, ld_src, rows, cols, dst, ld_dst, dst_rows, ld_rows);
   return hipGetLastError();
 }
 

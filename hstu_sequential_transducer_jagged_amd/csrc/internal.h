@@ -178,9 +178,11 @@ hipError_t launch_to_bf16x3(const float* src, int64_t rows, int cols, uint16_t* 
 hipError_t launch_sum_splits(const float* part, int splits, int64_t n, float* out, hipStream_t s);
 // dst[c * ld_dst + r] = bf16(src[r * ld_src + c]) for r < rows, c < cols, and
 // 0 for rows <= r < ld_dst: the transposed bf16 copy, zero-padded along r
-// (cols % 4 == 0, ld_src % 4 == 0, ld_dst % 8 == 0).
+// (cols % 4 == 0, ld_src % 4 == 0, ld_dst % 8 == 0). With dst_rows, also
+// dst_rows[r * ld_rows + c] = bf16(src[r * ld_src + c]) for r < rows, c < cols
+// (ld_rows % 4 == 0, 8-byte aligned).
 hipError_t launch_to_bf16_t(const float* src, int64_t ld_src, int64_t rows, int cols, uint16_t* dst,
-                            int64_t ld_dst, hipStream_t s);
+                            int64_t ld_dst, hipStream_t s, uint16_t* dst_rows = nullptr, int64_t ld_rows = 0);
 hipError_t launch_proj_bf16(const ProjArgs& a, hipStream_t s);
 hipError_t launch_proj_f32(const ProjArgs& a, hipStream_t s);
 hipError_t launch_out_bf16(const OutArgs& a, hipStream_t s);
@@ -271,7 +273,7 @@ hipError_t launch_ln_gate_fwd(const float* av, const float* u, const float* gamm
                               hipStream_t s);
 hipError_t launch_ln_gate_bwd(const float* dg, const float* u, const float* nhat, const float* rstd,
                               const float* gamma, const float* beta, float* du, int64_t ldu, float* dav,
-                              float* dgamma, float* dbeta, int64_t M, int d, hipStream_t s);
+                              uint16_t* dav16, float* dgamma, float* dbeta, int64_t M, int d, hipStream_t s);
 hipError_t launch_silu_bwd(float* dz, const float* z, int64_t n, hipStream_t s);
 // dZ = dz . SiLU'(z) over [T, n] fp32 (not written back): dz16 [T, n] bf16,
 // dzt [n, tp] bf16 (dZ^T, zero for T <= t < tp), and db1[c] += sum_t dZ[t, c]
