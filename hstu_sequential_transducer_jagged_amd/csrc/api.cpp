@@ -818,7 +818,8 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
   if (fwd && g16) {
     // f1 feeds every gradient: its operands are split into bf16 hi and lo
     // parts, [Xh | Xl | Xh] [Wh | Wh | Wl]^T over 3d, fp32-like products
-    HSTU_TRY(hstu::launch_to_bf16x3(XIN, T, d, XIN16, 0, s), "bf16 split");
+    // (the same pass writes Xin^T in bf16, which dW1 reads in the backward)
+    HSTU_TRY(hstu::launch_to_bf16_t(XIN, d, T, d, XINT, ts.tp, s, XIN16, 3 * d, true), "bf16 split");
     HSTU_TRY(hstu::launch_to_bf16x3(W1, d4, d, W1_16, 1, s), "bf16 split");
     hstu::GemmBf16Args g{XIN16, 3 * d, W1_16, 3 * d, Z, d4, nullptr, T, d4, 3 * d, 1};
     g.bias = params->b1;
@@ -925,7 +926,6 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
     // dZ in bf16 (row-major and transposed) and db1 in one pass; dW1 = dZ^T
     // Xin over the tokens, in splits; dX (or dXn) = dZ W1 (B = W1^T)
     HSTU_TRY(hstu::launch_silu_bwd_bf16(DZ, Z, T, d4, DZ16, DZT, ts.tp, grads->db1, s), "silu backward (bf16)");
-    HSTU_TRY(hstu::launch_to_bf16_t(XIN, d, T, d, XINT, ts.tp, s), "bf16 transpose");
     HSTU_TRY(hstu::launch_to_bf16_t(W1, d, d4, d, W1T, d4, s), "bf16 transpose");
     HSTU_TRY(gemm16(DZT, ts.tp, XINT, ts.tp, PART, d, nullptr, d4, d, ts.kc, ts.S), "dW1 gemm (bf16)");
     HSTU_TRY(hstu::launch_sum_splits(PART, ts.S, static_cast<int64_t>(d4) * d, grads->dw1, s), "dW1 sum");

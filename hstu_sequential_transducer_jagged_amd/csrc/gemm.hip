@@ -565,11 +565,12 @@ __global__ __launch_bounds__(256) void sum_splits_kernel(const float4* __restric
 // writes of the transposed rows (8 consecutive source rows per thread). The
 // 65-float LDS rows make both the stores and the column reads conflict-free.
 // With dst_rows the same rounded values also go out untransposed (row
-// stride ld_rows), from the row reads.
+// stride ld_rows), from the row reads; with rows_x3 as the hi/lo split rows
+// [hi | lo | hi] of to_bf16x3_kernel below (lo_last = 0).
 __global__ __launch_bounds__(256) void to_bf16_t_kernel(const float* __restrict__ src, int64_t ld_src,
                                                         int64_t rows, int cols, uint16_t* __restrict__ dst,
                                                         int64_t ld_dst, uint16_t* __restrict__ dst_rows,
-                                                        int64_t ld_rows) {
+                                                        int64_t ld_rows, int rows_x3) {
   __shared__ float t[64][65];
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 64;
   const int c0 = blockIdx.y * 64;
@@ -581,9 +582,17 @@ __global__ __launch_bounds__(256) void to_bf16_t_kernel(const float* __restrict_
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (r0 + r < rows && c0 + c < cols) {
       v = *reinterpret_cast<const float4*>(src + (r0 + r) * ld_src + c0 + c);
-      if (dst_rows)
-        *reinterpret_cast<uint2*>(dst_rows + (r0 + r) * ld_rows + c0 + c) =
-            make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+      if (dst_rows) {
+        uint16_t* const o = dst_rows + (r0 + r) * ld_rows + c0 + c;
+        const uint2 hi = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+        *reinterpret_cast<uint2*>(o) = hi;
+        if (rows_x3) {
+          const float4 l = make_float4(v.x - bf2f(hi.x & 0xffff), v.y - bf2f(hi.x >> 16),
+                                       v.z - bf2f(hi.y & 0xffff), v.w - bf2f(hi.y >> 16));
+          *reinterpret_cast<uint2*>(o + cols) = make_uint2(pack_bf16x2(l.x, l.y), pack_bf16x2(l.z, l.w));
+          *reinterpret_cast<uint2*>(o + 2 * cols) = hi;
+        }
+      }
     }
     t[r][c + 0] = v.x;
     t[r][c + 1] = v.y;
@@ -688,17 +697,18 @@ hipError_t launch_sum_splits(const float* part, int splits, int64_t n, float* ou
 }
 
 hipError_t launch_to_bf16_t(const float* src, int64_t ld_src, int64_t rows, int cols, uint16_t* dst,
-                            int64_t ld_dst, hipStream_t s, uint16_t* dst_rows, int64_t ld_rows) {
+                            int64_t ld_dst, hipStream_t s, uint16_t* dst_rows, int64_t ld_rows, bool rows_x3) {
   if (cols % 4 != 0 || ld_src % 4 != 0 || ld_src < cols || ld_dst % 8 != 0 || ld_dst < rows || !aligned16(src) ||
       !aligned16(dst))
     return hipErrorInvalidValue;
-  if (dst_rows && (ld_rows % 4 != 0 || ld_rows < cols || (reinterpret_cast<uintptr_t>(dst_rows) & 7u) != 0))
+  if (dst_rows && (ld_rows % 4 != 0 || ld_rows < (rows_x3 ? 3 : 1) * static_cast<int64_t>(cols) ||
+                   (reinterpret_cast<uintptr_t>(dst_rows) & 7u) != 0))
     return hipErrorInvalidValue;
   if (cols == 0 || ld_dst == 0) return hipSuccess;
   const int64_t gx = (ld_dst + 63) / 64;
   if (gx > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(to_bf16_t_kernel, dim3(static_cast<unsigned>(gx), (cols + 63) / 64), dim3(256), 0, s,
-                     src, ld_src, rows, cols, dst, ld_dst, dst_rows, ld_rows);
+                     src, ld_src, rows, cols, dst, ld_dst, dst_rows, ld_rows, rows_x3 ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -388,7 +388,8 @@ int hstu_layer_bwd(const hstu_layer_desc *desc, const hstu_layer_params *params,
  * on bf16 with desc->attn_bwd_bf16), writing y [T, d] (must not alias x) and keeping in `workspace`
  * (hstu_layer_bwd_workspace_size() bytes, 256-byte aligned) the activations
  * the backward reads: Z, U, V, Q, K, AV, the normalised AV, 1/sigma and G
- * (and LayerNorm(X) with input_norm).
+ * (and LayerNorm(X) with input_norm; with the bf16 flags also bf16 copies of
+ * Q, K, V and, with gemm_bwd_bf16, of the f1 input transposed).
  * hstu_layer_bwd_after_fwd: the backward of hstu_layer_bwd, reading those
  * activations instead of recomputing them; desc, params, jagged, x and the
  * workspace must be those of the hstu_layer_fwd_train call, with the
