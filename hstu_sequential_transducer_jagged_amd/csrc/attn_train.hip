@@ -718,39 +718,43 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
       for (int kt = 0; kt < 2; ++kt)
         *reinterpret_cast<float4*>(dsw + (16 * qt + lc) * DSR + 16 * kt + 4 * g) =
             make_float4(sacc[kt][qt][0], sacc[kt][qt][1], sacc[kt][qt][2], sacc[kt][qt][3]);
-    // dQ^T += K^T dS^T over the block's 32 keys
+    // dQ^T += K^T dS^T over the block's 32 keys, and the position gradient:
+    // lane l sums diagonal l of this wave's parked block (rows ir with key
+    // row jr = ir - l + 31 in the block; hidden pairs hold dS = 0). LDS
+    // accesses of one wave complete in order, so the block is read back
+    // without a barrier. The K^T operand reads go out first, then the first
+    // half of the diagonal reads, so that these land while the products run;
+    // the second half follows the products. (Adding each pair's dS to the
+    // accumulator with an LDS atomic instead, sixteen per lane and step, ran
+    // 3.4 times slower.)
     bf16x8 bs[2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) bs[qt] = pack_slots(sacc[0][qt], sacc[1][qt]);
+    bf16x8 kt_op[NCT];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const bf16x8 kt_op = load_block_tr<DH>(kblk, ct, lc, g);
+    for (int ct = 0; ct < NCT; ++ct) kt_op[ct] = load_block_tr<DH>(kblk, ct, lc, g);
+    float v[32];
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) acc[ct][qt] = mfma_16x16x32(kt_op, bs[qt], acc[ct][qt]);
+    for (int e = 0; e < 16; ++e) {
+      const int jr = e - lane + 31;   // in the block for ir = e in [lane - 31, lane]
+      v[e] = dsw[e * DSR + min(max(jr, 0), 31)];
     }
-    // position gradient: lane l sums diagonal l of this wave's parked block
-    // (rows ir with key row jr = ir - l + 31 in the block; hidden pairs hold
-    // dS = 0). LDS accesses of one wave complete in order, so the block is
-    // read back without a barrier.
-    // The reads go out eight at a time into distinct registers: left to
-    // itself the compiler reuses one register and waits for each read.
-    // (Adding each pair's dS to the accumulator with an LDS atomic instead,
-    // sixteen per lane and step, ran 3.4 times slower.)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) acc[ct][qt] = mfma_16x16x32(kt_op[ct], bs[qt], acc[ct][qt]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e = 16; e < 32; ++e) {
+      const int jr = e - lane + 31;
+      v[e] = dsw[e * DSR + min(max(jr, 0), 31)];
+    }
     float pos_sum = 0.0f;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int ir = 8 * b + e, jr = ir - lane + 31;   // in the block for ir in [lane - 31, lane]
-        v[e] = dsw[ir * DSR + min(max(jr, 0), 31)];
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int ir = 8 * b + e, jr = ir - lane + 31;
-        pos_sum += (jr >= 0 && jr < 32) ? v[e] : 0.0f;
-      }
+    for (int e = 0; e < 32; ++e) {
+      const int jr = e - lane + 31;
+      pos_sum += (jr >= 0 && jr < 32) ? v[e] : 0.0f;
     }
     if (lane < 63 && pos_sum != 0.0f) {
       const int gi = D + lane;   // difference D + lane - 31
