@@ -606,13 +606,14 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
   float tg_cur[2] = {0.0f, 0.0f};
   float wv = a.pos_bias[clampi(a.pos_center + q0 - 31 + lane, 0, a.pos_len - 1)];
   int64_t tsv = Ts[min(lane & 31, L - 1)];
-  // the next block's K and V rows, requested one block ahead
-  bf16x8 kn[2][NC], vn[2][NC];
+  // the block's K and V rows; each step requests the next block's rows into
+  // the same registers once the score products and the stash have read them
+  bf16x8 kf[2][NC], vf[2][NC];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     const int krow = min(16 * kt + lc, L - 1);
-    load_row16<NC>(Ks + krow * d, g, kn[kt]);
-    load_row16<NC>(Vs + krow * d, g, vn[kt]);
+    load_row16<NC>(Ks + krow * d, g, kf[kt]);
+    load_row16<NC>(Vs + krow * d, g, vf[kt]);
   }
 
   for (int kb = 0; kb <= pl.blk; ++kb) {
@@ -626,22 +627,6 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
     }
     wv = a.pos_bias[clampi(a.pos_center + D - 63 + lane, 0, a.pos_len - 1)];
     tsv = Ts[min(j0 + 32 + (lane & 31), L - 1)];
-    bf16x8 kf[2][NC], vf[2][NC];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        kf[kt][c] = kn[kt][c];
-        vf[kt][c] = vn[kt][c];
-      }
-    if (kb < pl.blk) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int krow = min(j0 + 32 + 16 * kt + lc, L - 1);
-        load_row16<NC>(Ks + krow * d, g, kn[kt]);
-        load_row16<NC>(Vs + krow * d, g, vn[kt]);
-      }
-    }
     // S^T = K Q^T (rows: keys, columns: queries); dP^T = V dAV^T
     f32x4 sacc[2][2], pacc[2][2];
 #pragma unroll
@@ -657,6 +642,14 @@ __global__ __launch_bounds__(512) void attn_train_dq_bf16_kernel(BwdAttnArgs a) 
       }
     // this block's keys, for the transposed reads of the second product
     stash_block<DH>(kblk, kf, lc, g);
+    if (kb < pl.blk) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int krow = min(j0 + 32 + 16 * kt + lc, L - 1);
+        load_row16<NC>(Ks + krow * d, g, kf[kt]);
+        load_row16<NC>(Vs + krow * d, g, vf[kt]);
+      }
+    }
     // per 16-key half: every LDS read first (key times and position-window
     // entries, then the time-table entries of the buckets), then the
     // arithmetic for every pair, masked by a select; read behind the
@@ -836,13 +829,15 @@ __global__ __launch_bounds__(512) void attn_train_kv_bf16_kernel(BwdAttnArgs a) 
   // window entry e <-> difference 32 qb - j0 - 31 + e; fetched a block ahead
   float wv = a.pos_bias[clampi(a.pos_center - 31 + lane, 0, a.pos_len - 1)];
   int64_t tsv = Ts[min(j0 + (lane & 31), L - 1)];
-  // the next block's Q and dAV rows, requested one block ahead
-  bf16x8 qn[2][NC], dn[2][NC];
+  // the block's Q and dAV rows; each step requests the next block's rows
+  // into the same registers once the score products and the stashes have
+  // read them
+  bf16x8 qf[2][NC], df[2][NC];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     const int qrow = min(j0 + 16 * qt + lc, L - 1);
-    load_row16<NC>(Qs + qrow * d, g, qn[qt]);
-    load_row16<NC>(Ds + qrow * d, g, dn[qt]);
+    load_row16<NC>(Qs + qrow * d, g, qf[qt]);
+    load_row16<NC>(Ds + qrow * d, g, df[qt]);
   }
   for (int qb = pl.blk; qb < nblk; ++qb) {
     const int q0 = qb * 32, D = q0 - j0;
@@ -855,22 +850,6 @@ __global__ __launch_bounds__(512) void attn_train_kv_bf16_kernel(BwdAttnArgs a) 
     }
     wv = a.pos_bias[clampi(a.pos_center + D + 1 + lane, 0, a.pos_len - 1)];
     tsv = Ts[min(q0 + 32 + (lane & 31), L - 1)];
-    bf16x8 qf[2][NC], df[2][NC];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        qf[qt][c] = qn[qt][c];
-        df[qt][c] = dn[qt][c];
-      }
-    if (qb + 1 < nblk) {
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const int qrow = min(q0 + 32 + 16 * qt + lc, L - 1);
-        load_row16<NC>(Qs + qrow * d, g, qn[qt]);
-        load_row16<NC>(Ds + qrow * d, g, dn[qt]);
-      }
-    }
     // S = Q K^T (rows: queries, columns: keys); dP = dAV V^T
     f32x4 sacc[2][2], pacc[2][2];
 #pragma unroll
@@ -887,6 +866,14 @@ __global__ __launch_bounds__(512) void attn_train_kv_bf16_kernel(BwdAttnArgs a) 
     // this block's queries and dAV rows, for the transposed reads
     stash_block<DH>(qblk, qf, lc, g);
     stash_block<DH>(dblk, df, lc, g);
+    if (qb + 1 < nblk) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const int qrow = min(q0 + 32 + 16 * qt + lc, L - 1);
+        load_row16<NC>(Qs + qrow * d, g, qf[qt]);
+        load_row16<NC>(Ds + qrow * d, g, df[qt]);
+      }
+    }
     // time buckets of the block's pairs, in 32 bits where the times allow
     int tbq[2][4][2];
     if (fast) {
@@ -1003,12 +990,14 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_rows_kernel(BwdAttnArgs a) 
   for (int ct = 0; ct < NCT; ++ct) acc[ct][0] = acc[ct][1] = f32x4{};
   float wv = a.pos_bias[clampi(a.pos_center + q0 - 31 + lane, 0, a.pos_len - 1)];
   int64_t tsv = Ts[min(lane & 31, L - 1)];
-  bf16x8 kn[2][NC], vn[2][NC];
+  // the block's K and V rows; the next block's go into the same registers
+  // once the score products and the stash have read them
+  bf16x8 kf[2][NC], vf[2][NC];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     const int krow = min(16 * kt + lc, L - 1);
-    load_row16<NC>(Ks + krow * d, g, kn[kt]);
-    load_row16<NC>(Vs + krow * d, g, vn[kt]);
+    load_row16<NC>(Ks + krow * d, g, kf[kt]);
+    load_row16<NC>(Vs + krow * d, g, vf[kt]);
   }
 
   for (int kb = 0; kb <= pl.blk; ++kb) {
@@ -1022,22 +1011,6 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_rows_kernel(BwdAttnArgs a) 
     }
     wv = a.pos_bias[clampi(a.pos_center + D - 63 + lane, 0, a.pos_len - 1)];
     tsv = Ts[min(j0 + 32 + (lane & 31), L - 1)];
-    bf16x8 kf[2][NC], vf[2][NC];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        kf[kt][c] = kn[kt][c];
-        vf[kt][c] = vn[kt][c];
-      }
-    if (kb < pl.blk) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int krow = min(j0 + 32 + 16 * kt + lc, L - 1);
-        load_row16<NC>(Ks + krow * d, g, kn[kt]);
-        load_row16<NC>(Vs + krow * d, g, vn[kt]);
-      }
-    }
     // S^T = K Q^T (rows: keys, columns: queries)
     f32x4 sacc[2][2];
 #pragma unroll
@@ -1050,6 +1023,14 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_rows_kernel(BwdAttnArgs a) 
       }
     // this block's values, for the transposed reads of the second product
     stash_block<DH>(vblk, vf, lc, g);
+    if (kb < pl.blk) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int krow = min(j0 + 32 + 16 * kt + lc, L - 1);
+        load_row16<NC>(Ks + krow * d, g, kf[kt]);
+        load_row16<NC>(Vs + krow * d, g, vf[kt]);
+      }
+    }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       float wq[4][2], tvq[4][2];
