@@ -893,8 +893,8 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
   if (g16) {
     // dG = dY W2 (B = W2^T); dW2 = dY^T G over the tokens, in splits
     HSTU_TRY(hstu::launch_to_bf16_t(W2, d, d, d, W2T, d, s), "bf16 transpose");
-    // dY^T and the row-major dY copy in one pass over dY
-    HSTU_TRY(hstu::launch_to_bf16_t(DY, d, T, d, DYT, ts.tp, s, DY16, d), "bf16 transpose");
+    // dY^T, the row-major dY copy and db2 (dY's column sums) in one pass over dY
+    HSTU_TRY(hstu::launch_to_bf16_t(DY, d, T, d, DYT, ts.tp, s, DY16, d, false, grads->db2), "bf16 transpose");
     HSTU_TRY(hstu::launch_to_bf16_t(G, d, T, d, GT, ts.tp, s), "bf16 transpose");
     HSTU_TRY(gemm16(DY16, d, W2T, d, DG, d, nullptr, T, d, d, 1), "dG gemm (bf16)");
     HSTU_TRY(gemm16(DYT, ts.tp, GT, ts.tp, PART, d, nullptr, d, d, ts.kc, ts.S), "dW2 gemm (bf16)");
@@ -905,7 +905,7 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
     HSTU_TRY(hstu::launch_gemm_f32s(DY, 1, d, G, d, 1, grads->dw2, d, nullptr, nullptr, d, d, T,
                                     splits(d, d), s), "dW2 gemm");
   }
-  HSTU_TRY(hstu::launch_colsum(DY, d, T, d, grads->db2, s), "db2");
+  if (!g16) HSTU_TRY(hstu::launch_colsum(DY, d, T, d, grads->db2, s), "db2");
   // G = (N^ gamma + beta) . U
   // (with the bf16 attention backward, dAV goes out in bf16 only: its one reader)
   HSTU_TRY(hstu::launch_ln_gate_bwd(DG, U, NH, RSTD, params->ln_gamma, params->ln_beta, DZ, d4,

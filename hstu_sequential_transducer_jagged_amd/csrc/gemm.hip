@@ -566,12 +566,14 @@ __global__ __launch_bounds__(256) void sum_splits_kernel(const float4* __restric
 // 65-float LDS rows make both the stores and the column reads conflict-free.
 // With dst_rows the same rounded values also go out untransposed (row
 // stride ld_rows), from the row reads; with rows_x3 as the hi/lo split rows
-// [hi | lo | hi] of to_bf16x3_kernel below (lo_last = 0).
+// [hi | lo | hi] of to_bf16x3_kernel below (lo_last = 0). With colsum, the
+// tile's fp32 column sums are added to colsum[c] atomically.
 __global__ __launch_bounds__(256) void to_bf16_t_kernel(const float* __restrict__ src, int64_t ld_src,
                                                         int64_t rows, int cols, uint16_t* __restrict__ dst,
                                                         int64_t ld_dst, uint16_t* __restrict__ dst_rows,
-                                                        int64_t ld_rows, int rows_x3) {
+                                                        int64_t ld_rows, int rows_x3, float* colsum) {
   __shared__ float t[64][65];
+  __shared__ float part[4][64];
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 64;
   const int c0 = blockIdx.y * 64;
   const int tid = threadIdx.x;
@@ -600,6 +602,17 @@ __global__ __launch_bounds__(256) void to_bf16_t_kernel(const float* __restrict_
     t[r][c + 3] = v.w;
   }
   __syncthreads();
+  if (colsum) {
+    // four quarters of 16 rows per column, then one atomic per column
+    const int cc = tid & 63, q = tid >> 6;
+    float sum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += t[16 * q + r][cc];
+    part[q][cc] = sum;
+    __syncthreads();
+    if (tid < 64 && c0 + tid < cols && r0 < rows)
+      atomicAdd(&colsum[c0 + tid], (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]));
+  }
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const int idx = it * 256 + tid;
@@ -697,7 +710,8 @@ hipError_t launch_sum_splits(const float* part, int splits, int64_t n, float* ou
 }
 
 hipError_t launch_to_bf16_t(const float* src, int64_t ld_src, int64_t rows, int cols, uint16_t* dst,
-                            int64_t ld_dst, hipStream_t s, uint16_t* dst_rows, int64_t ld_rows, bool rows_x3) {
+                            int64_t ld_dst, hipStream_t s, uint16_t* dst_rows, int64_t ld_rows, bool rows_x3,
+                            float* colsum) {
   if (cols % 4 != 0 || ld_src % 4 != 0 || ld_src < cols || ld_dst % 8 != 0 || ld_dst < rows || !aligned16(src) ||
       !aligned16(dst))
     return hipErrorInvalidValue;
@@ -708,7 +722,7 @@ hipError_t launch_to_bf16_t(const float* src, int64_t ld_src, int64_t rows, int 
   const int64_t gx = (ld_dst + 63) / 64;
   if (gx > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(to_bf16_t_kernel, dim3(static_cast<unsigned>(gx), (cols + 63) / 64), dim3(256), 0, s,
-                     src, ld_src, rows, cols, dst, ld_dst, dst_rows, ld_rows, rows_x3 ? 1 : 0);
+                     src, ld_src, rows, cols, dst, ld_dst, dst_rows, ld_rows, rows_x3 ? 1 : 0, colsum);
   return hipGetLastError();
 }
 

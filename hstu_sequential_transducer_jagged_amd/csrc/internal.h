@@ -181,10 +181,11 @@ hipError_t launch_sum_splits(const float* part, int splits, int64_t n, float* ou
 // (cols % 4 == 0, ld_src % 4 == 0, ld_dst % 8 == 0). With dst_rows, also
 // dst_rows[r * ld_rows + c] = bf16(src[r * ld_src + c]) for r < rows, c < cols
 // (ld_rows % 4 == 0, 8-byte aligned); with rows_x3, the rows of
-// launch_to_bf16x3(lo_last = 0) instead (ld_rows >= 3 cols).
+// launch_to_bf16x3(lo_last = 0) instead (ld_rows >= 3 cols). With colsum,
+// colsum[c] += sum over r of src[r * ld_src + c] (atomic fp32 adds).
 hipError_t launch_to_bf16_t(const float* src, int64_t ld_src, int64_t rows, int cols, uint16_t* dst,
                             int64_t ld_dst, hipStream_t s, uint16_t* dst_rows = nullptr, int64_t ld_rows = 0,
-                            bool rows_x3 = false);
+                            bool rows_x3 = false, float* colsum = nullptr);
 hipError_t launch_proj_bf16(const ProjArgs& a, hipStream_t s);
 hipError_t launch_proj_f32(const ProjArgs& a, hipStream_t s);
 hipError_t launch_out_bf16(const OutArgs& a, hipStream_t s);

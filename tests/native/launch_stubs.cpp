@@ -32,7 +32,7 @@ hipError_t launch_attn_bwd_bf16(const BwdAttnArgs&, hipStream_t) { reached("laun
 hipError_t launch_attn_fwd_bf16_rows(const BwdAttnArgs&, hipStream_t) { reached("launch_attn_fwd_bf16_rows"); }
 hipError_t launch_to_bf16(const float*, uint16_t*, int64_t, hipStream_t) { reached("launch_to_bf16"); }
 hipError_t launch_to_bf16_t(const float*, int64_t, int64_t, int, uint16_t*, int64_t, hipStream_t, uint16_t*, int64_t,
-                            bool) {
+                            bool, float*) {
   reached("launch_to_bf16_t");
 }
 hipError_t launch_gemm_bf16_f32(const GemmBf16Args&, hipStream_t) { reached("launch_gemm_bf16_f32"); }
