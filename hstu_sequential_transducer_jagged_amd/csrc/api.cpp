@@ -718,18 +718,23 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
   }
   hipStream_t s = as_stream(stream);
   if (bwd) {
-    // gradients start at zero (also for an empty batch)
+    // gradients start at zero (also for an empty batch), in one launch
     const struct { float* p; int64_t n; } zero[] = {
         {grads->dw1, 4LL * d * d}, {grads->db1, 4LL * d}, {grads->dw2, 1LL * d * d}, {grads->db2, d},
         {grads->dgamma, d}, {grads->dbeta, d}, {grads->dpos, desc->pos_table_len},
         {grads->dtime, desc->num_time_buckets},
         {norm1 ? grads->dln1_gamma : nullptr, norm1 ? d : 0},
         {norm1 ? grads->dln1_beta : nullptr, norm1 ? d : 0}};
+    static_assert(sizeof(zero) / sizeof(zero[0]) <= hstu::kZeroListMax, "zero list");
+    hstu::ZeroList zl{};
     for (const auto& z : zero) {
       if (z.n == 0) continue;
-      st = device_status(hstu::launch_fill_zero(z.p, z.n, s), "zero fill");
-      if (st) return st;
+      zl.p[zl.count] = z.p;
+      zl.n[zl.count] = z.n;
+      ++zl.count;
     }
+    st = device_status(hstu::launch_fill_zero_list(zl, s), "zero fill");
+    if (st) return st;
   }
   if (empty) return ok();
   const size_t td = round256(static_cast<size_t>(T) * d * sizeof(float));

@@ -94,7 +94,10 @@ __global__ __launch_bounds__(256) void gemm_f32s_kernel(const float* __restrict_
   }
 }
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(float* p, int64_t n) {
+// Zero fill of several buffers in one launch: blockIdx.y picks the buffer.
+__global__ __launch_bounds__(256) void fill_zero_list_kernel(ZeroList z) {
+  float* const p = z.p[blockIdx.y];
+  const int64_t n = z.n[blockIdx.y];
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * 256)
     p[i] = 0.0f;
@@ -416,9 +419,16 @@ hipError_t launch_ln1_bwd(const float* x, const float* dxn, const float* dy, con
   return hipGetLastError();
 }
 
-hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks_for(n)), dim3(256), 0, s, p, n);
+hipError_t launch_fill_zero_list(const ZeroList& z, hipStream_t s) {
+  if (z.count < 0 || z.count > kZeroListMax) return hipErrorInvalidValue;
+  int64_t most = 0;
+  for (int i = 0; i < z.count; ++i) {
+    if (z.n[i] < 0 || (z.n[i] > 0 && z.p[i] == nullptr)) return hipErrorInvalidValue;
+    most = z.n[i] > most ? z.n[i] : most;
+  }
+  if (most == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_zero_list_kernel, dim3(blocks_for(most), static_cast<unsigned>(z.count)), dim3(256), 0,
+                     s, z);
   return hipGetLastError();
 }
 

@@ -264,7 +264,14 @@ hipError_t launch_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_
 hipError_t launch_gemm_f32s(const float* A, int64_t sam, int64_t sak, const float* B, int64_t sbk,
                             int64_t sbn, float* C, int64_t ldc, const float* addend, const float* bias,
                             int M, int N, int64_t K, int splits, hipStream_t s);
-hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+// Zeroes up to kZeroListMax buffers (p[i], n[i] floats) in one launch.
+constexpr int kZeroListMax = 10;
+struct ZeroList {
+  float* p[kZeroListMax];
+  int64_t n[kZeroListMax];
+  int count;
+};
+hipError_t launch_fill_zero_list(const ZeroList& z, hipStream_t s);
 // Input LayerNorm backward (d <= 1024): dx = dy + LN'(x)^T dxn, with the
 // statistics recomputed from x; dgamma/dbeta += column sums of dxn * xhat
 // and dxn.

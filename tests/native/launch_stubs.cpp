@@ -44,7 +44,7 @@ hipError_t launch_gemm_f32s(const float*, int64_t, int64_t, const float*, int64_
                             const float*, const float*, int, int, int64_t, int, hipStream_t) {
   reached("launch_gemm_f32s");
 }
-hipError_t launch_fill_zero(float*, int64_t, hipStream_t) { reached("launch_fill_zero"); }
+hipError_t launch_fill_zero_list(const ZeroList&, hipStream_t) { reached("launch_fill_zero_list"); }
 hipError_t launch_ln1_bwd(const float*, const float*, const float*, const float*, float*, float*, float*,
                           int64_t, int, float, hipStream_t) {
   reached("launch_ln1_bwd");
