@@ -209,8 +209,9 @@ hstu::AttnArgs make_attn_args(const hstu_layer_desc* d, const hstu_jagged* j,
 }
 
 int do_proj(const hstu_layer_desc* d, const hstu_layer_params* p, int64_t T, const void* x,
-            void* u, void* v, void* q, void* k, hipStream_t s) {
+            void* u, void* v, void* q, void* k, hipStream_t s, const hstu::AttnArgs* sched = nullptr) {
   hstu::ProjArgs a{};
+  a.sched = sched;
   a.x = x;
   a.w = p->w1;
   a.bias = p->b1;
@@ -547,14 +548,13 @@ int hstu_layer_fwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
     if (st) return st;
     xin = xn;
   }
-  st = do_proj(desc, params, T, xin, u, v, q, k, s);
-  if (st) return st;
   if (tiled_bf16(desc) &&
       hstu::attn_can_fuse_norm_gate(jagged->num_seqs, jagged->max_seq_len, desc->num_heads, jagged->total_tokens,
                                     desc->d_model)) {
     // one head group covers each row: the attention kernel finishes the rows
     // into G = norm_gate(AV, U) itself (in place over U), with the same row
-    // code as hstu_norm_gate_fwd, so Y is bitwise that of the separate calls
+    // code as hstu_norm_gate_fwd, so Y is bitwise that of the separate calls.
+    // Its work list comes from one extra workgroup of the f1 launch.
     hstu::AttnArgs a = make_attn_args(desc, jagged, cache, q, k, v, params->pos_bias, params->time_bias, av,
                                       attn_work);
     a.fuse_ng = 1;
@@ -563,8 +563,13 @@ int hstu_layer_fwd(const hstu_layer_desc* desc, const hstu_layer_params* params,
     a.ng_gamma = params->ln_gamma;
     a.ng_beta = params->ln_beta;
     a.ng_eps = desc->ln_eps;
+    st = do_proj(desc, params, T, xin, u, v, q, k, s, &a);
+    if (st) return st;
+    a.sched_ready = 1;
     st = device_status(hstu::launch_attn_bf16(a, s), "attention launch");
   } else {
+    st = do_proj(desc, params, T, xin, u, v, q, k, s);
+    if (st) return st;
     st = do_attn(desc, jagged, cache, q, k, v, params->pos_bias, params->time_bias, av, attn_work, s);
     if (st) return st;
     st = do_norm_gate(desc, T, av, u, params->ln_gamma, params->ln_beta, u, s);

@@ -38,6 +38,7 @@
 //    time, a 64-bit path otherwise.
 #include "common.h"
 #include "internal.h"
+#include "attn_sched.h"
 
 #include <algorithm>
 #include <mutex>
@@ -46,7 +47,14 @@ namespace hstu {
 namespace {
 
 constexpr int kBM = kAttnBM;   // query rows per workgroup
-constexpr int kBN = 32;   // keys per step
+constexpr int kBN = kAttnBN;   // keys per step
+using sched::chunk_range;
+using sched::kListInts;
+using sched::kNumXcd;
+using sched::kSchedHead;
+using sched::seq_info;
+using sched::SeqInfo;
+using sched::tile_steps;
 constexpr int kDH = 64;   // head dim of the bf16 kernel
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -60,30 +68,6 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-struct SeqInfo {
-  int64_t s;     // first own token row
-  int L;         // own length
-  int m;         // number of targets (last m own tokens)
-  int64_t cs;    // first cache row
-  int nc;        // cache length
-};
-
-__device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b) {
-  SeqInfo si;
-  si.s = a.offsets[b];
-  si.L = static_cast<int>(a.offsets[b + 1] - si.s);
-  int m = a.num_targets ? a.num_targets[b] : 0;
-  si.m = m < 0 ? 0 : (m > si.L ? si.L : m);
-  if (a.c_offsets) {
-    si.cs = a.c_offsets[b];
-    si.nc = static_cast<int>(a.c_offsets[b + 1] - si.cs);
-  } else {
-    si.cs = 0;
-    si.nc = 0;
-  }
-  return si;
 }
 
 // Bias modes of the bf16 kernel (template parameter): the position and time
@@ -545,153 +529,11 @@ __device__ __forceinline__ void attn_step(
   }
 }
 
-// Number of key steps (32-key tiles visited) of query tile qt of a sequence:
-// the cost the schedule sorts by.
-__device__ __forceinline__ int tile_steps(const SeqInfo& si, int qt, int bm) {
-  const int q0 = qt * bm;
-  const int q_hi = min(q0 + bm, si.L);
-  const int nkeys = si.nc + q_hi;
-  const int n_kt = (nkeys + kBN - 1) / kBN;
-  const int first_tgt = si.L - si.m;
-  const int skip_a = (si.nc + first_tgt + kBN - 1) / kBN;
-  const int skip_b = max((si.nc + q0) / kBN, skip_a);
-  return n_kt - (skip_b - skip_a);
-}
-
-constexpr int kNumXcd = 8;            // XCDs of the chip; workgroup id -> XCD id % 8
-constexpr int kCostBuckets = 1024;    // cost classes of the per-XCD sort
-constexpr int kSchedHead = kAttnSchedHead;
-static_assert(kSchedHead == kNumXcd + 1, "work list header: one counter per XCD, then the total");
-
-// Key steps [lo, hi) of chunk c of an item with n steps: chunks of ceil(n / S)
-// steps; trailing chunks may be empty.
-__device__ __forceinline__ void chunk_range(int n, int S, int c, int& lo, int& hi) {
-  const int per = (n + S - 1) / S;
-  lo = min(c * per, n);
-  hi = min(lo + per, n);
-}
-
-// Cost of work unit u = item * S + chunk: its key steps, at least 1 for a
-// non-empty item (an empty chunk still writes its zero partial); 0 for an
-// empty tile (never scheduled).
-__device__ __forceinline__ int unit_cost(const AttnArgs& a, int n_qt, int u) {
-  const int S = a.splits;
-  const int i = u / S, ch = u - i * S;
-  const int b = i / n_qt, t = i - b * n_qt;
-  const SeqInfo si = seq_info(a, b);
-  // tiles past max_seq_len (a violated contract) are never reached: t < n_qt
-  if (t * a.bm >= si.L) return 0;
-  int lo, hi;
-  chunk_range(tile_steps(si, t, a.bm), S, ch, lo, hi);
-  return max(hi - lo, 1);
-}
-
-// Work list of the bf16 attention. Items are the non-empty (sequence,
-// 64-query tile) pairs, each cut into a.splits units of consecutive key steps
-// (one unit per item unless the batch has few items); a unit's cost is its
-// number of key steps.
-//  1. Units, in (sequence, tile, chunk) order, are cut into kNumXcd contiguous runs
-//     of equal total cost; run x goes to XCD x. The workgroups of one XCD
-//     then work on one or a few sequences at a time and share their K/V rows
-//     in that XCD's L2.
-//  2. Within a run, items are counting-sorted by cost, most expensive first,
-//     so that the XCD's compute units finish together.
-// sched[x] (x = 0..8): first list index of XCD x (sched[8] = unit count);
-// sched[9 + k]: unit ((seq * n_qt + tile) * splits + chunk) at list index k.
-// Exclusive prefix sum over the 1024 threads of the block (wave scans by
-// shuffles, then one pass over the 16 wave totals); *total receives the sum.
-__device__ __forceinline__ long long block_exclusive_scan(long long v, long long* wsum, long long* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  long long inc = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const long long t = __shfl_up(inc, off, 64);
-    if (lane >= off) inc += t;
-  }
-  if (lane == 63) wsum[wave] = inc;
-  __syncthreads();
-  if (wave == 0) {
-    long long w = lane < 16 ? wsum[lane] : 0;
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-      const long long t = __shfl_up(w, off, 64);
-      if (lane >= off) w += t;
-    }
-    if (lane < 16) wsum[lane] = w;
-  }
-  __syncthreads();
-  const long long excl = inc - v + (wave ? wsum[wave - 1] : 0);
-  *total = wsum[15];
-  __syncthreads();   // wsum may be reused by the next scan
-  return excl;
-}
-
+// The scheduling pass in its own launch: one workgroup of 1024 threads.
 __global__ __launch_bounds__(1024) void attn_schedule_kernel(AttnArgs a, int n_qt) {
-  constexpr int kKeep = 8;   // unit costs per thread kept in registers between the passes
-  __shared__ int cnt[kNumXcd * kCostBuckets];
+  __shared__ int cnt[kListInts];
   __shared__ long long wsum[16];
-  const int tid = threadIdx.x;
-  const int items = a.num_seqs * n_qt * a.splits;
-  for (int i = tid; i < kNumXcd * kCostBuckets; i += 1024) cnt[i] = 0;
-  // each thread owns a contiguous chunk of items
-  const int per = (items + 1023) / 1024;
-  const int i0 = min(tid * per, items), i1 = min(i0 + per, items);
-  int cst[kKeep];
-  long long sum = 0;
-#pragma unroll
-  for (int k = 0; k < kKeep; ++k) {
-    cst[k] = i0 + k < i1 ? unit_cost(a, n_qt, i0 + k) : 0;
-    sum += cst[k];
-  }
-  for (int i = i0 + kKeep; i < i1; ++i) sum += unit_cost(a, n_qt, i);
-  long long total_cost;
-  const long long run0 = block_exclusive_scan(sum, wsum, &total_cost);   // also orders cnt's zeroing
-  // sort key: XCD-major, cost descending; the item's XCD is the run holding
-  // the midpoint of its cost interval
-  auto key_of = [&](long long run, int c) __attribute__((always_inline)) {
-    const int x = static_cast<int>(min(static_cast<long long>(kNumXcd - 1),
-                                       ((2 * run + c) * kNumXcd) / (2 * total_cost)));
-    return x * kCostBuckets + (kCostBuckets - 1 - min(c, kCostBuckets - 1));
-  };
-  long long run = run0;
-#pragma unroll
-  for (int k = 0; k < kKeep; ++k) {
-    if (cst[k] > 0) atomicAdd(&cnt[key_of(run, cst[k])], 1);
-    run += cst[k];
-  }
-  for (int i = i0 + kKeep; i < i1; ++i) {
-    const int c = unit_cost(a, n_qt, i);
-    if (c > 0) atomicAdd(&cnt[key_of(run, c)], 1);
-    run += c;
-  }
-  __syncthreads();
-  // exclusive scan of the kNumXcd * kCostBuckets counters, 8 per thread
-  constexpr int kPer = kNumXcd * kCostBuckets / 1024;
-  int loc = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) loc += cnt[tid * kPer + i];
-  long long units;
-  int base = static_cast<int>(block_exclusive_scan(loc, wsum, &units));
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int c = cnt[tid * kPer + i];
-    cnt[tid * kPer + i] = base;
-    base += c;
-  }
-  __syncthreads();
-  if (tid < kNumXcd) a.sched[tid] = cnt[tid * kCostBuckets];
-  if (tid == kNumXcd) a.sched[kNumXcd] = static_cast<int>(units);
-  run = run0;
-#pragma unroll
-  for (int k = 0; k < kKeep; ++k) {
-    if (cst[k] > 0) a.sched[kSchedHead + atomicAdd(&cnt[key_of(run, cst[k])], 1)] = i0 + k;
-    run += cst[k];
-  }
-  for (int i = i0 + kKeep; i < i1; ++i) {
-    const int c = unit_cost(a, n_qt, i);
-    if (c > 0) a.sched[kSchedHead + atomicAdd(&cnt[key_of(run, c)], 1)] = i;
-    run += c;
-  }
+  sched::build<1024>(a, n_qt, cnt, wsum);
 }
 
 template <int HPB, bool FUSE_NG, int MODE>
@@ -1148,7 +990,7 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
   const int n_qt = (a.max_seq_len + kBM - 1) / kBM;
   if (a.num_seqs == 0 || n_qt == 0) return hipSuccess;
   if (a.bm != kBM) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, s, a, n_qt);
+  if (!a.sched_ready) hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, s, a, n_qt);
   // a multiple of the XCD count, one workgroup per unit on average
   const int64_t units = static_cast<int64_t>(a.num_seqs) * n_qt * a.splits;
   const unsigned gx = static_cast<unsigned>((units + kNumXcd - 1) / kNumXcd * kNumXcd);

@@ -17,6 +17,7 @@
 // ahead of the MFMAs.
 #include <algorithm>
 
+#include "attn_sched.h"
 #include "common.h"
 #include "internal.h"
 
@@ -81,12 +82,17 @@ __device__ __forceinline__ T* uniform_ptr(T* p) {
 
 struct ProjEpi {
   static constexpr bool kF32 = false;
+  static constexpr bool kSched = true;
   const float* bias;
   uint16_t* out0;   // U, V, Q, K: the four column blocks of width K
   uint16_t* out1;
   uint16_t* out2;
   uint16_t* out3;
   int K;   // d_model: width of each of U, V, Q, K
+  // the attention's work list, built by one extra workgroup when sched_nqt > 0
+  // (query tiles per sequence)
+  AttnArgs sched_args;
+  int sched_nqt;
   __device__ __forceinline__ uint2 load_extra(int64_t, int) const { return make_uint2(0, 0); }
   // SiLU of 16 outputs (v + bias), each step over all 16 so that the
   // transcendental latencies overlap
@@ -117,6 +123,7 @@ struct ProjEpi {
 
 struct OutEpi {
   static constexpr bool kF32 = false;
+  static constexpr bool kSched = false;
   const float* bias;
   const uint16_t* x;
   uint16_t* y;
@@ -146,6 +153,7 @@ struct OutEpi {
 // split-K product writes to out + s * split_stride (no bias, addend or act).
 struct F32Epi {
   static constexpr bool kF32 = true;
+  static constexpr bool kSched = false;
   const float* bias;      // [N] or nullptr
   float* out;             // or nullptr
   const float* addend;    // or nullptr
@@ -299,6 +307,17 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const uint16_t* __res
   __shared__ __attribute__((aligned(16))) uint8_t sW2[kGN * kRowB];
   __shared__ __attribute__((aligned(16))) float sbias[kGN];   // bias of the tile's columns (0 past N)
   static_assert(3 * BM * kRowB + 3 * kGN * kRowB >= BM * 256, "output tile must fit the ring");
+  if constexpr (Epi::kSched) {
+    // the extra last workgroup builds the following attention's work list,
+    // with the first ring stage as its counters and the bias slots as its
+    // scan slots
+    static_assert(BM * kRowB >= sched::kListInts * 4 && kGN * 4 >= 4 * 8, "work-list scratch");
+    if (epi.sched_nqt > 0 && blockIdx.x == gridDim.x - 1) {
+      sched::build<256>(epi.sched_args, epi.sched_nqt, reinterpret_cast<int*>(sX0),
+                        reinterpret_cast<long long*>(sbias));
+      return;
+    }
+  }
 
   const int id = blockIdx.x;
   int mb, nb, sp = 0;
@@ -529,14 +548,16 @@ hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, int64_t M, int
                             hipStream_t s) {
   const int nn = (N + kGN - 1) / kGN;
   const int64_t blocks256 = (M + 255) / 256 * nn;
+  int extra = 0;   // the work-list workgroup
+  if constexpr (Epi::kSched) extra = epi.sched_nqt > 0 ? 1 : 0;
   if (blocks256 >= 4 * 512) {
     const int nm = static_cast<int>((M + 255) / 256);
-    const int grid = 8 * ((nm + 7) / 8) * nn;
+    const int grid = 8 * ((nm + 7) / 8) * nn + extra;
     hipLaunchKernelGGL((gemm_bf16_kernel<4, Epi>), dim3(grid), dim3(256), 0, s, x, w, M, N, K,
                        static_cast<int64_t>(K), static_cast<int64_t>(K), nm, nn, 1, epi);
   } else {
     const int nm = static_cast<int>((M + 127) / 128);
-    const int grid = 8 * ((nm + 7) / 8) * nn;
+    const int grid = 8 * ((nm + 7) / 8) * nn + extra;
     hipLaunchKernelGGL((gemm_bf16_kernel<2, Epi>), dim3(grid), dim3(256), 0, s, x, w, M, N, K,
                        static_cast<int64_t>(K), static_cast<int64_t>(K), nm, nn, 1, epi);
   }
@@ -728,8 +749,18 @@ hipError_t launch_to_bf16_t(const float* src, int64_t ld_src, int64_t rows, int 
 
 hipError_t launch_proj_bf16(const ProjArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
-  ProjEpi epi{a.bias, static_cast<uint16_t*>(a.out[0]), static_cast<uint16_t*>(a.out[1]),
-              static_cast<uint16_t*>(a.out[2]), static_cast<uint16_t*>(a.out[3]), a.K};
+  ProjEpi epi{};
+  epi.bias = a.bias;
+  epi.out0 = static_cast<uint16_t*>(a.out[0]);
+  epi.out1 = static_cast<uint16_t*>(a.out[1]);
+  epi.out2 = static_cast<uint16_t*>(a.out[2]);
+  epi.out3 = static_cast<uint16_t*>(a.out[3]);
+  epi.K = a.K;
+  if (a.sched && a.sched->num_seqs > 0 && a.sched->max_seq_len > 0) {
+    if (a.sched->bm != kAttnBM) return hipErrorInvalidValue;
+    epi.sched_args = *a.sched;
+    epi.sched_nqt = (a.sched->max_seq_len + kAttnBM - 1) / kAttnBM;
+  }
   return launch_gemm_bf16(static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.w), a.M,
                           4 * a.K, a.K, epi, s);
 }

@@ -42,6 +42,7 @@ struct AttnArgs {
   int in_bf16;               // per-row kernel: q/k/v/ck/cv are bf16 (else fp32)
   int64_t total_tokens;      // T
   int* sched;                // bf16 path: work list built by the scheduling pass
+  int sched_ready;           // bf16 path: the work list is already built (by the f1 launch)
   int bm;                    // bf16 path: queries per work item (64)
   int splits;                // bf16 path: key-range chunks per (sequence, query tile)
   float* partial;            // [splits, T, d] fp32 partial outputs when splits > 1
@@ -61,6 +62,7 @@ struct AttnArgs {
 // XCD, then the total) ahead of the item ids; below kAttnSplitMinUnits items
 // the key range of each item is split into up to kAttnMaxSplits chunks.
 constexpr int kAttnBM = 64;
+constexpr int kAttnBN = 32;   // keys per step of the bf16 kernel
 constexpr int kAttnSchedHead = 9;
 constexpr int64_t kAttnSplitMinUnits = 512;
 constexpr int kAttnMaxSplits = 8;
@@ -104,6 +106,9 @@ struct ProjArgs {
   void* out[4];    // U, V, Q, K  [M, K] each
   int64_t M;
   int K;           // d_model
+  // bf16: when set, the launch also builds this attention's work list (one
+  // extra workgroup), which the attention then takes as ready
+  const AttnArgs* sched = nullptr;
 };
 struct OutArgs {
   const void* g;   // [M, K]
