@@ -881,13 +881,13 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
     } else {
       HSTU_TRY(hstu::launch_attn_train_fwd(ba, s), "attention forward");
     }
-    HSTU_TRY(hstu::launch_ln_gate_fwd(AV, U, params->ln_gamma, params->ln_beta, NH, RSTD, G, T, d,
-                                      desc->ln_eps, s), "ln/gate forward");
+    // (with the bf16 products G goes out in bf16 only: f2 and dW2 read it so)
+    HSTU_TRY(hstu::launch_ln_gate_fwd(AV, U, params->ln_gamma, params->ln_beta, NH, RSTD, g16 ? nullptr : G,
+                                      g16 ? G16 : nullptr, T, d, desc->ln_eps, s), "ln/gate forward");
   }
   if (!bwd) {
     // Y = X + G W2^T + b2
     if (g16) {
-      HSTU_TRY(hstu::launch_to_bf16(G, G16, T * d, s), "bf16 copy");
       HSTU_TRY(hstu::launch_to_bf16(W2, W2_16, static_cast<int64_t>(d) * d, s), "bf16 copy");
       hstu::GemmBf16Args g{G16, d, W2_16, d, static_cast<float*>(y), d, X, T, d, d, 1};
       g.bias = params->b2;
@@ -905,7 +905,7 @@ int layer_train(const hstu_layer_desc* desc, const hstu_layer_params* params, co
     HSTU_TRY(hstu::launch_to_bf16_t(W2, d, d, d, W2T, d, s), "bf16 transpose");
     // dY^T, the row-major dY copy and db2 (dY's column sums) in one pass over dY
     HSTU_TRY(hstu::launch_to_bf16_t(DY, d, T, d, DYT, ts.tp, s, DY16, d, false, grads->db2), "bf16 transpose");
-    HSTU_TRY(hstu::launch_to_bf16_t(G, d, T, d, GT, ts.tp, s), "bf16 transpose");
+    HSTU_TRY(hstu::launch_bf16_t(G16, d, T, d, GT, ts.tp, s), "bf16 transpose");
     HSTU_TRY(gemm16(DY16, d, W2T, d, DG, d, nullptr, T, d, d, 1), "dG gemm (bf16)");
     HSTU_TRY(gemm16(DYT, ts.tp, GT, ts.tp, PART, d, nullptr, d, d, ts.kc, ts.S), "dW2 gemm (bf16)");
     HSTU_TRY(hstu::launch_sum_splits(PART, ts.S, static_cast<int64_t>(d) * d, grads->dw2, s), "dW2 sum");

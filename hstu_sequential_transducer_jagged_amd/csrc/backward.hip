@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void ln_gate_fwd_kernel(const float* __restric
                                                           const float* __restrict__ u,
                                                           const float* gamma, const float* beta,
                                                           float* nhat, float* rstd_out, float* g,
-                                                          int64_t M, int d, float eps) {
+                                                          uint16_t* g16, int64_t M, int d, float eps) {
   const int lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
@@ -167,9 +167,12 @@ __global__ __launch_bounds__(256) void ln_gate_fwd_kernel(const float* __restric
     const float4 n = make_float4((xv[i].x - mean) * rstd, (xv[i].y - mean) * rstd, (xv[i].z - mean) * rstd,
                                  (xv[i].w - mean) * rstd);
     *reinterpret_cast<float4*>(nhat + row * d + 4 * c4) = n;
-    *reinterpret_cast<float4*>(g + row * d + 4 * c4) =
-        make_float4((n.x * gm.x + bt.x) * uv.x, (n.y * gm.y + bt.y) * uv.y, (n.z * gm.z + bt.z) * uv.z,
-                    (n.w * gm.w + bt.w) * uv.w);
+    const float4 o = make_float4((n.x * gm.x + bt.x) * uv.x, (n.y * gm.y + bt.y) * uv.y,
+                                 (n.z * gm.z + bt.z) * uv.z, (n.w * gm.w + bt.w) * uv.w);
+    if (g16)
+      *reinterpret_cast<uint2*>(g16 + row * d + 4 * c4) = make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
+    else
+      *reinterpret_cast<float4*>(g + row * d + 4 * c4) = o;
   }
   if (lane == 0) rstd_out[row] = rstd;
 }
@@ -440,15 +443,15 @@ hipError_t launch_colsum(const float* X, int64_t ldx, int64_t M, int N, float* o
 }
 
 hipError_t launch_ln_gate_fwd(const float* av, const float* u, const float* gamma, const float* beta,
-                              float* nhat, float* rstd, float* g, int64_t M, int d, float eps,
+                              float* nhat, float* rstd, float* g, uint16_t* g16, int64_t M, int d, float eps,
                               hipStream_t s) {
   if (M == 0) return hipSuccess;
   const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
   if (d % 4 != 0 || d > 64 * 4 * kRow4 || !a16(av) || !a16(u) || !a16(nhat) || !a16(g) || !a16(gamma) ||
-      !a16(beta))
+      !a16(beta) || (reinterpret_cast<uintptr_t>(g16) & 7u) != 0 || (g == nullptr && g16 == nullptr))
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(ln_gate_fwd_kernel, dim3(static_cast<unsigned>((M + 3) / 4)), dim3(256), 0, s, av, u,
-                     gamma, beta, nhat, rstd, g, M, d, eps);
+                     gamma, beta, nhat, rstd, g, g16, M, d, eps);
   return hipGetLastError();
 }
 

@@ -588,8 +588,15 @@ __global__ __launch_bounds__(256) void sum_splits_kernel(const float4* __restric
 // With dst_rows the same rounded values also go out untransposed (row
 // stride ld_rows), from the row reads; with rows_x3 as the hi/lo split rows
 // [hi | lo | hi] of to_bf16x3_kernel below (lo_last = 0). With colsum, the
-// tile's fp32 column sums are added to colsum[c] atomically.
-__global__ __launch_bounds__(256) void to_bf16_t_kernel(const float* __restrict__ src, int64_t ld_src,
+// tile's fp32 column sums are added to colsum[c] atomically. S: fp32 source,
+// or bf16 (raw 16-bit patterns; the copies are then exact).
+__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4(const uint16_t* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  return make_float4(bf2f(w.x & 0xffff), bf2f(w.x >> 16), bf2f(w.y & 0xffff), bf2f(w.y >> 16));
+}
+template <typename S>
+__global__ __launch_bounds__(256) void to_bf16_t_kernel(const S* __restrict__ src, int64_t ld_src,
                                                         int64_t rows, int cols, uint16_t* __restrict__ dst,
                                                         int64_t ld_dst, uint16_t* __restrict__ dst_rows,
                                                         int64_t ld_rows, int rows_x3, float* colsum) {
@@ -604,7 +611,7 @@ __global__ __launch_bounds__(256) void to_bf16_t_kernel(const float* __restrict_
     const int c = (tid & 15) * 4;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (r0 + r < rows && c0 + c < cols) {
-      v = *reinterpret_cast<const float4*>(src + (r0 + r) * ld_src + c0 + c);
+      v = load4(src + (r0 + r) * ld_src + c0 + c);
       if (dst_rows) {
         uint16_t* const o = dst_rows + (r0 + r) * ld_rows + c0 + c;
         const uint2 hi = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
@@ -742,8 +749,21 @@ hipError_t launch_to_bf16_t(const float* src, int64_t ld_src, int64_t rows, int 
   if (cols == 0 || ld_dst == 0) return hipSuccess;
   const int64_t gx = (ld_dst + 63) / 64;
   if (gx > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(to_bf16_t_kernel, dim3(static_cast<unsigned>(gx), (cols + 63) / 64), dim3(256), 0, s,
+  hipLaunchKernelGGL(to_bf16_t_kernel<float>, dim3(static_cast<unsigned>(gx), (cols + 63) / 64), dim3(256), 0, s,
                      src, ld_src, rows, cols, dst, ld_dst, dst_rows, ld_rows, rows_x3 ? 1 : 0, colsum);
+  return hipGetLastError();
+}
+
+hipError_t launch_bf16_t(const uint16_t* src, int64_t ld_src, int64_t rows, int cols, uint16_t* dst,
+                         int64_t ld_dst, hipStream_t s) {
+  if (cols % 4 != 0 || ld_src % 4 != 0 || ld_src < cols || ld_dst % 8 != 0 || ld_dst < rows ||
+      (reinterpret_cast<uintptr_t>(src) & 7u) != 0 || !aligned16(dst))
+    return hipErrorInvalidValue;
+  if (cols == 0 || ld_dst == 0) return hipSuccess;
+  const int64_t gx = (ld_dst + 63) / 64;
+  if (gx > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(to_bf16_t_kernel<uint16_t>, dim3(static_cast<unsigned>(gx), (cols + 63) / 64), dim3(256), 0,
+                     s, src, ld_src, rows, cols, dst, ld_dst, nullptr, 0, 0, nullptr);
   return hipGetLastError();
 }
 

@@ -191,6 +191,9 @@ hipError_t launch_sum_splits(const float* part, int splits, int64_t n, float* ou
 hipError_t launch_to_bf16_t(const float* src, int64_t ld_src, int64_t rows, int cols, uint16_t* dst,
                             int64_t ld_dst, hipStream_t s, uint16_t* dst_rows = nullptr, int64_t ld_rows = 0,
                             bool rows_x3 = false, float* colsum = nullptr);
+// The same transposed copy from a bf16 source (exact).
+hipError_t launch_bf16_t(const uint16_t* src, int64_t ld_src, int64_t rows, int cols, uint16_t* dst,
+                         int64_t ld_dst, hipStream_t s);
 hipError_t launch_proj_bf16(const ProjArgs& a, hipStream_t s);
 hipError_t launch_proj_f32(const ProjArgs& a, hipStream_t s);
 hipError_t launch_out_bf16(const OutArgs& a, hipStream_t s);
@@ -284,7 +287,7 @@ hipError_t launch_ln1_bwd(const float* x, const float* dxn, const float* dy, con
                           float* dgamma, float* dbeta, int64_t M, int d, float eps, hipStream_t s);
 hipError_t launch_colsum(const float* X, int64_t ldx, int64_t M, int N, float* out, hipStream_t s);
 hipError_t launch_ln_gate_fwd(const float* av, const float* u, const float* gamma, const float* beta,
-                              float* nhat, float* rstd, float* g, int64_t M, int d, float eps,
+                              float* nhat, float* rstd, float* g, uint16_t* g16, int64_t M, int d, float eps,
                               hipStream_t s);
 hipError_t launch_ln_gate_bwd(const float* dg, const float* u, const float* nhat, const float* rstd,
                               const float* gamma, const float* beta, float* du, int64_t ldu, float* dav,

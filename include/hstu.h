@@ -389,7 +389,8 @@ int hstu_layer_bwd(const hstu_layer_desc *desc, const hstu_layer_params *params,
  * (hstu_layer_bwd_workspace_size() bytes, 256-byte aligned) the activations
  * the backward reads: Z, U, V, Q, K, AV, the normalised AV, 1/sigma and G
  * (and LayerNorm(X) with input_norm; with the bf16 flags also bf16 copies of
- * Q, K, V and, with gemm_bwd_bf16, of the f1 input transposed).
+ * Q, K, V and, with gemm_bwd_bf16, of the f1 input transposed, G being kept
+ * in bf16 only).
  * hstu_layer_bwd_after_fwd: the backward of hstu_layer_bwd, reading those
  * activations instead of recomputing them; desc, params, jagged, x and the
  * workspace must be those of the hstu_layer_fwd_train call, with the

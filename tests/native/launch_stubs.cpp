@@ -35,6 +35,9 @@ hipError_t launch_to_bf16_t(const float*, int64_t, int64_t, int, uint16_t*, int6
                             bool, float*) {
   reached("launch_to_bf16_t");
 }
+hipError_t launch_bf16_t(const uint16_t*, int64_t, int64_t, int, uint16_t*, int64_t, hipStream_t) {
+  reached("launch_bf16_t");
+}
 hipError_t launch_gemm_bf16_f32(const GemmBf16Args&, hipStream_t) { reached("launch_gemm_bf16_f32"); }
 hipError_t launch_to_bf16x3(const float*, int64_t, int, uint16_t*, int, hipStream_t) {
   reached("launch_to_bf16x3");
@@ -51,7 +54,7 @@ hipError_t launch_ln1_bwd(const float*, const float*, const float*, const float*
 }
 hipError_t launch_colsum(const float*, int64_t, int64_t, int, float*, hipStream_t) { reached("launch_colsum"); }
 hipError_t launch_ln_gate_fwd(const float*, const float*, const float*, const float*, float*, float*, float*,
-                              int64_t, int, float, hipStream_t) {
+                              uint16_t*, int64_t, int, float, hipStream_t) {
   reached("launch_ln_gate_fwd");
 }
 hipError_t launch_ln_gate_bwd(const float*, const float*, const float*, const float*, const float*,
