@@ -15,9 +15,12 @@
 //    wave per head, and walks the visible 32-key tiles (tiles above the
 //    diagonal and tiles of other targets are never visited);
 //  * K and V tiles of all HPB heads arrive by direct global->LDS loads
-//    (global_load_lds_dwordx4) into a double buffer, one tile ahead;
+//    (global_load_lds_dwordx4, written as inline assembly so that the
+//    compiler's waits for LDS reads ignore them) into a double buffer: the
+//    step's barrier sits between its two halves, and the loads of tile st+2
+//    go into tile st's buffers right after it, with a whole step to land;
 //  * the relative bias is shared by all heads: the workgroup builds each
-//    64 x 32 bias tile once, one step ahead, from per-key timestamps staged in
+//    64 x 32 bias tile once, two steps ahead, from per-key timestamps staged in
 //    LDS and a sliding window of the position table, and every wave uses it
 //    as the initial accumulator of its Q.K MFMAs (the add is free);
 //  * scores are produced directly in the base-2 domain: Q is prescaled by
@@ -31,8 +34,8 @@
 //    (transposing 16-bit reads) from the row-major tile;
 //  * software pipeline in half tiles: while the score MFMAs of one 32-query
 //    block run, the SiLU and P.V of the previous block do, so the matrix
-//    cores and the vector ALUs of a wave overlap; the DMA of the next tile
-//    is spread over the step;
+//    cores and the vector ALUs of a wave overlap; the loads of a tile are
+//    spread over the second half of the step;
 //  * time buckets are exact integers: 32-bit |dt|+1 and a leading-zero count
 //    when every pair of the tile is within 2^30 s of the block's reference
 //    time, a 64-bit path otherwise.
@@ -68,6 +71,26 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Direct global->LDS loads written as inline assembly. The compiler does
+// not see their LDS writes, so it neither holds LDS reads of other buffers
+// behind them nor turns its waits for ordinary LDS reads into full drains.
+// The kernel orders every reader after them itself: an explicit
+// s_waitcnt vmcnt(0), then a workgroup barrier. M0 carries the wave's LDS
+// destination (one wait state between its write and the load); the loads
+// have no register results.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(const void, p)));
+}
+// 16 bytes per lane from row + voff into LDS [lds + 16 lane, +16)
+__device__ __forceinline__ void dma_b128(const void* row, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(row)
+               : "memory", "m0");
+}
+// 4 bytes per lane from src into LDS [lds + 4 lane, +4)
+__device__ __forceinline__ void dma_b32(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
 }
 
 // Bias modes of the bf16 kernel (template parameter): the position and time
@@ -134,19 +157,19 @@ __device__ __forceinline__ void load_keydata(const Ctx& c, const AttnArgs& a, Ke
       const int kk = min(tile * kBN + (lane & (kBN - 1)), c.nkeys - 1);
       const int64_t* tp = kk < c.nc ? a.c_ts + (c.cs + kk) : a.ts + (c.s + kk - c.nc);
       const uint32_t* src = reinterpret_cast<const uint32_t*>(tp) + (lane >> 5);
-      __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, kd.tlo), 4, 0, 0);
+      dma_b32(src, lds_addr(kd.tlo));
     } else if (item <= 2) {
       if (MODE == kBiasLinear) continue;
       const int half = item - 1;
       int idx = c.pos_center + window_origin(c, tile) + half * 64 + lane;
       idx = idx < 0 ? 0 : (idx >= c.pos_len ? c.pos_len - 1 : idx);
-      __builtin_amdgcn_global_load_lds(a.pos_bias + idx, LDS_PTR(void, kd.pos + half * 64), 4, 0, 0);
+      dma_b32(a.pos_bias + idx, lds_addr(kd.pos + half * 64));
     } else {
       if (MODE != kBiasTyped) continue;
       if (lane < kBN) {
         const int kk = min(tile * kBN + lane, c.nkeys - 1);
         const int32_t* src = kk < c.nc ? a.c_types + (c.cs + kk) : a.types + (c.s + kk - c.nc);
-        __builtin_amdgcn_global_load_lds(src, LDS_PTR(void, kd.ty), 4, 0, 0);
+        dma_b32(src, lds_addr(kd.ty));
       }
     }
   }
@@ -161,7 +184,7 @@ __device__ __forceinline__ void dma_row(const Ctx& c, const uint16_t* base_o, co
   if (HPB < 8 && lane >= HPB * 8) return;
   const int kk = min(k0 + r, c.nkeys - 1);
   const uint16_t* src = (kk < c.nc ? base_c : base_o) + static_cast<int64_t>(kk) * c.d;
-  __builtin_amdgcn_global_load_lds(src + lane * 8, LDS_PTR(void, dst + r * ROWB), 16, 0, 0);
+  dma_b128(src, static_cast<uint32_t>(lane) * 16u, lds_addr(dst + r * ROWB));
 }
 
 // P = S' / (1 + 2^S') for scores [8h, 8h + 8) of one accumulator, packed to
@@ -417,45 +440,31 @@ __device__ __forceinline__ void dma_slot(const Ctx& c, const uint16_t* kbase_o, 
   }
 }
 
-// One key step of the software pipeline (see the kernel). The LDS buffers
-// are distinct restrict-qualified arguments: the compiler can then tell that
-// a DMA into the next buffers does not alias the reads of the current ones,
-// and issues the DMA early without making those reads wait for it. MORE: a
-// later tile of the chunk follows (its DMA, key data and bias).
-template <int HPB, bool MORE, int MODE>
+// One key step of the software pipeline (see the kernel). The step reads
+// the K, V and bias tiles of tile st (cur*) before its barrier; after it,
+// every wave has read them, so the same buffers take the K/V rows and the
+// bias of tile st+2, and keyD (key data of tile st+3) replaces the key data
+// of tile st+1. The loads of tile st+2 then have until the barrier of step
+// st+1, a whole step, to land. AHEAD: 2 when tile st+2 exists (barrier,
+// loads and bias), 1 for the step before the last (barrier only: tile st+1
+// is landing), 0 for the last step. Key data past the chunk's last tile is
+// clamped to it (a few bytes, into a buffer that is not read again). FIRST:
+// the chunk's first step, which also builds the bias of tile st+1 into the
+// other buffer (othB, from the key data in othD) before its barrier.
+template <int HPB, int AHEAD, bool FIRST, int MODE>
 __device__ __forceinline__ void attn_step(
     const Ctx& c, const SlotQ<512 / (64 * HPB)>& sq, const AttnArgs& a, int st, int st_hi, int skip_a,
-    int n_skip, const uint8_t* __restrict__ curK, const float* __restrict__ curB,
-    const uint8_t* __restrict__ curV, uint8_t* __restrict__ nxtK, uint8_t* __restrict__ nxtV,
-    float* __restrict__ nxtB, const KeyData* __restrict__ nxtD, KeyData* __restrict__ curD,
-    const float* __restrict__ tb_clz, const float* __restrict__ tb_lin, const uint16_t* kbase_o,
-    const uint16_t* kbase_c, const uint16_t* vbase_o, const uint16_t* vbase_c, const bf16x8 (&qf)[2][4],
-    f32x16 (&acc)[2][2], f32x16& s0, f32x16& s1, bf16x8 (&vf)[2][2], int koff, int voff, int wave, int lane,
-    int tid) {
+    int n_skip, uint8_t* __restrict__ curK, float* __restrict__ curB, uint8_t* __restrict__ curV,
+    const KeyData* __restrict__ biasD, KeyData* __restrict__ keyD, float* __restrict__ othB,
+    const KeyData* __restrict__ othD, const float* __restrict__ tb_clz,
+    const float* __restrict__ tb_lin, const uint16_t* kbase_o, const uint16_t* kbase_c, const uint16_t* vbase_o,
+    const uint16_t* vbase_c, const bf16x8 (&qf)[2][4], f32x16 (&acc)[2][2], f32x16& s0, f32x16& s1,
+    bf16x8 (&vf)[2][2], int koff, int voff, int wave, int lane, int tid) {
   constexpr int ROWBV = Rows<HPB>::ROWBV;
-  const int t1 = MORE ? (st + 1 < skip_a ? st + 1 : st + 1 + n_skip) : 0;
-  const int k1 = t1 * kBN;
-  // the bias of tile st+1 takes the split fast path when all its keys are
-  // visible non-targets for the whole block and times fit 32 bits
-  const bool fast1 = (k1 + kBN - 1 - c.nc <= c.q0) && (k1 + kBN - 1 - c.nc < c.first_tgt) && !c.wide;
-  FastBias<512 / (64 * HPB)> fb;
-  // A0: the key-data reads of tile st+1's bias go first, so that their
-  // dependent time-bias lookups are not queued behind this step's big LDS
-  // reads; DMA of the key data of tile st+2 and a quarter of the K/V rows
-  if (MORE) fast_bias_issue<HPB, MODE>(c, sq, *nxtD, t1, tid, fb);
-  if (MORE && st + 2 < st_hi) {
-    const int t2 = st + 2 < skip_a ? st + 2 : st + 2 + n_skip;
-    load_keydata<HPB, MODE>(c, a, *curD, t2, wave, lane);
-  }
-  if (MORE) {
-    dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, nxtK, nxtV, k1, 0, wave, lane);
-    dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, nxtK, nxtV, k1, 1, wave, lane);
-  }
-  __builtin_amdgcn_sched_barrier(0);
   // R0: SiLU of block 1 of tile st-1 in quarters, each quarter's registers
   // then refilled with the block-1 bias of tile st; P.V with V of tile
   // st-1, each half of vf then refilled with V of tile st; the score MFMAs
-  // of block 0 in the second half; the rest of the DMA
+  // of block 0 in the second half
   bf16x8 kf[4];
   {
     uint32_t w[8];
@@ -466,19 +475,11 @@ __device__ __forceinline__ void attn_step(
       kf[cc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(curK + koff + cc * 32));
     load_bias_block(curB, 0, lane, s0);
     load_bias_quarter(curB, 1, 0, lane, s1);
-    if (MORE) {
-      dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, nxtK, nxtV, k1, 2, wave, lane);
-      dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, nxtK, nxtV, k1, 3, wave, lane);
-    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int sr = 1; sr < 4; ++sr) {
       silu4(s1, sr, w[2 * sr], w[2 * sr + 1]);
       load_bias_quarter(curB, 1, sr, lane, s1);
-      if (MORE && sr < 3) {
-        dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, nxtK, nxtV, k1, 2 + 2 * sr, wave, lane);
-        dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, nxtK, nxtV, k1, 3 + 2 * sr, wave, lane);
-      }
       if (sr >= 2) {
         s0 = mfma32(kf[2 * (sr - 2)], qf[0][2 * (sr - 2)], s0);
         s0 = mfma32(kf[2 * (sr - 2) + 1], qf[0][2 * (sr - 2) + 1], s0);
@@ -492,22 +493,52 @@ __device__ __forceinline__ void attn_step(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    asm volatile("" ::"v"(w[7]));
   }
+  if (FIRST && AHEAD >= 1) {
+    const int s1t = st + 1 < skip_a ? st + 1 : st + 1 + n_skip;
+    build_bias<HPB, MODE>(c, a, sq, *othD, othB, tb_clz, tb_lin, s1t, tid);
+  }
+  // the barrier: every wave has read tile st's buffers, and the loads of
+  // tile st+1 and of the key data of tile st+2 (issued one step earlier)
+  // have landed
+  constexpr bool MORE = AHEAD == 2;
+  int t2 = 0;
+  bool fast2 = false;
+  FastBias<512 / (64 * HPB)> fb;
+  if (AHEAD >= 1) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  if (MORE) {
+    const int s2 = st + 2;
+    t2 = s2 < skip_a ? s2 : s2 + n_skip;
+    // the bias of tile t2 takes the split fast path when all its keys are
+    // visible non-targets for the whole block and times fit 32 bits
+    const int k2 = t2 * kBN;
+    fast2 = (k2 + kBN - 1 - c.nc <= c.q0) && (k2 + kBN - 1 - c.nc < c.first_tgt) && !c.wide;
+    fast_bias_issue<HPB, MODE>(c, sq, *biasD, t2, tid, fb);
+    const int s3 = min(st + 3, st_hi - 1);
+    load_keydata<HPB, MODE>(c, a, *keyD, s3 < skip_a ? s3 : s3 + n_skip, wave, lane);
+    dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, curK, curV, k2, 0, wave, lane);
+    dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, curK, curV, k2, 1, wave, lane);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   // R1: SiLU of block 0 of tile st and its P.V; the score MFMAs of block 1;
-  // the time-bias lookups of tile st+1 after the first quarter and their
-  // combine and store after the last, so that each LDS round trip of the
-  // bias has most of a round to land
+  // the K/V rows of tile t2 spread over the quarters; the time-bias lookups
+  // of tile t2 after the first quarter and their combine and store after the
+  // last
   {
     uint32_t w[8];
 #pragma unroll
     for (int sr = 0; sr < 4; ++sr) {
       silu4(s0, sr, w[2 * sr], w[2 * sr + 1]);
-      if (MORE && sr == 0) fast_bias_lookup<HPB, MODE>(c, a, sq, tb_clz, fb);
-      // the store waits for every LDS read issued before it (the DMA keeps
-      // the compiler from counting partially): last, after the MFMAs
-      if (MORE && sr == 3) fast_bias_store<HPB, MODE>(a, fb, nxtB, tid);
-      // two score MFMAs every other quarter: the block-1 bias read last in
-      // R0 has time to land
+      if (MORE && sr == 1) fast_bias_lookup<HPB, MODE>(c, a, sq, tb_clz, fb);
+      if (MORE && sr < 3) {
+        dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, curK, curV, t2 * kBN, 2 + 2 * sr, wave, lane);
+        dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, curK, curV, t2 * kBN, 3 + 2 * sr, wave, lane);
+      }
+      if (MORE && sr == 3) fast_bias_store<HPB, MODE>(a, fb, curB, tid);
       if (sr & 1) {
         s1 = mfma32(kf[sr - 1], qf[1][sr - 1], s1);
         s1 = mfma32(kf[sr], qf[1][sr], s1);
@@ -518,15 +549,10 @@ __device__ __forceinline__ void attn_step(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // keep the wait and the barrier after the SiLU of this step
     asm volatile("" ::"v"(w[7]));
   }
   // tiles off the fast path: the full bias builder overwrites the tile
-  if (MORE && !fast1) build_bias<HPB, MODE>(c, a, sq, *nxtD, nxtB, tb_clz, tb_lin, t1, tid);
-  if (MORE) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
+  if (MORE && !fast2) build_bias<HPB, MODE>(c, a, sq, *biasD, curB, tb_clz, tb_lin, t2, tid);
 }
 
 // The scheduling pass in its own launch: one workgroup of 1024 threads.
@@ -722,36 +748,50 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
 #define SV(i) ((i) ? sV1 : sV0)
 #define SB(i) ((i) ? sB1 : sB0)
 #define SD(i) ((i) ? &sD1 : &sD0)
-  // ---- prologue: key data of tiles lo and lo+1, K/V rows and bias of tile lo ----
+  // ---- prologue: key data and K/V rows of tiles lo and lo+1 (key data of
+  // tile t in buffer (t - lo) & 1), the bias of tile lo, then the key data
+  // of tile lo+2 ----
+  const bool two = st_lo + 1 < st_hi;
   load_keydata<HPB, MODE>(c, a, sD0, tile_of(st_lo), wave, lane);
-  load_keydata<HPB, MODE>(c, a, sD1, tile_of(min(st_lo + 1, st_hi - 1)), wave, lane);
-  {
-    const int k0 = tile_of(st_lo) * kBN;
+  if (two) load_keydata<HPB, MODE>(c, a, sD1, tile_of(st_lo + 1), wave, lane);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (t == 1 && !two) break;
+    const int k0 = tile_of(st_lo + t) * kBN;
 #pragma unroll
     for (int it = 0; it < RPW; ++it) {
-      dma_row<HPB, ROWBK>(c, kbase_o, kbase_c, sK0, k0, wave + it * HPB, lane);
-      dma_row<HPB, ROWBV>(c, vbase_o, vbase_c, sV0, k0, wave + it * HPB, lane);
+      dma_row<HPB, ROWBK>(c, kbase_o, kbase_c, SK(t), k0, wave + it * HPB, lane);
+      dma_row<HPB, ROWBV>(c, vbase_o, vbase_c, SV(t), k0, wave + it * HPB, lane);
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // the K/V rows of tile lo+1 (this wave's last 2 RPW loads) may still be
+  // landing while bias lo is built; the first step's barrier waits for them
+  if (two) {
+    constexpr int kLate = 2 * RPW < 63 ? 2 * RPW : 63;
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLate) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   __syncthreads();
   build_bias<HPB, MODE>(c, a, sq, sD0, sB0, tb_clz, tb_lin, tile_of(st_lo), tid);
   __syncthreads();
+  if (st_lo + 2 < st_hi) load_keydata<HPB, MODE>(c, a, sD0, tile_of(st_lo + 2), wave, lane);
 
   // Software pipeline in half tiles. Registers carried from step st-1 to
   // step st: the scores of the second 32-query block of tile st-1 (s1) and
-  // the V operand of tile st-1 (vf). Step st (attn_step), buffers (st-lo)&1:
-  //  A0. LDS reads for the bias of tile st+1 (first, so that their dependent
-  //      time-bias lookups are not queued behind the big reads); DMA of the
-  //      key data of tile st+2 and of the K/V rows of tile st+1 (over A0 and
-  //      the first half of R0);
+  // the V operand of tile st-1 (vf). Step st (attn_step) uses buffer set
+  // p = (st-lo)&1 for the K, V and bias tiles of tile st:
   //  R0. SiLU of s1 in quarters and O1 += P V_{st-1}; each consumed quarter of
   //      s1 is refilled with the block-1 bias of tile st and each consumed
   //      half of vf with V of tile st; the score MFMAs of block 0 of tile st
   //      into s0 (K and its bias read in the first quarter) in the second
-  //      half; the bias of tile st+1 is finished and stored;
+  //      half;
+  //  barrier: set p is free, tile st+1 and the key data of tile st+2 have
+  //      landed;
   //  R1. SiLU of s0 and O0 += P V_st, overlapped with the score MFMAs of
-  //      block 1 into s1.
+  //      block 1 into s1; the K/V rows of tile st+2 go into set p and its
+  //      bias is built there (key data from buffer p), the key data of tile
+  //      st+3 goes into buffer p^1.
   // After the last step, a drain runs the SiLU and P.V of s1.
   // s1 and vf start at zero: the first step's R0 then adds exactly zero.
   f32x16 s0, s1;
@@ -763,20 +803,35 @@ __global__ __launch_bounds__(64 * HPB, 1) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) vf[db][kh] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
   // steps alternate between the two buffer sets
-#define HSTU_ATTN_STEP(MORE, K0, B0, V0, K1, V1, B1, D1, D0)                                          \
-  attn_step<HPB, MORE, MODE>(c, sq, a, st, st_hi, skip_a, n_skip, K0, B0, V0, K1, V1, B1, D1, D0, tb_clz,  \
-                       tb_lin, kbase_o, kbase_c, vbase_o, vbase_c, qf, acc, s0, s1, vf, koff, voff,      \
-                       wave, lane, tid)
+#define HSTU_ATTN_STEP(AHEAD, FIRST, K, B, V, DB, DK)                                                     \
+  attn_step<HPB, AHEAD, FIRST, MODE>(c, sq, a, st, st_hi, skip_a, n_skip, K, B, V, DB, DK, sB1, &sD1, tb_clz,  \
+                                     tb_lin, kbase_o, kbase_c, vbase_o, vbase_c, qf, acc, s0, s1, vf, koff,   \
+                                     voff, wave, lane, tid)
   int st = st_lo;
+  // the first step also builds the bias of tile lo+1 before its barrier
+  if (st + 2 < st_hi) {
+    HSTU_ATTN_STEP(2, true, sK0, sB0, sV0, &sD0, &sD1);
+    ++st;
+  } else if (st + 1 < st_hi) {
+    HSTU_ATTN_STEP(1, true, sK0, sB0, sV0, &sD0, &sD1);
+    ++st;
+  }
 #pragma clang loop unroll(disable)
-  for (; st + 1 < st_hi; ++st) {
+  for (; st + 2 < st_hi; ++st) {
     const int p = (st - st_lo) & 1;
-    HSTU_ATTN_STEP(true, SK(p), SB(p), SV(p), SK(p ^ 1), SV(p ^ 1), SB(p ^ 1), SD(p ^ 1), SD(p));
+    HSTU_ATTN_STEP(2, false, SK(p), SB(p), SV(p), SD(p), SD(p ^ 1));
+  }
+  if (st + 1 < st_hi) {
+    const int p = (st - st_lo) & 1;
+    HSTU_ATTN_STEP(1, false, SK(p), SB(p), SV(p), SD(p), SD(p ^ 1));
+    ++st;
   }
   {
     const int p = (st - st_lo) & 1;
-    HSTU_ATTN_STEP(false, SK(p), SB(p), SV(p), SK(p ^ 1), SV(p ^ 1), SB(p ^ 1), SD(p ^ 1), SD(p));
+    HSTU_ATTN_STEP(0, false, SK(p), SB(p), SV(p), SD(p), SD(p ^ 1));
   }
+  // the clamped key-data loads of the last full step may still be in flight
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   // drain: SiLU and P.V of block 1 of the last tile
 #pragma unroll
   for (int kh = 0; kh < 2; ++kh) {
