@@ -520,12 +520,11 @@ __device__ __forceinline__ void attn_step(
     fast_bias_issue<HPB, MODE>(c, sq, *biasD, t2, tid, fb);
     const int s3 = min(st + 3, st_hi - 1);
     load_keydata<HPB, MODE>(c, a, *keyD, s3 < skip_a ? s3 : s3 + n_skip, wave, lane);
-    dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, curK, curV, k2, 0, wave, lane);
-    dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, curK, curV, k2, 1, wave, lane);
   }
   __builtin_amdgcn_sched_barrier(0);
   // R1: SiLU of block 0 of tile st and its P.V; the score MFMAs of block 1;
-  // the K/V rows of tile t2 spread over the quarters; the time-bias lookups
+  // the K/V rows of tile t2, two loads per quarter (issued faster, they
+  // stall the wave; issued later, they land late); the time-bias lookups
   // of tile t2 after the first quarter and their combine and store after the
   // last
   {
@@ -534,9 +533,9 @@ __device__ __forceinline__ void attn_step(
     for (int sr = 0; sr < 4; ++sr) {
       silu4(s0, sr, w[2 * sr], w[2 * sr + 1]);
       if (MORE && sr == 1) fast_bias_lookup<HPB, MODE>(c, a, sq, tb_clz, fb);
-      if (MORE && sr < 3) {
-        dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, curK, curV, t2 * kBN, 2 + 2 * sr, wave, lane);
-        dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, curK, curV, t2 * kBN, 3 + 2 * sr, wave, lane);
+      if (MORE) {
+        dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, curK, curV, t2 * kBN, 2 * sr, wave, lane);
+        dma_slot<HPB>(c, kbase_o, kbase_c, vbase_o, vbase_c, curK, curV, t2 * kBN, 2 * sr + 1, wave, lane);
       }
       if (MORE && sr == 3) fast_bias_store<HPB, MODE>(a, fb, curB, tid);
       if (sr & 1) {
